@@ -1,0 +1,101 @@
+"""Pins of the oracle's block-wise INT8 stochastic rounding (oracle/int8.py).
+
+Properties fixed by the gradient-quantisation tutorial's INT8 recipe: codes
+stay in [-127, 127]; the dequantised value is within one scale step of the
+input; an input that is an exact multiple of the scale is coded exactly;
+zero blocks stay zero; the block maximum codes to 126 or 127; stochastic
+rounding is unbiased and rounds up with probability equal to the fraction.
+"""
+
+import numpy as np
+
+from oracle.int8 import int8_sr
+from oracle.philox import uniforms
+
+F32 = np.float32
+
+
+def _laplace(rng, n, b=1e-3):
+    return rng.laplace(0.0, b, size=n).astype(F32)
+
+
+def test_codes_range_and_error_bound():
+    rng = np.random.default_rng(0)
+    g = _laplace(rng, 256 * 64)
+    g[::997] *= 100
+    out = int8_sr(g, None, seed=4, step=1)
+    q = out["codes"].astype(np.int32)
+    assert q.min() >= -127 and q.max() <= 127
+    sc = np.repeat(out["scales"], 256).astype(np.float64)
+    err = np.abs(out["deq"].astype(np.float64) - g.astype(np.float64))
+    assert np.all(err < sc * (1 + 2.0 ** -20))
+    # scale = max|g| / 127 per block (one binary32 division)
+    M = np.abs(g).reshape(-1, 256).max(axis=1)
+    assert np.array_equal(out["scales"], (M / F32(127)).astype(F32))
+
+
+def test_integral_inputs_are_exact():
+    # block max 127 gives scale exactly 1, so integers code to themselves
+    rng = np.random.default_rng(1)
+    g = rng.integers(-127, 128, size=256).astype(F32)
+    g[17] = 127
+    out = int8_sr(g, None, seed=9, step=3)
+    assert out["scales"][0] == 1
+    assert np.array_equal(out["codes"].astype(F32), g)
+    assert np.array_equal(out["deq"], g)
+    assert np.all(out["e"] == 0)
+
+
+def test_zero_block_and_max_code():
+    rng = np.random.default_rng(2)
+    g = _laplace(rng, 512)
+    g[:256] = 0.0
+    out = int8_sr(g, None, seed=1, step=1)
+    assert np.all(out["codes"][:256] == 0) and np.all(out["deq"][:256] == 0)
+    assert out["scales"][0] == 0
+    j = 256 + int(np.argmax(np.abs(g[256:])))
+    assert abs(int(out["codes"][j])) in (126, 127)
+
+
+def test_error_feedback_adds_residual():
+    rng = np.random.default_rng(3)
+    g = _laplace(rng, 1024)
+    e = _laplace(rng, 1024, 1e-4)
+    a = int8_sr(g, e, seed=2, step=5)
+    b = int8_sr((g + e).astype(F32), None, seed=2, step=5)
+    for key in ("codes", "scales", "deq", "e"):
+        assert np.array_equal(a[key], b[key])
+    assert np.array_equal(a["e"], ((g + e).astype(F32) - a["deq"]).astype(F32))
+
+
+def test_rounds_up_with_probability_of_fraction():
+    # scale 1 (max 127): values k + 1/4 round up a quarter of the time
+    n = 256 * 400
+    g = np.full(n, F32(10.25))
+    g[::256] = 127
+    out = int8_sr(g, None, seed=11, step=2)
+    mask = np.ones(n, dtype=bool)
+    mask[::256] = False
+    up = (out["codes"][mask] == 11).mean()
+    assert abs(up - 0.25) < 4 * np.sqrt(0.25 * 0.75 / mask.sum())
+    assert set(np.unique(out["codes"][mask])) <= {10, 11}
+
+
+def test_unbiased_over_seeds():
+    rng = np.random.default_rng(4)
+    g = _laplace(rng, 256 * 4)
+    acc = np.zeros(g.size)
+    seeds = 256
+    for s in range(seeds):
+        acc += int8_sr(g, None, seed=1000 + s, step=1)["deq"].astype(np.float64) - g
+    mean_err = acc / seeds
+    sc = np.repeat(int8_sr(g, None, seed=0, step=1)["scales"], 256).astype(np.float64)
+    # each draw has |err| < scale, so the std of the mean is below scale/2/16
+    assert np.all(np.abs(mean_err) <= 4 * 0.5 * sc / np.sqrt(seeds))
+
+
+def test_uniforms_grid_and_range():
+    u = uniforms(12345, 10000, seed=7, step=3)
+    assert u.min() >= 0 and u.max() < 1
+    assert np.all((u * 2 ** 24) == np.floor(u * 2 ** 24))
+    assert abs(u.mean() - 0.5) < 0.02

@@ -1,0 +1,276 @@
+"""Pins of the oracle's 1-bit worker/server compression (oracle/onebit.py).
+
+Each test fixes the oracle against something it does not compute itself:
+exact rational arithmetic on tiny inputs, the error identity and the
+telescoping property the 1-bit Adam article states for error compensation
+(section 2.1), optimality of the mean-|.| scale for a fixed sign vector, the
+clamp bound the article's troubleshooting section asks for (error below
+clip_value), and closed forms of the server in degenerate cases.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import bits as B
+from oracle import onebit as O
+from tests._exactref import frac, rn, ulp
+
+F32 = np.float32
+
+
+def _draw(rng, shape, scale=1e-3):
+    return (rng.standard_normal(shape) * scale).astype(F32)
+
+
+def _brute_worker(m, e, clip, k):
+    """Element-by-element exact evaluation of compensation, scale, sign,
+    error, written from the equations with Fractions."""
+    n, N = m.shape
+    L = N // n
+    gc = np.empty_like(m)
+    s = np.empty((n, n), dtype=F32)
+    e_new = np.empty_like(m)
+    for i in range(n):
+        for j in range(N):
+            km = frac(m[i, j]) if k is None else frac(rn(frac(k[j]) * frac(m[i, j])))
+            v = rn(km + frac(e[i, j]))
+            if clip > 0:
+                v = min(max(v, F32(-clip)), F32(clip))
+            gc[i, j] = v
+        for c in range(n):
+            chunk = gc[i, c * L:(c + 1) * L]
+            s[i, c] = rn(sum(abs(frac(v)) for v in chunk) / L)
+            for j in range(L):
+                v = chunk[j]
+                q = frac(s[i, c]) if v >= 0 else -frac(s[i, c])
+                e_new[i, c * L + j] = rn(frac(v) - q)
+    return gc, s, e_new
+
+
+@pytest.mark.parametrize("clip,use_k", [(0.0, False), (2.5e-3, False), (0.0, True)])
+def test_worker_matches_exact_arithmetic(clip, use_k):
+    rng = np.random.default_rng(7)
+    n, N = 2, 128
+    m = _draw(rng, (n, N))
+    e = _draw(rng, (n, N), 3e-4)
+    # zeros of both signs must encode +1 (sign(0) = +1)
+    m[:, :4] = np.array([0.0, -0.0, 0.0, -0.0], dtype=F32)
+    e[:, :4] = np.array([0.0, 0.0, -0.0, -0.0], dtype=F32)
+    k = (2.0 ** rng.integers(-3, 4, size=N) * rng.uniform(0.5, 1.5, size=N)).astype(F32) if use_k else None
+    out = O.worker_compress(m, e, clip=clip, k=k)
+    gc, s, e_new = _brute_worker(m, e, clip, k)
+    assert np.array_equal(out["gc"], gc)
+    assert np.array_equal(out["s"], s)
+    assert np.array_equal(out["e"], e_new)
+    assert np.all(out["bits"][:, 0] & np.uint32(0xF) == 0xF)
+    want_bits = np.zeros((n, N // 32), dtype=np.uint32)
+    for i in range(n):
+        for j in range(N):
+            if gc[i, j] >= 0:
+                want_bits[i, j >> 5] |= np.uint32(1 << (j & 31))
+    assert np.array_equal(out["bits"], want_bits)
+
+
+def test_reset_ignores_error():
+    rng = np.random.default_rng(3)
+    m = _draw(rng, (2, 128))
+    e = _draw(rng, (2, 128))
+    a = O.worker_compress(m, e, reset=True)
+    b = O.worker_compress(m, np.zeros_like(e))
+    for key in ("gc", "s", "e", "bits"):
+        assert np.array_equal(a[key], b[key])
+
+
+def test_error_identity_within_one_rounding():
+    """e_t = g'_t - q_t up to the one binary32 rounding of the subtraction."""
+    rng = np.random.default_rng(11)
+    n, N = 4, 1024
+    out = O.worker_compress(_draw(rng, (n, N)), _draw(rng, (n, N), 1e-4))
+    L = N // n
+    for i in range(n):
+        for c in range(n):
+            sl = slice(c * L, (c + 1) * L)
+            q = B.signed(B.sign_bit(out["gc"][i, sl]), out["s"][i, c])
+            for gv, qv, ev in zip(out["gc"][i, sl][::7], q[::7], out["e"][i, sl][::7]):
+                assert abs(frac(ev) - (frac(gv) - frac(qv))) <= ulp(ev) / 2
+
+
+def _run_steps(ms, clip=0.0):
+    n, N = ms[0].shape
+    e = np.zeros((n, N), dtype=F32)
+    hist = []
+    for m in ms:
+        out = O.worker_compress(m, e, clip=clip)
+        hist.append((m, e, out))
+        e = out["e"]
+    return hist
+
+
+def test_telescoping_exact_on_dyadic_inputs():
+    """sum_t q_t + e_T = sum_t m_t exactly when no operation rounds: inputs
+    on a 2^-8 grid in (-1, 1), L = 64, two steps keep every value on a grid
+    binary32 represents."""
+    rng = np.random.default_rng(5)
+    n, N, T = 2, 128, 2
+    ms = [(rng.integers(-255, 256, size=(n, N)) / 256.0).astype(F32) for _ in range(T)]
+    hist = _run_steps(ms)
+    L = N // n
+    for i in range(n):
+        for j in range(N):
+            c = j // L
+            total_q = sum(frac(out["s"][i, c]) * (1 if out["gc"][i, j] >= 0 else -1) for _, _, out in hist)
+            total_m = sum(frac(m[i, j]) for m in ms)
+            assert total_q + frac(hist[-1][2]["e"][i, j]) == total_m
+
+
+@pytest.mark.parametrize("clip", [0.0, 1.5e-3])
+def test_telescoping_bounded_by_roundings(clip):
+    """Random inputs: |sum q + e_T - sum m + sum clipped| <= sum of half-ulps
+    of every rounded compensation and error."""
+    rng = np.random.default_rng(9)
+    n, N, T = 2, 256, 6
+    ms = [_draw(rng, (n, N)) for _ in range(T)]
+    hist = _run_steps(ms, clip=clip)
+    L = N // n
+    for i in range(n):
+        for j in range(0, N, 5):
+            c = j // L
+            lhs = frac(hist[-1][2]["e"][i, j])
+            rhs = Fraction(0)
+            bound = Fraction(0)
+            for m, e_prev, out in hist:
+                g = out["gc"][i, j]
+                lhs += frac(out["s"][i, c]) * (1 if g >= 0 else -1)
+                rhs += frac(m[i, j])
+                raw = F32(m[i, j] + e_prev[i, j])
+                rhs -= frac(raw) - frac(g)  # clipped-off amount
+                bound += (ulp(raw) + ulp(out["e"][i, j])) / 2
+            assert abs(lhs - rhs) <= bound
+
+
+def test_scale_is_the_l2_optimal_magnitude():
+    """For fixed signs, sum (g' - s sgn)^2 is minimal at s = mean|g'|: moving
+    s by one binary32 step in either direction must not lower it."""
+    rng = np.random.default_rng(21)
+    n, N = 4, 4096
+    out = O.worker_compress(_draw(rng, (n, N)) * np.float32(3), _draw(rng, (n, N)))
+    L = N // n
+    for i in range(n):
+        for c in range(n):
+            g = out["gc"][i, c * L:(c + 1) * L].astype(np.float64)
+            s = out["s"][i, c]
+            abs_sum = sum(abs(Fraction(float(x))) for x in g)
+            sq = sum(Fraction(float(x)) ** 2 for x in g)
+
+            def cost(sv):
+                sv = Fraction(float(sv))
+                return sq - 2 * sv * abs_sum + L * sv * sv
+
+            here = cost(s)
+            assert here <= cost(np.nextafter(s, F32(np.inf), dtype=F32))
+            assert here <= cost(np.nextafter(s, F32(0), dtype=F32))
+            # and the orthogonality <e, sgn> = sum|g'| - L s vanishes up to rounding of s
+            assert abs(float(np.sum(np.abs(g)) - L * float(s))) <= L * float(ulp(s))
+
+
+def test_clamp_bounds_error():
+    rng = np.random.default_rng(4)
+    n, N, clip = 4, 1024, 2e-3
+    e = np.zeros((n, N), dtype=F32)
+    for t in range(5):
+        m = _draw(rng, (n, N), 4e-3)
+        m[0, :8] = [np.inf, -np.inf, 1e30, -1e30, np.nan, 0, -0.0, 5]
+        out = O.worker_compress(m, e, clip=clip)
+        assert np.all(np.abs(out["gc"]) <= F32(clip))
+        assert np.all(np.abs(out["e"]) <= F32(clip))
+        assert out["gc"][0, 4] == F32(-clip)  # NaN clamps to -clip
+        e = out["e"]
+
+
+def test_server_single_worker_is_identity():
+    rng = np.random.default_rng(8)
+    N = 256
+    w = O.worker_compress(_draw(rng, (1, N)), np.zeros((1, N), dtype=F32))
+    sv = O.server_reduce(w["bits"], w["s"], np.zeros(N, dtype=F32))
+    assert np.array_equal(sv["bits"], w["bits"][0])
+    assert sv["S"][0] == w["s"][0, 0]
+    assert np.all(sv["E"] == 0)
+    assert np.array_equal(O.decompress(sv["bits"], sv["S"]), B.signed(B.sign_bit(w["gc"][0]), w["s"][0, 0]))
+
+
+def test_server_unanimous_signs():
+    rng = np.random.default_rng(12)
+    n, N = 4, 1024
+    base = O.worker_compress(_draw(rng, (1, N)), np.zeros((1, N), dtype=F32))["bits"][0]
+    bits = np.stack([base] * n)
+    s = np.abs(_draw(rng, (n, n))) + F32(1e-4)
+    sv = O.server_reduce(bits, s, np.zeros(N, dtype=F32))
+    assert np.array_equal(sv["bits"], base)
+
+
+def test_server_average_exact_sequence():
+    """n = 3 (not a power of two): sequential binary32 accumulation in worker
+    order, then one rounding of the division."""
+    rng = np.random.default_rng(13)
+    n, N = 3, 192
+    L = N // n
+    bits = rng.integers(0, 2**32, size=(n, N // 32), dtype=np.uint64).astype(np.uint32)
+    s = np.abs(_draw(rng, (n, n))).astype(F32)
+    sv = O.server_reduce(bits, s, np.zeros(N, dtype=F32))
+    for c in range(n):
+        for j in range(0, L, 3):
+            J = c * L + j
+            acc = F32(0.0)
+            for i in range(n):
+                bit = (int(bits[i, J >> 5]) >> (J & 31)) & 1
+                acc = rn(frac(acc) + (frac(s[i, c]) if bit else -frac(s[i, c])))
+            assert sv["avg"][J] == rn(frac(acc) / n)
+
+
+def test_two_level_momentum_identity():
+    """1-bit LAMB analysis paragraph with a unit step ratio: the transmitted
+    global momentum equals the workers' average momentum plus the previous
+    combined error minus the new one, delta = E + mean_i e_i.  Dyadic inputs,
+    n = 2, two steps: every operation is exact, so the identity is exact."""
+    rng = np.random.default_rng(17)
+    n, N, T = 2, 128, 2
+    e = np.zeros((n, N), dtype=F32)
+    E = np.zeros(N, dtype=F32)
+    delta_prev = [Fraction(0)] * N
+    for t in range(T):
+        m = (rng.integers(-255, 256, size=(n, N)) / 256.0).astype(F32)
+        w = O.worker_compress(m, e)
+        sv = O.server_reduce(w["bits"], w["s"], E)
+        mbar = O.decompress(sv["bits"], sv["S"])
+        for j in range(N):
+            delta = frac(sv["E"][j]) + (frac(w["e"][0, j]) + frac(w["e"][1, j])) / 2
+            avg_m = (frac(m[0, j]) + frac(m[1, j])) / 2
+            assert frac(mbar[j]) == avg_m + delta_prev[j] - delta
+            delta_prev[j] = delta
+        e, E = w["e"], sv["E"]
+
+
+def test_layer_scale_power_of_two_is_transparent():
+    """Uniform k = 2^p: scaling before compression and dividing after gives
+    exactly the unscaled path (positive homogeneity of the method)."""
+    rng = np.random.default_rng(19)
+    n, N = 4, 1024
+    m = _draw(rng, (n, N))
+    k = np.full(N, F32(8.0))
+    a = O.worker_compress(m, np.zeros_like(m), k=k)
+    b = O.worker_compress(m, np.zeros_like(m))
+    assert np.array_equal(a["bits"], b["bits"])
+    assert np.array_equal(a["s"], b["s"] * F32(8.0))
+    sa = O.server_reduce(a["bits"], a["s"], np.zeros(N, dtype=F32))
+    sb = O.server_reduce(b["bits"], b["s"], np.zeros(N, dtype=F32))
+    assert np.array_equal(O.decompress(sa["bits"], sa["S"], k=k), O.decompress(sb["bits"], sb["S"]))
+
+
+def test_layer_scale_segments():
+    buf = np.arange(1, 11, dtype=F32)
+    off = [0, 3, 4, 10]
+    k = np.array([2, 0.5, 4], dtype=F32)
+    assert list(O.layer_scale(buf, off, k, False)) == [2, 4, 6, 2, 20, 24, 28, 32, 36, 40]
+    assert list(O.layer_scale(buf, off, k, True)) == [0.5, 1, 1.5, 8, 1.25, 1.5, 1.75, 2, 2.25, 2.5]

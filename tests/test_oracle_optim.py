@@ -1,0 +1,127 @@
+"""Pins of the oracle's frozen-variance steps (oracle/optim.py).
+
+Hand-evaluated points fix operand order, the sign of the update and where
+eps sits; the LAMB pieces are pinned by the momentum round trip of the
+gradient reconstruction (1-bit LAMB algorithm paragraph), the clip bounds of
+r_t, the basic-1-bit-LAMB special case r_min = r_max = 1, and a fixed point
+where the fresh variance equals the frozen one.
+"""
+
+import numpy as np
+
+from oracle import optim as P
+
+F32 = np.float32
+
+
+def a(*v):
+    return np.array(v, dtype=F32)
+
+
+def test_adam_hand_points():
+    # x=1, m=0.5, v=0.25, eps=0, lr=0.5: 1 - 0.5 * (0.5 / 0.5) = 0.5
+    assert P.adam_frozen_step(a(1.0), a(0.5), a(0.25), 0.5, 0.0)[0] == F32(0.5)
+    # eps outside the root: x=0, m=1, v=0, eps=0.25, lr=1 -> -(1/0.25) = -4
+    assert P.adam_frozen_step(a(0.0), a(1.0), a(0.0), 1.0, 0.25)[0] == F32(-4.0)
+    # sqrt(4) + 0 = 2: x=3, m=-4, lr=0.25 -> 3 + 0.25*2 = 3.5
+    assert P.adam_frozen_step(a(3.0), a(-4.0), a(4.0), 0.25, 0.0)[0] == F32(3.5)
+
+
+def test_adam_special_cases():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(1000).astype(F32)
+    v = np.abs(rng.standard_normal(1000)).astype(F32)
+    m = rng.standard_normal(1000).astype(F32)
+    assert np.array_equal(P.adam_frozen_step(x, np.zeros_like(m), v, 6e-5, 1e-6), x)
+    assert np.array_equal(P.adam_frozen_step(x, m, v, 0.0, 1e-6), x)
+    up = P.adam_frozen_step(x, m, v, 6e-5, 1e-6)
+    assert np.all(np.sign(x - up)[m != 0] == np.sign(m[m != 0]))  # moves against m
+
+
+def test_gradient_reconstruction_round_trip_exact():
+    """beta1 = 1/2 keeps every operation exact: m = b1 m_prev + (1-b1) g
+    reconstructs g bit for bit."""
+    rng = np.random.default_rng(1)
+    g = (rng.integers(-1000, 1000, size=500) / 1024).astype(F32)
+    mp = (rng.integers(-1000, 1000, size=500) / 1024).astype(F32)
+    m = (F32(0.5) * mp + F32(0.5) * g).astype(F32)
+    assert np.array_equal(P.reconstruct_gradient(m, mp, 0.5), g)
+
+
+def test_gradient_reconstruction_round_trip_beta09():
+    """beta1 = 0.9: the momentum recursion evaluated in binary32 is inverted up
+    to its roundings, which the division by 1 - beta1 amplifies tenfold."""
+    rng = np.random.default_rng(2)
+    g = rng.standard_normal(2000).astype(F32)
+    mp = rng.standard_normal(2000).astype(F32)
+    b1 = F32(0.9)
+    m = ((b1 * mp).astype(F32) + ((F32(1) - b1) * g).astype(F32)).astype(F32)
+    rec = P.reconstruct_gradient(m, mp, 0.9).astype(np.float64)
+    u = 2.0 ** -24
+    tol = 10 * 2 * u * (np.abs(m) + np.abs(mp)) + 4 * u * np.abs(g)
+    assert np.all(np.abs(rec - g) <= tol)
+    # a wrong formula (e.g. dividing by beta1) is far outside that band
+    assert np.median(np.abs(rec - g) / np.abs(g)) < 1e-5
+
+
+def test_fresh_variance_hand_point():
+    assert P.fresh_variance(a(4.0), a(2.0), 0.5)[0] == F32(4.0)
+    assert P.fresh_variance(a(0.0), a(3.0), 0.75)[0] == F32(2.25)
+
+
+def test_ratio_clip_bounds():
+    rng = np.random.default_rng(3)
+    R = np.exp(rng.uniform(-3, 3, size=5000)).astype(F32)
+    r_prev = np.exp(rng.uniform(np.log(0.5), np.log(4.0), size=5000)).astype(F32)
+    r, c = P.lamb_ratio_update(R, r_prev, np.ones_like(R), 0.1, 0.5, 4.0)
+    lo = np.maximum(F32(0.5), F32(0.9) * r_prev)
+    hi = np.minimum(F32(4.0), F32(1.1) * r_prev)
+    assert np.all(r >= F32(0.5)) and np.all(r <= F32(4.0))
+    ok = lo <= hi
+    assert np.all((r >= lo)[ok]) and np.all((r <= hi)[ok])
+    inside = ok & (R >= lo) & (R <= hi)
+    assert np.array_equal(r[inside], R[inside])
+    assert np.array_equal(c, r)
+
+
+def test_ratio_no_valid_keeps_previous():
+    r, c = P.lamb_ratio_update(a(np.nan), a(1.7), a(2.0), 0.1, 0.5, 4.0)
+    assert r[0] == F32(1.7) and c[0] == F32(3.4)
+
+
+def test_basic_onebit_lamb_special_case():
+    """r_min = r_max = 1 freezes the coefficient at c_avg."""
+    rng = np.random.default_rng(4)
+    R = np.exp(rng.uniform(-5, 5, size=100)).astype(F32)
+    cav = rng.uniform(0.5, 2, size=100).astype(F32)
+    r, c = P.lamb_ratio_update(R, np.ones(100, dtype=F32), cav, 0.1, 1.0, 1.0)
+    assert np.all(r == 1) and np.array_equal(c, cav)
+
+
+def test_layer_max_semantics():
+    vals = a(1.0, np.nan, 3.0, np.nan, np.nan, -0.0, 0.0, np.inf, 2.0)
+    R = P.layer_max(vals, [0, 3, 5, 7, 9])
+    assert R[0] == 3.0 and np.isnan(R[1]) and R[2] == 0.0 and not np.signbit(R[2]) and R[3] == np.inf
+
+
+def test_lamb_fixed_point_and_step():
+    """g^2 = v_Tw with v = v_Tw and beta2 = 1/2: the fresh variance stays v_Tw,
+    every ratio is 1 and r_t = r_{t-1} = 1; the update uses c_{t-1}."""
+    g = a(2.0, -2.0, 0.5, 0.5)
+    mp = a(0.0, 0.0, 0.0, 0.0)
+    b1 = 0.5
+    m = (F32(1 - b1) * g).astype(F32)
+    v = (g * g).astype(F32)
+    x = a(1.0, 1.0, 1.0, 1.0)
+    out = P.lamb_frozen_step(x, m, mp, v, v, [0, 2, 4], c_avg=a(2.0, 3.0), r_prev=a(1.0, 1.0),
+                             c_prev=a(0.5, 0.25), lr=1.0, eps=0.0, beta1=b1, beta2=0.5,
+                             thr=0.1, r_min=0.5, r_max=4.0)
+    assert np.array_equal(out["v"], v)
+    assert np.array_equal(out["R"], a(1.0, 1.0)) and np.array_equal(out["r"], a(1.0, 1.0))
+    assert np.array_equal(out["c"], a(2.0, 3.0))
+    # x - (lr c_prev) * m / sqrt(v): layer 0 step 0.5 * (1/2 or -1/2) ; layer 1 step 0.25 * 0.5
+    assert np.array_equal(out["x"], a(0.75, 1.25, 0.875, 0.875))
+    out_b = P.lamb_frozen_step(x, m, mp, v, v, [0, 2, 4], c_avg=a(2.0, 3.0), r_prev=a(1.0, 1.0),
+                               c_prev=a(0.5, 0.25), lr=1.0, eps=0.0, beta1=b1, beta2=0.5,
+                               thr=0.1, r_min=0.5, r_max=4.0, use_c_t=True)
+    assert np.array_equal(out_b["x"], a(0.0, 2.0, -0.5, -0.5))
