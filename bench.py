@@ -1,0 +1,268 @@
+"""Benchmark of the error-compensated 1-bit compression stage on one MI355X.
+
+One step = the whole compressed 1-bit Adam hot path over one batch of
+synthetic momenta resident in HBM: worker compress of all n workers (reset,
+compensate, chunk scale, sign pack, error), server reduce (unpack, average,
+compensate, scale, pack, error), decompression of the global momentum, and
+the frozen-variance Adam update.  Default workload: BERT-Large-sized flat
+buffer of 335,141,888 fp32 elements, 8 simulated workers.
+
+Prints ONE JSON line.  `value` = compressed worker elements per second
+(n * N per step).  `roofline` reports the dominant kernel (worker compress)
+against 8 TB/s of HBM using its algorithmic bytes (12.125 B per element:
+read m and the error state, write the state and 1 bit), with the duration
+measured by HIP events on the launch stream.  `cpu_baseline` times the CPU
+oracle on a bounded sample of the same step (one worker chunk compressed,
+one chunk reduced, decompressed and stepped) and scales it to the full step.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --only compress|server|decompress|adam|copy  # profiling aid
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "compressed elements/s and HBM GB/s (% of peak), 1-bit EF compress+decompress"
+
+# algorithmic bytes per element (single pass, what the method must move)
+B_COMPRESS = 12.125            # m 4 + error state 4 in + 4 out + 1/8 bit
+B_DECOMPRESS = 4.125           # 1/8 bit in + 4 out
+B_ADAM = 16.0                  # x 4 in/out, m 4, v 4
+
+
+def b_server(n: int) -> float:  # n/8 bits in, state 4 in + 4 out, 1/8 bit out
+    return 8.125 + n / 8.0
+
+
+COUNTER_FILE = os.path.join(ROOT, "profiles", "compress_bert_large_335M_x8_counters.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "momentum_compression_amd", "csrc", f)
+                  for f in ("compress.hip", "common.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(launch_elems: int):
+    """HBM bytes per compress launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source (else None)."""
+    if not os.path.exists(COUNTER_FILE):
+        return None
+    vals = {}
+    for line in open(COUNTER_FILE):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        fetch = float(vals["FETCH_SIZE_KiB_per_dispatch"])
+        write = float(vals["WRITE_SIZE_KiB_per_dispatch"])
+        factor = float(vals.get("copy_scale_factor", "1.0"))
+        elems = int(vals["elements_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+    if elems != launch_elems:
+        return None
+    return (fetch + write) * 1024.0 * factor
+
+
+def cpu_baseline(wl, seed: int = 11):
+    """Time the CPU oracle on one chunk of each stage and scale to a step."""
+    import numpy as np
+
+    from oracle import onebit as O
+    from oracle import optim as P
+
+    rng = np.random.default_rng(seed)
+    L, n = wl.L, wl.n
+    m = (rng.standard_normal(L) * 1e-3).astype(np.float32)[None, :]
+    t0 = time.perf_counter()
+    w = O.worker_compress(m, np.zeros_like(m), reset=True)
+    t_wc = time.perf_counter() - t0
+    bits_c = np.stack([w["bits"][0]] * n)
+    bits_c[1::2] = ~bits_c[1::2]
+    s_c = np.full(n, w["s"][0, 0], dtype=np.float32)
+    t0 = time.perf_counter()
+    sv = O.server_chunk(bits_c, s_c, np.zeros(L, dtype=np.float32), reset=True)
+    t_sc = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    mbar = O.decompress(sv["bits"], np.array([sv["S"]], dtype=np.float32))
+    x = (rng.standard_normal(L) * 0.02).astype(np.float32)
+    v = np.abs(rng.standard_normal(L) * 1e-6).astype(np.float32) + np.float32(1e-8)
+    t_mid = time.perf_counter()
+    P.adam_frozen_step(x, mbar, v, 6e-5, 1e-6)
+    t_dec_adam = (t_mid - t0) + (time.perf_counter() - t_mid)
+    t_step = n * n * t_wc + n * (t_sc + t_dec_adam)
+    return {
+        "value": n * wl.N / t_step,
+        "unit": "elements/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"one {L}-element worker chunk compressed ({t_wc:.2f} s), one chunk server-reduced "
+                   f"from {n} workers ({t_sc:.2f} s), decompressed and Adam-stepped "
+                   f"({t_dec_adam:.2f} s); scaled to {n}x{n} worker chunks + {n} server chunks"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bert_large_335M_x8")
+    ap.add_argument("--only", default="", choices=["", "compress", "server", "decompress", "adam",
+                                                   "copy"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the n workers are simulated as a batch on one device)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from momentum_compression_amd import onebit as ob
+    from momentum_compression_amd.state import OneBitGroup
+    from workloads import configs as C
+    from workloads import synth as S
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    ob.load()
+    wl = C.get(args.workload)
+    if wl.kind != "adam":
+        print(f"workload {wl.name} is a parity case; the bench times the 1-bit Adam path",
+              file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    N, n = wl.N, wl.n
+    print(f"[bench] workload={wl.name} N={N} n={n} steps={args.steps} warmup={args.warmup}",
+          file=sys.stderr, flush=True)
+    sig = S.per_element(S.segment_sigmas(wl), wl, dev)
+    m = S.momentum(wl, 1, dev, sigma_elem=sig)
+    del sig
+    x = S.params(wl, dev)
+    v = S.frozen_variance(wl, dev)
+    grp = OneBitGroup(N, n, dev, clip=wl.clip, reset_interval=wl.reset_interval)
+    stream = torch.cuda.current_stream()
+
+    if args.only == "copy":
+        # plain copy of n*N floats: the reference for counter scaling
+        src = m.view(-1)
+        dst = grp.ef.view(-1)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "copy", "bytes_per_launch": 2 * 4 * src.numel()}))
+        return 0
+
+    ev = {k: [] for k in ("compress", "server", "decompress", "adam")}
+
+    def step(t: int, timed: bool) -> None:
+        first = t == 1
+        marks = []
+        if timed:
+            marks.append(torch.cuda.Event(enable_timing=True))
+            marks[-1].record(stream)
+        if args.only in ("", "compress"):
+            grp.compress(m, t, first=first)
+        if timed:
+            marks.append(torch.cuda.Event(enable_timing=True))
+            marks[-1].record(stream)
+        if args.only in ("", "server"):
+            grp.server(t, first=first, decompress=False)
+        if timed:
+            marks.append(torch.cuda.Event(enable_timing=True))
+            marks[-1].record(stream)
+        if args.only in ("", "decompress"):
+            ob.onebit_decompress(grp.sv_bits, grp.sv_scales, grp.mbar, N, n)
+        if timed:
+            marks.append(torch.cuda.Event(enable_timing=True))
+            marks[-1].record(stream)
+        if args.only in ("", "adam"):
+            grp.adam_step(x, v, wl.lr, wl.eps)
+        if timed:
+            marks.append(torch.cuda.Event(enable_timing=True))
+            marks[-1].record(stream)
+            for k, (a, b) in zip(ev, zip(marks[:-1], marks[1:])):
+                ev[k].append((a, b))
+
+    t = 1
+    for _ in range(args.warmup):
+        step(t, False)
+        t += 1
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(t, True)
+        t += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms = {k: sum(a.elapsed_time(b) for a, b in v_) / max(1, len(v_)) for k, v_ in ev.items()}
+    ms_per_step = wall * 1e3 / args.steps
+    bytes_ = {"compress": B_COMPRESS * n * N, "server": b_server(n) * N,
+              "decompress": B_DECOMPRESS * N, "adam": B_ADAM * N}
+    kernels = {}
+    for k in ms:
+        if args.only and args.only != k:
+            continue
+        gbs = bytes_[k] / (ms[k] * 1e-3) / 1e9 if ms[k] > 0 else 0.0
+        kernels[k] = {"ms": round(ms[k], 4), "algorithmic_GBps": round(gbs, 1),
+                      "frac_of_8TBps": round(gbs / PEAK_HBM_GBS, 4)}
+    if args.only:
+        print(json.dumps({"only": args.only, "kernels": kernels}))
+        return 0
+
+    comp_gbs = bytes_["compress"] / (ms["compress"] * 1e-3) / 1e9
+    traffic = read_traffic(n * N)
+    out = {
+        "metric": METRIC,
+        "value": n * N / (ms_per_step * 1e-3),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "N": N, "workers": n, "chunk": wl.L,
+                   "path": "compress+server+decompress+adam_frozen_v",
+                   "inputs": "momentum N(0, sigma), sigma log-uniform [1e-5, 1e-2] per 2^20 block"},
+        "roofline": {"bound": "hbm", "kernel": "onebit_compress", "achieved": round(comp_gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(comp_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic, 0),
+                     "bytes_per_elem": B_COMPRESS, "elems_per_launch": n * N,
+                     "launch_ms": round(ms["compress"], 4)},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

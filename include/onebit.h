@@ -1,0 +1,235 @@
+/*
+ * onebit.h -- C ABI of libonebit.so, the error-compensated 1-bit (and INT8)
+ * compression stage of 1-bit Adam / 1-bit LAMB on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument is a DEVICE pointer owned by the caller, except
+ *   the argument struct of frozen_v_step (host memory, read during the call).
+ *   The library never allocates, frees or synchronises; it validates
+ *   arguments on the host (before any HIP call) and enqueues kernels on
+ *   `stream` only.  Results are ready when the stream reaches them.
+ * - Return value: ONEBIT_OK (0) or a negative onebit_status.  Validation
+ *   failures leave every buffer untouched.  ONEBIT_E_HIP reports a launch
+ *   error from the HIP runtime.
+ * - Floating point is IEEE binary32 throughout: round to nearest even, no
+ *   fused multiply-add contraction, correctly rounded division and square
+ *   root, subnormals kept.  NaN and Inf in the data are not errors; they
+ *   propagate by IEEE rules.
+ * - n simulated workers each hold a flat buffer of N elements ("row").  A row
+ *   is split into n chunks of L = N / n consecutive elements; chunk c of
+ *   every worker is reduced by server c.  N must be a multiple of 64 * n (the
+ *   caller zero-pads).  1 <= n <= 64.  N == 0 is a no-op.
+ * - Sign convention: bit = 1 when x >= 0 (both zeros encode +1), 0 when
+ *   x < 0 or NaN.  Packed words: element j of a row is bit (j & 31) of
+ *   uint32 word (j >> 5) of that row (least significant bit first).
+ * - Chunk scales are the exact mean of |x| over the chunk, rounded once to
+ *   binary32 (ties to even): independent of launch geometry and bit-exact.
+ * - Alignment: float buffers that are streamed (m, ef, e_out, m_out, x, v,
+ *   g, err, deq, buf) must be 16-byte aligned; all others 4-byte (8 for
+ *   int64 tables).
+ *
+ * Error-feedback state ("lazy" error)
+ * -----------------------------------
+ * The error of error compensation (1-bit Adam article, section 2.1:
+ * e_t = g'_t - q_t) is not stored as e.  The state is the pair
+ * (ef, scales): ef holds the last compensated value g' and scales its chunk
+ * scale s, and e = g' - s (g' >= 0) or g' + s (g' < 0), the same single
+ * binary32 operation evaluated when the next call needs it.  This halves the
+ * memory passes of a step.  A zero-filled state means e = 0.
+ * onebit_error_materialize() writes e out explicitly.
+ */
+#ifndef ONEBIT_H
+#define ONEBIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ONEBIT_OK = 0,
+    ONEBIT_E_NULL = -1,      /* a required pointer is NULL               */
+    ONEBIT_E_SIZE = -2,      /* N, n, block or a size relation invalid   */
+    ONEBIT_E_ALIGN = -3,     /* pointer misaligned                       */
+    ONEBIT_E_WORKSPACE = -4, /* workspace NULL or smaller than required  */
+    ONEBIT_E_ARG = -5,       /* other invalid argument (mode, segments)  */
+    ONEBIT_E_HIP = -6        /* HIP runtime reported an error on launch  */
+} onebit_status;
+
+/*
+ * Worker side: reset, compensate, clamp, layer scale, chunk scale, sign pack.
+ *
+ * Source: 1-bit Adam article, section 2.1 (g' = g + e_prev; q = sign(g');
+ * e = g' - q), applied to the momentum as in 1-bit LAMB (layer-scaling
+ * paragraph); scaled sign mean(|g'|) * sign(g') from the gradient-quantisation
+ * tutorial ("1-bit gradient quantisation"), per chunk; periodic reset and
+ * clamp of the compensated value from the article's section 4.1 code example.
+ *
+ * For every worker i and element j:
+ *   e      = reset ? 0 : (ef >= 0 ? ef - s_prev[i][c] : ef + s_prev[i][c])
+ *   g'     = (seg ? k_l * m : m) + e
+ *   g'     = clip_on ? fminf(fmaxf(g', -clip), clip) : g'
+ *   ef     = g'                                   (new state)
+ *   bit    = g' >= 0                              -> bits
+ *   s[i][c]= mean over chunk c of |g'|            -> scales (exact, rounded)
+ *
+ * m       [n][N] float   momentum of each worker (read)
+ * ef      [n][N] float   error state, in/out
+ * scales  [n][n] float   in: previous scales (the error state's second half);
+ *                        out: this call's scales, s[i][c] at i * n + c
+ * bits    [n][N/32] u32  out: packed signs of g'
+ * clip    clamp bound; clip <= 0 or +inf disables the clamp
+ * reset   nonzero: treat the carried error as zero (first compressed step,
+ *         periodic reset)
+ * seg_off [n_seg+1] int64, seg_k [n_seg] float: optional (both NULL and
+ *         n_seg == 0 to disable) per-layer coefficients over the N elements
+ *         of a row; seg_off ascending, seg_off[0] = 0, seg_off[n_seg] = N
+ *         (1-bit LAMB page, layer-scaling paragraph: x k before compression)
+ * ws, ws_bytes  device workspace of at least onebit_workspace_bytes(N, n,
+ *         n_seg) bytes; contents need no initialisation and are scratch
+ */
+int onebit_compress(const float* m, float* ef, float* scales, uint32_t* bits,
+                    int64_t N, int32_t n, float clip, int32_t reset,
+                    const int64_t* seg_off, const float* seg_k, int32_t n_seg,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Server side: unpack and average n workers, compensate, chunk scale, pack;
+ * optionally decompress the global momentum.
+ *
+ * Source: 1-bit LAMB page, experiments paragraph (compressed all-to-all /
+ * all-gather backend: server c receives chunk c of every worker, averages,
+ * error-compensates and re-compresses; every worker decompresses all server
+ * chunks) and layer-scaling paragraph (divide by k_l after communication).
+ *
+ * For every chunk c and element j of it:
+ *   acc = +0; for i = 0..n-1: acc = acc + (bit_i ? s[i][c] : -s[i][c])
+ *   avg = acc / n
+ *   E   = reset ? 0 : (ef >= 0 ? ef - S_prev[c] : ef + S_prev[c])
+ *   g'' = avg + E;   ef = g'';   B = g'' >= 0;   S[c] = mean |g''| (exact)
+ *   m_out = (B ? S[c] : -S[c]) [/ k_l]      (only when m_out != NULL)
+ *
+ * bits    [n][N/32] u32, scales [n][n] float: the worker outputs
+ * ef      [N] float  server error state, in/out
+ * sv_scales [n] float  in: previous server scales; out: S
+ * sv_bits [N/32] u32   out
+ * m_out   [N] float or NULL: decompressed global momentum
+ * seg_off, seg_k, n_seg  as onebit_compress (applied as / k_l to m_out)
+ */
+int onebit_server_reduce(const uint32_t* bits, const float* scales, float* ef,
+                         float* sv_scales, uint32_t* sv_bits, float* m_out,
+                         const int64_t* seg_off, const float* seg_k, int32_t n_seg,
+                         int64_t N, int32_t n, int32_t reset,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Decompress only: m_out = (B ? S[c] : -S[c]) [/ k_l] from server words and
+ * scales (what every worker computes after the all-gather phase).
+ */
+int onebit_decompress(const uint32_t* sv_bits, const float* sv_scales, float* m_out,
+                      const int64_t* seg_off, const float* seg_k, int32_t n_seg,
+                      int64_t N, int32_t n, hipStream_t stream);
+
+/*
+ * Write out the error e of an error-feedback state:
+ *   e[r][j] = ef[r][j] >= 0 ? ef[r][j] - scales[r*n + c] : ef[r][j] + scales[r*n + c]
+ * with c = j / (N / n).  rows = n for the worker state, 1 for the server.
+ */
+int onebit_error_materialize(const float* ef, const float* scales, float* e_out,
+                             int64_t N, int32_t rows, int32_t n, hipStream_t stream);
+
+/*
+ * Segment-wise layer scaling of a [batch][N] buffer, in place:
+ * buf = divide ? buf / k_l : buf * k_l.
+ * Source: 1-bit LAMB page, layer-scaling paragraph.
+ */
+int lamb_layer_scale(float* buf, int64_t N, int32_t batch,
+                     const int64_t* seg_off, const float* seg_k, int32_t n_seg,
+                     int32_t divide, hipStream_t stream);
+
+/*
+ * Frozen-variance parameter step.
+ *
+ * mode 0, Adam (1-bit Adam article, sections 2.1 and 6; 1-bit LAMB page,
+ * algorithm paragraph for the frozen denominator):
+ *   x = x - lr * (m / (sqrtf(v) + eps))
+ *
+ * mode 1, LAMB (1-bit LAMB page, algorithm and analysis paragraphs):
+ *   g   = (m - beta1 * m_prev) / (1 - beta1)
+ *   v_f = beta2 * v_f + (1 - beta2) * (g * g)
+ *   R_l = max over layer l of v / v_f   (NaN skipped, +inf kept, +0 > -0)
+ *   r_l = fminf(fmaxf(R_l, (1-thr) r_prev_l), (1+thr) r_prev_l), then the
+ *         same clip to [r_min, r_max]; a layer without a valid ratio keeps
+ *         r_prev_l
+ *   c_l = c_avg_l * r_l
+ *   x   = x - (lr * c_used_l) * (m / (sqrtf(v) + eps))
+ *   where c_used = c_prev (coefficient of the previous step; default) or the
+ *   new c (use_c_t != 0, which costs a second pass).  On return r_prev and
+ *   c_prev hold r_t and c_t; ratio_max (optional) holds R (NaN: none).
+ *   First compressed step: r_prev = 1, c_prev = c_avg, v_f = v.
+ */
+typedef struct onebit_frozen_v_args {
+    int32_t mode;          /* 0: Adam, 1: LAMB                                */
+    int32_t use_c_t;       /* LAMB: 0 = update with c_{t-1}, 1 = with c_t     */
+    int64_t N;
+    float lr, eps, beta1, beta2;
+    float r_threshold, r_min, r_max;
+    int32_t n_seg;         /* LAMB: number of layers                          */
+    float* x;              /* [N] parameters, in/out                          */
+    const float* m;        /* [N] global (decompressed) momentum m_t          */
+    const float* v;        /* [N] frozen variance (v_Tw)                      */
+    const float* m_prev;   /* LAMB: [N] m_{t-1}                               */
+    float* v_fresh;        /* LAMB: [N] fresh variance, in/out                */
+    const int64_t* seg_off;/* LAMB: [n_seg+1]                                 */
+    const float* c_avg;    /* LAMB: [n_seg]                                   */
+    float* r_prev;         /* LAMB: [n_seg] in r_{t-1}, out r_t               */
+    float* c_prev;         /* LAMB: [n_seg] in c_{t-1}, out c_t               */
+    float* ratio_max;      /* LAMB: [n_seg] out, or NULL                      */
+} onebit_frozen_v_args;
+
+int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes,
+                  hipStream_t stream);
+
+/*
+ * Block-wise INT8 stochastic rounding with optional error feedback.
+ *
+ * Source: gradient-quantisation tutorial, "FP32 -> INT8" (scale = max/127,
+ * block-wise scales, stochastic rounding floor + Bernoulli(fraction), codes
+ * clamped to [-127, 127], dequantise q * scale) and error feedback.
+ *
+ * For block b of `block` consecutive elements and element J:
+ *   g'  = err ? g + err : g
+ *   M   = max(0, max over the block of non-NaN |g'|);  scale = M / 127
+ *   scale == 0: q = 0, deq = 0
+ *   else x = g' / scale, f = floorf(x), p = x - f,
+ *        q = fminf(fmaxf(f + (u_J < p), -127), 127),  deq = q * scale
+ *   err = g' - deq                          (when err != NULL)
+ *   u_J = (word J&3 of Philox4x32-10(counter = (J>>2 lo32, J>>2 hi32, step, 0),
+ *          key = (seed lo32, seed hi32)) >> 8) * 2^-24
+ *
+ * g [N] float (read); err [N] float in/out or NULL; codes [N] int8 out;
+ * block_scales [N/block] float out; deq [N] float out or NULL.
+ * block in {64, 128, 256, 512, 1024}; N a multiple of block.
+ */
+int int8_sr_quantize(const float* g, float* err, int8_t* codes, float* block_scales,
+                     float* deq, int64_t N, int32_t block, uint64_t seed, uint32_t step,
+                     hipStream_t stream);
+
+/* Workspace bytes needed by onebit_compress / onebit_server_reduce /
+ * frozen_v_step for these sizes (0 if the sizes are invalid). */
+size_t onebit_workspace_bytes(int64_t N, int32_t n, int32_t n_seg);
+
+/* Static description of a status code. */
+const char* onebit_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ONEBIT_H */

@@ -1,0 +1,198 @@
+// C ABI of libonebit: host-side validation, workspace carving, launches.
+// Every check runs before the first HIP call, so invalid calls touch nothing.
+#include <math.h>
+
+#include "common.h"
+
+using namespace onebit;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int32_t kMaxWorkers = 64;
+
+int check_rows(int64_t N, int32_t n) {
+    if (n < 1 || n > kMaxWorkers) return ONEBIT_E_SIZE;
+    if (N < 0) return ONEBIT_E_SIZE;
+    if (N % (64 * (int64_t)n)) return ONEBIT_E_SIZE;
+    if (N / n >= (int64_t)1 << 32) return ONEBIT_E_SIZE;  // chunk length must fit 32 bits
+    return ONEBIT_OK;
+}
+
+// Segment tables live in device memory; the host can check only what it sees.
+int check_segments(const int64_t* seg_off, const float* seg_k, int32_t n_seg, bool need_k) {
+    if (seg_off == nullptr && seg_k == nullptr && n_seg == 0) return ONEBIT_OK;
+    if (seg_off == nullptr || (need_k && seg_k == nullptr)) return ONEBIT_E_NULL;
+    if (n_seg < 1) return ONEBIT_E_ARG;
+    if (!aligned(seg_off, 8) || (seg_k && !aligned(seg_k, 4))) return ONEBIT_E_ALIGN;
+    return ONEBIT_OK;
+}
+
+size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t partial_bytes(int64_t N, int32_t n) {
+    const int64_t L = N / n;
+    const ChunkPlan pw = make_plan(L, (int64_t)n * n);
+    const ChunkPlan ps = make_plan(L, n);
+    const int64_t w = pw.bpc * n * n;
+    const int64_t s = ps.bpc * n;
+    return round_up((size_t)(w > s ? w : s) * sizeof(double));
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ONEBIT_OK : ONEBIT_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* onebit_strerror(int status) {
+    switch (status) {
+        case ONEBIT_OK: return "ok";
+        case ONEBIT_E_NULL: return "required pointer is NULL";
+        case ONEBIT_E_SIZE: return "invalid size (N must be a multiple of 64*n, 1 <= n <= 64, N/n < 2^32; block and N must agree)";
+        case ONEBIT_E_ALIGN: return "pointer misaligned (streamed float buffers need 16 bytes)";
+        case ONEBIT_E_WORKSPACE: return "workspace missing or smaller than onebit_workspace_bytes()";
+        case ONEBIT_E_ARG: return "invalid argument";
+        case ONEBIT_E_HIP: return "HIP runtime error on launch";
+        default: return "unknown status";
+    }
+}
+
+size_t onebit_workspace_bytes(int64_t N, int32_t n, int32_t n_seg) {
+    if (check_rows(N, n) != ONEBIT_OK || n_seg < 0) return 0;
+    if (N == 0) return 256;
+    return partial_bytes(N, n) + round_up((size_t)(n_seg > 0 ? n_seg : 1) * sizeof(uint32_t));
+}
+
+int onebit_compress(const float* m, float* ef, float* scales, uint32_t* bits, int64_t N, int32_t n,
+                    float clip, int32_t reset, const int64_t* seg_off, const float* seg_k,
+                    int32_t n_seg, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int st = check_rows(N, n);
+    if (st) return st;
+    if (!m || !ef || !scales || !bits) return ONEBIT_E_NULL;
+    if ((st = check_segments(seg_off, seg_k, n_seg, true))) return st;
+    if (!aligned(m, 16) || !aligned(ef, 16) || !aligned(scales, 4) || !aligned(bits, 4))
+        return ONEBIT_E_ALIGN;
+    if (clip != clip) return ONEBIT_E_ARG;
+    if (N == 0) return ONEBIT_OK;
+    const size_t need = onebit_workspace_bytes(N, n, n_seg);
+    if (!ws || ws_bytes < need) return ONEBIT_E_WORKSPACE;
+    if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
+
+    const int64_t L = N / n;
+    const ChunkPlan plan = make_plan(L, (int64_t)n * n);
+    if (sum_depth(plan) > 2048) return ONEBIT_E_SIZE;
+    const bool clamp_on = clip > 0.0f && !isinf(clip);
+    double* partials = static_cast<double*>(ws);
+    hipError_t e = launch_compress(m, ef, scales, bits, partials, N, n, plan, clip, clamp_on,
+                                   reset != 0, seg_off, seg_k, n_seg, stream);
+    if (e != hipSuccess) return ONEBIT_E_HIP;
+    MeanTarget tgt{ef, N, n, scales};
+    return hip_status(launch_mean_finalize(partials, plan, (int64_t)n * n, tgt, stream));
+}
+
+int onebit_server_reduce(const uint32_t* bits, const float* scales, float* ef, float* sv_scales,
+                         uint32_t* sv_bits, float* m_out, const int64_t* seg_off,
+                         const float* seg_k, int32_t n_seg, int64_t N, int32_t n, int32_t reset,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
+    int st = check_rows(N, n);
+    if (st) return st;
+    if (!bits || !scales || !ef || !sv_scales || !sv_bits) return ONEBIT_E_NULL;
+    if ((st = check_segments(seg_off, seg_k, n_seg, true))) return st;
+    if (!aligned(bits, 4) || !aligned(scales, 4) || !aligned(ef, 16) || !aligned(sv_scales, 4) ||
+        !aligned(sv_bits, 4) || (m_out && !aligned(m_out, 16)))
+        return ONEBIT_E_ALIGN;
+    if (N == 0) return ONEBIT_OK;
+    const size_t need = onebit_workspace_bytes(N, n, n_seg);
+    if (!ws || ws_bytes < need) return ONEBIT_E_WORKSPACE;
+    if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
+
+    const int64_t L = N / n;
+    const ChunkPlan plan = make_plan(L, n);
+    if (sum_depth(plan) > 2048) return ONEBIT_E_SIZE;
+    double* partials = static_cast<double*>(ws);
+    hipError_t e = launch_server(bits, scales, ef, sv_scales, sv_bits, partials, N, n, plan,
+                                 reset != 0, stream);
+    if (e != hipSuccess) return ONEBIT_E_HIP;
+    MeanTarget tgt{ef, N, n, sv_scales};
+    e = launch_mean_finalize(partials, plan, n, tgt, stream);
+    if (e != hipSuccess) return ONEBIT_E_HIP;
+    if (m_out)
+        return hip_status(
+            launch_decompress(sv_bits, sv_scales, m_out, seg_off, seg_k, n_seg, N, n, stream));
+    return ONEBIT_OK;
+}
+
+int onebit_decompress(const uint32_t* sv_bits, const float* sv_scales, float* m_out,
+                      const int64_t* seg_off, const float* seg_k, int32_t n_seg, int64_t N,
+                      int32_t n, hipStream_t stream) {
+    int st = check_rows(N, n);
+    if (st) return st;
+    if (!sv_bits || !sv_scales || !m_out) return ONEBIT_E_NULL;
+    if ((st = check_segments(seg_off, seg_k, n_seg, true))) return st;
+    if (!aligned(sv_bits, 4) || !aligned(sv_scales, 4) || !aligned(m_out, 16)) return ONEBIT_E_ALIGN;
+    if (N == 0) return ONEBIT_OK;
+    return hip_status(
+        launch_decompress(sv_bits, sv_scales, m_out, seg_off, seg_k, n_seg, N, n, stream));
+}
+
+int onebit_error_materialize(const float* ef, const float* scales, float* e_out, int64_t N,
+                             int32_t rows, int32_t n, hipStream_t stream) {
+    int st = check_rows(N, n);
+    if (st) return st;
+    if (rows < 1 || rows > kMaxWorkers) return ONEBIT_E_SIZE;
+    if (!ef || !scales || !e_out) return ONEBIT_E_NULL;
+    if (!aligned(ef, 16) || !aligned(e_out, 16) || !aligned(scales, 4)) return ONEBIT_E_ALIGN;
+    if (N == 0) return ONEBIT_OK;
+    return hip_status(launch_materialize(ef, scales, e_out, N, rows, n, stream));
+}
+
+int lamb_layer_scale(float* buf, int64_t N, int32_t batch, const int64_t* seg_off,
+                     const float* seg_k, int32_t n_seg, int32_t divide, hipStream_t stream) {
+    if (N < 0 || (N % 4) || batch < 1) return ONEBIT_E_SIZE;
+    if (!buf || !seg_off || !seg_k) return ONEBIT_E_NULL;
+    if (n_seg < 1) return ONEBIT_E_ARG;
+    if (!aligned(buf, 16) || !aligned(seg_off, 8) || !aligned(seg_k, 4)) return ONEBIT_E_ALIGN;
+    if (N == 0) return ONEBIT_OK;
+    return hip_status(launch_layer_scale(buf, N, batch, seg_off, seg_k, n_seg, divide != 0, stream));
+}
+
+int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!a) return ONEBIT_E_NULL;
+    if (a->N < 0 || (a->N % 4)) return ONEBIT_E_SIZE;
+    if (!a->x || !a->m || !a->v) return ONEBIT_E_NULL;
+    if (!aligned(a->x, 16) || !aligned(a->m, 16) || !aligned(a->v, 16)) return ONEBIT_E_ALIGN;
+    if (a->mode == 0) {
+        if (a->N == 0) return ONEBIT_OK;
+        return hip_status(launch_adam(a->x, a->m, a->v, a->N, a->lr, a->eps, stream));
+    }
+    if (a->mode != 1) return ONEBIT_E_ARG;
+    if (!a->m_prev || !a->v_fresh || !a->seg_off || !a->c_avg || !a->r_prev || !a->c_prev)
+        return ONEBIT_E_NULL;
+    if (a->n_seg < 1) return ONEBIT_E_ARG;
+    if (!aligned(a->m_prev, 16) || !aligned(a->v_fresh, 16) || !aligned(a->seg_off, 8) ||
+        !aligned(a->c_avg, 4) || !aligned(a->r_prev, 4) || !aligned(a->c_prev, 4) ||
+        (a->ratio_max && !aligned(a->ratio_max, 4)))
+        return ONEBIT_E_ALIGN;
+    if (a->N == 0) return ONEBIT_OK;
+    const size_t need = round_up((size_t)a->n_seg * sizeof(uint32_t));
+    if (!ws || ws_bytes < need) return ONEBIT_E_WORKSPACE;
+    if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
+    return hip_status(launch_lamb(*a, static_cast<uint32_t*>(ws), stream));
+}
+
+int int8_sr_quantize(const float* g, float* err, int8_t* codes, float* block_scales, float* deq,
+                     int64_t N, int32_t block, uint64_t seed, uint32_t step, hipStream_t stream) {
+    if (block != 64 && block != 128 && block != 256 && block != 512 && block != 1024)
+        return ONEBIT_E_SIZE;
+    if (N < 0 || (N % block)) return ONEBIT_E_SIZE;
+    if (!g || !codes || !block_scales) return ONEBIT_E_NULL;
+    if (!aligned(g, 16) || (err && !aligned(err, 16)) || !aligned(codes, 4) ||
+        !aligned(block_scales, 4) || (deq && !aligned(deq, 16)))
+        return ONEBIT_E_ALIGN;
+    if (N == 0) return ONEBIT_OK;
+    return hip_status(launch_int8(g, err, codes, block_scales, deq, N, block, seed, step, stream));
+}
+
+}  // extern "C"

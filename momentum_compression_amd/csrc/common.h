@@ -1,0 +1,137 @@
+// Internal helpers shared by the gfx950 kernels of libonebit (device side)
+// and the launch code (host side).  Wave64 throughout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "onebit.h"
+
+namespace onebit {
+
+using f4 = float __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;           // threads per workgroup (4 waves)
+constexpr int kTile = kThreads * 4;     // elements per workgroup iteration (float4 / lane)
+constexpr int kMaxIters = 16;           // iterations per workgroup in streaming kernels
+
+// ---------------------------------------------------------------- launch plan
+// One plan for the chunked kernels (worker compress, server reduce): the
+// workgroups of one chunk cover consecutive tiles, `iters` tiles each.
+struct ChunkPlan {
+    int64_t L;        // chunk length (elements)
+    int32_t iters;    // tiles per workgroup
+    int64_t bpc;      // workgroups per chunk
+};
+
+ChunkPlan make_plan(int64_t L, int64_t chunks);
+
+// Upper bound on the number of floating-point additions any one term passes
+// through in the fp64 chunk sum (per-thread sequence, wave butterfly, LDS
+// tree, finalize sequence, finalize tree, division).
+int64_t sum_depth(const ChunkPlan& p);
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// OR of a value over each aligned group of 8 lanes, broadcast to all 8 lanes
+// (quad swaps, then half-row mirror).  Pure register crosslane moves (DPP).
+__device__ __forceinline__ uint32_t or8(uint32_t v) {
+    v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+    v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+    v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true); // row_half_mirror
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Sum over a workgroup of kThreads threads; result valid in thread 0.
+__device__ __forceinline__ double block_sum(double v, double* lds /* [kThreads/64] */) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    if (lane_id() == 0) lds[w] = v;
+    __syncthreads();
+    double r = 0.0;
+    if (threadIdx.x == 0) {
+        r = (lds[0] + lds[1]) + (lds[2] + lds[3]);
+    }
+    return r;
+}
+
+// Nibble of 4 sign bits (bit k = (x_k >= 0)).
+__device__ __forceinline__ uint32_t sign_nibble(float a, float b, float c, float d) {
+    return (a >= 0.0f ? 1u : 0u) | (b >= 0.0f ? 2u : 0u) | (c >= 0.0f ? 4u : 0u) |
+           (d >= 0.0f ? 8u : 0u);
+}
+
+// e = g' - s for g' >= 0, g' + s otherwise (NaN takes the second branch).
+__device__ __forceinline__ float ef_error(float gp, float s) {
+    return gp >= 0.0f ? gp - s : gp + s;
+}
+
+// Index of the segment that contains element J: largest l with off[l] <= J.
+__device__ __forceinline__ int find_segment(const int64_t* off, int n_seg, int64_t J) {
+    int lo = 0, hi = n_seg - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= J) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Order-preserving map of a non-NaN float to uint32 (0 is below every key).
+__device__ __forceinline__ uint32_t float_key(float x) {
+    uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+}  // namespace onebit
+
+// ---------------------------------------------------------------- launchers
+// Host-side entry points into each kernel file (validation happens in api.hip).
+namespace onebit {
+
+struct MeanTarget {
+    const float* data;   // base of the stored values (ef)
+    int64_t row_stride;  // elements between rows
+    int32_t chunks;      // chunks per row (n)
+    float* out;          // [rows * chunks] scales
+};
+
+hipError_t launch_mean_finalize(const double* partials, const ChunkPlan& plan, int64_t pairs,
+                                MeanTarget tgt, hipStream_t st);
+
+hipError_t launch_compress(const float* m, float* ef, const float* s_prev, uint32_t* bits,
+                           double* partials, int64_t N, int32_t n, const ChunkPlan& plan,
+                           float clip, bool clamp_on, bool reset, const int64_t* seg_off,
+                           const float* seg_k, int32_t n_seg, hipStream_t st);
+
+hipError_t launch_server(const uint32_t* bits, const float* scales, float* ef, const float* S_prev,
+                         uint32_t* sv_bits, double* partials, int64_t N, int32_t n,
+                         const ChunkPlan& plan, bool reset, hipStream_t st);
+
+hipError_t launch_decompress(const uint32_t* sv_bits, const float* S, float* m_out,
+                             const int64_t* seg_off, const float* seg_k, int32_t n_seg,
+                             int64_t N, int32_t n, hipStream_t st);
+
+hipError_t launch_materialize(const float* ef, const float* scales, float* e_out, int64_t N,
+                              int32_t rows, int32_t n, hipStream_t st);
+
+hipError_t launch_layer_scale(float* buf, int64_t N, int32_t batch, const int64_t* seg_off,
+                              const float* seg_k, int32_t n_seg, bool divide, hipStream_t st);
+
+hipError_t launch_adam(float* x, const float* m, const float* v, int64_t N, float lr, float eps,
+                       hipStream_t st);
+
+hipError_t launch_lamb(const onebit_frozen_v_args& a, uint32_t* keys, hipStream_t st);
+
+hipError_t launch_int8(const float* g, float* err, int8_t* codes, float* scales, float* deq,
+                       int64_t N, int32_t block, uint64_t seed, uint32_t step, hipStream_t st);
+
+}  // namespace onebit

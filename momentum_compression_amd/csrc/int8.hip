@@ -1,0 +1,179 @@
+// Block-wise INT8 stochastic rounding with error feedback
+// (gradient-quantisation tutorial, "FP32 -> INT8": max/127 scale per block,
+// floor plus a Bernoulli(fraction) draw, clamp to [-127, 127], dequantise;
+// error feedback from its 1-bit section).
+//
+// Each lane owns 4 consecutive elements (one float4, one Philox4x32-10 call
+// whose 4 output words are the 4 uniforms, one 32-bit store of 4 codes).  A
+// quantisation block of B elements spans B/4 lanes; its max |g'| is a
+// butterfly over those lanes (B <= 256) or, for B = 512 / 1024, combined
+// across waves through LDS.
+//
+// Philox4x32-10 is the SC'11 construction: per round two 32x32->64
+// multiplies of counter words 0 and 2, xor of the high halves with the other
+// words and the round key; key bumped by the two Weyl constants.
+#include "common.h"
+
+namespace onebit {
+
+namespace {
+
+__device__ __forceinline__ void philox_round(uint32_t& c0, uint32_t& c1, uint32_t& c2,
+                                             uint32_t& c3, uint32_t k0, uint32_t k1) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n1 = (uint32_t)p1;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n3 = (uint32_t)p0;
+    c0 = n0;
+    c1 = n1;
+    c2 = n2;
+    c3 = n3;
+}
+
+__device__ __forceinline__ void philox10(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3,
+                                         uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        philox_round(c0, c1, c2, c3, k0, k1);
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+}
+
+template <int B>
+__device__ __forceinline__ float group_max(float v, float* lds) {
+    constexpr int lanes = B / 4;  // lanes per quantisation block
+    constexpr int wl = lanes < 64 ? lanes : 64;
+#pragma unroll
+    for (int off = 1; off < wl; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    if constexpr (lanes > 64) {
+        constexpr int waves = lanes / 64;  // waves per block (2 or 4)
+        const int w = threadIdx.x >> 6;
+        if (lane_id() == 0) lds[w] = v;
+        __syncthreads();
+        const int g0 = (w / waves) * waves;
+        float r = lds[g0];
+#pragma unroll
+        for (int q = 1; q < waves; ++q) r = fmaxf(r, lds[g0 + q]);
+        __syncthreads();
+        v = r;
+    }
+    return v;
+}
+
+}  // namespace
+
+template <int B, bool EF, bool DEQ>
+__global__ __launch_bounds__(kThreads) void int8_kernel(const float* __restrict__ g,
+                                                       float* __restrict__ err,
+                                                       int8_t* __restrict__ codes,
+                                                       float* __restrict__ scales,
+                                                       float* __restrict__ deq, int64_t N,
+                                                       int32_t iters, uint32_t k0, uint32_t k1,
+                                                       uint32_t step) {
+    __shared__ float lds[kThreads / 64];
+    constexpr int lanes = B / 4;
+    const int64_t base = (int64_t)blockIdx.x * iters * kTile;
+    for (int it = 0; it < iters; ++it) {
+        const int64_t J = base + (int64_t)it * kTile + 4 * (int64_t)threadIdx.x;
+        if (base + (int64_t)it * kTile >= N) break;  // workgroup-uniform
+        const bool active = J < N;
+        f4 gv = {0.f, 0.f, 0.f, 0.f};
+        f4 ev = {0.f, 0.f, 0.f, 0.f};
+        if (active) {
+            gv = __builtin_nontemporal_load(reinterpret_cast<const f4*>(g + J));
+            if (EF) ev = *reinterpret_cast<const f4*>(err + J);
+        }
+        float x[4] = {gv.x, gv.y, gv.z, gv.w};
+        if (EF) {
+            x[0] = x[0] + ev.x;
+            x[1] = x[1] + ev.y;
+            x[2] = x[2] + ev.z;
+            x[3] = x[3] + ev.w;
+        }
+        float M = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) M = fmaxf(M, fabsf(x[k]));
+        M = group_max<B>(M, lds);
+        const float scale = M / 127.0f;
+
+        uint32_t c0 = (uint32_t)((uint64_t)J >> 2), c1 = (uint32_t)((uint64_t)J >> 34), c2 = step,
+                 c3 = 0;
+        philox10(c0, c1, c2, c3, k0, k1);
+        const uint32_t w[4] = {c0, c1, c2, c3};
+
+        float q[4], d[4], e[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (scale == 0.0f) {
+                q[k] = 0.0f;
+                d[k] = 0.0f;
+            } else {
+                const float xs = x[k] / scale;
+                const float f = floorf(xs);
+                const float p = xs - f;
+                const float u = (float)(w[k] >> 8) * 0x1p-24f;
+                float qq = f + (u < p ? 1.0f : 0.0f);
+                qq = fminf(fmaxf(qq, -127.0f), 127.0f);
+                q[k] = qq;
+                d[k] = qq * scale;
+            }
+            e[k] = x[k] - d[k];
+        }
+        if (active) {
+            const uint32_t packed = ((uint32_t)(uint8_t)(int8_t)(int)q[0]) |
+                                    ((uint32_t)(uint8_t)(int8_t)(int)q[1] << 8) |
+                                    ((uint32_t)(uint8_t)(int8_t)(int)q[2] << 16) |
+                                    ((uint32_t)(uint8_t)(int8_t)(int)q[3] << 24);
+            *reinterpret_cast<uint32_t*>(codes + J) = packed;
+            if (EF) {
+                const f4 eo = {e[0], e[1], e[2], e[3]};
+                *reinterpret_cast<f4*>(err + J) = eo;
+            }
+            if (DEQ) {
+                const f4 dq = {d[0], d[1], d[2], d[3]};
+                __builtin_nontemporal_store(dq, reinterpret_cast<f4*>(deq + J));
+            }
+            if ((threadIdx.x % lanes) == 0) scales[J / B] = scale;
+        }
+    }
+}
+
+template <int B>
+static void launch_b(dim3 grid, hipStream_t st, const float* g, float* err, int8_t* codes,
+                     float* scales, float* deq, int64_t N, int32_t iters, uint32_t k0, uint32_t k1,
+                     uint32_t step) {
+    if (err && deq)
+        hipLaunchKernelGGL((int8_kernel<B, true, true>), grid, dim3(kThreads), 0, st, g, err, codes,
+                           scales, deq, N, iters, k0, k1, step);
+    else if (err)
+        hipLaunchKernelGGL((int8_kernel<B, true, false>), grid, dim3(kThreads), 0, st, g, err,
+                           codes, scales, deq, N, iters, k0, k1, step);
+    else if (deq)
+        hipLaunchKernelGGL((int8_kernel<B, false, true>), grid, dim3(kThreads), 0, st, g, err,
+                           codes, scales, deq, N, iters, k0, k1, step);
+    else
+        hipLaunchKernelGGL((int8_kernel<B, false, false>), grid, dim3(kThreads), 0, st, g, err,
+                           codes, scales, deq, N, iters, k0, k1, step);
+}
+
+hipError_t launch_int8(const float* g, float* err, int8_t* codes, float* scales, float* deq,
+                       int64_t N, int32_t block, uint64_t seed, uint32_t step, hipStream_t st) {
+    const int32_t iters = 4;
+    const int64_t tiles = (N + kTile - 1) / kTile;
+    const dim3 grid((unsigned)((tiles + iters - 1) / iters));
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    switch (block) {
+        case 64: launch_b<64>(grid, st, g, err, codes, scales, deq, N, iters, k0, k1, step); break;
+        case 128: launch_b<128>(grid, st, g, err, codes, scales, deq, N, iters, k0, k1, step); break;
+        case 256: launch_b<256>(grid, st, g, err, codes, scales, deq, N, iters, k0, k1, step); break;
+        case 512: launch_b<512>(grid, st, g, err, codes, scales, deq, N, iters, k0, k1, step); break;
+        case 1024: launch_b<1024>(grid, st, g, err, codes, scales, deq, N, iters, k0, k1, step); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace onebit

@@ -1,0 +1,130 @@
+// Server-side reduction and the decompression every worker performs.
+//
+// Server c owns chunk c (1-bit LAMB page, experiments paragraph: the
+// all-to-all phase delivers chunk c of every worker to server c; the
+// all-gather phase returns the server chunks to every worker).  On one GPU the
+// n workers are rows of one buffer, so both phases are addressing: the server
+// workgroups read chunk c's words of every row directly.
+//
+// Per element: the n decoded values +-s[i][c] are accumulated in ascending
+// worker order in binary32 from +0 and divided by n (a multiplication by 1/n
+// when n is a power of two, which is the same correctly rounded result);
+// the lazy server error is added, the sign packed, the state stored and |g''|
+// summed in fp64 for the exact chunk mean.
+#include "common.h"
+
+namespace onebit {
+
+__global__ __launch_bounds__(kThreads) void server_kernel(
+    const uint32_t* __restrict__ bits, const float* __restrict__ scales, float* __restrict__ ef,
+    const float* __restrict__ S_prev, uint32_t* __restrict__ sv_bits, double* __restrict__ partials,
+    int64_t N, int32_t n, int64_t L, int32_t iters, int64_t bpc, int32_t reset, int32_t pow2,
+    float inv_n) {
+    __shared__ double red[kThreads / 64];
+    __shared__ float sc[64];
+    const int64_t c = blockIdx.x / bpc;
+    const int64_t wg = blockIdx.x - c * bpc;
+    const int64_t cbase = c * L;
+    const int64_t start = wg * (int64_t)iters * kTile;
+    int64_t end = start + (int64_t)iters * kTile;
+    if (end > L) end = L;
+    if (threadIdx.x < n) sc[threadIdx.x] = scales[(int64_t)threadIdx.x * n + c];
+    __syncthreads();
+    const float S = reset ? 0.0f : S_prev[c];
+    const float nf = (float)n;
+    const int64_t wrow = N >> 5;  // words per worker row
+    const int lane8 = lane_id() & 7;
+
+    double acc = 0.0;
+    for (int it = 0; it < iters; ++it) {
+        const int64_t j = start + (int64_t)it * kTile + 4 * (int64_t)threadIdx.x;
+        const bool active = j < end;
+        const int64_t J = cbase + j;
+        const int sh = (int)(J & 31);
+        float a[4] = {0.f, 0.f, 0.f, 0.f};
+        f4 pv = {0.f, 0.f, 0.f, 0.f};
+        if (active) {
+            if (!reset) pv = *reinterpret_cast<const f4*>(ef + J);
+            const uint32_t* w = bits + (J >> 5);
+            for (int i = 0; i < n; ++i) {
+                const uint32_t word = w[(int64_t)i * wrow] >> sh;
+                const float s = sc[i];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) a[k] = a[k] + (((word >> k) & 1u) ? s : -s);
+            }
+        }
+        const float p[4] = {pv.x, pv.y, pv.z, pv.w};
+        float g[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float avg = pow2 ? a[k] * inv_n : a[k] / nf;
+            const float e = reset ? 0.0f : ef_error(p[k], S);
+            g[k] = avg + e;
+        }
+        const uint32_t word = or8(sign_nibble(g[0], g[1], g[2], g[3]) << (4 * lane8));
+        if (active) {
+            const f4 out = {g[0], g[1], g[2], g[3]};
+            *reinterpret_cast<f4*>(ef + J) = out;
+            acc += (double)fabsf(g[0]);
+            acc += (double)fabsf(g[1]);
+            acc += (double)fabsf(g[2]);
+            acc += (double)fabsf(g[3]);
+            if (lane8 == 0) sv_bits[J >> 5] = word;
+        }
+    }
+    const double tot = block_sum(acc, red);
+    if (threadIdx.x == 0) partials[blockIdx.x] = tot;
+}
+
+hipError_t launch_server(const uint32_t* bits, const float* scales, float* ef, const float* S_prev,
+                         uint32_t* sv_bits, double* partials, int64_t N, int32_t n,
+                         const ChunkPlan& plan, bool reset, hipStream_t st) {
+    const bool pow2 = (n & (n - 1)) == 0;
+    const float inv_n = 1.0f / (float)n;  // exact for powers of two
+    hipLaunchKernelGGL(server_kernel, dim3((unsigned)(plan.bpc * n)), dim3(kThreads), 0, st, bits,
+                       scales, ef, S_prev, sv_bits, partials, N, n, plan.L, plan.iters, plan.bpc,
+                       reset ? 1 : 0, pow2 ? 1 : 0, inv_n);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- decompress
+template <bool SEG>
+__global__ __launch_bounds__(kThreads) void decompress_kernel(
+    const uint32_t* __restrict__ sv_bits, const float* __restrict__ S, float* __restrict__ out,
+    const int64_t* __restrict__ seg_off, const float* __restrict__ seg_k, int32_t n_seg, int64_t N,
+    int64_t L) {
+    const int64_t J = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+    if (J >= N) return;
+    const float s = S[J / L];  // L is a multiple of 64, so the 4 elements share a chunk
+    const uint32_t word = sv_bits[J >> 5] >> (J & 31);
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = ((word >> k) & 1u) ? s : -s;
+    if (SEG) {
+        int seg = find_segment(seg_off, n_seg, J);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            while (J + k >= seg_off[seg + 1] && seg + 1 < n_seg) ++seg;
+            v[k] = v[k] / seg_k[seg];
+        }
+    }
+    const f4 o = {v[0], v[1], v[2], v[3]};
+    __builtin_nontemporal_store(o, reinterpret_cast<f4*>(out + J));
+}
+
+hipError_t launch_decompress(const uint32_t* sv_bits, const float* S, float* m_out,
+                             const int64_t* seg_off, const float* seg_k, int32_t n_seg,
+                             int64_t N, int32_t n, hipStream_t st) {
+    const int64_t groups = N / 4;
+    const dim3 grid((unsigned)((groups + kThreads - 1) / kThreads));
+    const int64_t L = N / n;
+    if (seg_off)
+        hipLaunchKernelGGL(decompress_kernel<true>, grid, dim3(kThreads), 0, st, sv_bits, S, m_out,
+                           seg_off, seg_k, n_seg, N, L);
+    else
+        hipLaunchKernelGGL(decompress_kernel<false>, grid, dim3(kThreads), 0, st, sv_bits, S,
+                           m_out, seg_off, seg_k, n_seg, N, L);
+    return hipGetLastError();
+}
+
+}  // namespace onebit

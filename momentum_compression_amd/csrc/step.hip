@@ -1,0 +1,223 @@
+// Frozen-variance parameter steps.
+//
+// Adam (1-bit Adam article, sections 2.1 and 6; frozen denominator from the
+// 1-bit LAMB page, algorithm paragraph):  x = x - lr * (m / (sqrtf(v) + eps)).
+//
+// LAMB (1-bit LAMB page, algorithm and analysis paragraphs), one streaming
+// pass:  g = (m - beta1 m_prev) / (1 - beta1);  v_f = beta2 v_f + (1-beta2) g^2;
+// per-layer max of v / v_f (order-preserving uint keys, NaN skipped, one
+// atomicMax per workgroup and layer);  x -= (lr c_{t-1,l}) m / (sqrtf(v)+eps).
+// A tiny per-layer kernel then forms r_t and c_t.  With use_c_t the x update
+// moves to a second pass after r_t / c_t are known.
+#include "common.h"
+
+namespace onebit {
+
+__global__ __launch_bounds__(kThreads) void adam_kernel(float* __restrict__ x,
+                                                        const float* __restrict__ m,
+                                                        const float* __restrict__ v, int64_t N,
+                                                        float lr, float eps) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads * 4;
+    for (int64_t j = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4; j < N; j += stride) {
+        const f4 xv = *reinterpret_cast<const f4*>(x + j);
+        const f4 mv = __builtin_nontemporal_load(reinterpret_cast<const f4*>(m + j));
+        const f4 vv = __builtin_nontemporal_load(reinterpret_cast<const f4*>(v + j));
+        const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
+        const float ms[4] = {mv.x, mv.y, mv.z, mv.w};
+        const float vs[4] = {vv.x, vv.y, vv.z, vv.w};
+        float o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float den = sqrtf(vs[k]) + eps;
+            const float upd = ms[k] / den;
+            o[k] = xs[k] - lr * upd;
+        }
+        const f4 ov = {o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<f4*>(x + j) = ov;
+    }
+}
+
+hipError_t launch_adam(float* x, const float* m, const float* v, int64_t N, float lr, float eps,
+                       hipStream_t st) {
+    const int64_t groups = N / 4;
+    int64_t blocks = (groups + kThreads - 1) / kThreads;
+    const int64_t cap = 256 * 32;  // persistent-ish grid: 32 workgroups per CU
+    if (blocks > cap) blocks = cap;
+    hipLaunchKernelGGL(adam_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, x, m, v, N, lr,
+                       eps);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- LAMB
+__global__ void fill_u32_kernel(uint32_t* p, int32_t n, uint32_t val) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = val;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+template <bool UPDATE_X>
+__global__ __launch_bounds__(kThreads) void lamb_kernel(
+    float* __restrict__ x, const float* __restrict__ m, const float* __restrict__ mp,
+    float* __restrict__ vf, const float* __restrict__ v, const int64_t* __restrict__ seg_off,
+    int32_t n_seg, const float* __restrict__ c_prev, uint32_t* __restrict__ keys, int64_t N,
+    int32_t iters, float lr, float eps, float beta1, float beta2) {
+    __shared__ uint32_t red[kThreads / 64];
+    const int64_t wstart = (int64_t)blockIdx.x * iters * kTile;
+    int64_t wend = wstart + (int64_t)iters * kTile;
+    if (wend > N) wend = N;
+    // workgroup-uniform segment test
+    const int seg0 = find_segment(seg_off, n_seg, wstart);
+    const bool uniform = seg_off[seg0 + 1] >= wend;
+    const float omb1 = 1.0f - beta1;
+    const float omb2 = 1.0f - beta2;
+
+    const int64_t j0 = wstart + 4 * (int64_t)threadIdx.x;
+    int seg = uniform ? seg0 : find_segment(seg_off, n_seg, j0 < N ? j0 : N - 1);
+    int64_t hi = seg_off[seg + 1];
+    float step = lr * c_prev[seg];
+    uint32_t kmax = 0;
+    for (int it = 0; it < iters; ++it) {
+        const int64_t j = j0 + (int64_t)it * kTile;
+        if (j >= wend) break;
+        const f4 mv = *reinterpret_cast<const f4*>(m + j);
+        const f4 pv = __builtin_nontemporal_load(reinterpret_cast<const f4*>(mp + j));
+        const f4 fv = *reinterpret_cast<const f4*>(vf + j);
+        const f4 vv = __builtin_nontemporal_load(reinterpret_cast<const f4*>(v + j));
+        f4 xv = {0.f, 0.f, 0.f, 0.f};
+        if (UPDATE_X) xv = *reinterpret_cast<const f4*>(x + j);
+        const float ms[4] = {mv.x, mv.y, mv.z, mv.w};
+        const float ps[4] = {pv.x, pv.y, pv.z, pv.w};
+        const float fs[4] = {fv.x, fv.y, fv.z, fv.w};
+        const float vs[4] = {vv.x, vv.y, vv.z, vv.w};
+        float xs[4] = {xv.x, xv.y, xv.z, xv.w};
+        float nf[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (!uniform) {
+                while (j + k >= hi && seg + 1 < n_seg) {
+                    if (kmax) atomicMax(&keys[seg], kmax);
+                    kmax = 0;
+                    ++seg;
+                    hi = seg_off[seg + 1];
+                    step = lr * c_prev[seg];
+                }
+            }
+            const float g = (ms[k] - beta1 * ps[k]) / omb1;
+            const float vn = beta2 * fs[k] + omb2 * (g * g);
+            nf[k] = vn;
+            const float ratio = vs[k] / vn;
+            if (ratio == ratio) {
+                const uint32_t key = float_key(ratio);
+                kmax = key > kmax ? key : kmax;
+            }
+            if (UPDATE_X) {
+                const float den = sqrtf(vs[k]) + eps;
+                const float upd = ms[k] / den;
+                xs[k] = xs[k] - step * upd;
+            }
+        }
+        const f4 nv = {nf[0], nf[1], nf[2], nf[3]};
+        *reinterpret_cast<f4*>(vf + j) = nv;
+        if (UPDATE_X) {
+            const f4 xo = {xs[0], xs[1], xs[2], xs[3]};
+            *reinterpret_cast<f4*>(x + j) = xo;
+        }
+    }
+    if (uniform) {
+        const uint32_t wm = wave_max_u32(kmax);
+        if (lane_id() == 0) red[threadIdx.x >> 6] = wm;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t b = red[0];
+            for (int w = 1; w < kThreads / 64; ++w) b = red[w] > b ? red[w] : b;
+            if (b) atomicMax(&keys[seg0], b);
+        }
+    } else if (kmax) {
+        atomicMax(&keys[seg], kmax);
+    }
+}
+
+__global__ void lamb_finalize_kernel(const uint32_t* __restrict__ keys, int32_t n_seg,
+                                     const float* __restrict__ c_avg, float* __restrict__ r_prev,
+                                     float* __restrict__ c_prev, float* __restrict__ ratio_max,
+                                     float thr, float r_min, float r_max) {
+    const int l = blockIdx.x * blockDim.x + threadIdx.x;
+    if (l >= n_seg) return;
+    const uint32_t key = keys[l];
+    const float R = key ? key_float(key) : __uint_as_float(0x7FC00000u);
+    const float rp = r_prev[l];
+    const float Rv = (R == R) ? R : rp;
+    const float lo = (1.0f - thr) * rp;
+    const float hi = (1.0f + thr) * rp;
+    float r = fminf(fmaxf(Rv, lo), hi);
+    r = fminf(fmaxf(r, r_min), r_max);
+    r_prev[l] = r;
+    c_prev[l] = c_avg[l] * r;
+    if (ratio_max) ratio_max[l] = R;
+}
+
+__global__ __launch_bounds__(kThreads) void lamb_apply_kernel(
+    float* __restrict__ x, const float* __restrict__ m, const float* __restrict__ v,
+    const int64_t* __restrict__ seg_off, int32_t n_seg, const float* __restrict__ c, int64_t N,
+    int32_t iters, float lr, float eps) {
+    const int64_t j0 = (int64_t)blockIdx.x * iters * kTile + 4 * (int64_t)threadIdx.x;
+    if (j0 >= N) return;
+    int seg = find_segment(seg_off, n_seg, j0);
+    int64_t hi = seg_off[seg + 1];
+    float step = lr * c[seg];
+    for (int it = 0; it < iters; ++it) {
+        const int64_t j = j0 + (int64_t)it * kTile;
+        if (j >= N) break;
+        const f4 xv = *reinterpret_cast<const f4*>(x + j);
+        const f4 mv = *reinterpret_cast<const f4*>(m + j);
+        const f4 vv = *reinterpret_cast<const f4*>(v + j);
+        float xs[4] = {xv.x, xv.y, xv.z, xv.w};
+        const float ms[4] = {mv.x, mv.y, mv.z, mv.w};
+        const float vs[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            while (j + k >= hi && seg + 1 < n_seg) {
+                ++seg;
+                hi = seg_off[seg + 1];
+                step = lr * c[seg];
+            }
+            const float den = sqrtf(vs[k]) + eps;
+            const float upd = ms[k] / den;
+            xs[k] = xs[k] - step * upd;
+        }
+        const f4 xo = {xs[0], xs[1], xs[2], xs[3]};
+        *reinterpret_cast<f4*>(x + j) = xo;
+    }
+}
+
+hipError_t launch_lamb(const onebit_frozen_v_args& a, uint32_t* keys, hipStream_t st) {
+    const int32_t iters = 8;
+    const int64_t tiles = (a.N + kTile - 1) / kTile;
+    const dim3 grid((unsigned)((tiles + iters - 1) / iters));
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((a.n_seg + 255) / 256), dim3(256), 0, st, keys,
+                       a.n_seg, 0u);
+    if (a.use_c_t)
+        hipLaunchKernelGGL(lamb_kernel<false>, grid, dim3(kThreads), 0, st, a.x, a.m, a.m_prev,
+                           a.v_fresh, a.v, a.seg_off, a.n_seg, a.c_prev, keys, a.N, iters, a.lr,
+                           a.eps, a.beta1, a.beta2);
+    else
+        hipLaunchKernelGGL(lamb_kernel<true>, grid, dim3(kThreads), 0, st, a.x, a.m, a.m_prev,
+                           a.v_fresh, a.v, a.seg_off, a.n_seg, a.c_prev, keys, a.N, iters, a.lr,
+                           a.eps, a.beta1, a.beta2);
+    hipLaunchKernelGGL(lamb_finalize_kernel, dim3((a.n_seg + 255) / 256), dim3(256), 0, st, keys,
+                       a.n_seg, a.c_avg, a.r_prev, a.c_prev, a.ratio_max, a.r_threshold, a.r_min,
+                       a.r_max);
+    if (a.use_c_t)
+        hipLaunchKernelGGL(lamb_apply_kernel, grid, dim3(kThreads), 0, st, a.x, a.m, a.v,
+                           a.seg_off, a.n_seg, a.c_prev, a.N, iters, a.lr, a.eps);
+    return hipGetLastError();
+}
+
+}  // namespace onebit

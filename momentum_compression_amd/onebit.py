@@ -1,0 +1,184 @@
+"""ctypes binding of libonebit.so (the C ABI declared in include/onebit.h).
+
+Argument marshalling only: tensors become device pointers, the stream
+defaults to torch's current HIP stream, and a nonzero status raises
+``OnebitError``.  Every step of the compression stage runs in the library's
+HIP kernels; nothing here computes.  The library must have been built
+(``python -m momentum_compression_amd.build``); a missing library is an
+error, never a fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libonebit.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "onebit.h")
+
+ONEBIT_OK = 0
+ONEBIT_E_NULL = -1
+ONEBIT_E_SIZE = -2
+ONEBIT_E_ALIGN = -3
+ONEBIT_E_WORKSPACE = -4
+ONEBIT_E_ARG = -5
+ONEBIT_E_HIP = -6
+
+_c_i32, _c_i64, _c_u32, _c_u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64
+_c_f, _c_p, _c_sz = ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class FrozenVArgs(ctypes.Structure):
+    """Mirror of onebit_frozen_v_args."""
+
+    _fields_ = [
+        ("mode", _c_i32), ("use_c_t", _c_i32), ("N", _c_i64),
+        ("lr", _c_f), ("eps", _c_f), ("beta1", _c_f), ("beta2", _c_f),
+        ("r_threshold", _c_f), ("r_min", _c_f), ("r_max", _c_f),
+        ("n_seg", _c_i32),
+        ("x", _c_p), ("m", _c_p), ("v", _c_p), ("m_prev", _c_p), ("v_fresh", _c_p),
+        ("seg_off", _c_p), ("c_avg", _c_p), ("r_prev", _c_p), ("c_prev", _c_p),
+        ("ratio_max", _c_p),
+    ]
+
+
+_SIGNATURES = {
+    "onebit_compress": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32, _c_f, _c_i32, _c_p, _c_p,
+                                 _c_i32, _c_p, _c_sz, _c_p]),
+    "onebit_server_reduce": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i64,
+                                      _c_i32, _c_i32, _c_p, _c_sz, _c_p]),
+    "onebit_decompress": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i64, _c_i32, _c_p]),
+    "onebit_error_materialize": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_i32, _c_i32, _c_p]),
+    "lamb_layer_scale": (_c_i32, [_c_p, _c_i64, _c_i32, _c_p, _c_p, _c_i32, _c_i32, _c_p]),
+    "frozen_v_step": (_c_i32, [ctypes.POINTER(FrozenVArgs), _c_p, _c_sz, _c_p]),
+    "int8_sr_quantize": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32, _c_u64, _c_u32, _c_p]),
+    "onebit_workspace_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32]),
+    "onebit_strerror": (ctypes.c_char_p, [_c_i32]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class OnebitError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({strerror(status)})")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libonebit.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m momentum_compression_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def declared_functions() -> list:
+    """Function names declared in include/onebit.h."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def strerror(status: int) -> str:
+    return load().onebit_strerror(status).decode()
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not x.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous")
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, st: int) -> None:
+    if st != ONEBIT_OK:
+        raise OnebitError(fn, st)
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def workspace_bytes(N: int, n: int, n_seg: int = 0) -> int:
+    return int(load().onebit_workspace_bytes(N, n, n_seg))
+
+
+def onebit_compress(m, ef, scales, bits, N: int, n: int, clip: float = 0.0, reset: bool = False,
+                    seg_off=None, seg_k=None, n_seg: int = 0, ws=None, stream=None) -> None:
+    _check("onebit_compress", load().onebit_compress(
+        _ptr(m), _ptr(ef), _ptr(scales), _ptr(bits), N, n, clip, int(bool(reset)),
+        _ptr(seg_off), _ptr(seg_k), n_seg, _ptr(ws), _nbytes(ws) if ws is not None else 0,
+        _stream(stream)))
+
+
+def onebit_server_reduce(bits, scales, ef, sv_scales, sv_bits, m_out, N: int, n: int,
+                         reset: bool = False, seg_off=None, seg_k=None, n_seg: int = 0, ws=None,
+                         stream=None) -> None:
+    _check("onebit_server_reduce", load().onebit_server_reduce(
+        _ptr(bits), _ptr(scales), _ptr(ef), _ptr(sv_scales), _ptr(sv_bits), _ptr(m_out),
+        _ptr(seg_off), _ptr(seg_k), n_seg, N, n, int(bool(reset)), _ptr(ws),
+        _nbytes(ws) if ws is not None else 0, _stream(stream)))
+
+
+def onebit_decompress(sv_bits, sv_scales, m_out, N: int, n: int, seg_off=None, seg_k=None,
+                      n_seg: int = 0, stream=None) -> None:
+    _check("onebit_decompress", load().onebit_decompress(
+        _ptr(sv_bits), _ptr(sv_scales), _ptr(m_out), _ptr(seg_off), _ptr(seg_k), n_seg, N, n,
+        _stream(stream)))
+
+
+def onebit_error_materialize(ef, scales, e_out, N: int, rows: int, n: int, stream=None) -> None:
+    _check("onebit_error_materialize", load().onebit_error_materialize(
+        _ptr(ef), _ptr(scales), _ptr(e_out), N, rows, n, _stream(stream)))
+
+
+def lamb_layer_scale(buf, N: int, batch: int, seg_off, seg_k, n_seg: int, divide: bool,
+                     stream=None) -> None:
+    _check("lamb_layer_scale", load().lamb_layer_scale(
+        _ptr(buf), N, batch, _ptr(seg_off), _ptr(seg_k), n_seg, int(bool(divide)), _stream(stream)))
+
+
+def frozen_v_step(*, mode: int, N: int, x, m, v, lr: float, eps: float, beta1: float = 0.9,
+                  beta2: float = 0.999, m_prev=None, v_fresh=None, seg_off=None, n_seg: int = 0,
+                  c_avg=None, r_prev=None, c_prev=None, ratio_max=None, r_threshold: float = 0.1,
+                  r_min: float = 0.5, r_max: float = 4.0, use_c_t: bool = False, ws=None,
+                  stream=None) -> None:
+    a = FrozenVArgs(mode=mode, use_c_t=int(bool(use_c_t)), N=N, lr=lr, eps=eps, beta1=beta1,
+                    beta2=beta2, r_threshold=r_threshold, r_min=r_min, r_max=r_max, n_seg=n_seg,
+                    x=_ptr(x), m=_ptr(m), v=_ptr(v), m_prev=_ptr(m_prev), v_fresh=_ptr(v_fresh),
+                    seg_off=_ptr(seg_off), c_avg=_ptr(c_avg), r_prev=_ptr(r_prev),
+                    c_prev=_ptr(c_prev), ratio_max=_ptr(ratio_max))
+    _check("frozen_v_step", load().frozen_v_step(
+        ctypes.byref(a), _ptr(ws), _nbytes(ws) if ws is not None else 0, _stream(stream)))
+
+
+def int8_sr_quantize(g, err, codes, block_scales, deq, N: int, block: int, seed: int, step: int,
+                     stream=None) -> None:
+    _check("int8_sr_quantize", load().int8_sr_quantize(
+        _ptr(g), _ptr(err), _ptr(codes), _ptr(block_scales), _ptr(deq), N, block,
+        seed & 0xFFFFFFFFFFFFFFFF, step & 0xFFFFFFFF, _stream(stream)))

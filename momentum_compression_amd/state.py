@@ -1,0 +1,120 @@
+"""Device buffers of one simulated data-parallel group and the calls of one
+compressed step, driven through the C ABI.
+
+PyTorch is used only to allocate device memory and to pick the stream; every
+element of every step is computed by libonebit's kernels.
+
+Buffers (n workers, N elements per worker row, chunk L = N / n):
+
+    ef        [n, N]    worker error state (last compensated value)
+    scales    [n, n]    worker chunk scales s[i][c] (error state, second half)
+    bits      [n, N/32] worker sign words
+    sv_ef     [N]       server error state
+    sv_scales [n]       server chunk scales
+    sv_bits   [N/32]    server sign words
+    mbar      [N]       decompressed global momentum
+    ws        bytes     scratch for the chunk sums and layer maxima
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import onebit as ob
+
+
+@dataclass
+class OneBitGroup:
+    N: int
+    n: int
+    device: torch.device
+    clip: float = 0.0
+    reset_interval: int = 0
+    seg_off: Optional[torch.Tensor] = None  # int64 [S+1] on device
+    seg_k: Optional[torch.Tensor] = None    # float32 [S] on device
+
+    def __post_init__(self):
+        N, n, dev = self.N, self.n, self.device
+        if N % (64 * n):
+            raise ValueError("N must be a multiple of 64 * n (pad the buffer)")
+        f32 = torch.float32
+        self.ef = torch.zeros((n, N), dtype=f32, device=dev)
+        self.scales = torch.zeros((n, n), dtype=f32, device=dev)
+        self.bits = torch.zeros((n, N // 32), dtype=torch.int32, device=dev)
+        self.sv_ef = torch.zeros(N, dtype=f32, device=dev)
+        self.sv_scales = torch.zeros(n, dtype=f32, device=dev)
+        self.sv_bits = torch.zeros(N // 32, dtype=torch.int32, device=dev)
+        self.mbar = torch.zeros(N, dtype=f32, device=dev)
+        n_seg = self.n_seg
+        self.ws = torch.empty(max(256, ob.workspace_bytes(N, n, n_seg)), dtype=torch.uint8, device=dev)
+
+    @property
+    def n_seg(self) -> int:
+        return 0 if self.seg_off is None else self.seg_off.numel() - 1
+
+    def is_reset(self, t: int) -> bool:
+        """Periodic error reset (1-bit Adam article, section 4.1): zero the
+        errors before compensation when t is a multiple of the interval."""
+        return self.reset_interval > 0 and t % self.reset_interval == 0
+
+    def compress(self, m: torch.Tensor, t: int, first: bool = False, stream=None) -> None:
+        ob.onebit_compress(m, self.ef, self.scales, self.bits, self.N, self.n, clip=self.clip,
+                           reset=first or self.is_reset(t), seg_off=self.seg_off, seg_k=self.seg_k,
+                           n_seg=self.n_seg, ws=self.ws, stream=stream)
+
+    def server(self, t: int, first: bool = False, decompress: bool = True, stream=None) -> None:
+        ob.onebit_server_reduce(self.bits, self.scales, self.sv_ef, self.sv_scales, self.sv_bits,
+                                self.mbar if decompress else None, self.N, self.n,
+                                reset=first or self.is_reset(t), seg_off=self.seg_off,
+                                seg_k=self.seg_k, n_seg=self.n_seg, ws=self.ws, stream=stream)
+
+    def worker_error(self) -> torch.Tensor:
+        e = torch.empty_like(self.ef)
+        ob.onebit_error_materialize(self.ef, self.scales, e, self.N, self.n, self.n)
+        return e
+
+    def server_error(self) -> torch.Tensor:
+        e = torch.empty_like(self.sv_ef)
+        ob.onebit_error_materialize(self.sv_ef, self.sv_scales, e, self.N, 1, self.n)
+        return e
+
+    def adam_step(self, x: torch.Tensor, v: torch.Tensor, lr: float, eps: float, stream=None) -> None:
+        ob.frozen_v_step(mode=0, N=self.N, x=x, m=self.mbar, v=v, lr=lr, eps=eps, stream=stream)
+
+
+@dataclass
+class LambState:
+    """Per-layer 1-bit LAMB state (1-bit LAMB page, algorithm paragraph)."""
+
+    x: torch.Tensor          # [N] parameters
+    v_frozen: torch.Tensor   # [N] v_Tw
+    v_fresh: torch.Tensor    # [N] v_t
+    m_prev: torch.Tensor     # [N] previous global momentum
+    seg_off: torch.Tensor    # int64 [S+1]
+    c_avg: torch.Tensor      # [S]
+    r: torch.Tensor          # [S] r_{t-1} -> r_t
+    c: torch.Tensor          # [S] c_{t-1} -> c_t
+    ratio_max: torch.Tensor  # [S]
+    ws: torch.Tensor
+
+    @classmethod
+    def create(cls, x, v_frozen, m_prev, seg_off, c_avg) -> "LambState":
+        S = seg_off.numel() - 1
+        dev = x.device
+        return cls(x=x, v_frozen=v_frozen, v_fresh=v_frozen.clone(), m_prev=m_prev,
+                   seg_off=seg_off, c_avg=c_avg, r=torch.ones(S, dtype=torch.float32, device=dev),
+                   c=c_avg.clone(), ratio_max=torch.empty(S, dtype=torch.float32, device=dev),
+                   ws=torch.empty(max(256, 4 * S + 256), dtype=torch.uint8, device=dev))
+
+    def step(self, mbar: torch.Tensor, lr: float, eps: float, beta1: float, beta2: float,
+             thr: float, r_min: float, r_max: float, use_c_t: bool = False, stream=None) -> None:
+        S = self.seg_off.numel() - 1
+        ob.frozen_v_step(mode=1, N=self.x.numel(), x=self.x, m=mbar, v=self.v_frozen, lr=lr,
+                         eps=eps, beta1=beta1, beta2=beta2, m_prev=self.m_prev,
+                         v_fresh=self.v_fresh, seg_off=self.seg_off, n_seg=S, c_avg=self.c_avg,
+                         r_prev=self.r, c_prev=self.c, ratio_max=self.ratio_max,
+                         r_threshold=thr, r_min=r_min, r_max=r_max, use_c_t=use_c_t, ws=self.ws,
+                         stream=stream)

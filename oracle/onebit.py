@@ -94,17 +94,29 @@ def worker_compress(m: np.ndarray, e: np.ndarray, clip: float = 0.0,
     return {"gc": gc, "bits": bits, "s": s, "e": e_out}
 
 
-def server_average(bits: np.ndarray, s: np.ndarray, c: int) -> np.ndarray:
-    """Decoded average of chunk c over the n workers: ascending worker order,
-    binary32 accumulation from +0, then one division by n."""
-    n = s.shape[0]
-    N = bits.shape[1] * 32
-    L = N // n
-    w0, w1 = c * L // 32, (c + 1) * L // 32
+def server_chunk(bits_c: np.ndarray, s_c: np.ndarray, E_c: np.ndarray,
+                 reset: bool = False) -> Dict[str, np.ndarray]:
+    """Server side of one chunk.
+
+    bits_c : uint32 [n, L/32] -- this chunk's sign words of every worker
+    s_c    : float32 [n]      -- this chunk's scale of every worker
+    E_c    : float32 [L]      -- the server error of this chunk
+    The decoded values +-s_c[i] are summed in ascending worker order in
+    binary32 from +0, then divided by n once; the server error is added and
+    the result compressed like a worker chunk."""
+    bits_c = np.asarray(bits_c, dtype=np.uint32)
+    s_c = np.asarray(s_c, dtype=f32)
+    n = s_c.shape[0]
+    L = bits_c.shape[1] * 32
     acc = np.zeros(L, dtype=f32)
     for i in range(n):
-        acc = (acc + B.signed(B.unpack(bits[i, w0:w1]), s[i, c])).astype(f32)
-    return (acc / f32(n)).astype(f32)
+        acc = (acc + B.signed(B.unpack(bits_c[i]), s_c[i])).astype(f32)
+    avg = (acc / f32(n)).astype(f32)
+    E_in = np.zeros(L, dtype=f32) if reset else np.asarray(E_c, dtype=f32)
+    g2 = (avg + E_in).astype(f32)
+    S = mean_abs_f32(g2)
+    return {"avg": avg, "g2": g2, "bits": B.pack(B.sign_bit(g2)), "S": S,
+            "E": error_from(g2, S)}
 
 
 def server_reduce(bits: np.ndarray, s: np.ndarray, E: np.ndarray,
@@ -120,18 +132,18 @@ def server_reduce(bits: np.ndarray, s: np.ndarray, E: np.ndarray,
     n = s.shape[0]
     N = bits.shape[1] * 32
     L = N // n
-    E_in = np.zeros(N, dtype=f32) if reset else np.asarray(E, dtype=f32)
-    avg = np.empty(N, dtype=f32)
-    g2 = np.empty(N, dtype=f32)
-    E_out = np.empty(N, dtype=f32)
-    S = np.empty(n, dtype=f32)
+    out = {"avg": np.empty(N, dtype=f32), "g2": np.empty(N, dtype=f32),
+           "E": np.empty(N, dtype=f32), "S": np.empty(n, dtype=f32),
+           "bits": np.empty(N // 32, dtype=np.uint32)}
+    E = np.zeros(N, dtype=f32) if reset else np.asarray(E, dtype=f32)
     for c in range(n):
         sl = slice(c * L, (c + 1) * L)
-        avg[sl] = server_average(bits, s, c)
-        g2[sl] = (avg[sl] + E_in[sl]).astype(f32)
-        S[c] = mean_abs_f32(g2[sl])
-        E_out[sl] = error_from(g2[sl], S[c])
-    return {"avg": avg, "g2": g2, "bits": B.pack(B.sign_bit(g2)), "S": S, "E": E_out}
+        r = server_chunk(bits[:, c * L // 32:(c + 1) * L // 32], s[:, c], E[sl], reset)
+        for key in ("avg", "g2", "E"):
+            out[key][sl] = r[key]
+        out["S"][c] = r["S"]
+        out["bits"][c * L // 32:(c + 1) * L // 32] = r["bits"]
+    return out
 
 
 def decompress(sbits: np.ndarray, S: np.ndarray, k: Optional[np.ndarray] = None) -> np.ndarray:

@@ -1,0 +1,59 @@
+"""Helpers for the GPU parity tests (device handling, comparisons).
+
+A GPU test never falls back to anything: if the library is missing the
+binding raises, and the test fails."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from momentum_compression_amd import onebit as ob
+
+
+def device() -> torch.device:
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    ob.load()  # raises if libonebit.so is missing
+    return torch.device("cuda:0")
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    a = t.detach().cpu().numpy()
+    if a.dtype == np.int32:
+        a = a.view(np.uint32)
+    return a
+
+
+def gen(seed: int, dev) -> torch.Generator:
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    return g
+
+
+def same_f32(got: np.ndarray, want: np.ndarray, name: str, rtol: float = 1e-6,
+             atol: float = 1e-9) -> None:
+    """Parity bar for binary32 values: within |a - b| <= atol + rtol |b|
+    (NaN matching NaN), and -- the design target -- bit-identical."""
+    got = np.asarray(got, dtype=np.float32)
+    want = np.asarray(want, dtype=np.float32)
+    assert got.shape == want.shape, (name, got.shape, want.shape)
+    gn, wn = np.isnan(got), np.isnan(want)
+    assert np.array_equal(gn, wn), f"{name}: NaN positions differ ({np.sum(gn != wn)})"
+    ok = ~gn
+    g64, w64 = got[ok].astype(np.float64), want[ok].astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        inf_ok = np.isinf(w64) & (g64 == w64)
+        diff = np.abs(g64 - w64)
+        close = inf_ok | (diff <= atol + rtol * np.abs(w64))
+    assert close.all(), f"{name}: {np.sum(~close)} of {close.size} outside tolerance"
+    bits_eq = got[ok].view(np.uint32) == want[ok].view(np.uint32)
+    assert bits_eq.all(), f"{name}: {np.sum(~bits_eq)} of {bits_eq.size} not bit-identical"
+
+
+def same_bits(got: np.ndarray, want: np.ndarray, name: str) -> None:
+    got = np.asarray(got).view(np.uint32) if np.asarray(got).dtype == np.int32 else np.asarray(got)
+    assert got.shape == want.shape, (name, got.shape, want.shape)
+    neq = got != want
+    assert not neq.any(), f"{name}: {int(neq.sum())} of {neq.size} words differ"

@@ -1,0 +1,101 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/onebit.h declares, sizes its workspace, and rejects invalid calls
+with the documented status before touching the HIP runtime (the fake
+device addresses below are never dereferenced)."""
+
+import ctypes
+
+import pytest
+
+from momentum_compression_amd import onebit as ob
+
+P = 0x10000  # a 16-byte aligned fake device address, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ob.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = ob.declared_functions()
+    assert {"onebit_compress", "onebit_server_reduce", "lamb_layer_scale", "frozen_v_step",
+            "int8_sr_quantize", "onebit_workspace_bytes", "onebit_strerror"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_strerror_covers_codes(lib):
+    for code in range(0, -7, -1):
+        assert ob.strerror(code) != "unknown status"
+    assert ob.strerror(-99) == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    assert ob.workspace_bytes(1 << 20, 4) > 0
+    assert ob.workspace_bytes(1000, 4) == 0           # not a multiple of 64 n
+    assert ob.workspace_bytes(1 << 20, 0) == 0
+    assert ob.workspace_bytes(1 << 20, 65) == 0
+    big = ob.workspace_bytes(1_311_528_960, 16, 291)
+    assert 0 < big < 64 << 20
+
+
+def _compress(lib, m=P, ef=P, sc=P, bits=P, N=1 << 12, n=4, clip=0.0, off=None, k=None, nseg=0,
+              ws=P, wsb=1 << 30):
+    return lib.onebit_compress(m, ef, sc, bits, N, n, clip, 0, off, k, nseg, ws, wsb, None)
+
+
+def test_compress_validation(lib):
+    assert _compress(lib, m=None) == ob.ONEBIT_E_NULL
+    assert _compress(lib, N=4 * 63) == ob.ONEBIT_E_SIZE
+    assert _compress(lib, n=0) == ob.ONEBIT_E_SIZE
+    assert _compress(lib, n=65, N=65 * 64) == ob.ONEBIT_E_SIZE
+    assert _compress(lib, N=-64 * 4) == ob.ONEBIT_E_SIZE
+    assert _compress(lib, m=P + 4) == ob.ONEBIT_E_ALIGN
+    assert _compress(lib, ws=None) == ob.ONEBIT_E_WORKSPACE
+    assert _compress(lib, wsb=16) == ob.ONEBIT_E_WORKSPACE
+    assert _compress(lib, ws=P + 16) == ob.ONEBIT_E_ALIGN
+    assert _compress(lib, off=P) == ob.ONEBIT_E_NULL         # offsets without coefficients
+    assert _compress(lib, off=P, k=P, nseg=0) == ob.ONEBIT_E_ARG
+    assert _compress(lib, clip=float("nan")) == ob.ONEBIT_E_ARG
+    assert _compress(lib, N=0) == ob.ONEBIT_OK              # empty: no-op, no launch
+
+
+def test_server_and_other_validation(lib):
+    f = lib.onebit_server_reduce
+    assert f(None, P, P, P, P, None, None, None, 0, 1 << 12, 4, 0, P, 1 << 30, None) == ob.ONEBIT_E_NULL
+    assert f(P, P, P, P, P, P + 4, None, None, 0, 1 << 12, 4, 0, P, 1 << 30, None) == ob.ONEBIT_E_ALIGN
+    assert f(P, P, P, P, P, None, None, None, 0, 100, 4, 0, P, 1 << 30, None) == ob.ONEBIT_E_SIZE
+    assert f(P, P, P, P, P, None, None, None, 0, 1 << 12, 4, 0, P, 8, None) == ob.ONEBIT_E_WORKSPACE
+    assert lib.onebit_decompress(P, P, None, None, None, 0, 1 << 12, 4, None) == ob.ONEBIT_E_NULL
+    assert lib.onebit_error_materialize(P, P, P, 1 << 12, 0, 4, None) == ob.ONEBIT_E_SIZE
+    assert lib.lamb_layer_scale(P, 1 << 12, 1, P, P, 0, 0, None) == ob.ONEBIT_E_ARG
+    assert lib.lamb_layer_scale(P, 6, 1, P, P, 1, 0, None) == ob.ONEBIT_E_SIZE
+    i8 = lib.int8_sr_quantize
+    assert i8(P, None, P, P, None, 1 << 12, 100, 1, 1, None) == ob.ONEBIT_E_SIZE
+    assert i8(P, None, P, P, None, 256 * 3 + 64, 256, 1, 1, None) == ob.ONEBIT_E_SIZE
+    assert i8(P, P + 8, P, P, None, 256, 256, 1, 1, None) == ob.ONEBIT_E_ALIGN
+    assert i8(None, None, P, P, None, 256, 256, 1, 1, None) == ob.ONEBIT_E_NULL
+
+
+def test_frozen_v_validation(lib):
+    a = ob.FrozenVArgs(mode=0, N=1024, x=P, m=P, v=None, lr=1e-3, eps=1e-6)
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_NULL
+    a = ob.FrozenVArgs(mode=2, N=1024, x=P, m=P, v=P)
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_ARG
+    a = ob.FrozenVArgs(mode=1, N=1024, x=P, m=P, v=P, m_prev=P, v_fresh=P, seg_off=P, c_avg=P,
+                       r_prev=P, c_prev=P, n_seg=4)
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_WORKSPACE
+    a.n_seg = 0
+    assert lib.frozen_v_step(ctypes.byref(a), P, 1 << 20, None) == ob.ONEBIT_E_ARG
+    a = ob.FrozenVArgs(mode=0, N=1022, x=P, m=P, v=P)
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_SIZE
+    assert lib.frozen_v_step(None, None, 0, None) == ob.ONEBIT_E_NULL
+
+
+def test_struct_layout_matches_header():
+    # offsets implied by the C declaration on x86-64 / amdgcn (LP64)
+    assert ob.FrozenVArgs.N.offset == 8
+    assert ob.FrozenVArgs.n_seg.offset == 44
+    assert ob.FrozenVArgs.x.offset == 48
+    assert ctypes.sizeof(ob.FrozenVArgs) == 48 + 10 * 8
