@@ -13,7 +13,8 @@ using f4 = float __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;           // threads per workgroup (4 waves)
 constexpr int kTile = kThreads * 4;     // elements per workgroup iteration (float4 / lane)
-constexpr int kMaxIters = 16;           // iterations per workgroup in streaming kernels
+constexpr int kMaxIters = 4;            // tiles per workgroup in the chunked streaming kernels
+constexpr int kUnroll = 4;              // tiles whose loads are issued together
 
 // ---------------------------------------------------------------- launch plan
 // One plan for the chunked kernels (worker compress, server reduce): the

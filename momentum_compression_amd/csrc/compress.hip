@@ -46,43 +46,53 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     }
 
     double acc = 0.0;
-    for (int it = 0; it < iters; ++it) {
-        const int64_t j = start + (int64_t)it * kTile + 4 * (int64_t)threadIdx.x;
-        const bool active = j < end;
-        const int64_t idx = row + cbase + j;
-        f4 mv = {0.f, 0.f, 0.f, 0.f};
-        f4 pv = {0.f, 0.f, 0.f, 0.f};
-        if (active) {
-            mv = __builtin_nontemporal_load(reinterpret_cast<const f4*>(m + idx));
-            if (!RESET) pv = *reinterpret_cast<const f4*>(ef + idx);
-        }
-        float g[4] = {mv.x, mv.y, mv.z, mv.w};
-        const float p[4] = {pv.x, pv.y, pv.z, pv.w};
+    for (int it0 = 0; it0 < iters; it0 += kUnroll) {
+        // issue the loads of kUnroll tiles before any use (memory-level parallelism)
+        f4 mv[kUnroll], pv[kUnroll];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if (SEG) {
-                const int64_t J = cbase + j + k;
-                while (active && J >= seg_hi && seg + 1 < n_seg) {
-                    ++seg;
-                    seg_hi = seg_off[seg + 1];
-                    kv = seg_k[seg];
-                }
-                g[k] = kv * g[k];
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t j = start + (int64_t)(it0 + u) * kTile + 4 * (int64_t)threadIdx.x;
+            mv[u] = f4{0.f, 0.f, 0.f, 0.f};
+            pv[u] = f4{0.f, 0.f, 0.f, 0.f};
+            if (it0 + u < iters && j < end) {
+                mv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(m + row + cbase + j));
+                if (!RESET)
+                    pv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(ef + row + cbase + j));
             }
-            const float e = RESET ? 0.0f : ef_error(p[k], s);
-            float v = g[k] + e;
-            if (CLAMP) v = fminf(fmaxf(v, -clip), clip);
-            g[k] = v;
         }
-        uint32_t word = or8(sign_nibble(g[0], g[1], g[2], g[3]) << (4 * lane8));
-        if (active) {
-            const f4 out = {g[0], g[1], g[2], g[3]};
-            *reinterpret_cast<f4*>(ef + idx) = out;
-            acc += (double)fabsf(g[0]);
-            acc += (double)fabsf(g[1]);
-            acc += (double)fabsf(g[2]);
-            acc += (double)fabsf(g[3]);
-            if (lane8 == 0) bits[(row >> 5) + ((cbase + j) >> 5)] = word;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t j = start + (int64_t)(it0 + u) * kTile + 4 * (int64_t)threadIdx.x;
+            const bool active = it0 + u < iters && j < end;
+            const int64_t idx = row + cbase + j;
+            float g[4] = {mv[u].x, mv[u].y, mv[u].z, mv[u].w};
+            const float p[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (SEG) {
+                    const int64_t J = cbase + j + k;
+                    while (active && J >= seg_hi && seg + 1 < n_seg) {
+                        ++seg;
+                        seg_hi = seg_off[seg + 1];
+                        kv = seg_k[seg];
+                    }
+                    g[k] = kv * g[k];
+                }
+                const float e = RESET ? 0.0f : ef_error(p[k], s);
+                float v = g[k] + e;
+                if (CLAMP) v = fminf(fmaxf(v, -clip), clip);
+                g[k] = v;
+            }
+            const uint32_t word = or8(sign_nibble(g[0], g[1], g[2], g[3]) << (4 * lane8));
+            if (active) {
+                const f4 out = {g[0], g[1], g[2], g[3]};
+                __builtin_nontemporal_store(out, reinterpret_cast<f4*>(ef + idx));
+                acc += (double)fabsf(g[0]);
+                acc += (double)fabsf(g[1]);
+                acc += (double)fabsf(g[2]);
+                acc += (double)fabsf(g[3]);
+                if (lane8 == 0) bits[(row >> 5) + ((cbase + j) >> 5)] = word;
+            }
         }
     }
     const double tot = block_sum(acc, red);

@@ -15,13 +15,19 @@
 
 namespace onebit {
 
+// Words of the kUnroll tiles a workgroup processes together, for every
+// worker, are staged through LDS with coalesced loads (32 consecutive words
+// per worker and tile); each lane then reads its word per worker from LDS.
 __global__ __launch_bounds__(kThreads) void server_kernel(
     const uint32_t* __restrict__ bits, const float* __restrict__ scales, float* __restrict__ ef,
     const float* __restrict__ S_prev, uint32_t* __restrict__ sv_bits, double* __restrict__ partials,
     int64_t N, int32_t n, int64_t L, int32_t iters, int64_t bpc, int32_t reset, int32_t pow2,
     float inv_n) {
+    constexpr int kWordsPerTile = kTile / 32;              // 32
+    constexpr int kGroupWords = kWordsPerTile * kUnroll;   // 128 words per worker per group
     __shared__ double red[kThreads / 64];
     __shared__ float sc[64];
+    extern __shared__ uint32_t stage[];                    // [n][kGroupWords]
     const int64_t c = blockIdx.x / bpc;
     const int64_t wg = blockIdx.x - c * bpc;
     const int64_t cbase = c * L;
@@ -29,47 +35,63 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
     int64_t end = start + (int64_t)iters * kTile;
     if (end > L) end = L;
     if (threadIdx.x < n) sc[threadIdx.x] = scales[(int64_t)threadIdx.x * n + c];
-    __syncthreads();
     const float S = reset ? 0.0f : S_prev[c];
     const float nf = (float)n;
     const int64_t wrow = N >> 5;  // words per worker row
     const int lane8 = lane_id() & 7;
 
     double acc = 0.0;
-    for (int it = 0; it < iters; ++it) {
-        const int64_t j = start + (int64_t)it * kTile + 4 * (int64_t)threadIdx.x;
-        const bool active = j < end;
-        const int64_t J = cbase + j;
-        const int sh = (int)(J & 31);
-        float a[4] = {0.f, 0.f, 0.f, 0.f};
-        f4 pv = {0.f, 0.f, 0.f, 0.f};
-        if (active) {
-            if (!reset) pv = *reinterpret_cast<const f4*>(ef + J);
-            const uint32_t* w = bits + (J >> 5);
+    for (int it0 = 0; it0 < iters; it0 += kUnroll) {
+        const int64_t g0 = start + (int64_t)it0 * kTile;   // first element of this group
+        const int64_t gw = (cbase + g0) >> 5;             // its first word in a row
+        const int64_t gwords = (end - g0 + 31) >> 5;      // words of this group inside the chunk
+        __syncthreads();                                  // previous group done with `stage`
+        for (int q = threadIdx.x; q < n * kGroupWords; q += kThreads) {
+            const int i = q / kGroupWords;
+            const int w = q - i * kGroupWords;
+            stage[q] = (w < gwords) ? bits[(int64_t)i * wrow + gw + w] : 0u;
+        }
+        f4 pv[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t j = g0 + (int64_t)u * kTile + 4 * (int64_t)threadIdx.x;
+            pv[u] = f4{0.f, 0.f, 0.f, 0.f};
+            if (!reset && it0 + u < iters && j < end)
+                pv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(ef + cbase + j));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t j = g0 + (int64_t)u * kTile + 4 * (int64_t)threadIdx.x;
+            const bool active = it0 + u < iters && j < end;
+            const int64_t J = cbase + j;
+            const int sh = (int)(J & 31);
+            const int wl = u * kWordsPerTile + (threadIdx.x >> 3);  // this lane's word in the group
+            float a[4] = {0.f, 0.f, 0.f, 0.f};
             for (int i = 0; i < n; ++i) {
-                const uint32_t word = w[(int64_t)i * wrow] >> sh;
+                const uint32_t word = stage[i * kGroupWords + wl] >> sh;
                 const float s = sc[i];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) a[k] = a[k] + (((word >> k) & 1u) ? s : -s);
             }
-        }
-        const float p[4] = {pv.x, pv.y, pv.z, pv.w};
-        float g[4];
+            const float p[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
+            float g[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float avg = pow2 ? a[k] * inv_n : a[k] / nf;
-            const float e = reset ? 0.0f : ef_error(p[k], S);
-            g[k] = avg + e;
-        }
-        const uint32_t word = or8(sign_nibble(g[0], g[1], g[2], g[3]) << (4 * lane8));
-        if (active) {
-            const f4 out = {g[0], g[1], g[2], g[3]};
-            *reinterpret_cast<f4*>(ef + J) = out;
-            acc += (double)fabsf(g[0]);
-            acc += (double)fabsf(g[1]);
-            acc += (double)fabsf(g[2]);
-            acc += (double)fabsf(g[3]);
-            if (lane8 == 0) sv_bits[J >> 5] = word;
+            for (int k = 0; k < 4; ++k) {
+                const float avg = pow2 ? a[k] * inv_n : a[k] / nf;
+                const float e = reset ? 0.0f : ef_error(p[k], S);
+                g[k] = avg + e;
+            }
+            const uint32_t word = or8(sign_nibble(g[0], g[1], g[2], g[3]) << (4 * lane8));
+            if (active) {
+                const f4 out = {g[0], g[1], g[2], g[3]};
+                __builtin_nontemporal_store(out, reinterpret_cast<f4*>(ef + J));
+                acc += (double)fabsf(g[0]);
+                acc += (double)fabsf(g[1]);
+                acc += (double)fabsf(g[2]);
+                acc += (double)fabsf(g[3]);
+                if (lane8 == 0) sv_bits[J >> 5] = word;
+            }
         }
     }
     const double tot = block_sum(acc, red);
@@ -81,42 +103,66 @@ hipError_t launch_server(const uint32_t* bits, const float* scales, float* ef, c
                          const ChunkPlan& plan, bool reset, hipStream_t st) {
     const bool pow2 = (n & (n - 1)) == 0;
     const float inv_n = 1.0f / (float)n;  // exact for powers of two
-    hipLaunchKernelGGL(server_kernel, dim3((unsigned)(plan.bpc * n)), dim3(kThreads), 0, st, bits,
+    const size_t lds = (size_t)n * (kTile / 32) * kUnroll * sizeof(uint32_t);
+    hipLaunchKernelGGL(server_kernel, dim3((unsigned)(plan.bpc * n)), dim3(kThreads), lds, st, bits,
                        scales, ef, S_prev, sv_bits, partials, N, n, plan.L, plan.iters, plan.bpc,
                        reset ? 1 : 0, pow2 ? 1 : 0, inv_n);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- decompress
+// Workgroups cover kMaxIters consecutive tiles; each lane writes 4 elements
+// per tile (nontemporal: the output is consumed by a later kernel).
 template <bool SEG>
 __global__ __launch_bounds__(kThreads) void decompress_kernel(
     const uint32_t* __restrict__ sv_bits, const float* __restrict__ S, float* __restrict__ out,
     const int64_t* __restrict__ seg_off, const float* __restrict__ seg_k, int32_t n_seg, int64_t N,
     int64_t L) {
-    const int64_t J = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
-    if (J >= N) return;
-    const float s = S[J / L];  // L is a multiple of 64, so the 4 elements share a chunk
-    const uint32_t word = sv_bits[J >> 5] >> (J & 31);
-    float v[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = ((word >> k) & 1u) ? s : -s;
+    const int64_t j0 = (int64_t)blockIdx.x * kMaxIters * kTile + 4 * (int64_t)threadIdx.x;
+    if (j0 >= N) return;
+    int seg = 0;
+    int64_t hi = 0;
+    float kv = 1.0f;
     if (SEG) {
-        int seg = find_segment(seg_off, n_seg, J);
+        seg = find_segment(seg_off, n_seg, j0);
+        hi = seg_off[seg + 1];
+        kv = seg_k[seg];
+    }
+    uint32_t words[kMaxIters];
+#pragma unroll
+    for (int u = 0; u < kMaxIters; ++u) {
+        const int64_t J = j0 + (int64_t)u * kTile;
+        words[u] = J < N ? sv_bits[J >> 5] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kMaxIters; ++u) {
+        const int64_t J = j0 + (int64_t)u * kTile;
+        if (J >= N) break;
+        const float s = S[J / L];  // L is a multiple of 64, so the 4 elements share a chunk
+        const uint32_t word = words[u] >> (J & 31);
+        float v[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            while (J + k >= seg_off[seg + 1] && seg + 1 < n_seg) ++seg;
-            v[k] = v[k] / seg_k[seg];
+            v[k] = ((word >> k) & 1u) ? s : -s;
+            if (SEG) {
+                while (J + k >= hi && seg + 1 < n_seg) {
+                    ++seg;
+                    hi = seg_off[seg + 1];
+                    kv = seg_k[seg];
+                }
+                v[k] = v[k] / kv;
+            }
         }
+        const f4 o = {v[0], v[1], v[2], v[3]};
+        __builtin_nontemporal_store(o, reinterpret_cast<f4*>(out + J));
     }
-    const f4 o = {v[0], v[1], v[2], v[3]};
-    __builtin_nontemporal_store(o, reinterpret_cast<f4*>(out + J));
 }
 
 hipError_t launch_decompress(const uint32_t* sv_bits, const float* S, float* m_out,
                              const int64_t* seg_off, const float* seg_k, int32_t n_seg,
                              int64_t N, int32_t n, hipStream_t st) {
-    const int64_t groups = N / 4;
-    const dim3 grid((unsigned)((groups + kThreads - 1) / kThreads));
+    const int64_t per_wg = (int64_t)kMaxIters * kTile;
+    const dim3 grid((unsigned)((N + per_wg - 1) / per_wg));
     const int64_t L = N / n;
     if (seg_off)
         hipLaunchKernelGGL(decompress_kernel<true>, grid, dim3(kThreads), 0, st, sv_bits, S, m_out,

@@ -17,14 +17,24 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(float* __restrict__ x,
                                                         const float* __restrict__ m,
                                                         const float* __restrict__ v, int64_t N,
                                                         float lr, float eps) {
-    const int64_t stride = (int64_t)gridDim.x * kThreads * 4;
-    for (int64_t j = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4; j < N; j += stride) {
-        const f4 xv = *reinterpret_cast<const f4*>(x + j);
-        const f4 mv = __builtin_nontemporal_load(reinterpret_cast<const f4*>(m + j));
-        const f4 vv = __builtin_nontemporal_load(reinterpret_cast<const f4*>(v + j));
-        const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
-        const float ms[4] = {mv.x, mv.y, mv.z, mv.w};
-        const float vs[4] = {vv.x, vv.y, vv.z, vv.w};
+    const int64_t j0 = (int64_t)blockIdx.x * kMaxIters * kTile + 4 * (int64_t)threadIdx.x;
+    f4 xv[kMaxIters], mv[kMaxIters], vv[kMaxIters];
+#pragma unroll
+    for (int u = 0; u < kMaxIters; ++u) {
+        const int64_t j = j0 + (int64_t)u * kTile;
+        if (j < N) {
+            xv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(x + j));
+            mv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(m + j));
+            vv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(v + j));
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kMaxIters; ++u) {
+        const int64_t j = j0 + (int64_t)u * kTile;
+        if (j >= N) break;
+        const float xs[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+        const float ms[4] = {mv[u].x, mv[u].y, mv[u].z, mv[u].w};
+        const float vs[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
         float o[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -33,18 +43,15 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(float* __restrict__ x,
             o[k] = xs[k] - lr * upd;
         }
         const f4 ov = {o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<f4*>(x + j) = ov;
+        __builtin_nontemporal_store(ov, reinterpret_cast<f4*>(x + j));
     }
 }
 
 hipError_t launch_adam(float* x, const float* m, const float* v, int64_t N, float lr, float eps,
                        hipStream_t st) {
-    const int64_t groups = N / 4;
-    int64_t blocks = (groups + kThreads - 1) / kThreads;
-    const int64_t cap = 256 * 32;  // persistent-ish grid: 32 workgroups per CU
-    if (blocks > cap) blocks = cap;
-    hipLaunchKernelGGL(adam_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, x, m, v, N, lr,
-                       eps);
+    const int64_t per_wg = (int64_t)kMaxIters * kTile;
+    hipLaunchKernelGGL(adam_kernel, dim3((unsigned)((N + per_wg - 1) / per_wg)), dim3(kThreads), 0,
+                       st, x, m, v, N, lr, eps);
     return hipGetLastError();
 }
 
