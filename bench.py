@@ -70,15 +70,14 @@ def read_traffic(launch_elems: int):
     if vals.get("source_sha256") != kernel_source_hash():
         return None
     try:
-        fetch = float(vals["FETCH_SIZE_KiB_per_dispatch"])
-        write = float(vals["WRITE_SIZE_KiB_per_dispatch"])
-        factor = float(vals.get("copy_scale_factor", "1.0"))
+        fetch = float(vals["FETCH_SIZE_KiB_per_dispatch"]) * float(vals["fetch_scale_factor"])
+        write = float(vals["WRITE_SIZE_KiB_per_dispatch"]) * float(vals["write_scale_factor"])
         elems = int(vals["elements_per_dispatch"])
     except (KeyError, ValueError):
         return None
     if elems != launch_elems:
         return None
-    return (fetch + write) * 1024.0 * factor
+    return (fetch + write) * 1024.0
 
 
 def cpu_baseline(wl, seed: int = 11):
@@ -119,6 +118,117 @@ def cpu_baseline(wl, seed: int = 11):
     }
 
 
+B_LAMB_STEP = 28.0             # read x, m, m_prev, v_fresh, v_Tw; write x, v_fresh
+B_INT8 = 17.015625             # read g, err; write code, err, deq; scale per 256
+
+
+def _time_calls(fns, warmup: int, steps: int, stream):
+    """Run the callables in order `warmup` + `steps` times; return the mean
+    event time (ms) of each callable over the timed repetitions."""
+    import torch
+
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    acc = [0.0] * len(fns)
+    for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+        ev[0].record(stream)
+        for k, f in enumerate(fns):
+            f()
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        for k in range(len(fns)):
+            acc[k] += ev[k].elapsed_time(ev[k + 1])
+    return [a / steps for a in acc]
+
+
+def _row(ms: float, nbytes: float, elems: int) -> dict:
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "elements_per_s": elems / (ms * 1e-3),
+            "algorithmic_GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def measure_lamb(steps: int, warmup: int) -> dict:
+    """1-bit LAMB path on the 302-tensor BERT-Large buffer, 16 workers:
+    compress with x k_l fused, server reduce with / k_l decompression fused,
+    LAMB frozen-variance step with the per-layer ratio and r/c update."""
+    import numpy as np
+    import torch
+
+    from momentum_compression_amd.state import LambState, OneBitGroup
+    from workloads import configs as C
+    from workloads import synth as S
+
+    dev = torch.device("cuda:0")
+    wl = C.get("bert_large_lamb_302t_x16")
+    N, n = wl.N, wl.n
+    print(f"[bench] rows: {wl.name} N={N} n={n}", file=sys.stderr, flush=True)
+    off = np.array(C.segment_offsets(wl.segments), dtype=np.int64)
+    k, c_avg = S.lamb_tables(wl)
+    off_d, k_d = torch.from_numpy(off).to(dev), torch.from_numpy(k).to(dev)
+    sig = S.per_element(S.segment_sigmas(wl), wl, dev)
+    m = S.momentum(wl, 1, dev, sigma_elem=sig)
+    grp = OneBitGroup(N, n, dev, seg_off=off_d, seg_k=k_d)
+    st = LambState.create(S.params(wl, dev), S.frozen_variance(wl, dev),
+                          S.lamb_prev_momentum(wl, dev, sig), off_d, torch.from_numpy(c_avg).to(dev))
+    del sig
+    stream = torch.cuda.current_stream()
+    grp.compress(m, 1, first=True)
+    grp.server(1, first=True)
+    t = [2]
+
+    def comp():
+        grp.compress(m, t[0])
+
+    def serv():
+        grp.server(t[0], decompress=True)
+
+    def lamb():
+        st.step(grp.mbar, wl.lr, wl.eps, wl.beta1, wl.beta2, wl.r_threshold, wl.r_min, wl.r_max)
+        t[0] += 1
+
+    ms = _time_calls([comp, serv, lamb], warmup, steps, stream)
+    out = {"workload": wl.name, "N": N, "workers": n, "layers": len(wl.segments),
+           "compress_x_k": _row(ms[0], B_COMPRESS * n * N, n * N),
+           "server_and_decompress_div_k": _row(ms[1], (b_server(n) + B_DECOMPRESS) * N, N),
+           "lamb_step": _row(ms[2], B_LAMB_STEP * N, N)}
+    del grp, st, m
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_int8(steps: int, warmup: int) -> dict:
+    """Block INT8 stochastic rounding with error feedback and dequantised
+    output on 2^30 Laplace gradients (block 256)."""
+    import torch
+
+    from momentum_compression_amd import onebit as ob
+    from workloads import synth as S
+
+    dev = torch.device("cuda:0")
+    N, block = 1 << 30, 256
+    print(f"[bench] rows: int8 N={N}", file=sys.stderr, flush=True)
+    g = S.laplace_gradient(N, 1, 4, dev)
+    err = torch.zeros(N, device=dev)
+    codes = torch.empty(N, dtype=torch.int8, device=dev)
+    scales = torch.empty(N // block, device=dev)
+    deq = torch.empty(N, device=dev)
+    stream = torch.cuda.current_stream()
+    step = [1]
+
+    def q():
+        ob.int8_sr_quantize(g, err, codes, scales, deq, N, block, 4, step[0])
+        step[0] += 1
+
+    ms = _time_calls([q], warmup, steps, stream)
+    out = {"workload": "int8_sr_2^30", "N": N, "block": block,
+           "int8_sr_ef_deq": _row(ms[0], B_INT8 * N, N)}
+    del g, err, codes, scales, deq
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +238,8 @@ def main() -> int:
     ap.add_argument("--only", default="", choices=["", "compress", "server", "decompress", "adam",
                                                    "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the LAMB and INT8 rows measured after the headline step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -255,6 +367,11 @@ def main() -> int:
                      "launch_ms": round(ms["compress"], 4)},
         "kernels": kernels,
     }
+    if not args.no_rows:
+        del grp, m, x, v
+        torch.cuda.empty_cache()
+        out["rows"] = {"lamb": measure_lamb(max(3, args.steps // 2), 1),
+                       "int8": measure_int8(max(3, args.steps // 2), 1)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl)

@@ -32,9 +32,9 @@ def pack(b: np.ndarray) -> np.ndarray:
 
 def unpack(words: np.ndarray, count: int | None = None) -> np.ndarray:
     """Inverse of ``pack``: bool vector of 32 * len(words) (or ``count``)."""
-    w = np.asarray(words, dtype=np.uint32).ravel().astype(np.uint64)
-    pos = np.arange(32, dtype=np.uint64)
-    b = ((w[:, None] >> pos[None, :]) & np.uint64(1)).astype(bool).ravel()
+    w = np.asarray(words, dtype=np.uint32).ravel()
+    pos = np.arange(32, dtype=np.uint32)
+    b = ((w[:, None] >> pos[None, :]) & np.uint32(1)).astype(bool).ravel()
     return b if count is None else b[:count]
 
 

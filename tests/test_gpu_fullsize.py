@@ -1,0 +1,194 @@
+"""Parity at the workloads' full sizes, in the launch configuration the bench
+times (the library derives its launch plan from N and n alone).  The oracle
+checks sampled worker chunks end to end (free-running over the steps run),
+server chunks in lock-step (the GPU's worker words and scales as inputs),
+and the parameter step on samples or on the whole buffer."""
+
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+from momentum_compression_amd import onebit as ob
+from momentum_compression_amd.state import LambState, OneBitGroup
+from oracle import onebit as O
+from oracle import optim as P
+from oracle.int8 import int8_sr
+from tests._gpu import device, host, same_bits, same_f32
+from workloads import configs as C
+from workloads import synth as S
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+F32 = np.float32
+
+
+def _free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _need(dev, nbytes):
+    free = torch.cuda.mem_get_info(dev)[0]
+    if free < nbytes:
+        pytest.skip(f"needs {nbytes / 2**30:.0f} GiB of device memory, {free / 2**30:.0f} free")
+
+
+def _chunk_words(c, L):
+    return slice(c * L // 32, (c + 1) * L // 32)
+
+
+def _run_adam_fullsize(wl, steps, pairs, server_chunks, t0=1, sample=1 << 20):
+    dev = device()
+    N, n, L = wl.N, wl.n, wl.L
+    _need(dev, int(n * N * 4 * 2.2 + N * 4 * 6))
+    print(f"[fullsize] {wl.name} N={N} n={n} steps={steps} t0={t0}", flush=True)
+    sig = S.per_element(S.segment_sigmas(wl), wl, dev)
+    grp = OneBitGroup(N, n, dev, clip=wl.clip, reset_interval=wl.reset_interval)
+    x = S.params(wl, dev)
+    v = S.frozen_variance(wl, dev)
+    m = torch.empty((n, N), dtype=torch.float32, device=dev)
+    rng = np.random.default_rng(0)
+    idx = np.sort(rng.choice(N, size=sample, replace=False))
+    idx_d = torch.from_numpy(idx).to(dev)
+    e_w = {p: np.zeros(L, dtype=F32) for p in pairs}
+    E_s = {c: np.zeros(L, dtype=F32) for c in server_chunks}
+    for t in range(t0, t0 + steps):
+        S.momentum(wl, t, dev, sigma_elem=sig, out=m)
+        first = t == t0
+        reset = first or grp.is_reset(t)
+        x_before = host(x[idx_d])
+        grp.compress(m, t, first=first)
+        grp.server(t, first=first)
+        grp.adam_step(x, v, wl.lr, wl.eps)
+        torch.cuda.synchronize()
+        tag = f"{wl.name} t={t}"
+        scales = host(grp.scales)
+        for (i, c) in pairs:
+            sl = slice(c * L, (c + 1) * L)
+            w = O.worker_compress(host(m[i, sl])[None, :], e_w[(i, c)][None, :], clip=wl.clip,
+                                  reset=reset)
+            same_f32(np.array([scales[i, c]]), w["s"][0, :1], f"{tag} scale[{i},{c}]")
+            same_bits(host(grp.bits[i, _chunk_words(c, L)]), w["bits"][0], f"{tag} bits[{i},{c}]")
+            same_f32(host(grp.ef[i, sl]), w["gc"][0], f"{tag} state[{i},{c}]")
+            e_w[(i, c)] = w["e"][0]
+        sv_scales = host(grp.sv_scales)
+        for c in server_chunks:
+            sl = slice(c * L, (c + 1) * L)
+            r = O.server_chunk(host(grp.bits[:, _chunk_words(c, L)]), scales[:, c], E_s[c],
+                               reset=reset)
+            same_f32(np.array([sv_scales[c]]), np.array([r["S"]]), f"{tag} server scale[{c}]")
+            same_bits(host(grp.sv_bits[_chunk_words(c, L)]), r["bits"], f"{tag} server bits[{c}]")
+            same_f32(host(grp.sv_ef[sl]), r["g2"], f"{tag} server state[{c}]")
+            same_f32(host(grp.mbar[sl]), O.decompress(r["bits"], np.array([r["S"]], dtype=F32)),
+                     f"{tag} decompressed[{c}]")
+            E_s[c] = r["E"]
+        x_want = P.adam_frozen_step(x_before, host(grp.mbar[idx_d]), host(v[idx_d]), wl.lr, wl.eps)
+        same_f32(host(x[idx_d]), x_want, f"{tag} parameters (sampled)")
+    del grp, x, v, m, sig
+    _free()
+
+
+def test_bert_large_335M_x8_bench_configuration():
+    wl = C.get("bert_large_335M_x8")
+    _run_adam_fullsize(wl, steps=3, pairs=[(0, 0), (3, 5), (7, 7)], server_chunks=[0, 5])
+
+
+def test_gpt_1_3B_x16_clamp_and_reset():
+    """The reset interval (2000) is crossed: t = 1999 (first step), 2000
+    (periodic reset), 2001; the 2.0 clamp is on."""
+    wl = C.get("gpt_1.3B_x16")
+    _run_adam_fullsize(wl, steps=3, pairs=[(0, 0), (15, 9)], server_chunks=[9], t0=1999,
+                       sample=1 << 18)
+
+
+def test_bert_large_lamb_302t_x16():
+    """Two 1-bit LAMB steps on the 302-tensor buffer; the LAMB step is
+    checked on the whole buffer (every layer's ratio, r_t, c_t, x, v)."""
+    dev = device()
+    wl = C.get("bert_large_lamb_302t_x16")
+    N, n, L = wl.N, wl.n, wl.L
+    _need(dev, int(n * N * 4 * 2.2 + N * 4 * 8))
+    print(f"[fullsize] {wl.name} N={N} n={n} segments={len(wl.segments)}", flush=True)
+    off = np.array(C.segment_offsets(wl.segments), dtype=np.int64)
+    k, c_avg = S.lamb_tables(wl)
+    k_el = O.per_element_k(off, k)
+    sig = S.per_element(S.segment_sigmas(wl), wl, dev)
+    off_d, k_d = torch.from_numpy(off).to(dev), torch.from_numpy(k).to(dev)
+    grp = OneBitGroup(N, n, dev, seg_off=off_d, seg_k=k_d)
+    st = LambState.create(S.params(wl, dev), S.frozen_variance(wl, dev),
+                          S.lamb_prev_momentum(wl, dev, sig), off_d, torch.from_numpy(c_avg).to(dev))
+    m = torch.empty((n, N), dtype=torch.float32, device=dev)
+    pairs = [(0, 0), (9, 15)]
+    e_w = {p: np.zeros(L, dtype=F32) for p in pairs}
+    E_c = np.zeros(L, dtype=F32)
+    csrv = 15
+    v_h = host(st.v_frozen)
+    for t in (1, 2):
+        S.momentum(wl, t, dev, sigma_elem=sig, out=m)
+        first = t == 1
+        x_h, vf_h, mp_h = host(st.x).copy(), host(st.v_fresh).copy(), host(st.m_prev).copy()
+        r_h, c_h = host(st.r).copy(), host(st.c).copy()
+        grp.compress(m, t, first=first)
+        grp.server(t, first=first)
+        st.step(grp.mbar, wl.lr, wl.eps, wl.beta1, wl.beta2, wl.r_threshold, wl.r_min, wl.r_max)
+        torch.cuda.synchronize()
+        tag = f"lamb t={t}"
+        scales = host(grp.scales)
+        for (i, c) in pairs:
+            sl = slice(c * L, (c + 1) * L)
+            w = O.worker_compress(host(m[i, sl])[None, :], e_w[(i, c)][None, :], reset=first,
+                                  k=k_el[sl])
+            same_f32(np.array([scales[i, c]]), w["s"][0, :1], f"{tag} scale[{i},{c}]")
+            same_bits(host(grp.bits[i, _chunk_words(c, L)]), w["bits"][0], f"{tag} bits[{i},{c}]")
+            e_w[(i, c)] = w["e"][0]
+        sl = slice(csrv * L, (csrv + 1) * L)
+        r = O.server_chunk(host(grp.bits[:, _chunk_words(csrv, L)]), scales[:, csrv], E_c, reset=first)
+        same_f32(np.array([host(grp.sv_scales)[csrv]]), np.array([r["S"]]), f"{tag} server scale")
+        same_bits(host(grp.sv_bits[_chunk_words(csrv, L)]), r["bits"], f"{tag} server bits")
+        same_f32(host(grp.mbar[sl]),
+                 O.decompress(r["bits"], np.array([r["S"]], dtype=F32), k=k_el[sl]), f"{tag} m / k")
+        E_c = r["E"]
+        out = P.lamb_frozen_step(x_h, host(grp.mbar), mp_h, vf_h, v_h, off, c_avg, r_h, c_h,
+                                 wl.lr, wl.eps, wl.beta1, wl.beta2, wl.r_threshold, wl.r_min,
+                                 wl.r_max)
+        same_f32(host(st.ratio_max), out["R"], f"{tag} layer max ratio")
+        same_f32(host(st.r), out["r"], f"{tag} r_t")
+        same_f32(host(st.c), out["c"], f"{tag} c_t")
+        same_f32(host(st.v_fresh), out["v"], f"{tag} fresh variance")
+        same_f32(host(st.x), out["x"], f"{tag} parameters")
+        st.m_prev.copy_(grp.mbar)
+        del out, x_h, vf_h, mp_h
+    del grp, st, m, sig
+    _free()
+
+
+def test_int8_2_30_with_error_feedback():
+    dev = device()
+    N, block, seed = 1 << 30, 256, 4
+    _need(dev, N * 18)
+    print(f"[fullsize] int8 N={N}", flush=True)
+    err = torch.zeros(N, device=dev)
+    codes = torch.empty(N, dtype=torch.int8, device=dev)
+    scales = torch.empty(N // block, device=dev)
+    deq = torch.empty(N, device=dev)
+    g = torch.empty(N, device=dev)
+    ranges = [0, (N // 2) - 4096, N - (1 << 20)]
+    e_prev = {a: np.zeros(1 << 20, dtype=F32) for a in ranges}
+    for step in (1, 2):
+        S.laplace_gradient(N, step, seed, dev, out=g)
+        ob.int8_sr_quantize(g, err, codes, scales, deq, N, block, seed, step)
+        torch.cuda.synchronize()
+        for a in ranges:
+            sl = slice(a, a + (1 << 20))
+            o = int8_sr(host(g[sl]), e_prev[a], seed, step, block, J0=a)
+            assert np.array_equal(host(codes[sl]), o["codes"]), f"step {step} codes at {a}"
+            same_f32(host(scales[a // block:(a + (1 << 20)) // block]), o["scales"], f"scales {a}")
+            same_f32(host(deq[sl]), o["deq"], f"deq {a}")
+            same_f32(host(err[sl]), o["e"], f"residual {a}")
+            e_prev[a] = o["e"]
+        q = host(codes)
+        assert q.min() >= -127 and q.max() <= 127
+        del q
+    del err, codes, scales, deq, g
+    _free()
