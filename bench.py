@@ -156,6 +156,7 @@ def measure_lamb(steps: int, warmup: int) -> dict:
     import numpy as np
     import torch
 
+    from momentum_compression_amd import onebit as ob
     from momentum_compression_amd.state import LambState, OneBitGroup
     from workloads import configs as C
     from workloads import synth as S
@@ -182,17 +183,22 @@ def measure_lamb(steps: int, warmup: int) -> dict:
         grp.compress(m, t[0])
 
     def serv():
-        grp.server(t[0], decompress=True)
+        grp.server(t[0], decompress=False)
+
+    def dec():
+        ob.onebit_decompress(grp.sv_bits, grp.sv_scales, grp.mbar, N, n, seg_off=off_d,
+                             seg_k=k_d, n_seg=len(k))
 
     def lamb():
         st.step(grp.mbar, wl.lr, wl.eps, wl.beta1, wl.beta2, wl.r_threshold, wl.r_min, wl.r_max)
         t[0] += 1
 
-    ms = _time_calls([comp, serv, lamb], warmup, steps, stream)
+    ms = _time_calls([comp, serv, dec, lamb], warmup, steps, stream)
     out = {"workload": wl.name, "N": N, "workers": n, "layers": len(wl.segments),
            "compress_x_k": _row(ms[0], B_COMPRESS * n * N, n * N),
-           "server_and_decompress_div_k": _row(ms[1], (b_server(n) + B_DECOMPRESS) * N, N),
-           "lamb_step": _row(ms[2], B_LAMB_STEP * N, N)}
+           "server": _row(ms[1], b_server(n) * N, N),
+           "decompress_div_k": _row(ms[2], B_DECOMPRESS * N, N),
+           "lamb_step": _row(ms[3], B_LAMB_STEP * N, N)}
     del grp, st, m
     torch.cuda.empty_cache()
     return out

@@ -76,22 +76,29 @@ __global__ __launch_bounds__(kThreads) void int8_kernel(const float* __restrict_
     __shared__ float lds[kThreads / 64];
     constexpr int lanes = B / 4;
     const int64_t base = (int64_t)blockIdx.x * iters * kTile;
-    for (int it = 0; it < iters; ++it) {
+    // loads of all tiles first (memory-level parallelism), then the blocks
+    f4 gv[kMaxIters], ev[kMaxIters];
+#pragma unroll
+    for (int it = 0; it < kMaxIters; ++it) {
         const int64_t J = base + (int64_t)it * kTile + 4 * (int64_t)threadIdx.x;
-        if (base + (int64_t)it * kTile >= N) break;  // workgroup-uniform
-        const bool active = J < N;
-        f4 gv = {0.f, 0.f, 0.f, 0.f};
-        f4 ev = {0.f, 0.f, 0.f, 0.f};
-        if (active) {
-            gv = __builtin_nontemporal_load(reinterpret_cast<const f4*>(g + J));
-            if (EF) ev = *reinterpret_cast<const f4*>(err + J);
+        gv[it] = f4{0.f, 0.f, 0.f, 0.f};
+        ev[it] = f4{0.f, 0.f, 0.f, 0.f};
+        if (it < iters && J < N) {
+            gv[it] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(g + J));
+            if (EF) ev[it] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(err + J));
         }
-        float x[4] = {gv.x, gv.y, gv.z, gv.w};
+    }
+#pragma unroll
+    for (int it = 0; it < kMaxIters; ++it) {
+        if (it >= iters || base + (int64_t)it * kTile >= N) break;  // workgroup-uniform
+        const int64_t J = base + (int64_t)it * kTile + 4 * (int64_t)threadIdx.x;
+        const bool active = J < N;
+        float x[4] = {gv[it].x, gv[it].y, gv[it].z, gv[it].w};
         if (EF) {
-            x[0] = x[0] + ev.x;
-            x[1] = x[1] + ev.y;
-            x[2] = x[2] + ev.z;
-            x[3] = x[3] + ev.w;
+            x[0] = x[0] + ev[it].x;
+            x[1] = x[1] + ev[it].y;
+            x[2] = x[2] + ev[it].z;
+            x[3] = x[3] + ev[it].w;
         }
         float M = 0.0f;
 #pragma unroll

@@ -46,11 +46,6 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
         const int64_t gw = (cbase + g0) >> 5;             // its first word in a row
         const int64_t gwords = (end - g0 + 31) >> 5;      // words of this group inside the chunk
         __syncthreads();                                  // previous group done with `stage`
-        for (int q = threadIdx.x; q < n * kGroupWords; q += kThreads) {
-            const int i = q / kGroupWords;
-            const int w = q - i * kGroupWords;
-            stage[q] = (w < gwords) ? bits[(int64_t)i * wrow + gw + w] : 0u;
-        }
         f4 pv[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -58,6 +53,30 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
             pv[u] = f4{0.f, 0.f, 0.f, 0.f};
             if (!reset && it0 + u < iters && j < end)
                 pv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(ef + cbase + j));
+        }
+        // coalesced word loads, kStageBatch in flight per thread before the
+        // LDS writes; inverted so that a clear bit (negative value) becomes
+        // the set sign bit in the decode below
+        constexpr int kStageBatch = 4;
+        const int total = n * kGroupWords;
+        for (int q0 = threadIdx.x; q0 < total; q0 += kStageBatch * kThreads) {
+            uint32_t v[kStageBatch];
+            bool ok[kStageBatch];
+#pragma unroll
+            for (int r = 0; r < kStageBatch; ++r) {
+                // unconditional loads (an out-of-range slot reads word 0 and is
+                // discarded) so that no branch waits on a load before the next
+                const int q = q0 + r * kThreads;
+                const int i = q / kGroupWords;
+                const int w = q - i * kGroupWords;
+                ok[r] = q < total && w < gwords;
+                v[r] = bits[ok[r] ? (int64_t)i * wrow + gw + w : 0];
+            }
+#pragma unroll
+            for (int r = 0; r < kStageBatch; ++r) {
+                const int q = q0 + r * kThreads;
+                if (q < total) stage[q] = ok[r] ? ~v[r] : ~0u;
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -69,10 +88,15 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
             const int wl = u * kWordsPerTile + (threadIdx.x >> 3);  // this lane's word in the group
             float a[4] = {0.f, 0.f, 0.f, 0.f};
             for (int i = 0; i < n; ++i) {
-                const uint32_t word = stage[i * kGroupWords + wl] >> sh;
-                const float s = sc[i];
+                // inverted bit of element k becomes the sign of +s[i][c]
+                // (one bit-field extract, one shift-or, one add)
+                const uint32_t w = stage[i * kGroupWords + wl];
+                const uint32_t sb = __float_as_uint(sc[i]);  // scales are >= 0
 #pragma unroll
-                for (int k = 0; k < 4; ++k) a[k] = a[k] + (((word >> k) & 1u) ? s : -s);
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t b = (w >> (sh + k)) & 1u;
+                    a[k] = a[k] + __uint_as_float((b << 31) | sb);
+                }
             }
             const float p[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
             float g[4];
@@ -118,40 +142,56 @@ __global__ __launch_bounds__(kThreads) void decompress_kernel(
     const uint32_t* __restrict__ sv_bits, const float* __restrict__ S, float* __restrict__ out,
     const int64_t* __restrict__ seg_off, const float* __restrict__ seg_k, int32_t n_seg, int64_t N,
     int64_t L) {
-    const int64_t j0 = (int64_t)blockIdx.x * kMaxIters * kTile + 4 * (int64_t)threadIdx.x;
+    const int64_t wstart = (int64_t)blockIdx.x * kMaxIters * kTile;
+    const int64_t j0 = wstart + 4 * (int64_t)threadIdx.x;
     if (j0 >= N) return;
-    int seg = 0;
-    int64_t hi = 0;
-    float kv = 1.0f;
-    if (SEG) {
-        seg = find_segment(seg_off, n_seg, j0);
-        hi = seg_off[seg + 1];
-        kv = seg_k[seg];
-    }
     uint32_t words[kMaxIters];
 #pragma unroll
     for (int u = 0; u < kMaxIters; ++u) {
         const int64_t J = j0 + (int64_t)u * kTile;
         words[u] = J < N ? sv_bits[J >> 5] : 0u;
     }
+    int seg = 0;
+    int64_t hi = 0;
+    float kv = 1.0f;
+    if (SEG) {
+        // workgroup-uniform search, then a short walk to this thread's start
+        seg = find_segment(seg_off, n_seg, wstart);
+        hi = seg_off[seg + 1];
+        while (j0 >= hi && seg + 1 < n_seg) {
+            ++seg;
+            hi = seg_off[seg + 1];
+        }
+        kv = seg_k[seg];
+    }
+    // value of a set bit: S[c], or S[c] / k_l for the current (chunk, layer);
+    // a clear bit gives its negation (the quotient of -S is exactly -(S / k))
+    int64_t cur_c = -1;
+    float q = 0.0f;
 #pragma unroll
     for (int u = 0; u < kMaxIters; ++u) {
         const int64_t J = j0 + (int64_t)u * kTile;
         if (J >= N) break;
-        const float s = S[J / L];  // L is a multiple of 64, so the 4 elements share a chunk
+        const int64_t c = J / L;  // L is a multiple of 64, so the 4 elements share a chunk
+        if (c != cur_c) {
+            cur_c = c;
+            q = SEG ? S[c] / kv : S[c];
+        }
         const uint32_t word = words[u] >> (J & 31);
         float v[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            v[k] = ((word >> k) & 1u) ? s : -s;
             if (SEG) {
-                while (J + k >= hi && seg + 1 < n_seg) {
-                    ++seg;
-                    hi = seg_off[seg + 1];
-                    kv = seg_k[seg];
+                if (J + k >= hi && seg + 1 < n_seg) {
+                    while (J + k >= hi && seg + 1 < n_seg) {
+                        ++seg;
+                        hi = seg_off[seg + 1];
+                        kv = seg_k[seg];
+                    }
+                    q = S[c] / kv;
                 }
-                v[k] = v[k] / kv;
             }
+            v[k] = ((word >> k) & 1u) ? q : -q;
         }
         const f4 o = {v[0], v[1], v[2], v[3]};
         __builtin_nontemporal_store(o, reinterpret_cast<f4*>(out + J));

@@ -56,6 +56,8 @@ hipError_t launch_adam(float* x, const float* m, const float* v, int64_t N, floa
 }
 
 // ---------------------------------------------------------------- LAMB
+constexpr int kLambTiles = 4;  // tiles per workgroup in the LAMB pass (5 streams in flight)
+
 __global__ void fill_u32_kernel(uint32_t* p, int32_t n, uint32_t val) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = val;
@@ -74,36 +76,49 @@ __global__ __launch_bounds__(kThreads) void lamb_kernel(
     float* __restrict__ x, const float* __restrict__ m, const float* __restrict__ mp,
     float* __restrict__ vf, const float* __restrict__ v, const int64_t* __restrict__ seg_off,
     int32_t n_seg, const float* __restrict__ c_prev, uint32_t* __restrict__ keys, int64_t N,
-    int32_t iters, float lr, float eps, float beta1, float beta2) {
+    float c_lr, float c_eps, float c_beta1, float c_beta2) {
     __shared__ uint32_t red[kThreads / 64];
-    const int64_t wstart = (int64_t)blockIdx.x * iters * kTile;
-    int64_t wend = wstart + (int64_t)iters * kTile;
+    const float c_omb1 = 1.0f - c_beta1;
+    const float c_omb2 = 1.0f - c_beta2;
+    const int64_t wstart = (int64_t)blockIdx.x * kLambTiles * kTile;
+    int64_t wend = wstart + (int64_t)kLambTiles * kTile;
     if (wend > N) wend = N;
     // workgroup-uniform segment test
     const int seg0 = find_segment(seg_off, n_seg, wstart);
     const bool uniform = seg_off[seg0 + 1] >= wend;
-    const float omb1 = 1.0f - beta1;
-    const float omb2 = 1.0f - beta2;
 
     const int64_t j0 = wstart + 4 * (int64_t)threadIdx.x;
     int seg = uniform ? seg0 : find_segment(seg_off, n_seg, j0 < N ? j0 : N - 1);
     int64_t hi = seg_off[seg + 1];
-    float step = lr * c_prev[seg];
+    float step = c_lr * c_prev[seg];
     uint32_t kmax = 0;
-    for (int it = 0; it < iters; ++it) {
-        const int64_t j = j0 + (int64_t)it * kTile;
+    f4 mv[kLambTiles], pv[kLambTiles], fv[kLambTiles], vv[kLambTiles], xv[kLambTiles];
+#pragma unroll
+    for (int u = 0; u < kLambTiles; ++u) {
+        const int64_t j = j0 + (int64_t)u * kTile;
+        if (j < wend) {
+            mv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(m + j));
+            pv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(mp + j));
+            fv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(vf + j));
+            vv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(v + j));
+            if (UPDATE_X) xv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(x + j));
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kLambTiles; ++u) {
+        const int64_t j = j0 + (int64_t)u * kTile;
         if (j >= wend) break;
-        const f4 mv = *reinterpret_cast<const f4*>(m + j);
-        const f4 pv = __builtin_nontemporal_load(reinterpret_cast<const f4*>(mp + j));
-        const f4 fv = *reinterpret_cast<const f4*>(vf + j);
-        const f4 vv = __builtin_nontemporal_load(reinterpret_cast<const f4*>(v + j));
-        f4 xv = {0.f, 0.f, 0.f, 0.f};
-        if (UPDATE_X) xv = *reinterpret_cast<const f4*>(x + j);
-        const float ms[4] = {mv.x, mv.y, mv.z, mv.w};
-        const float ps[4] = {pv.x, pv.y, pv.z, pv.w};
-        const float fs[4] = {fv.x, fv.y, fv.z, fv.w};
-        const float vs[4] = {vv.x, vv.y, vv.z, vv.w};
-        float xs[4] = {xv.x, xv.y, xv.z, xv.w};
+        const float ms[4] = {mv[u].x, mv[u].y, mv[u].z, mv[u].w};
+        const float ps[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
+        const float fs[4] = {fv[u].x, fv[u].y, fv[u].z, fv[u].w};
+        const float vs[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+        float xs[4] = {0.f, 0.f, 0.f, 0.f};
+        if (UPDATE_X) {
+            xs[0] = xv[u].x;
+            xs[1] = xv[u].y;
+            xs[2] = xv[u].z;
+            xs[3] = xv[u].w;
+        }
         float nf[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -113,11 +128,11 @@ __global__ __launch_bounds__(kThreads) void lamb_kernel(
                     kmax = 0;
                     ++seg;
                     hi = seg_off[seg + 1];
-                    step = lr * c_prev[seg];
+                    step = c_lr * c_prev[seg];
                 }
             }
-            const float g = (ms[k] - beta1 * ps[k]) / omb1;
-            const float vn = beta2 * fs[k] + omb2 * (g * g);
+            const float g = (ms[k] - c_beta1 * ps[k]) / c_omb1;
+            const float vn = c_beta2 * fs[k] + c_omb2 * (g * g);
             nf[k] = vn;
             const float ratio = vs[k] / vn;
             if (ratio == ratio) {
@@ -125,16 +140,16 @@ __global__ __launch_bounds__(kThreads) void lamb_kernel(
                 kmax = key > kmax ? key : kmax;
             }
             if (UPDATE_X) {
-                const float den = sqrtf(vs[k]) + eps;
+                const float den = sqrtf(vs[k]) + c_eps;
                 const float upd = ms[k] / den;
                 xs[k] = xs[k] - step * upd;
             }
         }
         const f4 nv = {nf[0], nf[1], nf[2], nf[3]};
-        *reinterpret_cast<f4*>(vf + j) = nv;
+        __builtin_nontemporal_store(nv, reinterpret_cast<f4*>(vf + j));
         if (UPDATE_X) {
             const f4 xo = {xs[0], xs[1], xs[2], xs[3]};
-            *reinterpret_cast<f4*>(x + j) = xo;
+            __builtin_nontemporal_store(xo, reinterpret_cast<f4*>(x + j));
         }
     }
     if (uniform) {
@@ -205,25 +220,24 @@ __global__ __launch_bounds__(kThreads) void lamb_apply_kernel(
 }
 
 hipError_t launch_lamb(const onebit_frozen_v_args& a, uint32_t* keys, hipStream_t st) {
-    const int32_t iters = 8;
-    const int64_t tiles = (a.N + kTile - 1) / kTile;
-    const dim3 grid((unsigned)((tiles + iters - 1) / iters));
+    const int64_t per_wg = (int64_t)kLambTiles * kTile;
+    const dim3 grid((unsigned)((a.N + per_wg - 1) / per_wg));
     hipLaunchKernelGGL(fill_u32_kernel, dim3((a.n_seg + 255) / 256), dim3(256), 0, st, keys,
                        a.n_seg, 0u);
     if (a.use_c_t)
         hipLaunchKernelGGL(lamb_kernel<false>, grid, dim3(kThreads), 0, st, a.x, a.m, a.m_prev,
-                           a.v_fresh, a.v, a.seg_off, a.n_seg, a.c_prev, keys, a.N, iters, a.lr,
-                           a.eps, a.beta1, a.beta2);
+                           a.v_fresh, a.v, a.seg_off, a.n_seg, a.c_prev, keys, a.N, a.lr, a.eps,
+                           a.beta1, a.beta2);
     else
         hipLaunchKernelGGL(lamb_kernel<true>, grid, dim3(kThreads), 0, st, a.x, a.m, a.m_prev,
-                           a.v_fresh, a.v, a.seg_off, a.n_seg, a.c_prev, keys, a.N, iters, a.lr,
-                           a.eps, a.beta1, a.beta2);
+                           a.v_fresh, a.v, a.seg_off, a.n_seg, a.c_prev, keys, a.N, a.lr, a.eps,
+                           a.beta1, a.beta2);
     hipLaunchKernelGGL(lamb_finalize_kernel, dim3((a.n_seg + 255) / 256), dim3(256), 0, st, keys,
                        a.n_seg, a.c_avg, a.r_prev, a.c_prev, a.ratio_max, a.r_threshold, a.r_min,
                        a.r_max);
     if (a.use_c_t)
         hipLaunchKernelGGL(lamb_apply_kernel, grid, dim3(kThreads), 0, st, a.x, a.m, a.v,
-                           a.seg_off, a.n_seg, a.c_prev, a.N, iters, a.lr, a.eps);
+                           a.seg_off, a.n_seg, a.c_prev, a.N, (int32_t)kLambTiles, a.lr, a.eps);
     return hipGetLastError();
 }
 
