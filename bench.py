@@ -118,6 +118,8 @@ def cpu_baseline(wl, seed: int = 11):
     }
 
 
+B_COMPRESS_GRAD = 12.25        # g 4 + state 4 in + 4 out + 1/8 bit + 1/8 packed previous momentum
+B_ADAM_PACKED = 12.125         # x 4 in/out, v 4, 1/8 packed momentum
 B_LAMB_STEP = 28.0             # read x, m, m_prev, v_fresh, v_Tw; write x, v_fresh
 B_INT8 = 17.015625             # read g, err; write code, err, deq; scale per 256
 
@@ -200,6 +202,54 @@ def measure_lamb(steps: int, warmup: int) -> dict:
            "decompress_div_k": _row(ms[2], B_DECOMPRESS * N, N),
            "lamb_step": _row(ms[3], B_LAMB_STEP * N, N)}
     del grp, st, m
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_fused(steps: int, warmup: int) -> dict:
+    """The 1-bit Adam step fed with gradients on the 335M x 8 workload, with
+    the local momentum update fused into compression and the decompression
+    fused into the Adam step: compress_grad, server (no decompressed
+    buffer), Adam from the packed global momentum."""
+    import torch
+
+    from momentum_compression_amd.state import OneBitGroup
+    from workloads import configs as C
+    from workloads import synth as S
+
+    dev = torch.device("cuda:0")
+    wl = C.get("bert_large_335M_x8")
+    N, n = wl.N, wl.n
+    print(f"[bench] rows: fused {wl.name} N={N} n={n}", file=sys.stderr, flush=True)
+    sig = S.per_element(S.segment_sigmas(wl), wl, dev)
+    g = S.momentum(wl, 7, dev, sigma_elem=sig)  # gradient stand-in drawn with the same recipe
+    del sig
+    x = S.params(wl, dev)
+    v = S.frozen_variance(wl, dev)
+    grp = OneBitGroup(N, n, dev)
+    stream = torch.cuda.current_stream()
+    grp.compress_grad(g, 1, wl.beta1, first=True)
+    grp.server(1, first=True, decompress=False)
+    t = [2]
+
+    def comp():
+        grp.compress_grad(g, t[0], wl.beta1)
+
+    def serv():
+        grp.server(t[0], decompress=False)
+
+    def adam():
+        grp.adam_step_packed(x, v, wl.lr, wl.eps)
+        t[0] += 1
+
+    ms = _time_calls([comp, serv, adam], warmup, steps, stream)
+    step_ms = sum(ms)
+    out = {"workload": wl.name, "N": N, "workers": n, "step_ms": round(step_ms, 4),
+           "worker_elements_per_s": n * N / (step_ms * 1e-3),
+           "compress_grad": _row(ms[0], B_COMPRESS_GRAD * n * N, n * N),
+           "server": _row(ms[1], b_server(n) * N, N),
+           "adam_packed": _row(ms[2], B_ADAM_PACKED * N, N)}
+    del grp, g, x, v
     torch.cuda.empty_cache()
     return out
 
@@ -377,7 +427,8 @@ def main() -> int:
         del grp, m, x, v
         torch.cuda.empty_cache()
         out["rows"] = {"lamb": measure_lamb(max(3, args.steps // 2), 1),
-                       "int8": measure_int8(max(3, args.steps // 2), 1)}
+                       "int8": measure_int8(max(3, args.steps // 2), 1),
+                       "fused_adam_from_gradients": measure_fused(max(3, args.steps // 2), 1)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl)

@@ -122,6 +122,25 @@ int onebit_compress(const float* m, float* ef, float* scales, uint32_t* bits,
  * m_out   [N] float or NULL: decompressed global momentum
  * seg_off, seg_k, n_seg  as onebit_compress (applied as / k_l to m_out)
  */
+/*
+ * Worker side fed with gradients: the local momentum update fused into
+ * onebit_compress (1-bit Adam article, section 2.1: m_t = beta1 m_{t-1} +
+ * (1 - beta1) g_t, where m_{t-1} is the global momentum every worker
+ * decompressed in the previous step).  The previous global momentum is read
+ * packed, as the server left it: sign words mb_bits [N/32] and chunk scales
+ * mb_scales [n] (divided by k_l when a layer table is given).  Per element
+ *   mbar = (bit ? S[c] : -S[c]) [/ k_l]
+ *   m    = beta1 * mbar + (1 - beta1) * g        (1 - beta1 rounded once)
+ * and then exactly onebit_compress on m.  m is never written to memory.
+ * Pass the server's sv_bits / sv_scales of step t-1 before calling
+ * onebit_server_reduce for step t (a zero-filled pair means mbar = 0).
+ */
+int onebit_compress_grad(const float* g, const uint32_t* mb_bits, const float* mb_scales,
+                         float beta1, float* ef, float* scales, uint32_t* bits,
+                         int64_t N, int32_t n, float clip, int32_t reset,
+                         const int64_t* seg_off, const float* seg_k, int32_t n_seg,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
 int onebit_server_reduce(const uint32_t* bits, const float* scales, float* ef,
                          float* sv_scales, uint32_t* sv_bits, float* m_out,
                          const int64_t* seg_off, const float* seg_k, int32_t n_seg,
@@ -173,6 +192,12 @@ int lamb_layer_scale(float* buf, int64_t N, int32_t batch,
  *   new c (use_c_t != 0, which costs a second pass).  On return r_prev and
  *   c_prev hold r_t and c_t; ratio_max (optional) holds R (NaN: none).
  *   First compressed step: r_prev = 1, c_prev = c_avg, v_f = v.
+ *
+ * mode 2, Adam with the global momentum given packed (the decompression every
+ * worker performs, fused into the step): m is ignored and
+ *   mbar = m_bits bit ? m_scales[c] : -m_scales[c],  c = j / (N / m_chunks)
+ *   x = x - lr * (mbar / (sqrtf(v) + eps))
+ * m_bits [N/32], m_scales [m_chunks]; N a multiple of 64 * m_chunks.
  */
 typedef struct onebit_frozen_v_args {
     int32_t mode;          /* 0: Adam, 1: LAMB                                */
@@ -191,6 +216,9 @@ typedef struct onebit_frozen_v_args {
     float* r_prev;         /* LAMB: [n_seg] in r_{t-1}, out r_t               */
     float* c_prev;         /* LAMB: [n_seg] in c_{t-1}, out c_t               */
     float* ratio_max;      /* LAMB: [n_seg] out, or NULL                      */
+    const uint32_t* m_bits;/* mode 2: [N/32] packed global momentum           */
+    const float* m_scales; /* mode 2: [m_chunks] its chunk scales             */
+    int32_t m_chunks;      /* mode 2: number of chunks (server ranks)         */
 } onebit_frozen_v_args;
 
 int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes,

@@ -14,6 +14,7 @@ from .onebit import (  # noqa: F401
     int8_sr_quantize,
     lamb_layer_scale,
     onebit_compress,
+    onebit_compress_grad,
     onebit_decompress,
     onebit_error_materialize,
     onebit_server_reduce,

@@ -85,8 +85,39 @@ int onebit_compress(const float* m, float* ef, float* scales, uint32_t* bits, in
     if (sum_depth(plan) > 2048) return ONEBIT_E_SIZE;
     const bool clamp_on = clip > 0.0f && !isinf(clip);
     double* partials = static_cast<double*>(ws);
-    hipError_t e = launch_compress(m, ef, scales, bits, partials, N, n, plan, clip, clamp_on,
-                                   reset != 0, seg_off, seg_k, n_seg, stream);
+    CompressArgs a{m, ef, scales, bits, partials, N, n, clip, clamp_on, reset != 0,
+                   seg_off, seg_k, n_seg, nullptr, nullptr, 0.0f};
+    hipError_t e = launch_compress(a, plan, stream);
+    if (e != hipSuccess) return ONEBIT_E_HIP;
+    MeanTarget tgt{ef, N, n, scales};
+    return hip_status(launch_mean_finalize(partials, plan, (int64_t)n * n, tgt, stream));
+}
+
+int onebit_compress_grad(const float* g, const uint32_t* mb_bits, const float* mb_scales,
+                         float beta1, float* ef, float* scales, uint32_t* bits, int64_t N,
+                         int32_t n, float clip, int32_t reset, const int64_t* seg_off,
+                         const float* seg_k, int32_t n_seg, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+    int st = check_rows(N, n);
+    if (st) return st;
+    if (!g || !mb_bits || !mb_scales || !ef || !scales || !bits) return ONEBIT_E_NULL;
+    if ((st = check_segments(seg_off, seg_k, n_seg, true))) return st;
+    if (!aligned(g, 16) || !aligned(ef, 16) || !aligned(scales, 4) || !aligned(bits, 4) ||
+        !aligned(mb_bits, 4) || !aligned(mb_scales, 4))
+        return ONEBIT_E_ALIGN;
+    if (clip != clip || beta1 != beta1) return ONEBIT_E_ARG;
+    if (N == 0) return ONEBIT_OK;
+    const size_t need = onebit_workspace_bytes(N, n, n_seg);
+    if (!ws || ws_bytes < need) return ONEBIT_E_WORKSPACE;
+    if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
+
+    const ChunkPlan plan = make_plan(N / n, (int64_t)n * n);
+    if (sum_depth(plan) > 2048) return ONEBIT_E_SIZE;
+    const bool clamp_on = clip > 0.0f && !isinf(clip);
+    double* partials = static_cast<double*>(ws);
+    CompressArgs a{g, ef, scales, bits, partials, N, n, clip, clamp_on, reset != 0,
+                   seg_off, seg_k, n_seg, mb_bits, mb_scales, beta1};
+    hipError_t e = launch_compress(a, plan, stream);
     if (e != hipSuccess) return ONEBIT_E_HIP;
     MeanTarget tgt{ef, N, n, scales};
     return hip_status(launch_mean_finalize(partials, plan, (int64_t)n * n, tgt, stream));
@@ -161,11 +192,20 @@ int lamb_layer_scale(float* buf, int64_t N, int32_t batch, const int64_t* seg_of
 int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (!a) return ONEBIT_E_NULL;
     if (a->N < 0 || (a->N % 4)) return ONEBIT_E_SIZE;
-    if (!a->x || !a->m || !a->v) return ONEBIT_E_NULL;
+    if (!a->x || (!a->m && a->mode != 2) || !a->v) return ONEBIT_E_NULL;
     if (!aligned(a->x, 16) || !aligned(a->m, 16) || !aligned(a->v, 16)) return ONEBIT_E_ALIGN;
     if (a->mode == 0) {
         if (a->N == 0) return ONEBIT_OK;
         return hip_status(launch_adam(a->x, a->m, a->v, a->N, a->lr, a->eps, stream));
+    }
+    if (a->mode == 2) {
+        if (!a->m_bits || !a->m_scales) return ONEBIT_E_NULL;
+        if (a->m_chunks < 1 || a->m_chunks > kMaxWorkers || (a->N % (64 * (int64_t)a->m_chunks)))
+            return ONEBIT_E_SIZE;
+        if (!aligned(a->m_bits, 4) || !aligned(a->m_scales, 4)) return ONEBIT_E_ALIGN;
+        if (a->N == 0) return ONEBIT_OK;
+        return hip_status(launch_adam_packed(a->x, a->m_bits, a->m_scales, a->v, a->N, a->m_chunks,
+                                             a->lr, a->eps, stream));
     }
     if (a->mode != 1) return ONEBIT_E_ARG;
     if (!a->m_prev || !a->v_fresh || !a->seg_off || !a->c_avg || !a->r_prev || !a->c_prev)

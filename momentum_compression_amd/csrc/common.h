@@ -108,10 +108,26 @@ struct MeanTarget {
 hipError_t launch_mean_finalize(const double* partials, const ChunkPlan& plan, int64_t pairs,
                                 MeanTarget tgt, hipStream_t st);
 
-hipError_t launch_compress(const float* m, float* ef, const float* s_prev, uint32_t* bits,
-                           double* partials, int64_t N, int32_t n, const ChunkPlan& plan,
-                           float clip, bool clamp_on, bool reset, const int64_t* seg_off,
-                           const float* seg_k, int32_t n_seg, hipStream_t st);
+struct CompressArgs {
+    const float* m;          // momentum [n][N], or the gradient when mb_bits != nullptr
+    float* ef;               // error state [n][N]
+    const float* s_prev;     // [n][n] scales: read as the previous ones, rewritten later
+    uint32_t* bits;          // [n][N/32]
+    double* partials;        // workspace
+    int64_t N;
+    int32_t n;
+    float clip;
+    bool clamp_on;
+    bool reset;
+    const int64_t* seg_off;  // layer table or nullptr
+    const float* seg_k;
+    int32_t n_seg;
+    const uint32_t* mb_bits; // previous global momentum (server words) or nullptr
+    const float* mb_scales;  // its chunk scales [n]
+    float beta1;
+};
+
+hipError_t launch_compress(const CompressArgs& a, const ChunkPlan& plan, hipStream_t st);
 
 hipError_t launch_server(const uint32_t* bits, const float* scales, float* ef, const float* S_prev,
                          uint32_t* sv_bits, double* partials, int64_t N, int32_t n,
@@ -129,6 +145,10 @@ hipError_t launch_layer_scale(float* buf, int64_t N, int32_t batch, const int64_
 
 hipError_t launch_adam(float* x, const float* m, const float* v, int64_t N, float lr, float eps,
                        hipStream_t st);
+
+hipError_t launch_adam_packed(float* x, const uint32_t* mbits, const float* mscales,
+                              const float* v, int64_t N, int32_t chunks, float lr, float eps,
+                              hipStream_t st);
 
 hipError_t launch_lamb(const onebit_frozen_v_args& a, uint32_t* keys, hipStream_t st);
 

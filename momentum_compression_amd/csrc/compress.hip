@@ -7,6 +7,12 @@
 // and the chunk's sum of |g'| in fp64 as one partial per workgroup, which the
 // finalize kernel turns into the exactly rounded mean.
 //
+// With MOM the input is the worker's gradient instead of its momentum: the
+// local momentum m = beta1 mbar + (1 - beta1) g is formed on the fly from the
+// previous step's packed global momentum (server sign words and chunk
+// scales, divided by k_l in LAMB mode), so m is never written to memory
+// (1-bit Adam article, section 2.1, momentum recursion).
+//
 // Layout: workgroup w of chunk (i, c) streams tiles of 1024 consecutive
 // elements (float4 per lane, fully coalesced) of worker row i, chunk c.  The
 // 4 sign bits of a lane are merged over 8 lanes with DPP into one 32-bit
@@ -15,12 +21,13 @@
 
 namespace onebit {
 
-template <bool SEG, bool CLAMP, bool RESET>
+template <bool SEG, bool CLAMP, bool RESET, bool MOM>
 __global__ __launch_bounds__(kThreads) void compress_kernel(
     const float* __restrict__ m, float* __restrict__ ef, const float* __restrict__ s_prev,
     uint32_t* __restrict__ bits, double* __restrict__ partials, int64_t N, int32_t n,
     int64_t L, int32_t iters, int64_t bpc, float clip, const int64_t* __restrict__ seg_off,
-    const float* __restrict__ seg_k, int32_t n_seg) {
+    const float* __restrict__ seg_k, int32_t n_seg, const uint32_t* __restrict__ mb_bits,
+    const float* __restrict__ mb_scales, float beta1) {
     __shared__ double red[kThreads / 64];
     const int64_t pair = blockIdx.x / bpc;
     const int64_t wg = blockIdx.x - pair * bpc;
@@ -45,19 +52,28 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
         kv = seg_k[seg];
     }
 
+    // MOM: value of a set bit of the previous global momentum in this chunk
+    // (S[c], or S[c] / k_l in LAMB mode), recomputed when the layer changes
+    const float omb1 = 1.0f - beta1;
+    const float mS = MOM ? mb_scales[c] : 0.0f;
+    float mq = (MOM && SEG) ? mS / kv : mS;
+
     double acc = 0.0;
     for (int it0 = 0; it0 < iters; it0 += kUnroll) {
         // issue the loads of kUnroll tiles before any use (memory-level parallelism)
         f4 mv[kUnroll], pv[kUnroll];
+        uint32_t mw[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int64_t j = start + (int64_t)(it0 + u) * kTile + 4 * (int64_t)threadIdx.x;
             mv[u] = f4{0.f, 0.f, 0.f, 0.f};
             pv[u] = f4{0.f, 0.f, 0.f, 0.f};
+            mw[u] = 0u;
             if (it0 + u < iters && j < end) {
                 mv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(m + row + cbase + j));
                 if (!RESET)
                     pv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(ef + row + cbase + j));
+                if (MOM) mw[u] = mb_bits[(cbase + j) >> 5];
             }
         }
 #pragma unroll
@@ -67,17 +83,27 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
             const int64_t idx = row + cbase + j;
             float g[4] = {mv[u].x, mv[u].y, mv[u].z, mv[u].w};
             const float p[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
+            const uint32_t mword = mw[u] >> ((cbase + j) & 31);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 if (SEG) {
                     const int64_t J = cbase + j + k;
-                    while (active && J >= seg_hi && seg + 1 < n_seg) {
-                        ++seg;
-                        seg_hi = seg_off[seg + 1];
-                        kv = seg_k[seg];
+                    if (active && J >= seg_hi && seg + 1 < n_seg) {
+                        while (J >= seg_hi && seg + 1 < n_seg) {
+                            ++seg;
+                            seg_hi = seg_off[seg + 1];
+                            kv = seg_k[seg];
+                        }
+                        if (MOM) mq = mS / kv;
                     }
-                    g[k] = kv * g[k];
                 }
+                if (MOM) {
+                    const float mbar = ((mword >> k) & 1u) ? mq : -mq;
+                    const float a = beta1 * mbar;
+                    const float b = omb1 * g[k];
+                    g[k] = a + b;
+                }
+                if (SEG) g[k] = kv * g[k];
                 const float e = RESET ? 0.0f : ef_error(p[k], s);
                 float v = g[k] + e;
                 if (CLAMP) v = fminf(fmaxf(v, -clip), clip);
@@ -99,38 +125,34 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     if (threadIdx.x == 0) partials[blockIdx.x] = tot;
 }
 
-template <bool SEG, bool CLAMP, bool RESET>
-static void launch_t(dim3 grid, hipStream_t st, const float* m, float* ef, const float* s_prev,
-                     uint32_t* bits, double* partials, int64_t N, int32_t n, const ChunkPlan& p,
-                     float clip, const int64_t* seg_off, const float* seg_k, int32_t n_seg) {
-    hipLaunchKernelGGL((compress_kernel<SEG, CLAMP, RESET>), grid, dim3(kThreads), 0, st, m, ef,
-                       s_prev, bits, partials, N, n, p.L, p.iters, p.bpc, clip, seg_off, seg_k,
-                       n_seg);
+template <bool SEG, bool CLAMP, bool RESET, bool MOM>
+static void launch_t(dim3 grid, hipStream_t st, const CompressArgs& a, const ChunkPlan& p) {
+    hipLaunchKernelGGL((compress_kernel<SEG, CLAMP, RESET, MOM>), grid, dim3(kThreads), 0, st, a.m,
+                       a.ef, a.s_prev, a.bits, a.partials, a.N, a.n, p.L, p.iters, p.bpc, a.clip,
+                       a.seg_off, a.seg_k, a.n_seg, a.mb_bits, a.mb_scales, a.beta1);
 }
 
-hipError_t launch_compress(const float* m, float* ef, const float* s_prev, uint32_t* bits,
-                           double* partials, int64_t N, int32_t n, const ChunkPlan& plan,
-                           float clip, bool clamp_on, bool reset, const int64_t* seg_off,
-                           const float* seg_k, int32_t n_seg, hipStream_t st) {
-    const dim3 grid((unsigned)(plan.bpc * (int64_t)n * n));
-    const bool seg = seg_off != nullptr;
-    const int sel = (seg ? 4 : 0) | (clamp_on ? 2 : 0) | (reset ? 1 : 0);
-#define ONEBIT_CASE(S, C, R)                                                                    \
-    case (S ? 4 : 0) | (C ? 2 : 0) | (R ? 1 : 0):                                               \
-        launch_t<S, C, R>(grid, st, m, ef, s_prev, bits, partials, N, n, plan, clip, seg_off,  \
-                          seg_k, n_seg);                                                        \
-        break;
+template <bool SEG, bool CLAMP, bool RESET>
+static void launch_m(dim3 grid, hipStream_t st, const CompressArgs& a, const ChunkPlan& p) {
+    if (a.mb_bits)
+        launch_t<SEG, CLAMP, RESET, true>(grid, st, a, p);
+    else
+        launch_t<SEG, CLAMP, RESET, false>(grid, st, a, p);
+}
+
+hipError_t launch_compress(const CompressArgs& a, const ChunkPlan& plan, hipStream_t st) {
+    const dim3 grid((unsigned)(plan.bpc * (int64_t)a.n * a.n));
+    const int sel = (a.seg_off ? 4 : 0) | (a.clamp_on ? 2 : 0) | (a.reset ? 1 : 0);
     switch (sel) {
-        ONEBIT_CASE(false, false, false)
-        ONEBIT_CASE(false, false, true)
-        ONEBIT_CASE(false, true, false)
-        ONEBIT_CASE(false, true, true)
-        ONEBIT_CASE(true, false, false)
-        ONEBIT_CASE(true, false, true)
-        ONEBIT_CASE(true, true, false)
-        ONEBIT_CASE(true, true, true)
+        case 0: launch_m<false, false, false>(grid, st, a, plan); break;
+        case 1: launch_m<false, false, true>(grid, st, a, plan); break;
+        case 2: launch_m<false, true, false>(grid, st, a, plan); break;
+        case 3: launch_m<false, true, true>(grid, st, a, plan); break;
+        case 4: launch_m<true, false, false>(grid, st, a, plan); break;
+        case 5: launch_m<true, false, true>(grid, st, a, plan); break;
+        case 6: launch_m<true, true, false>(grid, st, a, plan); break;
+        default: launch_m<true, true, true>(grid, st, a, plan); break;
     }
-#undef ONEBIT_CASE
     return hipGetLastError();
 }
 

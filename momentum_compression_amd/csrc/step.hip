@@ -55,6 +55,53 @@ hipError_t launch_adam(float* x, const float* m, const float* v, int64_t N, floa
     return hipGetLastError();
 }
 
+// Adam with the global momentum read packed: sign words and chunk scales of
+// the server (the decompression every worker performs, fused into the step).
+__global__ __launch_bounds__(kThreads) void adam_packed_kernel(
+    float* __restrict__ x, const uint32_t* __restrict__ mbits, const float* __restrict__ mscales,
+    const float* __restrict__ v, int64_t N, int64_t L, float lr, float eps) {
+    const int64_t j0 = (int64_t)blockIdx.x * kMaxIters * kTile + 4 * (int64_t)threadIdx.x;
+    f4 xv[kMaxIters], vv[kMaxIters];
+    uint32_t w[kMaxIters];
+#pragma unroll
+    for (int u = 0; u < kMaxIters; ++u) {
+        const int64_t j = j0 + (int64_t)u * kTile;
+        if (j < N) {
+            xv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(x + j));
+            vv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(v + j));
+            w[u] = mbits[j >> 5];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kMaxIters; ++u) {
+        const int64_t j = j0 + (int64_t)u * kTile;
+        if (j >= N) break;
+        const float S = mscales[j / L];  // L is a multiple of 64: the 4 elements share a chunk
+        const uint32_t word = w[u] >> (j & 31);
+        const float xs[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+        const float vs[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+        float o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float m = ((word >> k) & 1u) ? S : -S;
+            const float den = sqrtf(vs[k]) + eps;
+            const float upd = m / den;
+            o[k] = xs[k] - lr * upd;
+        }
+        const f4 ov = {o[0], o[1], o[2], o[3]};
+        __builtin_nontemporal_store(ov, reinterpret_cast<f4*>(x + j));
+    }
+}
+
+hipError_t launch_adam_packed(float* x, const uint32_t* mbits, const float* mscales,
+                              const float* v, int64_t N, int32_t chunks, float lr, float eps,
+                              hipStream_t st) {
+    const int64_t per_wg = (int64_t)kMaxIters * kTile;
+    hipLaunchKernelGGL(adam_packed_kernel, dim3((unsigned)((N + per_wg - 1) / per_wg)),
+                       dim3(kThreads), 0, st, x, mbits, mscales, v, N, N / chunks, lr, eps);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- LAMB
 constexpr int kLambTiles = 4;  // tiles per workgroup in the LAMB pass (5 streams in flight)
 

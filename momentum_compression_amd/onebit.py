@@ -42,12 +42,15 @@ class FrozenVArgs(ctypes.Structure):
         ("x", _c_p), ("m", _c_p), ("v", _c_p), ("m_prev", _c_p), ("v_fresh", _c_p),
         ("seg_off", _c_p), ("c_avg", _c_p), ("r_prev", _c_p), ("c_prev", _c_p),
         ("ratio_max", _c_p),
+        ("m_bits", _c_p), ("m_scales", _c_p), ("m_chunks", _c_i32),
     ]
 
 
 _SIGNATURES = {
     "onebit_compress": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32, _c_f, _c_i32, _c_p, _c_p,
                                  _c_i32, _c_p, _c_sz, _c_p]),
+    "onebit_compress_grad": (_c_i32, [_c_p, _c_p, _c_p, _c_f, _c_p, _c_p, _c_p, _c_i64, _c_i32, _c_f,
+                                      _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_sz, _c_p]),
     "onebit_server_reduce": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i64,
                                       _c_i32, _c_i32, _c_p, _c_sz, _c_p]),
     "onebit_decompress": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i64, _c_i32, _c_p]),
@@ -136,6 +139,15 @@ def onebit_compress(m, ef, scales, bits, N: int, n: int, clip: float = 0.0, rese
         _stream(stream)))
 
 
+def onebit_compress_grad(g, mb_bits, mb_scales, beta1: float, ef, scales, bits, N: int, n: int,
+                         clip: float = 0.0, reset: bool = False, seg_off=None, seg_k=None,
+                         n_seg: int = 0, ws=None, stream=None) -> None:
+    _check("onebit_compress_grad", load().onebit_compress_grad(
+        _ptr(g), _ptr(mb_bits), _ptr(mb_scales), beta1, _ptr(ef), _ptr(scales), _ptr(bits), N, n,
+        clip, int(bool(reset)), _ptr(seg_off), _ptr(seg_k), n_seg, _ptr(ws),
+        _nbytes(ws) if ws is not None else 0, _stream(stream)))
+
+
 def onebit_server_reduce(bits, scales, ef, sv_scales, sv_bits, m_out, N: int, n: int,
                          reset: bool = False, seg_off=None, seg_k=None, n_seg: int = 0, ws=None,
                          stream=None) -> None:
@@ -166,13 +178,14 @@ def lamb_layer_scale(buf, N: int, batch: int, seg_off, seg_k, n_seg: int, divide
 def frozen_v_step(*, mode: int, N: int, x, m, v, lr: float, eps: float, beta1: float = 0.9,
                   beta2: float = 0.999, m_prev=None, v_fresh=None, seg_off=None, n_seg: int = 0,
                   c_avg=None, r_prev=None, c_prev=None, ratio_max=None, r_threshold: float = 0.1,
-                  r_min: float = 0.5, r_max: float = 4.0, use_c_t: bool = False, ws=None,
-                  stream=None) -> None:
+                  r_min: float = 0.5, r_max: float = 4.0, use_c_t: bool = False, m_bits=None,
+                  m_scales=None, m_chunks: int = 0, ws=None, stream=None) -> None:
     a = FrozenVArgs(mode=mode, use_c_t=int(bool(use_c_t)), N=N, lr=lr, eps=eps, beta1=beta1,
                     beta2=beta2, r_threshold=r_threshold, r_min=r_min, r_max=r_max, n_seg=n_seg,
                     x=_ptr(x), m=_ptr(m), v=_ptr(v), m_prev=_ptr(m_prev), v_fresh=_ptr(v_fresh),
                     seg_off=_ptr(seg_off), c_avg=_ptr(c_avg), r_prev=_ptr(r_prev),
-                    c_prev=_ptr(c_prev), ratio_max=_ptr(ratio_max))
+                    c_prev=_ptr(c_prev), ratio_max=_ptr(ratio_max), m_bits=_ptr(m_bits),
+                    m_scales=_ptr(m_scales), m_chunks=m_chunks)
     _check("frozen_v_step", load().frozen_v_step(
         ctypes.byref(a), _ptr(ws), _nbytes(ws) if ws is not None else 0, _stream(stream)))
 

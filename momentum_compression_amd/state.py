@@ -65,6 +65,15 @@ class OneBitGroup:
                            reset=first or self.is_reset(t), seg_off=self.seg_off, seg_k=self.seg_k,
                            n_seg=self.n_seg, ws=self.ws, stream=stream)
 
+    def compress_grad(self, g: torch.Tensor, t: int, beta1: float, first: bool = False,
+                      stream=None) -> None:
+        """Compress from gradients: each worker's momentum is formed from g and
+        the previous step's packed global momentum (sv_bits, sv_scales)."""
+        ob.onebit_compress_grad(g, self.sv_bits, self.sv_scales, beta1, self.ef, self.scales,
+                                self.bits, self.N, self.n, clip=self.clip,
+                                reset=first or self.is_reset(t), seg_off=self.seg_off,
+                                seg_k=self.seg_k, n_seg=self.n_seg, ws=self.ws, stream=stream)
+
     def server(self, t: int, first: bool = False, decompress: bool = True, stream=None) -> None:
         ob.onebit_server_reduce(self.bits, self.scales, self.sv_ef, self.sv_scales, self.sv_bits,
                                 self.mbar if decompress else None, self.N, self.n,
@@ -83,6 +92,13 @@ class OneBitGroup:
 
     def adam_step(self, x: torch.Tensor, v: torch.Tensor, lr: float, eps: float, stream=None) -> None:
         ob.frozen_v_step(mode=0, N=self.N, x=x, m=self.mbar, v=v, lr=lr, eps=eps, stream=stream)
+
+    def adam_step_packed(self, x: torch.Tensor, v: torch.Tensor, lr: float, eps: float,
+                         stream=None) -> None:
+        """Adam step reading the global momentum packed (server words and
+        scales), without the decompressed buffer."""
+        ob.frozen_v_step(mode=2, N=self.N, x=x, m=None, v=v, lr=lr, eps=eps, m_bits=self.sv_bits,
+                         m_scales=self.sv_scales, m_chunks=self.n, stream=stream)
 
 
 @dataclass

@@ -163,6 +163,18 @@ def decompress(sbits: np.ndarray, S: np.ndarray, k: Optional[np.ndarray] = None)
     return out
 
 
+def local_momentum(g: np.ndarray, mbar_prev: np.ndarray, beta1: float) -> np.ndarray:
+    """Each worker's momentum from its gradient and the previous global
+    momentum (1-bit Adam article, section 2.1: m_t = beta1 m_{t-1} +
+    (1 - beta1) g_t; the previous momentum is the decompressed global one,
+    identical on every worker): fl(fl(beta1 m) + fl((1 - beta1) g)) with
+    1 - beta1 rounded once.  g: [n, N]; mbar_prev: [N]."""
+    b1 = f32(beta1)
+    omb1 = f32(f32(1.0) - b1)
+    a = (b1 * np.asarray(mbar_prev, dtype=f32)).astype(f32)
+    return (a[None, :] + (omb1 * np.asarray(g, dtype=f32)).astype(f32)).astype(f32)
+
+
 def layer_scale(buf: np.ndarray, seg_off, k: np.ndarray, divide: bool) -> np.ndarray:
     """Segment-wise x * k_l (or x / k_l) over the last axis of ``buf``."""
     buf = np.asarray(buf, dtype=f32)

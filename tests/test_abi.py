@@ -78,16 +78,33 @@ def test_server_and_other_validation(lib):
     assert i8(None, None, P, P, None, 256, 256, 1, 1, None) == ob.ONEBIT_E_NULL
 
 
+def test_compress_grad_validation(lib):
+    f = lib.onebit_compress_grad
+    args = [P, P, P, 0.9, P, P, P, 1 << 12, 4, 0.0, 0, None, None, 0, P, 1 << 30, None]
+    bad = list(args); bad[1] = None
+    assert f(*bad) == ob.ONEBIT_E_NULL
+    bad = list(args); bad[3] = float("nan")
+    assert f(*bad) == ob.ONEBIT_E_ARG
+    bad = list(args); bad[0] = P + 4
+    assert f(*bad) == ob.ONEBIT_E_ALIGN
+    bad = list(args); bad[14] = None
+    assert f(*bad) == ob.ONEBIT_E_WORKSPACE
+
+
 def test_frozen_v_validation(lib):
     a = ob.FrozenVArgs(mode=0, N=1024, x=P, m=P, v=None, lr=1e-3, eps=1e-6)
     assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_NULL
-    a = ob.FrozenVArgs(mode=2, N=1024, x=P, m=P, v=P)
+    a = ob.FrozenVArgs(mode=3, N=1024, x=P, m=P, v=P)
     assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_ARG
     a = ob.FrozenVArgs(mode=1, N=1024, x=P, m=P, v=P, m_prev=P, v_fresh=P, seg_off=P, c_avg=P,
                        r_prev=P, c_prev=P, n_seg=4)
     assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_WORKSPACE
     a.n_seg = 0
     assert lib.frozen_v_step(ctypes.byref(a), P, 1 << 20, None) == ob.ONEBIT_E_ARG
+    a = ob.FrozenVArgs(mode=2, N=1024, x=P, m=None, v=P, m_bits=None, m_scales=P, m_chunks=4)
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_NULL
+    a = ob.FrozenVArgs(mode=2, N=1024 + 64, x=P, m=None, v=P, m_bits=P, m_scales=P, m_chunks=4)
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_SIZE
     a = ob.FrozenVArgs(mode=0, N=1022, x=P, m=P, v=P)
     assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_SIZE
     assert lib.frozen_v_step(None, None, 0, None) == ob.ONEBIT_E_NULL
@@ -98,4 +115,6 @@ def test_struct_layout_matches_header():
     assert ob.FrozenVArgs.N.offset == 8
     assert ob.FrozenVArgs.n_seg.offset == 44
     assert ob.FrozenVArgs.x.offset == 48
-    assert ctypes.sizeof(ob.FrozenVArgs) == 48 + 10 * 8
+    assert ob.FrozenVArgs.m_bits.offset == 128
+    assert ob.FrozenVArgs.m_chunks.offset == 144
+    assert ctypes.sizeof(ob.FrozenVArgs) == 152

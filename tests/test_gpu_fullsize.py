@@ -192,3 +192,51 @@ def test_int8_2_30_with_error_feedback():
         del q
     del err, codes, scales, deq, g
     _free()
+
+
+def test_bert_large_335M_x8_from_gradients():
+    """The fused path at full size: two steps of compress_grad + server +
+    packed Adam; sampled worker chunks free-running, server in lock-step."""
+    dev = device()
+    wl = C.get("bert_large_335M_x8")
+    N, n, L = wl.N, wl.n, wl.L
+    _need(dev, int(n * N * 4 * 2.2 + N * 4 * 6))
+    print(f"[fullsize] fused {wl.name}", flush=True)
+    sig = S.per_element(S.segment_sigmas(wl), wl, dev)
+    grp = OneBitGroup(N, n, dev)
+    x = S.params(wl, dev)
+    v = S.frozen_variance(wl, dev)
+    g = torch.empty((n, N), dtype=torch.float32, device=dev)
+    rng = np.random.default_rng(1)
+    idx = torch.from_numpy(np.sort(rng.choice(N, size=1 << 20, replace=False))).to(dev)
+    pairs, csrv = [(2, 6), (7, 1)], 6
+    e_w = {p: np.zeros(L, dtype=F32) for p in pairs}
+    E_c = np.zeros(L, dtype=F32)
+    mbar_prev = np.zeros(N, dtype=F32)
+    for t in (1, 2):
+        S.momentum(wl, 100 + t, dev, sigma_elem=sig, out=g)
+        first = t == 1
+        x_before = host(x[idx])
+        grp.compress_grad(g, t, wl.beta1, first=first)
+        grp.server(t, first=first, decompress=True)
+        grp.adam_step_packed(x, v, wl.lr, wl.eps)
+        torch.cuda.synchronize()
+        scales = host(grp.scales)
+        for (i, c) in pairs:
+            sl = slice(c * L, (c + 1) * L)
+            m = O.local_momentum(host(g[i, sl])[None, :], mbar_prev[sl], wl.beta1)
+            w = O.worker_compress(m, e_w[(i, c)][None, :], reset=first)
+            same_f32(np.array([scales[i, c]]), w["s"][0, :1], f"t={t} scale[{i},{c}]")
+            same_bits(host(grp.bits[i, _chunk_words(c, L)]), w["bits"][0], f"t={t} bits[{i},{c}]")
+            e_w[(i, c)] = w["e"][0]
+        sl = slice(csrv * L, (csrv + 1) * L)
+        r = O.server_chunk(host(grp.bits[:, _chunk_words(csrv, L)]), scales[:, csrv], E_c, reset=first)
+        same_f32(np.array([host(grp.sv_scales)[csrv]]), np.array([r["S"]]), f"t={t} server scale")
+        same_bits(host(grp.sv_bits[_chunk_words(csrv, L)]), r["bits"], f"t={t} server bits")
+        E_c = r["E"]
+        mbar_now = host(grp.mbar)
+        x_want = P.adam_frozen_step(x_before, mbar_now[host(idx)], host(v[idx]), wl.lr, wl.eps)
+        same_f32(host(x[idx]), x_want, f"t={t} parameters (sampled)")
+        mbar_prev = mbar_now.copy()
+    del grp, x, v, g, sig
+    _free()

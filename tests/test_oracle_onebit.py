@@ -274,3 +274,26 @@ def test_layer_scale_segments():
     k = np.array([2, 0.5, 4], dtype=F32)
     assert list(O.layer_scale(buf, off, k, False)) == [2, 4, 6, 2, 20, 24, 28, 32, 36, 40]
     assert list(O.layer_scale(buf, off, k, True)) == [0.5, 1, 1.5, 8, 1.25, 1.5, 1.75, 2, 2.25, 2.5]
+
+
+def test_local_momentum_closed_forms():
+    """beta1 = 0 gives the gradient; beta1 = 1/2 the exact midpoint on dyadic
+    inputs; beta1 = 0.9 matches the recursion within two roundings."""
+    rng = np.random.default_rng(23)
+    g = (rng.integers(-512, 512, size=(3, 256)) / 1024).astype(F32)
+    mb = (rng.integers(-512, 512, size=256) / 1024).astype(F32)
+    assert np.array_equal(O.local_momentum(g, mb, 0.0), g)
+    half = O.local_momentum(g, mb, 0.5)
+    for i in range(3):
+        for j in range(0, 256, 7):
+            assert frac(half[i, j]) == (frac(g[i, j]) + frac(mb[j])) / 2
+    g9 = _draw(rng, (2, 512))
+    mb9 = _draw(rng, (512,))
+    m9 = O.local_momentum(g9, mb9, 0.9)
+    b1 = Fraction(float(F32(0.9)))
+    for i in range(2):
+        for j in range(0, 512, 5):
+            exact = b1 * frac(mb9[j]) + (1 - b1) * frac(g9[i, j])
+            assert abs(frac(m9[i, j]) - exact) <= ulp(m9[i, j]) + ulp(F32(0.9) * mb9[j]) / 2 + \
+                ulp(F32(F32(1) - F32(0.9)) * g9[i, j]) / 2 + abs(frac(g9[i, j])) * (
+                    abs(Fraction(float(F32(1) - F32(0.9))) - (1 - b1)))
