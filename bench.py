@@ -277,9 +277,20 @@ def measure_int8(steps: int, warmup: int) -> dict:
         ob.int8_sr_quantize(g, err, codes, scales, deq, N, block, 4, step[0])
         step[0] += 1
 
-    ms = _time_calls([q], warmup, steps, stream)
+    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+
+    def rtn():
+        ob.int8_quantize(g, err, codes, scales, deq, N, block, 1, 4, 1, ws=ws)
+
+    def tensor_scale():
+        ob.int8_quantize(g, err, codes, scales, deq, N, 0, 0, 4, 1, ws=ws)
+
+    ms = _time_calls([q, rtn, tensor_scale], warmup, steps, stream)
     out = {"workload": "int8_sr_2^30", "N": N, "block": block,
-           "int8_sr_ef_deq": _row(ms[0], B_INT8 * N, N)}
+           "int8_sr_ef_deq": _row(ms[0], B_INT8 * N, N),
+           "int8_nearest_ef_deq": _row(ms[1], B_INT8 * N, N),
+           # one extra read pass of g and the error for the tensor maximum
+           "int8_sr_tensor_scale_ef_deq": _row(ms[2], (B_INT8 + 8.0) * N, N)}
     del g, err, codes, scales, deq
     torch.cuda.empty_cache()
     return out

@@ -141,11 +141,49 @@ int onebit_compress_grad(const float* g, const uint32_t* mb_bits, const float* m
                          const int64_t* seg_off, const float* seg_k, int32_t n_seg,
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Options of the extended calls.
+ * ONEBIT_UNIT_SCALE: the unscaled 1-bit sign of the 1-bit Adam article,
+ * section 2.1 (q = sign(g'), i.e. every chunk scale is 1; e = g' -+ 1), at
+ * the worker and, in onebit_server_reduce_ex, at the server.
+ */
+#define ONEBIT_UNIT_SCALE 1u
+
+/*
+ * onebit_compress and onebit_compress_grad in one call, plus the variants.
+ *   m         momentum [n][N], or the gradient when mb_bits != NULL
+ *             (mb_bits, mb_scales, beta1: as onebit_compress_grad)
+ *   seg_err_ratio [n_seg] or NULL: step-ratio-scaled error feedback of the
+ *             1-bit LAMB page (analysis paragraph): the carried error of an
+ *             element of layer l is multiplied by seg_err_ratio[l]
+ *             (c_{t-2} / c_{t-1}, as frozen_v_step's err_ratio writes it)
+ *             before it is added; needs seg_off / seg_k
+ *   flags     0 or ONEBIT_UNIT_SCALE
+ */
+int onebit_compress_ex(const float* m, const uint32_t* mb_bits, const float* mb_scales,
+                       float beta1, float* ef, float* scales, uint32_t* bits,
+                       int64_t N, int32_t n, float clip, int32_t reset,
+                       const int64_t* seg_off, const float* seg_k, const float* seg_err_ratio,
+                       int32_t n_seg, uint32_t flags, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
 int onebit_server_reduce(const uint32_t* bits, const float* scales, float* ef,
                          float* sv_scales, uint32_t* sv_bits, float* m_out,
                          const int64_t* seg_off, const float* seg_k, int32_t n_seg,
                          int64_t N, int32_t n, int32_t reset,
                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * onebit_server_reduce with the variants of onebit_compress_ex: the server
+ * error E is multiplied by seg_err_ratio[l] of its element's layer before it
+ * is added (NULL: no factor), and ONEBIT_UNIT_SCALE makes every S[c] = 1.
+ */
+int onebit_server_reduce_ex(const uint32_t* bits, const float* scales, float* ef,
+                            float* sv_scales, uint32_t* sv_bits, float* m_out,
+                            const int64_t* seg_off, const float* seg_k,
+                            const float* seg_err_ratio, int32_t n_seg, int64_t N, int32_t n,
+                            int32_t reset, uint32_t flags, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
 
 /*
  * Decompress only: m_out = (B ? S[c] : -S[c]) [/ k_l] from server words and
@@ -219,6 +257,8 @@ typedef struct onebit_frozen_v_args {
     const uint32_t* m_bits;/* mode 2: [N/32] packed global momentum           */
     const float* m_scales; /* mode 2: [m_chunks] its chunk scales             */
     int32_t m_chunks;      /* mode 2: number of chunks (server ranks)         */
+    float* err_ratio;      /* LAMB: [n_seg] out, or NULL: c_{t-1} / c_t, the  */
+                           /* factor for the next step's error feedback      */
 } onebit_frozen_v_args;
 
 int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes,
@@ -248,6 +288,19 @@ int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes,
 int int8_sr_quantize(const float* g, float* err, int8_t* codes, float* block_scales,
                      float* deq, int64_t N, int32_t block, uint64_t seed, uint32_t step,
                      hipStream_t stream);
+
+/*
+ * int8_sr_quantize with the variants of the tutorial's INT8 recipe:
+ *   block 0     one scale for the whole tensor (the PyTorch example's max
+ *               over the tensor; one extra read pass), needs ws >= 256 bytes
+ *   rounding 1  deterministic rounding to the nearest integer, halves away
+ *               from zero ("FP32 -> INT8" step 1), instead of stochastic (0)
+ * Otherwise as int8_sr_quantize (block 64 ... 1024; N a multiple of block
+ * and of 4).
+ */
+int int8_quantize(const float* g, float* err, int8_t* codes, float* block_scales, float* deq,
+                  int64_t N, int32_t block, int32_t rounding, uint64_t seed, uint32_t step,
+                  void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes needed by onebit_compress / onebit_server_reduce /
  * frozen_v_step for these sizes (0 if the sizes are invalid). */

@@ -11,12 +11,15 @@ from . import onebit  # noqa: F401
 from .onebit import (  # noqa: F401
     OnebitError,
     frozen_v_step,
+    int8_quantize,
     int8_sr_quantize,
     lamb_layer_scale,
     onebit_compress,
+    onebit_compress_ex,
     onebit_compress_grad,
     onebit_decompress,
     onebit_error_materialize,
     onebit_server_reduce,
+    onebit_server_reduce_ex,
     workspace_bytes,
 )

@@ -65,47 +65,22 @@ size_t onebit_workspace_bytes(int64_t N, int32_t n, int32_t n_seg) {
     return partial_bytes(N, n) + round_up((size_t)(n_seg > 0 ? n_seg : 1) * sizeof(uint32_t));
 }
 
-int onebit_compress(const float* m, float* ef, float* scales, uint32_t* bits, int64_t N, int32_t n,
-                    float clip, int32_t reset, const int64_t* seg_off, const float* seg_k,
-                    int32_t n_seg, void* ws, size_t ws_bytes, hipStream_t stream) {
+int onebit_compress_ex(const float* m, const uint32_t* mb_bits, const float* mb_scales, float beta1,
+                       float* ef, float* scales, uint32_t* bits, int64_t N, int32_t n, float clip,
+                       int32_t reset, const int64_t* seg_off, const float* seg_k,
+                       const float* seg_err_ratio, int32_t n_seg, uint32_t flags, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
     int st = check_rows(N, n);
     if (st) return st;
     if (!m || !ef || !scales || !bits) return ONEBIT_E_NULL;
+    if ((mb_bits == nullptr) != (mb_scales == nullptr)) return ONEBIT_E_NULL;
     if ((st = check_segments(seg_off, seg_k, n_seg, true))) return st;
-    if (!aligned(m, 16) || !aligned(ef, 16) || !aligned(scales, 4) || !aligned(bits, 4))
+    if (seg_err_ratio && !seg_off) return ONEBIT_E_ARG;
+    if (!aligned(m, 16) || !aligned(ef, 16) || !aligned(scales, 4) || !aligned(bits, 4) ||
+        (mb_bits && !aligned(mb_bits, 4)) || (mb_scales && !aligned(mb_scales, 4)) ||
+        (seg_err_ratio && !aligned(seg_err_ratio, 4)))
         return ONEBIT_E_ALIGN;
-    if (clip != clip) return ONEBIT_E_ARG;
-    if (N == 0) return ONEBIT_OK;
-    const size_t need = onebit_workspace_bytes(N, n, n_seg);
-    if (!ws || ws_bytes < need) return ONEBIT_E_WORKSPACE;
-    if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
-
-    const int64_t L = N / n;
-    const ChunkPlan plan = make_plan(L, (int64_t)n * n);
-    if (sum_depth(plan) > 2048) return ONEBIT_E_SIZE;
-    const bool clamp_on = clip > 0.0f && !isinf(clip);
-    double* partials = static_cast<double*>(ws);
-    CompressArgs a{m, ef, scales, bits, partials, N, n, clip, clamp_on, reset != 0,
-                   seg_off, seg_k, n_seg, nullptr, nullptr, 0.0f};
-    hipError_t e = launch_compress(a, plan, stream);
-    if (e != hipSuccess) return ONEBIT_E_HIP;
-    MeanTarget tgt{ef, N, n, scales};
-    return hip_status(launch_mean_finalize(partials, plan, (int64_t)n * n, tgt, stream));
-}
-
-int onebit_compress_grad(const float* g, const uint32_t* mb_bits, const float* mb_scales,
-                         float beta1, float* ef, float* scales, uint32_t* bits, int64_t N,
-                         int32_t n, float clip, int32_t reset, const int64_t* seg_off,
-                         const float* seg_k, int32_t n_seg, void* ws, size_t ws_bytes,
-                         hipStream_t stream) {
-    int st = check_rows(N, n);
-    if (st) return st;
-    if (!g || !mb_bits || !mb_scales || !ef || !scales || !bits) return ONEBIT_E_NULL;
-    if ((st = check_segments(seg_off, seg_k, n_seg, true))) return st;
-    if (!aligned(g, 16) || !aligned(ef, 16) || !aligned(scales, 4) || !aligned(bits, 4) ||
-        !aligned(mb_bits, 4) || !aligned(mb_scales, 4))
-        return ONEBIT_E_ALIGN;
-    if (clip != clip || beta1 != beta1) return ONEBIT_E_ARG;
+    if (clip != clip || beta1 != beta1 || (flags & ~ONEBIT_UNIT_SCALE)) return ONEBIT_E_ARG;
     if (N == 0) return ONEBIT_OK;
     const size_t need = onebit_workspace_bytes(N, n, n_seg);
     if (!ws || ws_bytes < need) return ONEBIT_E_WORKSPACE;
@@ -115,44 +90,73 @@ int onebit_compress_grad(const float* g, const uint32_t* mb_bits, const float* m
     if (sum_depth(plan) > 2048) return ONEBIT_E_SIZE;
     const bool clamp_on = clip > 0.0f && !isinf(clip);
     double* partials = static_cast<double*>(ws);
-    CompressArgs a{g, ef, scales, bits, partials, N, n, clip, clamp_on, reset != 0,
-                   seg_off, seg_k, n_seg, mb_bits, mb_scales, beta1};
+    CompressArgs a{m, ef, scales, bits, partials, N, n, clip, clamp_on, reset != 0,
+                   seg_off, seg_k, n_seg, mb_bits, mb_scales, beta1, seg_err_ratio};
     hipError_t e = launch_compress(a, plan, stream);
     if (e != hipSuccess) return ONEBIT_E_HIP;
-    MeanTarget tgt{ef, N, n, scales};
+    MeanTarget tgt{ef, N, n, scales, (flags & ONEBIT_UNIT_SCALE) != 0};
     return hip_status(launch_mean_finalize(partials, plan, (int64_t)n * n, tgt, stream));
 }
 
-int onebit_server_reduce(const uint32_t* bits, const float* scales, float* ef, float* sv_scales,
-                         uint32_t* sv_bits, float* m_out, const int64_t* seg_off,
-                         const float* seg_k, int32_t n_seg, int64_t N, int32_t n, int32_t reset,
-                         void* ws, size_t ws_bytes, hipStream_t stream) {
+int onebit_compress(const float* m, float* ef, float* scales, uint32_t* bits, int64_t N, int32_t n,
+                    float clip, int32_t reset, const int64_t* seg_off, const float* seg_k,
+                    int32_t n_seg, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return onebit_compress_ex(m, nullptr, nullptr, 0.0f, ef, scales, bits, N, n, clip, reset,
+                              seg_off, seg_k, nullptr, n_seg, 0u, ws, ws_bytes, stream);
+}
+
+int onebit_compress_grad(const float* g, const uint32_t* mb_bits, const float* mb_scales,
+                         float beta1, float* ef, float* scales, uint32_t* bits, int64_t N,
+                         int32_t n, float clip, int32_t reset, const int64_t* seg_off,
+                         const float* seg_k, int32_t n_seg, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+    if (!mb_bits || !mb_scales) return ONEBIT_E_NULL;
+    return onebit_compress_ex(g, mb_bits, mb_scales, beta1, ef, scales, bits, N, n, clip, reset,
+                              seg_off, seg_k, nullptr, n_seg, 0u, ws, ws_bytes, stream);
+}
+
+int onebit_server_reduce_ex(const uint32_t* bits, const float* scales, float* ef,
+                            float* sv_scales, uint32_t* sv_bits, float* m_out,
+                            const int64_t* seg_off, const float* seg_k,
+                            const float* seg_err_ratio, int32_t n_seg, int64_t N, int32_t n,
+                            int32_t reset, uint32_t flags, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
     int st = check_rows(N, n);
     if (st) return st;
     if (!bits || !scales || !ef || !sv_scales || !sv_bits) return ONEBIT_E_NULL;
     if ((st = check_segments(seg_off, seg_k, n_seg, true))) return st;
+    if (seg_err_ratio && !seg_off) return ONEBIT_E_ARG;
     if (!aligned(bits, 4) || !aligned(scales, 4) || !aligned(ef, 16) || !aligned(sv_scales, 4) ||
-        !aligned(sv_bits, 4) || (m_out && !aligned(m_out, 16)))
+        !aligned(sv_bits, 4) || (m_out && !aligned(m_out, 16)) ||
+        (seg_err_ratio && !aligned(seg_err_ratio, 4)))
         return ONEBIT_E_ALIGN;
+    if (flags & ~ONEBIT_UNIT_SCALE) return ONEBIT_E_ARG;
     if (N == 0) return ONEBIT_OK;
     const size_t need = onebit_workspace_bytes(N, n, n_seg);
     if (!ws || ws_bytes < need) return ONEBIT_E_WORKSPACE;
     if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
 
-    const int64_t L = N / n;
-    const ChunkPlan plan = make_plan(L, n);
+    const ChunkPlan plan = make_plan(N / n, n);
     if (sum_depth(plan) > 2048) return ONEBIT_E_SIZE;
     double* partials = static_cast<double*>(ws);
     hipError_t e = launch_server(bits, scales, ef, sv_scales, sv_bits, partials, N, n, plan,
-                                 reset != 0, stream);
+                                 reset != 0, seg_off, seg_err_ratio, n_seg, stream);
     if (e != hipSuccess) return ONEBIT_E_HIP;
-    MeanTarget tgt{ef, N, n, sv_scales};
+    MeanTarget tgt{ef, N, n, sv_scales, (flags & ONEBIT_UNIT_SCALE) != 0};
     e = launch_mean_finalize(partials, plan, n, tgt, stream);
     if (e != hipSuccess) return ONEBIT_E_HIP;
     if (m_out)
         return hip_status(
             launch_decompress(sv_bits, sv_scales, m_out, seg_off, seg_k, n_seg, N, n, stream));
     return ONEBIT_OK;
+}
+
+int onebit_server_reduce(const uint32_t* bits, const float* scales, float* ef, float* sv_scales,
+                         uint32_t* sv_bits, float* m_out, const int64_t* seg_off,
+                         const float* seg_k, int32_t n_seg, int64_t N, int32_t n, int32_t reset,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
+    return onebit_server_reduce_ex(bits, scales, ef, sv_scales, sv_bits, m_out, seg_off, seg_k,
+                                   nullptr, n_seg, N, n, reset, 0u, ws, ws_bytes, stream);
 }
 
 int onebit_decompress(const uint32_t* sv_bits, const float* sv_scales, float* m_out,
@@ -213,7 +217,7 @@ int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes, hipS
     if (a->n_seg < 1) return ONEBIT_E_ARG;
     if (!aligned(a->m_prev, 16) || !aligned(a->v_fresh, 16) || !aligned(a->seg_off, 8) ||
         !aligned(a->c_avg, 4) || !aligned(a->r_prev, 4) || !aligned(a->c_prev, 4) ||
-        (a->ratio_max && !aligned(a->ratio_max, 4)))
+        (a->ratio_max && !aligned(a->ratio_max, 4)) || (a->err_ratio && !aligned(a->err_ratio, 4)))
         return ONEBIT_E_ALIGN;
     if (a->N == 0) return ONEBIT_OK;
     const size_t need = round_up((size_t)a->n_seg * sizeof(uint32_t));
@@ -222,17 +226,31 @@ int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes, hipS
     return hip_status(launch_lamb(*a, static_cast<uint32_t*>(ws), stream));
 }
 
-int int8_sr_quantize(const float* g, float* err, int8_t* codes, float* block_scales, float* deq,
-                     int64_t N, int32_t block, uint64_t seed, uint32_t step, hipStream_t stream) {
-    if (block != 64 && block != 128 && block != 256 && block != 512 && block != 1024)
+int int8_quantize(const float* g, float* err, int8_t* codes, float* block_scales, float* deq,
+                  int64_t N, int32_t block, int32_t rounding, uint64_t seed, uint32_t step,
+                  void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (block != 0 && block != 64 && block != 128 && block != 256 && block != 512 && block != 1024)
         return ONEBIT_E_SIZE;
-    if (N < 0 || (N % block)) return ONEBIT_E_SIZE;
+    if (N < 0 || (N % 4) || (block && (N % block))) return ONEBIT_E_SIZE;
+    if (rounding != 0 && rounding != 1) return ONEBIT_E_ARG;
     if (!g || !codes || !block_scales) return ONEBIT_E_NULL;
     if (!aligned(g, 16) || (err && !aligned(err, 16)) || !aligned(codes, 4) ||
         !aligned(block_scales, 4) || (deq && !aligned(deq, 16)))
         return ONEBIT_E_ALIGN;
     if (N == 0) return ONEBIT_OK;
-    return hip_status(launch_int8(g, err, codes, block_scales, deq, N, block, seed, step, stream));
+    if (block == 0) {
+        if (!ws || ws_bytes < 256) return ONEBIT_E_WORKSPACE;
+        if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
+    }
+    return hip_status(launch_int8(g, err, codes, block_scales, deq, N, block, seed, step,
+                                  rounding == 1, static_cast<uint32_t*>(ws), stream));
+}
+
+int int8_sr_quantize(const float* g, float* err, int8_t* codes, float* block_scales, float* deq,
+                     int64_t N, int32_t block, uint64_t seed, uint32_t step, hipStream_t stream) {
+    if (block == 0) return ONEBIT_E_SIZE;  // the per-tensor variant needs a workspace
+    return int8_quantize(g, err, codes, block_scales, deq, N, block, 0, seed, step, nullptr, 0,
+                         stream);
 }
 
 }  // extern "C"

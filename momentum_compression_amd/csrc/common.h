@@ -103,6 +103,7 @@ struct MeanTarget {
     int64_t row_stride;  // elements between rows
     int32_t chunks;      // chunks per row (n)
     float* out;          // [rows * chunks] scales
+    bool unit;           // write 1 (the unscaled sign) instead of the mean
 };
 
 hipError_t launch_mean_finalize(const double* partials, const ChunkPlan& plan, int64_t pairs,
@@ -125,13 +126,15 @@ struct CompressArgs {
     const uint32_t* mb_bits; // previous global momentum (server words) or nullptr
     const float* mb_scales;  // its chunk scales [n]
     float beta1;
+    const float* seg_r;      // per-layer factor of the carried error, or nullptr
 };
 
 hipError_t launch_compress(const CompressArgs& a, const ChunkPlan& plan, hipStream_t st);
 
 hipError_t launch_server(const uint32_t* bits, const float* scales, float* ef, const float* S_prev,
                          uint32_t* sv_bits, double* partials, int64_t N, int32_t n,
-                         const ChunkPlan& plan, bool reset, hipStream_t st);
+                         const ChunkPlan& plan, bool reset, const int64_t* seg_off,
+                         const float* seg_r, int32_t n_seg, hipStream_t st);
 
 hipError_t launch_decompress(const uint32_t* sv_bits, const float* S, float* m_out,
                              const int64_t* seg_off, const float* seg_k, int32_t n_seg,
@@ -153,6 +156,7 @@ hipError_t launch_adam_packed(float* x, const uint32_t* mbits, const float* msca
 hipError_t launch_lamb(const onebit_frozen_v_args& a, uint32_t* keys, hipStream_t st);
 
 hipError_t launch_int8(const float* g, float* err, int8_t* codes, float* scales, float* deq,
-                       int64_t N, int32_t block, uint64_t seed, uint32_t step, hipStream_t st);
+                       int64_t N, int32_t block, uint64_t seed, uint32_t step, bool nearest,
+                       uint32_t* tensor_max, hipStream_t st);
 
 }  // namespace onebit

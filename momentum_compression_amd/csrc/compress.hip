@@ -21,13 +21,13 @@
 
 namespace onebit {
 
-template <bool SEG, bool CLAMP, bool RESET, bool MOM>
+template <bool SEG, bool CLAMP, bool RESET, bool MOM, bool ERS>
 __global__ __launch_bounds__(kThreads) void compress_kernel(
     const float* __restrict__ m, float* __restrict__ ef, const float* __restrict__ s_prev,
     uint32_t* __restrict__ bits, double* __restrict__ partials, int64_t N, int32_t n,
     int64_t L, int32_t iters, int64_t bpc, float clip, const int64_t* __restrict__ seg_off,
     const float* __restrict__ seg_k, int32_t n_seg, const uint32_t* __restrict__ mb_bits,
-    const float* __restrict__ mb_scales, float beta1) {
+    const float* __restrict__ mb_scales, float beta1, const float* __restrict__ seg_r) {
     __shared__ double red[kThreads / 64];
     const int64_t pair = blockIdx.x / bpc;
     const int64_t wg = blockIdx.x - pair * bpc;
@@ -45,11 +45,13 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     int seg = 0;
     int64_t seg_hi = 0;
     float kv = 1.0f;
+    float rv = 1.0f;  // ERS: step-ratio factor of the carried error in this layer
     if (SEG) {
         const int64_t J0 = cbase + start + 4 * (int64_t)threadIdx.x;
         seg = find_segment(seg_off, n_seg, J0 < N ? J0 : N - 1);
         seg_hi = seg_off[seg + 1];
         kv = seg_k[seg];
+        if (ERS) rv = seg_r[seg];
     }
 
     // MOM: value of a set bit of the previous global momentum in this chunk
@@ -93,6 +95,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
                             ++seg;
                             seg_hi = seg_off[seg + 1];
                             kv = seg_k[seg];
+                            if (ERS) rv = seg_r[seg];
                         }
                         if (MOM) mq = mS / kv;
                     }
@@ -104,7 +107,8 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
                     g[k] = a + b;
                 }
                 if (SEG) g[k] = kv * g[k];
-                const float e = RESET ? 0.0f : ef_error(p[k], s);
+                float e = RESET ? 0.0f : ef_error(p[k], s);
+                if (ERS) e = rv * e;
                 float v = g[k] + e;
                 if (CLAMP) v = fminf(fmaxf(v, -clip), clip);
                 g[k] = v;
@@ -125,19 +129,26 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     if (threadIdx.x == 0) partials[blockIdx.x] = tot;
 }
 
-template <bool SEG, bool CLAMP, bool RESET, bool MOM>
+template <bool SEG, bool CLAMP, bool RESET, bool MOM, bool ERS>
 static void launch_t(dim3 grid, hipStream_t st, const CompressArgs& a, const ChunkPlan& p) {
-    hipLaunchKernelGGL((compress_kernel<SEG, CLAMP, RESET, MOM>), grid, dim3(kThreads), 0, st, a.m,
-                       a.ef, a.s_prev, a.bits, a.partials, a.N, a.n, p.L, p.iters, p.bpc, a.clip,
-                       a.seg_off, a.seg_k, a.n_seg, a.mb_bits, a.mb_scales, a.beta1);
+    hipLaunchKernelGGL((compress_kernel<SEG, CLAMP, RESET, MOM, ERS>), grid, dim3(kThreads), 0, st,
+                       a.m, a.ef, a.s_prev, a.bits, a.partials, a.N, a.n, p.L, p.iters, p.bpc,
+                       a.clip, a.seg_off, a.seg_k, a.n_seg, a.mb_bits, a.mb_scales, a.beta1,
+                       a.seg_r);
 }
 
 template <bool SEG, bool CLAMP, bool RESET>
 static void launch_m(dim3 grid, hipStream_t st, const CompressArgs& a, const ChunkPlan& p) {
-    if (a.mb_bits)
-        launch_t<SEG, CLAMP, RESET, true>(grid, st, a, p);
-    else
-        launch_t<SEG, CLAMP, RESET, false>(grid, st, a, p);
+    // the step-ratio factor needs a layer table and a carried error
+    constexpr bool kErsPossible = SEG && !RESET;
+    const bool ers = kErsPossible && a.seg_r != nullptr;
+    if (a.mb_bits) {
+        if (ers) launch_t<SEG, CLAMP, RESET, true, kErsPossible>(grid, st, a, p);
+        else launch_t<SEG, CLAMP, RESET, true, false>(grid, st, a, p);
+    } else {
+        if (ers) launch_t<SEG, CLAMP, RESET, false, kErsPossible>(grid, st, a, p);
+        else launch_t<SEG, CLAMP, RESET, false, false>(grid, st, a, p);
+    }
 }
 
 hipError_t launch_compress(const CompressArgs& a, const ChunkPlan& plan, hipStream_t st) {

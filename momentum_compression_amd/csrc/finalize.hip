@@ -96,11 +96,15 @@ __device__ float exact_mean_from_bins(const unsigned long long* bins, uint64_t L
 
 __global__ __launch_bounds__(kThreads) void mean_finalize_kernel(
     const double* __restrict__ partials, int64_t bpc, int64_t L, const float* __restrict__ data,
-    int64_t row_stride, int32_t chunks, float* __restrict__ out) {
+    int64_t row_stride, int32_t chunks, float* __restrict__ out, int32_t unit) {
     __shared__ double red[kThreads / 64];
     __shared__ unsigned long long bins[256];
     __shared__ int exact;
     const int64_t pair = blockIdx.x;
+    if (unit) {  // the unscaled sign: every scale is 1
+        if (threadIdx.x == 0) out[pair] = 1.0f;
+        return;
+    }
     const double* p = partials + pair * bpc;
     double acc = 0.0;
     for (int64_t k = threadIdx.x; k < bpc; k += kThreads) acc += p[k];
@@ -147,7 +151,8 @@ __global__ __launch_bounds__(kThreads) void mean_finalize_kernel(
 hipError_t launch_mean_finalize(const double* partials, const ChunkPlan& plan, int64_t pairs,
                                 MeanTarget tgt, hipStream_t st) {
     hipLaunchKernelGGL(mean_finalize_kernel, dim3((unsigned)pairs), dim3(kThreads), 0, st,
-                       partials, plan.bpc, plan.L, tgt.data, tgt.row_stride, tgt.chunks, tgt.out);
+                       partials, plan.bpc, plan.L, tgt.data, tgt.row_stride, tgt.chunks, tgt.out,
+                       tgt.unit ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -65,16 +65,22 @@ __device__ __forceinline__ float group_max(float v, float* lds) {
 
 }  // namespace
 
-template <int B, bool EF, bool DEQ>
+// B = 0: one scale for the whole tensor, from the maximum a previous kernel
+// left in *tensor_max (bit pattern of a non-negative float).
+// NEAREST: round to the nearest integer, halves away from zero, instead of
+// the stochastic draw.
+template <int B, bool EF, bool DEQ, bool NEAREST>
 __global__ __launch_bounds__(kThreads) void int8_kernel(const float* __restrict__ g,
                                                        float* __restrict__ err,
                                                        int8_t* __restrict__ codes,
                                                        float* __restrict__ scales,
                                                        float* __restrict__ deq, int64_t N,
                                                        int32_t iters, uint32_t k0, uint32_t k1,
-                                                       uint32_t step) {
+                                                       uint32_t step,
+                                                       const uint32_t* __restrict__ tensor_max) {
     __shared__ float lds[kThreads / 64];
-    constexpr int lanes = B / 4;
+    constexpr int lanes = B == 0 ? 64 : B / 4;
+    const float Mt = B == 0 ? __uint_as_float(*tensor_max) : 0.0f;
     const int64_t base = (int64_t)blockIdx.x * iters * kTile;
     // loads of all tiles first (memory-level parallelism), then the blocks
     f4 gv[kMaxIters], ev[kMaxIters];
@@ -100,16 +106,24 @@ __global__ __launch_bounds__(kThreads) void int8_kernel(const float* __restrict_
             x[2] = x[2] + ev[it].z;
             x[3] = x[3] + ev[it].w;
         }
-        float M = 0.0f;
+        float M = Mt;
+        if constexpr (B != 0) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) M = fmaxf(M, fabsf(x[k]));
-        M = group_max<B>(M, lds);
+            for (int k = 0; k < 4; ++k) M = fmaxf(M, fabsf(x[k]));
+            M = group_max<B>(M, lds);
+        }
         const float scale = M / 127.0f;
 
-        uint32_t c0 = (uint32_t)((uint64_t)J >> 2), c1 = (uint32_t)((uint64_t)J >> 34), c2 = step,
-                 c3 = 0;
-        philox10(c0, c1, c2, c3, k0, k1);
-        const uint32_t w[4] = {c0, c1, c2, c3};
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        if constexpr (!NEAREST) {
+            uint32_t c0 = (uint32_t)((uint64_t)J >> 2), c1 = (uint32_t)((uint64_t)J >> 34),
+                     c2 = step, c3 = 0;
+            philox10(c0, c1, c2, c3, k0, k1);
+            w[0] = c0;
+            w[1] = c1;
+            w[2] = c2;
+            w[3] = c3;
+        }
 
         float q[4], d[4], e[4];
 #pragma unroll
@@ -119,10 +133,15 @@ __global__ __launch_bounds__(kThreads) void int8_kernel(const float* __restrict_
                 d[k] = 0.0f;
             } else {
                 const float xs = x[k] / scale;
-                const float f = floorf(xs);
-                const float p = xs - f;
-                const float u = (float)(w[k] >> 8) * 0x1p-24f;
-                float qq = f + (u < p ? 1.0f : 0.0f);
+                float qq;
+                if constexpr (NEAREST) {
+                    qq = roundf(xs);
+                } else {
+                    const float f = floorf(xs);
+                    const float p = xs - f;
+                    const float u = (float)(w[k] >> 8) * 0x1p-24f;
+                    qq = f + (u < p ? 1.0f : 0.0f);
+                }
                 qq = fminf(fmaxf(qq, -127.0f), 127.0f);
                 q[k] = qq;
                 d[k] = qq * scale;
@@ -143,44 +162,105 @@ __global__ __launch_bounds__(kThreads) void int8_kernel(const float* __restrict_
                 const f4 dq = {d[0], d[1], d[2], d[3]};
                 __builtin_nontemporal_store(dq, reinterpret_cast<f4*>(deq + J));
             }
-            if ((threadIdx.x % lanes) == 0) scales[J / B] = scale;
+            if constexpr (B == 0) {
+                if (J == 0) scales[0] = scale;
+            } else if ((threadIdx.x % lanes) == 0) {
+                scales[J / B] = scale;
+            }
         }
     }
 }
 
-template <int B>
-static void launch_b(dim3 grid, hipStream_t st, const float* g, float* err, int8_t* codes,
-                     float* scales, float* deq, int64_t N, int32_t iters, uint32_t k0, uint32_t k1,
-                     uint32_t step) {
-    if (err && deq)
-        hipLaunchKernelGGL((int8_kernel<B, true, true>), grid, dim3(kThreads), 0, st, g, err, codes,
-                           scales, deq, N, iters, k0, k1, step);
-    else if (err)
-        hipLaunchKernelGGL((int8_kernel<B, true, false>), grid, dim3(kThreads), 0, st, g, err,
-                           codes, scales, deq, N, iters, k0, k1, step);
-    else if (deq)
-        hipLaunchKernelGGL((int8_kernel<B, false, true>), grid, dim3(kThreads), 0, st, g, err,
-                           codes, scales, deq, N, iters, k0, k1, step);
-    else
-        hipLaunchKernelGGL((int8_kernel<B, false, false>), grid, dim3(kThreads), 0, st, g, err,
-                           codes, scales, deq, N, iters, k0, k1, step);
+// max over the tensor of |g (+ err)| (NaN skipped) as the bit pattern of a
+// non-negative float, accumulated with one atomicMax per workgroup
+__global__ __launch_bounds__(kThreads) void tensor_absmax_kernel(const float* __restrict__ g,
+                                                                const float* __restrict__ err,
+                                                                int64_t N, int32_t iters,
+                                                                uint32_t* __restrict__ out) {
+    __shared__ uint32_t red[kThreads / 64];
+    const int64_t base = (int64_t)blockIdx.x * iters * kTile;
+    float M = 0.0f;
+    for (int it = 0; it < iters; ++it) {
+        const int64_t J = base + (int64_t)it * kTile + 4 * (int64_t)threadIdx.x;
+        if (J < N) {
+            f4 gv = __builtin_nontemporal_load(reinterpret_cast<const f4*>(g + J));
+            if (err) {
+                const f4 ev = *reinterpret_cast<const f4*>(err + J);
+                gv = f4{gv.x + ev.x, gv.y + ev.y, gv.z + ev.z, gv.w + ev.w};
+            }
+            M = fmaxf(M, fabsf(gv.x));
+            M = fmaxf(M, fabsf(gv.y));
+            M = fmaxf(M, fabsf(gv.z));
+            M = fmaxf(M, fabsf(gv.w));
+        }
+    }
+    uint32_t u = __float_as_uint(M);  // non-negative: integer order is value order
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)u, off, 64);
+        u = o > u ? o : u;
+    }
+    if (lane_id() == 0) red[threadIdx.x >> 6] = u;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t b = red[0];
+        for (int w = 1; w < kThreads / 64; ++w) b = red[w] > b ? red[w] : b;
+        atomicMax(out, b);
+    }
 }
 
-hipError_t launch_int8(const float* g, float* err, int8_t* codes, float* scales, float* deq,
-                       int64_t N, int32_t block, uint64_t seed, uint32_t step, hipStream_t st) {
-    const int32_t iters = 4;
-    const int64_t tiles = (N + kTile - 1) / kTile;
-    const dim3 grid((unsigned)((tiles + iters - 1) / iters));
-    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+__global__ void zero_u32_kernel(uint32_t* p) { *p = 0u; }
+
+template <int B, bool NEAREST>
+static void launch_b(dim3 grid, hipStream_t st, const float* g, float* err, int8_t* codes,
+                     float* scales, float* deq, int64_t N, int32_t iters, uint32_t k0, uint32_t k1,
+                     uint32_t step, const uint32_t* tmax) {
+    if (err && deq)
+        hipLaunchKernelGGL((int8_kernel<B, true, true, NEAREST>), grid, dim3(kThreads), 0, st, g,
+                           err, codes, scales, deq, N, iters, k0, k1, step, tmax);
+    else if (err)
+        hipLaunchKernelGGL((int8_kernel<B, true, false, NEAREST>), grid, dim3(kThreads), 0, st, g,
+                           err, codes, scales, deq, N, iters, k0, k1, step, tmax);
+    else if (deq)
+        hipLaunchKernelGGL((int8_kernel<B, false, true, NEAREST>), grid, dim3(kThreads), 0, st, g,
+                           err, codes, scales, deq, N, iters, k0, k1, step, tmax);
+    else
+        hipLaunchKernelGGL((int8_kernel<B, false, false, NEAREST>), grid, dim3(kThreads), 0, st, g,
+                           err, codes, scales, deq, N, iters, k0, k1, step, tmax);
+}
+
+template <bool NEAREST>
+static hipError_t launch_r(dim3 grid, hipStream_t st, const float* g, float* err, int8_t* codes,
+                           float* scales, float* deq, int64_t N, int32_t block, int32_t iters,
+                           uint32_t k0, uint32_t k1, uint32_t step, uint32_t* tmax) {
     switch (block) {
-        case 64: launch_b<64>(grid, st, g, err, codes, scales, deq, N, iters, k0, k1, step); break;
-        case 128: launch_b<128>(grid, st, g, err, codes, scales, deq, N, iters, k0, k1, step); break;
-        case 256: launch_b<256>(grid, st, g, err, codes, scales, deq, N, iters, k0, k1, step); break;
-        case 512: launch_b<512>(grid, st, g, err, codes, scales, deq, N, iters, k0, k1, step); break;
-        case 1024: launch_b<1024>(grid, st, g, err, codes, scales, deq, N, iters, k0, k1, step); break;
+        case 0:
+            hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, st, tmax);
+            hipLaunchKernelGGL(tensor_absmax_kernel, grid, dim3(kThreads), 0, st, g, err, N, iters,
+                               tmax);
+            launch_b<0, NEAREST>(grid, st, g, err, codes, scales, deq, N, iters, k0, k1, step, tmax);
+            break;
+        case 64: launch_b<64, NEAREST>(grid, st, g, err, codes, scales, deq, N, iters, k0, k1, step, tmax); break;
+        case 128: launch_b<128, NEAREST>(grid, st, g, err, codes, scales, deq, N, iters, k0, k1, step, tmax); break;
+        case 256: launch_b<256, NEAREST>(grid, st, g, err, codes, scales, deq, N, iters, k0, k1, step, tmax); break;
+        case 512: launch_b<512, NEAREST>(grid, st, g, err, codes, scales, deq, N, iters, k0, k1, step, tmax); break;
+        case 1024: launch_b<1024, NEAREST>(grid, st, g, err, codes, scales, deq, N, iters, k0, k1, step, tmax); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_int8(const float* g, float* err, int8_t* codes, float* scales, float* deq,
+                       int64_t N, int32_t block, uint64_t seed, uint32_t step, bool nearest,
+                       uint32_t* tensor_max, hipStream_t st) {
+    const int32_t iters = kMaxIters;
+    const int64_t tiles = (N + kTile - 1) / kTile;
+    const dim3 grid((unsigned)((tiles + iters - 1) / iters));
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    if (nearest)
+        return launch_r<true>(grid, st, g, err, codes, scales, deq, N, block, iters, k0, k1, step,
+                              tensor_max);
+    return launch_r<false>(grid, st, g, err, codes, scales, deq, N, block, iters, k0, k1, step,
+                           tensor_max);
 }
 
 }  // namespace onebit

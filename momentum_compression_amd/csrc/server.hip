@@ -18,11 +18,13 @@ namespace onebit {
 // Words of the kUnroll tiles a workgroup processes together, for every
 // worker, are staged through LDS with coalesced loads (32 consecutive words
 // per worker and tile); each lane then reads its word per worker from LDS.
+template <bool ERS>
 __global__ __launch_bounds__(kThreads) void server_kernel(
     const uint32_t* __restrict__ bits, const float* __restrict__ scales, float* __restrict__ ef,
     const float* __restrict__ S_prev, uint32_t* __restrict__ sv_bits, double* __restrict__ partials,
     int64_t N, int32_t n, int64_t L, int32_t iters, int64_t bpc, int32_t reset, int32_t pow2,
-    float inv_n) {
+    float inv_n, const int64_t* __restrict__ seg_off, const float* __restrict__ seg_r,
+    int32_t n_seg) {
     constexpr int kWordsPerTile = kTile / 32;              // 32
     constexpr int kGroupWords = kWordsPerTile * kUnroll;   // 128 words per worker per group
     __shared__ double red[kThreads / 64];
@@ -39,6 +41,20 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
     const float nf = (float)n;
     const int64_t wrow = N >> 5;  // words per worker row
     const int lane8 = lane_id() & 7;
+    // ERS: step-ratio factor of the carried error, per layer (segment walk)
+    int seg = 0;
+    int64_t seg_hi = 0;
+    float rv = 1.0f;
+    if (ERS) {
+        const int64_t j0 = cbase + start + 4 * (int64_t)threadIdx.x;
+        seg = find_segment(seg_off, n_seg, cbase + start);
+        seg_hi = seg_off[seg + 1];
+        while (j0 >= seg_hi && seg + 1 < n_seg) {
+            ++seg;
+            seg_hi = seg_off[seg + 1];
+        }
+        rv = seg_r[seg];
+    }
 
     double acc = 0.0;
     for (int it0 = 0; it0 < iters; it0 += kUnroll) {
@@ -103,7 +119,17 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const float avg = pow2 ? a[k] * inv_n : a[k] / nf;
-                const float e = reset ? 0.0f : ef_error(p[k], S);
+                float e = reset ? 0.0f : ef_error(p[k], S);
+                if (ERS) {
+                    if (active && J + k >= seg_hi && seg + 1 < n_seg) {
+                        while (J + k >= seg_hi && seg + 1 < n_seg) {
+                            ++seg;
+                            seg_hi = seg_off[seg + 1];
+                        }
+                        rv = seg_r[seg];
+                    }
+                    e = rv * e;
+                }
                 g[k] = avg + e;
             }
             const uint32_t word = or8(sign_nibble(g[0], g[1], g[2], g[3]) << (4 * lane8));
@@ -124,13 +150,20 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
 
 hipError_t launch_server(const uint32_t* bits, const float* scales, float* ef, const float* S_prev,
                          uint32_t* sv_bits, double* partials, int64_t N, int32_t n,
-                         const ChunkPlan& plan, bool reset, hipStream_t st) {
+                         const ChunkPlan& plan, bool reset, const int64_t* seg_off,
+                         const float* seg_r, int32_t n_seg, hipStream_t st) {
     const bool pow2 = (n & (n - 1)) == 0;
     const float inv_n = 1.0f / (float)n;  // exact for powers of two
     const size_t lds = (size_t)n * (kTile / 32) * kUnroll * sizeof(uint32_t);
-    hipLaunchKernelGGL(server_kernel, dim3((unsigned)(plan.bpc * n)), dim3(kThreads), lds, st, bits,
-                       scales, ef, S_prev, sv_bits, partials, N, n, plan.L, plan.iters, plan.bpc,
-                       reset ? 1 : 0, pow2 ? 1 : 0, inv_n);
+    const dim3 grid((unsigned)(plan.bpc * n));
+    if (seg_r && seg_off && !reset)
+        hipLaunchKernelGGL(server_kernel<true>, grid, dim3(kThreads), lds, st, bits, scales, ef,
+                           S_prev, sv_bits, partials, N, n, plan.L, plan.iters, plan.bpc, 0,
+                           pow2 ? 1 : 0, inv_n, seg_off, seg_r, n_seg);
+    else
+        hipLaunchKernelGGL(server_kernel<false>, grid, dim3(kThreads), lds, st, bits, scales, ef,
+                           S_prev, sv_bits, partials, N, n, plan.L, plan.iters, plan.bpc,
+                           reset ? 1 : 0, pow2 ? 1 : 0, inv_n, seg_off, seg_r, n_seg);
     return hipGetLastError();
 }
 

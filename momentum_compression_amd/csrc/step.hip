@@ -216,7 +216,8 @@ __global__ __launch_bounds__(kThreads) void lamb_kernel(
 __global__ void lamb_finalize_kernel(const uint32_t* __restrict__ keys, int32_t n_seg,
                                      const float* __restrict__ c_avg, float* __restrict__ r_prev,
                                      float* __restrict__ c_prev, float* __restrict__ ratio_max,
-                                     float thr, float r_min, float r_max) {
+                                     float* __restrict__ err_ratio, float thr, float r_min,
+                                     float r_max) {
     const int l = blockIdx.x * blockDim.x + threadIdx.x;
     if (l >= n_seg) return;
     const uint32_t key = keys[l];
@@ -227,8 +228,10 @@ __global__ void lamb_finalize_kernel(const uint32_t* __restrict__ keys, int32_t 
     const float hi = (1.0f + thr) * rp;
     float r = fminf(fmaxf(Rv, lo), hi);
     r = fminf(fmaxf(r, r_min), r_max);
+    const float c = c_avg[l] * r;
+    if (err_ratio) err_ratio[l] = c_prev[l] / c;  // c_{t-1} / c_t for the next error feedback
     r_prev[l] = r;
-    c_prev[l] = c_avg[l] * r;
+    c_prev[l] = c;
     if (ratio_max) ratio_max[l] = R;
 }
 
@@ -280,8 +283,8 @@ hipError_t launch_lamb(const onebit_frozen_v_args& a, uint32_t* keys, hipStream_
                            a.v_fresh, a.v, a.seg_off, a.n_seg, a.c_prev, keys, a.N, a.lr, a.eps,
                            a.beta1, a.beta2);
     hipLaunchKernelGGL(lamb_finalize_kernel, dim3((a.n_seg + 255) / 256), dim3(256), 0, st, keys,
-                       a.n_seg, a.c_avg, a.r_prev, a.c_prev, a.ratio_max, a.r_threshold, a.r_min,
-                       a.r_max);
+                       a.n_seg, a.c_avg, a.r_prev, a.c_prev, a.ratio_max, a.err_ratio,
+                       a.r_threshold, a.r_min, a.r_max);
     if (a.use_c_t)
         hipLaunchKernelGGL(lamb_apply_kernel, grid, dim3(kThreads), 0, st, a.x, a.m, a.v,
                            a.seg_off, a.n_seg, a.c_prev, a.N, (int32_t)kLambTiles, a.lr, a.eps);

@@ -26,6 +26,7 @@ ONEBIT_E_ALIGN = -3
 ONEBIT_E_WORKSPACE = -4
 ONEBIT_E_ARG = -5
 ONEBIT_E_HIP = -6
+ONEBIT_UNIT_SCALE = 1
 
 _c_i32, _c_i64, _c_u32, _c_u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64
 _c_f, _c_p, _c_sz = ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -43,6 +44,7 @@ class FrozenVArgs(ctypes.Structure):
         ("seg_off", _c_p), ("c_avg", _c_p), ("r_prev", _c_p), ("c_prev", _c_p),
         ("ratio_max", _c_p),
         ("m_bits", _c_p), ("m_scales", _c_p), ("m_chunks", _c_i32),
+        ("err_ratio", _c_p),
     ]
 
 
@@ -51,6 +53,13 @@ _SIGNATURES = {
                                  _c_i32, _c_p, _c_sz, _c_p]),
     "onebit_compress_grad": (_c_i32, [_c_p, _c_p, _c_p, _c_f, _c_p, _c_p, _c_p, _c_i64, _c_i32, _c_f,
                                       _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_sz, _c_p]),
+    "onebit_compress_ex": (_c_i32, [_c_p, _c_p, _c_p, _c_f, _c_p, _c_p, _c_p, _c_i64, _c_i32, _c_f,
+                                    _c_i32, _c_p, _c_p, _c_p, _c_i32, _c_u32, _c_p, _c_sz, _c_p]),
+    "onebit_server_reduce_ex": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                         _c_i32, _c_i64, _c_i32, _c_i32, _c_u32, _c_p, _c_sz,
+                                         _c_p]),
+    "int8_quantize": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32, _c_i32, _c_u64, _c_u32,
+                               _c_p, _c_sz, _c_p]),
     "onebit_server_reduce": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i64,
                                       _c_i32, _c_i32, _c_p, _c_sz, _c_p]),
     "onebit_decompress": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i64, _c_i32, _c_p]),
@@ -148,6 +157,25 @@ def onebit_compress_grad(g, mb_bits, mb_scales, beta1: float, ef, scales, bits, 
         _nbytes(ws) if ws is not None else 0, _stream(stream)))
 
 
+def onebit_compress_ex(m, ef, scales, bits, N: int, n: int, mb_bits=None, mb_scales=None,
+                       beta1: float = 0.0, clip: float = 0.0, reset: bool = False, seg_off=None,
+                       seg_k=None, seg_err_ratio=None, n_seg: int = 0, flags: int = 0, ws=None,
+                       stream=None) -> None:
+    _check("onebit_compress_ex", load().onebit_compress_ex(
+        _ptr(m), _ptr(mb_bits), _ptr(mb_scales), beta1, _ptr(ef), _ptr(scales), _ptr(bits), N, n,
+        clip, int(bool(reset)), _ptr(seg_off), _ptr(seg_k), _ptr(seg_err_ratio), n_seg, flags,
+        _ptr(ws), _nbytes(ws) if ws is not None else 0, _stream(stream)))
+
+
+def onebit_server_reduce_ex(bits, scales, ef, sv_scales, sv_bits, m_out, N: int, n: int,
+                            reset: bool = False, seg_off=None, seg_k=None, seg_err_ratio=None,
+                            n_seg: int = 0, flags: int = 0, ws=None, stream=None) -> None:
+    _check("onebit_server_reduce_ex", load().onebit_server_reduce_ex(
+        _ptr(bits), _ptr(scales), _ptr(ef), _ptr(sv_scales), _ptr(sv_bits), _ptr(m_out),
+        _ptr(seg_off), _ptr(seg_k), _ptr(seg_err_ratio), n_seg, N, n, int(bool(reset)), flags,
+        _ptr(ws), _nbytes(ws) if ws is not None else 0, _stream(stream)))
+
+
 def onebit_server_reduce(bits, scales, ef, sv_scales, sv_bits, m_out, N: int, n: int,
                          reset: bool = False, seg_off=None, seg_k=None, n_seg: int = 0, ws=None,
                          stream=None) -> None:
@@ -179,13 +207,13 @@ def frozen_v_step(*, mode: int, N: int, x, m, v, lr: float, eps: float, beta1: f
                   beta2: float = 0.999, m_prev=None, v_fresh=None, seg_off=None, n_seg: int = 0,
                   c_avg=None, r_prev=None, c_prev=None, ratio_max=None, r_threshold: float = 0.1,
                   r_min: float = 0.5, r_max: float = 4.0, use_c_t: bool = False, m_bits=None,
-                  m_scales=None, m_chunks: int = 0, ws=None, stream=None) -> None:
+                  m_scales=None, m_chunks: int = 0, err_ratio=None, ws=None, stream=None) -> None:
     a = FrozenVArgs(mode=mode, use_c_t=int(bool(use_c_t)), N=N, lr=lr, eps=eps, beta1=beta1,
                     beta2=beta2, r_threshold=r_threshold, r_min=r_min, r_max=r_max, n_seg=n_seg,
                     x=_ptr(x), m=_ptr(m), v=_ptr(v), m_prev=_ptr(m_prev), v_fresh=_ptr(v_fresh),
                     seg_off=_ptr(seg_off), c_avg=_ptr(c_avg), r_prev=_ptr(r_prev),
                     c_prev=_ptr(c_prev), ratio_max=_ptr(ratio_max), m_bits=_ptr(m_bits),
-                    m_scales=_ptr(m_scales), m_chunks=m_chunks)
+                    m_scales=_ptr(m_scales), m_chunks=m_chunks, err_ratio=_ptr(err_ratio))
     _check("frozen_v_step", load().frozen_v_step(
         ctypes.byref(a), _ptr(ws), _nbytes(ws) if ws is not None else 0, _stream(stream)))
 
@@ -195,3 +223,11 @@ def int8_sr_quantize(g, err, codes, block_scales, deq, N: int, block: int, seed:
     _check("int8_sr_quantize", load().int8_sr_quantize(
         _ptr(g), _ptr(err), _ptr(codes), _ptr(block_scales), _ptr(deq), N, block,
         seed & 0xFFFFFFFFFFFFFFFF, step & 0xFFFFFFFF, _stream(stream)))
+
+
+def int8_quantize(g, err, codes, block_scales, deq, N: int, block: int, rounding: int, seed: int,
+                  step: int, ws=None, stream=None) -> None:
+    _check("int8_quantize", load().int8_quantize(
+        _ptr(g), _ptr(err), _ptr(codes), _ptr(block_scales), _ptr(deq), N, block, rounding,
+        seed & 0xFFFFFFFFFFFFFFFF, step & 0xFFFFFFFF, _ptr(ws), _nbytes(ws) if ws is not None else 0,
+        _stream(stream)))

@@ -35,6 +35,8 @@ class OneBitGroup:
     reset_interval: int = 0
     seg_off: Optional[torch.Tensor] = None  # int64 [S+1] on device
     seg_k: Optional[torch.Tensor] = None    # float32 [S] on device
+    unit_scale: bool = False                # unscaled +-1 signs at both levels
+    seg_err_ratio: Optional[torch.Tensor] = None  # float32 [S]: step-ratio error factor
 
     def __post_init__(self):
         N, n, dev = self.N, self.n, self.device
@@ -60,25 +62,34 @@ class OneBitGroup:
         errors before compensation when t is a multiple of the interval."""
         return self.reset_interval > 0 and t % self.reset_interval == 0
 
+    @property
+    def flags(self) -> int:
+        return ob.ONEBIT_UNIT_SCALE if self.unit_scale else 0
+
     def compress(self, m: torch.Tensor, t: int, first: bool = False, stream=None) -> None:
-        ob.onebit_compress(m, self.ef, self.scales, self.bits, self.N, self.n, clip=self.clip,
-                           reset=first or self.is_reset(t), seg_off=self.seg_off, seg_k=self.seg_k,
-                           n_seg=self.n_seg, ws=self.ws, stream=stream)
+        ob.onebit_compress_ex(m, self.ef, self.scales, self.bits, self.N, self.n, clip=self.clip,
+                              reset=first or self.is_reset(t), seg_off=self.seg_off,
+                              seg_k=self.seg_k, seg_err_ratio=self.seg_err_ratio,
+                              n_seg=self.n_seg, flags=self.flags, ws=self.ws, stream=stream)
 
     def compress_grad(self, g: torch.Tensor, t: int, beta1: float, first: bool = False,
                       stream=None) -> None:
         """Compress from gradients: each worker's momentum is formed from g and
         the previous step's packed global momentum (sv_bits, sv_scales)."""
-        ob.onebit_compress_grad(g, self.sv_bits, self.sv_scales, beta1, self.ef, self.scales,
-                                self.bits, self.N, self.n, clip=self.clip,
-                                reset=first or self.is_reset(t), seg_off=self.seg_off,
-                                seg_k=self.seg_k, n_seg=self.n_seg, ws=self.ws, stream=stream)
+        ob.onebit_compress_ex(g, self.ef, self.scales, self.bits, self.N, self.n,
+                              mb_bits=self.sv_bits, mb_scales=self.sv_scales, beta1=beta1,
+                              clip=self.clip, reset=first or self.is_reset(t),
+                              seg_off=self.seg_off, seg_k=self.seg_k,
+                              seg_err_ratio=self.seg_err_ratio, n_seg=self.n_seg,
+                              flags=self.flags, ws=self.ws, stream=stream)
 
     def server(self, t: int, first: bool = False, decompress: bool = True, stream=None) -> None:
-        ob.onebit_server_reduce(self.bits, self.scales, self.sv_ef, self.sv_scales, self.sv_bits,
-                                self.mbar if decompress else None, self.N, self.n,
-                                reset=first or self.is_reset(t), seg_off=self.seg_off,
-                                seg_k=self.seg_k, n_seg=self.n_seg, ws=self.ws, stream=stream)
+        ob.onebit_server_reduce_ex(self.bits, self.scales, self.sv_ef, self.sv_scales,
+                                   self.sv_bits, self.mbar if decompress else None, self.N,
+                                   self.n, reset=first or self.is_reset(t),
+                                   seg_off=self.seg_off, seg_k=self.seg_k,
+                                   seg_err_ratio=self.seg_err_ratio, n_seg=self.n_seg,
+                                   flags=self.flags, ws=self.ws, stream=stream)
 
     def worker_error(self) -> torch.Tensor:
         e = torch.empty_like(self.ef)
@@ -114,6 +125,7 @@ class LambState:
     r: torch.Tensor          # [S] r_{t-1} -> r_t
     c: torch.Tensor          # [S] c_{t-1} -> c_t
     ratio_max: torch.Tensor  # [S]
+    err_ratio: torch.Tensor  # [S] c_{t-1} / c_t, for the next step's error feedback
     ws: torch.Tensor
 
     @classmethod
@@ -123,6 +135,7 @@ class LambState:
         return cls(x=x, v_frozen=v_frozen, v_fresh=v_frozen.clone(), m_prev=m_prev,
                    seg_off=seg_off, c_avg=c_avg, r=torch.ones(S, dtype=torch.float32, device=dev),
                    c=c_avg.clone(), ratio_max=torch.empty(S, dtype=torch.float32, device=dev),
+                   err_ratio=torch.ones(S, dtype=torch.float32, device=dev),
                    ws=torch.empty(max(256, 4 * S + 256), dtype=torch.uint8, device=dev))
 
     def step(self, mbar: torch.Tensor, lr: float, eps: float, beta1: float, beta2: float,
@@ -132,5 +145,5 @@ class LambState:
                          eps=eps, beta1=beta1, beta2=beta2, m_prev=self.m_prev,
                          v_fresh=self.v_fresh, seg_off=self.seg_off, n_seg=S, c_avg=self.c_avg,
                          r_prev=self.r, c_prev=self.c, ratio_max=self.ratio_max,
-                         r_threshold=thr, r_min=r_min, r_max=r_max, use_c_t=use_c_t, ws=self.ws,
-                         stream=stream)
+                         r_threshold=thr, r_min=r_min, r_max=r_max, use_c_t=use_c_t,
+                         err_ratio=self.err_ratio, ws=self.ws, stream=stream)

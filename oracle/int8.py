@@ -21,6 +21,9 @@ Readings:
   index and step);
 * new error e = g' - q * scale.
 
+Variants: a per-tensor scale (block 0) and deterministic rounding to the
+nearest integer, halves away from zero.
+
 Parity pins (tests/test_oracle_int8.py): codes in range, |deq - g'| < scale
 away from the clamp, integral x gives a deterministic code, all-zero blocks,
 the block maximum's code, and unbiasedness over seeds.
@@ -37,12 +40,28 @@ from .philox import uniforms
 f32 = np.float32
 
 
+def round_half_away(x: np.ndarray) -> np.ndarray:
+    """Nearest integer, halves away from zero (the ordinary rounding the
+    tutorial's step 1 names); exact on binary32."""
+    x = np.asarray(x, dtype=f32)
+    t = np.trunc(x).astype(f32)
+    frac = np.abs((x - t).astype(f32))
+    return np.where(frac >= f32(0.5), (t + np.sign(x)).astype(f32), t).astype(f32)
+
+
 def int8_sr(g: np.ndarray, e: Optional[np.ndarray], seed: int, step: int,
-            block: int = 256, J0: int = 0) -> Dict[str, np.ndarray]:
+            block: int = 256, J0: int = 0, rounding: str = "stochastic") -> Dict[str, np.ndarray]:
     """Quantise g (+ e when given).  ``J0`` is the global index of g[0] for
-    the Philox counter (so a slice can be checked on its own)."""
+    the Philox counter (so a slice can be checked on its own).
+
+    block = 0 takes one scale for the whole tensor (the PyTorch example's
+    max over the tensor); rounding = "nearest" replaces the stochastic draw
+    by rounding to the nearest integer, halves away from zero ("FP32 ->
+    INT8" step 1)."""
     g = np.asarray(g, dtype=f32).ravel()
     N = g.size
+    if block == 0:
+        block = N
     if N % block:
         raise ValueError("length must be a multiple of the block")
     gc = g if e is None else (g + np.asarray(e, dtype=f32).ravel()).astype(f32)
@@ -52,12 +71,15 @@ def int8_sr(g: np.ndarray, e: Optional[np.ndarray], seed: int, step: int,
     M = np.fmax(M, f32(0.0))
     scale = (M / f32(127.0)).astype(f32)
     sc = np.repeat(scale, block)
-    u = uniforms(J0, N, seed, step)
     with np.errstate(divide="ignore", invalid="ignore"):
         x = (gc / sc).astype(f32)
-        f = np.floor(x).astype(f32)
-        p = (x - f).astype(f32)
-        q = (f + np.where(u < p, f32(1.0), f32(0.0))).astype(f32)
+        if rounding == "nearest":
+            q = round_half_away(x)
+        else:
+            u = uniforms(J0, N, seed, step)
+            f = np.floor(x).astype(f32)
+            p = (x - f).astype(f32)
+            q = (f + np.where(u < p, f32(1.0), f32(0.0))).astype(f32)
         q = np.fmin(np.fmax(q, f32(-127.0)), f32(127.0))
     zero = sc == 0
     q = np.where(zero, f32(0.0), q)

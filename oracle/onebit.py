@@ -28,7 +28,10 @@ Readings where the pages are silent (the same ones the HIP path follows):
   worker errors; the clamp applies to the worker's compensated value only;
 * the server average sums the n decoded chunks in ascending worker order in
   binary32, starting from +0, then divides by n;
-* clamp(x) = fmin(fmax(x, -clip), clip), so NaN becomes -clip.
+* clamp(x) = fmin(fmax(x, -clip), clip), so NaN becomes -clip;
+* the step-ratio factor of the 1-bit LAMB analysis multiplies the carried
+  error of both levels (worker and server) by the factor of its layer, so
+  that the two-level momentum identity keeps the ratio.
 
 Parity pins (tests/test_oracle_onebit.py): brute force with Fractions on tiny
 inputs, the error identity, exact telescoping of the error feedback on dyadic
@@ -63,12 +66,20 @@ def error_from(gc: np.ndarray, s: np.float32) -> np.ndarray:
 
 
 def worker_compress(m: np.ndarray, e: np.ndarray, clip: float = 0.0,
-                    reset: bool = False, k: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                    reset: bool = False, k: Optional[np.ndarray] = None,
+                    unit_scale: bool = False,
+                    err_ratio: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """One worker-side compression of all n workers.
 
     m, e : float32 [n, N] momentum and carried error (N a multiple of 64 n)
     k    : optional float32 [N] per-element layer coefficient (x k before
            compensation)
+    unit_scale : the unscaled 1-bit sign q = +-1 of the 1-bit Adam article,
+           section 2.1 (s = 1 instead of the chunk mean)
+    err_ratio : optional float32 [N] per-element factor on the carried error,
+           the step-ratio-scaled error feedback of the 1-bit LAMB page
+           (analysis paragraph: the error is multiplied by c_{t-2}/c_{t-1}
+           of its layer before it is added)
     Returns gc (compensated, clamped) [n, N], bits uint32 [n, N/32],
     s float32 [n, n] (s[i][c] for worker i, chunk c) and the new error
     e [n, N]."""
@@ -78,6 +89,8 @@ def worker_compress(m: np.ndarray, e: np.ndarray, clip: float = 0.0,
         raise ValueError("N must be a multiple of 64 n")
     L = N // n
     e_in = np.zeros_like(m) if reset else np.asarray(e, dtype=f32)
+    if err_ratio is not None and not reset:
+        e_in = (np.asarray(err_ratio, dtype=f32)[None, :] * e_in).astype(f32)
     gc = np.empty_like(m)
     e_out = np.empty_like(m)
     s = np.empty((n, n), dtype=f32)
@@ -88,14 +101,15 @@ def worker_compress(m: np.ndarray, e: np.ndarray, clip: float = 0.0,
         gc[i] = gi
         for c in range(n):
             sl = slice(c * L, (c + 1) * L)
-            s[i, c] = mean_abs_f32(gi[sl])
+            s[i, c] = f32(1.0) if unit_scale else mean_abs_f32(gi[sl])
             e_out[i, sl] = error_from(gi[sl], s[i, c])
         bits[i] = B.pack(B.sign_bit(gi))
     return {"gc": gc, "bits": bits, "s": s, "e": e_out}
 
 
 def server_chunk(bits_c: np.ndarray, s_c: np.ndarray, E_c: np.ndarray,
-                 reset: bool = False) -> Dict[str, np.ndarray]:
+                 reset: bool = False, unit_scale: bool = False,
+                 err_ratio_c: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """Server side of one chunk.
 
     bits_c : uint32 [n, L/32] -- this chunk's sign words of every worker
@@ -113,14 +127,17 @@ def server_chunk(bits_c: np.ndarray, s_c: np.ndarray, E_c: np.ndarray,
         acc = (acc + B.signed(B.unpack(bits_c[i]), s_c[i])).astype(f32)
     avg = (acc / f32(n)).astype(f32)
     E_in = np.zeros(L, dtype=f32) if reset else np.asarray(E_c, dtype=f32)
+    if err_ratio_c is not None and not reset:
+        E_in = (np.asarray(err_ratio_c, dtype=f32) * E_in).astype(f32)
     g2 = (avg + E_in).astype(f32)
-    S = mean_abs_f32(g2)
+    S = f32(1.0) if unit_scale else mean_abs_f32(g2)
     return {"avg": avg, "g2": g2, "bits": B.pack(B.sign_bit(g2)), "S": S,
             "E": error_from(g2, S)}
 
 
 def server_reduce(bits: np.ndarray, s: np.ndarray, E: np.ndarray,
-                  reset: bool = False) -> Dict[str, np.ndarray]:
+                  reset: bool = False, unit_scale: bool = False,
+                  err_ratio: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """Server side for every chunk c (server rank c).
 
     bits : uint32 [n, N/32] worker sign words; s : float32 [n, n] worker scales
@@ -138,7 +155,8 @@ def server_reduce(bits: np.ndarray, s: np.ndarray, E: np.ndarray,
     E = np.zeros(N, dtype=f32) if reset else np.asarray(E, dtype=f32)
     for c in range(n):
         sl = slice(c * L, (c + 1) * L)
-        r = server_chunk(bits[:, c * L // 32:(c + 1) * L // 32], s[:, c], E[sl], reset)
+        r = server_chunk(bits[:, c * L // 32:(c + 1) * L // 32], s[:, c], E[sl], reset,
+                         unit_scale, None if err_ratio is None else np.asarray(err_ratio)[sl])
         for key in ("avg", "g2", "E"):
             out[key][sl] = r[key]
         out["S"][c] = r["S"]

@@ -123,4 +123,6 @@ def lamb_frozen_step(x, m, m_prev, v_f, v_tw, seg_off, c_avg, r_prev, c_prev,
     r, c = lamb_ratio_update(R, r_prev, c_avg, thr, r_min, r_max)
     c_used = c if use_c_t else np.asarray(c_prev, dtype=f32)
     x_new = lamb_apply(x, m, v_tw, seg_off, c_used, lr, eps)
-    return {"x": x_new, "v": v_new, "R": R, "r": r, "c": c, "g": g}
+    # factor for the next step's error feedback: c_{t-1} / c_t of each layer
+    rho = (np.asarray(c_prev, dtype=f32) / c).astype(f32)
+    return {"x": x_new, "v": v_new, "R": R, "r": r, "c": c, "g": g, "err_ratio": rho}

@@ -117,4 +117,29 @@ def test_struct_layout_matches_header():
     assert ob.FrozenVArgs.x.offset == 48
     assert ob.FrozenVArgs.m_bits.offset == 128
     assert ob.FrozenVArgs.m_chunks.offset == 144
-    assert ctypes.sizeof(ob.FrozenVArgs) == 152
+    assert ob.FrozenVArgs.err_ratio.offset == 152
+    assert ctypes.sizeof(ob.FrozenVArgs) == 160
+
+
+def test_extended_entries_validation(lib):
+    cx = lib.onebit_compress_ex
+    base = [P, None, None, 0.0, P, P, P, 1 << 12, 4, 0.0, 0, None, None, None, 0, 0, P, 1 << 30, None]
+    bad = list(base); bad[18 - 2] = None  # no workspace
+    assert cx(*bad) == ob.ONEBIT_E_WORKSPACE
+    bad = list(base); bad[15] = 2         # unknown flag
+    assert cx(*bad) == ob.ONEBIT_E_ARG
+    bad = list(base); bad[13] = P         # error ratio without a layer table
+    assert cx(*bad) == ob.ONEBIT_E_ARG
+    bad = list(base); bad[1] = P          # words without scales
+    assert cx(*bad) == ob.ONEBIT_E_NULL
+    sx = lib.onebit_server_reduce_ex
+    sbase = [P, P, P, P, P, None, None, None, None, 0, 1 << 12, 4, 0, 0, P, 1 << 30, None]
+    bad = list(sbase); bad[13] = 4
+    assert sx(*bad) == ob.ONEBIT_E_ARG
+    bad = list(sbase); bad[8] = P
+    assert sx(*bad) == ob.ONEBIT_E_ARG
+    q = lib.int8_quantize
+    assert q(P, None, P, P, None, 4096, 0, 0, 1, 1, None, 0, None) == ob.ONEBIT_E_WORKSPACE
+    assert q(P, None, P, P, None, 4096, 256, 2, 1, 1, None, 0, None) == ob.ONEBIT_E_ARG
+    assert q(P, None, P, P, None, 4098, 0, 0, 1, 1, P, 256, None) == ob.ONEBIT_E_SIZE
+    assert lib.int8_sr_quantize(P, None, P, P, None, 4096, 0, 1, 1, None) == ob.ONEBIT_E_SIZE

@@ -99,3 +99,30 @@ def test_uniforms_grid_and_range():
     assert u.min() >= 0 and u.max() < 1
     assert np.all((u * 2 ** 24) == np.floor(u * 2 ** 24))
     assert abs(u.mean() - 0.5) < 0.02
+
+
+def test_nearest_rounding_hand_values():
+    """Round to nearest, halves away from zero (tutorial, step 1)."""
+    from oracle.int8 import round_half_away
+    x = np.array([2.5, -2.5, 2.4999998, -0.5, 0.5, 126.5, -126.5, 3.0, -0.49999997, 0.0],
+                 dtype=F32)
+    assert round_half_away(x).tolist() == [3, -3, 2, -1, 1, 127, -127, 3, -0, 0]
+    # block max 127 -> scale 1: codes are the rounded inputs, clamped to +-127
+    g = np.zeros(256, dtype=F32)
+    g[:6] = [127, -126.5, 2.5, -2.5, 0.4, 1.5]
+    out = int8_sr(g, None, seed=1, step=1, rounding="nearest")
+    assert out["codes"][:6].tolist() == [127, -127, 3, -3, 0, 2]
+
+
+def test_per_tensor_scale():
+    """block = 0: one scale from the max over the whole tensor (the PyTorch
+    example)."""
+    rng = np.random.default_rng(6)
+    g = _laplace(rng, 4096)
+    g[1234] = 0.5
+    out = int8_sr(g, None, seed=3, step=2, block=0)
+    assert out["scales"].shape == (1,)
+    assert out["scales"][0] == F32(0.5) / F32(127)
+    assert out["codes"][1234] in (126, 127)
+    q = out["codes"].astype(np.int32)
+    assert q.min() >= -127 and q.max() <= 127

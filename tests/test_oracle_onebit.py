@@ -297,3 +297,58 @@ def test_local_momentum_closed_forms():
             assert abs(frac(m9[i, j]) - exact) <= ulp(m9[i, j]) + ulp(F32(0.9) * mb9[j]) / 2 + \
                 ulp(F32(F32(1) - F32(0.9)) * g9[i, j]) / 2 + abs(frac(g9[i, j])) * (
                     abs(Fraction(float(F32(1) - F32(0.9))) - (1 - b1)))
+
+
+def test_unit_scale_is_the_plain_sign():
+    """The 1-bit Adam article's q = sign(g'): every scale is 1 and the error
+    is g' -+ 1 (exact on dyadic inputs); the server's scales are 1 too."""
+    rng = np.random.default_rng(29)
+    n, N = 4, 512
+    m = (rng.integers(-255, 256, size=(n, N)) / 256.0).astype(F32)
+    w = O.worker_compress(m, np.zeros_like(m), unit_scale=True)
+    assert np.all(w["s"] == 1)
+    for i in range(n):
+        for j in range(0, N, 3):
+            q = 1 if m[i, j] >= 0 else -1
+            assert frac(w["e"][i, j]) == frac(m[i, j]) - q
+    sv = O.server_reduce(w["bits"], w["s"], np.zeros(N, dtype=F32), unit_scale=True)
+    assert np.all(sv["S"] == 1)
+    # the average of +-1 over 4 workers takes values in {-1, -1/2, 0, 1/2, 1}
+    assert set(np.unique(sv["avg"]).tolist()) <= {-1.0, -0.5, 0.0, 0.5, 1.0}
+
+
+def test_error_ratio_one_is_transparent():
+    rng = np.random.default_rng(31)
+    n, N = 4, 1024
+    m = _draw(rng, (n, N))
+    e = _draw(rng, (n, N), 3e-4)
+    a = O.worker_compress(m, e, err_ratio=np.ones(N, dtype=F32))
+    b = O.worker_compress(m, e)
+    for key in ("gc", "s", "e", "bits"):
+        assert np.array_equal(a[key], b[key])
+
+
+def test_two_level_identity_with_step_ratio():
+    """1-bit LAMB analysis paragraph: with the carried errors scaled by the
+    step ratio rho at both levels, m_bar_t = mean_i m_t^(i) + rho
+    delta_{t-1} - delta_t.  Inputs on a 2^-4 grid in (-1/4, 1/4), chunks of
+    64 and two steps keep every operation exact (each chunk mean adds six
+    binary digits), so the identity holds exactly for rho = 1/2 and 2."""
+    rng = np.random.default_rng(37)
+    n, N = 2, 128
+    for rho in (0.5, 2.0):
+        e = np.zeros((n, N), dtype=F32)
+        E = np.zeros(N, dtype=F32)
+        delta_prev = [Fraction(0)] * N
+        for t in range(2):
+            m = (rng.integers(-3, 4, size=(n, N)) / 16.0).astype(F32)
+            ratio = np.full(N, F32(rho))
+            w = O.worker_compress(m, e, err_ratio=ratio)
+            sv = O.server_reduce(w["bits"], w["s"], E, err_ratio=ratio)
+            mbar = O.decompress(sv["bits"], sv["S"])
+            for j in range(N):
+                delta = frac(sv["E"][j]) + (frac(w["e"][0, j]) + frac(w["e"][1, j])) / 2
+                avg_m = (frac(m[0, j]) + frac(m[1, j])) / 2
+                assert frac(mbar[j]) == avg_m + Fraction(rho) * delta_prev[j] - delta
+                delta_prev[j] = delta
+            e, E = w["e"], sv["E"]

@@ -125,3 +125,12 @@ def test_lamb_fixed_point_and_step():
                                c_prev=a(0.5, 0.25), lr=1.0, eps=0.0, beta1=b1, beta2=0.5,
                                thr=0.1, r_min=0.5, r_max=4.0, use_c_t=True)
     assert np.array_equal(out_b["x"], a(0.0, 2.0, -0.5, -0.5))
+
+
+def test_lamb_error_ratio_output():
+    """The factor for the next step's error feedback is c_{t-1} / c_t."""
+    out = P.lamb_frozen_step(a(1.0, 1.0), a(0.5, 0.5), a(0.0, 0.0), a(1.0, 1.0), a(1.0, 1.0),
+                             [0, 1, 2], c_avg=a(2.0, 3.0), r_prev=a(1.0, 1.0), c_prev=a(1.0, 6.0),
+                             lr=1.0, eps=0.0, beta1=0.5, beta2=0.5, thr=0.1, r_min=1.0, r_max=1.0)
+    assert np.array_equal(out["c"], a(2.0, 3.0))
+    assert np.array_equal(out["err_ratio"], a(0.5, 2.0))
