@@ -172,26 +172,39 @@ __global__ __launch_bounds__(kThreads) void int8_kernel(const float* __restrict_
 }
 
 // max over the tensor of |g (+ err)| (NaN skipped) as the bit pattern of a
-// non-negative float, accumulated with one atomicMax per workgroup
+// non-negative float.  A fixed grid strides over the tensor, four tiles per
+// pass with all loads issued before the maxima, and each workgroup ends with
+// one atomicMax, so the single accumulator sees a few thousand atomics rather
+// than one per tile.
+template <bool EF>
 __global__ __launch_bounds__(kThreads) void tensor_absmax_kernel(const float* __restrict__ g,
                                                                 const float* __restrict__ err,
-                                                                int64_t N, int32_t iters,
+                                                                int64_t N,
                                                                 uint32_t* __restrict__ out) {
     __shared__ uint32_t red[kThreads / 64];
-    const int64_t base = (int64_t)blockIdx.x * iters * kTile;
+    constexpr int64_t span = (int64_t)kMaxIters * kTile;
+    const int64_t stride = (int64_t)gridDim.x * span;
     float M = 0.0f;
-    for (int it = 0; it < iters; ++it) {
-        const int64_t J = base + (int64_t)it * kTile + 4 * (int64_t)threadIdx.x;
-        if (J < N) {
-            f4 gv = __builtin_nontemporal_load(reinterpret_cast<const f4*>(g + J));
-            if (err) {
-                const f4 ev = *reinterpret_cast<const f4*>(err + J);
-                gv = f4{gv.x + ev.x, gv.y + ev.y, gv.z + ev.z, gv.w + ev.w};
+    for (int64_t base = (int64_t)blockIdx.x * span; base < N; base += stride) {
+        f4 gv[kMaxIters], ev[kMaxIters];
+#pragma unroll
+        for (int it = 0; it < kMaxIters; ++it) {
+            const int64_t J = base + (int64_t)it * kTile + 4 * (int64_t)threadIdx.x;
+            gv[it] = f4{0.f, 0.f, 0.f, 0.f};
+            ev[it] = f4{0.f, 0.f, 0.f, 0.f};
+            if (J < N) {
+                gv[it] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(g + J));
+                if (EF) ev[it] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(err + J));
             }
-            M = fmaxf(M, fabsf(gv.x));
-            M = fmaxf(M, fabsf(gv.y));
-            M = fmaxf(M, fabsf(gv.z));
-            M = fmaxf(M, fabsf(gv.w));
+        }
+#pragma unroll
+        for (int it = 0; it < kMaxIters; ++it) {
+            f4 x = gv[it];
+            if (EF) x = f4{x.x + ev[it].x, x.y + ev[it].y, x.z + ev[it].z, x.w + ev[it].w};
+            M = fmaxf(M, fabsf(x.x));
+            M = fmaxf(M, fabsf(x.y));
+            M = fmaxf(M, fabsf(x.z));
+            M = fmaxf(M, fabsf(x.w));
         }
     }
     uint32_t u = __float_as_uint(M);  // non-negative: integer order is value order
@@ -207,6 +220,8 @@ __global__ __launch_bounds__(kThreads) void tensor_absmax_kernel(const float* __
         atomicMax(out, b);
     }
 }
+
+constexpr int64_t kAbsmaxBlocks = 2048;
 
 __global__ void zero_u32_kernel(uint32_t* p) { *p = 0u; }
 
@@ -235,8 +250,17 @@ static hipError_t launch_r(dim3 grid, hipStream_t st, const float* g, float* err
     switch (block) {
         case 0:
             hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, st, tmax);
-            hipLaunchKernelGGL(tensor_absmax_kernel, grid, dim3(kThreads), 0, st, g, err, N, iters,
-                               tmax);
+            {
+                // 8 workgroups per CU; fewer when the tensor is small
+                const int64_t spans = (N + (int64_t)kMaxIters * kTile - 1) / ((int64_t)kMaxIters * kTile);
+                const dim3 mgrid((unsigned)(spans < kAbsmaxBlocks ? spans : kAbsmaxBlocks));
+                if (err)
+                    hipLaunchKernelGGL(tensor_absmax_kernel<true>, mgrid, dim3(kThreads), 0, st, g,
+                                       err, N, tmax);
+                else
+                    hipLaunchKernelGGL(tensor_absmax_kernel<false>, mgrid, dim3(kThreads), 0, st, g,
+                                       err, N, tmax);
+            }
             launch_b<0, NEAREST>(grid, st, g, err, codes, scales, deq, N, iters, k0, k1, step, tmax);
             break;
         case 64: launch_b<64, NEAREST>(grid, st, g, err, codes, scales, deq, N, iters, k0, k1, step, tmax); break;

@@ -120,3 +120,30 @@ def test_int8_variants(block, rounding):
         same_f32(host(deq), o["deq"], f"step {step} deq")
         same_f32(host(err), o["e"], f"step {step} residual")
         e_h = o["e"]
+
+
+@pytest.mark.parametrize("with_err", [True, False])
+def test_int8_tensor_scale_grid_stride(with_err):
+    """Per-tensor scale on a tensor long enough that every workgroup of the
+    max pass strides over it more than once; the maximum sits in the ragged
+    last span."""
+    dev = device()
+    N = 2 * 2048 * 4096 + 4 * 333
+    print(f"[int8 tensor scale] N={N} err={with_err}", flush=True)
+    g = S.laplace_gradient(N, 3, 8, dev)
+    g[N - 3] = -4.0  # far above the x100 outliers of the Laplace(1e-3) draw
+    g[N // 2] = 2.0
+    err = torch.zeros(N, device=dev) if with_err else None
+    if with_err:
+        err[N - 7] = 3.875  # g' = 3.875 + g, below 4
+    codes = torch.empty(N, dtype=torch.int8, device=dev)
+    scales = torch.empty(1, device=dev)
+    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    e_h = host(err) if with_err else None
+    ob.int8_quantize(g, err, codes, scales, None, N, 0, 1, 5, 1, ws=ws)
+    torch.cuda.synchronize()
+    o = int8_sr(host(g), e_h, 5, 1, block=0, rounding="nearest")
+    assert host(scales)[0] == o["scales"][0] == np.float32(4.0) / np.float32(127)
+    assert np.array_equal(host(codes), o["codes"])
+    if with_err:
+        same_f32(host(err), o["e"], "residual")
