@@ -230,6 +230,9 @@ int lamb_layer_scale(float* buf, int64_t N, int32_t batch,
  *   new c (use_c_t != 0, which costs a second pass).  On return r_prev and
  *   c_prev hold r_t and c_t; ratio_max (optional) holds R (NaN: none).
  *   First compressed step: r_prev = 1, c_prev = c_avg, v_f = v.
+ *   ws: device workspace of at least frozen_v_workspace_bytes(N, n_seg)
+ *   bytes, 256-byte aligned (layer maxima; mode 1 only, modes 0 and 2 take
+ *   none).  Calls that share a workspace must not overlap.
  *
  * mode 2, Adam with the global momentum given packed (the decompression every
  * worker performs, fused into the step): m is ignored and
@@ -302,9 +305,14 @@ int int8_quantize(const float* g, float* err, int8_t* codes, float* block_scales
                   int64_t N, int32_t block, int32_t rounding, uint64_t seed, uint32_t step,
                   void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes needed by onebit_compress / onebit_server_reduce /
- * frozen_v_step for these sizes (0 if the sizes are invalid). */
+/* Workspace bytes needed by onebit_compress(_ex) / onebit_compress_grad /
+ * onebit_server_reduce(_ex) for these sizes (0 if the sizes are invalid). */
 size_t onebit_workspace_bytes(int64_t N, int32_t n, int32_t n_seg);
+
+/* Workspace bytes needed by frozen_v_step in mode 1 (LAMB) for N elements
+ * in n_seg layers: the layer keys plus one slot per workgroup of the pass,
+ * about N / 1024 bytes (0 if N < 0, N is not a multiple of 4 or n_seg < 1). */
+size_t frozen_v_workspace_bytes(int64_t N, int32_t n_seg);
 
 /* Static description of a status code. */
 const char* onebit_strerror(int status);

@@ -22,4 +22,5 @@ from .onebit import (  # noqa: F401
     onebit_server_reduce,
     onebit_server_reduce_ex,
     workspace_bytes,
+    frozen_v_workspace_bytes,
 )

@@ -31,6 +31,12 @@ int check_segments(const int64_t* seg_off, const float* seg_k, int32_t n_seg, bo
 
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// LAMB step: the layer keys, then one slot per workgroup of the pass
+size_t lamb_ws_bytes(int64_t N, int32_t n_seg) {
+    return round_up((size_t)n_seg * sizeof(uint32_t)) +
+           round_up((size_t)lamb_workgroups(N) * sizeof(uint32_t));
+}
+
 size_t partial_bytes(int64_t N, int32_t n) {
     const int64_t L = N / n;
     const ChunkPlan pw = make_plan(L, (int64_t)n * n);
@@ -63,6 +69,11 @@ size_t onebit_workspace_bytes(int64_t N, int32_t n, int32_t n_seg) {
     if (check_rows(N, n) != ONEBIT_OK || n_seg < 0) return 0;
     if (N == 0) return 256;
     return partial_bytes(N, n) + round_up((size_t)(n_seg > 0 ? n_seg : 1) * sizeof(uint32_t));
+}
+
+size_t frozen_v_workspace_bytes(int64_t N, int32_t n_seg) {
+    if (N < 0 || (N % 4) || n_seg < 1) return 0;
+    return lamb_ws_bytes(N, n_seg);
 }
 
 int onebit_compress_ex(const float* m, const uint32_t* mb_bits, const float* mb_scales, float beta1,
@@ -220,10 +231,12 @@ int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes, hipS
         (a->ratio_max && !aligned(a->ratio_max, 4)) || (a->err_ratio && !aligned(a->err_ratio, 4)))
         return ONEBIT_E_ALIGN;
     if (a->N == 0) return ONEBIT_OK;
-    const size_t need = round_up((size_t)a->n_seg * sizeof(uint32_t));
+    const size_t need = lamb_ws_bytes(a->N, a->n_seg);
     if (!ws || ws_bytes < need) return ONEBIT_E_WORKSPACE;
     if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
-    return hip_status(launch_lamb(*a, static_cast<uint32_t*>(ws), stream));
+    uint32_t* keys = static_cast<uint32_t*>(ws);
+    uint32_t* wg_max = keys + round_up((size_t)a->n_seg * sizeof(uint32_t)) / sizeof(uint32_t);
+    return hip_status(launch_lamb(*a, keys, wg_max, stream));
 }
 
 int int8_quantize(const float* g, float* err, int8_t* codes, float* block_scales, float* deq,

@@ -15,6 +15,13 @@ constexpr int kThreads = 256;           // threads per workgroup (4 waves)
 constexpr int kTile = kThreads * 4;     // elements per workgroup iteration (float4 / lane)
 constexpr int kMaxIters = 4;            // tiles per workgroup in the chunked streaming kernels
 constexpr int kUnroll = 4;              // tiles whose loads are issued together
+constexpr int kLambTiles = 4;           // tiles per workgroup in the LAMB pass (5 streams in flight)
+
+// workgroups of the LAMB pass over N elements
+inline int64_t lamb_workgroups(int64_t N) {
+    const int64_t span = (int64_t)kLambTiles * kTile;
+    return (N + span - 1) / span;
+}
 
 // ---------------------------------------------------------------- launch plan
 // One plan for the chunked kernels (worker compress, server reduce): the
@@ -153,7 +160,8 @@ hipError_t launch_adam_packed(float* x, const uint32_t* mbits, const float* msca
                               const float* v, int64_t N, int32_t chunks, float lr, float eps,
                               hipStream_t st);
 
-hipError_t launch_lamb(const onebit_frozen_v_args& a, uint32_t* keys, hipStream_t st);
+hipError_t launch_lamb(const onebit_frozen_v_args& a, uint32_t* keys, uint32_t* wg_max,
+                       hipStream_t st);
 
 hipError_t launch_int8(const float* g, float* err, int8_t* codes, float* scales, float* deq,
                        int64_t N, int32_t block, uint64_t seed, uint32_t step, bool nearest,

@@ -103,7 +103,6 @@ hipError_t launch_adam_packed(float* x, const uint32_t* mbits, const float* msca
 }
 
 // ---------------------------------------------------------------- LAMB
-constexpr int kLambTiles = 4;  // tiles per workgroup in the LAMB pass (5 streams in flight)
 
 __global__ void fill_u32_kernel(uint32_t* p, int32_t n, uint32_t val) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -122,9 +121,13 @@ template <bool UPDATE_X>
 __global__ __launch_bounds__(kThreads) void lamb_kernel(
     float* __restrict__ x, const float* __restrict__ m, const float* __restrict__ mp,
     float* __restrict__ vf, const float* __restrict__ v, const int64_t* __restrict__ seg_off,
-    int32_t n_seg, const float* __restrict__ c_prev, uint32_t* __restrict__ keys, int64_t N,
-    float c_lr, float c_eps, float c_beta1, float c_beta2) {
+    int32_t n_seg, const float* __restrict__ c_prev, uint32_t* __restrict__ keys,
+    uint32_t* __restrict__ wg_max, int64_t N, float c_lr, float c_eps, float c_beta1,
+    float c_beta2) {
     __shared__ uint32_t red[kThreads / 64];
+    // workgroups across layer boundaries: maxima of layers seg0 .. seg0 + 255,
+    // merged in LDS so that each layer takes one global atomic per workgroup
+    __shared__ uint32_t win[kThreads];
     const float c_omb1 = 1.0f - c_beta1;
     const float c_omb2 = 1.0f - c_beta2;
     const int64_t wstart = (int64_t)blockIdx.x * kLambTiles * kTile;
@@ -139,6 +142,15 @@ __global__ __launch_bounds__(kThreads) void lamb_kernel(
     int64_t hi = seg_off[seg + 1];
     float step = c_lr * c_prev[seg];
     uint32_t kmax = 0;
+    if (!uniform) {  // workgroup-uniform branch
+        win[threadIdx.x] = 0u;
+        __syncthreads();
+    }
+    auto flush = [&](int sg, uint32_t km) {
+        const int d = sg - seg0;  // >= 0: a thread's layers start at or after seg0
+        if (d < kThreads) atomicMax(&win[d], km);
+        else atomicMax(&keys[sg], km);
+    };
     f4 mv[kLambTiles], pv[kLambTiles], fv[kLambTiles], vv[kLambTiles], xv[kLambTiles];
 #pragma unroll
     for (int u = 0; u < kLambTiles; ++u) {
@@ -171,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void lamb_kernel(
         for (int k = 0; k < 4; ++k) {
             if (!uniform) {
                 while (j + k >= hi && seg + 1 < n_seg) {
-                    if (kmax) atomicMax(&keys[seg], kmax);
+                    if (kmax) flush(seg, kmax);
                     kmax = 0;
                     ++seg;
                     hi = seg_off[seg + 1];
@@ -199,6 +211,12 @@ __global__ __launch_bounds__(kThreads) void lamb_kernel(
             __builtin_nontemporal_store(xo, reinterpret_cast<f4*>(x + j));
         }
     }
+    // A workgroup inside one layer leaves its maximum in its own slot (the
+    // finalize reduces a layer's slots): one atomic per workgroup on the
+    // layer's key would serialise thousands of workgroups on one address.
+    // Workgroups across a layer boundary (at most one per boundary) raise
+    // the keys of their layers atomically and leave 0 (no ratio) in their
+    // slot.
     if (uniform) {
         const uint32_t wm = wave_max_u32(kmax);
         if (lane_id() == 0) red[threadIdx.x >> 6] = wm;
@@ -206,21 +224,44 @@ __global__ __launch_bounds__(kThreads) void lamb_kernel(
         if (threadIdx.x == 0) {
             uint32_t b = red[0];
             for (int w = 1; w < kThreads / 64; ++w) b = red[w] > b ? red[w] : b;
-            if (b) atomicMax(&keys[seg0], b);
+            wg_max[blockIdx.x] = b;
         }
-    } else if (kmax) {
-        atomicMax(&keys[seg], kmax);
+    } else {
+        if (kmax) flush(seg, kmax);
+        __syncthreads();
+        if (threadIdx.x == 0) wg_max[blockIdx.x] = 0u;
+        const uint32_t w = win[threadIdx.x];
+        if (w) atomicMax(&keys[seg0 + threadIdx.x], w);
     }
 }
 
-__global__ void lamb_finalize_kernel(const uint32_t* __restrict__ keys, int32_t n_seg,
-                                     const float* __restrict__ c_avg, float* __restrict__ r_prev,
-                                     float* __restrict__ c_prev, float* __restrict__ ratio_max,
-                                     float* __restrict__ err_ratio, float thr, float r_min,
-                                     float r_max) {
-    const int l = blockIdx.x * blockDim.x + threadIdx.x;
+// One wave per layer: the maximum over the slots of the workgroups that
+// overlap the layer (those inside it hold their maximum, the others 0),
+// combined with the key the boundary workgroups raised atomically.
+__global__ __launch_bounds__(64) void lamb_finalize_kernel(
+    const uint32_t* __restrict__ keys, const uint32_t* __restrict__ wg_max,
+    const int64_t* __restrict__ seg_off, int64_t n_wg, int32_t n_seg,
+    const float* __restrict__ c_avg, float* __restrict__ r_prev, float* __restrict__ c_prev,
+    float* __restrict__ ratio_max, float* __restrict__ err_ratio, float thr, float r_min,
+    float r_max) {
+    const int l = blockIdx.x;
     if (l >= n_seg) return;
-    const uint32_t key = keys[l];
+    constexpr int64_t span = (int64_t)kLambTiles * kTile;
+    const int64_t a = seg_off[l], b = seg_off[l + 1];
+    uint32_t km = 0;
+    if (b > a) {
+        const int64_t w0 = a > 0 ? a / span : 0;
+        int64_t w1 = (b - 1) / span;
+        if (w1 > n_wg - 1) w1 = n_wg - 1;
+        for (int64_t w = w0 + threadIdx.x; w <= w1; w += 64) {
+            const uint32_t v = wg_max[w];
+            km = v > km ? v : km;
+        }
+    }
+    km = wave_max_u32(km);
+    if (threadIdx.x != 0) return;
+    const uint32_t k0 = keys[l];
+    const uint32_t key = k0 > km ? k0 : km;
     const float R = key ? key_float(key) : __uint_as_float(0x7FC00000u);
     const float rp = r_prev[l];
     const float Rv = (R == R) ? R : rp;
@@ -269,22 +310,23 @@ __global__ __launch_bounds__(kThreads) void lamb_apply_kernel(
     }
 }
 
-hipError_t launch_lamb(const onebit_frozen_v_args& a, uint32_t* keys, hipStream_t st) {
-    const int64_t per_wg = (int64_t)kLambTiles * kTile;
-    const dim3 grid((unsigned)((a.N + per_wg - 1) / per_wg));
+hipError_t launch_lamb(const onebit_frozen_v_args& a, uint32_t* keys, uint32_t* wg_max,
+                       hipStream_t st) {
+    const int64_t n_wg = lamb_workgroups(a.N);
+    const dim3 grid((unsigned)n_wg);
     hipLaunchKernelGGL(fill_u32_kernel, dim3((a.n_seg + 255) / 256), dim3(256), 0, st, keys,
                        a.n_seg, 0u);
     if (a.use_c_t)
         hipLaunchKernelGGL(lamb_kernel<false>, grid, dim3(kThreads), 0, st, a.x, a.m, a.m_prev,
-                           a.v_fresh, a.v, a.seg_off, a.n_seg, a.c_prev, keys, a.N, a.lr, a.eps,
-                           a.beta1, a.beta2);
+                           a.v_fresh, a.v, a.seg_off, a.n_seg, a.c_prev, keys, wg_max, a.N, a.lr,
+                           a.eps, a.beta1, a.beta2);
     else
         hipLaunchKernelGGL(lamb_kernel<true>, grid, dim3(kThreads), 0, st, a.x, a.m, a.m_prev,
-                           a.v_fresh, a.v, a.seg_off, a.n_seg, a.c_prev, keys, a.N, a.lr, a.eps,
-                           a.beta1, a.beta2);
-    hipLaunchKernelGGL(lamb_finalize_kernel, dim3((a.n_seg + 255) / 256), dim3(256), 0, st, keys,
-                       a.n_seg, a.c_avg, a.r_prev, a.c_prev, a.ratio_max, a.err_ratio,
-                       a.r_threshold, a.r_min, a.r_max);
+                           a.v_fresh, a.v, a.seg_off, a.n_seg, a.c_prev, keys, wg_max, a.N, a.lr,
+                           a.eps, a.beta1, a.beta2);
+    hipLaunchKernelGGL(lamb_finalize_kernel, dim3(a.n_seg), dim3(64), 0, st, keys, wg_max,
+                       a.seg_off, n_wg, a.n_seg, a.c_avg, a.r_prev, a.c_prev, a.ratio_max,
+                       a.err_ratio, a.r_threshold, a.r_min, a.r_max);
     if (a.use_c_t)
         hipLaunchKernelGGL(lamb_apply_kernel, grid, dim3(kThreads), 0, st, a.x, a.m, a.v,
                            a.seg_off, a.n_seg, a.c_prev, a.N, (int32_t)kLambTiles, a.lr, a.eps);

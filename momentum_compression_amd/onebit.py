@@ -68,6 +68,7 @@ _SIGNATURES = {
     "frozen_v_step": (_c_i32, [ctypes.POINTER(FrozenVArgs), _c_p, _c_sz, _c_p]),
     "int8_sr_quantize": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32, _c_u64, _c_u32, _c_p]),
     "onebit_workspace_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32]),
+    "frozen_v_workspace_bytes": (_c_sz, [_c_i64, _c_i32]),
     "onebit_strerror": (ctypes.c_char_p, [_c_i32]),
 }
 
@@ -138,6 +139,10 @@ def _nbytes(t) -> int:
 
 def workspace_bytes(N: int, n: int, n_seg: int = 0) -> int:
     return int(load().onebit_workspace_bytes(N, n, n_seg))
+
+
+def frozen_v_workspace_bytes(N: int, n_seg: int) -> int:
+    return int(load().frozen_v_workspace_bytes(N, n_seg))
 
 
 def onebit_compress(m, ef, scales, bits, N: int, n: int, clip: float = 0.0, reset: bool = False,

@@ -136,7 +136,8 @@ class LambState:
                    seg_off=seg_off, c_avg=c_avg, r=torch.ones(S, dtype=torch.float32, device=dev),
                    c=c_avg.clone(), ratio_max=torch.empty(S, dtype=torch.float32, device=dev),
                    err_ratio=torch.ones(S, dtype=torch.float32, device=dev),
-                   ws=torch.empty(max(256, 4 * S + 256), dtype=torch.uint8, device=dev))
+                   ws=torch.empty(max(256, ob.frozen_v_workspace_bytes(x.numel(), S)),
+                                  dtype=torch.uint8, device=dev))
 
     def step(self, mbar: torch.Tensor, lr: float, eps: float, beta1: float, beta2: float,
              thr: float, r_min: float, r_max: float, use_c_t: bool = False, stream=None) -> None:

@@ -20,7 +20,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = ob.declared_functions()
     assert {"onebit_compress", "onebit_server_reduce", "lamb_layer_scale", "frozen_v_step",
-            "int8_sr_quantize", "onebit_workspace_bytes", "onebit_strerror"} <= set(names)
+            "int8_sr_quantize", "onebit_workspace_bytes", "frozen_v_workspace_bytes",
+            "onebit_strerror"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -38,6 +39,15 @@ def test_workspace_bytes(lib):
     assert ob.workspace_bytes(1 << 20, 65) == 0
     big = ob.workspace_bytes(1_311_528_960, 16, 291)
     assert 0 < big < 64 << 20
+
+
+def test_frozen_v_workspace_bytes(lib):
+    # layer keys (rounded to 256 bytes) + one 4-byte slot per 4096 elements
+    assert ob.frozen_v_workspace_bytes(4096 * 300 - 16, 8) == 256 + 1280
+    assert ob.frozen_v_workspace_bytes(336_226_304, 303) == 1280 + 328_448
+    assert ob.frozen_v_workspace_bytes(0, 1) == 256
+    assert ob.frozen_v_workspace_bytes(1022, 4) == 0
+    assert ob.frozen_v_workspace_bytes(1024, 0) == 0
 
 
 def _compress(lib, m=P, ef=P, sc=P, bits=P, N=1 << 12, n=4, clip=0.0, off=None, k=None, nseg=0,

@@ -127,3 +127,41 @@ def test_lamb_basic_special_case_and_nan_layers():
         assert np.isnan(host(st.ratio_max)[0])
         if rmin == rmax == 1.0:
             assert np.all(host(st.r) == 1.0)
+
+
+def test_lamb_layer_maxima_across_workgroups():
+    """Layer maxima when layers are empty, end on a workgroup boundary, share
+    a workgroup, or span hundreds of workgroups (the per-layer reduction over
+    workgroup slots strides more than once), with a ragged end."""
+    dev = device()
+    span = 4096
+    N = 301 * span - 16
+    off = np.array([0, span, span, span + 4, 3 * span, 3 * span + 100, 300 * span + 12,
+                    300 * span + 12, N], dtype=np.int64)
+    S_ = len(off) - 1
+    print(f"[lamb maxima] N={N} layers={S_}", flush=True)
+    g = gen(21, dev)
+    m = torch.randn(N, generator=g, device=dev) * 1e-3
+    mp = torch.randn(N, generator=g, device=dev) * 1e-3
+    v = torch.rand(N, generator=g, device=dev) * 1e-6 + 1e-8
+    # the largest ratio of the big layer sits late in it, in a workgroup of
+    # the last stride of the reduction
+    v[250 * span + 77] = 1.0
+    x = torch.randn(N, generator=g, device=dev)
+    c_avg = torch.linspace(0.5, 2.0, S_, device=dev)
+    st = LambState.create(x.clone(), v, mp, torch.from_numpy(off).to(dev), c_avg)
+    st.step(m, lr=6e-5, eps=1e-6, beta1=0.9, beta2=0.999, thr=0.5, r_min=0.01, r_max=100.0)
+    torch.cuda.synchronize()
+    out = P.lamb_frozen_step(host(x), host(m), host(mp), host(v), host(v), off, host(c_avg),
+                             np.ones(S_, dtype=F32), host(c_avg), 6e-5, 1e-6, 0.9, 0.999, 0.5,
+                             0.01, 100.0)
+    R = host(st.ratio_max)
+    assert np.array_equal(np.isnan(R), np.isnan(out["R"]))
+    assert np.isnan(R[1]) and np.isnan(R[6])  # empty layers
+    ok = ~np.isnan(R)
+    assert np.array_equal(R[ok], out["R"][ok])
+    same_f32(host(st.r), out["r"], "r")
+    same_f32(host(st.c), out["c"], "c")
+    same_f32(host(st.x), out["x"], "x")
+    same_f32(host(st.v_fresh), out["v"], "v")
+    same_f32(host(st.err_ratio), out["err_ratio"], "err_ratio")
