@@ -1,0 +1,150 @@
+"""Pins of the oracle's warmup phase (oracle/warmup.py).
+
+Hand-evaluated steps fix the operand order, the sign of the update, where eps
+sits and which x the trust ratio reads; a constant gradient with dyadic betas
+gives the moments in closed form; beta2 = 1 reduces the Adam warmup step to
+the frozen-variance step; the trust ratio is checked against numpy's norm
+and for scale invariance; k_l against layers of constant magnitude.
+"""
+
+import math
+
+import numpy as np
+
+from oracle import optim as P
+from oracle import warmup as W
+
+F32 = np.float32
+
+
+def a(*v):
+    return np.array(v, dtype=F32)
+
+
+def test_adam_warmup_hand_point():
+    # beta1 = 1/2, beta2 = 3/4: m = (2 + 2)/2 = 2, v = 3 + 1 = 4;
+    # x = 3 - 0.5 * (2 / (2 + 0)) = 2.5
+    out = W.adam_warmup_step(a(3.0), a(2.0), a(4.0), a(2.0), lr=0.5, eps=0.0, beta1=0.5,
+                             beta2=0.75)
+    assert out["m"][0] == 2.0 and out["v"][0] == 4.0 and out["x"][0] == 2.5
+    # eps outside the root: m = 1/2 g = 1, v = 0 -> x = 0 - 1 * (1 / 0.25) = -4
+    out = W.adam_warmup_step(a(0.0), a(0.0), a(0.0), a(2.0), lr=1.0, eps=0.25, beta1=0.5,
+                             beta2=1.0)
+    assert out["m"][0] == 1.0 and out["v"][0] == 0.0 and out["x"][0] == -4.0
+
+
+def test_moments_closed_form_constant_gradient():
+    """g = 1, beta1 = beta2 = 1/2 from zero: m_t = v_t = 1 - 2^-t exactly."""
+    m = v = np.zeros(3, dtype=F32)
+    x = np.ones(3, dtype=F32)
+    ref_x = 1.0
+    lr = 2.0 ** -10
+    for t in range(1, 21):
+        out = W.adam_warmup_step(x, m, v, np.ones(3, dtype=F32), lr, 0.0, 0.5, 0.5)
+        m, v, x = out["m"], out["v"], out["x"]
+        assert np.all(m == 1 - 2.0 ** -t) and np.all(v == 1 - 2.0 ** -t)
+        ref_x -= lr * (1 - 2.0 ** -t) / math.sqrt(1 - 2.0 ** -t)
+        assert np.all(np.abs(x.astype(np.float64) - ref_x) <= t * 2.0 ** -23)
+
+
+def test_beta2_one_is_frozen_step():
+    rng = np.random.default_rng(0)
+    x, m, g = (rng.standard_normal(500).astype(F32) for _ in range(3))
+    v = np.abs(rng.standard_normal(500)).astype(F32)
+    out = W.adam_warmup_step(x, m, v, g, 6e-5, 1e-6, 0.9, 1.0)
+    assert np.array_equal(out["v"], v)
+    b1 = F32(0.9)
+    m_loc = ((b1 * m).astype(F32) + ((F32(1) - b1) * g).astype(F32)).astype(F32)
+    assert np.array_equal(out["m"], m_loc)
+    assert np.array_equal(out["x"], P.adam_frozen_step(x, m_loc, v, 6e-5, 1e-6))
+
+
+def test_lamb_warmup_hand_layers():
+    """Layer 0: x = (3, 4), u = (1, 0) -> c = 5; layer 1: x = 0 -> c = 1;
+    layer 2: u = 0 -> c = 1 and x stays."""
+    x = a(3.0, 4.0, 0.0, 0.0, 7.0, -2.0)
+    m = a(0.5, 0.0, 0.5, 0.5, 0.0, 0.0)
+    v = a(0.25, 0.25, 0.25, 0.25, 1.0, 1.0)
+    g = a(0.5, 0.0, 0.5, 0.5, 0.0, 0.0)
+    out = W.lamb_warmup_step(x, m, v, g, [0, 2, 4, 6], lr=0.25, eps=0.0, beta1=0.5, beta2=0.5)
+    # m = (0.5, 0, 0.5, 0.5, 0, 0); v = (0.25, 0.125, 0.25, 0.25, 0.5, 0.5)
+    assert np.array_equal(out["u"], a(1.0, 0.0, 1.0, 1.0, 0.0, 0.0))
+    assert np.array_equal(out["c"], a(5.0, 1.0, 1.0))
+    assert np.array_equal(out["x"], a(3.0 - 1.25, 4.0, -0.25, -0.25, 7.0, -2.0))
+    assert np.array_equal(out["c_avg"], out["c"])  # first step starts the average
+
+
+def test_trust_ratio_library_norm_and_scale():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(3000).astype(F32)
+    u = (rng.standard_normal(3000) * 1e-3).astype(F32)
+    c = W.trust_ratio(x, u)
+    ref = np.linalg.norm(x.astype(np.float64)) / np.linalg.norm(u.astype(np.float64))
+    assert abs(float(c) - ref) <= 2.0 ** -24 * ref * 1.01
+    # powers of two scale the ratio exactly
+    assert W.trust_ratio((x * F32(4)).astype(F32), u) == F32(4) * c
+    assert W.trust_ratio(x, (u * F32(8)).astype(F32)) == c / F32(8)
+    assert W.trust_ratio(np.zeros(4, F32), u[:4]) == 1 and W.trust_ratio(x[:4], np.zeros(4, F32)) == 1
+
+
+def test_lamb_uses_x_before_update():
+    """The ratio reads x before the step: with x = (3, 4) the update is lr * 5 * u,
+    not a ratio of the updated x."""
+    out = W.lamb_warmup_step(a(3.0, 4.0), a(0.5, 0.0), a(0.25, 0.25), a(0.5, 0.0), [0, 2],
+                             lr=0.5, eps=0.0, beta1=0.5, beta2=0.5)
+    assert out["x"][0] == F32(3.0 - 2.5)
+
+
+def test_coefficient_average_by_hand():
+    c1, c2, c3 = a(2.0, 8.0), a(4.0, 0.0), a(1.0, 1.0)
+    avg = W.coefficient_average(None, c1, 0.5)
+    assert np.array_equal(avg, c1)
+    avg = W.coefficient_average(avg, c2, 0.5)
+    assert np.array_equal(avg, a(3.0, 4.0))
+    avg = W.coefficient_average(avg, c3, 0.75)
+    assert np.array_equal(avg, a(2.5, 3.25))
+
+
+def test_momentum_scale_constant_magnitude_layers():
+    """RMS (1, 1, 4) over layers of 4, 16 and 8 elements: mean 2, k = (2, 2, 1/2).
+    A wrong normalisation (norm instead of RMS) would split layers 0 and 1."""
+    m = np.concatenate([a(1, -1, 1, -1), np.full(16, F32(-1.0)), np.full(8, F32(4.0))])
+    off = [0, 4, 20, 28]
+    assert np.array_equal(W.momentum_scale(m, off), a(2.0, 2.0, 0.5))
+    # sign and scale (power of two) invariance; permutation within a layer
+    assert np.array_equal(W.momentum_scale((-8 * m).astype(F32), off), a(2.0, 2.0, 0.5))
+    perm = m.copy()
+    perm[20:28] = perm[20:28][::-1]
+    assert np.array_equal(W.momentum_scale(perm, off), a(2.0, 2.0, 0.5))
+
+
+def test_momentum_scale_zero_and_empty_layers():
+    m = np.concatenate([np.zeros(4, F32), np.full(4, F32(3.0)), np.full(4, F32(1.0))])
+    off = [0, 4, 4, 8, 12]  # zero layer, empty layer, RMS 3, RMS 1
+    k = W.momentum_scale(m, off)
+    assert np.array_equal(k, a(1.0, 1.0, 2.0 / 3.0, 2.0))
+
+
+def test_momentum_scale_equalises_rms():
+    """After scaling by k_l every layer's RMS equals the mean RMS (to rounding)."""
+    rng = np.random.default_rng(2)
+    sizes = [5, 100, 1000, 64, 3000]
+    sig = [1e-5, 1e-2, 3e-4, 1.0, 2e-3]
+    m = np.concatenate([(rng.standard_normal(d) * s).astype(F32) for d, s in zip(sizes, sig)])
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    k = W.momentum_scale(m, off)
+    rms = [math.sqrt(float(W.exact_rms_ratio(m, off, l))) for l in range(len(sizes))]
+    mean = sum(rms) / len(rms)
+    for l in range(len(sizes)):
+        assert abs(float(k[l]) * rms[l] / mean - 1.0) < 1e-6
+
+
+def test_lamb_direction_uses_new_moments():
+    """u reads the updated m and v: m = 0 -> 1/2, v = 0 -> 1/4 gives u = 1
+    (the old moments would give 0/0)."""
+    out = W.lamb_warmup_step(a(0.0, 2.0), a(0.0, 0.0), a(0.0, 1.0), a(1.0, 0.0), [0, 2],
+                             lr=0.5, eps=0.0, beta1=0.5, beta2=0.75)
+    assert np.array_equal(out["m"], a(0.5, 0.0)) and np.array_equal(out["v"], a(0.25, 0.75))
+    assert np.array_equal(out["u"], a(1.0, 0.0))
+    # ||x|| = 2, ||u|| = 1: c = 2, x = (0 - 0.5 * 2 * 1, 2)
+    assert out["c"][0] == 2.0 and np.array_equal(out["x"], a(-1.0, 2.0))
