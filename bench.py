@@ -122,6 +122,9 @@ B_COMPRESS_GRAD = 12.25        # g 4 + state 4 in + 4 out + 1/8 bit + 1/8 packed
 B_ADAM_PACKED = 12.125         # x 4 in/out, v 4, 1/8 packed momentum
 B_LAMB_STEP = 28.0             # read x, m, m_prev, v_fresh, v_Tw; write x, v_fresh
 B_INT8 = 17.015625             # read g, err; write code, err, deq; scale per 256
+B_WARMUP_ADAM = 28.0           # read x, m, v, g; write x, m, v
+B_WARMUP_LAMB = 40.0           # pass 1: read x, m, v, g, write m, v; pass 2: read x, m, v, write x
+B_MOMENTUM_SCALE = 4.0         # read m
 
 
 def _time_calls(fns, warmup: int, steps: int, stream):
@@ -254,6 +257,55 @@ def measure_fused(steps: int, warmup: int) -> dict:
     return out
 
 
+def measure_warmup(steps: int, warmup: int) -> dict:
+    """Uncompressed warmup steps before the compressed phase: Adam on the
+    335M buffer, LAMB (per-layer trust ratio and coefficient average) on the
+    302-tensor BERT-Large buffer, and the per-layer momentum scale taken at
+    the end of warmup."""
+    import numpy as np
+    import torch
+
+    from momentum_compression_amd import onebit as ob
+    from momentum_compression_amd.state import AdamWarmup, LambWarmup
+    from workloads import configs as C
+    from workloads import synth as S
+
+    dev = torch.device("cuda:0")
+    wa = C.get("bert_large_335M_x8")
+    wlb = C.get("bert_large_lamb_302t_x16")
+    print(f"[bench] rows: warmup {wa.name} N={wa.N}, {wlb.name} N={wlb.N}", file=sys.stderr,
+          flush=True)
+    stream = torch.cuda.current_stream()
+    ad = AdamWarmup.create(S.params(wa, dev))
+    g = S.laplace_gradient(wa.N, 1, 21, dev)
+
+    def adam():
+        ad.step(g, wa.lr, wa.eps, wa.beta1, wa.beta2)
+
+    ms_a = _time_calls([adam], warmup, steps, stream)[0]
+    del ad, g
+    torch.cuda.empty_cache()
+    off = torch.from_numpy(np.array(C.segment_offsets(wlb.segments), dtype=np.int64)).to(dev)
+    lw = LambWarmup.create(S.params(wlb, dev), off)
+    g = S.laplace_gradient(wlb.N, 1, 22, dev)
+    k = torch.empty(off.numel() - 1, device=dev)
+
+    def lamb():
+        lw.step(g, wlb.lr, wlb.eps, wlb.beta1, wlb.beta2, 0.9)
+
+    def scale():
+        ob.lamb_momentum_scale(lw.m, wlb.N, off, off.numel() - 1, k, lw.ws)
+
+    ms = _time_calls([lamb, scale], warmup, steps, stream)
+    out = {"adam_workload": wa.name, "lamb_workload": wlb.name, "layers": len(wlb.segments),
+           "adam_warmup_step": _row(ms_a, B_WARMUP_ADAM * wa.N, wa.N),
+           "lamb_warmup_step": _row(ms[0], B_WARMUP_LAMB * wlb.N, wlb.N),
+           "momentum_scale": _row(ms[1], B_MOMENTUM_SCALE * wlb.N, wlb.N)}
+    del lw, g
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_int8(steps: int, warmup: int) -> dict:
     """Block INT8 stochastic rounding with error feedback and dequantised
     output on 2^30 Laplace gradients (block 256)."""
@@ -306,7 +358,7 @@ def main() -> int:
                                                    "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true",
-                    help="skip the LAMB and INT8 rows measured after the headline step")
+                    help="skip the LAMB, INT8, fused and warmup rows measured after the headline step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -439,7 +491,8 @@ def main() -> int:
         torch.cuda.empty_cache()
         out["rows"] = {"lamb": measure_lamb(max(3, args.steps // 2), 1),
                        "int8": measure_int8(max(3, args.steps // 2), 1),
-                       "fused_adam_from_gradients": measure_fused(max(3, args.steps // 2), 1)}
+                       "fused_adam_from_gradients": measure_fused(max(3, args.steps // 2), 1),
+                       "warmup": measure_warmup(max(3, args.steps // 2), 1)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl)

@@ -305,6 +305,63 @@ int int8_quantize(const float* g, float* err, int8_t* codes, float* block_scales
                   int64_t N, int32_t block, int32_t rounding, uint64_t seed, uint32_t step,
                   void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Warmup phase (uncompressed steps before the compressed phase) and the
+ * inputs it hands over.
+ *
+ * Sources: 1-bit Adam article, section 2.1 (Adam's moment recursions) and its
+ * configuration block (the first warmup steps run without quantisation);
+ * 1-bit LAMB page, algorithm paragraph (v_Tw and the warmup moving average
+ * c_avg of LAMB's layer coefficient are kept for the compressed phase) and
+ * layer-scaling paragraph (a fixed per-layer momentum scale from the average
+ * momentum norm at the end of warmup).
+ *
+ * warmup_adam_step, on the averaged gradient g (every argument [N] float,
+ * device memory, 16-byte aligned; N a multiple of 4):
+ *   m = beta1 m + (1 - beta1) g;  v = beta2 v + (1 - beta2) (g * g)
+ *   x = x - lr * (m / (sqrtf(v) + eps))
+ * binary32, one rounding per operation in this order, 1 - beta rounded once;
+ * no bias correction, no weight decay.  x, m, v are updated in place.
+ * N = 0 returns ONEBIT_OK without launching (pointers may then be NULL).
+ */
+int warmup_adam_step(float* x, float* m, float* v, const float* g, int64_t N, float lr, float eps,
+                     float beta1, float beta2, hipStream_t stream);
+
+/*
+ * warmup_lamb_step: the same m and v, u = m / (sqrtf(v) + eps), then per
+ * layer l = [seg_off[l], seg_off[l+1]) LAMB's trust ratio
+ *   c_l = ||x_l|| / ||u_l||   (x before the step; 1 when either norm is 0)
+ *   x   = x - (lr * c_l) * u
+ *   c_avg_l = first ? c_l : beta_c * c_avg_l + (1 - beta_c) * c_l
+ * The squared norms are summed in binary64 per workgroup and then in a fixed
+ * order per layer (results do not depend on scheduling); c_l is the binary32
+ * rounding of sqrt(Sx) / sqrt(Su).  c [n_seg] receives c_l.
+ * seg_off [n_seg + 1] int64, device memory: seg_off[0] = 0, non-decreasing,
+ * seg_off[n_seg] = N; any offset (a layer edge may fall inside a float4).
+ * ws: at least warmup_workspace_bytes(N, n_seg) bytes, 256-byte aligned.
+ * Two streaming passes (about 40 bytes per element).  With N = 0 every layer
+ * is empty (c = 1) and x, m, v, g may be NULL.
+ */
+int warmup_lamb_step(float* x, float* m, float* v, const float* g, int64_t N,
+                     const int64_t* seg_off, int32_t n_seg, float lr, float eps, float beta1,
+                     float beta2, float beta_c, int32_t first, float* c, float* c_avg, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+/*
+ * lamb_momentum_scale: the per-layer coefficient k_l of the layer-scaling
+ * paragraph, from the momentum m [N] at the end of warmup:
+ *   a_l = sqrt(sum over layer l of m^2 / d_l)   (RMS, binary64)
+ *   k_l = mean of a over layers with a > 0, divided by a_l; 1 if a_l = 0
+ * k [n_seg] float out (the seg_k input of the compression entry points).
+ * Same seg_off and workspace rules as warmup_lamb_step.
+ */
+int lamb_momentum_scale(const float* m, int64_t N, const int64_t* seg_off, int32_t n_seg,
+                        float* k, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes of warmup_lamb_step and lamb_momentum_scale (0 if N < 0,
+ * N is not a multiple of 4 or n_seg < 1): about N / 256 bytes. */
+size_t warmup_workspace_bytes(int64_t N, int32_t n_seg);
+
 /* Workspace bytes needed by onebit_compress(_ex) / onebit_compress_grad /
  * onebit_server_reduce(_ex) for these sizes (0 if the sizes are invalid). */
 size_t onebit_workspace_bytes(int64_t N, int32_t n, int32_t n_seg);

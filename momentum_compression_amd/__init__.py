@@ -23,4 +23,8 @@ from .onebit import (  # noqa: F401
     onebit_server_reduce_ex,
     workspace_bytes,
     frozen_v_workspace_bytes,
+    lamb_momentum_scale,
+    warmup_adam_step,
+    warmup_lamb_step,
+    warmup_workspace_bytes,
 )

@@ -23,7 +23,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libonebit.so")
 
 SOURCES = ["api.hip", "compress.hip", "finalize.hip", "server.hip", "scale.hip", "step.hip",
-           "int8.hip"]
+           "int8.hip", "warmup.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -37,6 +37,18 @@ size_t lamb_ws_bytes(int64_t N, int32_t n_seg) {
            round_up((size_t)lamb_workgroups(N) * sizeof(uint32_t));
 }
 
+// Warmup layer passes: plan table, per-workgroup binary64 pairs, layer RMS.
+WarmupWs split_warmup_ws(void* ws, int64_t N, int32_t n_seg) {
+    char* p = static_cast<char*>(ws);
+    WarmupWs w;
+    w.wg_first = reinterpret_cast<int64_t*>(p);
+    p += round_up((size_t)(n_seg + 1) * sizeof(int64_t));
+    w.part = reinterpret_cast<double2*>(p);
+    p += round_up((size_t)layer_grid(N, n_seg) * 2 * sizeof(double));
+    w.rms = reinterpret_cast<double*>(p);
+    return w;
+}
+
 size_t partial_bytes(int64_t N, int32_t n) {
     const int64_t L = N / n;
     const ChunkPlan pw = make_plan(L, (int64_t)n * n);
@@ -264,6 +276,69 @@ int int8_sr_quantize(const float* g, float* err, int8_t* codes, float* block_sca
     if (block == 0) return ONEBIT_E_SIZE;  // the per-tensor variant needs a workspace
     return int8_quantize(g, err, codes, block_scales, deq, N, block, 0, seed, step, nullptr, 0,
                          stream);
+}
+
+// ---------------------------------------------------------------- warmup
+
+size_t warmup_workspace_bytes(int64_t N, int32_t n_seg) {
+    if (N < 0 || (N % 4) || n_seg < 1) return 0;
+    return round_up((size_t)(n_seg + 1) * sizeof(int64_t)) +
+           round_up((size_t)layer_grid(N, n_seg) * 2 * sizeof(double)) +
+           round_up((size_t)n_seg * sizeof(double));
+}
+
+int warmup_adam_step(float* x, float* m, float* v, const float* g, int64_t N, float lr, float eps,
+                     float beta1, float beta2, hipStream_t stream) {
+    if (N < 0 || (N % 4)) return ONEBIT_E_SIZE;
+    if (N == 0) return ONEBIT_OK;
+    if (!x || !m || !v || !g) return ONEBIT_E_NULL;
+    if (!aligned(x, 16) || !aligned(m, 16) || !aligned(v, 16) || !aligned(g, 16))
+        return ONEBIT_E_ALIGN;
+    return hip_status(launch_warmup_adam(x, m, v, g, N, lr, eps, beta1, beta2, stream));
+}
+
+int warmup_lamb_step(float* x, float* m, float* v, const float* g, int64_t N,
+                     const int64_t* seg_off, int32_t n_seg, float lr, float eps, float beta1,
+                     float beta2, float beta_c, int32_t first, float* c, float* c_avg, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+    if (N < 0 || (N % 4)) return ONEBIT_E_SIZE;
+    if ((N > 0 && (!x || !m || !v || !g)) || !seg_off || !c || !c_avg) return ONEBIT_E_NULL;
+    if (n_seg < 1 || (first != 0 && first != 1)) return ONEBIT_E_ARG;
+    if (!aligned(x, 16) || !aligned(m, 16) || !aligned(v, 16) || !aligned(g, 16) ||
+        !aligned(seg_off, 8) || !aligned(c, 4) || !aligned(c_avg, 4))
+        return ONEBIT_E_ALIGN;
+    if (!ws || ws_bytes < warmup_workspace_bytes(N, n_seg)) return ONEBIT_E_WORKSPACE;
+    if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
+    WarmupLambArgs a;
+    a.x = x;
+    a.m = m;
+    a.v = v;
+    a.g = g;
+    a.seg_off = seg_off;
+    a.n_seg = n_seg;
+    a.N = N;
+    a.lr = lr;
+    a.eps = eps;
+    a.beta1 = beta1;
+    a.beta2 = beta2;
+    a.beta_c = beta_c;
+    a.first = first;
+    a.c = c;
+    a.c_avg = c_avg;
+    // N == 0: every layer is empty, c = 1 (the coefficient of a zero norm)
+    return hip_status(launch_warmup_lamb(a, split_warmup_ws(ws, N, n_seg), stream));
+}
+
+int lamb_momentum_scale(const float* m, int64_t N, const int64_t* seg_off, int32_t n_seg,
+                        float* k, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (N < 0 || (N % 4)) return ONEBIT_E_SIZE;
+    if ((N > 0 && !m) || !seg_off || !k) return ONEBIT_E_NULL;
+    if (n_seg < 1) return ONEBIT_E_ARG;
+    if (!aligned(m, 16) || !aligned(seg_off, 8) || !aligned(k, 4)) return ONEBIT_E_ALIGN;
+    if (!ws || ws_bytes < warmup_workspace_bytes(N, n_seg)) return ONEBIT_E_WORKSPACE;
+    if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
+    return hip_status(
+        launch_momentum_scale(m, N, seg_off, n_seg, k, split_warmup_ws(ws, N, n_seg), stream));
 }
 
 }  // extern "C"

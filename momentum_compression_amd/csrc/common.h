@@ -167,4 +167,36 @@ hipError_t launch_int8(const float* g, float* err, int8_t* codes, float* scales,
                        int64_t N, int32_t block, uint64_t seed, uint32_t step, bool nearest,
                        uint32_t* tensor_max, hipStream_t st);
 
+// Warmup phase: layer passes with one workgroup range inside one layer.
+struct WarmupLambArgs {
+    float* x;
+    float* m;
+    float* v;
+    const float* g;
+    const int64_t* seg_off;
+    int32_t n_seg;
+    int64_t N;
+    float lr, eps, beta1, beta2, beta_c;
+    int32_t first;
+    float* c;      // [n_seg] this step's coefficients
+    float* c_avg;  // [n_seg] moving average, in/out
+};
+
+struct WarmupWs {
+    int64_t* wg_first;  // [n_seg + 1] first workgroup of each layer
+    double2* part;      // [layer_grid] per-workgroup binary64 sums
+    double* rms;        // [n_seg]
+};
+
+// Upper bound on the workgroups of a layer pass (launch grid and slot count).
+int64_t layer_grid(int64_t N, int32_t n_seg);
+
+hipError_t launch_warmup_adam(float* x, float* m, float* v, const float* g, int64_t N, float lr,
+                              float eps, float b1, float b2, hipStream_t st);
+
+hipError_t launch_warmup_lamb(const WarmupLambArgs& a, const WarmupWs& ws, hipStream_t st);
+
+hipError_t launch_momentum_scale(const float* m, int64_t N, const int64_t* seg_off, int32_t n_seg,
+                                 float* k, const WarmupWs& ws, hipStream_t st);
+
 }  // namespace onebit

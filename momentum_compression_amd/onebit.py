@@ -69,6 +69,11 @@ _SIGNATURES = {
     "int8_sr_quantize": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32, _c_u64, _c_u32, _c_p]),
     "onebit_workspace_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32]),
     "frozen_v_workspace_bytes": (_c_sz, [_c_i64, _c_i32]),
+    "warmup_adam_step": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_f, _c_f, _c_f, _c_f, _c_p]),
+    "warmup_lamb_step": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i32, _c_f, _c_f, _c_f,
+                                  _c_f, _c_f, _c_i32, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "lamb_momentum_scale": (_c_i32, [_c_p, _c_i64, _c_p, _c_i32, _c_p, _c_p, _c_sz, _c_p]),
+    "warmup_workspace_bytes": (_c_sz, [_c_i64, _c_i32]),
     "onebit_strerror": (ctypes.c_char_p, [_c_i32]),
 }
 
@@ -236,3 +241,25 @@ def int8_quantize(g, err, codes, block_scales, deq, N: int, block: int, rounding
         _ptr(g), _ptr(err), _ptr(codes), _ptr(block_scales), _ptr(deq), N, block, rounding,
         seed & 0xFFFFFFFFFFFFFFFF, step & 0xFFFFFFFF, _ptr(ws), _nbytes(ws) if ws is not None else 0,
         _stream(stream)))
+
+
+def warmup_workspace_bytes(N: int, n_seg: int) -> int:
+    return int(load().warmup_workspace_bytes(N, n_seg))
+
+
+def warmup_adam_step(x, m, v, g, N: int, lr: float, eps: float, beta1: float, beta2: float,
+                     stream=None) -> None:
+    _check("warmup_adam_step", load().warmup_adam_step(
+        _ptr(x), _ptr(m), _ptr(v), _ptr(g), N, lr, eps, beta1, beta2, _stream(stream)))
+
+
+def warmup_lamb_step(x, m, v, g, N: int, seg_off, n_seg: int, lr: float, eps: float, beta1: float,
+                     beta2: float, beta_c: float, first: bool, c, c_avg, ws, stream=None) -> None:
+    _check("warmup_lamb_step", load().warmup_lamb_step(
+        _ptr(x), _ptr(m), _ptr(v), _ptr(g), N, _ptr(seg_off), n_seg, lr, eps, beta1, beta2,
+        beta_c, 1 if first else 0, _ptr(c), _ptr(c_avg), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def lamb_momentum_scale(m, N: int, seg_off, n_seg: int, k, ws, stream=None) -> None:
+    _check("lamb_momentum_scale", load().lamb_momentum_scale(
+        _ptr(m), N, _ptr(seg_off), n_seg, _ptr(k), _ptr(ws), _nbytes(ws), _stream(stream)))

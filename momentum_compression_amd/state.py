@@ -148,3 +148,70 @@ class LambState:
                          r_prev=self.r, c_prev=self.c, ratio_max=self.ratio_max,
                          r_threshold=thr, r_min=r_min, r_max=r_max, use_c_t=use_c_t,
                          err_ratio=self.err_ratio, ws=self.ws, stream=stream)
+
+
+@dataclass
+class AdamWarmup:
+    """Uncompressed Adam steps before the compressed phase (1-bit Adam
+    article, section 2.1 and its warmup setting); ``v`` at the end is the
+    frozen variance v_Tw of the compressed steps."""
+
+    x: torch.Tensor  # [N] parameters
+    m: torch.Tensor  # [N] momentum
+    v: torch.Tensor  # [N] variance
+
+    @classmethod
+    def create(cls, x: torch.Tensor) -> "AdamWarmup":
+        return cls(x=x, m=torch.zeros_like(x), v=torch.zeros_like(x))
+
+    def step(self, g: torch.Tensor, lr: float, eps: float, beta1: float, beta2: float,
+             stream=None) -> None:
+        """One step on the gradient averaged over the data-parallel group."""
+        ob.warmup_adam_step(self.x, self.m, self.v, g, self.x.numel(), lr, eps, beta1, beta2,
+                            stream=stream)
+
+
+@dataclass
+class LambWarmup:
+    """Uncompressed LAMB steps before the compressed phase, and what they hand
+    over (1-bit LAMB page): v_Tw, the coefficient average c_avg and the
+    per-layer momentum scale k_l."""
+
+    x: torch.Tensor        # [N] parameters
+    m: torch.Tensor        # [N] momentum
+    v: torch.Tensor        # [N] variance
+    seg_off: torch.Tensor  # int64 [S+1]
+    c: torch.Tensor        # [S] coefficients of the last step
+    c_avg: torch.Tensor    # [S] their moving average
+    ws: torch.Tensor
+    steps: int = 0
+
+    @classmethod
+    def create(cls, x: torch.Tensor, seg_off: torch.Tensor) -> "LambWarmup":
+        S = seg_off.numel() - 1
+        dev = x.device
+        return cls(x=x, m=torch.zeros_like(x), v=torch.zeros_like(x), seg_off=seg_off,
+                   c=torch.ones(S, dtype=torch.float32, device=dev),
+                   c_avg=torch.ones(S, dtype=torch.float32, device=dev),
+                   ws=torch.empty(max(256, ob.warmup_workspace_bytes(x.numel(), S)),
+                                  dtype=torch.uint8, device=dev))
+
+    def step(self, g: torch.Tensor, lr: float, eps: float, beta1: float, beta2: float,
+             beta_c: float, stream=None) -> None:
+        """One step on the averaged gradient; the first starts the average."""
+        ob.warmup_lamb_step(self.x, self.m, self.v, g, self.x.numel(), self.seg_off,
+                            self.seg_off.numel() - 1, lr, eps, beta1, beta2, beta_c,
+                            self.steps == 0, self.c, self.c_avg, self.ws, stream=stream)
+        self.steps += 1
+
+    def momentum_scale(self, stream=None) -> torch.Tensor:
+        """k_l from the momentum at the end of warmup."""
+        S = self.seg_off.numel() - 1
+        k = torch.empty(S, dtype=torch.float32, device=self.x.device)
+        ob.lamb_momentum_scale(self.m, self.x.numel(), self.seg_off, S, k, self.ws, stream=stream)
+        return k
+
+    def to_compressed(self) -> LambState:
+        """The compressed phase's state: v_Tw = v, r = 1, c = c_avg, fresh
+        variance v_Tw, previous global momentum m_Tw."""
+        return LambState.create(self.x, self.v, self.m.clone(), self.seg_off, self.c_avg.clone())

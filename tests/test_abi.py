@@ -153,3 +153,48 @@ def test_extended_entries_validation(lib):
     assert q(P, None, P, P, None, 4096, 256, 2, 1, 1, None, 0, None) == ob.ONEBIT_E_ARG
     assert q(P, None, P, P, None, 4098, 0, 0, 1, 1, P, 256, None) == ob.ONEBIT_E_SIZE
     assert lib.int8_sr_quantize(P, None, P, P, None, 4096, 0, 1, 1, None) == ob.ONEBIT_E_SIZE
+
+
+def test_warmup_validation(lib):
+    """Only argument errors (no launch): P is not a device address."""
+    f = lib.warmup_adam_step
+    assert f(P, P, P, P, 1022, 1e-3, 1e-6, 0.9, 0.999, None) == ob.ONEBIT_E_SIZE
+    assert f(P, None, P, P, 1024, 1e-3, 1e-6, 0.9, 0.999, None) == ob.ONEBIT_E_NULL
+    assert f(P, P, P, P + 4, 1024, 1e-3, 1e-6, 0.9, 0.999, None) == ob.ONEBIT_E_ALIGN
+    assert f(P, P, P, P, 0, 1e-3, 1e-6, 0.9, 0.999, None) == ob.ONEBIT_OK  # empty: no launch
+
+    def lamb(**kw):
+        a = dict(x=P, m=P, v=P, g=P, N=4096, off=P, nseg=3, first=1, c=P, cavg=P, ws=P,
+                 wsb=1 << 30)
+        a.update(kw)
+        return lib.warmup_lamb_step(a["x"], a["m"], a["v"], a["g"], a["N"], a["off"], a["nseg"],
+                                    1e-3, 1e-6, 0.9, 0.999, 0.9, a["first"], a["c"], a["cavg"],
+                                    a["ws"], a["wsb"], None)
+    assert lamb(N=4098) == ob.ONEBIT_E_SIZE
+    assert lamb(off=None) == ob.ONEBIT_E_NULL
+    assert lamb(c=None) == ob.ONEBIT_E_NULL
+    assert lamb(nseg=0) == ob.ONEBIT_E_ARG
+    assert lamb(first=2) == ob.ONEBIT_E_ARG
+    assert lamb(off=P + 4) == ob.ONEBIT_E_ALIGN
+    assert lamb(ws=None) == ob.ONEBIT_E_WORKSPACE
+    assert lamb(wsb=256) == ob.ONEBIT_E_WORKSPACE
+    assert lamb(ws=P + 128) == ob.ONEBIT_E_ALIGN
+
+    g = lib.lamb_momentum_scale
+    assert g(P, 4098, P, 3, P, P, 1 << 30, None) == ob.ONEBIT_E_SIZE
+    assert g(P, 4096, None, 3, P, P, 1 << 30, None) == ob.ONEBIT_E_NULL
+    assert g(P, 4096, P, 0, P, P, 1 << 30, None) == ob.ONEBIT_E_ARG
+    assert g(P, 4096, P, 3, P, P, 64, None) == ob.ONEBIT_E_WORKSPACE
+
+
+def test_warmup_workspace_bytes(lib):
+    # plan (n_seg + 1 int64), one binary64 pair per workgroup of the upper
+    # bound ceil(N / 4096) + 2 n_seg + 1, layer RMS (n_seg binary64); each
+    # part rounded up to 256 bytes
+    def rup(x):
+        return (x + 255) // 256 * 256
+    for N, S in [(4096, 3), (336_226_304, 303), (0, 1)]:
+        grid = -(-N // 4096) + 2 * S + 1
+        assert ob.warmup_workspace_bytes(N, S) == rup(8 * (S + 1)) + rup(16 * grid) + rup(8 * S)
+    assert ob.warmup_workspace_bytes(1022, 3) == 0
+    assert ob.warmup_workspace_bytes(1024, 0) == 0

@@ -240,3 +240,74 @@ def test_bert_large_335M_x8_from_gradients():
         mbar_prev = mbar_now.copy()
     del grp, x, v, g, sig
     _free()
+
+
+def test_warmup_fullsize():
+    """The warmup rows the bench times, at full size: Adam on the 335M
+    buffer (sampled elements against the oracle), LAMB on the 302-tensor
+    buffer (whole sampled layers through the oracle: m, v, x, c, c_avg;
+    among them the 31M-element word embedding, small LayerNorm vectors and
+    the pad), and k_l for every layer against a binary64 reference."""
+    from momentum_compression_amd.state import AdamWarmup, LambWarmup
+    from oracle import warmup as W
+
+    dev = device()
+    wa = C.get("bert_large_335M_x8")
+    N = wa.N
+    _need(dev, N * 4 * 8)
+    print(f"[fullsize warmup] adam N={N}", flush=True)
+    hp = dict(lr=wa.lr, eps=wa.eps, beta1=wa.beta1, beta2=wa.beta2)
+    ad = AdamWarmup.create(S.params(wa, dev))
+    rng = np.random.default_rng(4)
+    idx_d = torch.from_numpy(np.sort(rng.choice(N, size=1 << 20, replace=False))).to(dev)
+    for t in range(1, 3):
+        g = S.laplace_gradient(N, t, 21, dev)
+        xb, mb, vb = host(ad.x[idx_d]), host(ad.m[idx_d]), host(ad.v[idx_d])
+        ad.step(g, **hp)
+        torch.cuda.synchronize()
+        o = W.adam_warmup_step(xb, mb, vb, host(g[idx_d]), **hp)
+        for key in ("x", "m", "v"):
+            same_f32(host(getattr(ad, key)[idx_d]), o[key], f"adam warmup t={t} {key} (sampled)")
+    del ad, g
+    _free()
+
+    wl = C.get("bert_large_lamb_302t_x16")
+    N = wl.N
+    off = np.array(C.segment_offsets(wl.segments), dtype=np.int64)
+    Sg = len(off) - 1
+    print(f"[fullsize warmup] lamb N={N} layers={Sg}", flush=True)
+    lw = LambWarmup.create(S.params(wl, dev), torch.from_numpy(off).to(dev))
+    layers = [0, 1, 3, 4, 5, 6, 150, Sg - 3, Sg - 2, Sg - 1]
+    cav = {l: None for l in layers}
+    for t in range(1, 3):
+        g = S.laplace_gradient(N, t, 22, dev)
+        before = {}
+        for l in layers:
+            sl = slice(int(off[l]), int(off[l + 1]))
+            before[l] = (host(lw.x[sl]), host(lw.m[sl]), host(lw.v[sl]), host(g[sl]))
+        lw.step(g, wl.lr, wl.eps, wl.beta1, wl.beta2, 0.9)
+        torch.cuda.synchronize()
+        c = host(lw.c)
+        c_avg = host(lw.c_avg)
+        for l in layers:
+            sl = slice(int(off[l]), int(off[l + 1]))
+            xb, mb, vb, gb = before[l]
+            o = W.lamb_warmup_step(xb, mb, vb, gb, [0, xb.size], wl.lr, wl.eps, wl.beta1,
+                                   wl.beta2, c_avg=cav[l], beta_c=0.9)
+            tag = f"lamb warmup t={t} layer {l} ({xb.size})"
+            same_f32(c[l:l + 1], o["c"], f"{tag} c")
+            same_f32(c_avg[l:l + 1], o["c_avg"], f"{tag} c_avg")
+            same_f32(host(lw.m[sl]), o["m"], f"{tag} m")
+            same_f32(host(lw.v[sl]), o["v"], f"{tag} v")
+            same_f32(host(lw.x[sl]), o["x"], f"{tag} x")
+            cav[l] = o["c_avg"]
+    k = host(lw.momentum_scale())
+    torch.cuda.synchronize()
+    mh = host(lw.m).astype(np.float64)
+    rms = np.array([np.sqrt(np.dot(mh[int(off[l]):int(off[l + 1])], mh[int(off[l]):int(off[l + 1])])
+                            / max(1, int(off[l + 1] - off[l]))) for l in range(Sg)])
+    ok = rms > 0
+    want = np.where(ok, rms[ok].mean() / np.where(ok, rms, 1.0), 1.0)
+    assert np.all(np.abs(k.astype(np.float64) - want) <= 1e-6 * np.abs(want)), "k_l"
+    del lw, g, mh
+    _free()
