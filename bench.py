@@ -198,12 +198,26 @@ def measure_lamb(steps: int, warmup: int) -> dict:
         st.step(grp.mbar, wl.lr, wl.eps, wl.beta1, wl.beta2, wl.r_threshold, wl.r_min, wl.r_max)
         t[0] += 1
 
-    ms = _time_calls([comp, serv, dec, lamb], warmup, steps, stream)
+    # step-ratio-scaled error feedback: the carried errors times c_{t-1}/c_t
+    # per layer, at both levels (the same bytes as the plain kernels)
+    def comp_ers():
+        grp.seg_err_ratio = st.err_ratio
+        grp.compress(m, t[0])
+        grp.seg_err_ratio = None
+
+    def serv_ers():
+        grp.seg_err_ratio = st.err_ratio
+        grp.server(t[0], decompress=False)
+        grp.seg_err_ratio = None
+
+    ms = _time_calls([comp, serv, dec, lamb, comp_ers, serv_ers], warmup, steps, stream)
     out = {"workload": wl.name, "N": N, "workers": n, "layers": len(wl.segments),
            "compress_x_k": _row(ms[0], B_COMPRESS * n * N, n * N),
            "server": _row(ms[1], b_server(n) * N, N),
            "decompress_div_k": _row(ms[2], B_DECOMPRESS * N, N),
-           "lamb_step": _row(ms[3], B_LAMB_STEP * N, N)}
+           "lamb_step": _row(ms[3], B_LAMB_STEP * N, N),
+           "compress_x_k_step_ratio_ef": _row(ms[4], B_COMPRESS * n * N, n * N),
+           "server_step_ratio_ef": _row(ms[5], b_server(n) * N, N)}
     del grp, st, m
     torch.cuda.empty_cache()
     return out
@@ -245,13 +259,20 @@ def measure_fused(steps: int, warmup: int) -> dict:
         grp.adam_step_packed(x, v, wl.lr, wl.eps)
         t[0] += 1
 
-    ms = _time_calls([comp, serv, adam], warmup, steps, stream)
-    step_ms = sum(ms)
+    # the unscaled +-1 variant of the worker compression
+    def comp_unit():
+        grp.unit_scale = True
+        grp.compress_grad(g, t[0], wl.beta1)
+        grp.unit_scale = False
+
+    ms = _time_calls([comp, serv, adam, comp_unit], warmup, steps, stream)
+    step_ms = sum(ms[:3])
     out = {"workload": wl.name, "N": N, "workers": n, "step_ms": round(step_ms, 4),
            "worker_elements_per_s": n * N / (step_ms * 1e-3),
            "compress_grad": _row(ms[0], B_COMPRESS_GRAD * n * N, n * N),
            "server": _row(ms[1], b_server(n) * N, N),
-           "adam_packed": _row(ms[2], B_ADAM_PACKED * N, N)}
+           "adam_packed": _row(ms[2], B_ADAM_PACKED * N, N),
+           "compress_grad_unit_scale": _row(ms[3], B_COMPRESS_GRAD * n * N, n * N)}
     del grp, g, x, v
     torch.cuda.empty_cache()
     return out

@@ -238,28 +238,41 @@ __global__ __launch_bounds__(kThreads) void lamb_kernel(
 // One wave per layer: the maximum over the slots of the workgroups that
 // overlap the layer (those inside it hold their maximum, the others 0),
 // combined with the key the boundary workgroups raised atomically.
-__global__ __launch_bounds__(64) void lamb_finalize_kernel(
+__global__ __launch_bounds__(kThreads) void lamb_finalize_kernel(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ wg_max,
     const int64_t* __restrict__ seg_off, int64_t n_wg, int32_t n_seg,
     const float* __restrict__ c_avg, float* __restrict__ r_prev, float* __restrict__ c_prev,
     float* __restrict__ ratio_max, float* __restrict__ err_ratio, float thr, float r_min,
     float r_max) {
+    __shared__ uint32_t red[kThreads / 64];
     const int l = blockIdx.x;
     if (l >= n_seg) return;
     constexpr int64_t span = (int64_t)kLambTiles * kTile;
+    constexpr int kBatch = 8;  // slot loads in flight per thread
     const int64_t a = seg_off[l], b = seg_off[l + 1];
     uint32_t km = 0;
     if (b > a) {
         const int64_t w0 = a > 0 ? a / span : 0;
         int64_t w1 = (b - 1) / span;
         if (w1 > n_wg - 1) w1 = n_wg - 1;
-        for (int64_t w = w0 + threadIdx.x; w <= w1; w += 64) {
-            const uint32_t v = wg_max[w];
-            km = v > km ? v : km;
+        for (int64_t wb = w0; wb <= w1; wb += (int64_t)kThreads * kBatch) {
+            uint32_t v[kBatch];
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                const int64_t w = wb + (int64_t)q * kThreads + threadIdx.x;
+                v[q] = w <= w1 ? wg_max[w] : 0u;
+            }
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) km = v[q] > km ? v[q] : km;
         }
     }
     km = wave_max_u32(km);
+    if (lane_id() == 0) red[threadIdx.x >> 6] = km;
+    __syncthreads();
     if (threadIdx.x != 0) return;
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) km = red[w] > km ? red[w] : km;
+    km = red[0] > km ? red[0] : km;
     const uint32_t k0 = keys[l];
     const uint32_t key = k0 > km ? k0 : km;
     const float R = key ? key_float(key) : __uint_as_float(0x7FC00000u);
@@ -324,7 +337,7 @@ hipError_t launch_lamb(const onebit_frozen_v_args& a, uint32_t* keys, uint32_t* 
         hipLaunchKernelGGL(lamb_kernel<true>, grid, dim3(kThreads), 0, st, a.x, a.m, a.m_prev,
                            a.v_fresh, a.v, a.seg_off, a.n_seg, a.c_prev, keys, wg_max, a.N, a.lr,
                            a.eps, a.beta1, a.beta2);
-    hipLaunchKernelGGL(lamb_finalize_kernel, dim3(a.n_seg), dim3(64), 0, st, keys, wg_max,
+    hipLaunchKernelGGL(lamb_finalize_kernel, dim3(a.n_seg), dim3(kThreads), 0, st, keys, wg_max,
                        a.seg_off, n_wg, a.n_seg, a.c_avg, a.r_prev, a.c_prev, a.ratio_max,
                        a.err_ratio, a.r_threshold, a.r_min, a.r_max);
     if (a.use_c_t)

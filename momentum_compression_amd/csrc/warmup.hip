@@ -69,6 +69,32 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
     return s;
 }
 
+// Sum over the workgroup of part[w].x (and .y) for w in [w0, w1), in a fixed
+// order: each thread adds the slots w0 + tid + 256 q in ascending q (8 loads
+// in flight), then block_sum_f64; valid in thread 0.
+__device__ __forceinline__ double2 slot_sum(const double2* __restrict__ part, int64_t w0,
+                                            int64_t w1, double* red) {
+    constexpr int kBatch = 8;
+    double sx = 0.0, sy = 0.0;
+    for (int64_t wb = w0; wb < w1; wb += (int64_t)kThreads * kBatch) {
+        double2 p[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int64_t w = wb + (int64_t)q * kThreads + threadIdx.x;
+            p[q] = w < w1 ? part[w] : make_double2(0.0, 0.0);
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            sx += p[q].x;
+            sy += p[q].y;
+        }
+    }
+    const double tx = block_sum_f64(sx, red);
+    __syncthreads();  // red is reused
+    const double ty = block_sum_f64(sy, red);
+    return make_double2(tx, ty);
+}
+
 // The workgroup's layer and element range; false for the spare workgroups of
 // the launch (the grid is an upper bound on the plan's total).
 struct WgRange {
@@ -238,23 +264,19 @@ __global__ __launch_bounds__(kThreads) void warmup_lamb_moments_kernel(
     if (threadIdx.x == 0) part[blockIdx.x] = make_double2(tx, tu);
 }
 
-// One wave per layer: the layer's slots in order, c and the moving average.
-__global__ __launch_bounds__(64) void warmup_lamb_finalize_kernel(
+// One workgroup per layer: the layer's slots in a fixed order, c and the
+// moving average.
+__global__ __launch_bounds__(kThreads) void warmup_lamb_finalize_kernel(
     const double2* __restrict__ part, const int64_t* __restrict__ wg_first, int32_t n_seg,
     int64_t n_wg, float* __restrict__ c_out, float* __restrict__ c_avg, float b_c,
     int32_t first) {
+    __shared__ double red[kThreads / 64];
     const int l = blockIdx.x;
     if (l >= n_seg) return;
     const int64_t w1 = wg_first[l + 1] < n_wg ? wg_first[l + 1] : n_wg;
-    double sx = 0.0, su = 0.0;
-    for (int64_t w = wg_first[l] + threadIdx.x; w < w1; w += 64) {
-        const double2 p = part[w];
-        sx += p.x;
-        su += p.y;
-    }
-    sx = wave_sum_f64(sx);
-    su = wave_sum_f64(su);
+    const double2 t = slot_sum(part, wg_first[l], w1, red);
     if (threadIdx.x != 0) return;
+    const double sx = t.x, su = t.y;
     const float c = (sx == 0.0 || su == 0.0) ? 1.0f : (float)(sqrt(sx) / sqrt(su));
     c_out[l] = c;
     c_avg[l] = first ? c : b_c * c_avg[l] + (1.0f - b_c) * c;
@@ -323,18 +345,16 @@ __global__ __launch_bounds__(kThreads) void momentum_sq_kernel(
     if (threadIdx.x == 0) part[blockIdx.x] = make_double2(t, 0.0);
 }
 
-// Momentum scale, pass 2: one wave per layer, rms[l] = sqrt(sum / d_l).
-__global__ __launch_bounds__(64) void momentum_rms_kernel(const double2* __restrict__ part,
-                                                          const int64_t* __restrict__ wg_first,
-                                                          const int64_t* __restrict__ seg_off,
-                                                          int32_t n_seg, int64_t N, int64_t n_wg,
-                                                          double* __restrict__ rms) {
+// Momentum scale, pass 2: one workgroup per layer, rms[l] = sqrt(sum / d_l).
+__global__ __launch_bounds__(kThreads) void momentum_rms_kernel(
+    const double2* __restrict__ part, const int64_t* __restrict__ wg_first,
+    const int64_t* __restrict__ seg_off, int32_t n_seg, int64_t N, int64_t n_wg,
+    double* __restrict__ rms) {
+    __shared__ double red[kThreads / 64];
     const int l = blockIdx.x;
     if (l >= n_seg) return;
     const int64_t w1 = wg_first[l + 1] < n_wg ? wg_first[l + 1] : n_wg;
-    double s = 0.0;
-    for (int64_t w = wg_first[l] + threadIdx.x; w < w1; w += 64) s += part[w].x;
-    s = wave_sum_f64(s);
+    const double s = slot_sum(part, wg_first[l], w1, red).x;
     if (threadIdx.x != 0) return;
     int64_t lo, hi;
     layer_bounds(seg_off, l, N, lo, hi);
@@ -393,7 +413,7 @@ hipError_t launch_warmup_lamb(const WarmupLambArgs& a, const WarmupWs& ws, hipSt
                        ws.wg_first);
     hipLaunchKernelGGL(warmup_lamb_moments_kernel, grid, dim3(kThreads), 0, st, a.x, a.m, a.v, a.g,
                        a.seg_off, ws.wg_first, a.n_seg, a.N, ws.part, a.eps, a.beta1, a.beta2);
-    hipLaunchKernelGGL(warmup_lamb_finalize_kernel, dim3(a.n_seg), dim3(64), 0, st, ws.part,
+    hipLaunchKernelGGL(warmup_lamb_finalize_kernel, dim3(a.n_seg), dim3(kThreads), 0, st, ws.part,
                        ws.wg_first, a.n_seg, n_wg, a.c, a.c_avg, a.beta_c, a.first);
     hipLaunchKernelGGL(warmup_lamb_apply_kernel, grid, dim3(kThreads), 0, st, a.x, a.m, a.v,
                        a.seg_off, ws.wg_first, a.n_seg, a.N, a.c, a.lr, a.eps);
@@ -407,7 +427,7 @@ hipError_t launch_momentum_scale(const float* m, int64_t N, const int64_t* seg_o
                        ws.wg_first);
     hipLaunchKernelGGL(momentum_sq_kernel, dim3((unsigned)n_wg), dim3(kThreads), 0, st, m, seg_off,
                        ws.wg_first, n_seg, N, ws.part);
-    hipLaunchKernelGGL(momentum_rms_kernel, dim3(n_seg), dim3(64), 0, st, ws.part, ws.wg_first,
+    hipLaunchKernelGGL(momentum_rms_kernel, dim3(n_seg), dim3(kThreads), 0, st, ws.part, ws.wg_first,
                        seg_off, n_seg, N, n_wg, ws.rms);
     hipLaunchKernelGGL(momentum_scale_kernel, dim3(1), dim3(kThreads), 0, st, ws.rms, n_seg, k);
     return hipGetLastError();
