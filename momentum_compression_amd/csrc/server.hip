@@ -18,7 +18,22 @@ namespace onebit {
 // Words of the kUnroll tiles a workgroup processes together, for every
 // worker, are staged through LDS with coalesced loads (32 consecutive words
 // per worker and tile); each lane then reads its word per worker from LDS.
-template <bool ERS>
+//
+// Within one chunk every worker's scale is fixed, so the binary32 sum over
+// the first m = min(n, 8) workers, taken in order from +0, depends only on
+// their m sign bits: a 2^m-entry LDS table, built once per workgroup in the
+// same order, gives it exactly.  A lane forms the 4 table indices of its 4
+// elements at once: worker i's nibble (the 4 bits at the lane's offset) is
+// spread to bit i of bytes 0..3 by a multiplication with 0x204081 and the
+// mask 0x01010101 (the copies at shifts 0, 7, 14, 21 do not overlap, and of
+// the copy at shift 7k only bit k reaches a masked position, bit 8k).
+// Workers m .. n-1 are then added one by one as before.
+#ifndef ONEBIT_SERVER_LUT
+#define ONEBIT_SERVER_LUT 1
+#endif
+
+// NW: the worker count when known at compile time (8, 16), else 0 (any n).
+template <bool ERS, int NW>
 __global__ __launch_bounds__(kThreads) void server_kernel(
     const uint32_t* __restrict__ bits, const float* __restrict__ scales, float* __restrict__ ef,
     const float* __restrict__ S_prev, uint32_t* __restrict__ sv_bits, double* __restrict__ partials,
@@ -29,6 +44,7 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
     constexpr int kGroupWords = kWordsPerTile * kUnroll;   // 128 words per worker per group
     __shared__ double red[kThreads / 64];
     __shared__ float sc[64];
+    __shared__ float lut[256];
     extern __shared__ uint32_t stage[];                    // [n][kGroupWords]
     const int64_t c = blockIdx.x / bpc;
     const int64_t wg = blockIdx.x - c * bpc;
@@ -37,6 +53,19 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
     int64_t end = start + (int64_t)iters * kTile;
     if (end > L) end = L;
     if (threadIdx.x < n) sc[threadIdx.x] = scales[(int64_t)threadIdx.x * n + c];
+    const int nn = NW > 0 ? NW : n;
+    const int m8 = ONEBIT_SERVER_LUT ? (nn < 8 ? nn : 8) : 0;
+    __syncthreads();
+    if (m8 > 0 && threadIdx.x < (1 << m8)) {
+        // entry b: bit i set = worker i's (inverted) sign bit set = -s[i][c]
+        float a = 0.0f;
+        for (int i = 0; i < m8; ++i) {
+            const uint32_t b = (threadIdx.x >> i) & 1u;
+            a = a + __uint_as_float((b << 31) | __float_as_uint(sc[i]));
+        }
+        lut[threadIdx.x] = a;
+    }
+    // (the first group's __syncthreads orders the table before its use)
     const float S = reset ? 0.0f : S_prev[c];
     const float nf = (float)n;
     const int64_t wrow = N >> 5;  // words per worker row
@@ -102,8 +131,24 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
             const int64_t J = cbase + j;
             const int sh = (int)(J & 31);
             const int wl = u * kWordsPerTile + (threadIdx.x >> 3);  // this lane's word in the group
+            // first m workers: table indices, one byte per element
+            uint32_t idx = 0;
+#pragma unroll
+            for (int i = 0; i < m8; ++i) {
+                // rotate the lane's nibble to bits i..i+3 (so that the 24-bit
+                // multiplier stays 0x204081), spread, mask to bit i of each byte
+                const uint32_t w = stage[i * kGroupWords + wl];
+                const uint32_t nib = __builtin_amdgcn_alignbit(w, w, (uint32_t)(sh - i) & 31u) &
+                                     (0xFu << i);
+                idx |= __umul24(nib, 0x204081u) & (0x01010101u << i);
+            }
             float a[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int i = 0; i < n; ++i) {
+            if (m8 > 0) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) a[k] = lut[(idx >> (8 * k)) & 0xFFu];
+            }
+#pragma unroll
+            for (int i = m8; i < nn; ++i) {
                 // inverted bit of element k becomes the sign of +s[i][c]
                 // (one bit-field extract, one shift-or, one add)
                 const uint32_t w = stage[i * kGroupWords + wl];
@@ -156,14 +201,21 @@ hipError_t launch_server(const uint32_t* bits, const float* scales, float* ef, c
     const float inv_n = 1.0f / (float)n;  // exact for powers of two
     const size_t lds = (size_t)n * (kTile / 32) * kUnroll * sizeof(uint32_t);
     const dim3 grid((unsigned)(plan.bpc * n));
-    if (seg_r && seg_off && !reset)
-        hipLaunchKernelGGL(server_kernel<true>, grid, dim3(kThreads), lds, st, bits, scales, ef,
-                           S_prev, sv_bits, partials, N, n, plan.L, plan.iters, plan.bpc, 0,
+    const bool ers = seg_r && seg_off && !reset;
+    auto launch = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, bits, scales, ef, S_prev, sv_bits,
+                           partials, N, n, plan.L, plan.iters, plan.bpc, reset ? 1 : 0,
                            pow2 ? 1 : 0, inv_n, seg_off, seg_r, n_seg);
-    else
-        hipLaunchKernelGGL(server_kernel<false>, grid, dim3(kThreads), lds, st, bits, scales, ef,
-                           S_prev, sv_bits, partials, N, n, plan.L, plan.iters, plan.bpc,
-                           reset ? 1 : 0, pow2 ? 1 : 0, inv_n, seg_off, seg_r, n_seg);
+    };
+    if (ers) {
+        if (n == 8) launch(server_kernel<true, 8>);
+        else if (n == 16) launch(server_kernel<true, 16>);
+        else launch(server_kernel<true, 0>);
+    } else {
+        if (n == 8) launch(server_kernel<false, 8>);
+        else if (n == 16) launch(server_kernel<false, 16>);
+        else launch(server_kernel<false, 0>);
+    }
     return hipGetLastError();
 }
 
