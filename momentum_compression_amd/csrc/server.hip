@@ -71,13 +71,16 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
     const int64_t wrow = N >> 5;  // words per worker row
     const int lane8 = lane_id() & 7;
     // ERS: step-ratio factor of the carried error, per layer (segment walk)
+    // (a workgroup inside one layer takes the layer's factor once)
     int seg = 0;
     int64_t seg_hi = 0;
     float rv = 1.0f;
+    bool seg_uniform = true;
     if (ERS) {
         const int64_t j0 = cbase + start + 4 * (int64_t)threadIdx.x;
         seg = find_segment(seg_off, n_seg, cbase + start);
         seg_hi = seg_off[seg + 1];
+        seg_uniform = seg_hi >= cbase + end;  // workgroup-uniform
         while (j0 >= seg_hi && seg + 1 < n_seg) {
             ++seg;
             seg_hi = seg_off[seg + 1];
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
                 const float avg = pow2 ? a[k] * inv_n : a[k] / nf;
                 float e = reset ? 0.0f : ef_error(p[k], S);
                 if (ERS) {
-                    if (active && J + k >= seg_hi && seg + 1 < n_seg) {
+                    if (!seg_uniform && active && J + k >= seg_hi && seg + 1 < n_seg) {
                         while (J + k >= seg_hi && seg + 1 < n_seg) {
                             ++seg;
                             seg_hi = seg_off[seg + 1];

@@ -45,11 +45,14 @@ def test_unit_scale_free_running():
         e, E = w["e"], sv["E"]
 
 
-def test_lamb_step_ratio_error_feedback_chained():
+@pytest.mark.parametrize("n", [8, 16, 5])
+def test_lamb_step_ratio_error_feedback_chained(n):
     """The LAMB step writes c_{t-1}/c_t per layer; the next compression and
-    server reduce scale the carried errors by it."""
+    server reduce scale the carried errors by it.  n = 8 and 16 run the
+    server kernels specialised for those worker counts, n = 5 the general
+    one."""
     dev = device()
-    wl = C.scaled_lamb(n=8, target_elems=1 << 20, seed=9)
+    wl = C.scaled_lamb(n=n, target_elems=1 << 20, seed=9)
     N, n = wl.N, wl.n
     print(f"[step-ratio EF] N={N} n={n} segments={len(wl.segments)}", flush=True)
     off = np.array(C.segment_offsets(wl.segments), dtype=np.int64)
