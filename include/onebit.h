@@ -55,7 +55,12 @@ extern "C" {
 typedef enum {
     ONEBIT_OK = 0,
     ONEBIT_E_NULL = -1,      /* a required pointer is NULL               */
-    ONEBIT_E_SIZE = -2,      /* N, n, block or a size relation invalid   */
+    ONEBIT_E_SIZE = -2,      /* N, n, block or a size relation invalid,  */
+                             /* or a launch beyond the device's 2^32     */
+                             /* work-items along x: per row about 1.7e10 */
+                             /* elements for onebit_error_materialize,   */
+                             /* 3.4e10 for the INT8 entry points, 6.9e10 */
+                             /* for the other per-element passes        */
     ONEBIT_E_ALIGN = -3,     /* pointer misaligned                       */
     ONEBIT_E_WORKSPACE = -4, /* workspace NULL or smaller than required  */
     ONEBIT_E_ARG = -5,       /* other invalid argument (mode, segments)  */

@@ -31,6 +31,13 @@ int check_segments(const int64_t* seg_off, const float* seg_k, int32_t n_seg, bo
 
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// A dispatch counts its grid in work-items with 32 bits: a launch takes at
+// most 2^32 - 1 work-items along x, i.e. 16,777,215 workgroups of 256.
+// Larger requests would be cut short without an error, so they are refused.
+bool groups_ok(int64_t groups) { return groups <= (int64_t)(0xFFFFFFFFu / kThreads); }
+
 // LAMB step: the layer keys, then one slot per workgroup of the pass
 size_t lamb_ws_bytes(int64_t N, int32_t n_seg) {
     return round_up((size_t)n_seg * sizeof(uint32_t)) +
@@ -51,8 +58,8 @@ WarmupWs split_warmup_ws(void* ws, int64_t N, int32_t n_seg) {
 
 size_t partial_bytes(int64_t N, int32_t n) {
     const int64_t L = N / n;
-    const ChunkPlan pw = make_plan(L, (int64_t)n * n);
-    const ChunkPlan ps = make_plan(L, n);
+    const ChunkPlan pw = make_plan(L, (int64_t)n * n, kCompressIters);
+    const ChunkPlan ps = make_plan(L, n, kServerIters);
     const int64_t w = pw.bpc * n * n;
     const int64_t s = ps.bpc * n;
     return round_up((size_t)(w > s ? w : s) * sizeof(double));
@@ -109,8 +116,8 @@ int onebit_compress_ex(const float* m, const uint32_t* mb_bits, const float* mb_
     if (!ws || ws_bytes < need) return ONEBIT_E_WORKSPACE;
     if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
 
-    const ChunkPlan plan = make_plan(N / n, (int64_t)n * n);
-    if (sum_depth(plan) > 2048) return ONEBIT_E_SIZE;
+    const ChunkPlan plan = make_plan(N / n, (int64_t)n * n, kCompressIters);
+    if (sum_depth(plan) > 2048 || !groups_ok(plan.bpc)) return ONEBIT_E_SIZE;
     const bool clamp_on = clip > 0.0f && !isinf(clip);
     double* partials = static_cast<double*>(ws);
     CompressArgs a{m, ef, scales, bits, partials, N, n, clip, clamp_on, reset != 0,
@@ -159,8 +166,9 @@ int onebit_server_reduce_ex(const uint32_t* bits, const float* scales, float* ef
     if (!ws || ws_bytes < need) return ONEBIT_E_WORKSPACE;
     if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
 
-    const ChunkPlan plan = make_plan(N / n, n);
-    if (sum_depth(plan) > 2048) return ONEBIT_E_SIZE;
+    const ChunkPlan plan = make_plan(N / n, n, kServerIters);
+    if (sum_depth(plan) > 2048 || !groups_ok(plan.bpc)) return ONEBIT_E_SIZE;
+    if (m_out && !groups_ok(ceil_div(N, (int64_t)kMaxIters * kTile))) return ONEBIT_E_SIZE;
     double* partials = static_cast<double*>(ws);
     hipError_t e = launch_server(bits, scales, ef, sv_scales, sv_bits, partials, N, n, plan,
                                  reset != 0, seg_off, seg_err_ratio, n_seg, stream);
@@ -191,6 +199,7 @@ int onebit_decompress(const uint32_t* sv_bits, const float* sv_scales, float* m_
     if ((st = check_segments(seg_off, seg_k, n_seg, true))) return st;
     if (!aligned(sv_bits, 4) || !aligned(sv_scales, 4) || !aligned(m_out, 16)) return ONEBIT_E_ALIGN;
     if (N == 0) return ONEBIT_OK;
+    if (!groups_ok(ceil_div(N, (int64_t)kMaxIters * kTile))) return ONEBIT_E_SIZE;
     return hip_status(
         launch_decompress(sv_bits, sv_scales, m_out, seg_off, seg_k, n_seg, N, n, stream));
 }
@@ -203,6 +212,7 @@ int onebit_error_materialize(const float* ef, const float* scales, float* e_out,
     if (!ef || !scales || !e_out) return ONEBIT_E_NULL;
     if (!aligned(ef, 16) || !aligned(e_out, 16) || !aligned(scales, 4)) return ONEBIT_E_ALIGN;
     if (N == 0) return ONEBIT_OK;
+    if (!groups_ok(ceil_div(N, kTile))) return ONEBIT_E_SIZE;
     return hip_status(launch_materialize(ef, scales, e_out, N, rows, n, stream));
 }
 
@@ -213,12 +223,15 @@ int lamb_layer_scale(float* buf, int64_t N, int32_t batch, const int64_t* seg_of
     if (n_seg < 1) return ONEBIT_E_ARG;
     if (!aligned(buf, 16) || !aligned(seg_off, 8) || !aligned(seg_k, 4)) return ONEBIT_E_ALIGN;
     if (N == 0) return ONEBIT_OK;
+    if (batch > 65535 || !groups_ok(ceil_div(ceil_div(N, kTile), 8))) return ONEBIT_E_SIZE;
     return hip_status(launch_layer_scale(buf, N, batch, seg_off, seg_k, n_seg, divide != 0, stream));
 }
 
 int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (!a) return ONEBIT_E_NULL;
     if (a->N < 0 || (a->N % 4)) return ONEBIT_E_SIZE;
+    if (!groups_ok(ceil_div(a->N, (int64_t)kMaxIters * kTile)) || !groups_ok(lamb_workgroups(a->N)))
+        return ONEBIT_E_SIZE;
     if (!a->x || (!a->m && a->mode != 2) || !a->v) return ONEBIT_E_NULL;
     if (!aligned(a->x, 16) || !aligned(a->m, 16) || !aligned(a->v, 16)) return ONEBIT_E_ALIGN;
     if (a->mode == 0) {
@@ -238,6 +251,7 @@ int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes, hipS
     if (!a->m_prev || !a->v_fresh || !a->seg_off || !a->c_avg || !a->r_prev || !a->c_prev)
         return ONEBIT_E_NULL;
     if (a->n_seg < 1) return ONEBIT_E_ARG;
+    if (!groups_ok(a->n_seg)) return ONEBIT_E_SIZE;
     if (!aligned(a->m_prev, 16) || !aligned(a->v_fresh, 16) || !aligned(a->seg_off, 8) ||
         !aligned(a->c_avg, 4) || !aligned(a->r_prev, 4) || !aligned(a->c_prev, 4) ||
         (a->ratio_max && !aligned(a->ratio_max, 4)) || (a->err_ratio && !aligned(a->err_ratio, 4)))
@@ -257,6 +271,7 @@ int int8_quantize(const float* g, float* err, int8_t* codes, float* block_scales
     if (block != 0 && block != 64 && block != 128 && block != 256 && block != 512 && block != 1024)
         return ONEBIT_E_SIZE;
     if (N < 0 || (N % 4) || (block && (N % block))) return ONEBIT_E_SIZE;
+    if (!groups_ok(ceil_div(N, (int64_t)kInt8Tiles * kTile))) return ONEBIT_E_SIZE;
     if (rounding != 0 && rounding != 1) return ONEBIT_E_ARG;
     if (!g || !codes || !block_scales) return ONEBIT_E_NULL;
     if (!aligned(g, 16) || (err && !aligned(err, 16)) || !aligned(codes, 4) ||
@@ -289,7 +304,8 @@ size_t warmup_workspace_bytes(int64_t N, int32_t n_seg) {
 
 int warmup_adam_step(float* x, float* m, float* v, const float* g, int64_t N, float lr, float eps,
                      float beta1, float beta2, hipStream_t stream) {
-    if (N < 0 || (N % 4)) return ONEBIT_E_SIZE;
+    if (N < 0 || (N % 4) || !groups_ok(ceil_div(N, (int64_t)kMaxIters * kTile)))
+        return ONEBIT_E_SIZE;
     if (N == 0) return ONEBIT_OK;
     if (!x || !m || !v || !g) return ONEBIT_E_NULL;
     if (!aligned(x, 16) || !aligned(m, 16) || !aligned(v, 16) || !aligned(g, 16))
@@ -304,6 +320,7 @@ int warmup_lamb_step(float* x, float* m, float* v, const float* g, int64_t N,
     if (N < 0 || (N % 4)) return ONEBIT_E_SIZE;
     if ((N > 0 && (!x || !m || !v || !g)) || !seg_off || !c || !c_avg) return ONEBIT_E_NULL;
     if (n_seg < 1 || (first != 0 && first != 1)) return ONEBIT_E_ARG;
+    if (!groups_ok(layer_grid(N, n_seg)) || !groups_ok(n_seg)) return ONEBIT_E_SIZE;
     if (!aligned(x, 16) || !aligned(m, 16) || !aligned(v, 16) || !aligned(g, 16) ||
         !aligned(seg_off, 8) || !aligned(c, 4) || !aligned(c_avg, 4))
         return ONEBIT_E_ALIGN;
@@ -334,6 +351,7 @@ int lamb_momentum_scale(const float* m, int64_t N, const int64_t* seg_off, int32
     if (N < 0 || (N % 4)) return ONEBIT_E_SIZE;
     if ((N > 0 && !m) || !seg_off || !k) return ONEBIT_E_NULL;
     if (n_seg < 1) return ONEBIT_E_ARG;
+    if (!groups_ok(layer_grid(N, n_seg)) || !groups_ok(n_seg)) return ONEBIT_E_SIZE;
     if (!aligned(m, 16) || !aligned(seg_off, 8) || !aligned(k, 4)) return ONEBIT_E_ALIGN;
     if (!ws || ws_bytes < warmup_workspace_bytes(N, n_seg)) return ONEBIT_E_WORKSPACE;
     if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;

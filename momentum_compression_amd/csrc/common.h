@@ -13,8 +13,16 @@ using f4 = float __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;           // threads per workgroup (4 waves)
 constexpr int kTile = kThreads * 4;     // elements per workgroup iteration (float4 / lane)
-constexpr int kMaxIters = 4;            // tiles per workgroup in the chunked streaming kernels
+constexpr int kMaxIters = 4;            // tiles per workgroup: Adam, decompress, warmup Adam
 constexpr int kUnroll = 4;              // tiles whose loads are issued together
+// Tiles per workgroup of the kernels whose best shape differs (measured on
+// the full-size workloads): many one-tile workgroups for the worker
+// compression, two tiles for the server and the INT8 pass.
+constexpr int kCompressIters = 1;
+constexpr int kCompressUnroll = 1;
+constexpr int kServerIters = 2;
+constexpr int kServerUnroll = 2;
+constexpr int kInt8Tiles = 2;
 constexpr int kLambTiles = 4;           // tiles per workgroup in the LAMB pass (5 streams in flight)
 
 // workgroups of the LAMB pass over N elements
@@ -32,7 +40,7 @@ struct ChunkPlan {
     int64_t bpc;      // workgroups per chunk
 };
 
-ChunkPlan make_plan(int64_t L, int64_t chunks);
+ChunkPlan make_plan(int64_t L, int64_t chunks, int32_t max_iters);
 
 // Upper bound on the number of floating-point additions any one term passes
 // through in the fp64 chunk sum (per-thread sequence, wave butterfly, LDS

@@ -29,8 +29,10 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     const float* __restrict__ seg_k, int32_t n_seg, const uint32_t* __restrict__ mb_bits,
     const float* __restrict__ mb_scales, float beta1, const float* __restrict__ seg_r) {
     __shared__ double red[kThreads / 64];
-    const int64_t pair = blockIdx.x / bpc;
-    const int64_t wg = blockIdx.x - pair * bpc;
+    // grid (bpc, n * n): x = workgroup within the chunk, y = (worker, chunk);
+    // a 1-D grid of all of them could exceed 2^32 work-items
+    const int64_t pair = blockIdx.y;
+    const int64_t wg = blockIdx.x;
     const int32_t i = (int32_t)(pair / n);
     const int32_t c = (int32_t)(pair - (int64_t)i * n);
     const int64_t row = (int64_t)i * N;
@@ -47,9 +49,16 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     float kv = 1.0f;
     float rv = 1.0f;  // ERS: step-ratio factor of the carried error in this layer
     if (SEG) {
-        const int64_t J0 = cbase + start + 4 * (int64_t)threadIdx.x;
-        seg = find_segment(seg_off, n_seg, J0 < N ? J0 : N - 1);
+        // one (scalar) search for the workgroup's first element, then each
+        // thread walks to the layer of its own first element
+        const int64_t W0 = cbase + start;
+        seg = find_segment(seg_off, n_seg, W0);
         seg_hi = seg_off[seg + 1];
+        const int64_t J0 = W0 + 4 * (int64_t)threadIdx.x;
+        while (J0 >= seg_hi && seg + 1 < n_seg) {
+            ++seg;
+            seg_hi = seg_off[seg + 1];
+        }
         kv = seg_k[seg];
         if (ERS) rv = seg_r[seg];
     }
@@ -61,12 +70,12 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     float mq = (MOM && SEG) ? mS / kv : mS;
 
     double acc = 0.0;
-    for (int it0 = 0; it0 < iters; it0 += kUnroll) {
-        // issue the loads of kUnroll tiles before any use (memory-level parallelism)
-        f4 mv[kUnroll], pv[kUnroll];
-        uint32_t mw[kUnroll];
+    for (int it0 = 0; it0 < iters; it0 += kCompressUnroll) {
+        // issue the loads of kCompressUnroll tiles before any use
+        f4 mv[kCompressUnroll], pv[kCompressUnroll];
+        uint32_t mw[kCompressUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kCompressUnroll; ++u) {
             const int64_t j = start + (int64_t)(it0 + u) * kTile + 4 * (int64_t)threadIdx.x;
             mv[u] = f4{0.f, 0.f, 0.f, 0.f};
             pv[u] = f4{0.f, 0.f, 0.f, 0.f};
@@ -79,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
             }
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kCompressUnroll; ++u) {
             const int64_t j = start + (int64_t)(it0 + u) * kTile + 4 * (int64_t)threadIdx.x;
             const bool active = it0 + u < iters && j < end;
             const int64_t idx = row + cbase + j;
@@ -126,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
         }
     }
     const double tot = block_sum(acc, red);
-    if (threadIdx.x == 0) partials[blockIdx.x] = tot;
+    if (threadIdx.x == 0) partials[pair * bpc + wg] = tot;
 }
 
 template <bool SEG, bool CLAMP, bool RESET, bool MOM, bool ERS>
@@ -152,7 +161,7 @@ static void launch_m(dim3 grid, hipStream_t st, const CompressArgs& a, const Chu
 }
 
 hipError_t launch_compress(const CompressArgs& a, const ChunkPlan& plan, hipStream_t st) {
-    const dim3 grid((unsigned)(plan.bpc * (int64_t)a.n * a.n));
+    const dim3 grid((unsigned)plan.bpc, (unsigned)((int64_t)a.n * a.n));
     const int sel = (a.seg_off ? 4 : 0) | (a.clamp_on ? 2 : 0) | (a.reset ? 1 : 0);
     switch (sel) {
         case 0: launch_m<false, false, false>(grid, st, a, plan); break;

@@ -157,12 +157,12 @@ hipError_t launch_mean_finalize(const double* partials, const ChunkPlan& plan, i
 }
 
 // ---------------------------------------------------------------- plan
-ChunkPlan make_plan(int64_t L, int64_t chunks) {
+ChunkPlan make_plan(int64_t L, int64_t chunks, int32_t max_iters) {
     ChunkPlan p;
     p.L = L;
     const int64_t tiles = (L + kTile - 1) / kTile;
     // aim for at least ~8 workgroups per CU (256 CUs) over all chunks
-    int64_t iters = kMaxIters;
+    int64_t iters = max_iters;
     while (iters > 1 && ((tiles + iters - 1) / iters) * chunks < 2048) iters >>= 1;
     p.iters = (int32_t)iters;
     p.bpc = (tiles + iters - 1) / iters;

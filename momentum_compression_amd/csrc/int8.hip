@@ -83,9 +83,9 @@ __global__ __launch_bounds__(kThreads) void int8_kernel(const float* __restrict_
     const float Mt = B == 0 ? __uint_as_float(*tensor_max) : 0.0f;
     const int64_t base = (int64_t)blockIdx.x * iters * kTile;
     // loads of all tiles first (memory-level parallelism), then the blocks
-    f4 gv[kMaxIters], ev[kMaxIters];
+    f4 gv[kInt8Tiles], ev[kInt8Tiles];
 #pragma unroll
-    for (int it = 0; it < kMaxIters; ++it) {
+    for (int it = 0; it < kInt8Tiles; ++it) {
         const int64_t J = base + (int64_t)it * kTile + 4 * (int64_t)threadIdx.x;
         gv[it] = f4{0.f, 0.f, 0.f, 0.f};
         ev[it] = f4{0.f, 0.f, 0.f, 0.f};
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void int8_kernel(const float* __restrict_
         }
     }
 #pragma unroll
-    for (int it = 0; it < kMaxIters; ++it) {
+    for (int it = 0; it < kInt8Tiles; ++it) {
         if (it >= iters || base + (int64_t)it * kTile >= N) break;  // workgroup-uniform
         const int64_t J = base + (int64_t)it * kTile + 4 * (int64_t)threadIdx.x;
         const bool active = J < N;
@@ -276,7 +276,7 @@ static hipError_t launch_r(dim3 grid, hipStream_t st, const float* g, float* err
 hipError_t launch_int8(const float* g, float* err, int8_t* codes, float* scales, float* deq,
                        int64_t N, int32_t block, uint64_t seed, uint32_t step, bool nearest,
                        uint32_t* tensor_max, hipStream_t st) {
-    const int32_t iters = kMaxIters;
+    const int32_t iters = kInt8Tiles;
     const int64_t tiles = (N + kTile - 1) / kTile;
     const dim3 grid((unsigned)((tiles + iters - 1) / iters));
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);

@@ -10,9 +10,8 @@ template <bool DIV>
 __global__ __launch_bounds__(kThreads) void layer_scale_kernel(
     float* __restrict__ buf, int64_t N, int64_t tiles_per_row, int32_t iters,
     const int64_t* __restrict__ seg_off, const float* __restrict__ seg_k, int32_t n_seg) {
-    const int64_t wg_per_row = (tiles_per_row + iters - 1) / iters;
-    const int64_t row = blockIdx.x / wg_per_row;
-    const int64_t wg = blockIdx.x - row * wg_per_row;
+    const int64_t row = blockIdx.y;  // grid (workgroups per row, batch)
+    const int64_t wg = blockIdx.x;
     float* b = buf + row * N;
     const int64_t j0 = wg * (int64_t)iters * kTile + 4 * (int64_t)threadIdx.x;
     if (j0 >= N) return;
@@ -42,24 +41,25 @@ hipError_t launch_layer_scale(float* buf, int64_t N, int32_t batch, const int64_
                               const float* seg_k, int32_t n_seg, bool divide, hipStream_t st) {
     const int64_t tiles = (N + kTile - 1) / kTile;
     const int32_t iters = 8;
-    const int64_t wg = ((tiles + iters - 1) / iters) * batch;
+    const dim3 grid((unsigned)((tiles + iters - 1) / iters), (unsigned)batch);
     if (divide)
-        hipLaunchKernelGGL(layer_scale_kernel<true>, dim3((unsigned)wg), dim3(kThreads), 0, st, buf,
-                           N, tiles, iters, seg_off, seg_k, n_seg);
+        hipLaunchKernelGGL(layer_scale_kernel<true>, grid, dim3(kThreads), 0, st, buf, N, tiles,
+                           iters, seg_off, seg_k, n_seg);
     else
-        hipLaunchKernelGGL(layer_scale_kernel<false>, dim3((unsigned)wg), dim3(kThreads), 0, st,
-                           buf, N, tiles, iters, seg_off, seg_k, n_seg);
+        hipLaunchKernelGGL(layer_scale_kernel<false>, grid, dim3(kThreads), 0, st, buf, N, tiles,
+                           iters, seg_off, seg_k, n_seg);
     return hipGetLastError();
 }
 
 // e = ef >= 0 ? ef - s : ef + s with s the scale of the element's chunk.
 __global__ __launch_bounds__(kThreads) void materialize_kernel(
     const float* __restrict__ ef, const float* __restrict__ scales, float* __restrict__ e,
-    int64_t N, int64_t total, int32_t n, int64_t L) {
-    const int64_t idx = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
-    if (idx >= total) return;
-    const int64_t row = idx / N;
-    const int64_t c = (idx - row * N) / L;
+    int64_t N, int32_t n, int64_t L) {
+    const int64_t row = blockIdx.y;  // grid (ceil(N / 1024), rows)
+    const int64_t j = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+    if (j >= N) return;
+    const int64_t idx = row * N + j;
+    const int64_t c = j / L;
     const float s = scales[row * n + c];
     const f4 v = *reinterpret_cast<const f4*>(ef + idx);
     const f4 o = {ef_error(v.x, s), ef_error(v.y, s), ef_error(v.z, s), ef_error(v.w, s)};
@@ -68,10 +68,9 @@ __global__ __launch_bounds__(kThreads) void materialize_kernel(
 
 hipError_t launch_materialize(const float* ef, const float* scales, float* e_out, int64_t N,
                               int32_t rows, int32_t n, hipStream_t st) {
-    const int64_t total = N * rows;
-    const dim3 grid((unsigned)((total / 4 + kThreads - 1) / kThreads));
-    hipLaunchKernelGGL(materialize_kernel, grid, dim3(kThreads), 0, st, ef, scales, e_out, N, total,
-                       n, N / n);
+    const dim3 grid((unsigned)((N / 4 + kThreads - 1) / kThreads), (unsigned)rows);
+    hipLaunchKernelGGL(materialize_kernel, grid, dim3(kThreads), 0, st, ef, scales, e_out, N, n,
+                       N / n);
     return hipGetLastError();
 }
 

@@ -15,7 +15,7 @@
 
 namespace onebit {
 
-// Words of the kUnroll tiles a workgroup processes together, for every
+// Words of the kServerUnroll tiles a workgroup processes together, for every
 // worker, are staged through LDS with coalesced loads (32 consecutive words
 // per worker and tile); each lane then reads its word per worker from LDS.
 //
@@ -41,13 +41,13 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
     float inv_n, const int64_t* __restrict__ seg_off, const float* __restrict__ seg_r,
     int32_t n_seg) {
     constexpr int kWordsPerTile = kTile / 32;              // 32
-    constexpr int kGroupWords = kWordsPerTile * kUnroll;   // 128 words per worker per group
+    constexpr int kGroupWords = kWordsPerTile * kServerUnroll;  // words per worker per group
     __shared__ double red[kThreads / 64];
     __shared__ float sc[64];
     __shared__ float lut[256];
     extern __shared__ uint32_t stage[];                    // [n][kGroupWords]
-    const int64_t c = blockIdx.x / bpc;
-    const int64_t wg = blockIdx.x - c * bpc;
+    const int64_t c = blockIdx.y;  // grid (bpc, n)
+    const int64_t wg = blockIdx.x;
     const int64_t cbase = c * L;
     const int64_t start = wg * (int64_t)iters * kTile;
     int64_t end = start + (int64_t)iters * kTile;
@@ -89,14 +89,14 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
     }
 
     double acc = 0.0;
-    for (int it0 = 0; it0 < iters; it0 += kUnroll) {
+    for (int it0 = 0; it0 < iters; it0 += kServerUnroll) {
         const int64_t g0 = start + (int64_t)it0 * kTile;   // first element of this group
         const int64_t gw = (cbase + g0) >> 5;             // its first word in a row
         const int64_t gwords = (end - g0 + 31) >> 5;      // words of this group inside the chunk
         __syncthreads();                                  // previous group done with `stage`
-        f4 pv[kUnroll];
+        f4 pv[kServerUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kServerUnroll; ++u) {
             const int64_t j = g0 + (int64_t)u * kTile + 4 * (int64_t)threadIdx.x;
             pv[u] = f4{0.f, 0.f, 0.f, 0.f};
             if (!reset && it0 + u < iters && j < end)
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
         }
         __syncthreads();
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kServerUnroll; ++u) {
             const int64_t j = g0 + (int64_t)u * kTile + 4 * (int64_t)threadIdx.x;
             const bool active = it0 + u < iters && j < end;
             const int64_t J = cbase + j;
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
         }
     }
     const double tot = block_sum(acc, red);
-    if (threadIdx.x == 0) partials[blockIdx.x] = tot;
+    if (threadIdx.x == 0) partials[c * bpc + wg] = tot;
 }
 
 hipError_t launch_server(const uint32_t* bits, const float* scales, float* ef, const float* S_prev,
@@ -202,8 +202,8 @@ hipError_t launch_server(const uint32_t* bits, const float* scales, float* ef, c
                          const float* seg_r, int32_t n_seg, hipStream_t st) {
     const bool pow2 = (n & (n - 1)) == 0;
     const float inv_n = 1.0f / (float)n;  // exact for powers of two
-    const size_t lds = (size_t)n * (kTile / 32) * kUnroll * sizeof(uint32_t);
-    const dim3 grid((unsigned)(plan.bpc * n));
+    const size_t lds = (size_t)n * (kTile / 32) * kServerUnroll * sizeof(uint32_t);
+    const dim3 grid((unsigned)plan.bpc, (unsigned)n);
     const bool ers = seg_r && seg_off && !reset;
     auto launch = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, bits, scales, ef, S_prev, sv_bits,

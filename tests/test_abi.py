@@ -37,8 +37,10 @@ def test_workspace_bytes(lib):
     assert ob.workspace_bytes(1000, 4) == 0           # not a multiple of 64 n
     assert ob.workspace_bytes(1 << 20, 0) == 0
     assert ob.workspace_bytes(1 << 20, 65) == 0
+    # one binary64 partial per workgroup of the compression (one 1024-element
+    # tile each, 16 x 16 chunks of 81,970,560) dominates: 80,049 x 256 x 8 B
     big = ob.workspace_bytes(1_311_528_960, 16, 291)
-    assert 0 < big < 64 << 20
+    assert 80_049 * 256 * 8 <= big < 80_049 * 256 * 8 + (1 << 20)
 
 
 def test_frozen_v_workspace_bytes(lib):
@@ -198,3 +200,14 @@ def test_warmup_workspace_bytes(lib):
         assert ob.warmup_workspace_bytes(N, S) == rup(8 * (S + 1)) + rup(16 * grid) + rup(8 * S)
     assert ob.warmup_workspace_bytes(1022, 3) == 0
     assert ob.warmup_workspace_bytes(1024, 0) == 0
+
+
+def test_grid_limit_refused(lib):
+    """Sizes whose launch would pass 2^32 work-items along x are refused before
+    any launch (the hardware would cut the grid short without an error)."""
+    a = ob.FrozenVArgs(mode=0, N=1 << 37, x=P, m=P, v=P, lr=1e-3, eps=1e-6)
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_SIZE
+    assert lib.int8_quantize(P, P, P, P, P, 1 << 36, 256, 0, 1, 1, None, 0, None) == ob.ONEBIT_E_SIZE
+    # 2^35 elements in 64 chunks of 2^29: a valid chunking, but 2^25 workgroups
+    assert lib.onebit_error_materialize(P, P, P, 1 << 35, 64, 64, None) == ob.ONEBIT_E_SIZE
+    assert lib.warmup_adam_step(P, P, P, P, 1 << 37, 1e-3, 1e-6, 0.9, 0.999, None) == ob.ONEBIT_E_SIZE
