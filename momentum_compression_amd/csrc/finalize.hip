@@ -106,8 +106,20 @@ __global__ __launch_bounds__(kThreads) void mean_finalize_kernel(
         return;
     }
     const double* p = partials + pair * bpc;
+    // thread t adds partials t, t + 256, t + 512, ... in that order; the loads
+    // of 8 of them are issued before the additions
+    constexpr int kBatch = 8;
     double acc = 0.0;
-    for (int64_t k = threadIdx.x; k < bpc; k += kThreads) acc += p[k];
+    for (int64_t k0 = threadIdx.x; k0 < bpc; k0 += (int64_t)kThreads * kBatch) {
+        double v[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int64_t k = k0 + (int64_t)q * kThreads;
+            v[q] = k < bpc ? p[k] : 0.0;
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) acc += v[q];
+    }
     const double tot = block_sum(acc, red);
     if (threadIdx.x == 0) {
         const double mu = tot / (double)L;
