@@ -28,10 +28,6 @@ namespace onebit {
 // mask 0x01010101 (the copies at shifts 0, 7, 14, 21 do not overlap, and of
 // the copy at shift 7k only bit k reaches a masked position, bit 8k).
 // Workers m .. n-1 are then added one by one as before.
-#ifndef ONEBIT_SERVER_LUT
-#define ONEBIT_SERVER_LUT 1
-#endif
-
 // NW: the worker count when known at compile time (8, 16), else 0 (any n).
 template <bool ERS, int NW>
 __global__ __launch_bounds__(kThreads) void server_kernel(
@@ -42,6 +38,7 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
     int32_t n_seg) {
     constexpr int kWordsPerTile = kTile / 32;              // 32
     constexpr int kGroupWords = kWordsPerTile * kServerUnroll;  // words per worker per group
+    static_assert(kGroupWords == 64, "staging maps one wave to one worker's words");
     __shared__ double red[kThreads / 64];
     __shared__ float sc[64];
     __shared__ float lut[256];
@@ -54,9 +51,9 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
     if (end > L) end = L;
     if (threadIdx.x < n) sc[threadIdx.x] = scales[(int64_t)threadIdx.x * n + c];
     const int nn = NW > 0 ? NW : n;
-    const int m8 = ONEBIT_SERVER_LUT ? (nn < 8 ? nn : 8) : 0;
+    const int m8 = nn < 8 ? nn : 8;  // n >= 1
     __syncthreads();
-    if (m8 > 0 && threadIdx.x < (1 << m8)) {
+    if (threadIdx.x < (1 << m8)) {
         // entry b: bit i set = worker i's (inverted) sign bit set = -s[i][c]
         float a = 0.0f;
         for (int i = 0; i < m8; ++i) {
@@ -102,28 +99,30 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
             if (!reset && it0 + u < iters && j < end)
                 pv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(ef + cbase + j));
         }
-        // coalesced word loads, kStageBatch in flight per thread before the
-        // LDS writes; inverted so that a clear bit (negative value) becomes
-        // the set sign bit in the decode below
-        constexpr int kStageBatch = 4;
-        const int total = n * kGroupWords;
-        for (int q0 = threadIdx.x; q0 < total; q0 += kStageBatch * kThreads) {
-            uint32_t v[kStageBatch];
-            bool ok[kStageBatch];
+        // Staging: a group holds 64 words per worker, so wave w stages workers
+        // w, w + 4, w + 8, ... with one coalesced 256-byte load each (lane l
+        // takes word l); the worker, hence the row pointer, is wave-uniform.
+        // The words are inverted so that a clear bit (negative value) becomes
+        // the set sign bit in the decode below.  A lane past the chunk's end
+        // reads the group's first word and stores all-ones (discarded later).
+        {
+            const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+            const int lane = lane_id();
+            const bool okw = lane < gwords;
+            constexpr int kBatch = 4;  // workers per wave whose loads are in flight together
+            for (int r0 = 0; r0 < nn; r0 += 4 * kBatch) {
+                uint32_t v[kBatch];
 #pragma unroll
-            for (int r = 0; r < kStageBatch; ++r) {
-                // unconditional loads (an out-of-range slot reads word 0 and is
-                // discarded) so that no branch waits on a load before the next
-                const int q = q0 + r * kThreads;
-                const int i = q / kGroupWords;
-                const int w = q - i * kGroupWords;
-                ok[r] = q < total && w < gwords;
-                v[r] = bits[ok[r] ? (int64_t)i * wrow + gw + w : 0];
-            }
+                for (int b = 0; b < kBatch; ++b) {
+                    const int i = r0 + 4 * b + wave;  // wave-uniform
+                    v[b] = 0u;
+                    if (i < nn) v[b] = bits[(int64_t)i * wrow + gw + (okw ? lane : 0)];
+                }
 #pragma unroll
-            for (int r = 0; r < kStageBatch; ++r) {
-                const int q = q0 + r * kThreads;
-                if (q < total) stage[q] = ok[r] ? ~v[r] : ~0u;
+                for (int b = 0; b < kBatch; ++b) {
+                    const int i = r0 + 4 * b + wave;
+                    if (i < nn) stage[i * kGroupWords + lane] = okw ? ~v[b] : ~0u;
+                }
             }
         }
         __syncthreads();
@@ -145,11 +144,9 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
                                      (0xFu << i);
                 idx |= __umul24(nib, 0x204081u) & (0x01010101u << i);
             }
-            float a[4] = {0.f, 0.f, 0.f, 0.f};
-            if (m8 > 0) {
+            float a[4];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) a[k] = lut[(idx >> (8 * k)) & 0xFFu];
-            }
+            for (int k = 0; k < 4; ++k) a[k] = lut[(idx >> (8 * k)) & 0xFFu];
 #pragma unroll
             for (int i = m8; i < nn; ++i) {
                 // inverted bit of element k becomes the sign of +s[i][c]
