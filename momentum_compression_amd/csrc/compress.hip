@@ -13,10 +13,12 @@
 // scales, divided by k_l in LAMB mode), so m is never written to memory
 // (1-bit Adam article, section 2.1, momentum recursion).
 //
-// Layout: workgroup w of chunk (i, c) streams tiles of 1024 consecutive
-// elements (float4 per lane, fully coalesced) of worker row i, chunk c.  The
-// 4 sign bits of a lane are merged over 8 lanes with DPP into one 32-bit
-// word, stored by the first lane of each group.
+// Layout: the grid is (workgroups per chunk, n * n); workgroup (w, i n + c)
+// streams kCompressIters tiles of 1024 consecutive elements (float4 per
+// lane, fully coalesced) of worker row i, chunk c.  One tile per workgroup
+// measured fastest: millions of short workgroups keep every CU's memory
+// pipeline full.  The 4 sign bits of a lane are merged over 8 lanes with DPP
+// into one 32-bit word, stored by the first lane of each group.
 #include "common.h"
 
 namespace onebit {

@@ -5,10 +5,11 @@
 //
 // LAMB (1-bit LAMB page, algorithm and analysis paragraphs), one streaming
 // pass:  g = (m - beta1 m_prev) / (1 - beta1);  v_f = beta2 v_f + (1-beta2) g^2;
-// per-layer max of v / v_f (order-preserving uint keys, NaN skipped, one
-// atomicMax per workgroup and layer);  x -= (lr c_{t-1,l}) m / (sqrtf(v)+eps).
-// A tiny per-layer kernel then forms r_t and c_t.  With use_c_t the x update
-// moves to a second pass after r_t / c_t are known.
+// per-layer max of v / v_f (order-preserving uint keys, NaN skipped; one slot
+// per workgroup inside a layer, LDS-merged atomics for the workgroups across
+// layer boundaries);  x -= (lr c_{t-1,l}) m / (sqrtf(v)+eps).  A per-layer
+// kernel then reduces the slots and forms r_t and c_t.  With use_c_t the x
+// update moves to a second pass after r_t / c_t are known.
 #include "common.h"
 
 namespace onebit {
