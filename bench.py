@@ -25,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -50,10 +51,15 @@ KERNEL_SOURCES = [os.path.join(ROOT, "momentum_compression_amd", "csrc", f)
 
 
 def kernel_source_hash() -> str:
+    """Hash of the compress kernel's code: comments and whitespace removed, so
+    that only a change of the code makes the stored counters stale."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
