@@ -20,7 +20,7 @@
  * - n simulated workers each hold a flat buffer of N elements ("row").  A row
  *   is split into n chunks of L = N / n consecutive elements; chunk c of
  *   every worker is reduced by server c.  N must be a multiple of 64 * n (the
- *   caller zero-pads).  1 <= n <= 64.  N == 0 is a no-op.
+ *   caller zero-pads).  1 <= n <= 64, L < 2^31.  N == 0 is a no-op.
  * - Sign convention: bit = 1 when x >= 0 (both zeros encode +1), 0 when
  *   x < 0 or NaN.  Packed words: element j of a row is bit (j & 31) of
  *   uint32 word (j >> 5) of that row (least significant bit first).

@@ -16,7 +16,9 @@ int check_rows(int64_t N, int32_t n) {
     if (n < 1 || n > kMaxWorkers) return ONEBIT_E_SIZE;
     if (N < 0) return ONEBIT_E_SIZE;
     if (N % (64 * (int64_t)n)) return ONEBIT_E_SIZE;
-    if (N / n >= (int64_t)1 << 32) return ONEBIT_E_SIZE;  // chunk length must fit 32 bits
+    // chunk length below 2^31: keeps the fp64 sums' addition depth (about
+    // L / 2^18 + 21) within the finalize's certified bound
+    if (N / n >= (int64_t)1 << 31) return ONEBIT_E_SIZE;
     return ONEBIT_OK;
 }
 
@@ -117,7 +119,7 @@ int onebit_compress_ex(const float* m, const uint32_t* mb_bits, const float* mb_
     if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
 
     const ChunkPlan plan = make_plan(N / n, (int64_t)n * n, kCompressIters);
-    if (sum_depth(plan) > 2048 || !groups_ok(plan.bpc)) return ONEBIT_E_SIZE;
+    if (sum_depth(plan) > kMaxSumDepth || !groups_ok(plan.bpc)) return ONEBIT_E_SIZE;
     const bool clamp_on = clip > 0.0f && !isinf(clip);
     double* partials = static_cast<double*>(ws);
     CompressArgs a{m, ef, scales, bits, partials, N, n, clip, clamp_on, reset != 0,
@@ -167,7 +169,7 @@ int onebit_server_reduce_ex(const uint32_t* bits, const float* scales, float* ef
     if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
 
     const ChunkPlan plan = make_plan(N / n, n, kServerIters);
-    if (sum_depth(plan) > 2048 || !groups_ok(plan.bpc)) return ONEBIT_E_SIZE;
+    if (sum_depth(plan) > kMaxSumDepth || !groups_ok(plan.bpc)) return ONEBIT_E_SIZE;
     if (m_out && !groups_ok(ceil_div(N, (int64_t)kMaxIters * kTile))) return ONEBIT_E_SIZE;
     double* partials = static_cast<double*>(ws);
     hipError_t e = launch_server(bits, scales, ef, sv_scales, sv_bits, partials, N, n, plan,

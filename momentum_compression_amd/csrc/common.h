@@ -46,6 +46,7 @@ ChunkPlan make_plan(int64_t L, int64_t chunks, int32_t max_iters);
 // through in the fp64 chunk sum (per-thread sequence, wave butterfly, LDS
 // tree, finalize sequence, finalize tree, division).
 int64_t sum_depth(const ChunkPlan& p);
+constexpr int64_t kMaxSumDepth = 12288;  // bound the finalize's certification assumes
 
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

@@ -211,3 +211,12 @@ def test_grid_limit_refused(lib):
     # 2^35 elements in 64 chunks of 2^29: a valid chunking, but 2^25 workgroups
     assert lib.onebit_error_materialize(P, P, P, 1 << 35, 64, 64, None) == ob.ONEBIT_E_SIZE
     assert lib.warmup_adam_step(P, P, P, P, 1 << 37, 1e-3, 1e-6, 0.9, 0.999, None) == ob.ONEBIT_E_SIZE
+
+
+def test_chunk_length_limit(lib):
+    """Chunks below 2^31 elements keep the fp64 sums' depth inside the bound
+    the finalize certifies; longer chunks are refused."""
+    assert ob.workspace_bytes((1 << 31) - 64, 1) > 0
+    assert ob.workspace_bytes(1 << 31, 1) == 0
+    assert ob.workspace_bytes(1 << 32, 2) == 0
+    assert _compress(lib, N=1 << 32, n=2) == ob.ONEBIT_E_SIZE
