@@ -126,7 +126,14 @@ int onebit_compress(const float* m, float* ef, float* scales, uint32_t* bits,
  * sv_bits [N/32] u32   out
  * m_out   [N] float or NULL: decompressed global momentum
  * seg_off, seg_k, n_seg  as onebit_compress (applied as / k_l to m_out)
+ * ws, ws_bytes  as onebit_compress (onebit_workspace_bytes serves both)
  */
+int onebit_server_reduce(const uint32_t* bits, const float* scales, float* ef,
+                         float* sv_scales, uint32_t* sv_bits, float* m_out,
+                         const int64_t* seg_off, const float* seg_k, int32_t n_seg,
+                         int64_t N, int32_t n, int32_t reset,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
 /*
  * Worker side fed with gradients: the local momentum update fused into
  * onebit_compress (1-bit Adam article, section 2.1: m_t = beta1 m_{t-1} +
@@ -171,12 +178,6 @@ int onebit_compress_ex(const float* m, const uint32_t* mb_bits, const float* mb_
                        const int64_t* seg_off, const float* seg_k, const float* seg_err_ratio,
                        int32_t n_seg, uint32_t flags, void* ws, size_t ws_bytes,
                        hipStream_t stream);
-
-int onebit_server_reduce(const uint32_t* bits, const float* scales, float* ef,
-                         float* sv_scales, uint32_t* sv_bits, float* m_out,
-                         const int64_t* seg_off, const float* seg_k, int32_t n_seg,
-                         int64_t N, int32_t n, int32_t reset,
-                         void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * onebit_server_reduce with the variants of onebit_compress_ex: the server
