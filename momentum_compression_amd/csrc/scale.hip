@@ -8,7 +8,7 @@ namespace onebit {
 // walks the segment table forward from its first element.
 template <bool DIV>
 __global__ __launch_bounds__(kThreads) void layer_scale_kernel(
-    float* __restrict__ buf, int64_t N, int64_t tiles_per_row, int32_t iters,
+    float* __restrict__ buf, int64_t N, int32_t iters,
     const int64_t* __restrict__ seg_off, const float* __restrict__ seg_k, int32_t n_seg) {
     const int64_t row = blockIdx.y;  // grid (workgroups per row, batch)
     const int64_t wg = blockIdx.x;
@@ -43,11 +43,11 @@ hipError_t launch_layer_scale(float* buf, int64_t N, int32_t batch, const int64_
     const int32_t iters = 8;
     const dim3 grid((unsigned)((tiles + iters - 1) / iters), (unsigned)batch);
     if (divide)
-        hipLaunchKernelGGL(layer_scale_kernel<true>, grid, dim3(kThreads), 0, st, buf, N, tiles,
-                           iters, seg_off, seg_k, n_seg);
+        hipLaunchKernelGGL(layer_scale_kernel<true>, grid, dim3(kThreads), 0, st, buf, N, iters,
+                           seg_off, seg_k, n_seg);
     else
-        hipLaunchKernelGGL(layer_scale_kernel<false>, grid, dim3(kThreads), 0, st, buf, N, tiles,
-                           iters, seg_off, seg_k, n_seg);
+        hipLaunchKernelGGL(layer_scale_kernel<false>, grid, dim3(kThreads), 0, st, buf, N, iters,
+                           seg_off, seg_k, n_seg);
     return hipGetLastError();
 }
 

@@ -49,11 +49,11 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
     const int64_t start = wg * (int64_t)iters * kTile;
     int64_t end = start + (int64_t)iters * kTile;
     if (end > L) end = L;
-    if (threadIdx.x < n) sc[threadIdx.x] = scales[(int64_t)threadIdx.x * n + c];
+    if ((int)threadIdx.x < n) sc[threadIdx.x] = scales[(int64_t)threadIdx.x * n + c];
     const int nn = NW > 0 ? NW : n;
     const int m8 = nn < 8 ? nn : 8;  // n >= 1
     __syncthreads();
-    if (threadIdx.x < (1 << m8)) {
+    if ((int)threadIdx.x < (1 << m8)) {
         // entry b: bit i set = worker i's (inverted) sign bit set = -s[i][c]
         float a = 0.0f;
         for (int i = 0; i < m8; ++i) {
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
             const int wl = u * kWordsPerTile + (threadIdx.x >> 3);  // this lane's word in the group
             // first m workers: table indices, one byte per element
             uint32_t idx = 0;
-#pragma unroll
+#pragma unroll 8
             for (int i = 0; i < m8; ++i) {
                 // rotate the lane's nibble to bits i..i+3 (so that the 24-bit
                 // multiplier stays 0x204081), spread, mask to bit i of each byte
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
             float a[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) a[k] = lut[(idx >> (8 * k)) & 0xFFu];
-#pragma unroll
+#pragma unroll 8
             for (int i = m8; i < nn; ++i) {
                 // inverted bit of element k becomes the sign of +s[i][c]
                 // (one bit-field extract, one shift-or, one add)
