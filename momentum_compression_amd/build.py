@@ -36,6 +36,7 @@ FLAGS = [
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
+    "-Wextra",
     "-Wno-unused-function",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
@@ -55,6 +56,13 @@ def _compile(src: str) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")
+    # the host pass does not know the GPU feature switched off above; every
+    # other diagnostic is shown
+    notes = [ln for ln in res.stderr.splitlines()
+             if ln.strip() and "packed-fp32-ops" not in ln and "warnings generated" not in ln
+             and "warning generated" not in ln]
+    if notes:
+        print(f"{src}:\n" + "\n".join(notes), file=sys.stderr)
     return obj
 
 
