@@ -333,6 +333,76 @@ def measure_warmup(steps: int, warmup: int) -> dict:
     return out
 
 
+def measure_gpt(steps: int, warmup: int) -> dict:
+    """The 1.3B GPT-style buffer with 16 workers (clamp 2.0, reset every 2000
+    steps): compress, server, decompress and the frozen-v Adam step at about
+    190 GB resident."""
+    import torch
+
+    from momentum_compression_amd import onebit as ob
+    from momentum_compression_amd.state import OneBitGroup
+    from workloads import configs as C
+    from workloads import synth as S
+
+    dev = torch.device("cuda:0")
+    wl = C.get("gpt_1.3B_x16")
+    N, n = wl.N, wl.n
+    print(f"[bench] rows: {wl.name} N={N} n={n}", file=sys.stderr, flush=True)
+    sig = S.per_element(S.segment_sigmas(wl), wl, dev)
+    m = S.momentum(wl, 1, dev, sigma_elem=sig)
+    del sig
+    x = S.params(wl, dev)
+    v = S.frozen_variance(wl, dev)
+    grp = OneBitGroup(N, n, dev, clip=wl.clip, reset_interval=wl.reset_interval)
+    stream = torch.cuda.current_stream()
+    grp.compress(m, 1, first=True)
+    grp.server(1, first=True, decompress=False)
+    t = [2]
+
+    def comp():
+        grp.compress(m, t[0])
+
+    def serv():
+        grp.server(t[0], decompress=False)
+
+    def dec():
+        ob.onebit_decompress(grp.sv_bits, grp.sv_scales, grp.mbar, N, n)
+
+    def adam():
+        grp.adam_step(x, v, wl.lr, wl.eps)
+        t[0] += 1
+
+    ms = _time_calls([comp, serv, dec, adam], warmup, steps, stream)
+    out = {"workload": wl.name, "N": N, "workers": n, "step_ms": round(sum(ms), 4),
+           "worker_elements_per_s": n * N / (sum(ms) * 1e-3),
+           "compress_clamp": _row(ms[0], B_COMPRESS * n * N, n * N),
+           "server": _row(ms[1], b_server(n) * N, N),
+           "decompress": _row(ms[2], B_DECOMPRESS * N, N),
+           "adam": _row(ms[3], B_ADAM * N, N)}
+    del grp, m, x, v
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_copy(steps: int, warmup: int) -> dict:
+    """A plain device copy of 2^31 floats (torch's copy kernel): the bandwidth
+    a simple read-one-write-one stream reaches, as context for the rows."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    src = torch.empty(1 << 31, device=dev)
+    src.fill_(1.0)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    ms = _time_calls([lambda: dst.copy_(src)], warmup, steps, stream)[0]
+    out = {"floats": src.numel(), "ms": round(ms, 4),
+           "GBps": round(8.0 * src.numel() / (ms * 1e-3) / 1e9, 1),
+           "frac_of_8TBps": round(8.0 * src.numel() / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_int8(steps: int, warmup: int) -> dict:
     """Block INT8 stochastic rounding with error feedback and dequantised
     output on 2^30 Laplace gradients (block 256)."""
@@ -385,7 +455,8 @@ def main() -> int:
                                                    "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true",
-                    help="skip the LAMB, INT8, fused and warmup rows measured after the headline step")
+                    help="skip the rows measured after the headline step (LAMB, INT8, fused, "
+                         "warmup, GPT 1.3B, copy reference)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -519,7 +590,9 @@ def main() -> int:
         out["rows"] = {"lamb": measure_lamb(max(3, args.steps // 2), 1),
                        "int8": measure_int8(max(3, args.steps // 2), 1),
                        "fused_adam_from_gradients": measure_fused(max(3, args.steps // 2), 1),
-                       "warmup": measure_warmup(max(3, args.steps // 2), 1)}
+                       "warmup": measure_warmup(max(3, args.steps // 2), 1),
+                       "gpt_1.3B_x16": measure_gpt(max(3, args.steps // 2), 1),
+                       "copy_reference": measure_copy(max(3, args.steps // 2), 1)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl)
