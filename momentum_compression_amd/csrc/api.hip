@@ -170,7 +170,7 @@ int onebit_server_reduce_ex(const uint32_t* bits, const float* scales, float* ef
 
     const ChunkPlan plan = make_plan(N / n, n, kServerIters);
     if (sum_depth(plan) > kMaxSumDepth || !groups_ok(plan.bpc)) return ONEBIT_E_SIZE;
-    if (m_out && !groups_ok(ceil_div(N, (int64_t)kMaxIters * kTile))) return ONEBIT_E_SIZE;
+    if (m_out && !groups_ok(ceil_div(N, (int64_t)kDecompressTiles * kTile))) return ONEBIT_E_SIZE;
     double* partials = static_cast<double*>(ws);
     hipError_t e = launch_server(bits, scales, ef, sv_scales, sv_bits, partials, N, n, plan,
                                  reset != 0, seg_off, seg_err_ratio, n_seg, stream);
@@ -201,7 +201,7 @@ int onebit_decompress(const uint32_t* sv_bits, const float* sv_scales, float* m_
     if ((st = check_segments(seg_off, seg_k, n_seg, true))) return st;
     if (!aligned(sv_bits, 4) || !aligned(sv_scales, 4) || !aligned(m_out, 16)) return ONEBIT_E_ALIGN;
     if (N == 0) return ONEBIT_OK;
-    if (!groups_ok(ceil_div(N, (int64_t)kMaxIters * kTile))) return ONEBIT_E_SIZE;
+    if (!groups_ok(ceil_div(N, (int64_t)kDecompressTiles * kTile))) return ONEBIT_E_SIZE;
     return hip_status(
         launch_decompress(sv_bits, sv_scales, m_out, seg_off, seg_k, n_seg, N, n, stream));
 }

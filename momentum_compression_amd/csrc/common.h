@@ -23,6 +23,7 @@ constexpr int kCompressUnroll = 1;
 constexpr int kServerIters = 2;
 constexpr int kServerUnroll = 2;
 constexpr int kInt8Tiles = 2;
+constexpr int kDecompressTiles = 4;
 constexpr int kLambTiles = 4;           // tiles per workgroup in the LAMB pass (5 streams in flight)
 
 // workgroups of the LAMB pass over N elements

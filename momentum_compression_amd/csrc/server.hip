@@ -220,19 +220,22 @@ hipError_t launch_server(const uint32_t* bits, const float* scales, float* ef, c
 }
 
 // ---------------------------------------------------------------- decompress
-// Workgroups cover kMaxIters consecutive tiles; each lane writes 4 elements
-// per tile (nontemporal: the output is consumed by a later kernel).
+// Workgroups cover kDecompressTiles consecutive tiles; each lane writes 4
+// elements per tile (nontemporal: the output is consumed by a later kernel).
+// The chunk of the workgroup's first element comes from one (scalar)
+// division; a lane steps to later chunks by comparison, since L is a
+// multiple of 64 and the 4 elements of a lane share a chunk.
 template <bool SEG>
 __global__ __launch_bounds__(kThreads) void decompress_kernel(
     const uint32_t* __restrict__ sv_bits, const float* __restrict__ S, float* __restrict__ out,
     const int64_t* __restrict__ seg_off, const float* __restrict__ seg_k, int32_t n_seg, int64_t N,
     int64_t L) {
-    const int64_t wstart = (int64_t)blockIdx.x * kMaxIters * kTile;
+    const int64_t wstart = (int64_t)blockIdx.x * kDecompressTiles * kTile;
     const int64_t j0 = wstart + 4 * (int64_t)threadIdx.x;
     if (j0 >= N) return;
-    uint32_t words[kMaxIters];
+    uint32_t words[kDecompressTiles];
 #pragma unroll
-    for (int u = 0; u < kMaxIters; ++u) {
+    for (int u = 0; u < kDecompressTiles; ++u) {
         const int64_t J = j0 + (int64_t)u * kTile;
         words[u] = J < N ? sv_bits[J >> 5] : 0u;
     }
@@ -251,15 +254,22 @@ __global__ __launch_bounds__(kThreads) void decompress_kernel(
     }
     // value of a set bit: S[c], or S[c] / k_l for the current (chunk, layer);
     // a clear bit gives its negation (the quotient of -S is exactly -(S / k))
-    int64_t cur_c = -1;
-    float q = 0.0f;
+    int64_t c = wstart / L;
+    int64_t c_end = (c + 1) * L;
+    while (j0 >= c_end) {
+        ++c;
+        c_end += L;
+    }
+    float q = SEG ? S[c] / kv : S[c];
 #pragma unroll
-    for (int u = 0; u < kMaxIters; ++u) {
+    for (int u = 0; u < kDecompressTiles; ++u) {
         const int64_t J = j0 + (int64_t)u * kTile;
         if (J >= N) break;
-        const int64_t c = J / L;  // L is a multiple of 64, so the 4 elements share a chunk
-        if (c != cur_c) {
-            cur_c = c;
+        if (J >= c_end) {
+            while (J >= c_end) {
+                ++c;
+                c_end += L;
+            }
             q = SEG ? S[c] / kv : S[c];
         }
         const uint32_t word = words[u] >> (J & 31);
@@ -286,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void decompress_kernel(
 hipError_t launch_decompress(const uint32_t* sv_bits, const float* S, float* m_out,
                              const int64_t* seg_off, const float* seg_k, int32_t n_seg,
                              int64_t N, int32_t n, hipStream_t st) {
-    const int64_t per_wg = (int64_t)kMaxIters * kTile;
+    const int64_t per_wg = (int64_t)kDecompressTiles * kTile;
     const dim3 grid((unsigned)((N + per_wg - 1) / per_wg));
     const int64_t L = N / n;
     if (seg_off)
