@@ -1,0 +1,246 @@
+"""Mutation check of the oracle's pins.
+
+Each case plants one plausible mistake in the oracle -- a flipped sign, a
+wrong bit order, a swapped factor, a missing term -- for the duration of the
+case only (on the CPU, through the module attribute the oracle itself looks
+up at call time), runs the pins of the affected oracle modules, and asserts
+that at least one of them fails.  A case that no pin caught would mean the
+oracle could carry that mistake unnoticed.
+
+The Philox cases rerun the rocRAND cross-check pins with the cross-check
+built once for this module.
+"""
+
+import importlib
+import inspect
+from unittest import mock
+
+import numpy as np
+import pytest
+
+from oracle import bits as B
+from oracle import exact as X
+from oracle import int8 as I
+from oracle import onebit as O
+from oracle import optim as P
+from oracle import philox as PH
+from oracle import warmup as W
+
+F32 = np.float32
+
+
+def _pin_calls(module_name, fixtures):
+    """(name, function, kwargs) for every pin of a module: no arguments, the
+    fixtures given, or a single parametrize mark expanded into its cases."""
+    mod = importlib.import_module(module_name)
+    for name, fn in sorted(vars(mod).items()):
+        if not name.startswith("test_") or not callable(fn):
+            continue
+        params = list(inspect.signature(fn).parameters)
+        marks = [m for m in getattr(fn, "pytestmark", []) if m.name == "parametrize"]
+        if not params:
+            yield name, fn, {}
+        elif set(params) <= set(fixtures):
+            yield name, fn, {p: fixtures[p] for p in params}
+        elif len(marks) == 1:
+            names = [p.strip() for p in marks[0].args[0].split(",")]
+            if set(names) != set(params):
+                continue
+            for vals in marks[0].args[1]:
+                vals = vals if isinstance(vals, (tuple, list)) else (vals,)
+                yield name, fn, dict(zip(names, vals))
+
+
+def _first_failing(modules, fixtures):
+    for m in modules:
+        for name, fn, kw in _pin_calls(m, fixtures):
+            try:
+                with np.errstate(all="ignore"):
+                    fn(**kw)
+            except AssertionError:  # only a failed pin counts (a broken mutant does not)
+                return f"{m}.{name}"
+    return None
+
+
+# ---------------------------------------------------------------- mutants
+
+def sign_gt(x):  # sign(0) = -1
+    return np.asarray(x) > 0
+
+
+def pack_msb_first(b):  # numpy's default bit order
+    b = np.asarray(b, dtype=bool).ravel()
+    weights = np.uint64(1) << np.arange(31, -1, -1, dtype=np.uint64)
+    return (b.reshape(-1, 32).astype(np.uint64) * weights).sum(axis=1).astype(np.uint32)
+
+
+def error_wrong_sign(gc, s):
+    s = F32(s)
+    return np.where(B.sign_bit(gc), gc + s, gc - s).astype(F32)
+
+
+def mean_over_n_minus_1(x):
+    a = np.asarray(x, dtype=F32).ravel()
+    return X.round_rational_to_f32(X.abs_units(a), max(1, a.size - 1) << 149)
+
+
+def round_truncating(num, den):  # toward zero instead of to nearest
+    q = F32(num / den)
+    if abs(float(q)) > num / den:
+        q = np.nextafter(q, F32(0))
+    return F32(q)
+
+
+def clamp_half(x, clip):
+    c = F32(clip)
+    if not (c > 0) or np.isinf(c):
+        return x
+    return np.fmin(np.fmax(x, -c / 2), c / 2).astype(F32)
+
+
+def local_momentum_swapped(g, mbar_prev, beta1):
+    b1 = F32(beta1)
+    omb1 = F32(F32(1.0) - b1)
+    a = (omb1 * np.asarray(mbar_prev, dtype=F32)).astype(F32)
+    return (a[None, :] + (b1 * np.asarray(g, dtype=F32)).astype(F32)).astype(F32)
+
+
+def decompress_times_k(sbits, S, k=None):
+    d = O.__dict__["_orig_decompress"](sbits, S)
+    return d if k is None else (d * np.asarray(k, dtype=F32)).astype(F32)
+
+
+def adam_eps_inside(x, m, v, lr, eps):
+    den = np.sqrt((np.asarray(v, dtype=F32) + F32(eps)).astype(F32)).astype(F32)
+    upd = (np.asarray(m, dtype=F32) / den).astype(F32)
+    return (np.asarray(x, dtype=F32) - (F32(lr) * upd).astype(F32)).astype(F32)
+
+
+def reconstruct_over_beta1(m, m_prev, beta1):
+    b1 = F32(beta1)
+    num = (np.asarray(m, dtype=F32) - (b1 * np.asarray(m_prev, dtype=F32)).astype(F32)).astype(F32)
+    return (num / b1).astype(F32)
+
+
+def fresh_variance_swapped(v_f, g, beta2):
+    b2 = F32(beta2)
+    omb2 = F32(F32(1.0) - b2)
+    g = np.asarray(g, dtype=F32)
+    return ((omb2 * np.asarray(v_f, dtype=F32)).astype(F32)
+            + (b2 * (g * g).astype(F32)).astype(F32)).astype(F32)
+
+
+def ratio_hard_clip_first(R, r_prev, c_avg, thr, r_min, r_max):
+    R = np.asarray(R, dtype=F32)
+    r_prev = np.asarray(r_prev, dtype=F32)
+    R = np.where(np.isnan(R), r_prev, R).astype(F32)
+    r = np.fmin(np.fmax(R, F32(r_min)), F32(r_max)).astype(F32)
+    lo = (F32(F32(1.0) - F32(thr)) * r_prev).astype(F32)
+    hi = (F32(F32(1.0) + F32(thr)) * r_prev).astype(F32)
+    r = np.fmin(np.fmax(r, lo), hi).astype(F32)
+    return r, (np.asarray(c_avg, dtype=F32) * r).astype(F32)
+
+
+def layer_max_keeps_nan(vals, seg_off):
+    out = np.full(len(seg_off) - 1, np.nan, dtype=F32)
+    for l in range(len(seg_off) - 1):
+        seg = np.asarray(vals[int(seg_off[l]):int(seg_off[l + 1])], dtype=F32)
+        if seg.size:
+            out[l] = seg.max()
+    return out
+
+
+def trust_ratio_inverted(x_l, u_l):
+    sx, su = W.exact_sumsq(x_l), W.exact_sumsq(u_l)
+    if sx == 0.0 or su == 0.0:
+        return F32(1.0)
+    return F32(np.sqrt(su) / np.sqrt(sx))
+
+
+def average_swapped(c_avg, c, beta_c):
+    c = np.asarray(c, dtype=F32)
+    if c_avg is None:
+        return c.copy()
+    return ((W._omb(beta_c) * np.asarray(c_avg, dtype=F32)).astype(F32)
+            + (F32(beta_c) * c).astype(F32)).astype(F32)
+
+
+def momentum_scale_by_norm(m, seg_off):
+    m = np.asarray(m, dtype=F32)
+    S = len(seg_off) - 1
+    nrm = [np.sqrt(W.exact_sumsq(m[int(seg_off[l]):int(seg_off[l + 1])])) for l in range(S)]
+    valid = [a for a in nrm if a > 0]
+    mean = sum(valid) / len(valid) if valid else 0.0
+    return np.array([F32(mean / a) if a > 0 else F32(1.0) for a in nrm], dtype=F32)
+
+
+def moments_abs_g(m, v, g, beta1, beta2):
+    b1, b2 = F32(beta1), F32(beta2)
+    g = np.asarray(g, dtype=F32)
+    m_new = ((b1 * np.asarray(m, dtype=F32)).astype(F32) + (W._omb(beta1) * g).astype(F32)).astype(F32)
+    v_new = ((b2 * np.asarray(v, dtype=F32)).astype(F32)
+             + (W._omb(beta2) * np.abs(g)).astype(F32)).astype(F32)
+    return m_new, v_new
+
+
+def uniforms_squared(J0, count, seed, step):
+    u = I.__dict__["_orig_uniforms"](J0, count, seed, step)
+    return (u * u).astype(F32)
+
+
+def round_half_even(x):
+    return np.rint(np.asarray(x, dtype=F32)).astype(F32)
+
+
+CASES = [
+    # (id, module, attribute, replacement, pin modules)
+    ("sign(0) = -1", B, "sign_bit", sign_gt, ["tests.test_oracle_bits", "tests.test_oracle_onebit"]),
+    ("bit order MSB first", B, "pack", pack_msb_first, ["tests.test_oracle_bits"]),
+    ("error with the wrong sign", O, "error_from", error_wrong_sign, ["tests.test_oracle_onebit"]),
+    ("mean over L - 1", O, "mean_abs_f32", mean_over_n_minus_1, ["tests.test_oracle_onebit"]),
+    ("truncating rounding", X, "round_rational_to_f32", round_truncating, ["tests.test_oracle_exact"]),
+    ("clamp at half the bound", O, "clamp", clamp_half, ["tests.test_oracle_onebit"]),
+    ("momentum factors swapped", O, "local_momentum", local_momentum_swapped, ["tests.test_oracle_onebit"]),
+    ("decompress multiplies by k", O, "decompress", decompress_times_k, ["tests.test_oracle_onebit"]),
+    ("eps inside the root", P, "adam_frozen_step", adam_eps_inside,
+     ["tests.test_oracle_optim", "tests.test_oracle_warmup"]),
+    ("gradient over beta1", P, "reconstruct_gradient", reconstruct_over_beta1, ["tests.test_oracle_optim"]),
+    ("variance factors swapped", P, "fresh_variance", fresh_variance_swapped, ["tests.test_oracle_optim"]),
+    ("hard clip before soft clip", P, "lamb_ratio_update", ratio_hard_clip_first, ["tests.test_oracle_optim"]),
+    ("layer max keeps NaN", P, "layer_max", layer_max_keeps_nan, ["tests.test_oracle_optim"]),
+    ("trust ratio inverted", W, "trust_ratio", trust_ratio_inverted, ["tests.test_oracle_warmup"]),
+    ("average factors swapped", W, "coefficient_average", average_swapped, ["tests.test_oracle_warmup"]),
+    ("k from the norm, not the RMS", W, "momentum_scale", momentum_scale_by_norm,
+     ["tests.test_oracle_warmup"]),
+    ("variance from |g|", W, "moments", moments_abs_g, ["tests.test_oracle_warmup"]),
+    ("biased uniforms", I, "uniforms", uniforms_squared, ["tests.test_oracle_int8"]),
+    ("halves to even", I, "round_half_away", round_half_even, ["tests.test_oracle_int8"]),
+    ("Weyl constant", PH, "W0", np.uint64(0x9E3779BB), ["tests.test_oracle_philox"]),
+    ("multiplier", PH, "M1", np.uint64(0xCD9E8D59), ["tests.test_oracle_philox"]),
+]
+
+
+@pytest.fixture(scope="module")
+def fixtures():
+    from tests.test_oracle_philox import build_rocrand_dump
+
+    run = build_rocrand_dump()
+    return {} if run is None else {"rocrand_dump": run}
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_pins_catch_planted_mistake(case, fixtures):
+    _, module, attr, mutant, pins = case
+    if "tests.test_oracle_philox" in pins and "rocrand_dump" not in fixtures:
+        pytest.skip("hipcc not available to build the rocRAND cross-check")
+    original = getattr(module, attr)
+    extra = {}
+    if attr == "decompress":
+        extra = {"_orig_decompress": original}
+    if attr == "uniforms":
+        extra = {"_orig_uniforms": PH.uniforms}
+    with mock.patch.dict(module.__dict__, extra), mock.patch.object(module, attr, mutant):
+        caught = _first_failing(pins, fixtures)
+    assert caught is not None, f"no pin caught the planted mistake in {module.__name__}.{attr}"
+    # and the unmodified oracle passes the same pins
+    assert getattr(module, attr) is original

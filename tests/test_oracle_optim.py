@@ -84,6 +84,18 @@ def test_ratio_clip_bounds():
     assert np.array_equal(c, r)
 
 
+def test_ratio_outer_clip_is_hard():
+    """The page nests the soft clip inside the hard one, so with r_{t-1}
+    outside [r_min, r_max] the hard bounds win: r_{t-1} = 1.3 with
+    r_min = r_max = 1 gives 1 (the other nesting would give 1.17), and
+    r_{t-1} = 5 with r_max = 4 gives 4 (not 4.5)."""
+    r, _ = P.lamb_ratio_update(a(0.2, 1.0, 10.0), a(1.3, 1.3, 5.0), a(1.0, 1.0, 1.0), 0.1,
+                               1.0, 1.0)
+    assert r.tolist() == [1.0, 1.0, 1.0]
+    r, c = P.lamb_ratio_update(a(10.0, 1.0), a(5.0, 5.0), a(2.0, 2.0), 0.1, 0.5, 4.0)
+    assert r.tolist() == [4.0, 4.0] and c.tolist() == [8.0, 8.0]
+
+
 def test_ratio_no_valid_keeps_previous():
     r, c = P.lamb_ratio_update(a(np.nan), a(1.7), a(2.0), 0.1, 0.5, 4.0)
     assert r[0] == F32(1.7) and c[0] == F32(3.4)

@@ -22,11 +22,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "xcheck", "rocrand_philox.cpp")
 
 
-@pytest.fixture(scope="module")
-def rocrand_dump():
+def build_rocrand_dump():
+    """Compile the rocRAND cross-check for the host; returns a function from
+    (seed, subsequence, offset) triples to rocRAND's output words, or None
+    when hipcc is not available."""
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(hipcc):
-        pytest.skip("hipcc not available to build the rocRAND cross-check")
+        return None
     out = os.path.join(tempfile.mkdtemp(prefix="philox_xcheck_"), "rocrand_philox")
     subprocess.run([hipcc, "-O1", "-o", out, SRC], check=True, capture_output=True, timeout=300)
 
@@ -36,6 +38,14 @@ def rocrand_dump():
         return np.array([[int(w, 16) for w in line.split()] for line in res.stdout.splitlines()],
                         dtype=np.uint64).astype(np.uint32)
 
+    return run
+
+
+@pytest.fixture(scope="module")
+def rocrand_dump():
+    run = build_rocrand_dump()
+    if run is None:
+        pytest.skip("hipcc not available to build the rocRAND cross-check")
     return run
 
 
