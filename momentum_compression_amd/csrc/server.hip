@@ -220,11 +220,8 @@ hipError_t launch_server(const uint32_t* bits, const float* scales, float* ef, c
 }
 
 // ---------------------------------------------------------------- decompress
-// Workgroups cover kDecompressTiles consecutive tiles; each lane writes 4
-// elements per tile (nontemporal: the output is consumed by a later kernel).
-// The chunk of the workgroup's first element comes from one (scalar)
-// division; a lane steps to later chunks by comparison, since L is a
-// multiple of 64 and the 4 elements of a lane share a chunk.
+// Workgroups cover kDecompressTiles consecutive tiles; each lane writes 4 elements
+// per tile (nontemporal: the output is consumed by a later kernel).
 template <bool SEG>
 __global__ __launch_bounds__(kThreads) void decompress_kernel(
     const uint32_t* __restrict__ sv_bits, const float* __restrict__ S, float* __restrict__ out,
@@ -254,22 +251,15 @@ __global__ __launch_bounds__(kThreads) void decompress_kernel(
     }
     // value of a set bit: S[c], or S[c] / k_l for the current (chunk, layer);
     // a clear bit gives its negation (the quotient of -S is exactly -(S / k))
-    int64_t c = wstart / L;
-    int64_t c_end = (c + 1) * L;
-    while (j0 >= c_end) {
-        ++c;
-        c_end += L;
-    }
-    float q = SEG ? S[c] / kv : S[c];
+    int64_t cur_c = -1;
+    float q = 0.0f;
 #pragma unroll
     for (int u = 0; u < kDecompressTiles; ++u) {
         const int64_t J = j0 + (int64_t)u * kTile;
         if (J >= N) break;
-        if (J >= c_end) {
-            while (J >= c_end) {
-                ++c;
-                c_end += L;
-            }
+        const int64_t c = J / L;  // L is a multiple of 64, so the 4 elements share a chunk
+        if (c != cur_c) {
+            cur_c = c;
             q = SEG ? S[c] / kv : S[c];
         }
         const uint32_t word = words[u] >> (J & 31);
