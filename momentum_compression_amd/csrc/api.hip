@@ -77,7 +77,7 @@ const char* onebit_strerror(int status) {
     switch (status) {
         case ONEBIT_OK: return "ok";
         case ONEBIT_E_NULL: return "required pointer is NULL";
-        case ONEBIT_E_SIZE: return "invalid size (N must be a multiple of 64*n, 1 <= n <= 64, N/n < 2^32; block and N must agree)";
+        case ONEBIT_E_SIZE: return "invalid size (N must be a multiple of 64*n, 1 <= n <= 64, N/n < 2^31; block and N must agree; grids within 2^32 work-items)";
         case ONEBIT_E_ALIGN: return "pointer misaligned (streamed float buffers need 16 bytes)";
         case ONEBIT_E_WORKSPACE: return "workspace missing or smaller than onebit_workspace_bytes()";
         case ONEBIT_E_ARG: return "invalid argument";
