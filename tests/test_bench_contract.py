@@ -1,0 +1,54 @@
+"""Host-side checks of bench.py: the one-GPU refusal, the stored counters'
+reading, and the CPU baseline's record (timed here on a small workload)."""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from workloads import configs as C  # noqa: E402
+
+
+@pytest.mark.parametrize("gpus", ["2", "8"])
+def test_more_than_one_gpu_is_refused(gpus):
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", gpus],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+    assert res.stdout.strip() == ""
+
+
+def test_counter_summary_reads_per_launch_bytes():
+    wl = C.get("bert_large_335M_x8")
+    elems = wl.n * wl.N
+    assert bench.read_traffic(elems + 1) is None  # another launch size: not this summary
+    t = bench.read_traffic(elems)
+    if t is None:
+        pytest.skip("the stored counters predate the current compress source")
+    # every stream once: within 2 % of the algorithmic 12.125 B per element
+    assert abs(t / (bench.B_COMPRESS * elems) - 1.0) < 0.02
+
+
+def test_source_hash_ignores_comments(tmp_path, monkeypatch):
+    a, b = tmp_path / "a.hip", tmp_path / "b.hip"
+    a.write_text("int f(int x) { return x + 1; }  // one\n")
+    b.write_text("/* other words */\nint  f(int x)\n{ return x + 1; }\n")
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(a)])
+    ha = bench.kernel_source_hash()
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(b)])
+    assert bench.kernel_source_hash() == ha
+    b.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.kernel_source_hash() != ha
+
+
+def test_cpu_baseline_record():
+    wl = C.get("adam_2^20_x4")
+    rec = bench.cpu_baseline(wl)
+    assert rec["kind"] == "oracle" and rec["cores"] == 1 and rec["unit"] == "elements/s"
+    assert rec["value"] > 0
+    assert f"{wl.L}-element" in rec["sample"]
