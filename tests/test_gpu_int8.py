@@ -63,6 +63,27 @@ def test_int8_without_feedback_and_specials():
     assert np.all(host(codes)[:256] == 0)
 
 
+def test_int8_fraction_equal_to_its_uniform():
+    """Elements whose fraction equals their own Philox uniform round down
+    (u < p); one grid step of the uniforms above, they round up."""
+    from tests.test_oracle_int8 import _tie_block
+
+    dev = device()
+    for above in (False, True):
+        g_h, idx = _tie_block(5, 2, above)
+        print(f"[int8 tie] above={above}", flush=True)
+        g = torch.from_numpy(g_h).to(dev)
+        codes = torch.empty(256, dtype=torch.int8, device=dev)
+        scales = torch.empty(1, device=dev)
+        deq = torch.empty(256, device=dev)
+        ob.int8_sr_quantize(g, None, codes, scales, deq, 256, 256, 5, 2)
+        torch.cuda.synchronize()
+        o = int8_sr(g_h, None, 5, 2, 256)
+        assert np.array_equal(host(codes), o["codes"])
+        assert np.all(host(codes)[idx] == (1 if above else 0))
+        same_f32(host(deq), o["deq"], "deq")
+
+
 def test_int8_large_step_counter_and_index():
     """Element indices beyond 2^32 exercise the high counter word."""
     dev = device()

@@ -4,7 +4,8 @@ Properties fixed by the gradient-quantisation tutorial's INT8 recipe: codes
 stay in [-127, 127]; the dequantised value is within one scale step of the
 input; an input that is an exact multiple of the scale is coded exactly;
 zero blocks stay zero; the block maximum codes to 126 or 127; stochastic
-rounding is unbiased and rounds up with probability equal to the fraction.
+rounding is unbiased and rounds up with probability equal to the fraction,
+which fixes the comparison u < p (a fraction equal to its uniform rounds down).
 """
 
 import numpy as np
@@ -44,6 +45,31 @@ def test_integral_inputs_are_exact():
     assert np.array_equal(out["codes"].astype(F32), g)
     assert np.array_equal(out["deq"], g)
     assert np.all(out["e"] == 0)
+
+
+def _tie_block(seed, step, above):
+    """One block whose maximum 127 gives scale 1 and whose other elements
+    carry x = u_J (above=False) or u_J + 2^-24 (above=True): fraction p = x."""
+    u = uniforms(0, 256, seed, step)
+    idx = np.array([j for j in range(1, 256) if u[j] > 0][:64])
+    g = np.zeros(256, dtype=F32)
+    g[0] = 127
+    g[idx] = (u[idx] + (F32(2.0 ** -24) if above else F32(0))).astype(F32)
+    return g, idx
+
+
+def test_fraction_equal_to_its_uniform_rounds_down():
+    """Rounding up with probability p, the fraction: of the 2^24 equally likely
+    uniforms (multiples of 2^-24 in [0, 1)) exactly p * 2^24 lie below a p that
+    is itself such a multiple, so the unbiased rule is u < p, and u == p rounds
+    down (u <= p would round up with probability p + 2^-24)."""
+    g, idx = _tie_block(5, 2, above=False)
+    out = int8_sr(g, None, seed=5, step=2)
+    assert out["scales"][0] == 1
+    assert np.all(out["codes"][idx] == 0)
+    g, idx = _tie_block(5, 2, above=True)
+    out = int8_sr(g, None, seed=5, step=2)
+    assert np.all(out["codes"][idx] == 1)
 
 
 def test_zero_block_and_max_code():

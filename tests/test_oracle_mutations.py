@@ -192,6 +192,158 @@ def round_half_even(x):
     return np.rint(np.asarray(x, dtype=F32)).astype(F32)
 
 
+def unpack_msb_first(words, count=None):
+    w = np.asarray(words, dtype=np.uint32).ravel()
+    pos = np.arange(31, -1, -1, dtype=np.uint32)
+    b = ((w[:, None] >> pos[None, :]) & np.uint32(1)).astype(bool).ravel()
+    return b if count is None else b[:count]
+
+
+def signed_swapped(b, s):
+    s = F32(s)
+    return np.where(b, -s, s).astype(F32)
+
+
+def _server_chunk_variant(order="up", reciprocal=False, keep_error_on_reset=False):
+    def server_chunk(bits_c, s_c, E_c, reset=False, unit_scale=False, err_ratio_c=None):
+        bits_c = np.asarray(bits_c, dtype=np.uint32)
+        s_c = np.asarray(s_c, dtype=F32)
+        n = s_c.shape[0]
+        L = bits_c.shape[1] * 32
+        acc = np.zeros(L, dtype=F32)
+        for i in (range(n) if order == "up" else range(n - 1, -1, -1)):
+            acc = (acc + B.signed(B.unpack(bits_c[i]), s_c[i])).astype(F32)
+        avg = ((acc * F32(F32(1.0) / F32(n))) if reciprocal else (acc / F32(n))).astype(F32)
+        E_in = np.zeros(L, dtype=F32) if (reset and not keep_error_on_reset) else np.asarray(E_c, dtype=F32)
+        if err_ratio_c is not None and not reset:
+            E_in = (np.asarray(err_ratio_c, dtype=F32) * E_in).astype(F32)
+        g2 = (avg + E_in).astype(F32)
+        S = F32(1.0) if unit_scale else O.mean_abs_f32(g2)
+        return {"avg": avg, "g2": g2, "bits": B.pack(B.sign_bit(g2)), "S": S,
+                "E": O.error_from(g2, S)}
+    return server_chunk
+
+
+def _worker_variant(clip_before=False, ignore_reset=False):
+    def worker_compress(m, e, clip=0.0, reset=False, k=None, unit_scale=False, err_ratio=None):
+        m = np.asarray(m, dtype=F32)
+        n, N = m.shape
+        L = N // n
+        e_in = np.zeros_like(m) if (reset and not ignore_reset) else np.asarray(e, dtype=F32)
+        if err_ratio is not None and not reset:
+            e_in = (np.asarray(err_ratio, dtype=F32)[None, :] * e_in).astype(F32)
+        gc = np.empty_like(m)
+        e_out = np.empty_like(m)
+        s = np.empty((n, n), dtype=F32)
+        bits = np.empty((n, N // 32), dtype=np.uint32)
+        for i in range(n):
+            mi = m[i] if k is None else (np.asarray(k, dtype=F32) * m[i]).astype(F32)
+            if clip_before:
+                gi = (O.clamp(mi, clip) + e_in[i]).astype(F32)
+            else:
+                gi = O.clamp((mi + e_in[i]).astype(F32), clip)
+            gc[i] = gi
+            for c in range(n):
+                sl = slice(c * L, (c + 1) * L)
+                s[i, c] = F32(1.0) if unit_scale else O.mean_abs_f32(gi[sl])
+                e_out[i, sl] = O.error_from(gi[sl], s[i, c])
+            bits[i] = B.pack(B.sign_bit(gi))
+        return {"gc": gc, "bits": bits, "s": s, "e": e_out}
+    return worker_compress
+
+
+def decompress_first_scale(sbits, S, k=None):
+    S = np.asarray(S, dtype=F32)
+    return O.__dict__["_orig_decompress"](sbits, np.full_like(S, S[0]), k)
+
+
+def layer_scale_swapped(buf, seg_off, k, divide):
+    return O.__dict__["_orig_layer_scale"](buf, seg_off, k, not divide)
+
+
+def per_element_k_shifted(seg_off, k):
+    k = np.asarray(k, dtype=F32)
+    sizes = np.diff(np.asarray(seg_off, dtype=np.int64))
+    return np.repeat(np.roll(k, 1), sizes).astype(F32)
+
+
+def local_momentum_unrounded(g, mbar_prev, beta1):
+    b1 = F32(beta1)
+    a = (b1 * np.asarray(mbar_prev, dtype=F32)).astype(F32)
+    t = ((1.0 - float(beta1)) * np.asarray(g, dtype=F32).astype(np.float64)).astype(F32)
+    return (a[None, :] + t).astype(F32)
+
+
+def lamb_apply_without_c(x, m, v_tw, seg_off, c_used, lr, eps):
+    return P.__dict__["_orig_lamb_apply"](x, m, v_tw, seg_off, np.ones_like(np.asarray(c_used, dtype=F32)),
+                                           lr, eps)
+
+
+def lamb_step_ratio_inverted(*args, **kw):
+    out = P.__dict__["_orig_lamb_frozen_step"](*args, **kw)
+    out["err_ratio"] = (F32(1.0) / out["err_ratio"]).astype(F32)
+    return out
+
+
+def philox_nine_rounds(ctr, key):
+    x = np.asarray(ctr, dtype=np.uint32).astype(np.uint64)
+    k = np.broadcast_to(np.asarray(key, dtype=np.uint32), x.shape[:-1] + (2,)).astype(np.uint64)
+    x0, x1, x2, x3 = x[..., 0], x[..., 1], x[..., 2], x[..., 3]
+    k0, k1 = k[..., 0].copy(), k[..., 1].copy()
+    mask = np.uint64(0xFFFFFFFF)
+    for rnd in range(9):
+        if rnd:
+            k0 = (k0 + PH.W0) & mask
+            k1 = (k1 + PH.W1) & mask
+        p0, p1 = PH.M0 * x0, PH.M1 * x2
+        x0, x1, x2, x3 = (p1 >> np.uint64(32)) ^ x1 ^ k0, p1 & mask, (p0 >> np.uint64(32)) ^ x3 ^ k1, p0 & mask
+    return np.stack([x0, x1, x2, x3], axis=-1).astype(np.uint32)
+
+
+def uniforms_down_half_step(J0, count, seed, step):  # u <= p in place of u < p
+    u = I.__dict__["_orig_uniforms"](J0, count, seed, step)
+    return (u.astype(np.float64) - 2.0 ** -25).astype(F32)
+
+
+def sumsq_binary32(a):
+    acc = F32(0.0)
+    for t in np.asarray(a, dtype=F32):
+        acc = F32(acc + F32(t * t))
+    return float(acc)
+
+
+def trust_ratio_zero_norm_zero(x_l, u_l):
+    sx, su = W.exact_sumsq(x_l), W.exact_sumsq(u_l)
+    if sx == 0.0 or su == 0.0:
+        return F32(0.0)
+    return F32(np.sqrt(sx) / np.sqrt(su))
+
+
+def average_started_at_one(c_avg, c, beta_c):
+    if c_avg is None:
+        c_avg = np.ones_like(np.asarray(c, dtype=F32))
+    return W.__dict__["_orig_coefficient_average"](c_avg, c, beta_c)
+
+
+def momentum_scale_counts_empty(m, seg_off):
+    import math
+    m = np.asarray(m, dtype=F32)
+    S = len(seg_off) - 1
+    rms = []
+    for l in range(S):
+        a, b = int(seg_off[l]), int(seg_off[l + 1])
+        rms.append(math.sqrt(W.exact_sumsq(m[a:b]) / (b - a)) if b > a else 0.0)
+    valid = [r for r in rms if r > 0.0]
+    k = np.ones(S, dtype=F32)
+    if not valid:
+        return k
+    mean = math.fsum(rms) / S
+    for l in range(S):
+        if rms[l] > 0.0:
+            k[l] = F32(mean / rms[l])
+    return k
+
+
 CASES = [
     # (id, module, attribute, replacement, pin modules)
     ("sign(0) = -1", B, "sign_bit", sign_gt, ["tests.test_oracle_bits", "tests.test_oracle_onebit"]),
@@ -217,6 +369,30 @@ CASES = [
     ("halves to even", I, "round_half_away", round_half_even, ["tests.test_oracle_int8"]),
     ("Weyl constant", PH, "W0", np.uint64(0x9E3779BB), ["tests.test_oracle_philox"]),
     ("multiplier", PH, "M1", np.uint64(0xCD9E8D59), ["tests.test_oracle_philox"]),
+    ("unpack MSB first", B, "unpack", unpack_msb_first, ["tests.test_oracle_bits", "tests.test_oracle_onebit"]),
+    ("scaled sign swapped", B, "signed", signed_swapped, ["tests.test_oracle_onebit"]),
+    ("server sums workers in reverse", O, "server_chunk", _server_chunk_variant(order="down"),
+     ["tests.test_oracle_onebit"]),
+    ("server average by a reciprocal", O, "server_chunk", _server_chunk_variant(reciprocal=True),
+     ["tests.test_oracle_onebit"]),
+    ("server error kept at reset", O, "server_chunk", _server_chunk_variant(keep_error_on_reset=True),
+     ["tests.test_oracle_onebit"]),
+    ("clip before compensation", O, "worker_compress", _worker_variant(clip_before=True),
+     ["tests.test_oracle_onebit"]),
+    ("worker reset ignored", O, "worker_compress", _worker_variant(ignore_reset=True),
+     ["tests.test_oracle_onebit"]),
+    ("decompress with chunk 0's scale", O, "decompress", decompress_first_scale, ["tests.test_oracle_onebit"]),
+    ("layer scale multiply / divide swapped", O, "layer_scale", layer_scale_swapped, ["tests.test_oracle_onebit"]),
+    ("layer coefficient one layer off", O, "per_element_k", per_element_k_shifted, ["tests.test_oracle_onebit"]),
+    ("1 - beta1 unrounded", O, "local_momentum", local_momentum_unrounded, ["tests.test_oracle_onebit"]),
+    ("LAMB step without c", P, "lamb_apply", lamb_apply_without_c, ["tests.test_oracle_optim"]),
+    ("error ratio inverted", P, "lamb_frozen_step", lamb_step_ratio_inverted, ["tests.test_oracle_optim"]),
+    ("Philox with 9 rounds", PH, "philox4x32_10", philox_nine_rounds, ["tests.test_oracle_philox"]),
+    ("u <= p", I, "uniforms", uniforms_down_half_step, ["tests.test_oracle_int8"]),
+    ("sum of squares in binary32", W, "exact_sumsq", sumsq_binary32, ["tests.test_oracle_warmup"]),
+    ("zero norm gives c = 0", W, "trust_ratio", trust_ratio_zero_norm_zero, ["tests.test_oracle_warmup"]),
+    ("average started at 1", W, "coefficient_average", average_started_at_one, ["tests.test_oracle_warmup"]),
+    ("k averages empty layers", W, "momentum_scale", momentum_scale_counts_empty, ["tests.test_oracle_warmup"]),
 ]
 
 
@@ -234,9 +410,7 @@ def test_pins_catch_planted_mistake(case, fixtures):
     if "tests.test_oracle_philox" in pins and "rocrand_dump" not in fixtures:
         pytest.skip("hipcc not available to build the rocRAND cross-check")
     original = getattr(module, attr)
-    extra = {}
-    if attr == "decompress":
-        extra = {"_orig_decompress": original}
+    extra = {f"_orig_{attr}": original}
     if attr == "uniforms":
         extra = {"_orig_uniforms": PH.uniforms}
     with mock.patch.dict(module.__dict__, extra), mock.patch.object(module, attr, mutant):

@@ -83,6 +83,27 @@ def test_reset_ignores_error():
         assert np.array_equal(a[key], b[key])
 
 
+def test_server_reset_ignores_error():
+    """The error reset (1-bit Adam article, section 4.1) drops the server's
+    carried error too: a reset step equals a step from zero error, both for
+    one chunk and for the whole buffer."""
+    rng = np.random.default_rng(31)
+    n, N = 4, 512
+    L = N // n
+    w = O.worker_compress(_draw(rng, (n, N)), np.zeros((n, N), dtype=F32))
+    E = _draw(rng, N)
+    zero = np.zeros(N, dtype=F32)
+    a = O.server_reduce(w["bits"], w["s"], E, reset=True)
+    b = O.server_reduce(w["bits"], w["s"], zero)
+    for key in ("g2", "S", "E", "bits"):
+        assert np.array_equal(a[key], b[key])
+    words = slice(L // 32, 2 * L // 32)
+    a = O.server_chunk(w["bits"][:, words], w["s"][:, 1], E[L:2 * L], reset=True)
+    b = O.server_chunk(w["bits"][:, words], w["s"][:, 1], zero[L:2 * L])
+    for key in ("g2", "S", "E", "bits"):
+        assert np.array_equal(a[key], b[key])
+
+
 def test_error_identity_within_one_rounding():
     """e_t = g'_t - q_t up to the one binary32 rounding of the subtraction."""
     rng = np.random.default_rng(11)
@@ -274,6 +295,16 @@ def test_layer_scale_segments():
     k = np.array([2, 0.5, 4], dtype=F32)
     assert list(O.layer_scale(buf, off, k, False)) == [2, 4, 6, 2, 20, 24, 28, 32, 36, 40]
     assert list(O.layer_scale(buf, off, k, True)) == [0.5, 1, 1.5, 8, 1.25, 1.5, 1.75, 2, 2.25, 2.5]
+
+
+def test_per_element_k_layout():
+    """Layer l's coefficient on elements seg_off[l] .. seg_off[l+1]-1, empty
+    layers taking none; it agrees with the segment-wise layer scale."""
+    off = [0, 2, 2, 5, 6]
+    k = np.array([3, 7, 5, 9], dtype=F32)
+    assert list(O.per_element_k(off, k)) == [3, 3, 5, 5, 5, 9]
+    buf = np.arange(1, 7, dtype=F32)
+    assert np.array_equal(O.layer_scale(buf, off, k, False), buf * O.per_element_k(off, k))
 
 
 def test_local_momentum_closed_forms():
