@@ -4,8 +4,12 @@ One step = the whole compressed 1-bit Adam hot path over one batch of
 synthetic momenta resident in HBM: worker compress of all n workers (reset,
 compensate, chunk scale, sign pack, error), server reduce (unpack, average,
 compensate, scale, pack, error), decompression of the global momentum, and
-the frozen-variance Adam update.  Default workload: BERT-Large-sized flat
-buffer of 335,141,888 fp32 elements, 8 simulated workers.
+the frozen-variance Adam update.  The decompression runs inside the Adam
+pass, which reads the packed server words once and writes both the
+decompressed momentum and the parameters; the separate decompression and
+Adam kernels are timed after the step as a row of their own.  Default
+workload: BERT-Large-sized flat buffer of 335,141,888 fp32 elements,
+8 simulated workers.
 
 Prints ONE JSON line.  `value` = compressed worker elements per second
 (n * N per step).  `roofline` reports the dominant kernel (worker compress)
@@ -16,7 +20,7 @@ oracle on a bounded sample of the same step (one worker chunk compressed,
 one chunk reduced, decompressed and stepped) and scales it to the full step.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
-    python bench.py --only compress|server|decompress|adam|copy  # profiling aid
+    python bench.py --only compress|server|decompress_adam|decompress|adam|copy  # profiling aid
 """
 
 from __future__ import annotations
@@ -39,6 +43,7 @@ METRIC = "compressed elements/s and HBM GB/s (% of peak), 1-bit EF compress+deco
 B_COMPRESS = 12.125            # m 4 + error state 4 in + 4 out + 1/8 bit
 B_DECOMPRESS = 4.125           # 1/8 bit in + 4 out
 B_ADAM = 16.0                  # x 4 in/out, m 4, v 4
+B_DECOMPRESS_ADAM = 16.125     # 1/8 bit, x 4, v 4 in; x 4, decompressed momentum 4 out
 
 
 def b_server(n: int) -> float:  # n/8 bits in, state 4 in + 4 out, 1/8 bit out
@@ -335,8 +340,9 @@ def measure_warmup(steps: int, warmup: int) -> dict:
 
 def measure_gpt(steps: int, warmup: int) -> dict:
     """The 1.3B GPT-style buffer with 16 workers (clamp 2.0, reset every 2000
-    steps): compress, server, decompress and the frozen-v Adam step at about
-    190 GB resident."""
+    steps): compress, server, and the decompression with the frozen-v Adam
+    step in one pass, at about 190 GB resident; the decompression and Adam
+    kernels are also timed on their own."""
     import torch
 
     from momentum_compression_amd import onebit as ob
@@ -370,13 +376,18 @@ def measure_gpt(steps: int, warmup: int) -> dict:
 
     def adam():
         grp.adam_step(x, v, wl.lr, wl.eps)
+
+    def dec_adam():
+        grp.adam_step_packed(x, v, wl.lr, wl.eps, decompress=True)
         t[0] += 1
 
-    ms = _time_calls([comp, serv, dec, adam], warmup, steps, stream)
-    out = {"workload": wl.name, "N": N, "workers": n, "step_ms": round(sum(ms), 4),
-           "worker_elements_per_s": n * N / (sum(ms) * 1e-3),
+    ms = _time_calls([comp, serv, dec, adam, dec_adam], warmup, steps, stream)
+    step_ms = ms[0] + ms[1] + ms[4]  # the step with the decompression inside the Adam pass
+    out = {"workload": wl.name, "N": N, "workers": n, "step_ms": round(step_ms, 4),
+           "worker_elements_per_s": n * N / (step_ms * 1e-3),
            "compress_clamp": _row(ms[0], B_COMPRESS * n * N, n * N),
            "server": _row(ms[1], b_server(n) * N, N),
+           "decompress_adam": _row(ms[4], B_DECOMPRESS_ADAM * N, N),
            "decompress": _row(ms[2], B_DECOMPRESS * N, N),
            "adam": _row(ms[3], B_ADAM * N, N)}
     del grp, m, x, v
@@ -451,8 +462,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bert_large_335M_x8")
-    ap.add_argument("--only", default="", choices=["", "compress", "server", "decompress", "adam",
-                                                   "copy"])
+    ap.add_argument("--only", default="", choices=["", "compress", "server", "decompress_adam",
+                                                   "decompress", "adam", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the rows measured after the headline step (LAMB, INT8, fused, "
@@ -501,34 +512,34 @@ def main() -> int:
         print(json.dumps({"only": "copy", "bytes_per_launch": 2 * 4 * src.numel()}))
         return 0
 
-    ev = {k: [] for k in ("compress", "server", "decompress", "adam")}
+    ev = {k: [] for k in ("compress", "server", "decompress_adam")}
+    # with --only decompress or adam, that standalone kernel takes the third slot
+    tail_only = args.only in ("decompress", "adam")
 
     def step(t: int, timed: bool) -> None:
         first = t == 1
         marks = []
-        if timed:
-            marks.append(torch.cuda.Event(enable_timing=True))
-            marks[-1].record(stream)
+
+        def mark():
+            if timed:
+                marks.append(torch.cuda.Event(enable_timing=True))
+                marks[-1].record(stream)
+
+        mark()
         if args.only in ("", "compress"):
             grp.compress(m, t, first=first)
-        if timed:
-            marks.append(torch.cuda.Event(enable_timing=True))
-            marks[-1].record(stream)
+        mark()
         if args.only in ("", "server"):
             grp.server(t, first=first, decompress=False)
-        if timed:
-            marks.append(torch.cuda.Event(enable_timing=True))
-            marks[-1].record(stream)
-        if args.only in ("", "decompress"):
+        mark()
+        if args.only in ("", "decompress_adam"):
+            grp.adam_step_packed(x, v, wl.lr, wl.eps, decompress=True)
+        elif args.only == "decompress":
             ob.onebit_decompress(grp.sv_bits, grp.sv_scales, grp.mbar, N, n)
-        if timed:
-            marks.append(torch.cuda.Event(enable_timing=True))
-            marks[-1].record(stream)
-        if args.only in ("", "adam"):
+        elif args.only == "adam":
             grp.adam_step(x, v, wl.lr, wl.eps)
+        mark()
         if timed:
-            marks.append(torch.cuda.Event(enable_timing=True))
-            marks[-1].record(stream)
             for k, (a, b) in zip(ev, zip(marks[:-1], marks[1:])):
                 ev[k].append((a, b))
 
@@ -546,7 +557,10 @@ def main() -> int:
     ms = {k: sum(a.elapsed_time(b) for a, b in v_) / max(1, len(v_)) for k, v_ in ev.items()}
     ms_per_step = wall * 1e3 / args.steps
     bytes_ = {"compress": B_COMPRESS * n * N, "server": b_server(n) * N,
-              "decompress": B_DECOMPRESS * N, "adam": B_ADAM * N}
+              "decompress_adam": B_DECOMPRESS_ADAM * N, "decompress": B_DECOMPRESS * N,
+              "adam": B_ADAM * N}
+    if tail_only:
+        ms[args.only] = ms.pop("decompress_adam")
     kernels = {}
     for k in ms:
         if args.only and args.only != k:
@@ -557,6 +571,18 @@ def main() -> int:
     if args.only:
         print(json.dumps({"only": args.only, "kernels": kernels}))
         return 0
+
+    # the same tail as two kernels: decompression, then Adam reading it
+    def dec():
+        ob.onebit_decompress(grp.sv_bits, grp.sv_scales, grp.mbar, N, n)
+
+    def adam():
+        grp.adam_step(x, v, wl.lr, wl.eps)
+
+    ms_u = _time_calls([dec, adam], 1, max(3, args.steps // 2), stream)
+    separate = {"decompress": _row(ms_u[0], B_DECOMPRESS * N, N),
+                "adam": _row(ms_u[1], B_ADAM * N, N),
+                "sum_ms": round(ms_u[0] + ms_u[1], 4)}
 
     comp_gbs = bytes_["compress"] / (ms["compress"] * 1e-3) / 1e9
     traffic = read_traffic(n * N)
@@ -574,7 +600,7 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "N": N, "workers": n, "chunk": wl.L,
-                   "path": "compress+server+decompress+adam_frozen_v",
+                   "path": "compress+server+(decompress+adam_frozen_v in one pass)",
                    "inputs": "momentum N(0, sigma), sigma log-uniform [1e-5, 1e-2] per 2^20 block"},
         "roofline": {"bound": "hbm", "kernel": "onebit_compress", "achieved": round(comp_gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -584,15 +610,16 @@ def main() -> int:
                      "launch_ms": round(ms["compress"], 4)},
         "kernels": kernels,
     }
+    out["rows"] = {"decompress_then_adam": separate}
     if not args.no_rows:
         del grp, m, x, v
         torch.cuda.empty_cache()
-        out["rows"] = {"lamb": measure_lamb(max(3, args.steps // 2), 1),
+        out["rows"].update({"lamb": measure_lamb(max(3, args.steps // 2), 1),
                        "int8": measure_int8(max(3, args.steps // 2), 1),
                        "fused_adam_from_gradients": measure_fused(max(3, args.steps // 2), 1),
                        "warmup": measure_warmup(max(3, args.steps // 2), 1),
                        "gpt_1.3B_x16": measure_gpt(max(3, args.steps // 2), 1),
-                       "copy_reference": measure_copy(max(3, args.steps // 2), 1)}
+                       "copy_reference": measure_copy(max(3, args.steps // 2), 1)})
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl)

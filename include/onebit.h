@@ -249,6 +249,9 @@ int lamb_layer_scale(float* buf, int64_t N, int32_t batch,
  *   mbar = m_bits bit ? m_scales[c] : -m_scales[c],  c = j / (N / m_chunks)
  *   x = x - lr * (mbar / (sqrtf(v) + eps))
  * m_bits [N/32], m_scales [m_chunks]; N a multiple of 64 * m_chunks.
+ * m_out [N] (optional, 16-byte aligned): also receives mbar, the same values
+ * onebit_decompress writes, so a caller that keeps the decompressed momentum
+ * reads the packed words once for both.
  */
 typedef struct onebit_frozen_v_args {
     int32_t mode;          /* 0: Adam, 1: LAMB                                */
@@ -272,6 +275,7 @@ typedef struct onebit_frozen_v_args {
     int32_t m_chunks;      /* mode 2: number of chunks (server ranks)         */
     float* err_ratio;      /* LAMB: [n_seg] out, or NULL: c_{t-1} / c_t, the  */
                            /* factor for the next step's error feedback      */
+    float* m_out;          /* mode 2: [N] out, or NULL: mbar as decompressed  */
 } onebit_frozen_v_args;
 
 int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes,

@@ -244,10 +244,11 @@ int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes, hipS
         if (!a->m_bits || !a->m_scales) return ONEBIT_E_NULL;
         if (a->m_chunks < 1 || a->m_chunks > kMaxWorkers || (a->N % (64 * (int64_t)a->m_chunks)))
             return ONEBIT_E_SIZE;
-        if (!aligned(a->m_bits, 4) || !aligned(a->m_scales, 4)) return ONEBIT_E_ALIGN;
+        if (!aligned(a->m_bits, 4) || !aligned(a->m_scales, 4) || !aligned(a->m_out, 16))
+            return ONEBIT_E_ALIGN;
         if (a->N == 0) return ONEBIT_OK;
-        return hip_status(launch_adam_packed(a->x, a->m_bits, a->m_scales, a->v, a->N, a->m_chunks,
-                                             a->lr, a->eps, stream));
+        return hip_status(launch_adam_packed(a->x, a->m_bits, a->m_scales, a->v, a->m_out, a->N,
+                                             a->m_chunks, a->lr, a->eps, stream));
     }
     if (a->mode != 1) return ONEBIT_E_ARG;
     if (!a->m_prev || !a->v_fresh || !a->seg_off || !a->c_avg || !a->r_prev || !a->c_prev)

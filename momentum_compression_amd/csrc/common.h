@@ -167,8 +167,8 @@ hipError_t launch_adam(float* x, const float* m, const float* v, int64_t N, floa
                        hipStream_t st);
 
 hipError_t launch_adam_packed(float* x, const uint32_t* mbits, const float* mscales,
-                              const float* v, int64_t N, int32_t chunks, float lr, float eps,
-                              hipStream_t st);
+                              const float* v, float* m_out, int64_t N, int32_t chunks, float lr,
+                              float eps, hipStream_t st);
 
 hipError_t launch_lamb(const onebit_frozen_v_args& a, uint32_t* keys, uint32_t* wg_max,
                        hipStream_t st);

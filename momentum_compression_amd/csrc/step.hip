@@ -58,9 +58,12 @@ hipError_t launch_adam(float* x, const float* m, const float* v, int64_t N, floa
 
 // Adam with the global momentum read packed: sign words and chunk scales of
 // the server (the decompression every worker performs, fused into the step).
+// OUT: the decompressed momentum is stored as well (nontemporal).
+template <bool OUT>
 __global__ __launch_bounds__(kThreads) void adam_packed_kernel(
     float* __restrict__ x, const uint32_t* __restrict__ mbits, const float* __restrict__ mscales,
-    const float* __restrict__ v, int64_t N, int64_t L, float lr, float eps) {
+    const float* __restrict__ v, float* __restrict__ m_out, int64_t N, int64_t L, float lr,
+    float eps) {
     const int64_t j0 = (int64_t)blockIdx.x * kMaxIters * kTile + 4 * (int64_t)threadIdx.x;
     f4 xv[kMaxIters], vv[kMaxIters];
     uint32_t w[kMaxIters];
@@ -81,25 +84,34 @@ __global__ __launch_bounds__(kThreads) void adam_packed_kernel(
         const uint32_t word = w[u] >> (j & 31);
         const float xs[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
         const float vs[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
-        float o[4];
+        float o[4], mb[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const float m = ((word >> k) & 1u) ? S : -S;
+            mb[k] = ((word >> k) & 1u) ? S : -S;
             const float den = sqrtf(vs[k]) + eps;
-            const float upd = m / den;
+            const float upd = mb[k] / den;
             o[k] = xs[k] - lr * upd;
         }
         const f4 ov = {o[0], o[1], o[2], o[3]};
         __builtin_nontemporal_store(ov, reinterpret_cast<f4*>(x + j));
+        if (OUT) {
+            const f4 mv = {mb[0], mb[1], mb[2], mb[3]};
+            __builtin_nontemporal_store(mv, reinterpret_cast<f4*>(m_out + j));
+        }
     }
 }
 
 hipError_t launch_adam_packed(float* x, const uint32_t* mbits, const float* mscales,
-                              const float* v, int64_t N, int32_t chunks, float lr, float eps,
-                              hipStream_t st) {
+                              const float* v, float* m_out, int64_t N, int32_t chunks, float lr,
+                              float eps, hipStream_t st) {
     const int64_t per_wg = (int64_t)kMaxIters * kTile;
-    hipLaunchKernelGGL(adam_packed_kernel, dim3((unsigned)((N + per_wg - 1) / per_wg)),
-                       dim3(kThreads), 0, st, x, mbits, mscales, v, N, N / chunks, lr, eps);
+    const dim3 grid((unsigned)((N + per_wg - 1) / per_wg));
+    if (m_out)
+        hipLaunchKernelGGL(adam_packed_kernel<true>, grid, dim3(kThreads), 0, st, x, mbits,
+                           mscales, v, m_out, N, N / chunks, lr, eps);
+    else
+        hipLaunchKernelGGL(adam_packed_kernel<false>, grid, dim3(kThreads), 0, st, x, mbits,
+                           mscales, v, m_out, N, N / chunks, lr, eps);
     return hipGetLastError();
 }
 

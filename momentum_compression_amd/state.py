@@ -105,11 +105,13 @@ class OneBitGroup:
         ob.frozen_v_step(mode=0, N=self.N, x=x, m=self.mbar, v=v, lr=lr, eps=eps, stream=stream)
 
     def adam_step_packed(self, x: torch.Tensor, v: torch.Tensor, lr: float, eps: float,
-                         stream=None) -> None:
+                         decompress: bool = False, stream=None) -> None:
         """Adam step reading the global momentum packed (server words and
-        scales), without the decompressed buffer."""
+        scales); with ``decompress`` the same pass also writes the
+        decompressed momentum to ``mbar``."""
         ob.frozen_v_step(mode=2, N=self.N, x=x, m=None, v=v, lr=lr, eps=eps, m_bits=self.sv_bits,
-                         m_scales=self.sv_scales, m_chunks=self.n, stream=stream)
+                         m_scales=self.sv_scales, m_chunks=self.n,
+                         m_out=self.mbar if decompress else None, stream=stream)
 
 
 @dataclass

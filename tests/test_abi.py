@@ -117,6 +117,9 @@ def test_frozen_v_validation(lib):
     assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_NULL
     a = ob.FrozenVArgs(mode=2, N=1024 + 64, x=P, m=None, v=P, m_bits=P, m_scales=P, m_chunks=4)
     assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_SIZE
+    a = ob.FrozenVArgs(mode=2, N=1024, x=P, m=None, v=P, m_bits=P, m_scales=P, m_chunks=4,
+                       m_out=P + 4)
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_ALIGN
     a = ob.FrozenVArgs(mode=0, N=1022, x=P, m=P, v=P)
     assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_SIZE
     assert lib.frozen_v_step(None, None, 0, None) == ob.ONEBIT_E_NULL
@@ -130,7 +133,8 @@ def test_struct_layout_matches_header():
     assert ob.FrozenVArgs.m_bits.offset == 128
     assert ob.FrozenVArgs.m_chunks.offset == 144
     assert ob.FrozenVArgs.err_ratio.offset == 152
-    assert ctypes.sizeof(ob.FrozenVArgs) == 160
+    assert ob.FrozenVArgs.m_out.offset == 160
+    assert ctypes.sizeof(ob.FrozenVArgs) == 168
 
 
 def test_extended_entries_validation(lib):

@@ -63,10 +63,18 @@ def test_packed_adam_equals_decompress_then_adam():
     x = torch.randn(N, generator=g0, device=dev)
     v = torch.rand(N, generator=g0, device=dev) * 1e-6
     x2 = x.clone()
+    x3 = x.clone()
     grp.adam_step(x, v, 1e-3, 1e-6)
     grp.adam_step_packed(x2, v, 1e-3, 1e-6)
+    mbar = grp.mbar.clone()
+    grp.mbar.fill_(float("nan"))
+    grp.adam_step_packed(x3, v, 1e-3, 1e-6, decompress=True)   # also writes mbar
     torch.cuda.synchronize()
     assert np.array_equal(host(x).view(np.uint32), host(x2).view(np.uint32))
+    assert np.array_equal(host(x).view(np.uint32), host(x3).view(np.uint32))
+    assert np.array_equal(host(grp.mbar).view(np.uint32), host(mbar).view(np.uint32))
+    sv_bits, S = host(grp.sv_bits), host(grp.sv_scales)
+    same_f32(host(grp.mbar), O.decompress(sv_bits, S), "decompressed by the step")
 
 
 def test_lamb_from_gradients():
