@@ -252,9 +252,17 @@ int lamb_layer_scale(float* buf, int64_t N, int32_t batch,
  * m_out [N] (optional, 16-byte aligned): also receives mbar, the same values
  * onebit_decompress writes, so a caller that keeps the decompressed momentum
  * reads the packed words once for both.
+ *
+ * mode 3, LAMB (as mode 1) with the global momentum given packed: m is
+ * ignored and
+ *   m_t = (m_bits bit ? m_scales[c] : -m_scales[c]) / m_seg_k[l]
+ * for element j of chunk c = j / (N / m_chunks) and layer l, the values
+ * onebit_decompress writes with the layer table.  m_out [N] receives m_t
+ * (the caller's next m_prev); it is optional unless use_c_t is set, whose
+ * second pass reads it.  m_out must not overlap m_prev.
  */
 typedef struct onebit_frozen_v_args {
-    int32_t mode;          /* 0: Adam, 1: LAMB                                */
+    int32_t mode;          /* 0: Adam, 1: LAMB, 2: Adam packed, 3: LAMB packed */
     int32_t use_c_t;       /* LAMB: 0 = update with c_{t-1}, 1 = with c_t     */
     int64_t N;
     float lr, eps, beta1, beta2;
@@ -275,7 +283,9 @@ typedef struct onebit_frozen_v_args {
     int32_t m_chunks;      /* mode 2: number of chunks (server ranks)         */
     float* err_ratio;      /* LAMB: [n_seg] out, or NULL: c_{t-1} / c_t, the  */
                            /* factor for the next step's error feedback      */
-    float* m_out;          /* mode 2: [N] out, or NULL: mbar as decompressed  */
+    float* m_out;          /* modes 2, 3: [N] out, or NULL: mbar as           */
+                           /* decompressed                                    */
+    const float* m_seg_k;  /* mode 3: [n_seg] layer coefficients k_l          */
 } onebit_frozen_v_args;
 
 int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes,

@@ -234,7 +234,8 @@ int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes, hipS
     if (a->N < 0 || (a->N % 4)) return ONEBIT_E_SIZE;
     if (!groups_ok(ceil_div(a->N, (int64_t)kMaxIters * kTile)) || !groups_ok(lamb_workgroups(a->N)))
         return ONEBIT_E_SIZE;
-    if (!a->x || (!a->m && a->mode != 2) || !a->v) return ONEBIT_E_NULL;
+    const bool packed_m = a->mode == 2 || a->mode == 3;  // momentum given as sign words
+    if (!a->x || (!a->m && !packed_m) || !a->v) return ONEBIT_E_NULL;
     if (!aligned(a->x, 16) || !aligned(a->m, 16) || !aligned(a->v, 16)) return ONEBIT_E_ALIGN;
     if (a->mode == 0) {
         if (a->N == 0) return ONEBIT_OK;
@@ -250,9 +251,23 @@ int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes, hipS
         return hip_status(launch_adam_packed(a->x, a->m_bits, a->m_scales, a->v, a->m_out, a->N,
                                              a->m_chunks, a->lr, a->eps, stream));
     }
-    if (a->mode != 1) return ONEBIT_E_ARG;
+    if (a->mode != 1 && a->mode != 3) return ONEBIT_E_ARG;
     if (!a->m_prev || !a->v_fresh || !a->seg_off || !a->c_avg || !a->r_prev || !a->c_prev)
         return ONEBIT_E_NULL;
+    if (a->mode == 3) {
+        if (!a->m_bits || !a->m_scales || !a->m_seg_k || (a->use_c_t && !a->m_out))
+            return ONEBIT_E_NULL;
+        if (a->m_chunks < 1 || a->m_chunks > kMaxWorkers || (a->N % (64 * (int64_t)a->m_chunks)))
+            return ONEBIT_E_SIZE;
+        if (!aligned(a->m_bits, 4) || !aligned(a->m_scales, 4) || !aligned(a->m_seg_k, 4) ||
+            !aligned(a->m_out, 16))
+            return ONEBIT_E_ALIGN;
+        if (a->m_out) {  // the decompressed output must not overlap m_prev, which is read
+            const uintptr_t o = (uintptr_t)a->m_out, p = (uintptr_t)a->m_prev;
+            const uintptr_t bytes = (uintptr_t)a->N * sizeof(float);
+            if (o < p + bytes && p < o + bytes) return ONEBIT_E_ARG;
+        }
+    }
     if (a->n_seg < 1) return ONEBIT_E_ARG;
     if (!groups_ok(a->n_seg)) return ONEBIT_E_SIZE;
     if (!aligned(a->m_prev, 16) || !aligned(a->v_fresh, 16) || !aligned(a->seg_off, 8) ||

@@ -130,13 +130,25 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
-template <bool UPDATE_X>
+// The global momentum m_t arrives decompressed (m), or PACKED: the server's
+// sign words and chunk scales with the layer coefficients, decoded here as
+// (bit ? S_c : -S_c) / k_l exactly as the decompression computes it, and
+// stored to m_out when that is given.
+struct PackedMomentum {
+    const uint32_t* bits;  // [N/32]
+    const float* scales;   // [chunks]
+    const float* seg_k;    // [n_seg]
+    float* out;            // [N] or null
+    int64_t L;             // chunk length
+};
+
+template <bool UPDATE_X, bool PACKED>
 __global__ __launch_bounds__(kThreads) void lamb_kernel(
     float* __restrict__ x, const float* __restrict__ m, const float* __restrict__ mp,
     float* __restrict__ vf, const float* __restrict__ v, const int64_t* __restrict__ seg_off,
     int32_t n_seg, const float* __restrict__ c_prev, uint32_t* __restrict__ keys,
     uint32_t* __restrict__ wg_max, int64_t N, float c_lr, float c_eps, float c_beta1,
-    float c_beta2) {
+    float c_beta2, PackedMomentum pk) {
     __shared__ uint32_t red[kThreads / 64];
     // workgroups across layer boundaries: maxima of layers seg0 .. seg0 + 255,
     // merged in LDS so that each layer takes one global atomic per workgroup
@@ -165,22 +177,36 @@ __global__ __launch_bounds__(kThreads) void lamb_kernel(
         else atomicMax(&keys[sg], km);
     };
     f4 mv[kLambTiles], pv[kLambTiles], fv[kLambTiles], vv[kLambTiles], xv[kLambTiles];
+    uint32_t mw[kLambTiles];
 #pragma unroll
     for (int u = 0; u < kLambTiles; ++u) {
         const int64_t j = j0 + (int64_t)u * kTile;
         if (j < wend) {
-            mv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(m + j));
+            if (PACKED) mw[u] = pk.bits[j >> 5];
+            else mv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(m + j));
             pv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(mp + j));
             fv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(vf + j));
             vv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(v + j));
             if (UPDATE_X) xv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(x + j));
         }
     }
+    // PACKED: value of a set bit for the current (chunk, layer)
+    int64_t q_c = -1;
+    int q_seg = -1;
+    float q = 0.0f;
 #pragma unroll
     for (int u = 0; u < kLambTiles; ++u) {
         const int64_t j = j0 + (int64_t)u * kTile;
         if (j >= wend) break;
-        const float ms[4] = {mv[u].x, mv[u].y, mv[u].z, mv[u].w};
+        float ms[4];
+        if (!PACKED) {
+            ms[0] = mv[u].x;
+            ms[1] = mv[u].y;
+            ms[2] = mv[u].z;
+            ms[3] = mv[u].w;
+        }
+        const int64_t c = PACKED ? j / pk.L : 0;  // L is a multiple of 64: one chunk per quad
+        const uint32_t word = PACKED ? mw[u] >> (j & 31) : 0u;
         const float ps[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
         const float fs[4] = {fv[u].x, fv[u].y, fv[u].z, fv[u].w};
         const float vs[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
@@ -203,6 +229,14 @@ __global__ __launch_bounds__(kThreads) void lamb_kernel(
                     step = c_lr * c_prev[seg];
                 }
             }
+            if (PACKED) {
+                if (c != q_c || seg != q_seg) {
+                    q_c = c;
+                    q_seg = seg;
+                    q = pk.scales[c] / pk.seg_k[seg];
+                }
+                ms[k] = ((word >> k) & 1u) ? q : -q;  // -S / k is exactly -(S / k)
+            }
             const float g = (ms[k] - c_beta1 * ps[k]) / c_omb1;
             const float vn = c_beta2 * fs[k] + c_omb2 * (g * g);
             nf[k] = vn;
@@ -219,6 +253,10 @@ __global__ __launch_bounds__(kThreads) void lamb_kernel(
         }
         const f4 nv = {nf[0], nf[1], nf[2], nf[3]};
         __builtin_nontemporal_store(nv, reinterpret_cast<f4*>(vf + j));
+        if (PACKED && pk.out) {
+            const f4 mo = {ms[0], ms[1], ms[2], ms[3]};
+            __builtin_nontemporal_store(mo, reinterpret_cast<f4*>(pk.out + j));
+        }
         if (UPDATE_X) {
             const f4 xo = {xs[0], xs[1], xs[2], xs[3]};
             __builtin_nontemporal_store(xo, reinterpret_cast<f4*>(x + j));
@@ -342,20 +380,29 @@ hipError_t launch_lamb(const onebit_frozen_v_args& a, uint32_t* keys, uint32_t* 
     const dim3 grid((unsigned)n_wg);
     hipLaunchKernelGGL(fill_u32_kernel, dim3((a.n_seg + 255) / 256), dim3(256), 0, st, keys,
                        a.n_seg, 0u);
-    if (a.use_c_t)
-        hipLaunchKernelGGL(lamb_kernel<false>, grid, dim3(kThreads), 0, st, a.x, a.m, a.m_prev,
-                           a.v_fresh, a.v, a.seg_off, a.n_seg, a.c_prev, keys, wg_max, a.N, a.lr,
-                           a.eps, a.beta1, a.beta2);
-    else
-        hipLaunchKernelGGL(lamb_kernel<true>, grid, dim3(kThreads), 0, st, a.x, a.m, a.m_prev,
-                           a.v_fresh, a.v, a.seg_off, a.n_seg, a.c_prev, keys, wg_max, a.N, a.lr,
-                           a.eps, a.beta1, a.beta2);
+    const bool packed = a.mode == 3;
+    PackedMomentum pk{a.m_bits, a.m_scales, a.m_seg_k, a.m_out,
+                      packed ? a.N / a.m_chunks : (int64_t)1};
+    auto launch = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, st, a.x, a.m, a.m_prev, a.v_fresh, a.v,
+                           a.seg_off, a.n_seg, a.c_prev, keys, wg_max, a.N, a.lr, a.eps, a.beta1,
+                           a.beta2, pk);
+    };
+    if (a.use_c_t) {
+        if (packed) launch(lamb_kernel<false, true>);
+        else launch(lamb_kernel<false, false>);
+    } else {
+        if (packed) launch(lamb_kernel<true, true>);
+        else launch(lamb_kernel<true, false>);
+    }
     hipLaunchKernelGGL(lamb_finalize_kernel, dim3(a.n_seg), dim3(kThreads), 0, st, keys, wg_max,
                        a.seg_off, n_wg, a.n_seg, a.c_avg, a.r_prev, a.c_prev, a.ratio_max,
                        a.err_ratio, a.r_threshold, a.r_min, a.r_max);
+    // second pass with c_t; a packed momentum was decompressed into m_out
     if (a.use_c_t)
-        hipLaunchKernelGGL(lamb_apply_kernel, grid, dim3(kThreads), 0, st, a.x, a.m, a.v,
-                           a.seg_off, a.n_seg, a.c_prev, a.N, (int32_t)kLambTiles, a.lr, a.eps);
+        hipLaunchKernelGGL(lamb_apply_kernel, grid, dim3(kThreads), 0, st, a.x,
+                           packed ? a.m_out : a.m, a.v, a.seg_off, a.n_seg, a.c_prev, a.N,
+                           (int32_t)kLambTiles, a.lr, a.eps);
     return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@ class FrozenVArgs(ctypes.Structure):
         ("ratio_max", _c_p),
         ("m_bits", _c_p), ("m_scales", _c_p), ("m_chunks", _c_i32),
         ("err_ratio", _c_p),
-        ("m_out", _c_p),
+        ("m_out", _c_p), ("m_seg_k", _c_p),
     ]
 
 
@@ -218,15 +218,15 @@ def frozen_v_step(*, mode: int, N: int, x, m, v, lr: float, eps: float, beta1: f
                   beta2: float = 0.999, m_prev=None, v_fresh=None, seg_off=None, n_seg: int = 0,
                   c_avg=None, r_prev=None, c_prev=None, ratio_max=None, r_threshold: float = 0.1,
                   r_min: float = 0.5, r_max: float = 4.0, use_c_t: bool = False, m_bits=None,
-                  m_scales=None, m_chunks: int = 0, err_ratio=None, m_out=None, ws=None,
-                  stream=None) -> None:
+                  m_scales=None, m_chunks: int = 0, err_ratio=None, m_out=None, m_seg_k=None,
+                  ws=None, stream=None) -> None:
     a = FrozenVArgs(mode=mode, use_c_t=int(bool(use_c_t)), N=N, lr=lr, eps=eps, beta1=beta1,
                     beta2=beta2, r_threshold=r_threshold, r_min=r_min, r_max=r_max, n_seg=n_seg,
                     x=_ptr(x), m=_ptr(m), v=_ptr(v), m_prev=_ptr(m_prev), v_fresh=_ptr(v_fresh),
                     seg_off=_ptr(seg_off), c_avg=_ptr(c_avg), r_prev=_ptr(r_prev),
                     c_prev=_ptr(c_prev), ratio_max=_ptr(ratio_max), m_bits=_ptr(m_bits),
                     m_scales=_ptr(m_scales), m_chunks=m_chunks, err_ratio=_ptr(err_ratio),
-                    m_out=_ptr(m_out))
+                    m_out=_ptr(m_out), m_seg_k=_ptr(m_seg_k))
     _check("frozen_v_step", load().frozen_v_step(
         ctypes.byref(a), _ptr(ws), _nbytes(ws) if ws is not None else 0, _stream(stream)))
 

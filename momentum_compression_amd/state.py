@@ -129,6 +129,7 @@ class LambState:
     ratio_max: torch.Tensor  # [S]
     err_ratio: torch.Tensor  # [S] c_{t-1} / c_t, for the next step's error feedback
     ws: torch.Tensor
+    m_next: Optional[torch.Tensor] = None  # [N] spare buffer of step_packed
 
     @classmethod
     def create(cls, x, v_frozen, m_prev, seg_off, c_avg) -> "LambState":
@@ -150,6 +151,27 @@ class LambState:
                          r_prev=self.r, c_prev=self.c, ratio_max=self.ratio_max,
                          r_threshold=thr, r_min=r_min, r_max=r_max, use_c_t=use_c_t,
                          err_ratio=self.err_ratio, ws=self.ws, stream=stream)
+
+    def step_packed(self, bits: torch.Tensor, scales: torch.Tensor, seg_k: torch.Tensor,
+                    chunks: int, lr: float, eps: float, beta1: float, beta2: float, thr: float,
+                    r_min: float, r_max: float, use_c_t: bool = False,
+                    stream=None) -> torch.Tensor:
+        """LAMB step reading the global momentum as the server's sign words and
+        chunk scales, divided by the layer coefficients in the same pass.  The
+        decompressed momentum it writes becomes ``m_prev`` for the next step
+        and is returned."""
+        if self.m_next is None:
+            self.m_next = torch.empty_like(self.m_prev)
+        S = self.seg_off.numel() - 1
+        ob.frozen_v_step(mode=3, N=self.x.numel(), x=self.x, m=None, v=self.v_frozen, lr=lr,
+                         eps=eps, beta1=beta1, beta2=beta2, m_prev=self.m_prev,
+                         v_fresh=self.v_fresh, seg_off=self.seg_off, n_seg=S, c_avg=self.c_avg,
+                         r_prev=self.r, c_prev=self.c, ratio_max=self.ratio_max,
+                         r_threshold=thr, r_min=r_min, r_max=r_max, use_c_t=use_c_t,
+                         err_ratio=self.err_ratio, m_bits=bits, m_scales=scales, m_chunks=chunks,
+                         m_seg_k=seg_k, m_out=self.m_next, ws=self.ws, stream=stream)
+        self.m_prev, self.m_next = self.m_next, self.m_prev
+        return self.m_prev
 
 
 @dataclass

@@ -106,7 +106,7 @@ def test_compress_grad_validation(lib):
 def test_frozen_v_validation(lib):
     a = ob.FrozenVArgs(mode=0, N=1024, x=P, m=P, v=None, lr=1e-3, eps=1e-6)
     assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_NULL
-    a = ob.FrozenVArgs(mode=3, N=1024, x=P, m=P, v=P)
+    a = ob.FrozenVArgs(mode=4, N=1024, x=P, m=P, v=P)
     assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_ARG
     a = ob.FrozenVArgs(mode=1, N=1024, x=P, m=P, v=P, m_prev=P, v_fresh=P, seg_off=P, c_avg=P,
                        r_prev=P, c_prev=P, n_seg=4)
@@ -120,6 +120,18 @@ def test_frozen_v_validation(lib):
     a = ob.FrozenVArgs(mode=2, N=1024, x=P, m=None, v=P, m_bits=P, m_scales=P, m_chunks=4,
                        m_out=P + 4)
     assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_ALIGN
+    lamb = dict(mode=3, N=1024, x=P, m=None, v=P, m_prev=P, v_fresh=P, seg_off=P, c_avg=P,
+                r_prev=P, c_prev=P, n_seg=4, m_bits=P, m_scales=P, m_chunks=4, m_seg_k=P)
+    a = ob.FrozenVArgs(**{**lamb, "m_seg_k": None})
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_NULL
+    a = ob.FrozenVArgs(**{**lamb, "use_c_t": 1})          # the second pass reads m_out
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_NULL
+    a = ob.FrozenVArgs(**{**lamb, "m_chunks": 3})
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_SIZE
+    a = ob.FrozenVArgs(**{**lamb, "m_out": P + 64})       # overlaps m_prev
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_ARG
+    a = ob.FrozenVArgs(**{**lamb, "m_out": P + 4 * 1024})  # adjacent: accepted up to the workspace
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_WORKSPACE
     a = ob.FrozenVArgs(mode=0, N=1022, x=P, m=P, v=P)
     assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_SIZE
     assert lib.frozen_v_step(None, None, 0, None) == ob.ONEBIT_E_NULL
@@ -134,7 +146,8 @@ def test_struct_layout_matches_header():
     assert ob.FrozenVArgs.m_chunks.offset == 144
     assert ob.FrozenVArgs.err_ratio.offset == 152
     assert ob.FrozenVArgs.m_out.offset == 160
-    assert ctypes.sizeof(ob.FrozenVArgs) == 168
+    assert ob.FrozenVArgs.m_seg_k.offset == 168
+    assert ctypes.sizeof(ob.FrozenVArgs) == 176
 
 
 def test_extended_entries_validation(lib):

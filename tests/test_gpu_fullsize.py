@@ -104,11 +104,13 @@ def test_gpt_1_3B_x16_clamp_and_reset():
 
 def test_bert_large_lamb_302t_x16():
     """Two 1-bit LAMB steps on the 302-tensor buffer; the LAMB step is
-    checked on the whole buffer (every layer's ratio, r_t, c_t, x, v)."""
+    checked on the whole buffer (every layer's ratio, r_t, c_t, x, v).  A
+    second state stepping from the server's sign words (decompression inside
+    the LAMB pass) must match it bit for bit on the whole buffer."""
     dev = device()
     wl = C.get("bert_large_lamb_302t_x16")
     N, n, L = wl.N, wl.n, wl.L
-    _need(dev, int(n * N * 4 * 2.2 + N * 4 * 8))
+    _need(dev, int(n * N * 4 * 2.2 + N * 4 * 12))
     print(f"[fullsize] {wl.name} N={N} n={n} segments={len(wl.segments)}", flush=True)
     off = np.array(C.segment_offsets(wl.segments), dtype=np.int64)
     k, c_avg = S.lamb_tables(wl)
@@ -118,6 +120,8 @@ def test_bert_large_lamb_302t_x16():
     grp = OneBitGroup(N, n, dev, seg_off=off_d, seg_k=k_d)
     st = LambState.create(S.params(wl, dev), S.frozen_variance(wl, dev),
                           S.lamb_prev_momentum(wl, dev, sig), off_d, torch.from_numpy(c_avg).to(dev))
+    st2 = LambState.create(st.x.clone(), st.v_frozen, st.m_prev.clone(), off_d,
+                           torch.from_numpy(c_avg).to(dev))
     m = torch.empty((n, N), dtype=torch.float32, device=dev)
     pairs = [(0, 0), (9, 15)]
     e_w = {p: np.zeros(L, dtype=F32) for p in pairs}
@@ -132,6 +136,8 @@ def test_bert_large_lamb_302t_x16():
         grp.compress(m, t, first=first)
         grp.server(t, first=first)
         st.step(grp.mbar, wl.lr, wl.eps, wl.beta1, wl.beta2, wl.r_threshold, wl.r_min, wl.r_max)
+        st2.step_packed(grp.sv_bits, grp.sv_scales, k_d, n, wl.lr, wl.eps, wl.beta1, wl.beta2,
+                        wl.r_threshold, wl.r_min, wl.r_max)
         torch.cuda.synchronize()
         tag = f"lamb t={t}"
         scales = host(grp.scales)
@@ -158,8 +164,11 @@ def test_bert_large_lamb_302t_x16():
         same_f32(host(st.v_fresh), out["v"], f"{tag} fresh variance")
         same_f32(host(st.x), out["x"], f"{tag} parameters")
         st.m_prev.copy_(grp.mbar)
+        for name in ("x", "v_fresh", "ratio_max", "r", "c", "err_ratio", "m_prev"):
+            assert torch.equal(getattr(st, name).view(torch.int32),
+                               getattr(st2, name).view(torch.int32)), f"{tag} packed {name}"
         del out, x_h, vf_h, mp_h
-    del grp, st, m, sig
+    del grp, st, st2, m, sig
     _free()
 
 

@@ -81,6 +81,43 @@ def test_lamb_scaled_bert_free_running(use_c_t):
         st.m_prev.copy_(grp.mbar)
 
 
+@pytest.mark.parametrize("use_c_t", [False, True])
+def test_lamb_packed_equals_decompress_then_step(use_c_t):
+    """The LAMB step fed with the server's sign words (decompression with / k_l
+    inside the step) gives bit-identical parameters, fresh variance, maxima,
+    r, c, error ratios and decompressed momentum to decompression followed by
+    the step, over free-running steps on the BERT layer layout."""
+    dev = device()
+    wl = C.scaled_lamb(n=16, target_elems=1 << 20)
+    N, n = wl.N, wl.n
+    print(f"[lamb packed] N={N} n={n} segments={len(wl.segments)} use_c_t={use_c_t}", flush=True)
+    off, k, c_avg, sig = _setup(wl, dev)
+    off_d = torch.from_numpy(off).to(dev)
+    k_d = torch.from_numpy(k).to(dev)
+    grp = OneBitGroup(N, n, dev, seg_off=off_d, seg_k=k_d)
+    x = S.params(wl, dev)
+    v = S.frozen_variance(wl, dev)
+    mprev = S.lamb_prev_momentum(wl, dev, sig)
+    c0 = torch.from_numpy(c_avg).to(dev)
+    a = LambState.create(x.clone(), v, mprev.clone(), off_d, c0)
+    b = LambState.create(x.clone(), v, mprev.clone(), off_d, c0)
+    hp = dict(lr=wl.lr, eps=wl.eps, beta1=wl.beta1, beta2=wl.beta2, thr=wl.r_threshold,
+              r_min=wl.r_min, r_max=wl.r_max, use_c_t=use_c_t)
+    for t in range(1, 4):
+        m = S.momentum(wl, t, dev, sigma_elem=sig)
+        grp.compress(m, t, first=t == 1)
+        grp.server(t, first=t == 1)                      # decompresses into grp.mbar
+        a.step(grp.mbar, **hp)
+        a.m_prev.copy_(grp.mbar)
+        mb = b.step_packed(grp.sv_bits, grp.sv_scales, k_d, n, **hp)
+        torch.cuda.synchronize()
+        tag = f"t={t}"
+        for name in ("x", "v_fresh", "ratio_max", "r", "c", "err_ratio", "m_prev"):
+            assert np.array_equal(host(getattr(a, name)).view(np.uint32),
+                                  host(getattr(b, name)).view(np.uint32)), f"{tag} {name}"
+        assert mb is b.m_prev
+
+
 def test_layer_scale_entry():
     dev = device()
     wl = C.scaled_lamb(n=4, target_elems=1 << 20, seed=8)
