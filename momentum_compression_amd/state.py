@@ -19,7 +19,7 @@ Buffers (n workers, N elements per worker row, chunk L = N / n):
 from __future__ import annotations
 
 from dataclasses import dataclass
-from typing import Optional
+from typing import Dict, Mapping, Optional
 
 import torch
 
@@ -91,6 +91,38 @@ class OneBitGroup:
                                    seg_err_ratio=self.seg_err_ratio, n_seg=self.n_seg,
                                    flags=self.flags, ws=self.ws, stream=stream)
 
+    # buffers that carry over from one step to the next (the worker sign words
+    # and the workspace are rewritten by every step)
+    _STATE = ("ef", "scales", "sv_ef", "sv_scales", "sv_bits", "mbar")
+
+    def config(self) -> dict:
+        return {"N": self.N, "n": self.n, "clip": self.clip,
+                "reset_interval": self.reset_interval, "unit_scale": self.unit_scale}
+
+    def state_dict(self) -> Dict[str, Optional[torch.Tensor]]:
+        """The group's carried state and its layer tables (None where unset),
+        for ``checkpoint.save``."""
+        d = {k: getattr(self, k) for k in self._STATE}
+        d.update(seg_off=self.seg_off, seg_k=self.seg_k, seg_err_ratio=self.seg_err_ratio)
+        return d
+
+    @classmethod
+    def from_state(cls, tensors: Mapping[str, torch.Tensor], config: dict,
+                   device) -> "OneBitGroup":
+        """A group rebuilt from ``state_dict`` tensors and ``config()``."""
+        grp = cls(int(config["N"]), int(config["n"]), device, clip=float(config["clip"]),
+                  reset_interval=int(config["reset_interval"]),
+                  seg_off=tensors.get("seg_off"), seg_k=tensors.get("seg_k"),
+                  unit_scale=bool(config["unit_scale"]),
+                  seg_err_ratio=tensors.get("seg_err_ratio"))
+        for k in cls._STATE:
+            dst, src = getattr(grp, k), tensors[k]
+            if dst.shape != src.shape or dst.dtype != src.dtype:
+                raise ValueError(f"{k}: expected {tuple(dst.shape)} {dst.dtype}, "
+                                 f"got {tuple(src.shape)} {src.dtype}")
+            dst.copy_(src)
+        return grp
+
     def worker_error(self) -> torch.Tensor:
         e = torch.empty_like(self.ef)
         ob.onebit_error_materialize(self.ef, self.scales, e, self.N, self.n, self.n)
@@ -141,6 +173,19 @@ class LambState:
                    err_ratio=torch.ones(S, dtype=torch.float32, device=dev),
                    ws=torch.empty(max(256, ob.frozen_v_workspace_bytes(x.numel(), S)),
                                   dtype=torch.uint8, device=dev))
+
+    _STATE = ("x", "v_frozen", "v_fresh", "m_prev", "seg_off", "c_avg", "r", "c", "err_ratio")
+
+    def state_dict(self) -> Dict[str, torch.Tensor]:
+        return {k: getattr(self, k) for k in self._STATE}
+
+    @classmethod
+    def from_state(cls, tensors: Mapping[str, torch.Tensor]) -> "LambState":
+        st = cls.create(tensors["x"], tensors["v_frozen"], tensors["m_prev"], tensors["seg_off"],
+                        tensors["c_avg"])
+        for k in ("v_fresh", "r", "c", "err_ratio"):
+            getattr(st, k).copy_(tensors[k])
+        return st
 
     def step(self, mbar: torch.Tensor, lr: float, eps: float, beta1: float, beta2: float,
              thr: float, r_min: float, r_max: float, use_c_t: bool = False, stream=None) -> None:

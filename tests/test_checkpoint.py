@@ -1,0 +1,101 @@
+"""Checkpoint files on the host: round trip of every supported dtype, the
+manifest, and refusal of damaged or escaping entries; the group and LAMB
+state round trip through ``from_state`` (host tensors, no kernel runs)."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from momentum_compression_amd import checkpoint as ck
+from momentum_compression_amd.state import LambState, OneBitGroup
+
+
+def _tensors():
+    g = torch.Generator().manual_seed(3)
+    return {
+        "f32": torch.randn(7, 33, generator=g),
+        "f64": torch.randn(5, generator=g, dtype=torch.float64),
+        "i32": torch.randint(-2**31, 2**31 - 1, (64,), generator=g, dtype=torch.int32),
+        "i64": torch.tensor([0, -1, 2**62, -2**62], dtype=torch.int64),
+        "u8": torch.randint(0, 256, (3, 4), generator=g, dtype=torch.uint8),
+        "i8": torch.randint(-128, 128, (9,), generator=g, dtype=torch.int8),
+        "scalar": torch.tensor(1.5),
+        "empty": torch.zeros(0, 4),
+    }
+
+
+def test_round_trip_every_dtype(tmp_path):
+    t = _tensors()
+    ck.save(str(tmp_path), {**t, "absent": None}, meta={"t": 17, "seed": 2**40 + 3})
+    back, meta = ck.load(str(tmp_path), "cpu")
+    assert meta == {"t": 17, "seed": 2**40 + 3}
+    assert set(back) == set(t)
+    for k, v in t.items():
+        assert back[k].dtype == v.dtype and back[k].shape == v.shape
+        assert torch.equal(back[k], v), k
+    man = json.load(open(tmp_path / ck.MANIFEST))
+    assert man["format"] == ck.FORMAT
+    assert man["tensors"]["f32"] == {"file": "f32.bin", "dtype": "<f4", "shape": [7, 33],
+                                     "bytes": 7 * 33 * 4}
+    # raw little-endian: the file is the array's bytes in that order
+    raw = np.fromfile(tmp_path / "i64.bin", dtype="<i8")
+    assert list(raw) == [0, -1, 2**62, -2**62]
+
+
+def test_damaged_files_are_refused(tmp_path):
+    ck.save(str(tmp_path), {"a": torch.arange(10, dtype=torch.float32)})
+    with open(tmp_path / "a.bin", "r+b") as f:
+        f.truncate(36)
+    with pytest.raises(ValueError):
+        ck.load(str(tmp_path), "cpu")
+    ck.save(str(tmp_path), {"a": torch.arange(10, dtype=torch.float32)})
+    man = json.load(open(tmp_path / ck.MANIFEST))
+    man["tensors"]["a"]["file"] = "../a.bin"
+    json.dump(man, open(tmp_path / ck.MANIFEST, "w"))
+    with pytest.raises(ValueError):
+        ck.load(str(tmp_path), "cpu")
+    man["tensors"]["a"]["file"] = "a.bin"
+    man["format"] = 99
+    json.dump(man, open(tmp_path / ck.MANIFEST, "w"))
+    with pytest.raises(ValueError):
+        ck.load(str(tmp_path), "cpu")
+
+
+def test_group_and_lamb_state_round_trip(tmp_path):
+    N, n = 4096, 4
+    off = torch.tensor([0, 100, 100, 3000, N], dtype=torch.int64)
+    k = torch.tensor([1.0, 2.0, 0.5, 4.0])
+    grp = OneBitGroup(N, n, torch.device("cpu"), clip=2.0, reset_interval=2000, seg_off=off,
+                      seg_k=k)
+    g = torch.Generator().manual_seed(5)
+    for name in grp._STATE:
+        buf = getattr(grp, name)
+        if buf.dtype == torch.float32:
+            buf.copy_(torch.randn(buf.shape, generator=g))
+        else:
+            buf.copy_(torch.randint(-2**31, 2**31 - 1, buf.shape, generator=g, dtype=buf.dtype))
+    S = off.numel() - 1
+    st = LambState.create(torch.randn(N, generator=g), torch.rand(N, generator=g),
+                          torch.randn(N, generator=g), off, torch.rand(S, generator=g))
+    st.v_fresh.copy_(torch.rand(N, generator=g))
+    st.r.copy_(torch.rand(S, generator=g))
+    st.c.copy_(torch.rand(S, generator=g))
+    ck.save(str(tmp_path / "g"), grp.state_dict(), meta={"t": 5, "group": grp.config()})
+    ck.save(str(tmp_path / "l"), st.state_dict())
+    tg, meta = ck.load(str(tmp_path / "g"), "cpu")
+    grp2 = OneBitGroup.from_state(tg, meta["group"], torch.device("cpu"))
+    assert grp2.config() == grp.config() and meta["t"] == 5
+    for name, v in grp.state_dict().items():
+        w = grp2.state_dict()[name]
+        assert (v is None and w is None) or torch.equal(v, w), name
+    tl, _ = ck.load(str(tmp_path / "l"), "cpu")
+    st2 = LambState.from_state(tl)
+    for name, v in st.state_dict().items():
+        assert torch.equal(v, getattr(st2, name)), name
+    bad = dict(tg)
+    bad["ef"] = bad["ef"][:, :64]
+    with pytest.raises(ValueError):
+        OneBitGroup.from_state(bad, meta["group"], torch.device("cpu"))
