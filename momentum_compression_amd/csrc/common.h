@@ -13,8 +13,8 @@ using f4 = float __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;           // threads per workgroup (4 waves)
 constexpr int kTile = kThreads * 4;     // elements per workgroup iteration (float4 / lane)
-constexpr int kMaxIters = 4;            // tiles per workgroup: Adam, decompress, warmup Adam
-constexpr int kUnroll = 4;              // tiles whose loads are issued together
+constexpr int kMaxIters = 4;            // tiles per workgroup: Adam (both forms), warmup Adam,
+                                        // the INT8 tensor maximum pass
 // Tiles per workgroup of the kernels whose best shape differs (measured on
 // the full-size workloads): many one-tile workgroups for the worker
 // compression, two tiles for the server and the INT8 pass.
