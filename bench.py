@@ -160,6 +160,16 @@ def _time_calls(fns, warmup: int, steps: int, stream):
     return [a / steps for a in acc]
 
 
+def _rel(a, b) -> float:
+    """||a|| / ||b|| (binary64 norms): a report-only diagnostic of the
+    compression error against what was compressed."""
+    import torch
+
+    na = torch.linalg.vector_norm(a.double()).item()
+    nb = torch.linalg.vector_norm(b.double()).item()
+    return na / nb if nb > 0 else float("nan")
+
+
 def _row(ms: float, nbytes: float, elems: int) -> dict:
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"ms": round(ms, 4), "elements_per_s": elems / (ms * 1e-3),
@@ -243,6 +253,8 @@ def measure_lamb(steps: int, warmup: int) -> dict:
            "lamb_step": _row(ms[3], B_LAMB_STEP * N, N),
            "compress_x_k_step_ratio_ef": _row(ms[4], B_COMPRESS * n * N, n * N),
            "server_step_ratio_ef": _row(ms[5], b_server(n) * N, N)}
+    r = st2.r.double()
+    out["r_t"] = {"min": r.min().item(), "median": r.median().item(), "max": r.max().item()}
     del grp, st, st2, m
     torch.cuda.empty_cache()
     return out
@@ -460,7 +472,11 @@ def measure_int8(steps: int, warmup: int) -> dict:
         ob.int8_quantize(g, err, codes, scales, deq, N, 0, 0, 4, 1, ws=ws)
 
     ms = _time_calls([q, rtn, tensor_scale], warmup, steps, stream)
-    out = {"workload": "int8_sr_2^30", "N": N, "block": block,
+    # report-only: ||deq - g|| / ||g|| of one call from zero error
+    err.zero_()
+    q()
+    rel = _rel(deq - g, g)
+    out = {"workload": "int8_sr_2^30", "N": N, "block": block, "dequantised_error_rel": rel,
            "int8_sr_ef_deq": _row(ms[0], B_INT8 * N, N),
            "int8_nearest_ef_deq": _row(ms[1], B_INT8 * N, N),
            # one extra read pass of g and the error for the tensor maximum
@@ -597,6 +613,10 @@ def main() -> int:
     separate = {"decompress": _row(ms_u[0], B_DECOMPRESS * N, N),
                 "adam": _row(ms_u[1], B_ADAM * N, N),
                 "sum_ms": round(ms_u[0] + ms_u[1], 4)}
+    # compression error relative to the compensated values after the last
+    # step (worker 0 and the server), outside every timed region
+    diagnostics = {"worker0_error_rel": _rel(grp.worker_error()[0], grp.ef[0]),
+                   "server_error_rel": _rel(grp.server_error(), grp.sv_ef)}
 
     comp_gbs = bytes_["compress"] / (ms["compress"] * 1e-3) / 1e9
     traffic = read_traffic(n * N)
@@ -624,6 +644,7 @@ def main() -> int:
                      "launch_ms": round(ms["compress"], 4)},
         "kernels": kernels,
     }
+    out["diagnostics"] = diagnostics
     out["rows"] = {"decompress_then_adam": separate}
     if not args.no_rows:
         del grp, m, x, v
