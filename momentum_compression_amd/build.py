@@ -66,8 +66,34 @@ def _compile(src: str) -> str:
     return obj
 
 
+CAPI_SRC = os.path.join(ROOT, "tests", "capi", "capi_roundtrip.c")
+CAPI_BIN = os.path.join(BUILD, "capi_roundtrip")
+
+
+def _rocm() -> str:
+    return os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+
+
+def build_capi() -> str:
+    """The plain C consumer of the ABI (host code only: gcc, the HIP runtime
+    and libonebit.so, found next to the binary's parent directory)."""
+    rocm = _rocm()
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler for the C ABI test program")
+    cmd = [cc, "-std=c99", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           f"-I{rocm}/include", f"-I{INCLUDE}", CAPI_SRC, f"-L{HERE}", "-lonebit",
+           f"-L{rocm}/lib", "-lamdhip64", "-lm", "-Wl,-rpath,$ORIGIN/..",
+           f"-Wl,-rpath,{rocm}/lib", "-o", CAPI_BIN]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"C ABI test program failed to build:\n{res.stderr}")
+    return CAPI_BIN
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every kernel source for gfx950 and link libonebit.so."""
+    """Compile every kernel source for gfx950, link libonebit.so, and build
+    the plain C test program against it."""
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
@@ -77,8 +103,9 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
     os.replace(tmp, LIB)
+    build_capi()
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CAPI_BIN}")
     return LIB
 
 
