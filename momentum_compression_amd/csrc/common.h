@@ -25,6 +25,7 @@ constexpr int kServerUnroll = 2;
 constexpr int kInt8Tiles = 2;
 constexpr int kDecompressTiles = 4;
 constexpr int kLambTiles = 4;           // tiles per workgroup in the LAMB pass (5 streams in flight)
+constexpr int kFinThreads = 1024;       // threads of a chunk-mean finalize workgroup (16 waves)
 
 // workgroups of the LAMB pass over N elements
 inline int64_t lamb_workgroups(int64_t N) {

@@ -93,12 +93,33 @@ __device__ float exact_mean_from_bins(const unsigned long long* bins, uint64_t L
     return __uint_as_float(((uint32_t)b << 23) + m24);
 }
 
+// Sum over the kFinThreads threads of the finalize workgroup: wave
+// butterflies (6 levels), then a pairwise tree over the 16 wave sums (4
+// levels); valid in thread 0.
+__device__ __forceinline__ double fin_block_sum(double v, double* red) {
+    v = wave_sum(v);
+    if (lane_id() == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double r = 0.0;
+    if (threadIdx.x == 0) {
+        double t[kFinThreads / 64];
+#pragma unroll
+        for (int w = 0; w < kFinThreads / 64; ++w) t[w] = red[w];
+#pragma unroll
+        for (int width = kFinThreads / 128; width >= 1; width >>= 1)
+#pragma unroll
+            for (int w = 0; w < width; ++w) t[w] = t[2 * w] + t[2 * w + 1];
+        r = t[0];
+    }
+    return r;
+}
+
 }  // namespace
 
-__global__ __launch_bounds__(kThreads) void mean_finalize_kernel(
+__global__ __launch_bounds__(kFinThreads) void mean_finalize_kernel(
     const double* __restrict__ partials, int64_t bpc, int64_t L, const float* __restrict__ data,
     int64_t row_stride, int32_t chunks, float* __restrict__ out, int32_t unit) {
-    __shared__ double red[kThreads / 64];
+    __shared__ double red[kFinThreads / 64];
     __shared__ unsigned long long bins[256];
     __shared__ int exact;
     const int64_t pair = blockIdx.x;
@@ -107,21 +128,21 @@ __global__ __launch_bounds__(kThreads) void mean_finalize_kernel(
         return;
     }
     const double* p = partials + pair * bpc;
-    // thread t adds partials t, t + 256, t + 512, ... in that order; the loads
-    // of 8 of them are issued before the additions
+    // thread t adds partials t, t + T, t + 2T, ... (T = kFinThreads) in that
+    // order; the loads of 8 of them are issued before the additions
     constexpr int kBatch = 8;
     double acc = 0.0;
-    for (int64_t k0 = threadIdx.x; k0 < bpc; k0 += (int64_t)kThreads * kBatch) {
+    for (int64_t k0 = threadIdx.x; k0 < bpc; k0 += (int64_t)kFinThreads * kBatch) {
         double v[kBatch];
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
-            const int64_t k = k0 + (int64_t)q * kThreads;
+            const int64_t k = k0 + (int64_t)q * kFinThreads;
             v[q] = k < bpc ? p[k] : 0.0;
         }
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) acc += v[q];
     }
-    const double tot = block_sum(acc, red);
+    const double tot = fin_block_sum(acc, red);
     if (threadIdx.x == 0) {
         const double mu = tot / (double)L;
         const float r = (float)mu;
@@ -145,12 +166,12 @@ __global__ __launch_bounds__(kThreads) void mean_finalize_kernel(
     if (!exact) return;
 
     // exact path: per-exponent significand sums of the stored chunk values
-    for (int k = threadIdx.x; k < 256; k += kThreads) bins[k] = 0;
+    for (int k = threadIdx.x; k < 256; k += kFinThreads) bins[k] = 0;
     __syncthreads();
     const int64_t row = pair / chunks;
     const int64_t c = pair - row * chunks;
     const float* x = data + row * row_stride + c * L;
-    for (int64_t j = threadIdx.x; j < L; j += kThreads) {
+    for (int64_t j = threadIdx.x; j < L; j += kFinThreads) {
         const uint32_t a = __float_as_uint(x[j]) & 0x7FFFFFFFu;
         uint32_t e = a >> 23;
         uint32_t mant = a & 0x7FFFFFu;
@@ -163,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void mean_finalize_kernel(
 
 hipError_t launch_mean_finalize(const double* partials, const ChunkPlan& plan, int64_t pairs,
                                 MeanTarget tgt, hipStream_t st) {
-    hipLaunchKernelGGL(mean_finalize_kernel, dim3((unsigned)pairs), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL(mean_finalize_kernel, dim3((unsigned)pairs), dim3(kFinThreads), 0, st,
                        partials, plan.bpc, plan.L, tgt.data, tgt.row_stride, tgt.chunks, tgt.out,
                        tgt.unit ? 1 : 0);
     return hipGetLastError();
@@ -183,9 +204,10 @@ ChunkPlan make_plan(int64_t L, int64_t chunks, int32_t max_iters) {
 }
 
 int64_t sum_depth(const ChunkPlan& p) {
-    // per thread 4 * iters sequential adds, 6 butterfly levels, 2 LDS levels,
-    // ceil(bpc / 256) sequential adds in the finalize, 8 tree levels, 1 division
-    return 4 * (int64_t)p.iters + 6 + 2 + (p.bpc + kThreads - 1) / kThreads + 8 + 1;
+    // producer workgroup: per thread 4 * iters sequential adds, 6 butterfly
+    // levels, 2 LDS levels; finalize: ceil(bpc / kFinThreads) sequential adds,
+    // 6 butterfly levels, 4 tree levels over the 16 waves; 1 division
+    return 4 * (int64_t)p.iters + 6 + 2 + (p.bpc + kFinThreads - 1) / kFinThreads + 6 + 4 + 1;
 }
 
 }  // namespace onebit
