@@ -29,13 +29,13 @@ namespace onebit {
 // the copy at shift 7k only bit k reaches a masked position, bit 8k).
 // Workers m .. n-1 are then added one by one as before.
 // NW: the worker count when known at compile time (8, 16), else 0 (any n).
-template <bool ERS, int NW>
+// RESET: the carried server error is dropped (not read).
+template <bool ERS, int NW, bool RESET>
 __global__ __launch_bounds__(kThreads) void server_kernel(
     const uint32_t* __restrict__ bits, const float* __restrict__ scales, float* __restrict__ ef,
     const float* __restrict__ S_prev, uint32_t* __restrict__ sv_bits, double* __restrict__ partials,
-    int64_t N, int32_t n, int64_t L, int32_t iters, int64_t bpc, int32_t reset, int32_t pow2,
-    float inv_n, const int64_t* __restrict__ seg_off, const float* __restrict__ seg_r,
-    int32_t n_seg) {
+    int64_t N, int32_t n, int64_t L, int32_t iters, int64_t bpc, int32_t pow2, float inv_n,
+    const int64_t* __restrict__ seg_off, const float* __restrict__ seg_r, int32_t n_seg) {
     constexpr int kWordsPerTile = kTile / 32;              // 32
     constexpr int kGroupWords = kWordsPerTile * kServerUnroll;  // words per worker per group
     static_assert(kGroupWords == 64, "staging maps one wave to one worker's words");
@@ -63,7 +63,11 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
         lut[threadIdx.x] = a;
     }
     // (the first group's __syncthreads orders the table before its use)
-    const float S = reset ? 0.0f : S_prev[c];
+    const float S = RESET ? 0.0f : S_prev[c];
+    // a lane's 4 elements start at bit (4 tid) & 31 of their word in every
+    // tile: chunk starts are multiples of 64 and workgroup starts of kTile
+    const int sh = (4 * (int)threadIdx.x) & 31;
+    const bool p2 = NW > 0 ? (NW & (NW - 1)) == 0 : pow2 != 0;
     const float nf = (float)n;
     const int64_t wrow = N >> 5;  // words per worker row
     const int lane8 = lane_id() & 7;
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
         for (int u = 0; u < kServerUnroll; ++u) {
             const int64_t j = g0 + (int64_t)u * kTile + 4 * (int64_t)threadIdx.x;
             pv[u] = f4{0.f, 0.f, 0.f, 0.f};
-            if (!reset && it0 + u < iters && j < end)
+            if (!RESET && it0 + u < iters && j < end)
                 pv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(ef + cbase + j));
         }
         // Staging: a group holds 64 words per worker, so wave w stages workers
@@ -131,7 +135,6 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
             const int64_t j = g0 + (int64_t)u * kTile + 4 * (int64_t)threadIdx.x;
             const bool active = it0 + u < iters && j < end;
             const int64_t J = cbase + j;
-            const int sh = (int)(J & 31);
             const int wl = u * kWordsPerTile + (threadIdx.x >> 3);  // this lane's word in the group
             // first m workers: table indices, one byte per element
             uint32_t idx = 0;
@@ -163,8 +166,8 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
             float g[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const float avg = pow2 ? a[k] * inv_n : a[k] / nf;
-                float e = reset ? 0.0f : ef_error(p[k], S);
+                const float avg = p2 ? a[k] * inv_n : a[k] / nf;
+                float e = RESET ? 0.0f : ef_error(p[k], S);
                 if (ERS) {
                     if (!seg_uniform && active && J + k >= seg_hi && seg + 1 < n_seg) {
                         while (J + k >= seg_hi && seg + 1 < n_seg) {
@@ -204,17 +207,21 @@ hipError_t launch_server(const uint32_t* bits, const float* scales, float* ef, c
     const bool ers = seg_r && seg_off && !reset;
     auto launch = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, bits, scales, ef, S_prev, sv_bits,
-                           partials, N, n, plan.L, plan.iters, plan.bpc, reset ? 1 : 0,
-                           pow2 ? 1 : 0, inv_n, seg_off, seg_r, n_seg);
+                           partials, N, n, plan.L, plan.iters, plan.bpc, pow2 ? 1 : 0, inv_n,
+                           seg_off, seg_r, n_seg);
     };
     if (ers) {
-        if (n == 8) launch(server_kernel<true, 8>);
-        else if (n == 16) launch(server_kernel<true, 16>);
-        else launch(server_kernel<true, 0>);
+        if (n == 8) launch(server_kernel<true, 8, false>);
+        else if (n == 16) launch(server_kernel<true, 16, false>);
+        else launch(server_kernel<true, 0, false>);
+    } else if (reset) {
+        if (n == 8) launch(server_kernel<false, 8, true>);
+        else if (n == 16) launch(server_kernel<false, 16, true>);
+        else launch(server_kernel<false, 0, true>);
     } else {
-        if (n == 8) launch(server_kernel<false, 8>);
-        else if (n == 16) launch(server_kernel<false, 16>);
-        else launch(server_kernel<false, 0>);
+        if (n == 8) launch(server_kernel<false, 8, false>);
+        else if (n == 16) launch(server_kernel<false, 16, false>);
+        else launch(server_kernel<false, 0, false>);
     }
     return hipGetLastError();
 }
