@@ -486,6 +486,65 @@ def measure_int8(steps: int, warmup: int) -> dict:
     return out
 
 
+def measure_sweep(wl, steps: int, warmup: int) -> list:
+    """The step (compress, server, decompression inside the Adam pass) of the
+    workload's worker count over buffer sizes from 2^20 elements to N: where
+    launches and the finalize stop mattering next to the streams."""
+    import torch
+
+    from momentum_compression_amd.state import OneBitGroup
+
+    dev = torch.device("cuda:0")
+    n = wl.n
+    sizes = [1 << k for k in range(20, 30, 2) if (1 << k) < wl.N] + [wl.N]
+    out = []
+    for N in sizes:
+        N -= N % (64 * n)
+        print(f"[bench] sweep N={N} n={n}", file=sys.stderr, flush=True)
+        g = torch.Generator(device=dev)
+        g.manual_seed(N)
+        m = torch.randn((n, N), generator=g, device=dev) * 1e-3
+        x = torch.randn(N, generator=g, device=dev) * 0.02
+        v = torch.rand(N, generator=g, device=dev) * 1e-6 + 1e-8
+        grp = OneBitGroup(N, n, dev)
+        stream = torch.cuda.current_stream()
+
+        def step(t):
+            grp.compress(m, t, first=t == 1)
+            grp.server(t, first=t == 1, decompress=False)
+            grp.adam_step_packed(x, v, wl.lr, wl.eps, decompress=True)
+
+        for t in range(1, warmup + 1):
+            step(t)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for t in range(warmup + 1, warmup + steps + 1):
+            step(t)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        # the same non-reset step as one HIP graph per replay
+        graph = grp.capture_step(m, x, v, wl.lr, wl.eps)
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_g = e0.elapsed_time(e1) / steps
+        nbytes = B_COMPRESS * n * N + b_server(n) * N + B_DECOMPRESS_ADAM * N
+        out.append({"N": N, "workers": n, "ms_per_step": round(ms, 4),
+                    "elements_per_s": n * N / (ms * 1e-3),
+                    "algorithmic_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                    "graph_ms_per_step": round(ms_g, 4)})
+        del m, x, v, grp, graph
+        torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -495,6 +554,9 @@ def main() -> int:
     ap.add_argument("--only", default="", choices=["", "compress", "server", "decompress_adam",
                                                    "decompress", "adam", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the step over buffer sizes from 2^20 to the workload's N "
+                         "(profiling aid; prints its own JSON line)")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the rows measured after the headline step (LAMB, INT8, fused, "
                          "warmup, GPT 1.3B, copy reference)")
@@ -522,6 +584,9 @@ def main() -> int:
         return 2
     dev = torch.device("cuda:0")
     N, n = wl.N, wl.n
+    if args.sweep:
+        print(json.dumps({"sweep": measure_sweep(wl, args.steps, args.warmup)}))
+        return 0
     print(f"[bench] workload={wl.name} N={N} n={n} steps={args.steps} warmup={args.warmup}",
           file=sys.stderr, flush=True)
     sig = S.per_element(S.segment_sigmas(wl), wl, dev)

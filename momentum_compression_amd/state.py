@@ -136,6 +136,35 @@ class OneBitGroup:
     def adam_step(self, x: torch.Tensor, v: torch.Tensor, lr: float, eps: float, stream=None) -> None:
         ob.frozen_v_step(mode=0, N=self.N, x=x, m=self.mbar, v=v, lr=lr, eps=eps, stream=stream)
 
+    def capture_step(self, m: torch.Tensor, x: torch.Tensor, v: torch.Tensor, lr: float,
+                     eps: float) -> "torch.cuda.CUDAGraph":
+        """A HIP graph of one compressed Adam step that does not reset the
+        errors: compress ``m``, server, and the decompression inside the Adam
+        pass (x updated, the decompressed momentum in ``mbar``), on these fixed
+        buffers.  Write the next momenta into ``m`` and replay it; the first
+        step and every ``reset_interval``-th step reset the errors and run
+        eagerly.  Nothing in the step allocates, clears memory or
+        synchronises, so the graph holds only the library's kernels."""
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(device=self.device)  # default priority
+        side.wait_stream(torch.cuda.current_stream(self.device))
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                ob.onebit_compress_ex(m, self.ef, self.scales, self.bits, self.N, self.n,
+                                      clip=self.clip, reset=False, seg_off=self.seg_off,
+                                      seg_k=self.seg_k, seg_err_ratio=self.seg_err_ratio,
+                                      n_seg=self.n_seg, flags=self.flags, ws=self.ws)
+                ob.onebit_server_reduce_ex(self.bits, self.scales, self.sv_ef, self.sv_scales,
+                                           self.sv_bits, None, self.N, self.n, reset=False,
+                                           seg_off=self.seg_off, seg_k=self.seg_k,
+                                           seg_err_ratio=self.seg_err_ratio, n_seg=self.n_seg,
+                                           flags=self.flags, ws=self.ws)
+                ob.frozen_v_step(mode=2, N=self.N, x=x, m=None, v=v, lr=lr, eps=eps,
+                                 m_bits=self.sv_bits, m_scales=self.sv_scales, m_chunks=self.n,
+                                 m_out=self.mbar)
+        torch.cuda.current_stream(self.device).wait_stream(side)
+        return graph
+
     def adam_step_packed(self, x: torch.Tensor, v: torch.Tensor, lr: float, eps: float,
                          decompress: bool = False, stream=None) -> None:
         """Adam step reading the global momentum packed (server words and
