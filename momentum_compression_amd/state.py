@@ -262,6 +262,13 @@ class AdamWarmup:
     def create(cls, x: torch.Tensor) -> "AdamWarmup":
         return cls(x=x, m=torch.zeros_like(x), v=torch.zeros_like(x))
 
+    def state_dict(self) -> Dict[str, torch.Tensor]:
+        return {"x": self.x, "m": self.m, "v": self.v}
+
+    @classmethod
+    def from_state(cls, tensors: Mapping[str, torch.Tensor]) -> "AdamWarmup":
+        return cls(x=tensors["x"], m=tensors["m"], v=tensors["v"])
+
     def step(self, g: torch.Tensor, lr: float, eps: float, beta1: float, beta2: float,
              stream=None) -> None:
         """One step on the gradient averaged over the data-parallel group."""
@@ -293,6 +300,20 @@ class LambWarmup:
                    c_avg=torch.ones(S, dtype=torch.float32, device=dev),
                    ws=torch.empty(max(256, ob.warmup_workspace_bytes(x.numel(), S)),
                                   dtype=torch.uint8, device=dev))
+
+    def state_dict(self) -> Dict[str, torch.Tensor]:
+        """Carried tensors; the step count goes with the checkpoint's meta."""
+        return {"x": self.x, "m": self.m, "v": self.v, "seg_off": self.seg_off, "c": self.c,
+                "c_avg": self.c_avg}
+
+    @classmethod
+    def from_state(cls, tensors: Mapping[str, torch.Tensor], steps: int) -> "LambWarmup":
+        lw = cls.create(tensors["x"], tensors["seg_off"])
+        lw.m, lw.v = tensors["m"], tensors["v"]
+        lw.c.copy_(tensors["c"])
+        lw.c_avg.copy_(tensors["c_avg"])
+        lw.steps = int(steps)
+        return lw
 
     def step(self, g: torch.Tensor, lr: float, eps: float, beta1: float, beta2: float,
              beta_c: float, stream=None) -> None:

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from momentum_compression_amd import checkpoint as ck
-from momentum_compression_amd.state import LambState, OneBitGroup
+from momentum_compression_amd.state import AdamWarmup, LambState, LambWarmup, OneBitGroup
 
 
 def _tensors():
@@ -99,3 +99,29 @@ def test_group_and_lamb_state_round_trip(tmp_path):
     bad["ef"] = bad["ef"][:, :64]
     with pytest.raises(ValueError):
         OneBitGroup.from_state(bad, meta["group"], torch.device("cpu"))
+
+
+def test_warmup_state_round_trip(tmp_path):
+    g = torch.Generator().manual_seed(9)
+    N = 1000
+    off = torch.tensor([0, 10, 10, 600, N], dtype=torch.int64)
+    aw = AdamWarmup.create(torch.randn(N, generator=g))
+    aw.m.copy_(torch.randn(N, generator=g))
+    aw.v.copy_(torch.rand(N, generator=g))
+    lw = LambWarmup.create(torch.randn(N, generator=g), off)
+    lw.m.copy_(torch.randn(N, generator=g))
+    lw.v.copy_(torch.rand(N, generator=g))
+    lw.c.copy_(torch.rand(4, generator=g))
+    lw.c_avg.copy_(torch.rand(4, generator=g))
+    lw.steps = 7
+    ck.save(str(tmp_path / "a"), aw.state_dict())
+    ck.save(str(tmp_path / "l"), lw.state_dict(), meta={"steps": lw.steps})
+    ta, _ = ck.load(str(tmp_path / "a"), "cpu")
+    aw2 = AdamWarmup.from_state(ta)
+    for k, v in aw.state_dict().items():
+        assert torch.equal(v, aw2.state_dict()[k]), k
+    tl, meta = ck.load(str(tmp_path / "l"), "cpu")
+    lw2 = LambWarmup.from_state(tl, meta["steps"])
+    assert lw2.steps == 7
+    for k, v in lw.state_dict().items():
+        assert torch.equal(v, lw2.state_dict()[k]), k
