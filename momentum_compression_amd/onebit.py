@@ -124,6 +124,31 @@ def _ptr(x) -> Optional[int]:
     return x.data_ptr()
 
 
+def _on_gpu(t) -> bool:
+    return t.device.type == "cuda"
+
+
+# element kinds of the C ABI's buffers and the tensor dtypes that carry them
+_KINDS = {"f32": ("float32",), "u32": ("int32", "uint32"), "i64": ("int64",),
+          "i8": ("int8",), "u8": ("uint8",)}
+
+
+def _buf(x, count: int, kind: str, name: str) -> Optional[int]:
+    """Device pointer of a tensor argument that must hold at least ``count``
+    elements of ``kind``.  Plain integers (raw device addresses) pass as they
+    are; a host tensor, a wrong dtype or a short buffer raises ValueError
+    before the library sees the call (the C ABI cannot check sizes)."""
+    if x is None or isinstance(x, int):
+        return x
+    if not _on_gpu(x):
+        raise ValueError(f"{name} must be a device tensor (got {x.device})")
+    if str(x.dtype).replace("torch.", "") not in _KINDS[kind]:
+        raise ValueError(f"{name} must be {' or '.join(_KINDS[kind])} (got {x.dtype})")
+    if x.numel() < count:
+        raise ValueError(f"{name} holds {x.numel()} elements, the call needs {count}")
+    return _ptr(x)
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         import torch
@@ -154,17 +179,21 @@ def frozen_v_workspace_bytes(N: int, n_seg: int) -> int:
 def onebit_compress(m, ef, scales, bits, N: int, n: int, clip: float = 0.0, reset: bool = False,
                     seg_off=None, seg_k=None, n_seg: int = 0, ws=None, stream=None) -> None:
     _check("onebit_compress", load().onebit_compress(
-        _ptr(m), _ptr(ef), _ptr(scales), _ptr(bits), N, n, clip, int(bool(reset)),
-        _ptr(seg_off), _ptr(seg_k), n_seg, _ptr(ws), _nbytes(ws) if ws is not None else 0,
-        _stream(stream)))
+        _buf(m, n * N, "f32", "m"), _buf(ef, n * N, "f32", "ef"), _buf(scales, n * n, "f32", "scales"),
+        _buf(bits, n * N // 32, "u32", "bits"), N, n, clip, int(bool(reset)),
+        _buf(seg_off, n_seg + 1, "i64", "seg_off"), _buf(seg_k, n_seg, "f32", "seg_k"), n_seg,
+        _buf(ws, 0, "u8", "ws"), _nbytes(ws) if ws is not None else 0, _stream(stream)))
 
 
 def onebit_compress_grad(g, mb_bits, mb_scales, beta1: float, ef, scales, bits, N: int, n: int,
                          clip: float = 0.0, reset: bool = False, seg_off=None, seg_k=None,
                          n_seg: int = 0, ws=None, stream=None) -> None:
     _check("onebit_compress_grad", load().onebit_compress_grad(
-        _ptr(g), _ptr(mb_bits), _ptr(mb_scales), beta1, _ptr(ef), _ptr(scales), _ptr(bits), N, n,
-        clip, int(bool(reset)), _ptr(seg_off), _ptr(seg_k), n_seg, _ptr(ws),
+        _buf(g, n * N, "f32", "g"), _buf(mb_bits, N // 32, "u32", "mb_bits"),
+        _buf(mb_scales, n, "f32", "mb_scales"), beta1, _buf(ef, n * N, "f32", "ef"),
+        _buf(scales, n * n, "f32", "scales"), _buf(bits, n * N // 32, "u32", "bits"), N, n,
+        clip, int(bool(reset)), _buf(seg_off, n_seg + 1, "i64", "seg_off"),
+        _buf(seg_k, n_seg, "f32", "seg_k"), n_seg, _buf(ws, 0, "u8", "ws"),
         _nbytes(ws) if ws is not None else 0, _stream(stream)))
 
 
@@ -173,45 +202,58 @@ def onebit_compress_ex(m, ef, scales, bits, N: int, n: int, mb_bits=None, mb_sca
                        seg_k=None, seg_err_ratio=None, n_seg: int = 0, flags: int = 0, ws=None,
                        stream=None) -> None:
     _check("onebit_compress_ex", load().onebit_compress_ex(
-        _ptr(m), _ptr(mb_bits), _ptr(mb_scales), beta1, _ptr(ef), _ptr(scales), _ptr(bits), N, n,
-        clip, int(bool(reset)), _ptr(seg_off), _ptr(seg_k), _ptr(seg_err_ratio), n_seg, flags,
-        _ptr(ws), _nbytes(ws) if ws is not None else 0, _stream(stream)))
+        _buf(m, n * N, "f32", "m"), _buf(mb_bits, N // 32, "u32", "mb_bits"),
+        _buf(mb_scales, n, "f32", "mb_scales"), beta1, _buf(ef, n * N, "f32", "ef"),
+        _buf(scales, n * n, "f32", "scales"), _buf(bits, n * N // 32, "u32", "bits"), N, n,
+        clip, int(bool(reset)), _buf(seg_off, n_seg + 1, "i64", "seg_off"),
+        _buf(seg_k, n_seg, "f32", "seg_k"), _buf(seg_err_ratio, n_seg, "f32", "seg_err_ratio"),
+        n_seg, flags, _buf(ws, 0, "u8", "ws"), _nbytes(ws) if ws is not None else 0,
+        _stream(stream)))
 
 
 def onebit_server_reduce_ex(bits, scales, ef, sv_scales, sv_bits, m_out, N: int, n: int,
                             reset: bool = False, seg_off=None, seg_k=None, seg_err_ratio=None,
                             n_seg: int = 0, flags: int = 0, ws=None, stream=None) -> None:
     _check("onebit_server_reduce_ex", load().onebit_server_reduce_ex(
-        _ptr(bits), _ptr(scales), _ptr(ef), _ptr(sv_scales), _ptr(sv_bits), _ptr(m_out),
-        _ptr(seg_off), _ptr(seg_k), _ptr(seg_err_ratio), n_seg, N, n, int(bool(reset)), flags,
-        _ptr(ws), _nbytes(ws) if ws is not None else 0, _stream(stream)))
+        _buf(bits, n * N // 32, "u32", "bits"), _buf(scales, n * n, "f32", "scales"),
+        _buf(ef, N, "f32", "ef"), _buf(sv_scales, n, "f32", "sv_scales"),
+        _buf(sv_bits, N // 32, "u32", "sv_bits"), _buf(m_out, N, "f32", "m_out"),
+        _buf(seg_off, n_seg + 1, "i64", "seg_off"), _buf(seg_k, n_seg, "f32", "seg_k"),
+        _buf(seg_err_ratio, n_seg, "f32", "seg_err_ratio"), n_seg, N, n, int(bool(reset)), flags,
+        _buf(ws, 0, "u8", "ws"), _nbytes(ws) if ws is not None else 0, _stream(stream)))
 
 
 def onebit_server_reduce(bits, scales, ef, sv_scales, sv_bits, m_out, N: int, n: int,
                          reset: bool = False, seg_off=None, seg_k=None, n_seg: int = 0, ws=None,
                          stream=None) -> None:
     _check("onebit_server_reduce", load().onebit_server_reduce(
-        _ptr(bits), _ptr(scales), _ptr(ef), _ptr(sv_scales), _ptr(sv_bits), _ptr(m_out),
-        _ptr(seg_off), _ptr(seg_k), n_seg, N, n, int(bool(reset)), _ptr(ws),
-        _nbytes(ws) if ws is not None else 0, _stream(stream)))
+        _buf(bits, n * N // 32, "u32", "bits"), _buf(scales, n * n, "f32", "scales"),
+        _buf(ef, N, "f32", "ef"), _buf(sv_scales, n, "f32", "sv_scales"),
+        _buf(sv_bits, N // 32, "u32", "sv_bits"), _buf(m_out, N, "f32", "m_out"),
+        _buf(seg_off, n_seg + 1, "i64", "seg_off"), _buf(seg_k, n_seg, "f32", "seg_k"), n_seg, N,
+        n, int(bool(reset)), _buf(ws, 0, "u8", "ws"), _nbytes(ws) if ws is not None else 0,
+        _stream(stream)))
 
 
 def onebit_decompress(sv_bits, sv_scales, m_out, N: int, n: int, seg_off=None, seg_k=None,
                       n_seg: int = 0, stream=None) -> None:
     _check("onebit_decompress", load().onebit_decompress(
-        _ptr(sv_bits), _ptr(sv_scales), _ptr(m_out), _ptr(seg_off), _ptr(seg_k), n_seg, N, n,
-        _stream(stream)))
+        _buf(sv_bits, N // 32, "u32", "sv_bits"), _buf(sv_scales, n, "f32", "sv_scales"),
+        _buf(m_out, N, "f32", "m_out"), _buf(seg_off, n_seg + 1, "i64", "seg_off"),
+        _buf(seg_k, n_seg, "f32", "seg_k"), n_seg, N, n, _stream(stream)))
 
 
 def onebit_error_materialize(ef, scales, e_out, N: int, rows: int, n: int, stream=None) -> None:
     _check("onebit_error_materialize", load().onebit_error_materialize(
-        _ptr(ef), _ptr(scales), _ptr(e_out), N, rows, n, _stream(stream)))
+        _buf(ef, rows * N, "f32", "ef"), _buf(scales, rows * n, "f32", "scales"),
+        _buf(e_out, rows * N, "f32", "e_out"), N, rows, n, _stream(stream)))
 
 
 def lamb_layer_scale(buf, N: int, batch: int, seg_off, seg_k, n_seg: int, divide: bool,
                      stream=None) -> None:
     _check("lamb_layer_scale", load().lamb_layer_scale(
-        _ptr(buf), N, batch, _ptr(seg_off), _ptr(seg_k), n_seg, int(bool(divide)), _stream(stream)))
+        _buf(buf, batch * N, "f32", "buf"), N, batch, _buf(seg_off, n_seg + 1, "i64", "seg_off"),
+        _buf(seg_k, n_seg, "f32", "seg_k"), n_seg, int(bool(divide)), _stream(stream)))
 
 
 def frozen_v_step(*, mode: int, N: int, x, m, v, lr: float, eps: float, beta1: float = 0.9,
@@ -222,28 +264,39 @@ def frozen_v_step(*, mode: int, N: int, x, m, v, lr: float, eps: float, beta1: f
                   ws=None, stream=None) -> None:
     a = FrozenVArgs(mode=mode, use_c_t=int(bool(use_c_t)), N=N, lr=lr, eps=eps, beta1=beta1,
                     beta2=beta2, r_threshold=r_threshold, r_min=r_min, r_max=r_max, n_seg=n_seg,
-                    x=_ptr(x), m=_ptr(m), v=_ptr(v), m_prev=_ptr(m_prev), v_fresh=_ptr(v_fresh),
-                    seg_off=_ptr(seg_off), c_avg=_ptr(c_avg), r_prev=_ptr(r_prev),
-                    c_prev=_ptr(c_prev), ratio_max=_ptr(ratio_max), m_bits=_ptr(m_bits),
-                    m_scales=_ptr(m_scales), m_chunks=m_chunks, err_ratio=_ptr(err_ratio),
-                    m_out=_ptr(m_out), m_seg_k=_ptr(m_seg_k))
+                    x=_buf(x, N, "f32", "x"), m=_buf(m, N, "f32", "m"), v=_buf(v, N, "f32", "v"),
+                    m_prev=_buf(m_prev, N, "f32", "m_prev"),
+                    v_fresh=_buf(v_fresh, N, "f32", "v_fresh"),
+                    seg_off=_buf(seg_off, n_seg + 1, "i64", "seg_off"),
+                    c_avg=_buf(c_avg, n_seg, "f32", "c_avg"), r_prev=_buf(r_prev, n_seg, "f32", "r_prev"),
+                    c_prev=_buf(c_prev, n_seg, "f32", "c_prev"),
+                    ratio_max=_buf(ratio_max, n_seg, "f32", "ratio_max"),
+                    m_bits=_buf(m_bits, N // 32, "u32", "m_bits"),
+                    m_scales=_buf(m_scales, m_chunks, "f32", "m_scales"), m_chunks=m_chunks,
+                    err_ratio=_buf(err_ratio, n_seg, "f32", "err_ratio"),
+                    m_out=_buf(m_out, N, "f32", "m_out"), m_seg_k=_buf(m_seg_k, n_seg, "f32", "m_seg_k"))
     _check("frozen_v_step", load().frozen_v_step(
-        ctypes.byref(a), _ptr(ws), _nbytes(ws) if ws is not None else 0, _stream(stream)))
+        ctypes.byref(a), _buf(ws, 0, "u8", "ws"), _nbytes(ws) if ws is not None else 0,
+        _stream(stream)))
 
 
 def int8_sr_quantize(g, err, codes, block_scales, deq, N: int, block: int, seed: int, step: int,
                      stream=None) -> None:
+    nsc = N // block if block > 0 else 1
     _check("int8_sr_quantize", load().int8_sr_quantize(
-        _ptr(g), _ptr(err), _ptr(codes), _ptr(block_scales), _ptr(deq), N, block,
+        _buf(g, N, "f32", "g"), _buf(err, N, "f32", "err"), _buf(codes, N, "i8", "codes"),
+        _buf(block_scales, nsc, "f32", "block_scales"), _buf(deq, N, "f32", "deq"), N, block,
         seed & 0xFFFFFFFFFFFFFFFF, step & 0xFFFFFFFF, _stream(stream)))
 
 
 def int8_quantize(g, err, codes, block_scales, deq, N: int, block: int, rounding: int, seed: int,
                   step: int, ws=None, stream=None) -> None:
+    nsc = N // block if block > 0 else 1
     _check("int8_quantize", load().int8_quantize(
-        _ptr(g), _ptr(err), _ptr(codes), _ptr(block_scales), _ptr(deq), N, block, rounding,
-        seed & 0xFFFFFFFFFFFFFFFF, step & 0xFFFFFFFF, _ptr(ws), _nbytes(ws) if ws is not None else 0,
-        _stream(stream)))
+        _buf(g, N, "f32", "g"), _buf(err, N, "f32", "err"), _buf(codes, N, "i8", "codes"),
+        _buf(block_scales, nsc, "f32", "block_scales"), _buf(deq, N, "f32", "deq"), N, block,
+        rounding, seed & 0xFFFFFFFFFFFFFFFF, step & 0xFFFFFFFF, _buf(ws, 0, "u8", "ws"),
+        _nbytes(ws) if ws is not None else 0, _stream(stream)))
 
 
 def warmup_workspace_bytes(N: int, n_seg: int) -> int:
@@ -253,16 +306,20 @@ def warmup_workspace_bytes(N: int, n_seg: int) -> int:
 def warmup_adam_step(x, m, v, g, N: int, lr: float, eps: float, beta1: float, beta2: float,
                      stream=None) -> None:
     _check("warmup_adam_step", load().warmup_adam_step(
-        _ptr(x), _ptr(m), _ptr(v), _ptr(g), N, lr, eps, beta1, beta2, _stream(stream)))
+        _buf(x, N, "f32", "x"), _buf(m, N, "f32", "m"), _buf(v, N, "f32", "v"),
+        _buf(g, N, "f32", "g"), N, lr, eps, beta1, beta2, _stream(stream)))
 
 
 def warmup_lamb_step(x, m, v, g, N: int, seg_off, n_seg: int, lr: float, eps: float, beta1: float,
                      beta2: float, beta_c: float, first: bool, c, c_avg, ws, stream=None) -> None:
     _check("warmup_lamb_step", load().warmup_lamb_step(
-        _ptr(x), _ptr(m), _ptr(v), _ptr(g), N, _ptr(seg_off), n_seg, lr, eps, beta1, beta2,
-        beta_c, 1 if first else 0, _ptr(c), _ptr(c_avg), _ptr(ws), _nbytes(ws), _stream(stream)))
+        _buf(x, N, "f32", "x"), _buf(m, N, "f32", "m"), _buf(v, N, "f32", "v"),
+        _buf(g, N, "f32", "g"), N, _buf(seg_off, n_seg + 1, "i64", "seg_off"), n_seg, lr, eps,
+        beta1, beta2, beta_c, 1 if first else 0, _buf(c, n_seg, "f32", "c"),
+        _buf(c_avg, n_seg, "f32", "c_avg"), _buf(ws, 0, "u8", "ws"), _nbytes(ws), _stream(stream)))
 
 
 def lamb_momentum_scale(m, N: int, seg_off, n_seg: int, k, ws, stream=None) -> None:
     _check("lamb_momentum_scale", load().lamb_momentum_scale(
-        _ptr(m), N, _ptr(seg_off), n_seg, _ptr(k), _ptr(ws), _nbytes(ws), _stream(stream)))
+        _buf(m, N, "f32", "m"), N, _buf(seg_off, n_seg + 1, "i64", "seg_off"), n_seg,
+        _buf(k, n_seg, "f32", "k"), _buf(ws, 0, "u8", "ws"), _nbytes(ws), _stream(stream)))

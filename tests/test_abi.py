@@ -237,3 +237,40 @@ def test_chunk_length_limit(lib):
     assert ob.workspace_bytes(1 << 31, 1) == 0
     assert ob.workspace_bytes(1 << 32, 2) == 0
     assert _compress(lib, N=1 << 32, n=2) == ob.ONEBIT_E_SIZE
+
+
+def test_binding_refuses_host_short_and_mistyped_tensors(monkeypatch):
+    """The Python binding checks what the C ABI cannot see: tensors must live
+    on the device, carry the element type of their buffer and hold enough
+    elements.  Every call below fails in Python, before the library is
+    entered (no call here reaches a kernel)."""
+    import torch
+
+    N, n = 4096, 4
+    host = torch.zeros((n, N))
+    with pytest.raises(ValueError, match="device tensor"):
+        ob.onebit_compress(host, host, torch.zeros((n, n)), torch.zeros((n, N // 32),
+                           dtype=torch.int32), N, n, ws=torch.zeros(1 << 20, dtype=torch.uint8))
+    # pretend host tensors are device tensors to reach the size and type checks
+    monkeypatch.setattr(ob, "_on_gpu", lambda t: True)
+    scales = torch.zeros((n, n))
+    bits = torch.zeros((n, N // 32), dtype=torch.int32)
+    ws = torch.zeros(1 << 20, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="needs"):
+        ob.onebit_compress(torch.zeros((n, N - 64)), host, scales, bits, N, n, ws=ws)
+    with pytest.raises(ValueError, match="float32"):
+        ob.onebit_compress(host.double(), host, scales, bits, N, n, ws=ws)
+    with pytest.raises(ValueError, match="int32 or uint32"):
+        ob.onebit_compress(host, host, scales, bits.long(), N, n, ws=ws)
+    with pytest.raises(ValueError, match="needs"):
+        ob.onebit_server_reduce(bits, scales, torch.zeros(N - 4), torch.zeros(n),
+                                torch.zeros(N // 32, dtype=torch.int32), None, N, n, ws=ws)
+    with pytest.raises(ValueError, match="int8"):
+        ob.int8_sr_quantize(torch.zeros(N), None, torch.zeros(N, dtype=torch.uint8),
+                            torch.zeros(N // 256), None, N, 256, 1, 1)
+    with pytest.raises(ValueError, match="needs"):
+        ob.frozen_v_step(mode=0, N=N, x=torch.zeros(N), m=torch.zeros(N // 2), v=torch.zeros(N),
+                         lr=1e-3, eps=1e-6)
+    with pytest.raises(ValueError, match="int64"):
+        ob.lamb_layer_scale(torch.zeros(N), N, 1, torch.zeros(3, dtype=torch.int32),
+                            torch.zeros(2), 2, False)

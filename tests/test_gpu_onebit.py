@@ -150,11 +150,13 @@ def test_exact_tie_takes_exact_path():
 def test_zero_size_is_a_noop():
     dev = device()
     t = torch.zeros(16, device=dev)
-    ob.onebit_compress(t, t, t, t, 0, 4, ws=None)
-    ob.int8_sr_quantize(t, None, t, t, None, 0, 256, 1, 1)
+    w = torch.zeros(16, dtype=torch.int32, device=dev)
+    q = torch.zeros(16, dtype=torch.int8, device=dev)
+    ob.onebit_compress(t, t, t, w, 0, 4, ws=None)
+    ob.int8_sr_quantize(t, None, q, t, None, 0, 256, 1, 1)
     ob.frozen_v_step(mode=0, N=0, x=t, m=t, v=t, lr=1.0, eps=0.0)
     torch.cuda.synchronize()
-    assert torch.all(t == 0)
+    assert torch.all(t == 0) and torch.all(w == 0) and torch.all(q == 0)
 
 
 def test_invalid_arguments_rejected_before_launch():
