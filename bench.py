@@ -91,41 +91,46 @@ def read_traffic(launch_elems: int):
     return (fetch + write) * 1024.0
 
 
-def cpu_baseline(wl, seed: int = 11):
-    """Time the CPU oracle on one chunk of each stage and scale to a step."""
+def cpu_baseline(wl, seed: int = 11, repeats: int = 3):
+    """Time the CPU oracle on one chunk of each stage, `repeats` times on fresh
+    inputs (about 10 s of one core at the 335M x 8 chunk size), and scale the
+    mean to a whole step."""
     import numpy as np
 
     from oracle import onebit as O
     from oracle import optim as P
 
-    rng = np.random.default_rng(seed)
     L, n = wl.L, wl.n
-    m = (rng.standard_normal(L) * 1e-3).astype(np.float32)[None, :]
-    t0 = time.perf_counter()
-    w = O.worker_compress(m, np.zeros_like(m), reset=True)
-    t_wc = time.perf_counter() - t0
-    bits_c = np.stack([w["bits"][0]] * n)
-    bits_c[1::2] = ~bits_c[1::2]
-    s_c = np.full(n, w["s"][0, 0], dtype=np.float32)
-    t0 = time.perf_counter()
-    sv = O.server_chunk(bits_c, s_c, np.zeros(L, dtype=np.float32), reset=True)
-    t_sc = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    mbar = O.decompress(sv["bits"], np.array([sv["S"]], dtype=np.float32))
-    x = (rng.standard_normal(L) * 0.02).astype(np.float32)
-    v = np.abs(rng.standard_normal(L) * 1e-6).astype(np.float32) + np.float32(1e-8)
-    t_mid = time.perf_counter()
-    P.adam_frozen_step(x, mbar, v, 6e-5, 1e-6)
-    t_dec_adam = (t_mid - t0) + (time.perf_counter() - t_mid)
+    t_wc = t_sc = t_dec_adam = 0.0
+    for r in range(repeats):
+        rng = np.random.default_rng(seed + r)
+        m = (rng.standard_normal(L) * 1e-3).astype(np.float32)[None, :]
+        t0 = time.perf_counter()
+        w = O.worker_compress(m, np.zeros_like(m), reset=True)
+        t_wc += time.perf_counter() - t0
+        bits_c = np.stack([w["bits"][0]] * n)
+        bits_c[1::2] = ~bits_c[1::2]
+        s_c = np.full(n, w["s"][0, 0], dtype=np.float32)
+        t0 = time.perf_counter()
+        sv = O.server_chunk(bits_c, s_c, np.zeros(L, dtype=np.float32), reset=True)
+        t_sc += time.perf_counter() - t0
+        x = (rng.standard_normal(L) * 0.02).astype(np.float32)
+        v = np.abs(rng.standard_normal(L) * 1e-6).astype(np.float32) + np.float32(1e-8)
+        t0 = time.perf_counter()
+        mbar = O.decompress(sv["bits"], np.array([sv["S"]], dtype=np.float32))
+        P.adam_frozen_step(x, mbar, v, 6e-5, 1e-6)
+        t_dec_adam += time.perf_counter() - t0
+    t_wc, t_sc, t_dec_adam = t_wc / repeats, t_sc / repeats, t_dec_adam / repeats
     t_step = n * n * t_wc + n * (t_sc + t_dec_adam)
     return {
         "value": n * wl.N / t_step,
         "unit": "elements/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"one {L}-element worker chunk compressed ({t_wc:.2f} s), one chunk server-reduced "
-                   f"from {n} workers ({t_sc:.2f} s), decompressed and Adam-stepped "
-                   f"({t_dec_adam:.2f} s); scaled to {n}x{n} worker chunks + {n} server chunks"),
+        "sample": (f"{repeats} x (one {L}-element worker chunk compressed ({t_wc:.2f} s), one chunk "
+                   f"server-reduced from {n} workers ({t_sc:.2f} s), decompressed and Adam-stepped "
+                   f"({t_dec_adam:.2f} s)), mean scaled to {n}x{n} worker chunks + {n} server "
+                   f"chunks"),
     }
 
 
