@@ -320,3 +320,14 @@ def test_warmup_fullsize():
     assert np.all(np.abs(k.astype(np.float64) - want) <= 1e-6 * np.abs(want)), "k_l"
     del lw, g, mh
     _free()
+
+
+def test_64_workers_largest_worker_count():
+    """The largest worker count (64, the general-n server) on a 2^27-element
+    buffer: 4096 (worker, chunk) pairs of 2^21 elements, about 69 GB of
+    momenta and error states."""
+    wl = C.Workload(name="adam_2^27_x64", kind="adam", N=1 << 27, n=64, steps=2,
+                    segments=[1 << 20] * 128, seg_names=[f"seg{i}" for i in range(128)],
+                    sigma_mode="loguniform_1e-5_1e-2", seed=6)
+    _run_adam_fullsize(wl, steps=2, pairs=[(0, 0), (17, 40), (63, 63)], server_chunks=[0, 63],
+                       sample=1 << 18)
