@@ -1,0 +1,248 @@
+"""Python access to the C++ oracle (oracle/cpp/onebit_ref.cpp).
+
+TEST INFRASTRUCTURE ONLY, like the rest of this package: the tests, the smoke
+check and the benchmark's CPU baseline use it; the GPU library never does.
+
+The C++ oracle computes what the numpy oracle computes, as plain loops, fast
+enough for whole full-size buffers. The functions below only marshal numpy
+arrays into it and have the numpy oracle's names and return keys. Rows
+(workers) and server chunks are independent, so ``threads`` > 1 runs them in
+parallel Python threads (ctypes releases the interpreter lock during each
+call); that changes no arithmetic.
+"""
+
+from __future__ import annotations
+
+import ctypes as ct
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+from typing import Dict, Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "cpp", "onebit_ref.cpp")
+LIB = os.path.join(HERE, "cpp", "libonebit_ref.so")
+FLAGS = ["-O2", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+         "-Wall", "-Wextra", "-Werror"]
+
+_lib = None
+f32 = np.float32
+_P = ct.c_void_p
+_I64, _I32, _U32, _U64, _F = ct.c_int64, ct.c_int32, ct.c_uint32, ct.c_uint64, ct.c_float
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the C++ oracle with g++ (plain binary32 arithmetic, nothing
+    contracted or reassociated) and return the library path."""
+    tmp = LIB + ".tmp"
+    cmd = ["g++", *FLAGS, "-o", tmp, SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        build()
+    lib = ct.CDLL(LIB)
+    sig = {
+        "ref_mean_abs": (_F, [_P, _I64]),
+        "ref_worker_compress_row": (_I32, [_P, _P, _P, _P, _I64, _I32, _F, _I32, _I32,
+                                           _P, _P, _P, _P]),
+        "ref_local_momentum": (None, [_P, _P, _F, _I64, _P]),
+        "ref_server_chunk": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
+                                    _P, _P, _P, _P, _P]),
+        "ref_decompress": (_I32, [_P, _P, _P, _I64, _I32, _P]),
+        "ref_adam_frozen_step": (None, [_P, _P, _P, _I64, _F, _F]),
+        "ref_lamb_frozen_step": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _P, _P, _P,
+                                        _F, _F, _F, _F, _F, _F, _F, _I32, _P, _P, _P, _P]),
+        "ref_philox4x32_10": (None, [_P, _P, _P]),
+        "ref_uniform": (_F, [_U64, _U64, _U32]),
+        "ref_int8_quantize": (_I32, [_P, _P, _I64, _I64, _I32, _U64, _U32, _I64,
+                                     _P, _P, _P, _P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _arr(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def _ok(rc: int, what: str) -> None:
+    if rc:
+        raise ValueError(f"C++ oracle rejected the arguments of {what}")
+
+
+def _run(fn, items, threads: int) -> None:
+    if threads <= 1:
+        for it in items:
+            fn(it)
+        return
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        for _ in ex.map(fn, items):
+            pass
+
+
+def mean_abs_f32(x) -> np.float32:
+    x = _arr(x, f32).ravel()
+    if x.size == 0:
+        raise ValueError("mean of an empty chunk")
+    if x.size >= 1 << 39:
+        raise ValueError("too many terms for the per-exponent accumulation")
+    return f32(load().ref_mean_abs(_p(x), x.size))
+
+
+def worker_compress(m, e, clip: float = 0.0, reset: bool = False, k=None,
+                    unit_scale: bool = False, err_ratio=None, threads: int = 1,
+                    keep_gc: bool = True) -> Dict[str, np.ndarray]:
+    """Same contract as ``oracle.onebit.worker_compress``. With
+    ``keep_gc=False`` the compensated values are not returned (one row of
+    scratch instead of n)."""
+    lib = load()
+    m = _arr(m, f32)
+    n, N = m.shape
+    e = None if reset else _arr(e, f32)
+    k = None if k is None else _arr(k, f32)
+    ratio = None if err_ratio is None else _arr(err_ratio, f32)
+    e_out = np.empty((n, N), dtype=f32)
+    bits = np.zeros((n, N // 32), dtype=np.uint32)
+    s = np.empty((n, n), dtype=f32)
+    gc = np.empty((n, N), dtype=f32) if keep_gc else None
+
+    def row(i):
+        g_i = gc[i] if keep_gc else np.empty(N, dtype=f32)
+        rc = lib.ref_worker_compress_row(_p(m[i]), None if e is None else _p(e[i]), _p(k),
+                                         _p(ratio), N, n, float(clip), int(bool(reset)),
+                                         int(bool(unit_scale)), _p(g_i), _p(e_out[i]),
+                                         _p(bits[i]), _p(s[i]))
+        _ok(rc, "worker_compress")
+
+    _run(row, range(n), threads)
+    out = {"bits": bits, "s": s, "e": e_out}
+    if keep_gc:
+        out["gc"] = gc
+    return out
+
+
+def local_momentum(g, mbar_prev, beta1: float) -> np.ndarray:
+    lib = load()
+    g = _arr(g, f32)
+    mb = _arr(mbar_prev, f32)
+    out = np.empty_like(g)
+    for i in range(g.shape[0]):
+        lib.ref_local_momentum(_p(g[i]), _p(mb), float(beta1), g.shape[1], _p(out[i]))
+    return out
+
+
+def server_reduce(bits, s, E, reset: bool = False, unit_scale: bool = False, err_ratio=None,
+                  threads: int = 1) -> Dict[str, np.ndarray]:
+    """Same contract as ``oracle.onebit.server_reduce``."""
+    lib = load()
+    bits = _arr(bits, np.uint32)
+    s = _arr(s, f32)
+    n = s.shape[0]
+    N = bits.shape[1] * 32
+    E = None if reset else _arr(E, f32)
+    ratio = None if err_ratio is None else _arr(err_ratio, f32)
+    out = {"avg": np.empty(N, dtype=f32), "g2": np.empty(N, dtype=f32),
+           "E": np.empty(N, dtype=f32), "S": np.empty(n, dtype=f32),
+           "bits": np.zeros(N // 32, dtype=np.uint32)}
+
+    def chunk(c):
+        rc = lib.ref_server_chunk(_p(bits), _p(s), _p(E), _p(ratio), N, n, c, int(bool(reset)),
+                                  int(bool(unit_scale)), _p(out["avg"]), _p(out["g2"]),
+                                  _p(out["E"]), _p(out["bits"]), _p(out["S"]))
+        _ok(rc, "server_reduce")
+
+    _run(chunk, range(n), threads)
+    return out
+
+
+def decompress(sbits, S, k=None) -> np.ndarray:
+    lib = load()
+    sbits = _arr(sbits, np.uint32)
+    S = _arr(S, f32)
+    N = sbits.size * 32
+    k = None if k is None else _arr(k, f32)
+    out = np.empty(N, dtype=f32)
+    _ok(lib.ref_decompress(_p(sbits), _p(S), _p(k), N, S.size, _p(out)), "decompress")
+    return out
+
+
+def adam_frozen_step(x, m, v, lr: float, eps: float) -> np.ndarray:
+    lib = load()
+    x = _arr(x, f32).copy()
+    m, v = _arr(m, f32), _arr(v, f32)
+    lib.ref_adam_frozen_step(_p(x), _p(m), _p(v), x.size, float(lr), float(eps))
+    return x
+
+
+def lamb_frozen_step(x, m, m_prev, v_f, v_tw, seg_off, c_avg, r_prev, c_prev,
+                     lr: float, eps: float, beta1: float, beta2: float,
+                     thr: float, r_min: float, r_max: float,
+                     use_c_t: bool = False) -> Dict[str, np.ndarray]:
+    """Same contract as ``oracle.optim.lamb_frozen_step`` (without ``g``)."""
+    lib = load()
+    x = _arr(x, f32).copy()
+    v = _arr(v_f, f32).copy()
+    m, m_prev, v_tw = _arr(m, f32), _arr(m_prev, f32), _arr(v_tw, f32)
+    off = _arr(seg_off, np.int64)
+    L = off.size - 1
+    c_avg, r_prev, c_prev = _arr(c_avg, f32), _arr(r_prev, f32), _arr(c_prev, f32)
+    R, r, c, rho = (np.empty(L, dtype=f32) for _ in range(4))
+    rc = lib.ref_lamb_frozen_step(_p(x), _p(m), _p(m_prev), _p(v), _p(v_tw), _p(off), L,
+                                  _p(c_avg), _p(r_prev), _p(c_prev), float(lr), float(eps),
+                                  float(beta1), float(beta2), float(thr), float(r_min),
+                                  float(r_max), int(bool(use_c_t)), _p(R), _p(r), _p(c), _p(rho))
+    _ok(rc, "lamb_frozen_step")
+    return {"x": x, "v": v, "R": R, "r": r, "c": c, "err_ratio": rho}
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    lib = load()
+    ctr = _arr(ctr, np.uint32).reshape(-1, 4)
+    key = np.broadcast_to(_arr(key, np.uint32), (ctr.shape[0], 2)).copy()
+    out = np.empty_like(ctr)
+    for i in range(ctr.shape[0]):
+        lib.ref_philox4x32_10(_p(ctr[i]), _p(key[i]), _p(out[i]))
+    return out
+
+
+def uniforms(J0: int, count: int, seed: int, step: int) -> np.ndarray:
+    lib = load()
+    return np.array([lib.ref_uniform(J0 + j, seed, step) for j in range(count)], dtype=f32)
+
+
+def int8_sr(g, e, seed: int, step: int, block: int = 256, J0: int = 0,
+            rounding: str = "stochastic") -> Dict[str, np.ndarray]:
+    """Same contract as ``oracle.int8.int8_sr`` (without ``gc``)."""
+    lib = load()
+    g = _arr(g, f32).ravel()
+    e = None if e is None else _arr(e, f32).ravel()
+    N = g.size
+    nb = 1 if block == 0 else N // block
+    codes = np.empty(N, dtype=np.int8)
+    scales = np.empty(nb, dtype=f32)
+    deq = np.empty(N, dtype=f32)
+    e_out = np.empty(N, dtype=f32)
+    mode = {"stochastic": 0, "nearest": 1}[rounding]
+    rc = lib.ref_int8_quantize(_p(g), _p(e), N, block, mode, seed, step, J0, _p(codes),
+                               _p(scales), _p(deq), _p(e_out))
+    _ok(rc, "int8_sr")
+    return {"codes": codes, "scales": scales, "deq": deq, "e": e_out}

@@ -1,0 +1,292 @@
+"""The C++ oracle (oracle/cpp) against the numpy oracle and against the pins
+that do not depend on either.
+
+Two implementations written apart from the same passages must agree bit for
+bit on every output, on seeded inputs that reach each branch: resets, the
+clamp (with NaN and infinities), layer coefficients, the unit scale, the
+step-ratio factor, ties of the mean, subnormals, every INT8 block size and
+both roundings. The independent pins (brute force with fractions for the
+exact mean, numpy's own float64 -> float32 rounding for midpoints, closed
+forms of the server) run on the C++ oracle directly.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import cref as R
+from oracle import int8 as I
+from oracle import onebit as O
+from oracle import optim as P
+from oracle import philox as PH
+from oracle.exact import mean_abs_f32
+from tests.test_oracle_int8 import _tie_block
+
+F32 = np.float32
+
+
+def _eq(got, want, name):
+    got, want = np.asarray(got), np.asarray(want)
+    assert got.shape == want.shape, (name, got.shape, want.shape)
+    if got.dtype == np.float32:
+        g, w = got.view(np.uint32), want.astype(F32).view(np.uint32)
+        nan_g, nan_w = np.isnan(got), np.isnan(want)
+        assert np.array_equal(nan_g, nan_w), f"{name}: NaN positions differ"
+        ok = (g == w) | nan_g
+    else:
+        ok = got == want
+    assert ok.all(), f"{name}: {int((~ok).sum())} of {ok.size} differ"
+
+
+def _momentum(rng, n, N, spread=3.0):
+    sig = 10.0 ** rng.uniform(-5, -5 + spread, size=-(-N // 64))
+    return (rng.standard_normal((n, N)) * np.repeat(sig, 64)[None, :N]).astype(F32)
+
+
+# ------------------------------------------------------------------ exact mean
+
+@pytest.mark.parametrize("L", [1, 2, 3, 64, 257, 4096])
+def test_mean_matches_fractions(L):
+    rng = np.random.default_rng(100 + L)
+    trials = 30 if L <= 257 else 4
+    for trial in range(trials):
+        x = (rng.standard_normal(L) * 10.0 ** rng.uniform(-40, 35, size=L)).astype(F32)
+        if trial % 3 == 0:
+            x[: L // 2] = F32(1e-45) * rng.integers(0, 50, size=L // 2)  # subnormals
+        exact = sum((abs(Fraction(float(v))) for v in x), Fraction(0)) / L
+        got = R.mean_abs_f32(x)
+        # nearest binary32 to the exact mean: no binary32 value is closer
+        lo, hi = np.nextafter(got, F32(0)), np.nextafter(got, F32(np.inf))
+        d = abs(Fraction(float(got)) - exact)
+        assert d <= abs(Fraction(float(lo)) - exact)
+        if np.isfinite(hi):
+            assert d <= abs(Fraction(float(hi)) - exact)
+        assert got == mean_abs_f32(x)
+
+
+def test_mean_ties_round_to_even():
+    """Two neighbours a < b average to their exact midpoint: the tie goes to
+    the one with an even significand (numpy's float64 -> float32 cast, one
+    correct rounding, gives the same)."""
+    rng = np.random.default_rng(7)
+    a = rng.integers(1, 0x7F000000, size=4000, dtype=np.int64).astype(np.uint32)
+    lo, hi = a.view(F32), (a + 1).view(F32)
+    for x, y in zip(lo, hi):
+        got = R.mean_abs_f32(np.array([x, y], dtype=F32))
+        mid = (float(x) + float(y)) / 2  # exact in float64
+        assert got == F32(mid)
+        even = x if (x.view(np.uint32) & 1) == 0 else y
+        assert got == even
+
+
+def test_mean_special_values():
+    assert np.isnan(R.mean_abs_f32(np.array([1.0, np.nan, np.inf], dtype=F32)))
+    assert R.mean_abs_f32(np.array([1.0, -np.inf], dtype=F32)) == np.inf
+    assert R.mean_abs_f32(np.zeros(96, dtype=F32)) == 0.0
+    assert R.mean_abs_f32(np.array([-0.0, 0.0], dtype=F32)) == 0.0
+    big = np.full(1000, np.finfo(F32).max, dtype=F32)
+    assert R.mean_abs_f32(big) == np.finfo(F32).max  # the sum overflows binary32, the mean not
+    tiny = np.array([2.0 ** -149, 0.0], dtype=F32)  # mean 2^-150: a tie with 0, even is 0
+    assert R.mean_abs_f32(tiny) == 0.0
+    tiny3 = np.array([2.0 ** -149, 2.0 ** -148], dtype=F32)  # 1.5 units: tie, even is 2 units
+    assert R.mean_abs_f32(tiny3) == F32(2.0 ** -148)
+
+
+def test_mean_matches_numpy_oracle_random():
+    rng = np.random.default_rng(11)
+    for trial in range(200):
+        L = int(rng.integers(1, 3000))
+        x = (rng.standard_normal(L) * 10.0 ** rng.uniform(-45, 38, size=L)).astype(F32)
+        assert R.mean_abs_f32(x).view(np.uint32) == mean_abs_f32(x).view(np.uint32), trial
+
+
+# --------------------------------------------------------------- worker, server
+
+CASES = [
+    dict(n=1, N=64 * 7, clip=0.0),
+    dict(n=4, N=4 * 3136, clip=0.0),
+    dict(n=3, N=3 * 64 * 33, clip=2e-3),
+    dict(n=8, N=8 * 1024, clip=0.0, k=True),
+    dict(n=5, N=5 * 64 * 9, clip=0.0, unit=True),
+    dict(n=6, N=6 * 640, clip=1e-3, ratio=True),
+    dict(n=16, N=16 * 128, clip=0.0, k=True, ratio=True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_compressed_steps_match_numpy_oracle(case):
+    """Four steps of worker compress, server reduce and decompression, the
+    first a reset, fed back into themselves on both sides."""
+    cfg = CASES[case]
+    n, N = cfg["n"], cfg["N"]
+    rng = np.random.default_rng(case)
+    k = (10.0 ** rng.uniform(-1, 1, size=N)).astype(F32) if cfg.get("k") else None
+    unit = cfg.get("unit", False)
+    e_np = e_c = np.zeros((n, N), dtype=F32)
+    E_np = E_c = np.zeros(N, dtype=F32)
+    for t in range(4):
+        m = _momentum(rng, n, N)
+        if t == 2:
+            m[0, :5] = [np.nan, np.inf, -np.inf, 0.0, -0.0]  # clamp and sign conventions
+        ratio = (1.0 + 0.1 * rng.standard_normal(N)).astype(F32) if cfg.get("ratio") else None
+        reset = t == 0
+        w_np = O.worker_compress(m, e_np, clip=cfg["clip"], reset=reset, k=k, unit_scale=unit,
+                                 err_ratio=ratio)
+        w_c = R.worker_compress(m, e_c, clip=cfg["clip"], reset=reset, k=k, unit_scale=unit,
+                                err_ratio=ratio, threads=2)
+        for key in ("gc", "bits", "s", "e"):
+            _eq(w_c[key], w_np[key], f"case {case} t={t} worker {key}")
+        s_np = O.server_reduce(w_np["bits"], w_np["s"], E_np, reset=reset, unit_scale=unit,
+                               err_ratio=ratio)
+        s_c = R.server_reduce(w_c["bits"], w_c["s"], E_c, reset=reset, unit_scale=unit,
+                              err_ratio=ratio, threads=3)
+        for key in ("avg", "g2", "bits", "S", "E"):
+            _eq(s_c[key], s_np[key], f"case {case} t={t} server {key}")
+        _eq(R.decompress(s_c["bits"], s_c["S"], k), O.decompress(s_np["bits"], s_np["S"], k),
+            f"case {case} t={t} decompressed")
+        e_np, e_c, E_np, E_c = w_np["e"], w_c["e"], s_np["E"], s_c["E"]
+
+
+def test_worker_without_compensated_values():
+    rng = np.random.default_rng(3)
+    m = _momentum(rng, 4, 4 * 256)
+    a = R.worker_compress(m, None, reset=True)
+    b = R.worker_compress(m, None, reset=True, keep_gc=False, threads=4)
+    assert "gc" not in b
+    for key in ("bits", "s", "e"):
+        _eq(b[key], a[key], key)
+
+
+def test_server_closed_forms():
+    """n = 1: the server sees +-s, so with a zero error its output is the
+    worker's own scaled sign (scale s, same bits). Unanimous workers with
+    scales s_i average to sum(s_i)/n on every element."""
+    rng = np.random.default_rng(5)
+    m = _momentum(rng, 1, 64 * 40)
+    w = R.worker_compress(m, None, reset=True)
+    s = R.server_reduce(w["bits"], w["s"], None, reset=True)
+    assert np.array_equal(s["bits"], w["bits"][0])
+    assert s["S"][0] == w["s"][0, 0]
+    assert not s["E"].any()
+    n, N = 4, 4 * 64
+    bits = np.full((n, N // 32), 0xFFFFFFFF, dtype=np.uint32)
+    sc = np.array([[1.0, 2.0, 4.0, 8.0]] * n, dtype=F32).T.copy()  # s[i][c] = 2^i
+    out = R.server_reduce(bits, sc, None, reset=True)
+    assert np.all(out["avg"] == F32(15.0 / 4))
+    assert np.all(out["S"] == F32(15.0 / 4))
+
+
+def test_local_momentum_matches_numpy_oracle():
+    rng = np.random.default_rng(9)
+    g = _momentum(rng, 3, 3 * 512)
+    mb = _momentum(rng, 1, 3 * 512)[0]
+    _eq(R.local_momentum(g, mb, 0.9), O.local_momentum(g, mb, 0.9), "local momentum")
+
+
+# ----------------------------------------------------------------------- steps
+
+def test_adam_step_matches_numpy_oracle_and_closed_form():
+    rng = np.random.default_rng(12)
+    N = 4096
+    x = rng.standard_normal(N).astype(F32)
+    m = _momentum(rng, 1, N)[0]
+    v = (np.abs(rng.standard_normal(N)) * 1e-6 + 1e-8).astype(F32)
+    v[:4] = [0.0, np.inf, 1.0, 4.0]
+    _eq(R.adam_frozen_step(x, m, v, 6e-5, 1e-6), P.adam_frozen_step(x, m, v, 6e-5, 1e-6), "adam")
+    # v = 4, eps = 0, m = 2, lr = 1/2: x - 1/2 * (2 / 2) = x - 1/2, exact
+    out = R.adam_frozen_step(np.array([3.0] * 4, F32), np.array([2.0] * 4, F32),
+                             np.array([4.0] * 4, F32), 0.5, 0.0)
+    assert np.all(out == F32(2.5))
+
+
+@pytest.mark.parametrize("use_c_t", [False, True])
+def test_lamb_step_matches_numpy_oracle(use_c_t):
+    rng = np.random.default_rng(20 + use_c_t)
+    sizes = [64, 1, 300, 1024, 4, 0, 77, 2048]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    N = int(off[-1])
+    L = len(sizes)
+    x = rng.standard_normal(N).astype(F32)
+    m_prev = _momentum(rng, 1, N)[0]
+    m = (0.9 * m_prev + 0.1 * _momentum(rng, 1, N)[0]).astype(F32)
+    v_tw = (np.abs(rng.standard_normal(N)) * 1e-6 + 1e-9).astype(F32)
+    v_f = (v_tw * (1 + 0.3 * rng.standard_normal(N))).astype(F32)
+    # a layer of ratio 0/0 (no valid ratio: r stays), one with signed zeros
+    lay1 = slice(off[1], off[2])
+    m[lay1], m_prev[lay1], v_f[lay1], v_tw[lay1] = 0, 0, 0, 0
+    lay4 = slice(off[4], off[5])
+    v_tw[lay4] = [-0.0, -0.0, 0.0, -0.0]  # the first valid ratio is -0, a later one +0
+    c_avg = (10.0 ** rng.uniform(-1, 1, size=L)).astype(F32)
+    r_prev = (1 + 0.2 * rng.standard_normal(L)).astype(F32)
+    c_prev = (c_avg * r_prev).astype(F32)
+    args = (x, m, m_prev, v_f, v_tw, off, c_avg, r_prev, c_prev, 1e-3, 1e-6, 0.9, 0.999,
+            0.1, 0.5, 4.0, use_c_t)
+    got, want = R.lamb_frozen_step(*args), P.lamb_frozen_step(*args)
+    for key in ("x", "v", "R", "r", "c", "err_ratio"):
+        _eq(got[key], want[key], f"lamb {key}")
+    assert np.isnan(got["R"][1]) and got["r"][1] == r_prev[1]
+    assert got["R"][4] == 0.0 and not np.signbit(got["R"][4])
+    lo = (F32(0.9) * r_prev).astype(F32)
+    hi = (F32(1.1) * r_prev).astype(F32)
+    assert np.all(got["r"] >= np.maximum(np.minimum(lo, 4.0), 0.5))
+    assert np.all(got["r"] <= np.minimum(np.maximum(hi, 0.5), 4.0))
+
+
+def test_lamb_gradient_round_trip():
+    """With v_f = 0 and beta2 = 0 the fresh variance is g^2 of the rebuilt
+    gradient; m built from m_prev and a dyadic g by exact operations gives
+    back that g exactly (beta1 = 1/2)."""
+    rng = np.random.default_rng(30)
+    N = 256
+    g = (rng.integers(-64, 64, size=N) / 64).astype(F32)
+    m_prev = (rng.integers(-64, 64, size=N) / 64).astype(F32)
+    m = (F32(0.5) * m_prev + F32(0.5) * g).astype(F32)
+    off = np.array([0, N], dtype=np.int64)
+    one = np.ones(1, F32)
+    out = R.lamb_frozen_step(np.zeros(N, F32), m, m_prev, np.zeros(N, F32), np.ones(N, F32), off,
+                             one, one, one, 0.0, 0.0, 0.5, 0.0, 0.1, 0.5, 4.0)
+    assert np.array_equal(out["v"], (g * g).astype(F32))
+
+
+# ------------------------------------------------------------------ INT8, Philox
+
+def test_philox_matches_numpy_oracle():
+    rng = np.random.default_rng(40)
+    ctr = rng.integers(0, 2**32, size=(300, 4), dtype=np.uint64).astype(np.uint32)
+    key = rng.integers(0, 2**32, size=(300, 2), dtype=np.uint64).astype(np.uint32)
+    got = np.stack([R.philox4x32_10(ctr[i], key[i])[0] for i in range(300)])
+    assert np.array_equal(got, PH.philox4x32_10(ctr, key))
+    J0 = (1 << 33) + 5
+    assert np.array_equal(R.uniforms(J0, 40, 0xDEADBEEF12345, 7), PH.uniforms(J0, 40, 0xDEADBEEF12345, 7))
+
+
+@pytest.mark.parametrize("block", [0, 64, 128, 256, 512, 1024])
+@pytest.mark.parametrize("rounding", ["stochastic", "nearest"])
+def test_int8_matches_numpy_oracle(block, rounding):
+    rng = np.random.default_rng(block + (rounding == "nearest"))
+    N = 4096
+    g = rng.laplace(0, 1e-3, size=N).astype(F32)
+    out_idx = rng.choice(N, size=4, replace=False)
+    g[out_idx] *= 100  # outliers
+    e = (rng.standard_normal(N) * 1e-5).astype(F32)
+    g[64:128] = 0.0
+    e[64:128] = 0.0  # an all-zero block of 64: scale 0, code 0
+    g[300], g[301] = np.nan, -0.0
+    J0 = 12345 * 4
+    for err in (None, e):
+        got = R.int8_sr(g, err, 77, 3, block=block, J0=J0, rounding=rounding)
+        want = I.int8_sr(g, err, 77, 3, block=block, J0=J0, rounding=rounding)
+        for key in ("codes", "scales", "deq", "e"):
+            _eq(got[key], want[key], f"int8 block={block} {rounding} {key}")
+        assert np.all(np.abs(got["codes"].astype(int)) <= 127)
+
+
+def test_int8_fraction_equal_to_its_uniform_rounds_down():
+    """The pin of the numpy oracle's comparison u < p, on the C++ oracle: a
+    fraction equal to its own uniform rounds down, one 2^-24 above it up."""
+    for above, code in ((False, 0), (True, 1)):
+        g, idx = _tie_block(5, 2, above=above)
+        out = R.int8_sr(g, None, 5, 2)
+        assert out["scales"][0] == 1
+        assert np.all(out["codes"][idx] == code)
