@@ -6,6 +6,11 @@ pages' equations.  Only the tests, the smoke check and the benchmark's CPU
 baseline may import it; the library under ``momentum_compression_amd`` never
 does, and shares no code, table or helper with it.
 
+``cpp/onebit_ref.cpp`` (through ``cref``) is a second, plain C++
+implementation of the compressed phase, written apart from the numpy one as
+straight loops; the tests hold the two bit-identical and use the C++ one where
+whole full-size buffers are checked.
+
 Conventions (each module states the passage it follows):
 
 * All buffers are IEEE binary32 and every elementwise operation is one

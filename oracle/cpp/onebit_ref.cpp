@@ -61,10 +61,13 @@ bool sign_bit(float x) { return x >= 0.0f; }
 
 void put_bit(uint32_t* words, int64_t j, bool b) {
     const uint32_t mask = 1u << (j & 31);
-    if (b)
-        words[j >> 5] |= mask;
-    else
-        words[j >> 5] &= ~mask;
+    words[j >> 5] = (words[j >> 5] & ~mask) | (b ? mask : 0u);
+}
+
+// the scaled sign q = +s for bit 1, -s for bit 0
+float scaled_sign(bool b, float s) {
+    const float q[2] = {-s, s};
+    return q[b ? 1 : 0];
 }
 
 bool get_bit(const uint32_t* words, int64_t j) { return (words[j >> 5] >> (j & 31)) & 1u; }
@@ -163,11 +166,12 @@ float round_units(const Big& Q, uint64_t r, uint64_t d) {
 extern "C" {
 
 // binary32 nearest to mean(|x_0|, ..., |x_{L-1}|), exact, ties to even.
-// NaN anywhere gives NaN; otherwise an infinity gives +inf. L >= 1.
+// NaN anywhere gives NaN; otherwise an infinity gives +inf. 1 <= L < 2^39.
 float ref_mean_abs(const float* x, int64_t L) {
     bool nan = false, inf = false;
-    // per-exponent sums of significands: each below 2^24 * 2^31 = 2^55
-    uint64_t per_exp[256];
+    // per-exponent sums of significands, in 4 interleaved sets (integer sums:
+    // the split changes nothing); each below 2^24 * 2^39 = 2^63 for L < 2^39
+    uint64_t per_exp[4][256];
     std::memset(per_exp, 0, sizeof per_exp);
     for (int64_t j = 0; j < L; ++j) {
         uint32_t b;
@@ -180,14 +184,15 @@ float ref_mean_abs(const float* x, int64_t L) {
             else inf = true;
             continue;
         }
-        per_exp[E] += E ? (M | 0x800000u) : M;
+        per_exp[j & 3][E] += E ? (M | 0x800000u) : M;
     }
     if (nan) return NAN;
     if (inf) return INFINITY;
     Big S;
     big_zero(S);
-    for (int E = 0; E < 255; ++E)
-        if (per_exp[E]) big_add_shifted(S, per_exp[E], E ? E - 1 : 0);
+    for (int set = 0; set < 4; ++set)
+        for (int E = 0; E < 255; ++E)
+            if (per_exp[set][E]) big_add_shifted(S, per_exp[set][E], E ? E - 1 : 0);
     const uint64_t r = big_div_small(S, (uint64_t)L);
     return round_units(S, r, (uint64_t)L);
 }
@@ -225,8 +230,7 @@ int ref_worker_compress_row(const float* m, const float* e_in, const float* k,
     for (int32_t c = 0; c < n; ++c) {
         const float sc = unit ? 1.0f : ref_mean_abs(gc + c * L, L);
         s[c] = sc;
-        for (int64_t j = c * L; j < (c + 1) * L; ++j)
-            e_out[j] = sign_bit(gc[j]) ? gc[j] - sc : gc[j] + sc;
+        for (int64_t j = c * L; j < (c + 1) * L; ++j) e_out[j] = gc[j] - scaled_sign(sign_bit(gc[j]), sc);
     }
     return 0;
 }
@@ -263,7 +267,7 @@ int ref_server_chunk(const uint32_t* wbits, const float* ws, const float* E_in,
         float acc = 0.0f;
         for (int32_t i = 0; i < n; ++i) {
             const float si = ws[(int64_t)i * n + c];
-            acc = acc + (get_bit(wbits + (int64_t)i * W, j) ? si : -si);
+            acc = acc + scaled_sign(get_bit(wbits + (int64_t)i * W, j), si);
         }
         const float a = acc / nf;
         float e = 0.0f;
@@ -277,8 +281,7 @@ int ref_server_chunk(const uint32_t* wbits, const float* ws, const float* E_in,
     }
     const float sc = unit ? 1.0f : ref_mean_abs(g2 + c * L, L);
     S[c] = sc;
-    for (int64_t j = c * L; j < (c + 1) * L; ++j)
-        E_out[j] = sign_bit(g2[j]) ? g2[j] - sc : g2[j] + sc;
+    for (int64_t j = c * L; j < (c + 1) * L; ++j) E_out[j] = g2[j] - scaled_sign(sign_bit(g2[j]), sc);
     return 0;
 }
 
@@ -288,11 +291,12 @@ int ref_decompress(const uint32_t* sbits, const float* S, const float* k, int64_
                    float* out) {
     if (n < 1 || N % (64 * (int64_t)n)) return 1;
     const int64_t L = N / n;
-    for (int64_t j = 0; j < N; ++j) {
-        const float sc = S[j / L];
-        float v = get_bit(sbits, j) ? sc : -sc;
-        if (k) v = v / k[j];
-        out[j] = v;
+    for (int32_t c = 0; c < n; ++c) {
+        for (int64_t j = c * L; j < (c + 1) * L; ++j) {
+            float v = scaled_sign(get_bit(sbits, j), S[c]);
+            if (k) v = v / k[j];
+            out[j] = v;
+        }
     }
     return 0;
 }

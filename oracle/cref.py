@@ -24,8 +24,10 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "cpp", "onebit_ref.cpp")
 LIB = os.path.join(HERE, "cpp", "libonebit_ref.so")
-FLAGS = ["-O2", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
-         "-Wall", "-Wextra", "-Werror"]
+# -fno-math-errno only stops sqrt from setting errno; no flag here changes a
+# binary32 result
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+         "-fno-math-errno", "-Wall", "-Wextra", "-Werror"]
 
 _lib = None
 f32 = np.float32
@@ -138,6 +140,28 @@ def worker_compress(m, e, clip: float = 0.0, reset: bool = False, k=None,
     if keep_gc:
         out["gc"] = gc
     return out
+
+
+def worker_compress_row(m_row, e_row, n: int, clip: float = 0.0, reset: bool = False, k=None,
+                        unit_scale: bool = False, err_ratio=None) -> Dict[str, np.ndarray]:
+    """One worker's row of ``worker_compress`` (the row holds n chunks):
+    gc, bits (N/32), s (n) and the new error, which is written over ``e_row``
+    when that is a contiguous float32 array (a copy otherwise)."""
+    lib = load()
+    m_row = _arr(m_row, f32)
+    N = m_row.size
+    e = None if reset else _arr(e_row, f32)
+    e_out = e if e is not None else np.empty(N, dtype=f32)
+    k = None if k is None else _arr(k, f32)
+    ratio = None if err_ratio is None else _arr(err_ratio, f32)
+    gc = np.empty(N, dtype=f32)
+    bits = np.zeros(N // 32, dtype=np.uint32)
+    s = np.empty(n, dtype=f32)
+    rc = lib.ref_worker_compress_row(_p(m_row), _p(e), _p(k), _p(ratio), N, n, float(clip),
+                                     int(bool(reset)), int(bool(unit_scale)), _p(gc), _p(e_out),
+                                     _p(bits), _p(s))
+    _ok(rc, "worker_compress_row")
+    return {"gc": gc, "bits": bits, "s": s, "e": e_out}
 
 
 def local_momentum(g, mbar_prev, beta1: float) -> np.ndarray:

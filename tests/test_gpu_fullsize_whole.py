@@ -1,0 +1,228 @@
+"""Whole-buffer parity at full size, against the C++ oracle.
+
+The sampled full-size tests check chosen (worker, chunk) pairs with the numpy
+oracle. Here the C++ oracle, run on its own state from the same seeded
+inputs, gives every output of every step on the whole buffer, and each one
+must be bit-identical:
+* the 1-bit Adam step the bench times on BERT-Large 335M x 8 (compress,
+  server without decompression, decompression inside the Adam pass): all 8
+  workers' sign words, scales and compensated values, the server's, the
+  decompressed momentum and every parameter, over three steps;
+* the same step on GPT 1.3B x 16 with the clamp, across a periodic reset:
+  whole rows of three workers, the server, the decompressed momentum and
+  every parameter;
+* the 1-bit LAMB step on the 302-tensor buffer x 16 (compress with the layer
+  coefficients, server, LAMB step from the sign words): all 16 workers, the
+  server, m / k, x, the fresh variance and every layer's ratio, r_t, c_t and
+  error factor, over two steps.
+"""
+
+import gc
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+from momentum_compression_amd.state import LambState, OneBitGroup
+from oracle import cref as R
+from tests._gpu import device, host, same_f32
+from workloads import configs as C
+from workloads import synth as S
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
+F32 = np.float32
+THREADS = 16  # host threads for the oracle's independent rows and chunks
+
+
+def _free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _need(dev, nbytes):
+    free = torch.cuda.mem_get_info(dev)[0]
+    if free < nbytes:
+        pytest.skip(f"needs {nbytes / 2**30:.0f} GiB of device memory, {free / 2**30:.0f} free")
+
+
+def _same(got: np.ndarray, want: np.ndarray, name: str) -> None:
+    """Bit identity of a whole buffer; on a mismatch the differing elements
+    go through the float check, which names how many differ and by how much."""
+    got, want = np.ascontiguousarray(got), np.ascontiguousarray(want)
+    assert got.shape == want.shape, (name, got.shape, want.shape)
+    if got.dtype == np.float32:
+        gb, wb = got.view(np.uint32), want.view(np.uint32)
+        if np.array_equal(gb, wb):
+            return
+        bad = np.flatnonzero(gb != wb)
+        same_f32(got.ravel()[bad], want.ravel()[bad],
+                 f"{name}: {bad.size} of {got.size} differ, first at {bad[0]}")
+    else:
+        got = got.view(np.uint32) if got.dtype == np.int32 else got
+        neq = got != want
+        assert not neq.any(), f"{name}: {int(neq.sum())} of {neq.size} differ, first at " \
+                              f"{np.flatnonzero(neq)[0]}"
+
+
+def _workers(grp, m, e_state, reset, tag, clip=0.0, k=None, rows=None):
+    """The oracle's worker compression of the given rows (all by default; rows
+    in parallel), each compared with the GPU's state, sign words and scales
+    as it completes. ``e_state`` ([n, N] float32, or a dict row -> [N]) is
+    updated in place. Returns the oracle's sign words and scales of all rows
+    (rows not computed keep the GPU's)."""
+    n = grp.n
+    rows = range(n) if rows is None else rows
+    gpu_bits, gpu_s = host(grp.bits), host(grp.scales)
+    bits, s = gpu_bits.copy(), gpu_s.copy()
+    with ThreadPoolExecutor(max_workers=THREADS) as ex:
+        futs = {i: ex.submit(R.worker_compress_row, host(m[i]), e_state[i], n, clip, reset, k)
+                for i in rows}
+        for i in rows:
+            w = futs.pop(i).result()
+            _same(host(grp.ef[i]), w["gc"], f"{tag} worker {i} compensated values")
+            _same(gpu_bits[i], w["bits"], f"{tag} worker {i} sign words")
+            _same(gpu_s[i], w["s"], f"{tag} worker {i} scales")
+            bits[i], s[i] = w["bits"], w["s"]
+            if not np.shares_memory(w["e"], e_state[i]):  # a reset starts a fresh error
+                e_state[i][...] = w["e"]
+            del w
+    return bits, s
+
+
+def _server(grp, bits, s, E_state, reset, tag):
+    sv = R.server_reduce(bits, s, E_state, reset=reset, threads=THREADS)
+    _same(host(grp.sv_bits), sv["bits"], f"{tag} server sign words")
+    _same(host(grp.sv_scales), sv["S"], f"{tag} server scales")
+    _same(host(grp.sv_ef), sv["g2"], f"{tag} server compensated values")
+    return sv
+
+
+def test_bert_large_335M_x8_bench_step_whole_buffer():
+    dev = device()
+    wl = C.get("bert_large_335M_x8")
+    N, n = wl.N, wl.n
+    _need(dev, int(n * N * 4 * 2.2 + N * 4 * 6))
+    print(f"[whole] {wl.name} N={N} n={n}", flush=True)
+    sig = S.per_element(S.segment_sigmas(wl), wl, dev)
+    grp = OneBitGroup(N, n, dev, clip=wl.clip, reset_interval=wl.reset_interval)
+    x = S.params(wl, dev)
+    v = S.frozen_variance(wl, dev)
+    m = torch.empty((n, N), dtype=torch.float32, device=dev)
+    x_ref, v_h = host(x).copy(), host(v)
+    e_ref = np.zeros((n, N), dtype=F32)
+    E_ref = np.zeros(N, dtype=F32)
+    for t in (1, 2, 3):
+        S.momentum(wl, t, dev, sigma_elem=sig, out=m)
+        first = t == 1
+        reset = first or grp.is_reset(t)
+        grp.compress(m, t, first=first)
+        grp.server(t, first=first, decompress=False)
+        grp.adam_step_packed(x, v, wl.lr, wl.eps, decompress=True)
+        torch.cuda.synchronize()
+        tag = f"{wl.name} t={t}"
+        bits, s = _workers(grp, m, e_ref, reset, tag, clip=wl.clip)
+        sv = _server(grp, bits, s, E_ref, reset, tag)
+        E_ref = sv["E"]
+        mbar = R.decompress(sv["bits"], sv["S"])
+        _same(host(grp.mbar), mbar, f"{tag} decompressed momentum")
+        x_ref = R.adam_frozen_step(x_ref, mbar, v_h, wl.lr, wl.eps)
+        _same(host(x), x_ref, f"{tag} parameters")
+        del sv, mbar, bits, s
+        print(f"[whole] {tag} ok", flush=True)
+    del grp, x, v, m, sig, e_ref, E_ref, x_ref
+    _free()
+
+
+def test_gpt_1_3B_x16_whole_rows_server_and_step():
+    """GPT 1.3B x 16 with the 2.0 clamp, across the reset at t = 2000: whole
+    rows of workers 0, 7 and 15 free-running (all 16 rows' host copies would
+    pass 250 GB), and the server, the decompressed momentum and every
+    parameter on the whole buffer. The server takes the GPU's sign words and
+    scales of the other workers, checked bit for bit wherever computed."""
+    dev = device()
+    wl = C.get("gpt_1.3B_x16")
+    N, n = wl.N, wl.n
+    _need(dev, int(n * N * 4 * 2.2 + N * 4 * 6))
+    print(f"[whole] {wl.name} N={N} n={n}", flush=True)
+    sig = S.per_element(S.segment_sigmas(wl), wl, dev)
+    grp = OneBitGroup(N, n, dev, clip=wl.clip, reset_interval=wl.reset_interval)
+    x = S.params(wl, dev)
+    v = S.frozen_variance(wl, dev)
+    m = torch.empty((n, N), dtype=torch.float32, device=dev)
+    x_ref, v_h = host(x).copy(), host(v)
+    rows = (0, 7, 15)
+    e_ref = {i: np.zeros(N, dtype=F32) for i in rows}
+    E_ref = np.zeros(N, dtype=F32)
+    t0 = 1999
+    for t in (t0, t0 + 1, t0 + 2):
+        S.momentum(wl, t, dev, sigma_elem=sig, out=m)
+        first = t == t0
+        reset = first or grp.is_reset(t)
+        grp.compress(m, t, first=first)
+        grp.server(t, first=first, decompress=False)
+        grp.adam_step_packed(x, v, wl.lr, wl.eps, decompress=True)
+        torch.cuda.synchronize()
+        tag = f"{wl.name} t={t}{' (reset)' if reset else ''}"
+        bits, s = _workers(grp, m, e_ref, reset, tag, clip=wl.clip, rows=rows)
+        sv = _server(grp, bits, s, E_ref, reset, tag)
+        E_ref = sv["E"]
+        mbar = R.decompress(sv["bits"], sv["S"])
+        _same(host(grp.mbar), mbar, f"{tag} decompressed momentum")
+        x_ref = R.adam_frozen_step(x_ref, mbar, v_h, wl.lr, wl.eps)
+        _same(host(x), x_ref, f"{tag} parameters")
+        del sv, mbar, bits, s
+        print(f"[whole] {tag} ok", flush=True)
+    del grp, x, v, m, sig, e_ref, E_ref, x_ref
+    _free()
+
+
+def test_bert_large_lamb_302t_x16_whole_buffer():
+    dev = device()
+    wl = C.get("bert_large_lamb_302t_x16")
+    N, n = wl.N, wl.n
+    _need(dev, int(n * N * 4 * 2.2 + N * 4 * 12))
+    print(f"[whole] {wl.name} N={N} n={n} segments={len(wl.segments)}", flush=True)
+    off = np.array(C.segment_offsets(wl.segments), dtype=np.int64)
+    k, c_avg = S.lamb_tables(wl)
+    k_el = np.repeat(k, np.diff(off)).astype(F32)
+    sig = S.per_element(S.segment_sigmas(wl), wl, dev)
+    off_d, k_d = torch.from_numpy(off).to(dev), torch.from_numpy(k).to(dev)
+    grp = OneBitGroup(N, n, dev, seg_off=off_d, seg_k=k_d)
+    st = LambState.create(S.params(wl, dev), S.frozen_variance(wl, dev),
+                          S.lamb_prev_momentum(wl, dev, sig), off_d,
+                          torch.from_numpy(c_avg).to(dev))
+    m = torch.empty((n, N), dtype=torch.float32, device=dev)
+    x_ref, vf_ref, mp_ref = host(st.x).copy(), host(st.v_fresh).copy(), host(st.m_prev).copy()
+    r_ref, c_ref = host(st.r).copy(), host(st.c).copy()
+    v_tw = host(st.v_frozen)
+    e_ref = np.zeros((n, N), dtype=F32)
+    E_ref = np.zeros(N, dtype=F32)
+    for t in (1, 2):
+        S.momentum(wl, t, dev, sigma_elem=sig, out=m)
+        first = t == 1
+        grp.compress(m, t, first=first)
+        grp.server(t, first=first, decompress=False)
+        st.step_packed(grp.sv_bits, grp.sv_scales, k_d, n, wl.lr, wl.eps, wl.beta1, wl.beta2,
+                       wl.r_threshold, wl.r_min, wl.r_max)
+        torch.cuda.synchronize()
+        tag = f"lamb t={t}"
+        bits, s = _workers(grp, m, e_ref, first, tag, k=k_el)
+        sv = _server(grp, bits, s, E_ref, first, tag)
+        E_ref = sv["E"]
+        mbar = R.decompress(sv["bits"], sv["S"], k_el)
+        _same(host(st.m_prev), mbar, f"{tag} decompressed momentum / k")
+        out = R.lamb_frozen_step(x_ref, mbar, mp_ref, vf_ref, v_tw, off, c_avg, r_ref, c_ref,
+                                 wl.lr, wl.eps, wl.beta1, wl.beta2, wl.r_threshold, wl.r_min,
+                                 wl.r_max)
+        _same(host(st.x), out["x"], f"{tag} parameters")
+        _same(host(st.v_fresh), out["v"], f"{tag} fresh variance")
+        _same(host(st.ratio_max), out["R"], f"{tag} layer max ratio")
+        _same(host(st.r), out["r"], f"{tag} r_t")
+        _same(host(st.c), out["c"], f"{tag} c_t")
+        _same(host(st.err_ratio), out["err_ratio"], f"{tag} error factor c_(t-1)/c_t")
+        x_ref, vf_ref, r_ref, c_ref, mp_ref = out["x"], out["v"], out["r"], out["c"], mbar
+        del sv, bits, s, out
+        print(f"[whole] {tag} ok", flush=True)
+    del grp, st, m, sig, e_ref, E_ref
+    _free()
