@@ -15,9 +15,9 @@ Prints ONE JSON line.  `value` = compressed worker elements per second
 (n * N per step).  `roofline` reports the dominant kernel (worker compress)
 against 8 TB/s of HBM using its algorithmic bytes (12.125 B per element:
 read m and the error state, write the state and 1 bit), with the duration
-measured by HIP events on the launch stream.  `cpu_baseline` times the CPU
-oracle on a bounded sample of the same step (one worker chunk compressed,
-one chunk reduced, decompressed and stepped) and scales it to the full step.
+measured by HIP events on the launch stream.  `cpu_baseline` times the C++
+CPU oracle on one thread over one whole step of the same workload, on the
+bench's own inputs.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
     python bench.py --only compress|server|decompress_adam|decompress|adam|copy  # profiling aid
@@ -91,46 +91,36 @@ def read_traffic(launch_elems: int):
     return (fetch + write) * 1024.0
 
 
-def cpu_baseline(wl, seed: int = 11, repeats: int = 3):
-    """Time the CPU oracle on one chunk of each stage, `repeats` times on fresh
-    inputs (about 10 s of one core at the 335M x 8 chunk size), and scale the
-    mean to a whole step."""
-    import numpy as np
+def cpu_baseline(wl, m, x, v):
+    """Time the C++ oracle on one whole step of the workload on one thread:
+    compress of all n workers, the n server chunks, decompression and the
+    Adam step. A first (reset) step runs before it, so the timed step carries
+    the error like the steps on the GPU. m [n, N], x, v [N]: host float32."""
+    from oracle import cref as R
 
-    from oracle import onebit as O
-    from oracle import optim as P
-
-    L, n = wl.L, wl.n
-    t_wc = t_sc = t_dec_adam = 0.0
-    for r in range(repeats):
-        rng = np.random.default_rng(seed + r)
-        m = (rng.standard_normal(L) * 1e-3).astype(np.float32)[None, :]
+    n, N = wl.n, wl.N
+    R.load()
+    secs = []
+    e = E = None
+    for t in (1, 2):
+        reset = t == 1
         t0 = time.perf_counter()
-        w = O.worker_compress(m, np.zeros_like(m), reset=True)
-        t_wc += time.perf_counter() - t0
-        bits_c = np.stack([w["bits"][0]] * n)
-        bits_c[1::2] = ~bits_c[1::2]
-        s_c = np.full(n, w["s"][0, 0], dtype=np.float32)
-        t0 = time.perf_counter()
-        sv = O.server_chunk(bits_c, s_c, np.zeros(L, dtype=np.float32), reset=True)
-        t_sc += time.perf_counter() - t0
-        x = (rng.standard_normal(L) * 0.02).astype(np.float32)
-        v = np.abs(rng.standard_normal(L) * 1e-6).astype(np.float32) + np.float32(1e-8)
-        t0 = time.perf_counter()
-        mbar = O.decompress(sv["bits"], np.array([sv["S"]], dtype=np.float32))
-        P.adam_frozen_step(x, mbar, v, 6e-5, 1e-6)
-        t_dec_adam += time.perf_counter() - t0
-    t_wc, t_sc, t_dec_adam = t_wc / repeats, t_sc / repeats, t_dec_adam / repeats
-    t_step = n * n * t_wc + n * (t_sc + t_dec_adam)
+        w = R.worker_compress(m, e, clip=wl.clip, reset=reset, keep_gc=False)
+        sv = R.server_reduce(w["bits"], w["s"], E, reset=reset)
+        mbar = R.decompress(sv["bits"], sv["S"])
+        x = R.adam_frozen_step(x, mbar, v, wl.lr, wl.eps)
+        secs.append(time.perf_counter() - t0)
+        e, E = w["e"], sv["E"]
+        del w, sv, mbar
     return {
-        "value": n * wl.N / t_step,
+        "value": n * N / secs[1],
         "unit": "elements/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"{repeats} x (one {L}-element worker chunk compressed ({t_wc:.2f} s), one chunk "
-                   f"server-reduced from {n} workers ({t_sc:.2f} s), decompressed and Adam-stepped "
-                   f"({t_dec_adam:.2f} s)), mean scaled to {n}x{n} worker chunks + {n} server "
-                   f"chunks"),
+        "sample": (f"one whole step of the workload ({n} x {N} worker elements: compress, "
+                   f"{n} server chunks, decompression, Adam) by the C++ oracle on one thread, "
+                   f"on the bench's own inputs copied from the GPU, after a first (reset) "
+                   f"step; reset step {secs[0]:.1f} s, timed step {secs[1]:.1f} s"),
     }
 
 
@@ -716,6 +706,13 @@ def main() -> int:
     }
     out["diagnostics"] = diagnostics
     out["rows"] = {"decompress_then_adam": separate}
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on one step of the workload", file=sys.stderr,
+              flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, m.cpu().numpy(), x.cpu().numpy(),
+                                           v.cpu().numpy())
+    else:
+        out["cpu_baseline"] = None
     if not args.no_rows:
         del grp, m, x, v
         torch.cuda.empty_cache()
@@ -725,11 +722,6 @@ def main() -> int:
                        "warmup": measure_warmup(max(3, args.steps // 2), 1),
                        "gpt_1.3B_x16": measure_gpt(max(3, args.steps // 2), 1),
                        "copy_reference": measure_copy(max(3, args.steps // 2), 1)})
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl)
-    else:
-        out["cpu_baseline"] = None
     print(json.dumps(out))
     return 0
 

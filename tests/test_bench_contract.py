@@ -47,8 +47,12 @@ def test_source_hash_ignores_comments(tmp_path, monkeypatch):
 
 
 def test_cpu_baseline_record():
+    from workloads import synth as S
+
     wl = C.get("adam_2^20_x4")
-    rec = bench.cpu_baseline(wl)
+    m = S.momentum(wl, 1, "cpu").numpy()
+    x, v = S.params(wl, "cpu").numpy(), S.frozen_variance(wl, "cpu").numpy()
+    rec = bench.cpu_baseline(wl, m, x, v)
     assert rec["kind"] == "oracle" and rec["cores"] == 1 and rec["unit"] == "elements/s"
     assert rec["value"] > 0
-    assert f"{wl.L}-element" in rec["sample"]
+    assert f"{wl.n} x {wl.N} worker elements" in rec["sample"]
