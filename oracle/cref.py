@@ -254,19 +254,33 @@ def uniforms(J0: int, count: int, seed: int, step: int) -> np.ndarray:
 
 
 def int8_sr(g, e, seed: int, step: int, block: int = 256, J0: int = 0,
-            rounding: str = "stochastic") -> Dict[str, np.ndarray]:
-    """Same contract as ``oracle.int8.int8_sr`` (without ``gc``)."""
+            rounding: str = "stochastic", threads: int = 1) -> Dict[str, np.ndarray]:
+    """Same contract as ``oracle.int8.int8_sr`` (without ``gc``). With
+    ``threads`` > 1 and a block size, whole blocks are split into that many
+    slices, each keyed by its own first global index."""
     lib = load()
     g = _arr(g, f32).ravel()
     e = None if e is None else _arr(e, f32).ravel()
     N = g.size
+    if block and N % block:
+        raise ValueError("length must be a multiple of the block")
     nb = 1 if block == 0 else N // block
     codes = np.empty(N, dtype=np.int8)
     scales = np.empty(nb, dtype=f32)
     deq = np.empty(N, dtype=f32)
     e_out = np.empty(N, dtype=f32)
     mode = {"stochastic": 0, "nearest": 1}[rounding]
-    rc = lib.ref_int8_quantize(_p(g), _p(e), N, block, mode, seed, step, J0, _p(codes),
-                               _p(scales), _p(deq), _p(e_out))
-    _ok(rc, "int8_sr")
+    parts = 1 if block == 0 else max(1, min(threads, nb))
+    cuts = [(nb * p // parts) * (block or N) for p in range(parts + 1)]
+
+    def part(p):
+        a, b = cuts[p], cuts[p + 1]
+        if a == b:
+            return
+        rc = lib.ref_int8_quantize(_p(g[a:b]), None if e is None else _p(e[a:b]), b - a, block,
+                                   mode, seed, step, J0 + a, _p(codes[a:b]),
+                                   _p(scales[a // (block or N):]), _p(deq[a:b]), _p(e_out[a:b]))
+        _ok(rc, "int8_sr")
+
+    _run(part, range(parts), threads)
     return {"codes": codes, "scales": scales, "deq": deq, "e": e_out}

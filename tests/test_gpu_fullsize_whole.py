@@ -14,7 +14,11 @@ must be bit-identical:
 * the 1-bit LAMB step on the 302-tensor buffer x 16 (compress with the layer
   coefficients, server, LAMB step from the sign words): all 16 workers, the
   server, m / k, x, the fresh variance and every layer's ratio, r_t, c_t and
-  error factor, over two steps.
+  error factor, over two steps;
+* the fused step from gradients on 335M x 8 (momentum formed inside
+  compression from the packed global momentum), over two steps;
+* INT8 with Philox stochastic rounding on 2^30 elements, over two
+  error-feedback steps.
 """
 
 import gc
@@ -24,6 +28,7 @@ import numpy as np
 import pytest
 import torch
 
+from momentum_compression_amd import onebit as ob
 from momentum_compression_amd.state import LambState, OneBitGroup
 from oracle import cref as R
 from tests._gpu import device, host, same_f32
@@ -68,15 +73,17 @@ def _same(got: np.ndarray, want: np.ndarray, name: str) -> None:
 def _workers(grp, m, e_state, reset, tag, clip=0.0, k=None, rows=None):
     """The oracle's worker compression of the given rows (all by default; rows
     in parallel), each compared with the GPU's state, sign words and scales
-    as it completes. ``e_state`` ([n, N] float32, or a dict row -> [N]) is
-    updated in place. Returns the oracle's sign words and scales of all rows
-    (rows not computed keep the GPU's)."""
+    as it completes. ``m`` is the [n, N] device momentum, or a function that
+    returns row i's host momentum. ``e_state`` ([n, N] float32, or a dict
+    row -> [N]) is updated in place. Returns the oracle's sign words and
+    scales of all rows (rows not computed keep the GPU's)."""
+    row_m = m if callable(m) else (lambda i: host(m[i]))
     n = grp.n
     rows = range(n) if rows is None else rows
     gpu_bits, gpu_s = host(grp.bits), host(grp.scales)
     bits, s = gpu_bits.copy(), gpu_s.copy()
     with ThreadPoolExecutor(max_workers=THREADS) as ex:
-        futs = {i: ex.submit(R.worker_compress_row, host(m[i]), e_state[i], n, clip, reset, k)
+        futs = {i: ex.submit(R.worker_compress_row, row_m(i), e_state[i], n, clip, reset, k)
                 for i in rows}
         for i in rows:
             w = futs.pop(i).result()
@@ -225,4 +232,81 @@ def test_bert_large_lamb_302t_x16_whole_buffer():
         del sv, bits, s, out
         print(f"[whole] {tag} ok", flush=True)
     del grp, st, m, sig, e_ref, E_ref
+    _free()
+
+
+def test_bert_large_335M_x8_from_gradients_whole_buffer():
+    """The fused entry points on the whole buffer: each worker's momentum is
+    formed inside compression from its gradient and the previous step's
+    packed global momentum (all-zero words and scales before the first
+    step), and the Adam step reads the packed momentum."""
+    dev = device()
+    wl = C.get("bert_large_335M_x8")
+    N, n = wl.N, wl.n
+    _need(dev, int(n * N * 4 * 2.2 + N * 4 * 6))
+    print(f"[whole] fused {wl.name}", flush=True)
+    sig = S.per_element(S.segment_sigmas(wl), wl, dev)
+    grp = OneBitGroup(N, n, dev)
+    x = S.params(wl, dev)
+    v = S.frozen_variance(wl, dev)
+    g = torch.empty((n, N), dtype=torch.float32, device=dev)
+    x_ref, v_h = host(x).copy(), host(v)
+    e_ref = np.zeros((n, N), dtype=F32)
+    E_ref = np.zeros(N, dtype=F32)
+    sbits_prev, S_prev = np.zeros(N // 32, dtype=np.uint32), np.zeros(n, dtype=F32)
+    for t in (1, 2):
+        S.momentum(wl, 100 + t, dev, sigma_elem=sig, out=g)
+        first = t == 1
+        grp.compress_grad(g, t, wl.beta1, first=first)
+        grp.server(t, first=first, decompress=True)
+        grp.adam_step_packed(x, v, wl.lr, wl.eps)
+        torch.cuda.synchronize()
+        tag = f"fused t={t}"
+        mbar_prev = R.decompress(sbits_prev, S_prev)
+
+        def momentum_row(i):
+            return R.local_momentum(host(g[i])[None, :], mbar_prev, wl.beta1)[0]
+
+        bits, s = _workers(grp, momentum_row, e_ref, first, tag)
+        sv = _server(grp, bits, s, E_ref, first, tag)
+        E_ref = sv["E"]
+        mbar = R.decompress(sv["bits"], sv["S"])
+        _same(host(grp.mbar), mbar, f"{tag} decompressed momentum")
+        x_ref = R.adam_frozen_step(x_ref, mbar, v_h, wl.lr, wl.eps)
+        _same(host(x), x_ref, f"{tag} parameters")
+        sbits_prev, S_prev = sv["bits"], sv["S"]
+        del sv, mbar, bits, s
+        print(f"[whole] {tag} ok", flush=True)
+    del grp, x, v, g, sig, e_ref, E_ref, x_ref
+    _free()
+
+
+def test_int8_2_30_whole_buffer():
+    """INT8 block stochastic rounding on 2^30 Laplace gradients with outliers,
+    two error-feedback steps: every code, block scale, dequantised value and
+    residual."""
+    dev = device()
+    N, block, seed = 1 << 30, 256, 4
+    _need(dev, N * 18)
+    print(f"[whole] int8 N={N}", flush=True)
+    err = torch.zeros(N, device=dev)
+    codes = torch.empty(N, dtype=torch.int8, device=dev)
+    scales = torch.empty(N // block, device=dev)
+    deq = torch.empty(N, device=dev)
+    g = torch.empty(N, device=dev)
+    e_ref = np.zeros(N, dtype=F32)
+    for step in (1, 2):
+        S.laplace_gradient(N, step, seed, dev, out=g)
+        ob.int8_sr_quantize(g, err, codes, scales, deq, N, block, seed, step)
+        torch.cuda.synchronize()
+        o = R.int8_sr(host(g), e_ref, seed, step, block, threads=THREADS)
+        tag = f"int8 step {step}"
+        _same(host(codes), o["codes"], f"{tag} codes")
+        _same(host(scales), o["scales"], f"{tag} block scales")
+        _same(host(deq), o["deq"], f"{tag} dequantised")
+        _same(host(err), o["e"], f"{tag} residual")
+        e_ref = o["e"]
+        del o
+        print(f"[whole] {tag} ok", flush=True)
+    del err, codes, scales, deq, g, e_ref
     _free()

@@ -290,3 +290,14 @@ def test_int8_fraction_equal_to_its_uniform_rounds_down():
         out = R.int8_sr(g, None, 5, 2)
         assert out["scales"][0] == 1
         assert np.all(out["codes"][idx] == code)
+
+
+def test_int8_threaded_slices_equal_one_call():
+    rng = np.random.default_rng(50)
+    g = rng.laplace(0, 1e-3, size=256 * 37).astype(F32)
+    e = (rng.standard_normal(g.size) * 1e-5).astype(F32)
+    one = R.int8_sr(g, e, 9, 4, block=256, J0=1 << 33)
+    for threads in (2, 5, 37, 64):
+        many = R.int8_sr(g, e, 9, 4, block=256, J0=1 << 33, threads=threads)
+        for key in ("codes", "scales", "deq", "e"):
+            _eq(many[key], one[key], f"int8 threads={threads} {key}")
