@@ -301,3 +301,83 @@ def test_int8_threaded_slices_equal_one_call():
         many = R.int8_sr(g, e, 9, 4, block=256, J0=1 << 33, threads=threads)
         for key in ("codes", "scales", "deq", "e"):
             _eq(many[key], one[key], f"int8 threads={threads} {key}")
+
+
+# ------------------------------------- pins the pages fix, run on the C++ oracle
+
+def _frac(x):
+    return Fraction(float(x))
+
+
+def test_telescoping_exact_on_dyadic_inputs_both_levels():
+    """With inputs on a 2^-8 grid no operation rounds, so what was sent plus
+    what is still owed equals what came in, exactly: per worker element
+    sum_t q_t + e_T = sum_t m_t, and at the server sum_t Q_t + E_T =
+    sum_t avg_t (1-bit Adam article, section 2.1, error compensation)."""
+    rng = np.random.default_rng(60)
+    n, N, T = 2, 128, 2  # each step's mean over 64 adds 6 bits: two steps stay exact
+    L = N // n
+    e = E = None
+    sum_m = np.zeros((n, N), dtype=object)
+    sum_q = np.zeros((n, N), dtype=object)
+    sum_avg = np.zeros(N, dtype=object)
+    sum_Q = np.zeros(N, dtype=object)
+    sum_m[:] = Fraction(0)
+    sum_q[:] = Fraction(0)
+    sum_avg[:] = Fraction(0)
+    sum_Q[:] = Fraction(0)
+    for t in range(T):
+        m = (rng.integers(-255, 256, size=(n, N)) / 256.0).astype(F32)
+        w = R.worker_compress(m, e, reset=t == 0)
+        sv = R.server_reduce(w["bits"], w["s"], E, reset=t == 0)
+        for i in range(n):
+            for j in range(N):
+                sign = 1 if w["gc"][i, j] >= 0 else -1
+                sum_q[i, j] += sign * _frac(w["s"][i, j // L])
+                sum_m[i, j] += _frac(m[i, j])
+        for j in range(N):
+            sign = 1 if sv["g2"][j] >= 0 else -1
+            sum_Q[j] += sign * _frac(sv["S"][j // L])
+            sum_avg[j] += _frac(sv["avg"][j])
+        e, E = w["e"], sv["E"]
+    for i in range(n):
+        for j in range(N):
+            assert sum_q[i, j] + _frac(e[i, j]) == sum_m[i, j], (i, j)
+    for j in range(N):
+        assert sum_Q[j] + _frac(E[j]) == sum_avg[j], j
+
+
+def test_sign_words_match_numpy_packbits():
+    """Bit j of a row is (g'_j >= 0), least significant bit first: the same
+    bytes as numpy's packbits with little bit order, read as little-endian
+    32-bit words. The decompression inverts it: its sign is the bit."""
+    rng = np.random.default_rng(61)
+    n, N = 3, 3 * 64 * 5
+    m = _momentum(rng, n, N)
+    m[0, :4] = [0.0, -0.0, np.nan, -1e-30]
+    w = R.worker_compress(m, None, reset=True)
+    for i in range(n):
+        want = np.packbits(w["gc"][i] >= 0, bitorder="little").view("<u4")
+        assert np.array_equal(w["bits"][i], want)
+    S = np.ones(1, dtype=F32)
+    dec = R.decompress(w["bits"][0], S)
+    assert np.array_equal(dec > 0, w["gc"][0] >= 0)
+
+
+def test_error_is_the_nearest_binary32_to_g_minus_q():
+    """e = g' - q rounded once: no binary32 value lies closer to the exact
+    difference (checked with fractions on a sample)."""
+    rng = np.random.default_rng(62)
+    n, N = 2, 2 * 640
+    m = _momentum(rng, n, N, spread=6.0)
+    w = R.worker_compress(m, None, reset=True)
+    L = N // n
+    for i in range(n):
+        for j in range(0, N, 7):
+            s = _frac(w["s"][i, j // L])
+            g = _frac(w["gc"][i, j])
+            exact = g - (s if w["gc"][i, j] >= 0 else -s)
+            got = w["e"][i, j]
+            d = abs(_frac(got) - exact)
+            for nb in (np.nextafter(got, F32(-np.inf)), np.nextafter(got, F32(np.inf))):
+                assert d <= abs(_frac(nb) - exact)
