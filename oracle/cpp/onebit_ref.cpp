@@ -44,6 +44,10 @@
 //   [-127, 127], dequantisation, error feedback.
 // * Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2,
 //   3" (SC'11), section 4: the Philox4x32 bijection with 10 rounds.
+// * 1-bit Adam article, section 2.1 and its warmup setting: uncompressed Adam
+//   steps first. 1-bit LAMB page, algorithm paragraph: LAMB's layer
+//   coefficient and its warmup average c_avg; layer-scaling paragraph: k_l
+//   from the average momentum norm at the end of warmup.
 //
 // Readings where the pages are silent are the ones the numpy oracle states
 // (chunk = N/n consecutive elements; ascending worker order in the server
@@ -159,6 +163,108 @@ float round_units(const Big& Q, uint64_t r, uint64_t d) {
     // top <= 2^24: exact in binary32; the exponent stays in range because a
     // mean of finite values never exceeds the largest of them
     return (float)std::ldexp((double)top, lo - 149);
+}
+
+// ------------------------------------------------- exact binary64 sums
+//
+// A wide unsigned integer (2304 bits) that holds any exact sum of up to 2^31
+// non-negative binary64 values, or of squares of binary32 values, in units of
+// a fixed power of two; it is rounded once to binary64, ties to even.
+
+constexpr int kWide = 72;
+
+struct Wide {
+    uint32_t w[kWide];
+};
+
+void wide_zero(Wide& a) { std::memset(a.w, 0, sizeof a.w); }
+
+void wide_add_shifted(Wide& a, uint64_t v, int shift) {
+    const int limb = shift / 32;
+    unsigned __int128 part = (unsigned __int128)v << (shift % 32);
+    uint64_t carry = 0;
+    for (int i = limb; i < kWide; ++i) {
+        const uint64_t s = (uint64_t)a.w[i] + (uint64_t)(uint32_t)part + carry;
+        part >>= 32;
+        a.w[i] = (uint32_t)s;
+        carry = s >> 32;
+        if (part == 0 && carry == 0) break;
+    }
+}
+
+bool wide_bit(const Wide& a, int i) { return (a.w[i / 32] >> (i % 32)) & 1u; }
+
+// binary64 nearest to a * 2^unit_exp, ties to even (no overflow for the sums
+// formed here)
+double wide_to_double(const Wide& a, int unit_exp) {
+    int p = 0;
+    for (int i = kWide - 1; i >= 0; --i)
+        if (a.w[i]) {
+            p = 32 * i + (32 - __builtin_clz(a.w[i]));
+            break;
+        }
+    if (p == 0) return 0.0;
+    // keep 53 significant bits, never finer than 2^-1074
+    int lo = p > 53 ? p - 53 : 0;
+    if (unit_exp + lo < -1074) lo = -1074 - unit_exp;
+    uint64_t top = 0;
+    for (int i = p - 1; i >= lo; --i) top = (top << 1) | (wide_bit(a, i) ? 1u : 0u);
+    if (lo > 0 && wide_bit(a, lo - 1)) {
+        bool rest = false;
+        for (int i = 0; i < lo - 1 && !rest; ++i) rest = wide_bit(a, i);
+        if (rest || (top & 1)) top += 1;
+    }
+    return std::ldexp((double)top, unit_exp + lo);
+}
+
+// sum of squares of binary32 values, exact, rounded once to binary64. A
+// square of M * 2^e (M < 2^24, e >= -149) is M^2 * 2^(2e), an integer number
+// of units 2^-298.
+// (a NaN gives NaN, else an infinity gives +inf)
+double exact_sumsq(const float* x, int64_t n) {
+    Wide acc;
+    wide_zero(acc);
+    bool nan = false, inf = false;
+    for (int64_t j = 0; j < n; ++j) {
+        uint32_t b;
+        std::memcpy(&b, &x[j], 4);
+        b &= 0x7FFFFFFFu;
+        const uint32_t E = b >> 23;
+        if (E == 255) {
+            if (b & 0x7FFFFFu) nan = true;
+            else inf = true;
+            continue;
+        }
+        const uint64_t M = E ? ((b & 0x7FFFFFu) | 0x800000u) : (b & 0x7FFFFFu);
+        const int e = E ? (int)E - 150 : -149;
+        if (M) wide_add_shifted(acc, M * M, 2 * e + 298);
+    }
+    if (nan) return NAN;
+    if (inf) return INFINITY;
+    return wide_to_double(acc, -298);
+}
+
+// sum of non-negative binary64 values, exact, rounded once to binary64
+// (units 2^-1074; a NaN gives NaN, else an infinity gives +inf)
+double exact_sum_f64(const double* x, int64_t n) {
+    Wide acc;
+    wide_zero(acc);
+    bool nan = false, inf = false;
+    for (int64_t j = 0; j < n; ++j) {
+        uint64_t b;
+        std::memcpy(&b, &x[j], 8);
+        const int E = (int)(b >> 52) & 0x7FF;
+        if (E == 0x7FF) {
+            if (b & 0xFFFFFFFFFFFFFull) nan = true;
+            else inf = true;
+            continue;
+        }
+        const uint64_t M = E ? ((b & 0xFFFFFFFFFFFFFull) | (1ull << 52)) : (b & 0xFFFFFFFFFFFFFull);
+        if (M) wide_add_shifted(acc, M, E ? E - 1 : 0);
+    }
+    if (nan) return NAN;
+    if (inf) return INFINITY;
+    return wide_to_double(acc, -1074);
 }
 
 }  // namespace
@@ -457,6 +563,103 @@ int ref_int8_quantize(const float* g, const float* e, int64_t N, int64_t block, 
             if (e_out) e_out[j] = gc - dq;
         }
     }
+    return 0;
+}
+
+// ---------------------------------------------------------------- warmup
+//
+// Readings where the pages are silent: no bias correction and no weight
+// decay; u = m / (sqrt(v) + eps) from the new moments; LAMB's coefficient is
+// c_l = ||x_l|| / ||u_l|| with x before the update, 1 when either norm is 0,
+// the squared norms exact sums rounded once to binary64 and the ratio
+// sqrt(Sx) / sqrt(Su) in binary64 rounded once to binary32; c_avg starts at
+// the first coefficient, then c_avg <- beta_c c_avg + (1 - beta_c) c; k_l =
+// (mean over layers with a_l > 0 of a_l) / a_l with the RMS
+// a_l = sqrt(||m_l||^2 / d_l) in binary64, 1 for a layer with a_l = 0.
+
+namespace {
+
+void moments(float& m, float& v, float g, float beta1, float beta2) {
+    const float omb1 = 1.0f - beta1, omb2 = 1.0f - beta2;
+    const float m1 = beta1 * m;
+    const float m2 = omb1 * g;
+    const float v1 = beta2 * v;
+    const float v2 = omb2 * (g * g);
+    m = m1 + m2;
+    v = v1 + v2;
+}
+
+float direction(float m, float v, float eps) {
+    const float den = std::sqrt(v) + eps;
+    return m / den;
+}
+
+}  // namespace
+
+// The exact sums on their own, for pins against an independent exact sum.
+double ref_exact_sumsq(const float* x, int64_t n) { return exact_sumsq(x, n); }
+double ref_exact_sum_f64(const double* x, int64_t n) { return exact_sum_f64(x, n); }
+
+// One uncompressed Adam step on the averaged gradient g (x, m, v in place).
+void ref_adam_warmup_step(float* x, float* m, float* v, const float* g, int64_t N, float lr,
+                          float eps, float beta1, float beta2) {
+    for (int64_t j = 0; j < N; ++j) {
+        moments(m[j], v[j], g[j], beta1, beta2);
+        const float u = direction(m[j], v[j], eps);
+        x[j] = x[j] - lr * u;
+    }
+}
+
+// One uncompressed LAMB step over layers [seg_off[l], seg_off[l+1]) (x, m, v
+// in place); writes each layer's coefficient c and advances c_avg (c_avg_in
+// NULL: the first step, which starts the average at c).
+int ref_lamb_warmup_step(float* x, float* m, float* v, const float* g, const int64_t* seg_off,
+                         int32_t n_seg, float lr, float eps, float beta1, float beta2,
+                         const float* c_avg_in, float beta_c, float* c, float* c_avg_out) {
+    if (n_seg < 1) return 1;
+    const float ombc = 1.0f - beta_c;
+    for (int32_t l = 0; l < n_seg; ++l) {
+        const int64_t a = seg_off[l], b = seg_off[l + 1];
+        if (b < a) return 1;
+        float* u = new float[b > a ? b - a : 1];
+        for (int64_t j = a; j < b; ++j) {
+            moments(m[j], v[j], g[j], beta1, beta2);
+            u[j - a] = direction(m[j], v[j], eps);
+        }
+        const double sx = exact_sumsq(x + a, b - a);
+        const double su = exact_sumsq(u, b - a);
+        const float cl = (sx == 0.0 || su == 0.0) ? 1.0f : (float)(std::sqrt(sx) / std::sqrt(su));
+        c[l] = cl;
+        const float step = lr * cl;
+        for (int64_t j = a; j < b; ++j) x[j] = x[j] - step * u[j - a];
+        delete[] u;
+        if (c_avg_in) {
+            const float p = beta_c * c_avg_in[l];
+            const float q = ombc * cl;
+            c_avg_out[l] = p + q;
+        } else {
+            c_avg_out[l] = cl;
+        }
+    }
+    return 0;
+}
+
+// k_l of every layer from the momentum m at the end of warmup.
+int ref_momentum_scale(const float* m, const int64_t* seg_off, int32_t n_seg, float* k) {
+    if (n_seg < 1) return 1;
+    double* rms = new double[n_seg];
+    double* valid = new double[n_seg];
+    int32_t nv = 0;
+    for (int32_t l = 0; l < n_seg; ++l) {
+        const int64_t a = seg_off[l], b = seg_off[l + 1];
+        rms[l] = 0.0;
+        if (b > a) rms[l] = std::sqrt(exact_sumsq(m + a, b - a) / (double)(b - a));
+        if (rms[l] > 0.0) valid[nv++] = rms[l];
+    }
+    const double mean = nv ? exact_sum_f64(valid, nv) / (double)nv : 0.0;
+    for (int32_t l = 0; l < n_seg; ++l) k[l] = rms[l] > 0.0 ? (float)(mean / rms[l]) : 1.0f;
+    delete[] rms;
+    delete[] valid;
     return 0;
 }
 

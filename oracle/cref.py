@@ -69,6 +69,12 @@ def load():
         "ref_uniform": (_F, [_U64, _U64, _U32]),
         "ref_int8_quantize": (_I32, [_P, _P, _I64, _I64, _I32, _U64, _U32, _I64,
                                      _P, _P, _P, _P]),
+        "ref_adam_warmup_step": (None, [_P, _P, _P, _P, _I64, _F, _F, _F, _F]),
+        "ref_lamb_warmup_step": (_I32, [_P, _P, _P, _P, _P, _I32, _F, _F, _F, _F, _P, _F,
+                                        _P, _P]),
+        "ref_momentum_scale": (_I32, [_P, _P, _I32, _P]),
+        "ref_exact_sumsq": (ct.c_double, [_P, _I64]),
+        "ref_exact_sum_f64": (ct.c_double, [_P, _I64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -284,3 +290,52 @@ def int8_sr(g, e, seed: int, step: int, block: int = 256, J0: int = 0,
 
     _run(part, range(parts), threads)
     return {"codes": codes, "scales": scales, "deq": deq, "e": e_out}
+
+
+def adam_warmup_step(x, m, v, g, lr: float, eps: float, beta1: float,
+                     beta2: float) -> Dict[str, np.ndarray]:
+    """Same contract as ``oracle.warmup.adam_warmup_step``."""
+    lib = load()
+    x, m, v = (_arr(a, f32).copy() for a in (x, m, v))
+    g = _arr(g, f32)
+    lib.ref_adam_warmup_step(_p(x), _p(m), _p(v), _p(g), x.size, float(lr), float(eps),
+                             float(beta1), float(beta2))
+    return {"x": x, "m": m, "v": v}
+
+
+def lamb_warmup_step(x, m, v, g, seg_off, lr: float, eps: float, beta1: float, beta2: float,
+                     c_avg=None, beta_c: float = 0.9) -> Dict[str, np.ndarray]:
+    """Same contract as ``oracle.warmup.lamb_warmup_step`` (without ``u``)."""
+    lib = load()
+    x, m, v = (_arr(a, f32).copy() for a in (x, m, v))
+    g = _arr(g, f32)
+    off = _arr(seg_off, np.int64)
+    S = off.size - 1
+    c = np.empty(S, dtype=f32)
+    c_out = np.empty(S, dtype=f32)
+    c_in = None if c_avg is None else _arr(c_avg, f32)
+    rc = lib.ref_lamb_warmup_step(_p(x), _p(m), _p(v), _p(g), _p(off), S, float(lr), float(eps),
+                                  float(beta1), float(beta2), _p(c_in), float(beta_c), _p(c),
+                                  _p(c_out))
+    _ok(rc, "lamb_warmup_step")
+    return {"x": x, "m": m, "v": v, "c": c, "c_avg": c_out}
+
+
+def momentum_scale(m, seg_off) -> np.ndarray:
+    """Same contract as ``oracle.warmup.momentum_scale``."""
+    lib = load()
+    m = _arr(m, f32)
+    off = _arr(seg_off, np.int64)
+    k = np.empty(off.size - 1, dtype=f32)
+    _ok(lib.ref_momentum_scale(_p(m), _p(off), off.size - 1, _p(k)), "momentum_scale")
+    return k
+
+
+def exact_sumsq(x) -> float:
+    x = _arr(x, f32).ravel()
+    return load().ref_exact_sumsq(_p(x), x.size)
+
+
+def exact_sum_f64(x) -> float:
+    x = _arr(x, np.float64).ravel()
+    return load().ref_exact_sum_f64(_p(x), x.size)

@@ -381,3 +381,116 @@ def test_error_is_the_nearest_binary32_to_g_minus_q():
             d = abs(_frac(got) - exact)
             for nb in (np.nextafter(got, F32(-np.inf)), np.nextafter(got, F32(np.inf))):
                 assert d <= abs(_frac(nb) - exact)
+
+
+# ----------------------------------------------------------------------- warmup
+
+from oracle import warmup as W  # noqa: E402
+
+
+def _layers(rng, sizes):
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    return off, int(off[-1])
+
+
+def test_warmup_steps_match_numpy_oracle():
+    """Four free-running warmup steps of Adam and of LAMB (layers of 1 to
+    3000 elements, an empty layer, an all-zero layer, values spanning 1e-30
+    to 1e3), and k_l at the end."""
+    rng = np.random.default_rng(70)
+    off, N = _layers(rng, [64, 1, 3000, 0, 257, 128, 4, 1024])
+    hp = dict(lr=1e-3, eps=1e-6, beta1=0.9, beta2=0.999)
+    x = (rng.standard_normal(N) * 10.0 ** rng.uniform(-30, 3, size=N)).astype(F32)
+    m = np.zeros(N, F32)
+    v = np.zeros(N, F32)
+    xa, ma, va = x.copy(), m.copy(), v.copy()
+    c_np = c_c = None
+    for t in range(4):
+        g = (rng.standard_normal(N) * 1e-3).astype(F32)
+        g[off[5]:off[6]] = 0.0  # the layer's u stays 0: c = 1
+        a_np = W.adam_warmup_step(xa, ma, va, g, **hp)
+        a_c = R.adam_warmup_step(xa, ma, va, g, **hp)
+        for key in ("x", "m", "v"):
+            _eq(a_c[key], a_np[key], f"adam warmup t={t} {key}")
+        xa, ma, va = a_np["x"], a_np["m"], a_np["v"]
+        l_np = W.lamb_warmup_step(x, m, v, g, off, c_avg=c_np, beta_c=0.9, **hp)
+        l_c = R.lamb_warmup_step(x, m, v, g, off, c_avg=c_c, beta_c=0.9, **hp)
+        for key in ("x", "m", "v", "c", "c_avg"):
+            _eq(l_c[key], l_np[key], f"lamb warmup t={t} {key}")
+        x, m, v, c_np, c_c = l_np["x"], l_np["m"], l_np["v"], l_np["c_avg"], l_c["c_avg"]
+    assert l_c["c"][3] == 1 and l_c["c"][5] == 1
+    _eq(R.momentum_scale(m, off), W.momentum_scale(m, off), "k_l")
+
+
+def test_momentum_scale_pins():
+    """Layers of constant magnitude 1, 4 and 2 (RMS 1, 4, 2, mean 7/3) give
+    k = (7/3, 7/12, 7/6), each rounded once; an empty and an all-zero layer
+    give 1. The RMS uses an exact sum: the squares of 2^20 copies of 2^-75
+    vanish in binary32 (2^-150), but their RMS is 2^-75, so the layer counts:
+    k = (0.5 / 2^-75, 0.5 / 1) with mean (2^-75 + 1) / 2 = 0.5 in binary64."""
+    m = np.array([1, -1, 4, 4, -4, 2, 0, 0], dtype=F32)
+    off = np.array([0, 2, 5, 6, 6, 8], dtype=np.int64)
+    k = R.momentum_scale(m, off)
+    assert np.array_equal(k, np.array([7 / 3, 7 / 12, 7 / 6, 1, 1], dtype=F32))
+    tiny = np.full(1 << 20, 2.0 ** -75, dtype=F32)
+    m2 = np.concatenate([tiny, np.array([1.0], dtype=F32)])
+    k2 = R.momentum_scale(m2, np.array([0, 1 << 20, (1 << 20) + 1], dtype=np.int64))
+    assert np.array_equal(k2, np.array([2.0 ** 74, 0.5], dtype=F32))
+    assert np.array_equal(W.momentum_scale(m2, [0, 1 << 20, (1 << 20) + 1]), k2)
+
+
+def test_trust_ratio_pins():
+    """One layer x = (3, 4), and m, v chosen so that u = (1, 0) exactly: the
+    coefficient is ||x|| / ||u|| = 5, and x moves by lr * 5 * u. A layer
+    whose x is 0 keeps c = 1."""
+    x = np.array([3, 4, 0, 0], dtype=F32)
+    m0 = np.array([1, 0, 1, 1], dtype=F32)
+    v0 = np.ones(4, dtype=F32)
+    g = np.array([1, 0, 1, 1], dtype=F32)
+    off = np.array([0, 2, 4], dtype=np.int64)
+    # beta1 = 1/2 keeps m = 1 (or 0); beta2 = 1/2 keeps v = 1; eps = 0: u = m
+    out = R.lamb_warmup_step(x, m0, v0, g, off, lr=0.25, eps=0.0, beta1=0.5, beta2=0.5)
+    assert np.array_equal(out["c"], np.array([5, 1], dtype=F32))
+    assert np.array_equal(out["x"], np.array([3 - 1.25, 4, -0.25, -0.25], dtype=F32))
+    assert np.array_equal(out["c_avg"], out["c"])
+
+
+def test_exact_binary64_sums_against_fsum():
+    """The squared norms are the exact sums rounded once to binary64, which
+    math.fsum gives independently: checked through the coefficient of a
+    layer whose update direction has norm 1 exactly."""
+    import math
+
+    rng = np.random.default_rng(71)
+    for trial in range(20):
+        d = int(rng.integers(1, 500))
+        x = (rng.standard_normal(d) * 10.0 ** rng.uniform(-20, 20, size=d)).astype(F32)
+        # u = (1, 0, ..., 0) exactly: m = g = e0, v = 1, betas 1/2, eps 0
+        e0 = np.zeros(d, dtype=F32)
+        e0[0] = 1
+        out = R.lamb_warmup_step(x, e0, np.ones(d, F32), e0, np.array([0, d]), lr=0.0, eps=0.0,
+                                 beta1=0.5, beta2=0.5)
+        sx = math.fsum((x.astype(np.float64) ** 2).tolist())
+        assert out["c"][0] == F32(math.sqrt(sx)), trial
+
+
+def test_exact_sums_against_fsum_and_ties():
+    """The binary64 sums directly: math.fsum (an independent exact summation,
+    rounded once) on random data over 60 decades and subnormals, and
+    hand-made ties: 1 + 2^-52 + 2^-53 lies halfway between two binary64
+    values and goes to the even one, 1 + 2^-51; 1 + 2^-53 goes to 1."""
+    import math
+
+    rng = np.random.default_rng(72)
+    for trial in range(100):
+        d = int(rng.integers(1, 2000))
+        x = (rng.standard_normal(d) * 10.0 ** rng.uniform(-45, 15, size=d)).astype(F32)
+        assert R.exact_sumsq(x) == math.fsum((x.astype(np.float64) ** 2).tolist()), trial
+        y = np.abs(rng.standard_normal(d) * 10.0 ** rng.uniform(-300, 300, size=d))
+        y[: d // 7] = 5e-324 * rng.integers(0, 1000, size=d // 7)
+        assert R.exact_sum_f64(y) == math.fsum(y.tolist()), trial
+    assert R.exact_sumsq(np.array([1, 2.0 ** -26, 2.0 ** -27, 2.0 ** -27], F32)) == 1 + 2.0 ** -51
+    assert R.exact_sumsq(np.array([1, 2.0 ** -27, 2.0 ** -27], F32)) == 1.0
+    assert R.exact_sum_f64(np.array([1.0, 2.0 ** -52, 2.0 ** -53])) == 1 + 2.0 ** -51
+    assert np.isnan(R.exact_sumsq(np.array([1, np.nan, np.inf], F32)))
+    assert R.exact_sumsq(np.array([1, -np.inf], F32)) == np.inf
