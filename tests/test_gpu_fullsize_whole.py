@@ -310,3 +310,58 @@ def test_int8_2_30_whole_buffer():
         print(f"[whole] {tag} ok", flush=True)
     del err, codes, scales, deq, g, e_ref
     _free()
+
+
+def test_warmup_whole_buffers():
+    """The warmup rows at full size on the whole buffer: two Adam warmup
+    steps on 335M elements (x, m, v), two LAMB warmup steps on the 303-layer
+    buffer (x, m, v and every layer's c and c_avg), then k_l of every layer
+    (within 1e-6: the GPU's norms are binary64 sums in a fixed order, the
+    oracle's exact)."""
+    from momentum_compression_amd.state import AdamWarmup, LambWarmup
+
+    dev = device()
+    wa = C.get("bert_large_335M_x8")
+    N = wa.N
+    _need(dev, N * 4 * 8)
+    print(f"[whole] adam warmup N={N}", flush=True)
+    hp = dict(lr=wa.lr, eps=wa.eps, beta1=wa.beta1, beta2=wa.beta2)
+    ad = AdamWarmup.create(S.params(wa, dev))
+    ref = {"x": host(ad.x).copy(), "m": host(ad.m).copy(), "v": host(ad.v).copy()}
+    for t in (1, 2):
+        g = S.laplace_gradient(N, t, 21, dev)
+        ad.step(g, **hp)
+        torch.cuda.synchronize()
+        ref = R.adam_warmup_step(ref["x"], ref["m"], ref["v"], host(g), **hp)
+        for key in ("x", "m", "v"):
+            _same(host(getattr(ad, key)), ref[key], f"adam warmup t={t} {key}")
+        print(f"[whole] adam warmup t={t} ok", flush=True)
+    del ad, g, ref
+    _free()
+
+    wl = C.get("bert_large_lamb_302t_x16")
+    N = wl.N
+    off = np.array(C.segment_offsets(wl.segments), dtype=np.int64)
+    print(f"[whole] lamb warmup N={N} layers={len(off) - 1}", flush=True)
+    lw = LambWarmup.create(S.params(wl, dev), torch.from_numpy(off).to(dev))
+    ref = {"x": host(lw.x).copy(), "m": host(lw.m).copy(), "v": host(lw.v).copy()}
+    c_avg = None
+    for t in (1, 2):
+        g = S.laplace_gradient(N, t, 22, dev)
+        lw.step(g, wl.lr, wl.eps, wl.beta1, wl.beta2, 0.9)
+        torch.cuda.synchronize()
+        ref = R.lamb_warmup_step(ref["x"], ref["m"], ref["v"], host(g), off, wl.lr, wl.eps,
+                                 wl.beta1, wl.beta2, c_avg=c_avg, beta_c=0.9)
+        c_avg = ref["c_avg"]
+        for key in ("c", "c_avg", "x", "m", "v"):
+            _same(host(getattr(lw, key)), ref[key], f"lamb warmup t={t} {key}")
+        print(f"[whole] lamb warmup t={t} ok", flush=True)
+    k = host(lw.momentum_scale())
+    torch.cuda.synchronize()
+    want = R.momentum_scale(ref["m"], off)
+    rel = np.abs(k.astype(np.float64) - want) / np.abs(want.astype(np.float64))
+    assert rel.max() <= 1e-6, f"k_l: max relative difference {rel.max():.3g}"
+    print(f"[whole] k_l of {k.size} layers ok ({int((k == want).sum())} bit-identical)",
+          flush=True)
+    del lw, g, ref
+    _free()
