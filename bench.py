@@ -128,6 +128,7 @@ B_COMPRESS_GRAD = 12.25        # g 4 + state 4 in + 4 out + 1/8 bit + 1/8 packed
 B_ADAM_PACKED = 12.125         # x 4 in/out, v 4, 1/8 packed momentum
 B_LAMB_STEP = 28.0             # read x, m, m_prev, v_fresh, v_Tw; write x, v_fresh
 B_LAMB_PACKED = 28.125         # read 1/8 bit, x, m_prev, v_fresh, v_Tw; write x, v_fresh, m
+B_LAMB_PACKED_PREV = 20.25     # read 1/8 bit twice (m_t, m_{t-1}), x, v_fresh, v_Tw; write x, v_fresh
 B_INT8 = 17.015625             # read g, err; write code, err, deq; scale per 256
 B_WARMUP_ADAM = 28.0           # read x, m, v, g; write x, m, v
 B_WARMUP_LAMB = 40.0           # pass 1: read x, m, v, g, write m, v; pass 2: read x, m, v, write x
@@ -175,9 +176,11 @@ def measure_lamb(steps: int, warmup: int) -> dict:
     """1-bit LAMB path on the 302-tensor BERT-Large buffer, 16 workers:
     compress with x k_l fused, server reduce, the decompression with / k_l,
     and the LAMB frozen-variance step with the per-layer ratio and r/c
-    update -- as two kernels, and as one pass that reads the server's sign
-    words and writes the decompressed momentum (the step's total uses the
-    one pass)."""
+    update -- as two kernels, as one pass that reads the server's sign
+    words and writes the decompressed momentum, and as one pass that reads
+    the previous step's sign words for m_{t-1} and writes no momentum (the
+    steady state from the second compressed step on, which the step's total
+    uses)."""
     import numpy as np
     import torch
 
@@ -195,10 +198,12 @@ def measure_lamb(steps: int, warmup: int) -> dict:
     off_d, k_d = torch.from_numpy(off).to(dev), torch.from_numpy(k).to(dev)
     sig = S.per_element(S.segment_sigmas(wl), wl, dev)
     m = S.momentum(wl, 1, dev, sigma_elem=sig)
-    grp = OneBitGroup(N, n, dev, seg_off=off_d, seg_k=k_d)
+    grp = OneBitGroup(N, n, dev, seg_off=off_d, seg_k=k_d, keep_prev=True)
     st = LambState.create(S.params(wl, dev), S.frozen_variance(wl, dev),
                           S.lamb_prev_momentum(wl, dev, sig), off_d, torch.from_numpy(c_avg).to(dev))
     st2 = LambState.create(S.params(wl, dev), st.v_frozen, S.lamb_prev_momentum(wl, dev, sig),
+                           off_d, torch.from_numpy(c_avg).to(dev))
+    st3 = LambState.create(S.params(wl, dev), st.v_frozen, S.lamb_prev_momentum(wl, dev, sig),
                            off_d, torch.from_numpy(c_avg).to(dev))
     del sig
     stream = torch.cuda.current_stream()
@@ -224,6 +229,11 @@ def measure_lamb(steps: int, warmup: int) -> dict:
         st2.step_packed(grp.sv_bits, grp.sv_scales, k_d, n, wl.lr, wl.eps, wl.beta1, wl.beta2,
                         wl.r_threshold, wl.r_min, wl.r_max)
 
+    def lamb_packed_prev():
+        st3.step_packed(grp.sv_bits, grp.sv_scales, k_d, n, wl.lr, wl.eps, wl.beta1, wl.beta2,
+                        wl.r_threshold, wl.r_min, wl.r_max, prev_bits=grp.sv_bits_prev,
+                        prev_scales=grp.sv_scales_prev)
+
     # step-ratio-scaled error feedback: the carried errors times c_{t-1}/c_t
     # per layer, at both levels (the same bytes as the plain kernels)
     def comp_ers():
@@ -236,21 +246,22 @@ def measure_lamb(steps: int, warmup: int) -> dict:
         grp.server(t[0], decompress=False)
         grp.seg_err_ratio = None
 
-    ms = _time_calls([comp, serv, dec, lamb, comp_ers, serv_ers, lamb_packed], warmup, steps,
-                     stream)
-    step_ms = ms[0] + ms[1] + ms[6]
+    ms = _time_calls([comp, serv, dec, lamb, comp_ers, serv_ers, lamb_packed, lamb_packed_prev],
+                     warmup, steps, stream)
+    step_ms = ms[0] + ms[1] + ms[7]
     out = {"workload": wl.name, "N": N, "workers": n, "layers": len(wl.segments),
            "step_ms": round(step_ms, 4), "worker_elements_per_s": n * N / (step_ms * 1e-3),
            "compress_x_k": _row(ms[0], B_COMPRESS * n * N, n * N),
            "server": _row(ms[1], b_server(n) * N, N),
            "decompress_div_k_lamb_step": _row(ms[6], B_LAMB_PACKED * N, N),
+           "lamb_step_both_momenta_packed": _row(ms[7], B_LAMB_PACKED_PREV * N, N),
            "decompress_div_k": _row(ms[2], B_DECOMPRESS * N, N),
            "lamb_step": _row(ms[3], B_LAMB_STEP * N, N),
            "compress_x_k_step_ratio_ef": _row(ms[4], B_COMPRESS * n * N, n * N),
            "server_step_ratio_ef": _row(ms[5], b_server(n) * N, N)}
     r = st2.r.double()
     out["r_t"] = {"min": r.min().item(), "median": r.median().item(), "max": r.max().item()}
-    del grp, st, st2, m
+    del grp, st, st2, st3, m
     torch.cuda.empty_cache()
     return out
 

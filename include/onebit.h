@@ -162,8 +162,16 @@ int onebit_compress_grad(const float* g, const uint32_t* mb_bits, const float* m
  * ONEBIT_UNIT_SCALE: the unscaled 1-bit sign of the 1-bit Adam article,
  * section 2.1 (q = sign(g'), i.e. every chunk scale is 1; e = g' -+ 1), at
  * the worker and, in onebit_server_reduce_ex, at the server.
+ * ONEBIT_KEEP_PREV (onebit_server_reduce_ex only): sv_scales holds 2n floats.
+ * [0, n) are the scales as without the flag (the previous step's on entry,
+ * part of the server's error state; this step's on return), and [n, 2n)
+ * receives the values [0, n) held on entry, so the previous step's scales
+ * stay available next to its sign words (frozen_v_step mode 3, mp_scales).
+ * The sign words need no such copy: they are output only, so a caller can
+ * alternate two sv_bits buffers.
  */
 #define ONEBIT_UNIT_SCALE 1u
+#define ONEBIT_KEEP_PREV 2u
 
 /*
  * onebit_compress and onebit_compress_grad in one call, plus the variants.
@@ -186,7 +194,8 @@ int onebit_compress_ex(const float* m, const uint32_t* mb_bits, const float* mb_
 /*
  * onebit_server_reduce with the variants of onebit_compress_ex: the server
  * error E is multiplied by seg_err_ratio[l] of its element's layer before it
- * is added (NULL: no factor), and ONEBIT_UNIT_SCALE makes every S[c] = 1.
+ * is added (NULL: no factor), ONEBIT_UNIT_SCALE makes every S[c] = 1, and
+ * ONEBIT_KEEP_PREV keeps the scales found on entry in sv_scales[n .. 2n).
  */
 int onebit_server_reduce_ex(const uint32_t* bits, const float* scales, float* ef,
                             float* sv_scales, uint32_t* sv_bits, float* m_out,
@@ -260,6 +269,15 @@ int lamb_layer_scale(float* buf, int64_t N, int32_t batch,
  * onebit_decompress writes with the layer table.  m_out [N] receives m_t
  * (the caller's next m_prev); it is optional unless use_c_t is set, whose
  * second pass reads it.  m_out must not overlap m_prev.
+ * With mp_bits and mp_scales (both or neither; 4-byte aligned) the previous
+ * momentum is read packed as well: the previous step's server words and
+ * scales, decoded with the same layer table,
+ *   m_{t-1} = (mp_bits bit ? mp_scales[c] : -mp_scales[c]) / m_seg_k[l],
+ * which are exactly the values that step's m_out held; m_prev is then not
+ * read and may be NULL.  This holds from the second compressed step on (the
+ * first one's m_{t-1} is the warmup momentum, given as m_prev).  The words
+ * and scales are read only; the caller keeps them from the previous step
+ * (the server overwrites its own output buffers).
  */
 typedef struct onebit_frozen_v_args {
     int32_t mode;          /* 0: Adam, 1: LAMB, 2: Adam packed, 3: LAMB packed */
@@ -286,6 +304,8 @@ typedef struct onebit_frozen_v_args {
     float* m_out;          /* modes 2, 3: [N] out, or NULL: mbar as           */
                            /* decompressed                                    */
     const float* m_seg_k;  /* mode 3: [n_seg] layer coefficients k_l          */
+    const uint32_t* mp_bits;  /* mode 3: [N/32] m_{t-1} packed, or NULL       */
+    const float* mp_scales;   /* mode 3: [m_chunks] its chunk scales, or NULL */
 } onebit_frozen_v_args;
 
 int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes,

@@ -69,6 +69,14 @@ size_t partial_bytes(int64_t N, int32_t n) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ONEBIT_OK : ONEBIT_E_HIP; }
 
+// ONEBIT_KEEP_PREV: the server's scales as found on entry, copied to the
+// second half of the buffer before the call overwrites the first (n <= 64:
+// one wave)
+__global__ void keep_scales_kernel(float* __restrict__ sv_scales, int32_t n) {
+    const int i = threadIdx.x;
+    if (i < n) sv_scales[n + i] = sv_scales[i];
+}
+
 }  // namespace
 
 extern "C" {
@@ -162,7 +170,7 @@ int onebit_server_reduce_ex(const uint32_t* bits, const float* scales, float* ef
         !aligned(sv_bits, 4) || (m_out && !aligned(m_out, 16)) ||
         (seg_err_ratio && !aligned(seg_err_ratio, 4)))
         return ONEBIT_E_ALIGN;
-    if (flags & ~ONEBIT_UNIT_SCALE) return ONEBIT_E_ARG;
+    if (flags & ~(ONEBIT_UNIT_SCALE | ONEBIT_KEEP_PREV)) return ONEBIT_E_ARG;
     if (N == 0) return ONEBIT_OK;
     const size_t need = onebit_workspace_bytes(N, n, n_seg);
     if (!ws || ws_bytes < need) return ONEBIT_E_WORKSPACE;
@@ -172,7 +180,12 @@ int onebit_server_reduce_ex(const uint32_t* bits, const float* scales, float* ef
     if (sum_depth(plan) > kMaxSumDepth || !groups_ok(plan.bpc)) return ONEBIT_E_SIZE;
     if (m_out && !groups_ok(ceil_div(N, (int64_t)kDecompressTiles * kTile))) return ONEBIT_E_SIZE;
     double* partials = static_cast<double*>(ws);
-    hipError_t e = launch_server(bits, scales, ef, sv_scales, sv_bits, partials, N, n, plan,
+    hipError_t e = hipSuccess;
+    if (flags & ONEBIT_KEEP_PREV) {
+        hipLaunchKernelGGL(keep_scales_kernel, dim3(1), dim3(64), 0, stream, sv_scales, n);
+        if ((e = hipGetLastError()) != hipSuccess) return ONEBIT_E_HIP;
+    }
+    e = launch_server(bits, scales, ef, sv_scales, sv_bits, partials, N, n, plan,
                                  reset != 0, seg_off, seg_err_ratio, n_seg, stream);
     if (e != hipSuccess) return ONEBIT_E_HIP;
     MeanTarget tgt{ef, N, n, sv_scales, (flags & ONEBIT_UNIT_SCALE) != 0};
@@ -252,17 +265,21 @@ int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes, hipS
                                              a->m_chunks, a->lr, a->eps, stream));
     }
     if (a->mode != 1 && a->mode != 3) return ONEBIT_E_ARG;
-    if (!a->m_prev || !a->v_fresh || !a->seg_off || !a->c_avg || !a->r_prev || !a->c_prev)
+    // mode 3 may take the previous momentum packed instead of m_prev
+    const bool prev_packed = a->mode == 3 && a->mp_bits != nullptr;
+    if ((!a->m_prev && !prev_packed) || !a->v_fresh || !a->seg_off || !a->c_avg || !a->r_prev ||
+        !a->c_prev)
         return ONEBIT_E_NULL;
     if (a->mode == 3) {
         if (!a->m_bits || !a->m_scales || !a->m_seg_k || (a->use_c_t && !a->m_out))
             return ONEBIT_E_NULL;
+        if ((a->mp_bits == nullptr) != (a->mp_scales == nullptr)) return ONEBIT_E_NULL;
         if (a->m_chunks < 1 || a->m_chunks > kMaxWorkers || (a->N % (64 * (int64_t)a->m_chunks)))
             return ONEBIT_E_SIZE;
         if (!aligned(a->m_bits, 4) || !aligned(a->m_scales, 4) || !aligned(a->m_seg_k, 4) ||
-            !aligned(a->m_out, 16))
+            !aligned(a->m_out, 16) || !aligned(a->mp_bits, 4) || !aligned(a->mp_scales, 4))
             return ONEBIT_E_ALIGN;
-        if (a->m_out) {  // the decompressed output must not overlap m_prev, which is read
+        if (a->m_out && !prev_packed) {  // m_out must not overlap m_prev, which is read
             const uintptr_t o = (uintptr_t)a->m_out, p = (uintptr_t)a->m_prev;
             const uintptr_t bytes = (uintptr_t)a->N * sizeof(float);
             if (o < p + bytes && p < o + bytes) return ONEBIT_E_ARG;

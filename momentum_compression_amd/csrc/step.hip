@@ -133,16 +133,20 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // The global momentum m_t arrives decompressed (m), or PACKED: the server's
 // sign words and chunk scales with the layer coefficients, decoded here as
 // (bit ? S_c : -S_c) / k_l exactly as the decompression computes it, and
-// stored to m_out when that is given.
+// stored to m_out when that is given. With PREV_PACKED the previous step's
+// momentum m_{t-1} is decoded the same way from that step's words and scales
+// instead of being read as floats (1/8 byte per element instead of 4).
 struct PackedMomentum {
-    const uint32_t* bits;  // [N/32]
-    const float* scales;   // [chunks]
-    const float* seg_k;    // [n_seg]
-    float* out;            // [N] or null
-    int64_t L;             // chunk length
+    const uint32_t* bits;   // [N/32]
+    const float* scales;    // [chunks]
+    const float* seg_k;     // [n_seg]
+    float* out;             // [N] or null
+    int64_t L;              // chunk length
+    const uint32_t* pbits;  // [N/32] previous step's words (PREV_PACKED)
+    const float* pscales;   // [chunks] previous step's scales (PREV_PACKED)
 };
 
-template <bool UPDATE_X, bool PACKED>
+template <bool UPDATE_X, bool PACKED, bool PREV_PACKED>
 __global__ __launch_bounds__(kThreads) void lamb_kernel(
     float* __restrict__ x, const float* __restrict__ m, const float* __restrict__ mp,
     float* __restrict__ vf, const float* __restrict__ v, const int64_t* __restrict__ seg_off,
@@ -177,23 +181,25 @@ __global__ __launch_bounds__(kThreads) void lamb_kernel(
         else atomicMax(&keys[sg], km);
     };
     f4 mv[kLambTiles], pv[kLambTiles], fv[kLambTiles], vv[kLambTiles], xv[kLambTiles];
-    uint32_t mw[kLambTiles];
+    uint32_t mw[kLambTiles], pw[kLambTiles];
 #pragma unroll
     for (int u = 0; u < kLambTiles; ++u) {
         const int64_t j = j0 + (int64_t)u * kTile;
         if (j < wend) {
             if (PACKED) mw[u] = pk.bits[j >> 5];
             else mv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(m + j));
-            pv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(mp + j));
+            if (PREV_PACKED) pw[u] = pk.pbits[j >> 5];
+            else pv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(mp + j));
             fv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(vf + j));
             vv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(v + j));
             if (UPDATE_X) xv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(x + j));
         }
     }
-    // PACKED: value of a set bit for the current (chunk, layer)
+    // PACKED: value of a set bit for the current (chunk, layer), and
+    // (PREV_PACKED) of the previous step's set bit
     int64_t q_c = -1;
     int q_seg = -1;
-    float q = 0.0f;
+    float q = 0.0f, qp = 0.0f;
 #pragma unroll
     for (int u = 0; u < kLambTiles; ++u) {
         const int64_t j = j0 + (int64_t)u * kTile;
@@ -207,7 +213,14 @@ __global__ __launch_bounds__(kThreads) void lamb_kernel(
         }
         const int64_t c = PACKED ? j / pk.L : 0;  // L is a multiple of 64: one chunk per quad
         const uint32_t word = PACKED ? mw[u] >> (j & 31) : 0u;
-        const float ps[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
+        const uint32_t pword = PREV_PACKED ? pw[u] >> (j & 31) : 0u;
+        float ps[4];
+        if (!PREV_PACKED) {
+            ps[0] = pv[u].x;
+            ps[1] = pv[u].y;
+            ps[2] = pv[u].z;
+            ps[3] = pv[u].w;
+        }
         const float fs[4] = {fv[u].x, fv[u].y, fv[u].z, fv[u].w};
         const float vs[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
         float xs[4] = {0.f, 0.f, 0.f, 0.f};
@@ -234,8 +247,10 @@ __global__ __launch_bounds__(kThreads) void lamb_kernel(
                     q_c = c;
                     q_seg = seg;
                     q = pk.scales[c] / pk.seg_k[seg];
+                    if (PREV_PACKED) qp = pk.pscales[c] / pk.seg_k[seg];
                 }
                 ms[k] = ((word >> k) & 1u) ? q : -q;  // -S / k is exactly -(S / k)
+                if (PREV_PACKED) ps[k] = ((pword >> k) & 1u) ? qp : -qp;
             }
             const float g = (ms[k] - c_beta1 * ps[k]) / c_omb1;
             const float vn = c_beta2 * fs[k] + c_omb2 * (g * g);
@@ -381,19 +396,22 @@ hipError_t launch_lamb(const onebit_frozen_v_args& a, uint32_t* keys, uint32_t* 
     hipLaunchKernelGGL(fill_u32_kernel, dim3((a.n_seg + 255) / 256), dim3(256), 0, st, keys,
                        a.n_seg, 0u);
     const bool packed = a.mode == 3;
+    const bool prev_packed = packed && a.mp_bits != nullptr;
     PackedMomentum pk{a.m_bits, a.m_scales, a.m_seg_k, a.m_out,
-                      packed ? a.N / a.m_chunks : (int64_t)1};
+                      packed ? a.N / a.m_chunks : (int64_t)1, a.mp_bits, a.mp_scales};
     auto launch = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, st, a.x, a.m, a.m_prev, a.v_fresh, a.v,
                            a.seg_off, a.n_seg, a.c_prev, keys, wg_max, a.N, a.lr, a.eps, a.beta1,
                            a.beta2, pk);
     };
     if (a.use_c_t) {
-        if (packed) launch(lamb_kernel<false, true>);
-        else launch(lamb_kernel<false, false>);
+        if (prev_packed) launch(lamb_kernel<false, true, true>);
+        else if (packed) launch(lamb_kernel<false, true, false>);
+        else launch(lamb_kernel<false, false, false>);
     } else {
-        if (packed) launch(lamb_kernel<true, true>);
-        else launch(lamb_kernel<true, false>);
+        if (prev_packed) launch(lamb_kernel<true, true, true>);
+        else if (packed) launch(lamb_kernel<true, true, false>);
+        else launch(lamb_kernel<true, false, false>);
     }
     hipLaunchKernelGGL(lamb_finalize_kernel, dim3(a.n_seg), dim3(kThreads), 0, st, keys, wg_max,
                        a.seg_off, n_wg, a.n_seg, a.c_avg, a.r_prev, a.c_prev, a.ratio_max,

@@ -27,6 +27,7 @@ ONEBIT_E_WORKSPACE = -4
 ONEBIT_E_ARG = -5
 ONEBIT_E_HIP = -6
 ONEBIT_UNIT_SCALE = 1
+ONEBIT_KEEP_PREV = 2
 
 _c_i32, _c_i64, _c_u32, _c_u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64
 _c_f, _c_p, _c_sz = ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -46,6 +47,7 @@ class FrozenVArgs(ctypes.Structure):
         ("m_bits", _c_p), ("m_scales", _c_p), ("m_chunks", _c_i32),
         ("err_ratio", _c_p),
         ("m_out", _c_p), ("m_seg_k", _c_p),
+        ("mp_bits", _c_p), ("mp_scales", _c_p),
     ]
 
 
@@ -216,7 +218,8 @@ def onebit_server_reduce_ex(bits, scales, ef, sv_scales, sv_bits, m_out, N: int,
                             n_seg: int = 0, flags: int = 0, ws=None, stream=None) -> None:
     _check("onebit_server_reduce_ex", load().onebit_server_reduce_ex(
         _buf(bits, n * N // 32, "u32", "bits"), _buf(scales, n * n, "f32", "scales"),
-        _buf(ef, N, "f32", "ef"), _buf(sv_scales, n, "f32", "sv_scales"),
+        _buf(ef, N, "f32", "ef"),
+        _buf(sv_scales, 2 * n if flags & ONEBIT_KEEP_PREV else n, "f32", "sv_scales"),
         _buf(sv_bits, N // 32, "u32", "sv_bits"), _buf(m_out, N, "f32", "m_out"),
         _buf(seg_off, n_seg + 1, "i64", "seg_off"), _buf(seg_k, n_seg, "f32", "seg_k"),
         _buf(seg_err_ratio, n_seg, "f32", "seg_err_ratio"), n_seg, N, n, int(bool(reset)), flags,
@@ -261,7 +264,7 @@ def frozen_v_step(*, mode: int, N: int, x, m, v, lr: float, eps: float, beta1: f
                   c_avg=None, r_prev=None, c_prev=None, ratio_max=None, r_threshold: float = 0.1,
                   r_min: float = 0.5, r_max: float = 4.0, use_c_t: bool = False, m_bits=None,
                   m_scales=None, m_chunks: int = 0, err_ratio=None, m_out=None, m_seg_k=None,
-                  ws=None, stream=None) -> None:
+                  mp_bits=None, mp_scales=None, ws=None, stream=None) -> None:
     a = FrozenVArgs(mode=mode, use_c_t=int(bool(use_c_t)), N=N, lr=lr, eps=eps, beta1=beta1,
                     beta2=beta2, r_threshold=r_threshold, r_min=r_min, r_max=r_max, n_seg=n_seg,
                     x=_buf(x, N, "f32", "x"), m=_buf(m, N, "f32", "m"), v=_buf(v, N, "f32", "v"),
@@ -274,7 +277,9 @@ def frozen_v_step(*, mode: int, N: int, x, m, v, lr: float, eps: float, beta1: f
                     m_bits=_buf(m_bits, N // 32, "u32", "m_bits"),
                     m_scales=_buf(m_scales, m_chunks, "f32", "m_scales"), m_chunks=m_chunks,
                     err_ratio=_buf(err_ratio, n_seg, "f32", "err_ratio"),
-                    m_out=_buf(m_out, N, "f32", "m_out"), m_seg_k=_buf(m_seg_k, n_seg, "f32", "m_seg_k"))
+                    m_out=_buf(m_out, N, "f32", "m_out"), m_seg_k=_buf(m_seg_k, n_seg, "f32", "m_seg_k"),
+                    mp_bits=_buf(mp_bits, N // 32, "u32", "mp_bits"),
+                    mp_scales=_buf(mp_scales, m_chunks, "f32", "mp_scales"))
     _check("frozen_v_step", load().frozen_v_step(
         ctypes.byref(a), _buf(ws, 0, "u8", "ws"), _nbytes(ws) if ws is not None else 0,
         _stream(stream)))

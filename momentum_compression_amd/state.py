@@ -37,6 +37,12 @@ class OneBitGroup:
     seg_k: Optional[torch.Tensor] = None    # float32 [S] on device
     unit_scale: bool = False                # unscaled +-1 signs at both levels
     seg_err_ratio: Optional[torch.Tensor] = None  # float32 [S]: step-ratio error factor
+    # keep the previous step's server words and scales (sv_bits_prev,
+    # sv_scales_prev), so the LAMB step can read m_{t-1} packed: the server
+    # writes its words into the older of two buffers (they swap every step;
+    # the words are output only), and copies its scales, which are also its
+    # error state, to a second half before overwriting them
+    keep_prev: bool = False
 
     def __post_init__(self):
         N, n, dev = self.N, self.n, self.device
@@ -50,6 +56,11 @@ class OneBitGroup:
         self.sv_scales = torch.zeros(n, dtype=f32, device=dev)
         self.sv_bits = torch.zeros(N // 32, dtype=torch.int32, device=dev)
         self.mbar = torch.zeros(N, dtype=f32, device=dev)
+        if self.keep_prev:
+            self._sv_scales2 = torch.zeros(2 * n, dtype=f32, device=dev)
+            self.sv_scales = self._sv_scales2[:n]
+            self.sv_scales_prev = self._sv_scales2[n:]
+            self.sv_bits_prev = torch.zeros(N // 32, dtype=torch.int32, device=dev)
         n_seg = self.n_seg
         self.ws = torch.empty(max(256, ob.workspace_bytes(N, n, n_seg)), dtype=torch.uint8, device=dev)
 
@@ -84,25 +95,37 @@ class OneBitGroup:
                               flags=self.flags, ws=self.ws, stream=stream)
 
     def server(self, t: int, first: bool = False, decompress: bool = True, stream=None) -> None:
-        ob.onebit_server_reduce_ex(self.bits, self.scales, self.sv_ef, self.sv_scales,
+        flags = self.flags
+        sv_scales = self.sv_scales
+        if self.keep_prev:  # this step's words go to the older buffer
+            self.sv_bits, self.sv_bits_prev = self.sv_bits_prev, self.sv_bits
+            flags |= ob.ONEBIT_KEEP_PREV
+            sv_scales = self._sv_scales2
+        ob.onebit_server_reduce_ex(self.bits, self.scales, self.sv_ef, sv_scales,
                                    self.sv_bits, self.mbar if decompress else None, self.N,
                                    self.n, reset=first or self.is_reset(t),
                                    seg_off=self.seg_off, seg_k=self.seg_k,
                                    seg_err_ratio=self.seg_err_ratio, n_seg=self.n_seg,
-                                   flags=self.flags, ws=self.ws, stream=stream)
+                                   flags=flags, ws=self.ws, stream=stream)
 
     # buffers that carry over from one step to the next (the worker sign words
     # and the workspace are rewritten by every step)
     _STATE = ("ef", "scales", "sv_ef", "sv_scales", "sv_bits", "mbar")
 
+    _PREV = ("sv_bits_prev", "sv_scales_prev")
+
+    def _state_names(self):
+        return self._STATE + (self._PREV if self.keep_prev else ())
+
     def config(self) -> dict:
         return {"N": self.N, "n": self.n, "clip": self.clip,
-                "reset_interval": self.reset_interval, "unit_scale": self.unit_scale}
+                "reset_interval": self.reset_interval, "unit_scale": self.unit_scale,
+                "keep_prev": self.keep_prev}
 
     def state_dict(self) -> Dict[str, Optional[torch.Tensor]]:
         """The group's carried state and its layer tables (None where unset),
         for ``checkpoint.save``."""
-        d = {k: getattr(self, k) for k in self._STATE}
+        d = {k: getattr(self, k) for k in self._state_names()}
         d.update(seg_off=self.seg_off, seg_k=self.seg_k, seg_err_ratio=self.seg_err_ratio)
         return d
 
@@ -114,8 +137,9 @@ class OneBitGroup:
                   reset_interval=int(config["reset_interval"]),
                   seg_off=tensors.get("seg_off"), seg_k=tensors.get("seg_k"),
                   unit_scale=bool(config["unit_scale"]),
-                  seg_err_ratio=tensors.get("seg_err_ratio"))
-        for k in cls._STATE:
+                  seg_err_ratio=tensors.get("seg_err_ratio"),
+                  keep_prev=bool(config.get("keep_prev", False)))
+        for k in grp._state_names():
             dst, src = getattr(grp, k), tensors[k]
             if dst.shape != src.shape or dst.dtype != src.dtype:
                 raise ValueError(f"{k}: expected {tuple(dst.shape)} {dst.dtype}, "
@@ -145,6 +169,8 @@ class OneBitGroup:
         step and every ``reset_interval``-th step reset the errors and run
         eagerly.  Nothing in the step allocates, clears memory or
         synchronises, so the graph holds only the library's kernels."""
+        if self.keep_prev:
+            raise ValueError("capture_step needs fixed server buffers (keep_prev=False)")
         graph = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream(device=self.device)  # default priority
         side.wait_stream(torch.cuda.current_stream(self.device))
@@ -229,21 +255,35 @@ class LambState:
     def step_packed(self, bits: torch.Tensor, scales: torch.Tensor, seg_k: torch.Tensor,
                     chunks: int, lr: float, eps: float, beta1: float, beta2: float, thr: float,
                     r_min: float, r_max: float, use_c_t: bool = False,
-                    stream=None) -> torch.Tensor:
+                    prev_bits: Optional[torch.Tensor] = None,
+                    prev_scales: Optional[torch.Tensor] = None,
+                    stream=None) -> Optional[torch.Tensor]:
         """LAMB step reading the global momentum as the server's sign words and
         chunk scales, divided by the layer coefficients in the same pass.  The
         decompressed momentum it writes becomes ``m_prev`` for the next step
-        and is returned."""
-        if self.m_next is None:
-            self.m_next = torch.empty_like(self.m_prev)
+        and is returned.
+
+        With ``prev_bits`` and ``prev_scales`` (the previous step's server
+        words and scales, e.g. a ``keep_prev`` group's ``sv_bits_prev`` and
+        ``sv_scales_prev``) m_{t-1} is decoded from them instead of read from
+        ``m_prev``, and no decompressed momentum is written (unless
+        ``use_c_t``, whose second pass reads it): ``m_prev`` is then left
+        as it was and None is returned."""
         S = self.seg_off.numel() - 1
+        prev = prev_bits is not None
+        write_m = use_c_t or not prev
+        if write_m and self.m_next is None:
+            self.m_next = torch.empty_like(self.x)
         ob.frozen_v_step(mode=3, N=self.x.numel(), x=self.x, m=None, v=self.v_frozen, lr=lr,
-                         eps=eps, beta1=beta1, beta2=beta2, m_prev=self.m_prev,
+                         eps=eps, beta1=beta1, beta2=beta2, m_prev=None if prev else self.m_prev,
                          v_fresh=self.v_fresh, seg_off=self.seg_off, n_seg=S, c_avg=self.c_avg,
                          r_prev=self.r, c_prev=self.c, ratio_max=self.ratio_max,
                          r_threshold=thr, r_min=r_min, r_max=r_max, use_c_t=use_c_t,
                          err_ratio=self.err_ratio, m_bits=bits, m_scales=scales, m_chunks=chunks,
-                         m_seg_k=seg_k, m_out=self.m_next, ws=self.ws, stream=stream)
+                         m_seg_k=seg_k, m_out=self.m_next if write_m else None,
+                         mp_bits=prev_bits, mp_scales=prev_scales, ws=self.ws, stream=stream)
+        if not write_m:
+            return None
         self.m_prev, self.m_next = self.m_next, self.m_prev
         return self.m_prev
 

@@ -132,6 +132,19 @@ def test_frozen_v_validation(lib):
     assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_ARG
     a = ob.FrozenVArgs(**{**lamb, "m_out": P + 4 * 1024})  # adjacent: accepted up to the workspace
     assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_WORKSPACE
+    # m_{t-1} packed: words and scales both or neither; m_prev then not needed
+    a = ob.FrozenVArgs(**{**lamb, "mp_bits": P})
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_NULL
+    a = ob.FrozenVArgs(**{**lamb, "m_prev": None})
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_NULL
+    a = ob.FrozenVArgs(**{**lamb, "m_prev": None, "mp_bits": P, "mp_scales": P})
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_WORKSPACE
+    a = ob.FrozenVArgs(**{**lamb, "m_prev": None, "mp_bits": P + 2, "mp_scales": P})
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_ALIGN
+    a = ob.FrozenVArgs(**{**lamb, "m_out": P + 64, "mp_bits": P, "mp_scales": P})
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_WORKSPACE  # m_prev unread
+    a = ob.FrozenVArgs(**{**lamb, "mode": 1, "m": P, "m_prev": None, "mp_bits": P, "mp_scales": P})
+    assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_NULL  # mode 1 reads m_prev
     a = ob.FrozenVArgs(mode=0, N=1022, x=P, m=P, v=P)
     assert lib.frozen_v_step(ctypes.byref(a), None, 0, None) == ob.ONEBIT_E_SIZE
     assert lib.frozen_v_step(None, None, 0, None) == ob.ONEBIT_E_NULL
@@ -147,7 +160,9 @@ def test_struct_layout_matches_header():
     assert ob.FrozenVArgs.err_ratio.offset == 152
     assert ob.FrozenVArgs.m_out.offset == 160
     assert ob.FrozenVArgs.m_seg_k.offset == 168
-    assert ctypes.sizeof(ob.FrozenVArgs) == 176
+    assert ob.FrozenVArgs.mp_bits.offset == 176
+    assert ob.FrozenVArgs.mp_scales.offset == 184
+    assert ctypes.sizeof(ob.FrozenVArgs) == 192
 
 
 def test_extended_entries_validation(lib):
@@ -155,7 +170,7 @@ def test_extended_entries_validation(lib):
     base = [P, None, None, 0.0, P, P, P, 1 << 12, 4, 0.0, 0, None, None, None, 0, 0, P, 1 << 30, None]
     bad = list(base); bad[18 - 2] = None  # no workspace
     assert cx(*bad) == ob.ONEBIT_E_WORKSPACE
-    bad = list(base); bad[15] = 2         # unknown flag
+    bad = list(base); bad[15] = ob.ONEBIT_KEEP_PREV  # a server-only flag
     assert cx(*bad) == ob.ONEBIT_E_ARG
     bad = list(base); bad[13] = P         # error ratio without a layer table
     assert cx(*bad) == ob.ONEBIT_E_ARG
@@ -165,6 +180,8 @@ def test_extended_entries_validation(lib):
     sbase = [P, P, P, P, P, None, None, None, None, 0, 1 << 12, 4, 0, 0, P, 1 << 30, None]
     bad = list(sbase); bad[13] = 4
     assert sx(*bad) == ob.ONEBIT_E_ARG
+    ok = list(sbase); ok[13] = ob.ONEBIT_UNIT_SCALE | ob.ONEBIT_KEEP_PREV; ok[10] = 0
+    assert sx(*ok) == ob.ONEBIT_OK                 # both flags accepted (empty: no launch)
     bad = list(sbase); bad[8] = P
     assert sx(*bad) == ob.ONEBIT_E_ARG
     q = lib.int8_quantize

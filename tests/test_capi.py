@@ -36,3 +36,29 @@ def test_c_program_links_and_starts():
     res = subprocess.run([B.CAPI_BIN], capture_output=True, text=True, timeout=120)
     assert res.returncode in (0, 2), res.stdout + res.stderr
     assert res.stdout.strip() in ("capi ok", "no GPU")
+
+
+def test_struct_mirror_matches_the_c_compiler(tmp_path):
+    """Every field offset and the size of onebit_frozen_v_args as gcc lays
+    them out from the header, against the binding's ctypes mirror."""
+    import ctypes
+
+    from momentum_compression_amd import onebit as ob
+
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    names = [f[0] for f in ob.FrozenVArgs._fields_]
+    lines = "\n".join(f'    printf("{n} %zu\\n", offsetof(onebit_frozen_v_args, {n}));' for n in names)
+    src = tmp_path / "off.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "onebit.h"\nint main(void) {\n'
+                   f'{lines}\n    printf("sizeof %zu\\n", sizeof(onebit_frozen_v_args));\n'
+                   '    return 0;\n}\n')
+    exe = tmp_path / "off"
+    res = subprocess.run(["gcc", "-std=c99", "-D__HIP_PLATFORM_AMD__", f"-I{_rocm_include()}",
+                          f"-I{B.INCLUDE}", str(src), "-o", str(exe)], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    out = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True,
+                                                       text=True).stdout.splitlines())
+    for n in names:
+        assert int(out[n]) == getattr(ob.FrozenVArgs, n).offset, n
+    assert int(out["sizeof"]) == ctypes.sizeof(ob.FrozenVArgs)

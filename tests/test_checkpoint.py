@@ -64,14 +64,16 @@ def test_damaged_files_are_refused(tmp_path):
         ck.load(str(tmp_path), "cpu")
 
 
-def test_group_and_lamb_state_round_trip(tmp_path):
+@pytest.mark.parametrize("keep_prev", [False, True])
+def test_group_and_lamb_state_round_trip(tmp_path, keep_prev):
     N, n = 4096, 4
     off = torch.tensor([0, 100, 100, 3000, N], dtype=torch.int64)
     k = torch.tensor([1.0, 2.0, 0.5, 4.0])
     grp = OneBitGroup(N, n, torch.device("cpu"), clip=2.0, reset_interval=2000, seg_off=off,
-                      seg_k=k)
+                      seg_k=k, keep_prev=keep_prev)
+    assert ("sv_bits_prev" in grp.state_dict()) == keep_prev
     g = torch.Generator().manual_seed(5)
-    for name in grp._STATE:
+    for name in grp._state_names():
         buf = getattr(grp, name)
         if buf.dtype == torch.float32:
             buf.copy_(torch.randn(buf.shape, generator=g))

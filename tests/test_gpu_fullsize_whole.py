@@ -14,7 +14,8 @@ must be bit-identical:
 * the 1-bit LAMB step on the 302-tensor buffer x 16 (compress with the layer
   coefficients, server, LAMB step from the sign words): all 16 workers, the
   server, m / k, x, the fresh variance and every layer's ratio, r_t, c_t and
-  error factor, over two steps;
+  error factor, over two steps; a second LAMB state that reads m_{t-1} as
+  the previous step's words from the second step on matches it bit for bit;
 * the fused step from gradients on 335M x 8 (momentum formed inside
   compression from the packed global momentum), over two steps;
 * INT8 with Philox stochastic rounding on 2^30 elements, over two
@@ -195,10 +196,13 @@ def test_bert_large_lamb_302t_x16_whole_buffer():
     k_el = np.repeat(k, np.diff(off)).astype(F32)
     sig = S.per_element(S.segment_sigmas(wl), wl, dev)
     off_d, k_d = torch.from_numpy(off).to(dev), torch.from_numpy(k).to(dev)
-    grp = OneBitGroup(N, n, dev, seg_off=off_d, seg_k=k_d)
+    grp = OneBitGroup(N, n, dev, seg_off=off_d, seg_k=k_d, keep_prev=True)
     st = LambState.create(S.params(wl, dev), S.frozen_variance(wl, dev),
                           S.lamb_prev_momentum(wl, dev, sig), off_d,
                           torch.from_numpy(c_avg).to(dev))
+    # a second state that reads m_{t-1} packed from the second step on
+    st_p = LambState.create(st.x.clone(), st.v_frozen, st.m_prev.clone(), off_d,
+                            torch.from_numpy(c_avg).to(dev))
     m = torch.empty((n, N), dtype=torch.float32, device=dev)
     x_ref, vf_ref, mp_ref = host(st.x).copy(), host(st.v_fresh).copy(), host(st.m_prev).copy()
     r_ref, c_ref = host(st.r).copy(), host(st.c).copy()
@@ -210,10 +214,15 @@ def test_bert_large_lamb_302t_x16_whole_buffer():
         first = t == 1
         grp.compress(m, t, first=first)
         grp.server(t, first=first, decompress=False)
-        st.step_packed(grp.sv_bits, grp.sv_scales, k_d, n, wl.lr, wl.eps, wl.beta1, wl.beta2,
-                       wl.r_threshold, wl.r_min, wl.r_max)
+        hp = (wl.lr, wl.eps, wl.beta1, wl.beta2, wl.r_threshold, wl.r_min, wl.r_max)
+        st.step_packed(grp.sv_bits, grp.sv_scales, k_d, n, *hp)
+        prev = {} if first else dict(prev_bits=grp.sv_bits_prev, prev_scales=grp.sv_scales_prev)
+        st_p.step_packed(grp.sv_bits, grp.sv_scales, k_d, n, *hp, **prev)
         torch.cuda.synchronize()
         tag = f"lamb t={t}"
+        for name in ("x", "v_fresh", "ratio_max", "r", "c", "err_ratio"):
+            assert torch.equal(getattr(st, name).view(torch.int32),
+                               getattr(st_p, name).view(torch.int32)), f"{tag} m_(t-1) packed: {name}"
         bits, s = _workers(grp, m, e_ref, first, tag, k=k_el)
         sv = _server(grp, bits, s, E_ref, first, tag)
         E_ref = sv["E"]

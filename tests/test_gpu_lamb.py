@@ -118,6 +118,60 @@ def test_lamb_packed_equals_decompress_then_step(use_c_t):
         assert mb is b.m_prev
 
 
+@pytest.mark.parametrize("use_c_t", [False, True])
+def test_lamb_previous_momentum_packed(use_c_t):
+    """From the second step on, the LAMB step can read m_{t-1} as the previous
+    step's server words and scales (a keep_prev group swaps its two output
+    pairs) instead of the floats of m_prev: parameters, fresh variance,
+    maxima, r, c and error ratios stay bit-identical to the step that reads
+    m_prev, over five free-running steps crossing the layer layout's edges."""
+    dev = device()
+    wl = C.scaled_lamb(n=16, target_elems=1 << 20, seed=12)
+    N, n = wl.N, wl.n
+    print(f"[lamb prev packed] N={N} n={n} use_c_t={use_c_t}", flush=True)
+    off, k, c_avg, sig = _setup(wl, dev)
+    off_d = torch.from_numpy(off).to(dev)
+    k_d = torch.from_numpy(k).to(dev)
+    grp = OneBitGroup(N, n, dev, seg_off=off_d, seg_k=k_d, keep_prev=True)
+    plain = OneBitGroup(N, n, dev, seg_off=off_d, seg_k=k_d)  # the server without keep_prev
+    x = S.params(wl, dev)
+    v = S.frozen_variance(wl, dev)
+    mprev = S.lamb_prev_momentum(wl, dev, sig)
+    c0 = torch.from_numpy(c_avg).to(dev)
+    a = LambState.create(x.clone(), v, mprev.clone(), off_d, c0)
+    b = LambState.create(x.clone(), v, mprev.clone(), off_d, c0)
+    hp = dict(lr=wl.lr, eps=wl.eps, beta1=wl.beta1, beta2=wl.beta2, thr=wl.r_threshold,
+              r_min=wl.r_min, r_max=wl.r_max, use_c_t=use_c_t)
+    last = None
+    for t in range(1, 6):
+        m = S.momentum(wl, t, dev, sigma_elem=sig)
+        grp.compress(m, t, first=t == 1)
+        grp.server(t, first=t == 1, decompress=False)
+        plain.compress(m, t, first=t == 1)
+        plain.server(t, first=t == 1, decompress=False)
+        # keep_prev changes nothing the server computes, and keeps the last step's output
+        for name in ("sv_bits", "sv_scales", "sv_ef"):
+            assert torch.equal(getattr(grp, name), getattr(plain, name)), f"t={t} {name}"
+        if last is not None:
+            assert torch.equal(grp.sv_bits_prev, last[0]) and torch.equal(grp.sv_scales_prev, last[1])
+        last = (plain.sv_bits.clone(), plain.sv_scales.clone())
+        a.step_packed(grp.sv_bits, grp.sv_scales, k_d, n, **hp)
+        if t == 1:  # m_{t-1} is the warmup momentum: only m_prev has it
+            mb = b.step_packed(grp.sv_bits, grp.sv_scales, k_d, n, **hp)
+        else:
+            mb = b.step_packed(grp.sv_bits, grp.sv_scales, k_d, n, prev_bits=grp.sv_bits_prev,
+                               prev_scales=grp.sv_scales_prev, **hp)
+        torch.cuda.synchronize()
+        tag = f"t={t}"
+        names = ["x", "v_fresh", "ratio_max", "r", "c", "err_ratio"]
+        if use_c_t or t == 1:
+            names.append("m_prev")  # written when the second pass needs it
+        for name in names:
+            assert np.array_equal(host(getattr(a, name)).view(np.uint32),
+                                  host(getattr(b, name)).view(np.uint32)), f"{tag} {name}"
+        assert (mb is None) == (t > 1 and not use_c_t)
+
+
 def test_layer_scale_entry():
     dev = device()
     wl = C.scaled_lamb(n=4, target_elems=1 << 20, seed=8)
