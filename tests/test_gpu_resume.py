@@ -54,11 +54,15 @@ def test_adam_resume_bit_exact(tmp_path):
         assert _same(getattr(a, name), getattr(c, name)), name
 
 
-def test_lamb_resume_bit_exact(tmp_path):
+@pytest.mark.parametrize("keep_prev", [False, True])
+def test_lamb_resume_bit_exact(tmp_path, keep_prev):
+    """keep_prev: from the second step on the LAMB step reads m_{t-1} as the
+    previous step's server words, which the checkpoint carries."""
     dev = device()
     wl = C.scaled_lamb(n=16, target_elems=1 << 20)
     N, n, T, k = wl.N, wl.n, 5, 2
-    print(f"[resume lamb] N={N} n={n} segments={len(wl.segments)} T={T} k={k}", flush=True)
+    print(f"[resume lamb] N={N} n={n} segments={len(wl.segments)} T={T} k={k} "
+          f"keep_prev={keep_prev}", flush=True)
     off = torch.from_numpy(np.array(C.segment_offsets(wl.segments), dtype=np.int64)).to(dev)
     kk, c_avg = S.lamb_tables(wl)
     k_d, c_d = torch.from_numpy(kk).to(dev), torch.from_numpy(c_avg).to(dev)
@@ -74,12 +78,15 @@ def test_lamb_resume_bit_exact(tmp_path):
             grp.seg_err_ratio = st.err_ratio if t > 1 else None
             grp.compress(m, t, first=t == 1)
             grp.server(t, first=t == 1, decompress=False)
-            st.step_packed(grp.sv_bits, grp.sv_scales, k_d, n, **hp)
+            prev = {}
+            if grp.keep_prev and t > 1:
+                prev = dict(prev_bits=grp.sv_bits_prev, prev_scales=grp.sv_scales_prev)
+            st.step_packed(grp.sv_bits, grp.sv_scales, k_d, n, **hp, **prev)
 
-    a = OneBitGroup(N, n, dev, seg_off=off, seg_k=k_d)
+    a = OneBitGroup(N, n, dev, seg_off=off, seg_k=k_d, keep_prev=keep_prev)
     sa = LambState.create(x0.clone(), v0, mp0.clone(), off, c_d.clone())
     run(a, sa, 1, T + 1)
-    b = OneBitGroup(N, n, dev, seg_off=off, seg_k=k_d)
+    b = OneBitGroup(N, n, dev, seg_off=off, seg_k=k_d, keep_prev=keep_prev)
     sb = LambState.create(x0.clone(), v0, mp0.clone(), off, c_d.clone())
     run(b, sb, 1, k + 1)
     b.seg_err_ratio = None  # the ratio lives in the LAMB state
@@ -92,7 +99,8 @@ def test_lamb_resume_bit_exact(tmp_path):
     sc = LambState.from_state(tl)
     run(c, sc, meta["t"] + 1, T + 1)
     torch.cuda.synchronize()
-    for name in OneBitGroup._STATE:
+    assert c.keep_prev == keep_prev
+    for name in a._state_names():
         assert _same(getattr(a, name), getattr(c, name)), name
     for name in LambState._STATE:
         assert _same(getattr(sa, name), getattr(sc, name)), name
