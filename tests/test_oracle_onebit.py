@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 from oracle import bits as B
+from oracle import cref as R
 from oracle import onebit as O
 from tests._exactref import frac, rn, ulp
 
@@ -49,8 +50,12 @@ def _brute_worker(m, e, clip, k):
     return gc, s, e_new
 
 
+IMPLS = {"numpy": O, "cpp": R}  # both oracles against the same brute force
+
+
+@pytest.mark.parametrize("impl", sorted(IMPLS))
 @pytest.mark.parametrize("clip,use_k", [(0.0, False), (2.5e-3, False), (0.0, True)])
-def test_worker_matches_exact_arithmetic(clip, use_k):
+def test_worker_matches_exact_arithmetic(clip, use_k, impl):
     rng = np.random.default_rng(7)
     n, N = 2, 128
     m = _draw(rng, (n, N))
@@ -59,7 +64,7 @@ def test_worker_matches_exact_arithmetic(clip, use_k):
     m[:, :4] = np.array([0.0, -0.0, 0.0, -0.0], dtype=F32)
     e[:, :4] = np.array([0.0, 0.0, -0.0, -0.0], dtype=F32)
     k = (2.0 ** rng.integers(-3, 4, size=N) * rng.uniform(0.5, 1.5, size=N)).astype(F32) if use_k else None
-    out = O.worker_compress(m, e, clip=clip, k=k)
+    out = IMPLS[impl].worker_compress(m, e, clip=clip, k=k)
     gc, s, e_new = _brute_worker(m, e, clip, k)
     assert np.array_equal(out["gc"], gc)
     assert np.array_equal(out["s"], s)
@@ -231,7 +236,8 @@ def test_server_unanimous_signs():
     assert np.array_equal(sv["bits"], base)
 
 
-def test_server_average_exact_sequence():
+@pytest.mark.parametrize("impl", sorted(IMPLS))
+def test_server_average_exact_sequence(impl):
     """n = 3 (not a power of two): sequential binary32 accumulation in worker
     order, then one rounding of the division."""
     rng = np.random.default_rng(13)
@@ -239,7 +245,7 @@ def test_server_average_exact_sequence():
     L = N // n
     bits = rng.integers(0, 2**32, size=(n, N // 32), dtype=np.uint64).astype(np.uint32)
     s = np.abs(_draw(rng, (n, n))).astype(F32)
-    sv = O.server_reduce(bits, s, np.zeros(N, dtype=F32))
+    sv = IMPLS[impl].server_reduce(bits, s, np.zeros(N, dtype=F32))
     for c in range(n):
         for j in range(0, L, 3):
             J = c * L + j
