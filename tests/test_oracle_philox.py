@@ -60,9 +60,13 @@ def test_raw_blocks_match_rocrand(rocrand_dump):
         ctrs.append([blk & 0xFFFFFFFF, blk >> 32, sub & 0xFFFFFFFF, sub >> 32])
         keys.append([seed & 0xFFFFFFFF, seed >> 32])
     want = rocrand_dump(triples)
-    got = philox4x32_10(np.array(ctrs, dtype=np.uint64).astype(np.uint32),
-                        np.array(keys, dtype=np.uint64).astype(np.uint32))
-    assert np.array_equal(got, want)
+    c32 = np.array(ctrs, dtype=np.uint64).astype(np.uint32)
+    k32 = np.array(keys, dtype=np.uint64).astype(np.uint32)
+    assert np.array_equal(philox4x32_10(c32, k32), want)
+    from oracle import cref
+
+    got_cpp = np.stack([cref.philox4x32_10(c32[i], k32[i])[0] for i in range(len(c32))])
+    assert np.array_equal(got_cpp, want)  # the C++ oracle's generator, pinned the same way
 
 
 def test_element_uniforms_match_rocrand(rocrand_dump):
@@ -74,4 +78,8 @@ def test_element_uniforms_match_rocrand(rocrand_dump):
         count = 37
         want = rocrand_dump([(seed, step, J0 + j) for j in range(count)])[:, 0]
         u = uniforms(J0, count, seed, step)
-        assert np.array_equal(u, ((want >> np.uint32(8)).astype(np.float64) * 2.0 ** -24).astype(np.float32))
+        expect = ((want >> np.uint32(8)).astype(np.float64) * 2.0 ** -24).astype(np.float32)
+        assert np.array_equal(u, expect)
+        from oracle import cref
+
+        assert np.array_equal(cref.uniforms(J0, count, seed, step), expect)
