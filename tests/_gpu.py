@@ -57,3 +57,23 @@ def same_bits(got: np.ndarray, want: np.ndarray, name: str) -> None:
     assert got.shape == want.shape, (name, got.shape, want.shape)
     neq = got != want
     assert not neq.any(), f"{name}: {int(neq.sum())} of {neq.size} words differ"
+
+
+def same_whole(got: np.ndarray, want: np.ndarray, name: str) -> None:
+    """Bit identity of a whole (large) buffer, checked without float64
+    copies; on a mismatch the differing elements go through ``same_f32`` (or
+    are counted, for integer data), which names how many differ and where."""
+    got, want = np.ascontiguousarray(got), np.ascontiguousarray(want)
+    assert got.shape == want.shape, (name, got.shape, want.shape)
+    if got.dtype == np.float32:
+        gb, wb = got.view(np.uint32), want.view(np.uint32)
+        if np.array_equal(gb, wb):
+            return
+        bad = np.flatnonzero(gb != wb)
+        same_f32(got.ravel()[bad], want.ravel()[bad],
+                 f"{name}: {bad.size} of {got.size} differ, first at {bad[0]}")
+    else:
+        got = got.view(np.uint32) if got.dtype == np.int32 else got
+        neq = got != want
+        assert not neq.any(), (f"{name}: {int(neq.sum())} of {neq.size} differ, first at "
+                               f"{np.flatnonzero(neq)[0]}")

@@ -32,7 +32,7 @@ import torch
 from momentum_compression_amd import onebit as ob
 from momentum_compression_amd.state import LambState, OneBitGroup
 from oracle import cref as R
-from tests._gpu import device, host, same_f32
+from tests._gpu import device, host, same_whole
 from workloads import configs as C
 from workloads import synth as S
 
@@ -52,23 +52,7 @@ def _need(dev, nbytes):
         pytest.skip(f"needs {nbytes / 2**30:.0f} GiB of device memory, {free / 2**30:.0f} free")
 
 
-def _same(got: np.ndarray, want: np.ndarray, name: str) -> None:
-    """Bit identity of a whole buffer; on a mismatch the differing elements
-    go through the float check, which names how many differ and by how much."""
-    got, want = np.ascontiguousarray(got), np.ascontiguousarray(want)
-    assert got.shape == want.shape, (name, got.shape, want.shape)
-    if got.dtype == np.float32:
-        gb, wb = got.view(np.uint32), want.view(np.uint32)
-        if np.array_equal(gb, wb):
-            return
-        bad = np.flatnonzero(gb != wb)
-        same_f32(got.ravel()[bad], want.ravel()[bad],
-                 f"{name}: {bad.size} of {got.size} differ, first at {bad[0]}")
-    else:
-        got = got.view(np.uint32) if got.dtype == np.int32 else got
-        neq = got != want
-        assert not neq.any(), f"{name}: {int(neq.sum())} of {neq.size} differ, first at " \
-                              f"{np.flatnonzero(neq)[0]}"
+_same = same_whole
 
 
 def _workers(grp, m, e_state, reset, tag, clip=0.0, k=None, rows=None):
