@@ -127,3 +127,21 @@ def test_warmup_state_round_trip(tmp_path):
     assert lw2.steps == 7
     for k, v in lw.state_dict().items():
         assert torch.equal(v, lw2.state_dict()[k]), k
+
+
+def test_keep_prev_group_layout_and_capture_refused():
+    """A keep_prev group holds its scales as the two halves of one buffer of
+    2n (this step's, then the previous step's), which the server's
+    ONEBIT_KEEP_PREV call takes whole, and refuses graph capture (its word
+    buffers alternate, a graph would replay fixed pointers)."""
+    N, n = 4096, 4
+    grp = OneBitGroup(N, n, torch.device("cpu"), keep_prev=True)
+    assert grp._sv_scales2.numel() == 2 * n
+    assert grp.sv_scales.data_ptr() == grp._sv_scales2.data_ptr()
+    assert grp.sv_scales_prev.data_ptr() == grp._sv_scales2.data_ptr() + 4 * n
+    assert grp.sv_bits_prev.shape == grp.sv_bits.shape
+    assert grp.config()["keep_prev"] is True
+    with pytest.raises(ValueError):
+        grp.capture_step(None, None, None, 1e-3, 1e-6)
+    plain = OneBitGroup(N, n, torch.device("cpu"))
+    assert not hasattr(plain, "sv_bits_prev") and plain.config()["keep_prev"] is False
