@@ -91,22 +91,36 @@ def read_traffic(launch_elems: int):
     return (fetch + write) * 1024.0
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, m, x, v):
-    """Time the C++ oracle on one whole step of the workload on one thread:
-    compress of all n workers, the n server chunks, decompression and the
-    Adam step. A first (reset) step runs before it, so the timed step carries
-    the error like the steps on the GPU. m [n, N], x, v [N]: host float32."""
+    """Time the C++ oracle on one whole step of the workload: compress of all
+    n workers, the n server chunks, decompression and the Adam step. A first
+    (reset) step runs before it, so the timed step carries the error like the
+    steps on the GPU; it is timed on one thread (the reported value), then
+    once more with the workers' rows and the server chunks spread over the
+    host's threads (bit-identical: rows and chunks are independent).
+    m [n, N], x, v [N]: host float32."""
     from oracle import cref as R
 
     n, N = wl.n, wl.N
     R.load()
+    threads = max(1, min(16, os.cpu_count() or 1))
     secs = []
     e = E = None
-    for t in (1, 2):
+    for t, th in ((1, 1), (2, 1), (3, threads)):
         reset = t == 1
         t0 = time.perf_counter()
-        w = R.worker_compress(m, e, clip=wl.clip, reset=reset, keep_gc=False)
-        sv = R.server_reduce(w["bits"], w["s"], E, reset=reset)
+        w = R.worker_compress(m, e, clip=wl.clip, reset=reset, keep_gc=False, threads=th)
+        sv = R.server_reduce(w["bits"], w["s"], E, reset=reset, threads=th)
         mbar = R.decompress(sv["bits"], sv["S"])
         x = R.adam_frozen_step(x, mbar, v, wl.lr, wl.eps)
         secs.append(time.perf_counter() - t0)
@@ -121,6 +135,12 @@ def cpu_baseline(wl, m, x, v):
                    f"{n} server chunks, decompression, Adam) by the C++ oracle on one thread, "
                    f"on the bench's own inputs copied from the GPU, after a first (reset) "
                    f"step; reset step {secs[0]:.1f} s, timed step {secs[1]:.1f} s"),
+        "cpu_model": _cpu_model(),
+        "threads_available": os.cpu_count(),
+        "multithreaded": {"value": n * N / secs[2], "unit": "elements/s", "cores": threads,
+                          "sample": (f"the next step with the {n} worker rows and the {n} "
+                                     f"server chunks over {threads} threads (decompression "
+                                     f"and Adam on one): {secs[2]:.1f} s")},
     }
 
 

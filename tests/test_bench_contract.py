@@ -56,3 +56,6 @@ def test_cpu_baseline_record():
     assert rec["kind"] == "oracle" and rec["cores"] == 1 and rec["unit"] == "elements/s"
     assert rec["value"] > 0
     assert f"{wl.n} x {wl.N} worker elements" in rec["sample"]
+    mt = rec["multithreaded"]
+    assert mt["value"] > 0 and mt["cores"] >= 1 and mt["unit"] == "elements/s"
+    assert isinstance(rec["cpu_model"], str)
