@@ -732,7 +732,10 @@ def main() -> int:
                      "frac": round(comp_gbs / PEAK_HBM_GBS, 4),
                      "traffic": None if traffic is None else round(traffic, 0),
                      "bytes_per_elem": B_COMPRESS, "elems_per_launch": n * N,
-                     "launch_ms": round(ms["compress"], 4)},
+                     "launch_ms": round(ms["compress"], 4),
+                     # the counters' bytes over the same event-measured duration
+                     "counter_GBps": None if traffic is None else
+                     round(traffic / (ms["compress"] * 1e-3) / 1e9, 1)},
         "kernels": kernels,
     }
     out["diagnostics"] = diagnostics
