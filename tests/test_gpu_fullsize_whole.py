@@ -120,7 +120,7 @@ def test_bert_large_335M_x8_bench_step_whole_buffer():
         grp.adam_step_packed(x, v, wl.lr, wl.eps, decompress=True)
         torch.cuda.synchronize()
         tag = f"{wl.name} t={t}"
-        bits, s = _workers(grp, m, e_ref, reset, tag, clip=wl.clip, rows=rows)
+        bits, s = _workers(grp, m, e_ref, reset, tag, clip=wl.clip)
         sv = _server(grp, bits, s, E_ref, reset, tag)
         E_ref = sv["E"]
         mbar = R.decompress(sv["bits"], sv["S"])
