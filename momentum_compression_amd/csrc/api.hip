@@ -69,15 +69,14 @@ size_t partial_bytes(int64_t N, int32_t n) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ONEBIT_OK : ONEBIT_E_HIP; }
 
-// ONEBIT_KEEP_PREV: the server's scales as found on entry, copied to the
-// second half of the buffer before the call overwrites the first (n <= 64:
-// one wave)
-__global__ void keep_scales_kernel(float* __restrict__ sv_scales, int32_t n) {
-    const int i = threadIdx.x;
-    if (i < n) sv_scales[n + i] = sv_scales[i];
-}
-
 }  // namespace
+
+namespace onebit {
+// the chunk-mean finalize that first copies each scale it will overwrite to
+// prev (finalize.hip); ONEBIT_KEEP_PREV passes the second half of sv_scales
+hipError_t launch_mean_finalize_keep(const double* partials, const ChunkPlan& plan,
+                                     int64_t pairs, MeanTarget tgt, float* prev, hipStream_t st);
+}  // namespace onebit
 
 extern "C" {
 
@@ -180,16 +179,13 @@ int onebit_server_reduce_ex(const uint32_t* bits, const float* scales, float* ef
     if (sum_depth(plan) > kMaxSumDepth || !groups_ok(plan.bpc)) return ONEBIT_E_SIZE;
     if (m_out && !groups_ok(ceil_div(N, (int64_t)kDecompressTiles * kTile))) return ONEBIT_E_SIZE;
     double* partials = static_cast<double*>(ws);
-    hipError_t e = hipSuccess;
-    if (flags & ONEBIT_KEEP_PREV) {
-        hipLaunchKernelGGL(keep_scales_kernel, dim3(1), dim3(64), 0, stream, sv_scales, n);
-        if ((e = hipGetLastError()) != hipSuccess) return ONEBIT_E_HIP;
-    }
-    e = launch_server(bits, scales, ef, sv_scales, sv_bits, partials, N, n, plan,
+    hipError_t e = launch_server(bits, scales, ef, sv_scales, sv_bits, partials, N, n, plan,
                                  reset != 0, seg_off, seg_err_ratio, n_seg, stream);
     if (e != hipSuccess) return ONEBIT_E_HIP;
     MeanTarget tgt{ef, N, n, sv_scales, (flags & ONEBIT_UNIT_SCALE) != 0};
-    e = launch_mean_finalize(partials, plan, n, tgt, stream);
+    // ONEBIT_KEEP_PREV: the finalize copies the scales it replaces to [n, 2n)
+    e = launch_mean_finalize_keep(partials, plan, n, tgt,
+                                  (flags & ONEBIT_KEEP_PREV) ? sv_scales + n : nullptr, stream);
     if (e != hipSuccess) return ONEBIT_E_HIP;
     if (m_out)
         return hip_status(

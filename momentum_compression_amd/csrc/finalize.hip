@@ -116,13 +116,18 @@ __device__ __forceinline__ double fin_block_sum(double v, double* red) {
 
 }  // namespace
 
+// prev (or null): receives out[pair] as found on entry, before it is
+// overwritten (the server's scales of the previous step)
 __global__ __launch_bounds__(kFinThreads) void mean_finalize_kernel(
     const double* __restrict__ partials, int64_t bpc, int64_t L, const float* __restrict__ data,
-    int64_t row_stride, int32_t chunks, float* __restrict__ out, int32_t unit) {
+    int64_t row_stride, int32_t chunks, float* __restrict__ out, int32_t unit,
+    float* __restrict__ prev) {
     __shared__ double red[kFinThreads / 64];
     __shared__ unsigned long long bins[256];
     __shared__ int exact;
     const int64_t pair = blockIdx.x;
+    // thread 0 is the only writer of out[pair], and it copies it first
+    if (prev && threadIdx.x == 0) prev[pair] = out[pair];
     if (unit) {  // the unscaled sign: every scale is 1
         if (threadIdx.x == 0) out[pair] = 1.0f;
         return;
@@ -182,12 +187,17 @@ __global__ __launch_bounds__(kFinThreads) void mean_finalize_kernel(
     if (threadIdx.x == 0) out[pair] = exact_mean_from_bins(bins, (uint64_t)L);
 }
 
-hipError_t launch_mean_finalize(const double* partials, const ChunkPlan& plan, int64_t pairs,
-                                MeanTarget tgt, hipStream_t st) {
+hipError_t launch_mean_finalize_keep(const double* partials, const ChunkPlan& plan,
+                                     int64_t pairs, MeanTarget tgt, float* prev, hipStream_t st) {
     hipLaunchKernelGGL(mean_finalize_kernel, dim3((unsigned)pairs), dim3(kFinThreads), 0, st,
                        partials, plan.bpc, plan.L, tgt.data, tgt.row_stride, tgt.chunks, tgt.out,
-                       tgt.unit ? 1 : 0);
+                       tgt.unit ? 1 : 0, prev);
     return hipGetLastError();
+}
+
+hipError_t launch_mean_finalize(const double* partials, const ChunkPlan& plan, int64_t pairs,
+                                MeanTarget tgt, hipStream_t st) {
+    return launch_mean_finalize_keep(partials, plan, pairs, tgt, nullptr, st);
 }
 
 // ---------------------------------------------------------------- plan
