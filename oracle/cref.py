@@ -149,24 +149,53 @@ def worker_compress(m, e, clip: float = 0.0, reset: bool = False, k=None,
 
 
 def worker_compress_row(m_row, e_row, n: int, clip: float = 0.0, reset: bool = False, k=None,
-                        unit_scale: bool = False, err_ratio=None) -> Dict[str, np.ndarray]:
+                        unit_scale: bool = False, err_ratio=None, threads: int = 1,
+                        gc_out: Optional[np.ndarray] = None,
+                        e_out: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """One worker's row of ``worker_compress`` (the row holds n chunks):
     gc, bits (N/32), s (n) and the new error, which is written over ``e_row``
-    when that is a contiguous float32 array (a copy otherwise)."""
+    when that is a contiguous float32 array (a copy otherwise), or into
+    ``e_out`` when given (needed with ``reset``, where ``e_row`` is not read).
+    ``gc_out`` may pass the buffer for the compensated values.
+
+    With ``threads`` > 1 the row's n chunks run in parallel, each as a row of
+    one chunk: every step of the worker compression is per element except the
+    scale, which is per chunk, so the results are the same."""
     lib = load()
     m_row = _arr(m_row, f32)
     N = m_row.size
     e = None if reset else _arr(e_row, f32)
-    e_out = e if e is not None else np.empty(N, dtype=f32)
+    if e_out is None:
+        e_out = e if e is not None else np.empty(N, dtype=f32)
     k = None if k is None else _arr(k, f32)
     ratio = None if err_ratio is None else _arr(err_ratio, f32)
-    gc = np.empty(N, dtype=f32)
+    gc = np.empty(N, dtype=f32) if gc_out is None else gc_out
+    for buf in (gc, e_out):
+        if buf.dtype != f32 or buf.size != N or not buf.flags.c_contiguous:
+            raise ValueError("output buffers must be contiguous float32 rows of N elements")
     bits = np.zeros(N // 32, dtype=np.uint32)
     s = np.empty(n, dtype=f32)
-    rc = lib.ref_worker_compress_row(_p(m_row), _p(e), _p(k), _p(ratio), N, n, float(clip),
-                                     int(bool(reset)), int(bool(unit_scale)), _p(gc), _p(e_out),
-                                     _p(bits), _p(s))
-    _ok(rc, "worker_compress_row")
+    if N % (64 * n):
+        raise ValueError("N must be a multiple of 64 n")
+    L = N // n
+
+    def at(a, c, per=1):
+        return None if a is None else a[c * L // per:]
+
+    def chunk(c):
+        rc = lib.ref_worker_compress_row(_p(at(m_row, c)), _p(at(e, c)), _p(at(k, c)),
+                                         _p(at(ratio, c)), L, 1, float(clip), int(bool(reset)),
+                                         int(bool(unit_scale)), _p(at(gc, c)), _p(at(e_out, c)),
+                                         _p(at(bits, c, 32)), _p(s[c:]))
+        _ok(rc, "worker_compress_row")
+
+    if threads > 1:
+        _run(chunk, range(n), min(threads, n))
+    else:
+        rc = lib.ref_worker_compress_row(_p(m_row), _p(e), _p(k), _p(ratio), N, n, float(clip),
+                                         int(bool(reset)), int(bool(unit_scale)), _p(gc),
+                                         _p(e_out), _p(bits), _p(s))
+        _ok(rc, "worker_compress_row")
     return {"gc": gc, "bits": bits, "s": s, "e": e_out}
 
 
@@ -204,22 +233,78 @@ def server_reduce(bits, s, E, reset: bool = False, unit_scale: bool = False, err
     return out
 
 
-def decompress(sbits, S, k=None) -> np.ndarray:
+def server_reduce_chunk(bits, s, E, c: int, reset: bool = False, unit_scale: bool = False,
+                        err_ratio=None) -> Dict[str, np.ndarray]:
+    """The server of chunk c alone: ``server_reduce`` restricted to one chunk.
+    bits [n, N/32] and s [n, n] as there; E (not read with ``reset``) and
+    err_ratio need only the elements up to the chunk's end. The outputs
+    cover elements [0, (c + 1) L), of which only chunk c is written, and
+    S[c]."""
+    lib = load()
+    bits = _arr(bits, np.uint32)
+    s = _arr(s, f32)
+    n = s.shape[0]
+    N = bits.shape[1] * 32
+    if N % (64 * n) or not 0 <= c < n:
+        raise ValueError("bad chunk or buffer size")
+    end = (c + 1) * (N // n)
+    E = None if reset else _arr(E, f32)
+    ratio = None if err_ratio is None else _arr(err_ratio, f32)
+    for a in (E, ratio):
+        if a is not None and a.size < end:
+            raise ValueError("E and err_ratio must cover the chunk")
+    out = {"avg": np.empty(end, dtype=f32), "g2": np.empty(end, dtype=f32),
+           "E": np.empty(end, dtype=f32), "S": np.zeros(n, dtype=f32),
+           "bits": np.zeros(end // 32, dtype=np.uint32)}
+    rc = lib.ref_server_chunk(_p(bits), _p(s), _p(E), _p(ratio), N, n, c, int(bool(reset)),
+                              int(bool(unit_scale)), _p(out["avg"]), _p(out["g2"]),
+                              _p(out["E"]), _p(out["bits"]), _p(out["S"]))
+    _ok(rc, "server_reduce_chunk")
+    return out
+
+
+def decompress(sbits, S, k=None, threads: int = 1) -> np.ndarray:
+    """Same contract as ``oracle.onebit.decompress``. With ``threads`` > 1
+    the chunks run in parallel, each as a buffer of one chunk (every output
+    element depends only on its own bit, its chunk's scale and its k)."""
     lib = load()
     sbits = _arr(sbits, np.uint32)
     S = _arr(S, f32)
     N = sbits.size * 32
+    n = S.size
     k = None if k is None else _arr(k, f32)
     out = np.empty(N, dtype=f32)
-    _ok(lib.ref_decompress(_p(sbits), _p(S), _p(k), N, S.size, _p(out)), "decompress")
+    if threads <= 1 or n == 1:
+        _ok(lib.ref_decompress(_p(sbits), _p(S), _p(k), N, n, _p(out)), "decompress")
+        return out
+    if N % (64 * n):
+        raise ValueError("N must be a multiple of 64 n")
+    L = N // n
+
+    def chunk(c):
+        rc = lib.ref_decompress(_p(sbits[c * L // 32:]), _p(S[c:]),
+                                None if k is None else _p(k[c * L:]), L, 1, _p(out[c * L:]))
+        _ok(rc, "decompress")
+
+    _run(chunk, range(n), min(threads, n))
     return out
 
 
-def adam_frozen_step(x, m, v, lr: float, eps: float) -> np.ndarray:
+def adam_frozen_step(x, m, v, lr: float, eps: float, threads: int = 1) -> np.ndarray:
+    """Same contract as ``oracle.optim.adam_frozen_step``; with ``threads`` > 1
+    the (elementwise) step runs over that many slices in parallel."""
     lib = load()
     x = _arr(x, f32).copy()
     m, v = _arr(m, f32), _arr(v, f32)
-    lib.ref_adam_frozen_step(_p(x), _p(m), _p(v), x.size, float(lr), float(eps))
+    N = x.size
+    parts = max(1, min(threads, N // 4096))
+    cuts = [N * p // parts for p in range(parts + 1)]
+
+    def part(p):
+        a, b = cuts[p], cuts[p + 1]
+        lib.ref_adam_frozen_step(_p(x[a:]), _p(m[a:]), _p(v[a:]), b - a, float(lr), float(eps))
+
+    _run(part, range(parts), parts)
     return x
 
 

@@ -5,6 +5,8 @@ binding raises, and the test fails."""
 
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -77,3 +79,27 @@ def same_whole(got: np.ndarray, want: np.ndarray, name: str) -> None:
         neq = got != want
         assert not neq.any(), (f"{name}: {int(neq.sum())} of {neq.size} differ, first at "
                                f"{np.flatnonzero(neq)[0]}")
+
+
+def same_whole_par(got: np.ndarray, want: np.ndarray, name: str, threads: int = 16) -> None:
+    """``same_whole`` with the comparison split over slices that run in
+    parallel threads (numpy releases the interpreter lock while it compares);
+    a slice that differs goes through ``same_whole`` to name the elements."""
+    got, want = np.ascontiguousarray(got).ravel(), np.ascontiguousarray(want).ravel()
+    assert got.shape == want.shape and got.dtype == want.dtype, (name, got.shape, want.shape)
+    if got.dtype in (np.float32, np.int32):
+        gb, wb = got.view(np.uint32), want.view(np.uint32)
+    else:
+        gb, wb = got, want
+    parts = max(1, min(threads, gb.size // (1 << 20)))
+    cuts = [gb.size * p // parts for p in range(parts + 1)]
+
+    def equal(p):
+        return np.array_equal(gb[cuts[p]:cuts[p + 1]], wb[cuts[p]:cuts[p + 1]])
+
+    with ThreadPoolExecutor(max_workers=parts) as ex:
+        eq = list(ex.map(equal, range(parts)))
+    for p, ok in enumerate(eq):
+        if not ok:
+            a, b = cuts[p], cuts[p + 1]
+            same_whole(got[a:b], want[a:b], f"{name} (elements {a}..{b - 1})")

@@ -8,9 +8,12 @@ must be bit-identical:
   server without decompression, decompression inside the Adam pass): all 8
   workers' sign words, scales and compensated values, the server's, the
   decompressed momentum and every parameter, over three steps;
-* the same step on GPT 1.3B x 16 with the clamp, across a periodic reset:
-  whole rows of three workers, the server, the decompressed momentum and
-  every parameter;
+* the 2^20 x 4 workload (chunk 2^18) over its ten steps of compress,
+  server and decompression, with the Adam step after each: every output and
+  both materialised errors, every step;
+* the same step on GPT 1.3B x 16 with the clamp, over five steps across a
+  periodic reset: all 16 workers' rows, the server, the decompressed
+  momentum and every parameter;
 * the 1-bit LAMB step on the 302-tensor buffer x 16 (compress with the layer
   coefficients, server, LAMB step from the sign words): all 16 workers, the
   server, m / k, x, the fresh variance and every layer's ratio, r_t, c_t and
@@ -32,14 +35,13 @@ import torch
 from momentum_compression_amd import onebit as ob
 from momentum_compression_amd.state import LambState, OneBitGroup
 from oracle import cref as R
-from tests._gpu import device, host, same_whole
+from tests._gpu import device, host, same_whole, same_whole_par
 from workloads import configs as C
 from workloads import synth as S
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
 F32 = np.float32
 THREADS = 16  # host threads for the oracle's independent rows and chunks
-GPT_ROWS = (0, 7, 15)  # worker rows of the 1.3B x 16 test (None: all)
 
 
 def _free():
@@ -133,29 +135,114 @@ def test_bert_large_335M_x8_bench_step_whole_buffer():
     _free()
 
 
-def test_gpt_1_3B_x16_whole_rows_server_and_step():
-    """GPT 1.3B x 16 with the 2.0 clamp, across the reset at t = 2000: whole
-    rows of workers 0, 7 and 15 free-running, and the server, the
-    decompressed momentum and every parameter on the whole buffer. The server
-    takes the GPU's sign words and scales of the other workers, checked bit
-    for bit wherever computed. (All 16 rows pass too, but take four minutes
-    on the host: ROWS = None below.)"""
+class _Rows:
+    """Worker rows checked one at a time against the C++ oracle, each row's
+    chunks in parallel on the host, through pinned staging buffers: the host
+    holds the oracle's error rows and one row of everything else."""
+
+    def __init__(self, N: int):
+        self.pm = torch.empty(N, dtype=torch.float32, pin_memory=True)
+        self.pg = torch.empty(N, dtype=torch.float32, pin_memory=True)
+        self.gc = np.empty(N, dtype=F32)
+
+    def fetch(self, t: torch.Tensor) -> np.ndarray:
+        """A device row in the pinned buffer (valid until the next fetch)."""
+        self.pg.copy_(t)
+        return self.pg.numpy()
+
+    def workers(self, grp, m, e_state, reset, tag, clip=0.0, k=None):
+        """The oracle's worker compression of every row from its own error
+        state ``e_state`` (updated in place), compared with the GPU's
+        compensated values, sign words and scales. Returns those words and
+        scales (equal to the oracle's)."""
+        gpu_bits, gpu_s = host(grp.bits), host(grp.scales)
+        for i in range(grp.n):
+            self.pm.copy_(m[i])
+            w = R.worker_compress_row(self.pm.numpy(), e_state[i], grp.n, clip, reset, k,
+                                      threads=THREADS, gc_out=self.gc, e_out=e_state[i])
+            same_whole_par(self.fetch(grp.ef[i]), w["gc"], f"{tag} worker {i} compensated values")
+            same_whole(gpu_bits[i], w["bits"], f"{tag} worker {i} sign words")
+            same_whole(gpu_s[i], w["s"], f"{tag} worker {i} scales")
+        return gpu_bits, gpu_s
+
+
+def test_adam_2_20_x4_ten_steps_whole_buffer():
+    """The 2^20 x 4 workload at its own shape (chunk 2^18, m ~ N(0, 1e-3)
+    drawn fresh per worker and step, zero initial errors): ten free-running
+    steps of compress, server and decompression (1-bit Adam article, 2.1:
+    the error is carried over every step), then the frozen-v Adam step.
+    Every worker's compensated values, sign words, scales and materialised
+    error, the server's, the decompressed momentum and the parameters are
+    compared with the C++ oracle on the whole buffer at every step."""
     dev = device()
-    wl = C.get("gpt_1.3B_x16")
+    wl = C.get("adam_2^20_x4")
     N, n = wl.N, wl.n
-    _need(dev, int(n * N * 4 * 2.2 + N * 4 * 6))
-    print(f"[whole] {wl.name} N={N} n={n}", flush=True)
+    assert (N, n, wl.L, wl.steps) == (1 << 20, 4, 1 << 18, 10)
+    print(f"[whole] {wl.name} N={N} n={n} steps={wl.steps}", flush=True)
     sig = S.per_element(S.segment_sigmas(wl), wl, dev)
     grp = OneBitGroup(N, n, dev, clip=wl.clip, reset_interval=wl.reset_interval)
     x = S.params(wl, dev)
     v = S.frozen_variance(wl, dev)
     m = torch.empty((n, N), dtype=torch.float32, device=dev)
     x_ref, v_h = host(x).copy(), host(v)
-    rows = GPT_ROWS if GPT_ROWS is not None else tuple(range(n))
-    e_ref = {i: np.zeros(N, dtype=F32) for i in rows}
+    e_ref = np.zeros((n, N), dtype=F32)
     E_ref = np.zeros(N, dtype=F32)
-    t0 = 1999
-    for t in (t0, t0 + 1, t0 + 2):
+    for t in range(1, wl.steps + 1):
+        S.momentum(wl, t, dev, sigma_elem=sig, out=m)
+        first = t == 1
+        grp.compress(m, t, first=first)
+        grp.server(t, first=first, decompress=True)
+        grp.adam_step(x, v, wl.lr, wl.eps)
+        e_gpu, E_gpu = grp.worker_error(), grp.server_error()
+        torch.cuda.synchronize()
+        tag = f"{wl.name} t={t}"
+        w = R.worker_compress(host(m), e_ref, clip=wl.clip, reset=first, threads=n)
+        _same(host(grp.ef), w["gc"], f"{tag} worker compensated values")
+        _same(host(grp.bits), w["bits"], f"{tag} worker sign words")
+        _same(host(grp.scales), w["s"], f"{tag} worker scales")
+        _same(host(e_gpu), w["e"], f"{tag} worker errors")
+        sv = R.server_reduce(w["bits"], w["s"], E_ref, reset=first, threads=n)
+        _same(host(grp.sv_bits), sv["bits"], f"{tag} server sign words")
+        _same(host(grp.sv_scales), sv["S"], f"{tag} server scales")
+        _same(host(grp.sv_ef), sv["g2"], f"{tag} server compensated values")
+        _same(host(E_gpu), sv["E"], f"{tag} server error")
+        mbar = R.decompress(sv["bits"], sv["S"])
+        _same(host(grp.mbar), mbar, f"{tag} decompressed momentum")
+        x_ref = R.adam_frozen_step(x_ref, mbar, v_h, wl.lr, wl.eps)
+        _same(host(x), x_ref, f"{tag} parameters")
+        e_ref, E_ref = w["e"], sv["E"]
+    print(f"[whole] {wl.name}: {wl.steps} steps ok", flush=True)
+    del grp, x, v, m, sig
+    _free()
+
+
+def test_gpt_1_3B_x16_whole_buffer_five_steps():
+    """GPT 1.3B x 16 with the 2.0 clamp (1-bit Adam article, 4.1) over the
+    five steps of the workload, numbered t = 1998 ... 2002 so that the
+    periodic reset at t = 2000 falls in the middle (the first step starts
+    from zero errors): all 16 workers' rows free-running on the oracle's own
+    error state, then the server, the decompressed momentum and every
+    parameter, each on the whole buffer."""
+    import time
+
+    dev = device()
+    wl = C.get("gpt_1.3B_x16")
+    N, n = wl.N, wl.n
+    _need(dev, int(n * N * 4 * 2.2 + N * 4 * 6))
+    print(f"[whole] {wl.name} N={N} n={n} steps={wl.steps}", flush=True)
+    sig = S.per_element(S.segment_sigmas(wl), wl, dev)
+    grp = OneBitGroup(N, n, dev, clip=wl.clip, reset_interval=wl.reset_interval)
+    x = S.params(wl, dev)
+    v = S.frozen_variance(wl, dev)
+    m = torch.empty((n, N), dtype=torch.float32, device=dev)
+    rows = _Rows(N)
+    x_ref, v_h = rows.fetch(x).copy(), rows.fetch(v).copy()
+    e_ref = [np.zeros(N, dtype=F32) for _ in range(n)]
+    E_ref = np.zeros(N, dtype=F32)
+    t0 = 1998
+    steps = list(range(t0, t0 + wl.steps))
+    assert 2000 in steps[1:]
+    for t in steps:
         S.momentum(wl, t, dev, sigma_elem=sig, out=m)
         first = t == t0
         reset = first or grp.is_reset(t)
@@ -164,33 +251,50 @@ def test_gpt_1_3B_x16_whole_rows_server_and_step():
         grp.adam_step_packed(x, v, wl.lr, wl.eps, decompress=True)
         torch.cuda.synchronize()
         tag = f"{wl.name} t={t}{' (reset)' if reset else ''}"
-        bits, s = _workers(grp, m, e_ref, reset, tag, clip=wl.clip, rows=rows)
-        sv = _server(grp, bits, s, E_ref, reset, tag)
+        a = time.perf_counter()
+        bits, s = rows.workers(grp, m, e_ref, reset, tag, clip=wl.clip)
+        b = time.perf_counter()
+        sv = R.server_reduce(bits, s, E_ref, reset=reset, threads=THREADS)
+        _same(host(grp.sv_bits), sv["bits"], f"{tag} server sign words")
+        _same(host(grp.sv_scales), sv["S"], f"{tag} server scales")
+        same_whole_par(rows.fetch(grp.sv_ef), sv["g2"], f"{tag} server compensated values")
         E_ref = sv["E"]
-        mbar = R.decompress(sv["bits"], sv["S"])
-        _same(host(grp.mbar), mbar, f"{tag} decompressed momentum")
-        x_ref = R.adam_frozen_step(x_ref, mbar, v_h, wl.lr, wl.eps)
-        _same(host(x), x_ref, f"{tag} parameters")
-        del sv, mbar, bits, s
-        print(f"[whole] {tag} ok", flush=True)
-    del grp, x, v, m, sig, e_ref, E_ref, x_ref
+        mbar = R.decompress(sv["bits"], sv["S"], threads=THREADS)
+        del sv
+        same_whole_par(rows.fetch(grp.mbar), mbar, f"{tag} decompressed momentum")
+        x_ref = R.adam_frozen_step(x_ref, mbar, v_h, wl.lr, wl.eps, threads=THREADS)
+        same_whole_par(rows.fetch(x), x_ref, f"{tag} parameters")
+        del mbar, bits, s
+        print(f"[whole] {tag} ok (workers {b - a:.0f} s, rest {time.perf_counter() - b:.0f} s)",
+              flush=True)
+    del grp, x, v, m, sig, e_ref, E_ref, x_ref, rows
     _free()
 
 
 def test_bert_large_lamb_302t_x16_whole_buffer():
+    """The fixed per-layer coefficients k_l are taken from the momentum at
+    the end of warmup (1-bit LAMB page, layer-scaling paragraph): the
+    library's momentum scale on m_Tw, bit-identical to the oracle's k_l, and
+    m_Tw is also the first compressed step's previous momentum."""
+    from momentum_compression_amd.state import momentum_scale
+
     dev = device()
     wl = C.get("bert_large_lamb_302t_x16")
     N, n = wl.N, wl.n
     _need(dev, int(n * N * 4 * 2.2 + N * 4 * 12))
     print(f"[whole] {wl.name} N={N} n={n} segments={len(wl.segments)}", flush=True)
     off = np.array(C.segment_offsets(wl.segments), dtype=np.int64)
-    k, c_avg = S.lamb_tables(wl)
-    k_el = np.repeat(k, np.diff(off)).astype(F32)
+    c_avg = S.lamb_c_avg(wl)
     sig = S.per_element(S.segment_sigmas(wl), wl, dev)
-    off_d, k_d = torch.from_numpy(off).to(dev), torch.from_numpy(k).to(dev)
+    off_d = torch.from_numpy(off).to(dev)
+    m_tw = S.lamb_prev_momentum(wl, dev, sig)
+    k_d = momentum_scale(m_tw, off_d)
+    k = R.momentum_scale(host(m_tw), off)
+    _same(host(k_d), k, "k_l from the warmup momentum")
+    assert np.all(k > 0) and len(np.unique(k)) > 100
+    k_el = np.repeat(k, np.diff(off)).astype(F32)
     grp = OneBitGroup(N, n, dev, seg_off=off_d, seg_k=k_d, keep_prev=True)
-    st = LambState.create(S.params(wl, dev), S.frozen_variance(wl, dev),
-                          S.lamb_prev_momentum(wl, dev, sig), off_d,
+    st = LambState.create(S.params(wl, dev), S.frozen_variance(wl, dev), m_tw, off_d,
                           torch.from_numpy(c_avg).to(dev))
     # a second state that reads m_{t-1} packed from the second step on
     st_p = LambState.create(st.x.clone(), st.v_frozen, st.m_prev.clone(), off_d,

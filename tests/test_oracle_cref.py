@@ -303,6 +303,50 @@ def test_int8_threaded_slices_equal_one_call():
             _eq(many[key], one[key], f"int8 threads={threads} {key}")
 
 
+def test_row_chunks_threaded_equal_one_call():
+    """The chunk-parallel worker row, slice-parallel decompression and Adam
+    step give the same bytes as one call (chunks and elements are
+    independent), with clamp, k, the step-ratio error and a reset."""
+    rng = np.random.default_rng(51)
+    n, L = 5, 64 * 7
+    N = n * L
+    m = (rng.standard_normal(N) * 1e-3).astype(F32)
+    e = (rng.standard_normal(N) * 1e-4).astype(F32)
+    k = np.exp(rng.uniform(-3, 3, N)).astype(F32)
+    ratio = np.exp(rng.uniform(-1, 1, N)).astype(F32)
+    for kw in (dict(), dict(clip=2e-3, k=k), dict(err_ratio=ratio), dict(reset=True),
+               dict(unit_scale=True)):
+        one = R.worker_compress_row(m, e.copy(), n, **kw)
+        gc, eo = np.empty(N, dtype=F32), np.empty(N, dtype=F32)
+        many = R.worker_compress_row(m, e.copy(), n, threads=3, gc_out=gc, e_out=eo, **kw)
+        for key in ("gc", "bits", "s", "e"):
+            _eq(many[key], one[key], f"row threads {kw.keys()} {key}")
+        assert many["gc"] is gc and many["e"] is eo
+    sb = rng.integers(0, 1 << 32, N // 32, dtype=np.uint32)
+    S = rng.uniform(0, 1e-3, n).astype(F32)
+    for kk in (None, k):
+        _eq(R.decompress(sb, S, kk, threads=4), R.decompress(sb, S, kk), "decompress threads")
+    wb = rng.integers(0, 1 << 32, (n, N // 32), dtype=np.uint32)
+    ws = rng.uniform(0, 1e-3, (n, n)).astype(F32)
+    E = (rng.standard_normal(N) * 1e-4).astype(F32)
+    for reset in (False, True):
+        full = R.server_reduce(wb, ws, E, reset=reset)
+        for c in (0, 2, n - 1):
+            one = R.server_reduce_chunk(wb, ws, E[:(c + 1) * L], c, reset=reset)
+            sl = slice(c * L, (c + 1) * L)
+            for key in ("avg", "g2", "E"):
+                _eq(one[key][sl], full[key][sl], f"server chunk {c} {key}")
+            _eq(one["bits"][c * L // 32:], full["bits"][c * L // 32:(c + 1) * L // 32],
+                f"server chunk {c} words")
+            assert one["S"][c] == full["S"][c]
+    N2 = 4096 * 3 + 64  # long enough for three slices
+    x = (rng.standard_normal(N2) * 0.02).astype(F32)
+    v = (np.abs(rng.standard_normal(N2)) * 1e-6 + 1e-8).astype(F32)
+    mb = (rng.standard_normal(N2) * 1e-3).astype(F32)
+    _eq(R.adam_frozen_step(x, mb, v, 6e-5, 1e-6, threads=3),
+        R.adam_frozen_step(x, mb, v, 6e-5, 1e-6), "adam threads")
+
+
 # ------------------------------------- pins the pages fix, run on the C++ oracle
 
 def _frac(x):
@@ -494,3 +538,29 @@ def test_exact_sums_against_fsum_and_ties():
     assert R.exact_sum_f64(np.array([1.0, 2.0 ** -52, 2.0 ** -53])) == 1 + 2.0 ** -51
     assert np.isnan(R.exact_sumsq(np.array([1, np.nan, np.inf], F32)))
     assert R.exact_sumsq(np.array([1, -np.inf], F32)) == np.inf
+
+
+def test_exact_sums_at_the_extreme_exponents():
+    """The wide-integer sums at the ends of their ranges: the largest binary32
+    squared (2^256 ulp-scale terms) and the smallest subnormal squared
+    (2^-298), the largest and smallest binary64 values, and the exact mean
+    of binary32 values at both ends, each against an independent exact sum
+    (math.fsum, Fractions)."""
+    import math
+
+    fmax, tiny32 = np.finfo(F32).max, F32(2.0 ** -149)
+    for x in (np.full(3000, fmax, F32), np.array([fmax, tiny32, -fmax, tiny32], F32),
+              np.full(777, tiny32, F32), np.array([tiny32, 1, fmax], F32)):
+        assert R.exact_sumsq(x) == math.fsum((x.astype(np.float64) ** 2).tolist())
+    dmax, dtiny = np.finfo(np.float64).max, 5e-324
+    for y in (np.array([dmax / 4, dmax / 4, dmax / 8]), np.full(999, dtiny),
+              np.array([dmax / 2, dtiny, dtiny]), np.array([dtiny, 1.0, dtiny])):
+        assert R.exact_sum_f64(y) == math.fsum(y.tolist())
+    for x in (np.array([fmax, fmax, tiny32, fmax], F32), np.array([tiny32] * 5 + [0] * 59, F32)):
+        exact = sum((abs(Fraction(float(v))) for v in x), Fraction(0)) / x.size
+        got = R.mean_abs_f32(x)
+        lo, hi = np.nextafter(got, F32(0)), np.nextafter(got, F32(np.inf))
+        d = abs(Fraction(float(got)) - exact)
+        assert d <= abs(Fraction(float(lo)) - exact)
+        if np.isfinite(hi):
+            assert d <= abs(Fraction(float(hi)) - exact)
