@@ -8,16 +8,18 @@ the frozen-variance Adam update.  The decompression runs inside the Adam
 pass, which reads the packed server words once and writes both the
 decompressed momentum and the parameters; the separate decompression and
 Adam kernels are timed after the step as a row of their own.  Default
-workload: BERT-Large-sized flat buffer of 335,141,888 fp32 elements,
-8 simulated workers.
+workload: the GPT-style 1.3B-parameter buffer (1,311,528,960 fp32 elements,
+291 tensors) with 16 simulated workers, clamp 2.0 and the error reset every
+2000 steps (the 1-bit Adam article's GPT-3 1.3B workload); the BERT-Large
+335M x 8 buffer, the LAMB, INT8, fused and warmup paths are rows.
 
 Prints ONE JSON line.  `value` = compressed worker elements per second
 (n * N per step).  `roofline` reports the dominant kernel (worker compress)
 against 8 TB/s of HBM using its algorithmic bytes (12.125 B per element:
 read m and the error state, write the state and 1 bit), with the duration
 measured by HIP events on the launch stream.  `cpu_baseline` times the C++
-CPU oracle on one thread over one whole step of the same workload, on the
-bench's own inputs.
+CPU oracle on a bounded sample of the same step (chunk 0 of every worker:
+1/n of the step's work), on the bench's own inputs.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
     python bench.py --only compress|server|decompress_adam|decompress|adam|copy  # profiling aid
@@ -50,7 +52,10 @@ def b_server(n: int) -> float:  # n/8 bits in, state 4 in + 4 out, 1/8 bit out
     return 8.125 + n / 8.0
 
 
-COUNTER_FILE = os.path.join(ROOT, "profiles", "compress_bert_large_335M_x8_counters.txt")
+def counter_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"compress_{workload}_counters.txt")
+
+
 KERNEL_SOURCES = [os.path.join(ROOT, "momentum_compression_amd", "csrc", f)
                   for f in ("compress.hip", "common.h")]
 
@@ -68,13 +73,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(launch_elems: int):
+def read_traffic(workload: str, launch_elems: int):
     """HBM bytes per compress launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source (else None)."""
-    if not os.path.exists(COUNTER_FILE):
+    summary of the workload, if it was taken on the current kernel source
+    (else None)."""
+    path = counter_file(workload)
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(COUNTER_FILE):
+    for line in open(path):
         if ":" in line:
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
@@ -102,45 +109,72 @@ def _cpu_model() -> str:
 
 
 def cpu_baseline(wl, m, x, v):
-    """Time the C++ oracle on one whole step of the workload: compress of all
-    n workers, the n server chunks, decompression and the Adam step. A first
-    (reset) step runs before it, so the timed step carries the error like the
-    steps on the GPU; it is timed on one thread (the reported value), then
-    once more with the workers' rows and the server chunks spread over the
-    host's threads (bit-identical: rows and chunks are independent).
-    m [n, N], x, v [N]: host float32."""
+    """Time the C++ oracle on a bounded sample of one step of the workload:
+    chunk 0 of every worker (compress of the n worker-chunk pairs, the server
+    of chunk 0, its decompression and Adam step), which is 1/n of the step's
+    work, so the step's rate is n L worker elements over the sample's time.
+    A reset step on the same momenta runs first, untimed, so the timed
+    compression carries the error like the steps on the GPU. The sample runs
+    on one thread (the reported value), then once more with the worker
+    chunks and the tail's slices over the host's threads (the server chunk
+    stays on one thread). m [n, N], x, v [N]: device float32; only chunk 0
+    is copied to the host."""
+    import numpy as np
+
     from oracle import cref as R
 
-    n, N = wl.n, wl.N
+    n, N, L = wl.n, wl.N, wl.L
     R.load()
     threads = max(1, min(16, os.cpu_count() or 1))
-    secs = []
-    e = E = None
-    for t, th in ((1, 1), (2, 1), (3, threads)):
-        reset = t == 1
+    mh = m[:, :L].cpu().numpy()
+    xh, vh = x[:L].cpu().numpy(), v[:L].cpu().numpy()
+    W = L // 32
+
+    def sample(reset, e, E, th):
+        """Worker rows of one chunk (n = 1 per call), the server of chunk 0
+        over those words, then the tail; returns (seconds, e, E)."""
         t0 = time.perf_counter()
-        w = R.worker_compress(m, e, clip=wl.clip, reset=reset, keep_gc=False, threads=th)
-        sv = R.server_reduce(w["bits"], w["s"], E, reset=reset, threads=th)
-        mbar = R.decompress(sv["bits"], sv["S"])
-        x = R.adam_frozen_step(x, mbar, v, wl.lr, wl.eps)
-        secs.append(time.perf_counter() - t0)
-        e, E = w["e"], sv["E"]
-        del w, sv, mbar
+        bits = np.zeros((n, N // 32), dtype=np.uint32)  # chunk 0's words at the row starts
+        s = np.zeros((n, n), dtype=np.float32)
+        e_new = np.empty((n, L), dtype=np.float32)
+
+        def pair(i):
+            w = R.worker_compress_row(mh[i], None if reset else e[i], 1, wl.clip, reset,
+                                      e_out=e_new[i])
+            bits[i, :W], s[i, 0] = w["bits"], w["s"][0]
+
+        R._run(pair, range(n), th)
+        t1 = time.perf_counter()
+        # the server of chunk 0 sees exactly these words and scales (the
+        # other chunks' words are zero and never read)
+        sv = R.server_reduce_chunk(bits, s, E, 0, reset=reset)
+        t2 = time.perf_counter()
+        mbar = R.decompress(sv["bits"][:W], sv["S"][:1], threads=th)
+        R.adam_frozen_step(xh, mbar, vh, wl.lr, wl.eps, threads=th)
+        t3 = time.perf_counter()
+        return (t3 - t0, (t1 - t0, t2 - t1, t3 - t2)), e_new, sv["E"]
+
+    _, e, E = sample(True, None, None, threads)
+    (sec1, parts1), _, _ = sample(False, e, E, 1)
+    (secm, partsm), _, _ = sample(False, e, E, threads)
+    fmt = "compress {:.1f} s, server {:.1f} s, decompression and Adam {:.1f} s"
     return {
-        "value": n * N / secs[1],
+        "value": n * L / sec1,
         "unit": "elements/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"one whole step of the workload ({n} x {N} worker elements: compress, "
-                   f"{n} server chunks, decompression, Adam) by the C++ oracle on one thread, "
-                   f"on the bench's own inputs copied from the GPU, after a first (reset) "
-                   f"step; reset step {secs[0]:.1f} s, timed step {secs[1]:.1f} s"),
+        "sample": (f"chunk 0 ({L} elements) of all {n} workers, 1/{n} of a step of "
+                   f"{wl.name}: compress of the {n} worker chunks, the server of chunk 0, its "
+                   f"decompression and Adam step, by the C++ oracle on one thread, on the "
+                   f"bench's own inputs copied from the GPU, after an untimed reset step on "
+                   f"the same momenta; {sec1:.1f} s ({fmt.format(*parts1)}), scaled to "
+                   f"the step as {n} L worker elements per sample"),
         "cpu_model": _cpu_model(),
         "threads_available": os.cpu_count(),
-        "multithreaded": {"value": n * N / secs[2], "unit": "elements/s", "cores": threads,
-                          "sample": (f"the next step with the {n} worker rows and the {n} "
-                                     f"server chunks over {threads} threads (decompression "
-                                     f"and Adam on one): {secs[2]:.1f} s")},
+        "multithreaded": {"value": n * L / secm, "unit": "elements/s", "cores": threads,
+                          "sample": (f"the same sample with the {n} worker chunks and the "
+                                     f"tail's slices over {threads} threads (the server "
+                                     f"chunk on one): {secm:.1f} s ({fmt.format(*partsm)})")},
     }
 
 
@@ -186,6 +220,15 @@ def _rel(a, b) -> float:
     return na / nb if nb > 0 else float("nan")
 
 
+def _inputs(wl) -> str:
+    if wl.sigma_mode == "const1e-3":
+        return "momentum N(0, 1e-3), fresh per worker"
+    per = "per 2^20-element block" if wl.name == "bert_large_335M_x8" else "per tensor"
+    lo, hi = {"loguniform_1e-5_1e-2": ("1e-5", "1e-2"),
+              "loguniform_1e-6_1e-1": ("1e-6", "1e-1")}[wl.sigma_mode]
+    return f"momentum N(0, sigma), sigma log-uniform [{lo}, {hi}] {per}"
+
+
 def _row(ms: float, nbytes: float, elems: int) -> dict:
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"ms": round(ms, 4), "elements_per_s": elems / (ms * 1e-3),
@@ -205,7 +248,7 @@ def measure_lamb(steps: int, warmup: int) -> dict:
     import torch
 
     from momentum_compression_amd import onebit as ob
-    from momentum_compression_amd.state import LambState, OneBitGroup
+    from momentum_compression_amd.state import LambState, OneBitGroup, momentum_scale
     from workloads import configs as C
     from workloads import synth as S
 
@@ -214,9 +257,12 @@ def measure_lamb(steps: int, warmup: int) -> dict:
     N, n = wl.N, wl.n
     print(f"[bench] rows: {wl.name} N={N} n={n}", file=sys.stderr, flush=True)
     off = np.array(C.segment_offsets(wl.segments), dtype=np.int64)
-    k, c_avg = S.lamb_tables(wl)
-    off_d, k_d = torch.from_numpy(off).to(dev), torch.from_numpy(k).to(dev)
+    c_avg = S.lamb_c_avg(wl)
+    off_d = torch.from_numpy(off).to(dev)
     sig = S.per_element(S.segment_sigmas(wl), wl, dev)
+    # the fixed layer coefficients k_l from the momentum at the end of warmup
+    k_d = momentum_scale(S.lamb_prev_momentum(wl, dev, sig), off_d)
+    n_seg = k_d.numel()
     m = S.momentum(wl, 1, dev, sigma_elem=sig)
     grp = OneBitGroup(N, n, dev, seg_off=off_d, seg_k=k_d, keep_prev=True)
     st = LambState.create(S.params(wl, dev), S.frozen_variance(wl, dev),
@@ -239,7 +285,7 @@ def measure_lamb(steps: int, warmup: int) -> dict:
 
     def dec():
         ob.onebit_decompress(grp.sv_bits, grp.sv_scales, grp.mbar, N, n, seg_off=off_d,
-                             seg_k=k_d, n_seg=len(k))
+                             seg_k=k_d, n_seg=n_seg)
 
     def lamb():
         st.step(grp.mbar, wl.lr, wl.eps, wl.beta1, wl.beta2, wl.r_threshold, wl.r_min, wl.r_max)
@@ -281,6 +327,9 @@ def measure_lamb(steps: int, warmup: int) -> dict:
            "server_step_ratio_ef": _row(ms[5], b_server(n) * N, N)}
     r = st2.r.double()
     out["r_t"] = {"min": r.min().item(), "median": r.median().item(), "max": r.max().item()}
+    kk = k_d.double()
+    out["k_l"] = {"from": "momentum scale of the warmup momentum", "min": kk.min().item(),
+                  "median": kk.median().item(), "max": kk.max().item()}
     del grp, st, st2, st3, m
     torch.cuda.empty_cache()
     return out
@@ -390,11 +439,11 @@ def measure_warmup(steps: int, warmup: int) -> dict:
     return out
 
 
-def measure_gpt(steps: int, warmup: int) -> dict:
-    """The 1.3B GPT-style buffer with 16 workers (clamp 2.0, reset every 2000
-    steps): compress, server, and the decompression with the frozen-v Adam
-    step in one pass, at about 190 GB resident; the decompression and Adam
-    kernels are also timed on their own."""
+def measure_adam_row(name: str, steps: int, warmup: int) -> dict:
+    """Another 1-bit Adam workload as a row (the BERT-Large 335M x 8 buffer,
+    or the 1.3B GPT-style buffer x 16 with its clamp and reset): compress,
+    server, and the decompression with the frozen-v Adam step in one pass;
+    the decompression and Adam kernels are also timed on their own."""
     import torch
 
     from momentum_compression_amd import onebit as ob
@@ -403,7 +452,7 @@ def measure_gpt(steps: int, warmup: int) -> dict:
     from workloads import synth as S
 
     dev = torch.device("cuda:0")
-    wl = C.get("gpt_1.3B_x16")
+    wl = C.get(name)
     N, n = wl.N, wl.n
     print(f"[bench] rows: {wl.name} N={N} n={n}", file=sys.stderr, flush=True)
     sig = S.per_element(S.segment_sigmas(wl), wl, dev)
@@ -437,7 +486,8 @@ def measure_gpt(steps: int, warmup: int) -> dict:
     step_ms = ms[0] + ms[1] + ms[4]  # the step with the decompression inside the Adam pass
     out = {"workload": wl.name, "N": N, "workers": n, "step_ms": round(step_ms, 4),
            "worker_elements_per_s": n * N / (step_ms * 1e-3),
-           "compress_clamp": _row(ms[0], B_COMPRESS * n * N, n * N),
+           "compress_clamp" if wl.clip > 0 else "compress": _row(ms[0], B_COMPRESS * n * N,
+                                                                  n * N),
            "server": _row(ms[1], b_server(n) * N, N),
            "decompress_adam": _row(ms[4], B_DECOMPRESS_ADAM * N, N),
            "decompress": _row(ms[2], B_DECOMPRESS * N, N),
@@ -576,7 +626,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="bert_large_335M_x8")
+    ap.add_argument("--workload", default="gpt_1.3B_x16")
     ap.add_argument("--only", default="", choices=["", "compress", "server", "decompress_adam",
                                                    "decompress", "adam", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -585,7 +635,7 @@ def main() -> int:
                          "(profiling aid; prints its own JSON line)")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the rows measured after the headline step (LAMB, INT8, fused, "
-                         "warmup, GPT 1.3B, copy reference)")
+                         "warmup, the other Adam workload, copy reference)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -710,7 +760,7 @@ def main() -> int:
                    "server_error_rel": _rel(grp.server_error(), grp.sv_ef)}
 
     comp_gbs = bytes_["compress"] / (ms["compress"] * 1e-3) / 1e9
-    traffic = read_traffic(n * N)
+    traffic = read_traffic(wl.name, n * N)
     out = {
         "metric": METRIC,
         "value": n * N / (ms_per_step * 1e-3),
@@ -725,8 +775,9 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "N": N, "workers": n, "chunk": wl.L,
+                   "clip": wl.clip, "reset_interval": wl.reset_interval,
                    "path": "compress+server+(decompress+adam_frozen_v in one pass)",
-                   "inputs": "momentum N(0, sigma), sigma log-uniform [1e-5, 1e-2] per 2^20 block"},
+                   "inputs": _inputs(wl)},
         "roofline": {"bound": "hbm", "kernel": "onebit_compress", "achieved": round(comp_gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(comp_gbs / PEAK_HBM_GBS, 4),
@@ -743,18 +794,18 @@ def main() -> int:
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on one step of the workload", file=sys.stderr,
               flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, m.cpu().numpy(), x.cpu().numpy(),
-                                           v.cpu().numpy())
+        out["cpu_baseline"] = cpu_baseline(wl, m, x, v)
     else:
         out["cpu_baseline"] = None
     if not args.no_rows:
+        other = "bert_large_335M_x8" if wl.name == "gpt_1.3B_x16" else "gpt_1.3B_x16"
         del grp, m, x, v
         torch.cuda.empty_cache()
         out["rows"].update({"lamb": measure_lamb(max(3, args.steps // 2), 1),
                        "int8": measure_int8(max(3, args.steps // 2), 1),
                        "fused_adam_from_gradients": measure_fused(max(3, args.steps // 2), 1),
                        "warmup": measure_warmup(max(3, args.steps // 2), 1),
-                       "gpt_1.3B_x16": measure_gpt(max(3, args.steps // 2), 1),
+                       other: measure_adam_row(other, max(3, args.steps // 2), 1),
                        "copy_reference": measure_copy(max(3, args.steps // 2), 1)})
     print(json.dumps(out))
     return 0
