@@ -374,3 +374,14 @@ class LambWarmup:
         """The compressed phase's state: v_Tw = v, r = 1, c = c_avg, fresh
         variance v_Tw, previous global momentum m_Tw."""
         return LambState.create(self.x, self.v, self.m.clone(), self.seg_off, self.c_avg.clone())
+
+
+def momentum_scale(m: torch.Tensor, seg_off: torch.Tensor, stream=None) -> torch.Tensor:
+    """k_l of every layer from a momentum buffer m [N] (the end of warmup):
+    ``lamb_momentum_scale`` with a workspace of its own."""
+    N, S = m.numel(), seg_off.numel() - 1
+    ws = torch.empty(max(256, ob.warmup_workspace_bytes(N, S)), dtype=torch.uint8,
+                     device=m.device)
+    k = torch.empty(S, dtype=torch.float32, device=m.device)
+    ob.lamb_momentum_scale(m, N, seg_off, S, k, ws, stream=stream)
+    return k

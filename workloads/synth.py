@@ -97,26 +97,35 @@ def params(wl: Workload, device="cpu") -> torch.Tensor:
     return x
 
 
+def lamb_c_avg(wl: Workload) -> np.ndarray:
+    """Per-segment warmup averages c_avg of LAMB's layer coefficient
+    (float32), log-uniform in [0.5, 2]; the pad segment gets 1."""
+    rng = np.random.Generator(np.random.Philox(key=wl.seed * 31 + TAG_CAVG))
+    c_avg = np.exp(rng.uniform(math.log(0.5), math.log(2.0),
+                               size=len(wl.segments))).astype(np.float32)
+    if wl.pad:
+        c_avg[-1] = 1.0
+    return c_avg
+
+
 def lamb_tables(wl: Workload) -> Tuple[np.ndarray, np.ndarray]:
     """Per-segment fixed momentum coefficients k and warmup averages c_avg
-    (float32).  k is the reciprocal of the segment's generating sigma, i.e.
-    the coefficient that brings the segment to unit scale, standing in for
-    the warmup-norm coefficient; c_avg is log-uniform in [0.5, 2].  The pad
-    segment gets k = 1, c_avg = 1."""
+    (float32) for the small tests.  k is the reciprocal of the segment's
+    generating sigma, the coefficient that brings the segment to unit scale
+    (a stand-in for the coefficient from the warmup momentum, which the
+    full-size runs take from ``lamb_prev_momentum`` with the library's
+    momentum scale); the pad segment gets k = 1."""
     sig = segment_sigmas(wl)
     k = np.ones(len(sig), dtype=np.float32)
     nz = sig > 0
     k[nz] = (1.0 / sig[nz]).astype(np.float32)
-    rng = np.random.Generator(np.random.Philox(key=wl.seed * 31 + TAG_CAVG))
-    c_avg = np.exp(rng.uniform(math.log(0.5), math.log(2.0), size=len(sig))).astype(np.float32)
-    if wl.pad:
-        c_avg[-1] = 1.0
-    return k, c_avg
+    return k, lamb_c_avg(wl)
 
 
 def lamb_prev_momentum(wl: Workload, device="cpu", sigma_elem=None) -> torch.Tensor:
-    """Stand-in for the global momentum of the step before the first
-    compressed step: N(0, sigma_l) per segment."""
+    """The global momentum at the end of warmup, m_Tw: N(0, sigma_l) per
+    segment.  It is the previous momentum of the first compressed LAMB step
+    and the momentum the per-layer coefficients k_l are taken from."""
     if sigma_elem is None:
         sigma_elem = per_element(segment_sigmas(wl), wl, device)
     g = _gen(wl.seed, TAG_MPREV, 0, device)
