@@ -61,7 +61,7 @@ WarmupWs split_warmup_ws(void* ws, int64_t N, int32_t n_seg) {
 size_t partial_bytes(int64_t N, int32_t n) {
     const int64_t L = N / n;
     const ChunkPlan pw = make_plan(L, (int64_t)n * n, kCompressIters);
-    const ChunkPlan ps = make_plan(L, n, kServerIters);
+    const ChunkPlan ps = server_plan(L, n);
     const int64_t w = pw.bpc * n * n;
     const int64_t s = ps.bpc * n;
     return round_up((size_t)(w > s ? w : s) * sizeof(double));
@@ -175,7 +175,7 @@ int onebit_server_reduce_ex(const uint32_t* bits, const float* scales, float* ef
     if (!ws || ws_bytes < need) return ONEBIT_E_WORKSPACE;
     if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
 
-    const ChunkPlan plan = make_plan(N / n, n, kServerIters);
+    const ChunkPlan plan = server_plan(N / n, n);
     if (sum_depth(plan) > kMaxSumDepth || !groups_ok(plan.bpc)) return ONEBIT_E_SIZE;
     if (m_out && !groups_ok(ceil_div(N, (int64_t)kDecompressTiles * kTile))) return ONEBIT_E_SIZE;
     double* partials = static_cast<double*>(ws);

@@ -20,7 +20,8 @@ constexpr int kMaxIters = 4;            // tiles per workgroup: Adam (both forms
 // compression, two tiles for the server and the INT8 pass.
 constexpr int kCompressIters = 1;
 constexpr int kCompressUnroll = 1;
-constexpr int kServerIters = 2;
+constexpr int kServerIters = 2;         // up to 8 workers: one group per workgroup
+constexpr int kServerItersWide = 8;     // more workers: four pipelined groups per workgroup
 constexpr int kServerUnroll = 2;
 constexpr int kInt8Tiles = 2;
 constexpr int kDecompressTiles = 4;
@@ -42,7 +43,15 @@ struct ChunkPlan {
     int64_t bpc;      // workgroups per chunk
 };
 
-ChunkPlan make_plan(int64_t L, int64_t chunks, int32_t max_iters);
+// min_iters: the tiles one workgroup always covers (the server's group of
+// kServerUnroll tiles), so that 4 * iters bounds every thread's additions.
+ChunkPlan make_plan(int64_t L, int64_t chunks, int32_t max_iters, int32_t min_iters = 1);
+
+// The server's plan for n workers with chunks of L elements (the workspace
+// size and the launch take it from here).
+inline ChunkPlan server_plan(int64_t L, int32_t n) {
+    return make_plan(L, n, n > 8 ? kServerItersWide : kServerIters, kServerUnroll);
+}
 
 // Upper bound on the number of floating-point additions any one term passes
 // through in the fp64 chunk sum (per-thread sequence, wave butterfly, LDS

@@ -3,11 +3,13 @@
 //
 // Fast path.  The fp64 sum of non-negative terms, each passing through at
 // most d additions, is within gamma_d = d u / (1 - d u) (u = 2^-53) of the
-// exact sum relative to itself; with the final division, d <= kMaxSumDepth
-// = 12288 gives a relative error below 12289 * 2^-53 < 1.37e-12, under the
-// slack 2^-39 = 1.82e-12 used here.  If mu_hat (1 -+ 2^-39) lies strictly between
-// the two binary32 rounding boundaries around (float)mu_hat, the exact mean
-// rounds to the same value and the result is certified.
+// exact sum relative to itself; with the final division the mean is within
+// gamma_{d+1} <= (d + 1) u (1 + 3e-12) for d <= kMaxSumDepth = 12288.  The
+// launch passes the relative slack (d + 4) u for the plan's own depth d,
+// which also covers the rounding of mu_hat -+ slack in the comparison.  If
+// mu_hat (1 -+ slack) lies strictly between the two binary32 rounding
+// boundaries around (float)mu_hat, the exact mean rounds to the same value
+// and the result is certified.
 //
 // Exact path (taken when certification fails, e.g. at an exact tie).  The
 // same workgroup re-reads the chunk's stored values and accumulates the
@@ -121,7 +123,7 @@ __device__ __forceinline__ double fin_block_sum(double v, double* red) {
 __global__ __launch_bounds__(kFinThreads) void mean_finalize_kernel(
     const double* __restrict__ partials, int64_t bpc, int64_t L, const float* __restrict__ data,
     int64_t row_stride, int32_t chunks, float* __restrict__ out, int32_t unit,
-    float* __restrict__ prev) {
+    float* __restrict__ prev, double slack_rel) {
     __shared__ double red[kFinThreads / 64];
     __shared__ unsigned long long bins[256];
     __shared__ int exact;
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(kFinThreads) void mean_finalize_kernel(
             const float ru = __uint_as_float(rb + 1u);
             const double mlo = ((double)rd + (double)r) * 0.5;
             const double mhi = ((double)r + (double)ru) * 0.5;
-            const double slack = mu * 0x1p-39;
+            const double slack = mu * slack_rel;
             if (mu - slack > mlo && mu + slack < mhi) need_exact = 0;
         }
         exact = need_exact;
@@ -189,9 +191,11 @@ __global__ __launch_bounds__(kFinThreads) void mean_finalize_kernel(
 
 hipError_t launch_mean_finalize_keep(const double* partials, const ChunkPlan& plan,
                                      int64_t pairs, MeanTarget tgt, float* prev, hipStream_t st) {
+    // relative slack of the certification for this plan's summation depth
+    const double slack_rel = (double)(sum_depth(plan) + 4) * 0x1p-53;
     hipLaunchKernelGGL(mean_finalize_kernel, dim3((unsigned)pairs), dim3(kFinThreads), 0, st,
                        partials, plan.bpc, plan.L, tgt.data, tgt.row_stride, tgt.chunks, tgt.out,
-                       tgt.unit ? 1 : 0, prev);
+                       tgt.unit ? 1 : 0, prev, slack_rel);
     return hipGetLastError();
 }
 
@@ -201,13 +205,14 @@ hipError_t launch_mean_finalize(const double* partials, const ChunkPlan& plan, i
 }
 
 // ---------------------------------------------------------------- plan
-ChunkPlan make_plan(int64_t L, int64_t chunks, int32_t max_iters) {
+ChunkPlan make_plan(int64_t L, int64_t chunks, int32_t max_iters, int32_t min_iters) {
     ChunkPlan p;
     p.L = L;
     const int64_t tiles = (L + kTile - 1) / kTile;
     // aim for at least ~8 workgroups per CU (256 CUs) over all chunks
     int64_t iters = max_iters;
-    while (iters > 1 && ((tiles + iters - 1) / iters) * chunks < 2048) iters >>= 1;
+    while (iters > min_iters && ((tiles + iters - 1) / iters) * chunks < 2048) iters >>= 1;
+    if (iters < min_iters) iters = min_iters;
     p.iters = (int32_t)iters;
     p.bpc = (tiles + iters - 1) / iters;
     return p;
