@@ -205,6 +205,31 @@ int onebit_server_reduce_ex(const uint32_t* bits, const float* scales, float* ef
                             hipStream_t stream);
 
 /*
+ * onebit_server_reduce_ex for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace: the per-workgroup partial sums of the
+ * chunk means go to a fixed scratch array of 8 MiB (2^20 doubles) that the
+ * library holds, one copy per device, until the process ends.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine);
+ * the scratch's device address is looked up on the first call on a device.
+ * Arguments, layouts and results are exactly those of
+ * onebit_server_reduce_ex (bit-identical outputs), on the current device
+ * (the stream must belong to it).
+ * Limit: the server needs one double per workgroup, about N / 2048 of them
+ * for n <= 8 and N / 8192 for n > 8; calls needing more than 2^20 (N above
+ * about 2^31 elements for n <= 8, 2^33 for n > 8) return ONEBIT_E_WORKSPACE
+ * before any launch.  The scratch keeps the last call's contents; each call
+ * writes every partial it reads, so nothing needs clearing.  Calls that
+ * overlap on one device (different streams, or host threads) share the one
+ * scratch and race: serialise them.
+ */
+int onebit_server_reduce_noalloc(const uint32_t* bits, const float* scales, float* ef,
+                                 float* sv_scales, uint32_t* sv_bits, float* m_out,
+                                 const int64_t* seg_off, const float* seg_k,
+                                 const float* seg_err_ratio, int32_t n_seg, int64_t N,
+                                 int32_t n, int32_t reset, uint32_t flags, hipStream_t stream);
+
+/*
  * Decompress only: m_out = (B ? S[c] : -S[c]) [/ k_l] from server words and
  * scales (what every worker computes after the all-gather phase).
  */

@@ -2,6 +2,8 @@
 // Every check runs before the first HIP call, so invalid calls touch nothing.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 
 using namespace onebit;
@@ -68,6 +70,34 @@ size_t partial_bytes(int64_t N, int32_t n) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ONEBIT_OK : ONEBIT_E_HIP; }
+
+// Scratch of onebit_server_reduce_noalloc: the fp64 partial sums of the
+// server's chunk means (one per workgroup), in a file-scope device array.
+// Every device the library runs on holds its own copy until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it
+// is only a stand-in symbol): the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+constexpr size_t kNoAllocDoubles = (size_t)1 << 20;  // 8 MiB
+__device__ __align__(256) double scratch[kNoAllocDoubles];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+double* g_scratch[kMaxDevices];  // device address of `scratch`, per device
+
+int scratch_of_current_device(double** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return ONEBIT_E_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return ONEBIT_E_ARG;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return ONEBIT_E_HIP;
+        g_scratch[dev] = static_cast<double*>(p);
+    }
+    *out = g_scratch[dev];
+    return ONEBIT_OK;
+}
 
 }  // namespace
 
@@ -154,12 +184,15 @@ int onebit_compress_grad(const float* g, const uint32_t* mb_bits, const float* m
                               seg_off, seg_k, nullptr, n_seg, 0u, ws, ws_bytes, stream);
 }
 
-int onebit_server_reduce_ex(const uint32_t* bits, const float* scales, float* ef,
-                            float* sv_scales, uint32_t* sv_bits, float* m_out,
-                            const int64_t* seg_off, const float* seg_k,
-                            const float* seg_err_ratio, int32_t n_seg, int64_t N, int32_t n,
-                            int32_t reset, uint32_t flags, void* ws, size_t ws_bytes,
-                            hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the server calls (everything but the scratch).
+int check_server(const uint32_t* bits, const float* scales, float* ef, float* sv_scales,
+                 uint32_t* sv_bits, float* m_out, const int64_t* seg_off, const float* seg_k,
+                 const float* seg_err_ratio, int32_t n_seg, int64_t N, int32_t n,
+                 uint32_t flags) {
     int st = check_rows(N, n);
     if (st) return st;
     if (!bits || !scales || !ef || !sv_scales || !sv_bits) return ONEBIT_E_NULL;
@@ -171,14 +204,19 @@ int onebit_server_reduce_ex(const uint32_t* bits, const float* scales, float* ef
         return ONEBIT_E_ALIGN;
     if (flags & ~(ONEBIT_UNIT_SCALE | ONEBIT_KEEP_PREV)) return ONEBIT_E_ARG;
     if (N == 0) return ONEBIT_OK;
-    const size_t need = onebit_workspace_bytes(N, n, n_seg);
-    if (!ws || ws_bytes < need) return ONEBIT_E_WORKSPACE;
-    if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
-
     const ChunkPlan plan = server_plan(N / n, n);
     if (sum_depth(plan) > kMaxSumDepth || !groups_ok(plan.bpc)) return ONEBIT_E_SIZE;
     if (m_out && !groups_ok(ceil_div(N, (int64_t)kDecompressTiles * kTile))) return ONEBIT_E_SIZE;
-    double* partials = static_cast<double*>(ws);
+    return ONEBIT_OK;
+}
+
+// The server's launches on validated arguments, with the partial sums in
+// `partials` (server_plan(N / n, n).bpc * n doubles).
+int server_launch(const uint32_t* bits, const float* scales, float* ef, float* sv_scales,
+                  uint32_t* sv_bits, float* m_out, const int64_t* seg_off, const float* seg_k,
+                  const float* seg_err_ratio, int32_t n_seg, int64_t N, int32_t n,
+                  int32_t reset, uint32_t flags, double* partials, hipStream_t stream) {
+    const ChunkPlan plan = server_plan(N / n, n);
     hipError_t e = launch_server(bits, scales, ef, sv_scales, sv_bits, partials, N, n, plan,
                                  reset != 0, seg_off, seg_err_ratio, n_seg, stream);
     if (e != hipSuccess) return ONEBIT_E_HIP;
@@ -191,6 +229,45 @@ int onebit_server_reduce_ex(const uint32_t* bits, const float* scales, float* ef
         return hip_status(
             launch_decompress(sv_bits, sv_scales, m_out, seg_off, seg_k, n_seg, N, n, stream));
     return ONEBIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int onebit_server_reduce_ex(const uint32_t* bits, const float* scales, float* ef,
+                            float* sv_scales, uint32_t* sv_bits, float* m_out,
+                            const int64_t* seg_off, const float* seg_k,
+                            const float* seg_err_ratio, int32_t n_seg, int64_t N, int32_t n,
+                            int32_t reset, uint32_t flags, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+    int st = check_server(bits, scales, ef, sv_scales, sv_bits, m_out, seg_off, seg_k,
+                          seg_err_ratio, n_seg, N, n, flags);
+    if (st || N == 0) return st;
+    const size_t need = onebit_workspace_bytes(N, n, n_seg);
+    if (!ws || ws_bytes < need) return ONEBIT_E_WORKSPACE;
+    if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
+    return server_launch(bits, scales, ef, sv_scales, sv_bits, m_out, seg_off, seg_k,
+                         seg_err_ratio, n_seg, N, n, reset, flags, static_cast<double*>(ws),
+                         stream);
+}
+
+int onebit_server_reduce_noalloc(const uint32_t* bits, const float* scales, float* ef,
+                                 float* sv_scales, uint32_t* sv_bits, float* m_out,
+                                 const int64_t* seg_off, const float* seg_k,
+                                 const float* seg_err_ratio, int32_t n_seg, int64_t N, int32_t n,
+                                 int32_t reset, uint32_t flags, hipStream_t stream) {
+    int st = check_server(bits, scales, ef, sv_scales, sv_bits, m_out, seg_off, seg_k,
+                          seg_err_ratio, n_seg, N, n, flags);
+    if (st || N == 0) return st;
+    const ChunkPlan plan = server_plan(N / n, n);
+    if ((size_t)(plan.bpc * n) > kNoAllocDoubles) return ONEBIT_E_WORKSPACE;
+    double* partials = nullptr;
+    if ((st = scratch_of_current_device(&partials))) return st;
+    // every partial the finalize reads is written by this call's server
+    // kernel first, so the scratch needs no clearing
+    return server_launch(bits, scales, ef, sv_scales, sv_bits, m_out, seg_off, seg_k,
+                         seg_err_ratio, n_seg, N, n, reset, flags, partials, stream);
 }
 
 int onebit_server_reduce(const uint32_t* bits, const float* scales, float* ef, float* sv_scales,

@@ -61,6 +61,8 @@ _SIGNATURES = {
     "onebit_server_reduce_ex": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                          _c_i32, _c_i64, _c_i32, _c_i32, _c_u32, _c_p, _c_sz,
                                          _c_p]),
+    "onebit_server_reduce_noalloc": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                              _c_p, _c_i32, _c_i64, _c_i32, _c_i32, _c_u32, _c_p]),
     "int8_quantize": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32, _c_i32, _c_u64, _c_u32,
                                _c_p, _c_sz, _c_p]),
     "onebit_server_reduce": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i64,
@@ -224,6 +226,22 @@ def onebit_server_reduce_ex(bits, scales, ef, sv_scales, sv_bits, m_out, N: int,
         _buf(seg_off, n_seg + 1, "i64", "seg_off"), _buf(seg_k, n_seg, "f32", "seg_k"),
         _buf(seg_err_ratio, n_seg, "f32", "seg_err_ratio"), n_seg, N, n, int(bool(reset)), flags,
         _buf(ws, 0, "u8", "ws"), _nbytes(ws) if ws is not None else 0, _stream(stream)))
+
+
+def onebit_server_reduce_noalloc(bits, scales, ef, sv_scales, sv_bits, m_out, N: int, n: int,
+                                 reset: bool = False, seg_off=None, seg_k=None,
+                                 seg_err_ratio=None, n_seg: int = 0, flags: int = 0,
+                                 stream=None) -> None:
+    """``onebit_server_reduce_ex`` without a workspace (the library's fixed
+    per-device scratch)."""
+    _check("onebit_server_reduce_noalloc", load().onebit_server_reduce_noalloc(
+        _buf(bits, n * N // 32, "u32", "bits"), _buf(scales, n * n, "f32", "scales"),
+        _buf(ef, N, "f32", "ef"),
+        _buf(sv_scales, 2 * n if flags & ONEBIT_KEEP_PREV else n, "f32", "sv_scales"),
+        _buf(sv_bits, N // 32, "u32", "sv_bits"), _buf(m_out, N, "f32", "m_out"),
+        _buf(seg_off, n_seg + 1, "i64", "seg_off"), _buf(seg_k, n_seg, "f32", "seg_k"),
+        _buf(seg_err_ratio, n_seg, "f32", "seg_err_ratio"), n_seg, N, n, int(bool(reset)), flags,
+        _stream(stream)))
 
 
 def onebit_server_reduce(bits, scales, ef, sv_scales, sv_bits, m_out, N: int, n: int,

@@ -90,6 +90,32 @@ def test_server_and_other_validation(lib):
     assert i8(None, None, P, P, None, 256, 256, 1, 1, None) == ob.ONEBIT_E_NULL
 
 
+def test_server_noalloc_validation(lib):
+    """The allocation-free server refuses what the workspace form refuses,
+    with the same codes, and refuses sizes whose partial sums would not fit
+    its fixed 2^20-double scratch with ONEBIT_E_WORKSPACE, all before any
+    HIP call (N = 0 is a no-op)."""
+    f = lib.onebit_server_reduce_noalloc
+
+    def call(bits=P, sc=P, ef=P, svs=P, svb=P, m=None, off=None, k=None, r=None, nseg=0,
+             N=1 << 12, n=4, reset=0, flags=0):
+        return f(bits, sc, ef, svs, svb, m, off, k, r, nseg, N, n, reset, flags, None)
+
+    assert call(bits=None) == ob.ONEBIT_E_NULL
+    assert call(m=P + 4) == ob.ONEBIT_E_ALIGN
+    assert call(N=100) == ob.ONEBIT_E_SIZE
+    assert call(n=65, N=65 * 64) == ob.ONEBIT_E_SIZE
+    assert call(flags=4) == ob.ONEBIT_E_ARG
+    assert call(r=P) == ob.ONEBIT_E_ARG          # a step-ratio factor needs a layer table
+    assert call(off=P, k=None, nseg=2) == ob.ONEBIT_E_NULL
+    assert call(N=0) == ob.ONEBIT_OK
+    # n <= 8: one partial per 2048 elements, so 2^20 of them end at N = 2^31
+    # (sizes that fit are not called here: they would launch)
+    assert call(N=(1 << 31) + 8 * 2048, n=8) == ob.ONEBIT_E_WORKSPACE
+    # n > 8: one partial per 8192 elements
+    assert call(N=(1 << 33) + 16 * 8192 * 64, n=16) == ob.ONEBIT_E_WORKSPACE
+
+
 def test_compress_grad_validation(lib):
     f = lib.onebit_compress_grad
     args = [P, P, P, 0.9, P, P, P, 1 << 12, 4, 0.0, 0, None, None, 0, P, 1 << 30, None]
