@@ -20,8 +20,7 @@ constexpr int kMaxIters = 4;            // tiles per workgroup: Adam (both forms
 // compression, two tiles for the server and the INT8 pass.
 constexpr int kCompressIters = 1;
 constexpr int kCompressUnroll = 1;
-constexpr int kServerIters = 2;         // up to 8 workers: one group per workgroup
-constexpr int kServerItersWide = 8;     // more workers: four pipelined groups per workgroup
+constexpr int kServerIters = 2;
 constexpr int kServerUnroll = 2;
 constexpr int kInt8Tiles = 2;
 constexpr int kDecompressTiles = 4;
@@ -50,7 +49,7 @@ ChunkPlan make_plan(int64_t L, int64_t chunks, int32_t max_iters, int32_t min_it
 // The server's plan for n workers with chunks of L elements (the workspace
 // size and the launch take it from here).
 inline ChunkPlan server_plan(int64_t L, int32_t n) {
-    return make_plan(L, n, n > 8 ? kServerItersWide : kServerIters, kServerUnroll);
+    return make_plan(L, n, kServerIters, kServerUnroll);
 }
 
 // Upper bound on the number of floating-point additions any one term passes

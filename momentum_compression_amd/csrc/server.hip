@@ -15,12 +15,9 @@
 
 namespace onebit {
 
-// A group is kServerUnroll consecutive tiles of one chunk (2048 elements);
-// a workgroup covers `iters` consecutive tiles (iters / kServerUnroll
-// groups) and overlaps the loads of its next group with the work on the
-// current one.  The words of a group, for every worker, are staged through
-// LDS with coalesced loads (32 consecutive words per worker and tile); each
-// lane then reads its word per worker from LDS.
+// Words of the kServerUnroll tiles a workgroup processes together, for every
+// worker, are staged through LDS with coalesced loads (32 consecutive words
+// per worker and tile); each lane then reads its word per worker from LDS.
 //
 // Within one chunk every worker's scale is fixed, so the binary32 sum over
 // the first m = min(n, 8) workers, taken in order from +0, depends only on
@@ -30,11 +27,7 @@ namespace onebit {
 // spread to bit i of bytes 0..3 by a multiplication with 0x204081 and the
 // mask 0x01010101 (the copies at shifts 0, 7, 14, 21 do not overlap, and of
 // the copy at shift 7k only bit k reaches a masked position, bit 8k).
-// Workers m .. n-1 are then added one by one, still in order: for each of
-// them a 16-entry LDS table holds, per value of the lane's nibble, the four
-// signed scales +-s[i][c] of its 4 elements (a float4), so a lane decodes a
-// worker's 4 values with one rotate, one mask and one 16-byte LDS read, and
-// adds them.
+// Workers m .. n-1 are then added one by one as before.
 // NW: the worker count when known at compile time (8, 16), else 0 (any n).
 // RESET: the carried server error is dropped (not read).
 template <bool ERS, int NW, bool RESET>
@@ -49,10 +42,7 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
     __shared__ double red[kThreads / 64];
     __shared__ float sc[64];
     __shared__ float lut[256];
-    // signed scales of workers 8 .. n-1 per nibble: sgn[i - 8][nib] = float4
-    // of (bit k of nib set ? -s[i][c] : s[i][c]) for k = 0..3
-    __shared__ f4 sgn[(NW > 0 ? (NW > 8 ? NW - 8 : 1) : 56) * 16];
-    extern __shared__ uint32_t stage[];                    // [2][n][kGroupWords]
+    extern __shared__ uint32_t stage[];                    // [n][kGroupWords]
     const int64_t c = blockIdx.y;  // grid (bpc, n)
     const int64_t wg = blockIdx.x;
     const int64_t cbase = c * L;
@@ -71,14 +61,6 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
             a = a + __uint_as_float((b << 31) | __float_as_uint(sc[i]));
         }
         lut[threadIdx.x] = a;
-    }
-    for (int e = threadIdx.x; e < (nn - m8) * 16; e += kThreads) {
-        const uint32_t sb = __float_as_uint(sc[m8 + (e >> 4)]);  // scales are >= 0
-        const uint32_t nib = (uint32_t)e & 15u;
-        sgn[e] = f4{__uint_as_float(((nib & 1u) << 31) | sb),
-                    __uint_as_float((((nib >> 1) & 1u) << 31) | sb),
-                    __uint_as_float((((nib >> 2) & 1u) << 31) | sb),
-                    __uint_as_float((((nib >> 3) & 1u) << 31) | sb)};
     }
     // (the first group's __syncthreads orders the table before its use)
     const float S = RESET ? 0.0f : S_prev[c];
@@ -107,61 +89,46 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
         rv = seg_r[seg];
     }
 
-    // Groups of kServerUnroll tiles, software-pipelined: the words and the
-    // carried state of group g + 1 are loaded into registers while group g is
-    // computed from its LDS stage (two stage buffers alternate; the one
-    // barrier per group also tells the writers of buffer g & 1 that every
-    // lane has finished group g - 2, which read it).
-    //
-    // Staging: a group holds 64 words per worker, so wave w stages workers
-    // w, w + 4, w + 8, ... with one coalesced 256-byte load each (lane l
-    // takes word l); the worker, hence the row pointer, is wave-uniform.  The
-    // words are inverted so that a clear bit (negative value) becomes the set
-    // sign bit in the decode below.  A lane past the chunk's end reads the
-    // group's first word and stores all-ones (discarded later).
-    constexpr int kRowsPerWave = NW > 0 ? (NW + 3) / 4 : 16;  // n <= 64
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = lane_id();
-    const int groups = (iters + kServerUnroll - 1) / kServerUnroll;
-    uint32_t wn[kRowsPerWave];
-    f4 pn[kServerUnroll];
-    auto prefetch = [&](int g) {
-        const int64_t g0 = start + (int64_t)g * kServerUnroll * kTile;
-        const int64_t gw = (cbase + g0) >> 5;
-        const bool okw = lane < ((end - g0 + 31) >> 5);
-#pragma unroll
-        for (int r = 0; r < kRowsPerWave; ++r) {
-            const int i = wave + 4 * r;  // wave-uniform
-            wn[r] = 0u;
-            if (i < nn) wn[r] = bits[(int64_t)i * wrow + gw + (okw ? lane : 0)];
-        }
+    double acc = 0.0;
+    for (int it0 = 0; it0 < iters; it0 += kServerUnroll) {
+        const int64_t g0 = start + (int64_t)it0 * kTile;   // first element of this group
+        const int64_t gw = (cbase + g0) >> 5;             // its first word in a row
+        const int64_t gwords = (end - g0 + 31) >> 5;      // words of this group inside the chunk
+        __syncthreads();                                  // previous group done with `stage`
+        f4 pv[kServerUnroll];
 #pragma unroll
         for (int u = 0; u < kServerUnroll; ++u) {
             const int64_t j = g0 + (int64_t)u * kTile + 4 * (int64_t)threadIdx.x;
-            pn[u] = f4{0.f, 0.f, 0.f, 0.f};
-            if (!RESET && g * kServerUnroll + u < iters && j < end)
-                pn[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(ef + cbase + j));
+            pv[u] = f4{0.f, 0.f, 0.f, 0.f};
+            if (!RESET && it0 + u < iters && j < end)
+                pv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(ef + cbase + j));
         }
-    };
-    prefetch(0);
-
-    double acc = 0.0;
-    for (int gi = 0; gi < groups; ++gi) {
-        const int it0 = gi * kServerUnroll;
-        const int64_t g0 = start + (int64_t)it0 * kTile;   // first element of this group
-        uint32_t* const st = stage + (gi & 1) * nn * kGroupWords;
+        // Staging: a group holds 64 words per worker, so wave w stages workers
+        // w, w + 4, w + 8, ... with one coalesced 256-byte load each (lane l
+        // takes word l); the worker, hence the row pointer, is wave-uniform.
+        // The words are inverted so that a clear bit (negative value) becomes
+        // the set sign bit in the decode below.  A lane past the chunk's end
+        // reads the group's first word and stores all-ones (discarded later).
         {
-            const bool okw = lane < ((end - g0 + 31) >> 5);
+            const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+            const int lane = lane_id();
+            const bool okw = lane < gwords;
+            constexpr int kBatch = 4;  // workers per wave whose loads are in flight together
+            for (int r0 = 0; r0 < nn; r0 += 4 * kBatch) {
+                uint32_t v[kBatch];
 #pragma unroll
-            for (int r = 0; r < kRowsPerWave; ++r) {
-                const int i = wave + 4 * r;
-                if (i < nn) st[i * kGroupWords + lane] = okw ? ~wn[r] : ~0u;
+                for (int b = 0; b < kBatch; ++b) {
+                    const int i = r0 + 4 * b + wave;  // wave-uniform
+                    v[b] = 0u;
+                    if (i < nn) v[b] = bits[(int64_t)i * wrow + gw + (okw ? lane : 0)];
+                }
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b) {
+                    const int i = r0 + 4 * b + wave;
+                    if (i < nn) stage[i * kGroupWords + lane] = okw ? ~v[b] : ~0u;
+                }
             }
         }
-        f4 pv[kServerUnroll];
-#pragma unroll
-        for (int u = 0; u < kServerUnroll; ++u) pv[u] = pn[u];
-        if (gi + 1 < groups) prefetch(gi + 1);
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < kServerUnroll; ++u) {
@@ -175,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
             for (int i = 0; i < m8; ++i) {
                 // rotate the lane's nibble to bits i..i+3 (so that the 24-bit
                 // multiplier stays 0x204081), spread, mask to bit i of each byte
-                const uint32_t w = st[i * kGroupWords + wl];
+                const uint32_t w = stage[i * kGroupWords + wl];
                 const uint32_t nib = __builtin_amdgcn_alignbit(w, w, (uint32_t)(sh - i) & 31u) &
                                      (0xFu << i);
                 idx |= __umul24(nib, 0x204081u) & (0x01010101u << i);
@@ -185,16 +152,15 @@ __global__ __launch_bounds__(kThreads) void server_kernel(
             for (int k = 0; k < 4; ++k) a[k] = lut[(idx >> (8 * k)) & 0xFFu];
 #pragma unroll 8
             for (int i = m8; i < nn; ++i) {
-                // the lane's nibble, rotated to bits 4..7: the byte offset of
-                // its float4 in worker i's table
-                const uint32_t w = st[i * kGroupWords + wl];
-                const uint32_t off = __builtin_amdgcn_alignbit(w, w, (uint32_t)(sh - 4) & 31u) & 0xF0u;
-                const f4 v = *reinterpret_cast<const f4*>(
-                    reinterpret_cast<const char*>(sgn + (i - m8) * 16) + off);
-                a[0] = a[0] + v.x;
-                a[1] = a[1] + v.y;
-                a[2] = a[2] + v.z;
-                a[3] = a[3] + v.w;
+                // inverted bit of element k becomes the sign of +s[i][c]
+                // (one bit-field extract, one shift-or, one add)
+                const uint32_t w = stage[i * kGroupWords + wl];
+                const uint32_t sb = __float_as_uint(sc[i]);  // scales are >= 0
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t b = (w >> (sh + k)) & 1u;
+                    a[k] = a[k] + __uint_as_float((b << 31) | sb);
+                }
             }
             const float p[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
             float g[4];
@@ -236,8 +202,7 @@ hipError_t launch_server(const uint32_t* bits, const float* scales, float* ef, c
                          const float* seg_r, int32_t n_seg, hipStream_t st) {
     const bool pow2 = (n & (n - 1)) == 0;
     const float inv_n = 1.0f / (float)n;  // exact for powers of two
-    // two alternating stage buffers of n x (words of one group)
-    const size_t lds = 2 * (size_t)n * (kTile / 32) * kServerUnroll * sizeof(uint32_t);
+    const size_t lds = (size_t)n * (kTile / 32) * kServerUnroll * sizeof(uint32_t);
     const dim3 grid((unsigned)plan.bpc, (unsigned)n);
     const bool ers = seg_r && seg_off && !reset;
     auto launch = [&](auto kern) {
