@@ -402,9 +402,12 @@ int warmup_adam_step(float* x, float* m, float* v, const float* g, int64_t N, fl
  *   c_l = ||x_l|| / ||u_l||   (x before the step; 1 when either norm is 0)
  *   x   = x - (lr * c_l) * u
  *   c_avg_l = first ? c_l : beta_c * c_avg_l + (1 - beta_c) * c_l
- * The squared norms are summed in binary64 per workgroup and then in a fixed
- * order per layer (results do not depend on scheduling); c_l is the binary32
- * rounding of sqrt(Sx) / sqrt(Su).  c [n_seg] receives c_l.
+ * Sx and Su are the exact sums of squares rounded once to binary64, and c_l
+ * is the binary32 rounding of sqrt(Sx) / sqrt(Su) (binary64 square roots and
+ * division).  The library sums in binary64 in a fixed order and certifies
+ * that the binary32 result is the one the exact sums give; a layer where it
+ * cannot (c_l within about 2^-47 of a rounding boundary) is summed again
+ * exactly.  Results do not depend on scheduling.  c [n_seg] receives c_l.
  * seg_off [n_seg + 1] int64, device memory: seg_off[0] = 0, non-decreasing,
  * seg_off[n_seg] = N; any offset (a layer edge may fall inside a float4).
  * ws: at least warmup_workspace_bytes(N, n_seg) bytes, 256-byte aligned.
@@ -421,6 +424,10 @@ int warmup_lamb_step(float* x, float* m, float* v, const float* g, int64_t N,
  * paragraph, from the momentum m [N] at the end of warmup:
  *   a_l = sqrt(sum over layer l of m^2 / d_l)   (RMS, binary64)
  *   k_l = mean of a over layers with a > 0, divided by a_l; 1 if a_l = 0
+ * with the sum of squares and the sum over layers exact, each rounded once
+ * to binary64, and k_l rounded once to binary32.  As for c_l, binary64
+ * sums in a fixed order are certified, and when any k_l cannot be, every
+ * layer is summed again exactly.
  * k [n_seg] float out (the seg_k input of the compression entry points).
  * Same seg_off and workspace rules as warmup_lamb_step.
  */

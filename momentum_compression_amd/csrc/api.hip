@@ -57,6 +57,12 @@ WarmupWs split_warmup_ws(void* ws, int64_t N, int32_t n_seg) {
     w.part = reinterpret_cast<double2*>(p);
     p += round_up((size_t)layer_grid(N, n_seg) * 2 * sizeof(double));
     w.rms = reinterpret_cast<double*>(p);
+    p += round_up((size_t)n_seg * sizeof(double));
+    w.need = reinterpret_cast<int32_t*>(p);
+    p += round_up((size_t)(n_seg + 1) * sizeof(int32_t));
+    w.rms_exact = reinterpret_cast<double*>(p);
+    p += round_up((size_t)n_seg * sizeof(double));
+    w.slots = reinterpret_cast<uint64_t*>(p);
     return w;
 }
 
@@ -407,7 +413,10 @@ size_t warmup_workspace_bytes(int64_t N, int32_t n_seg) {
     if (N < 0 || (N % 4) || n_seg < 1) return 0;
     return round_up((size_t)(n_seg + 1) * sizeof(int64_t)) +
            round_up((size_t)layer_grid(N, n_seg) * 2 * sizeof(double)) +
-           round_up((size_t)n_seg * sizeof(double));
+           round_up((size_t)n_seg * sizeof(double)) +
+           round_up((size_t)(n_seg + 1) * sizeof(int32_t)) +
+           round_up((size_t)n_seg * sizeof(double)) +
+           round_up((size_t)layer_grid(N, n_seg) * 2 * kExactLimbs * sizeof(uint64_t));
 }
 
 int warmup_adam_step(float* x, float* m, float* v, const float* g, int64_t N, float lr, float eps,

@@ -205,7 +205,17 @@ struct WarmupWs {
     int64_t* wg_first;  // [n_seg + 1] first workgroup of each layer
     double2* part;      // [layer_grid] per-workgroup binary64 sums
     double* rms;        // [n_seg]
+    // exact fallback of the squared norms (taken only where the binary64
+    // sums cannot certify the binary32 result)
+    int32_t* need;      // [n_seg + 1] 1: the layer's sums are recomputed exactly;
+                        // need[n_seg]: any layer does
+    double* rms_exact;  // [n_seg]
+    uint64_t* slots;    // [layer_grid][2][kExactLimbs] per-workgroup exact sums
 };
+
+// Limbs (64-bit) of an exact sum of squares of binary32 values in units of
+// 2^-298: a square is below 2^554 units, so 2^31 of them stay below 2^640.
+constexpr int kExactLimbs = 10;
 
 // Upper bound on the workgroups of a layer pass (launch grid and slot count).
 int64_t layer_grid(int64_t N, int32_t n_seg);

@@ -251,13 +251,16 @@ def test_warmup_validation(lib):
 
 def test_warmup_workspace_bytes(lib):
     # plan (n_seg + 1 int64), one binary64 pair per workgroup of the upper
-    # bound ceil(N / 4096) + 2 n_seg + 1, layer RMS (n_seg binary64); each
-    # part rounded up to 256 bytes
+    # bound ceil(N / 4096) + 2 n_seg + 1, layer RMS (n_seg binary64), the
+    # exact path's marks (n_seg + 1 int32), exact RMS (n_seg binary64) and
+    # two 640-bit integers per workgroup; each part rounded up to 256 bytes
     def rup(x):
         return (x + 255) // 256 * 256
     for N, S in [(4096, 3), (336_226_304, 303), (0, 1)]:
         grid = -(-N // 4096) + 2 * S + 1
-        assert ob.warmup_workspace_bytes(N, S) == rup(8 * (S + 1)) + rup(16 * grid) + rup(8 * S)
+        want = (rup(8 * (S + 1)) + rup(16 * grid) + rup(8 * S) + rup(4 * (S + 1)) + rup(8 * S)
+                + rup(grid * 2 * 10 * 8))
+        assert ob.warmup_workspace_bytes(N, S) == want
     assert ob.warmup_workspace_bytes(1022, 3) == 0
     assert ob.warmup_workspace_bytes(1024, 0) == 0
 

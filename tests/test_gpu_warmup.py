@@ -175,3 +175,177 @@ def test_warmup_empty_tensor():
     assert host(c).tolist() == [1.0, 1.0]
     assert host(cav).tolist() == [4.0, 4.0]
     assert host(k).tolist() == [1.0, 1.0]
+
+
+# ----------------------------------------------- exact path of the layer norms
+# The squared norms are exact sums rounded once to binary64; the GPU sums in
+# binary64 in a fixed order and certifies the binary32 result, else it
+# recomputes the sums exactly.  The cases below put c_l or k_l within far
+# less than the certification slack of a binary32 rounding boundary, so the
+# exact path must run, and must give the oracle's values bit for bit.
+
+from fractions import Fraction  # noqa: E402
+import math  # noqa: E402
+
+
+def _frac(a) -> Fraction:
+    return Fraction(float(a))
+
+
+def _midpoint_near(v: float) -> Fraction:
+    """The binary32 rounding boundary just above the binary32 value nearest v."""
+    f = F32(v)
+    return (_frac(f) + _frac(np.nextafter(f, F32(np.inf), dtype=F32))) / 2
+
+
+def _complete_squares(target: Fraction, count: int = 4) -> list:
+    """Up to `count` binary32 values whose squares sum to at most `target`,
+    within about target 2^-90 of it (each value takes the largest square that
+    still fits in what is left)."""
+    vals, rem = [], target
+    for _ in range(count):
+        if rem <= 0:
+            break
+        y = F32(math.sqrt(float(rem)))
+        while _frac(y) ** 2 > rem:
+            y = np.nextafter(y, F32(0), dtype=F32)
+        if y == 0:
+            break
+        vals.append(y)
+        rem -= _frac(y) ** 2
+    return vals
+
+
+def test_trust_ratio_exact_path():
+    """Layers whose trust ratio ||x|| / ||u|| lies within about 2^-90 of a
+    binary32 midpoint: x and u are random, then four binary32 values
+    complete sum x^2 to (T ||u||)^2 for a midpoint T.  One layer is the
+    plain tie: its fixed-order binary64 sum drops 12 small squares (each
+    below half a unit in the last place of the running sum, all in the thread
+    after the large ones), lands exactly on the midpoint and would round to
+    even, while the exact sum rounds up."""
+    dev = device()
+    rng = np.random.default_rng(31)
+    sizes = [4096, 4096 * 3 + 6, 6, 1018, 4096 * 2, 70_000, 2]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    N = int(off[-1])
+    hp = dict(lr=1e-3, eps=0.0, beta1=0.5, beta2=0.5)  # u = m_new / sqrt(v_new)
+    x = (rng.standard_normal(N) * 0.02).astype(F32)
+    m0 = (rng.standard_normal(N) * 1e-3).astype(F32)
+    v0 = (np.abs(rng.standard_normal(N)) * 1e-6 + 1e-8).astype(F32)
+    g = (rng.standard_normal(N) * 1e-3).astype(F32)
+    # layer 0: the plain tie (u = (1, 0, ...), sum x^2 = (1 + 2^-24)^2 + 12 small squares)
+    a, b = int(off[0]), int(off[1])
+    m0[a:b], v0[a:b], g[a:b], x[a:b] = 0, 2, 0, 0
+    m0[a] = 2
+    x[a:a + 4] = [1, 2.0 ** -12, 2.0 ** -12, 2.0 ** -24]
+    small = F32(11 * 2.0 ** -30)  # squares of 1.89 2^-54: below half a unit of 1 in binary64
+    for t in (1024, 2048, 3072):
+        x[a + t:a + t + 4] = small
+    # layers 1, 3, 4, 5: random, completed to a midpoint by their last 4 elements
+    m_new, v_new = W.moments(m0, v0, g, hp["beta1"], hp["beta2"])
+    u = W.adam_direction(m_new, v_new, hp["eps"])
+    targets = {}
+    for layer in (1, 3, 4, 5):
+        lo, hi = int(off[layer]), int(off[layer + 1])
+        su = sum(_frac(t) ** 2 for t in u[lo:hi])
+        x[hi - 4:hi] = 0
+        sx_rest = sum(_frac(t) ** 2 for t in x[lo:hi])
+        targets[layer] = _midpoint_near(math.sqrt(float(sx_rest / su)) * 1.01)
+        fill = _complete_squares(targets[layer] ** 2 * su - sx_rest)
+        x[hi - 4:hi - 4 + len(fill)] = fill
+    gd = torch.from_numpy(g).to(dev)
+    off_d = torch.from_numpy(off).to(dev)
+    st = LambWarmup.create(torch.from_numpy(x).to(dev), off_d)
+    st.m.copy_(torch.from_numpy(m0))
+    st.v.copy_(torch.from_numpy(v0))
+    st.step(gd, beta_c=0.9, **hp)
+    torch.cuda.synchronize()
+    o = W.lamb_warmup_step(x, m0, v0, g, off, beta_c=0.9, **hp)
+    # the plain tie: the fixed order's sum loses the small squares and would
+    # round the ratio to even, the exact one rounds up
+    fixed = 1.0 + 2.0 ** -24 + 2.0 ** -24 + 2.0 ** -48
+    for _ in range(12):
+        fixed += float(small) ** 2
+    assert F32(math.sqrt(fixed)) == 1.0 and o["c"][0] == np.nextafter(F32(1), F32(2))
+    # the constructed layers: the binary64 ratio lies within 2^-48 of its
+    # midpoint, inside the certification slack (about 2^-47 here)
+    for layer, t in targets.items():
+        lo, hi = int(off[layer]), int(off[layer + 1])
+        q = Fraction(math.sqrt(W.exact_sumsq(x[lo:hi])) / math.sqrt(W.exact_sumsq(u[lo:hi])))
+        assert abs(q - t) <= t * Fraction(1, 2 ** 48), layer
+    same_f32(host(st.c), o["c"], "c (exact path)")
+    same_f32(host(st.c_avg), o["c_avg"], "c_avg")
+    same_f32(host(st.x), o["x"], "x")
+    same_f32(host(st.m), o["m"], "m")
+    same_f32(host(st.v), o["v"], "v")
+
+
+def test_momentum_scale_exact_path():
+    """k_l of one layer within about 2^-90 of a binary32 midpoint: the other
+    layers are random (several workgroups, edges inside a float4, a zero
+    and an empty layer), and the first layer's 4 elements are chosen so that
+    mean / a_0 lands on a midpoint T: a_0 = R / ((c + 1) T - 1) for the
+    other layers' RMS sum R and count c.  Certification fails, every layer
+    takes the exact path, and all k_l must equal the oracle's."""
+    dev = device()
+    rng = np.random.default_rng(32)
+    sizes = [4, 4096 * 3 + 6, 1018, 0, 70_000, 4096, 2, 4096 * 2 + 2]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    N = int(off[-1])
+    sig = np.exp(rng.uniform(np.log(1e-5), np.log(1e-1), len(sizes)))
+    m = (rng.standard_normal(N) * np.repeat(sig, sizes)).astype(F32)
+    m[int(off[5]):int(off[6])] = 0  # zero layer: k = 1, left out of the mean
+    rms = []
+    for layer in range(1, len(sizes)):
+        lo, hi = int(off[layer]), int(off[layer + 1])
+        if hi > lo:
+            r = math.sqrt(W.exact_sumsq(m[lo:hi]) / (hi - lo))
+            if r > 0:
+                rms.append(Fraction(r))
+    R, c = sum(rms), len(rms)
+    T = _midpoint_near(1.7)
+    a0 = R / ((c + 1) * T - 1)
+    m[0:4] = 0
+    fill = _complete_squares(a0 * a0 * 4)
+    m[0:len(fill)] = fill
+    off_d = torch.from_numpy(off).to(dev)
+    md = torch.from_numpy(m).to(dev)
+    k = torch.empty(len(sizes), device=dev)
+    ws = torch.empty(ob.warmup_workspace_bytes(N, len(sizes)), dtype=torch.uint8, device=dev)
+    ob.lamb_momentum_scale(md, N, off_d, len(sizes), k, ws)
+    torch.cuda.synchronize()
+    want = W.momentum_scale(m, off)
+    kk = Fraction(float(W.momentum_scale(m, off)[0]))
+    assert abs(kk - T) <= T * Fraction(1, 2 ** 22)  # k_0 is one of T's neighbours
+    same_f32(host(k), want, "k (exact path)")
+    assert host(k)[3] == 1 and host(k)[5] == 1
+
+
+def test_momentum_scale_exact_path_plain_tie():
+    """Two layers where the fixed-order binary64 sums land exactly on a
+    binary32 tie for k_0 (rounding to even) while the exact sums round up:
+    layer 0 holds 1, layer 1 holds 1 + 2^-23 and 15 small values in the same
+    thread whose squares each fall below half a unit of the running sum;
+    both have 4^7 elements, so the RMS of a square sum is exact."""
+    dev = device()
+    sizes = [16384, 16384, 0, 8]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    N = int(off[-1])
+    m = np.zeros(N, F32)
+    m[0] = 1.0
+    b = int(off[1])
+    m[b] = F32(1 + 2.0 ** -23)
+    small = F32(11 * 2.0 ** -30)
+    m[b + 1:b + 4] = small
+    for t in (1024, 2048, 3072):
+        m[b + t:b + t + 4] = small
+    off_d = torch.from_numpy(off).to(dev)
+    k = torch.empty(len(sizes), device=dev)
+    ws = torch.empty(ob.warmup_workspace_bytes(N, len(sizes)), dtype=torch.uint8, device=dev)
+    ob.lamb_momentum_scale(torch.from_numpy(m).to(dev), N, off_d, len(sizes), k, ws)
+    torch.cuda.synchronize()
+    want = W.momentum_scale(m, off)
+    # without the small squares: a_1 = (1 + 2^-23) a_0 and k_0 = 1 + 2^-24, a tie
+    assert want[0] == np.nextafter(F32(1), F32(2))
+    same_f32(host(k), want, "k (plain tie)")
