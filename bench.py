@@ -108,17 +108,20 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+CPU_STEPS = 2  # compressed steps in the oracle's timed sample
+
+
 def cpu_baseline(wl, m, x, v):
-    """Time the C++ oracle on a bounded sample of one step of the workload:
-    chunk 0 of every worker (compress of the n worker-chunk pairs, the server
-    of chunk 0, its decompression and Adam step), which is 1/n of the step's
-    work, so the step's rate is n L worker elements over the sample's time.
-    A reset step on the same momenta runs first, untimed, so the timed
-    compression carries the error like the steps on the GPU. The sample runs
-    on one thread (the reported value), then once more with the worker
-    chunks and the tail's slices over the host's threads (the server chunk
-    stays on one thread). m [n, N], x, v [N]: device float32; only chunk 0
-    is copied to the host."""
+    """Time the C++ oracle on a bounded sample of the workload: chunk 0 of
+    every worker (compress of the n worker-chunk pairs, the server of chunk
+    0, its decompression and Adam step), which is 1/n of a step's work, over
+    CPU_STEPS consecutive steps, so the rate is CPU_STEPS n L worker elements
+    over the sample's time. A reset step on the same momenta runs first,
+    untimed, so the timed compression carries the error like the steps on
+    the GPU. The sample runs on one thread (the reported value), then once
+    more with the worker chunks and the tail's slices over the host's threads
+    (the server chunk stays on one thread). m [n, N], x, v [N]: device
+    float32; only chunk 0 is copied to the host."""
     import numpy as np
 
     from oracle import cref as R
@@ -154,24 +157,34 @@ def cpu_baseline(wl, m, x, v):
         t3 = time.perf_counter()
         return (t3 - t0, (t1 - t0, t2 - t1, t3 - t2)), e_new, sv["E"]
 
-    _, e, E = sample(True, None, None, threads)
-    (sec1, parts1), _, _ = sample(False, e, E, 1)
-    (secm, partsm), _, _ = sample(False, e, E, threads)
+    _, e0, E0 = sample(True, None, None, threads)
+
+    def steps(th):
+        e, E, sec, parts = e0, E0, 0.0, [0.0, 0.0, 0.0]
+        for _ in range(CPU_STEPS):
+            (s1, p1), e, E = sample(False, e, E, th)
+            sec, parts = sec + s1, [a + b for a, b in zip(parts, p1)]
+        return sec, parts
+
+    sec1, parts1 = steps(1)
+    secm, partsm = steps(threads)
     fmt = "compress {:.1f} s, server {:.1f} s, decompression and Adam {:.1f} s"
     return {
-        "value": n * L / sec1,
+        "value": CPU_STEPS * n * L / sec1,
         "unit": "elements/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"chunk 0 ({L} elements) of all {n} workers, 1/{n} of a step of "
-                   f"{wl.name}: compress of the {n} worker chunks, the server of chunk 0, its "
-                   f"decompression and Adam step, by the C++ oracle on one thread, on the "
-                   f"bench's own inputs copied from the GPU, after an untimed reset step on "
-                   f"the same momenta; {sec1:.1f} s ({fmt.format(*parts1)}), scaled to "
-                   f"the step as {n} L worker elements per sample"),
+        "sample": (f"chunk 0 ({L} elements) of all {n} workers over {CPU_STEPS} consecutive "
+                   f"steps, {CPU_STEPS}/{n} of a step of {wl.name}: compress of the {n} worker "
+                   f"chunks, the server of chunk 0, its decompression and Adam step, by the "
+                   f"C++ oracle on one thread, on the bench's own inputs copied from the GPU, "
+                   f"after an untimed reset step on the same momenta; {sec1:.1f} s "
+                   f"({fmt.format(*parts1)}), scaled to the step as {n} L worker elements "
+                   f"per step of the sample"),
         "cpu_model": _cpu_model(),
         "threads_available": os.cpu_count(),
-        "multithreaded": {"value": n * L / secm, "unit": "elements/s", "cores": threads,
+        "multithreaded": {"value": CPU_STEPS * n * L / secm, "unit": "elements/s",
+                          "cores": threads,
                           "sample": (f"the same sample with the {n} worker chunks and the "
                                      f"tail's slices over {threads} threads (the server "
                                      f"chunk on one): {secm:.1f} s ({fmt.format(*partsm)})")},
