@@ -215,11 +215,11 @@ int onebit_server_reduce_ex(const uint32_t* bits, const float* scales, float* ef
  * Arguments, layouts and results are exactly those of
  * onebit_server_reduce_ex (bit-identical outputs), on the current device
  * (the stream must belong to it).
- * Limit: the server needs one double per workgroup, about N / 2048 of them
- * for n <= 8 and N / 8192 for n > 8; calls needing more than 2^20 (N above
- * about 2^31 elements for n <= 8, 2^33 for n > 8) return ONEBIT_E_WORKSPACE
- * before any launch.  The scratch keeps the last call's contents; each call
- * writes every partial it reads, so nothing needs clearing.  Calls that
+ * Limit: the server needs one double per workgroup of 2048 elements of a
+ * chunk, n * ceil(N / n / 2048) of them; calls needing more than 2^20 (N
+ * above about 2^31 elements) return ONEBIT_E_WORKSPACE before any launch.
+ * The scratch keeps the last call's contents; each call writes every
+ * partial it reads, so nothing needs clearing.  Calls that
  * overlap on one device (different streams, or host threads) share the one
  * scratch and race: serialise them.
  */
