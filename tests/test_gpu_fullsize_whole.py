@@ -21,8 +21,8 @@ must be bit-identical:
   the previous step's words from the second step on matches it bit for bit;
 * the fused step from gradients on 335M x 8 (momentum formed inside
   compression from the packed global momentum), over two steps;
-* INT8 with Philox stochastic rounding on 2^30 elements, over two
-  error-feedback steps.
+* INT8 with Philox stochastic rounding on 2^30 elements, over the
+  workload's ten error-feedback steps.
 """
 
 import gc
@@ -388,8 +388,9 @@ def test_bert_large_335M_x8_from_gradients_whole_buffer():
 
 def test_int8_2_30_whole_buffer():
     """INT8 block stochastic rounding on 2^30 Laplace gradients with outliers,
-    two error-feedback steps: every code, block scale, dequantised value and
-    residual."""
+    the workload's ten error-feedback steps (a fresh gradient and Philox
+    step counter each): every code, block scale, dequantised value and
+    residual after every step."""
     dev = device()
     N, block, seed = 1 << 30, 256, 4
     _need(dev, N * 18)
@@ -400,7 +401,9 @@ def test_int8_2_30_whole_buffer():
     deq = torch.empty(N, device=dev)
     g = torch.empty(N, device=dev)
     e_ref = np.zeros(N, dtype=F32)
-    for step in (1, 2):
+    steps = C.get("int8_sr_2^30").steps
+    assert steps == 10
+    for step in range(1, steps + 1):
         S.laplace_gradient(N, step, seed, dev, out=g)
         ob.int8_sr_quantize(g, err, codes, scales, deq, N, block, seed, step)
         torch.cuda.synchronize()
