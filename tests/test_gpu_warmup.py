@@ -216,15 +216,15 @@ def _complete_squares(target: Fraction, count: int = 4) -> list:
     return vals
 
 
-def test_trust_ratio_exact_path():
+def _trust_ratio_midpoint_case():
     """Layers whose trust ratio ||x|| / ||u|| lies within about 2^-90 of a
     binary32 midpoint: x and u are random, then four binary32 values
-    complete sum x^2 to (T ||u||)^2 for a midpoint T.  One layer is the
-    plain tie: its fixed-order binary64 sum drops 12 small squares (each
-    below half a unit in the last place of the running sum, all in the thread
+    complete sum x^2 to (T ||u||)^2 for a midpoint T.  Layer 0 is the plain
+    tie: its fixed-order binary64 sum drops 12 small squares (each below
+    half a unit in the last place of the running sum, all in the thread
     after the large ones), lands exactly on the midpoint and would round to
-    even, while the exact sum rounds up."""
-    dev = device()
+    even, while the exact sum rounds up.  Returns x, m0, v0, g, off, the
+    step's hyperparameters, the small value and {layer: midpoint}."""
     rng = np.random.default_rng(31)
     sizes = [4096, 4096 * 3 + 6, 6, 1018, 4096 * 2, 70_000, 2]
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
@@ -254,13 +254,25 @@ def test_trust_ratio_exact_path():
         targets[layer] = _midpoint_near(math.sqrt(float(sx_rest / su)) * 1.01)
         fill = _complete_squares(targets[layer] ** 2 * su - sx_rest)
         x[hi - 4:hi - 4 + len(fill)] = fill
-    gd = torch.from_numpy(g).to(dev)
+    return x, m0, v0, g, off, hp, small, targets
+
+
+def _lamb_warmup_gpu(x, m0, v0, g, off, hp):
+    dev = device()
     off_d = torch.from_numpy(off).to(dev)
     st = LambWarmup.create(torch.from_numpy(x).to(dev), off_d)
     st.m.copy_(torch.from_numpy(m0))
     st.v.copy_(torch.from_numpy(v0))
-    st.step(gd, beta_c=0.9, **hp)
+    st.step(torch.from_numpy(g).to(dev), beta_c=0.9, **hp)
     torch.cuda.synchronize()
+    return st
+
+
+def test_trust_ratio_exact_path():
+    """The constructed midpoint layers and the plain tie: certification
+    fails, the exact path runs, and c, c_avg, x, m, v equal the oracle's."""
+    x, m0, v0, g, off, hp, small, targets = _trust_ratio_midpoint_case()
+    st = _lamb_warmup_gpu(x, m0, v0, g, off, hp)
     o = W.lamb_warmup_step(x, m0, v0, g, off, beta_c=0.9, **hp)
     # the plain tie: the fixed order's sum loses the small squares and would
     # round the ratio to even, the exact one rounds up
@@ -270,6 +282,8 @@ def test_trust_ratio_exact_path():
     assert F32(math.sqrt(fixed)) == 1.0 and o["c"][0] == np.nextafter(F32(1), F32(2))
     # the constructed layers: the binary64 ratio lies within 2^-48 of its
     # midpoint, inside the certification slack (about 2^-47 here)
+    m_new, v_new = W.moments(m0, v0, g, hp["beta1"], hp["beta2"])
+    u = W.adam_direction(m_new, v_new, hp["eps"])
     for layer, t in targets.items():
         lo, hi = int(off[layer]), int(off[layer + 1])
         q = Fraction(math.sqrt(W.exact_sumsq(x[lo:hi])) / math.sqrt(W.exact_sumsq(u[lo:hi])))
@@ -281,21 +295,26 @@ def test_trust_ratio_exact_path():
     same_f32(host(st.v), o["v"], "v")
 
 
-def test_momentum_scale_exact_path():
-    """k_l of one layer within about 2^-90 of a binary32 midpoint: the other
-    layers are random (several workgroups, edges inside a float4, a zero
-    and an empty layer), and the first layer's 4 elements are chosen so that
-    mean / a_0 lands on a midpoint T: a_0 = R / ((c + 1) T - 1) for the
-    other layers' RMS sum R and count c.  Certification fails, every layer
-    takes the exact path, and all k_l must equal the oracle's."""
-    dev = device()
-    rng = np.random.default_rng(32)
-    sizes = [4, 4096 * 3 + 6, 1018, 0, 70_000, 4096, 2, 4096 * 2 + 2]
-    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
-    N = int(off[-1])
-    sig = np.exp(rng.uniform(np.log(1e-5), np.log(1e-1), len(sizes)))
-    m = (rng.standard_normal(N) * np.repeat(sig, sizes)).astype(F32)
-    m[int(off[5]):int(off[6])] = 0  # zero layer: k = 1, left out of the mean
+def test_trust_ratio_exact_path_at_large_exponents():
+    """The same layers with x scaled by 2^64 (exact in binary32): every
+    trust ratio scales by 2^64, so the midpoints stay midpoints and the exact
+    path bins the squares of x near the top of its range (values up to
+    2^62); c must equal the oracle's, and 2^64 times the unscaled c."""
+    x, m0, v0, g, off, hp, _, _ = _trust_ratio_midpoint_case()
+    xs = (x * F32(2.0 ** 64)).astype(F32)
+    assert np.array_equal(xs / F32(2.0 ** 64), x) and np.all(np.isfinite(xs))
+    st = _lamb_warmup_gpu(xs, m0, v0, g, off, hp)
+    o = W.lamb_warmup_step(xs, m0, v0, g, off, beta_c=0.9, **hp)
+    o1 = W.lamb_warmup_step(x, m0, v0, g, off, beta_c=0.9, **hp)
+    assert np.array_equal(o["c"], (o1["c"] * F32(2.0 ** 64)).astype(F32))
+    same_f32(host(st.c), o["c"], "c (exact path, x scaled by 2^64)")
+    same_f32(host(st.x), o["x"], "x")
+
+
+def _momentum_midpoint_fill(m, off, sizes, T):
+    """Layer 0's 4 elements chosen so that k_0 = mean / a_0 lands within
+    about 2^-90 of the midpoint T: a_0 = R / ((c + 1) T - 1) for the other
+    layers' exact RMS sum R and count c (zero and empty layers left out)."""
     rms = []
     for layer in range(1, len(sizes)):
         lo, hi = int(off[layer]), int(off[layer + 1])
@@ -304,22 +323,91 @@ def test_momentum_scale_exact_path():
             if r > 0:
                 rms.append(Fraction(r))
     R, c = sum(rms), len(rms)
-    T = _midpoint_near(1.7)
     a0 = R / ((c + 1) * T - 1)
     m[0:4] = 0
     fill = _complete_squares(a0 * a0 * 4)
     m[0:len(fill)] = fill
+
+
+def _momentum_midpoint_case():
+    """Random layers (several workgroups, edges inside a float4, a zero and
+    an empty layer) and a first layer of 4 elements whose k_0 is within
+    about 2^-90 of the midpoint near 1.7."""
+    rng = np.random.default_rng(32)
+    sizes = [4, 4096 * 3 + 6, 1018, 0, 70_000, 4096, 2, 4096 * 2 + 2]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    N = int(off[-1])
+    sig = np.exp(rng.uniform(np.log(1e-5), np.log(1e-1), len(sizes)))
+    m = (rng.standard_normal(N) * np.repeat(sig, sizes)).astype(F32)
+    m[int(off[5]):int(off[6])] = 0  # zero layer: k = 1, left out of the mean
+    T = _midpoint_near(1.7)
+    _momentum_midpoint_fill(m, off, sizes, T)
+    return m, off, sizes, T
+
+
+def _momentum_scale_gpu(m, off, sizes):
+    dev = device()
+    N = int(off[-1])
     off_d = torch.from_numpy(off).to(dev)
-    md = torch.from_numpy(m).to(dev)
     k = torch.empty(len(sizes), device=dev)
     ws = torch.empty(ob.warmup_workspace_bytes(N, len(sizes)), dtype=torch.uint8, device=dev)
-    ob.lamb_momentum_scale(md, N, off_d, len(sizes), k, ws)
+    ob.lamb_momentum_scale(torch.from_numpy(m).to(dev), N, off_d, len(sizes), k, ws)
     torch.cuda.synchronize()
+    return host(k)
+
+
+def test_momentum_scale_exact_path():
+    """k_0 within about 2^-90 of a binary32 midpoint: certification fails,
+    every layer takes the exact path, and all k_l must equal the oracle's."""
+    m, off, sizes, T = _momentum_midpoint_case()
+    k = _momentum_scale_gpu(m, off, sizes)
     want = W.momentum_scale(m, off)
-    kk = Fraction(float(W.momentum_scale(m, off)[0]))
+    kk = Fraction(float(want[0]))
     assert abs(kk - T) <= T * Fraction(1, 2 ** 22)  # k_0 is one of T's neighbours
-    same_f32(host(k), want, "k (exact path)")
-    assert host(k)[3] == 1 and host(k)[5] == 1
+    same_f32(k, want, "k (exact path)")
+    assert k[3] == 1 and k[5] == 1
+
+
+def test_momentum_scale_exact_path_at_large_exponents():
+    """The same momentum scaled by 2^100 (exact in binary32; values up to
+    about 2^99): k is unchanged, so the exact path still runs, now binning
+    squares near the top of its range; k must equal the oracle's and the
+    unscaled k."""
+    m, off, sizes, _ = _momentum_midpoint_case()
+    ms = (m * F32(2.0 ** 100)).astype(F32)
+    assert np.array_equal(ms / F32(2.0 ** 100), m) and np.all(np.isfinite(ms))
+    k = _momentum_scale_gpu(ms, off, sizes)
+    want = W.momentum_scale(ms, off)
+    assert np.array_equal(want, W.momentum_scale(m, off))
+    same_f32(k, want, "k (exact path, momentum scaled by 2^100)")
+
+
+def test_momentum_scale_exact_path_with_subnormal_layer():
+    """A layer of binary32 subnormals (random multiples of 2^-149) next to
+    small normal layers, with k_0 on a midpoint so that every layer takes
+    the exact path: the subnormal squares fall in the lowest units of the
+    exact sums (down to 2^-298), and that layer's k is near 2^110."""
+    rng = np.random.default_rng(33)
+    sizes = [4, 4096 * 2 + 6, 2000, 70_000, 0, 6]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    N = int(off[-1])
+    m = np.zeros(N, F32)
+    a, b = int(off[1]), int(off[2])
+    m[a:b] = (rng.uniform(0.5, 1.0, b - a) * rng.choice([-1, 1], b - a) * 2.0 ** -10).astype(F32)
+    a, b = int(off[2]), int(off[3])
+    sub = rng.integers(1, 1 << 23, b - a) * rng.choice([-1, 1], b - a)
+    m[a:b] = (sub.astype(np.float64) * 2.0 ** -149).astype(F32)
+    assert np.all(np.abs(m[a:b]) < np.finfo(F32).tiny) and np.all(m[a:b] != 0)
+    a, b = int(off[3]), int(off[4])
+    m[a:b] = (rng.standard_normal(b - a) * 2.0 ** -20).astype(F32)
+    T = _midpoint_near(1.3)
+    _momentum_midpoint_fill(m, off, sizes, T)
+    k = _momentum_scale_gpu(m, off, sizes)
+    want = W.momentum_scale(m, off)
+    assert abs(Fraction(float(want[0])) - T) <= T * Fraction(1, 2 ** 22)
+    assert 2.0 ** 100 < want[2] < 2.0 ** 120 and np.all(np.isfinite(want))
+    same_f32(k, want, "k (exact path, a subnormal layer)")
+    assert k[4] == 1 and k[5] == 1
 
 
 def test_momentum_scale_exact_path_plain_tie():
