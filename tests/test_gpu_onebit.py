@@ -120,7 +120,8 @@ def test_all_zero_chunks():
 
 
 def test_exact_tie_takes_exact_path():
-    """Chunk means that are exact binary32 midpoints (ties to even) and
+    """Chunk means that are exact binary32 midpoints (ties to even), among
+    normal values, subnormals and values near the top of the range, and
     means within one unit of the last place of a midpoint."""
     dev = device()
     n, L = 4, 2048
@@ -131,6 +132,7 @@ def test_exact_tie_takes_exact_path():
     m_h[:, 0::2] = one
     m_h[:, 1::2] = -up            # mean |.| = 1 + 2^-24: a tie, rounds to 1
     m_h[1, :L] *= np.float32(2.0 ** -130)  # the same tie among subnormals
+    m_h[0, L:2 * L] *= np.float32(2.0 ** 126)  # and among values near 2^126
     m_h[2, 3] = -np.nextafter(up, np.float32(2), dtype=F32)  # mean just above the tie
     m_h[3, L:2 * L] = np.float32(3.0)
     m_h[3, L] = np.float32(3.0 + 2 ** -22)  # mean 3 + 2^-33: not a tie, close to 3
@@ -142,6 +144,7 @@ def test_exact_tie_takes_exact_path():
     w = O.worker_compress(m_h, np.zeros_like(m_h), reset=True)
     same_f32(host(grp.scales), w["s"], "tie scales")
     assert host(grp.scales)[0, 0] == one
+    assert host(grp.scales)[0, 1] == np.float32(2.0 ** 126)
     sv = O.server_reduce(w["bits"], w["s"], np.zeros(N, dtype=F32), reset=True)
     same_f32(host(grp.sv_scales), sv["S"], "tie server scales")
     same_bits(host(grp.sv_bits), sv["bits"], "tie server bits")
