@@ -634,6 +634,67 @@ def measure_sweep(wl, steps: int, warmup: int) -> list:
     return out
 
 
+PROBE_MODES = [(0, "stream: read m and state, write state"),
+               (1, "stream + sign words"),
+               (2, "stream + binary64 block sum"),
+               (3, "stream + sign words + block sum (the compression's memory operations)")]
+
+
+def measure_probe(wl, steps: int, warmup: int) -> dict:
+    """The ceiling of the worker compression's memory pattern: probe kernels
+    (libonebit_probe.so) with the compression's geometry and launch shape that
+    only move its bytes, each extra output switched on in turn, timed with
+    HIP events interleaved with the real compression (clamp on, non-reset) on
+    the same two [n][N] buffers, so that placement is shared."""
+    import ctypes
+
+    import torch
+
+    from momentum_compression_amd import onebit as ob
+    from momentum_compression_amd.build import PROBE_LIB
+
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is not built (python __graft_entry__.py build)")
+    lib = ctypes.CDLL(PROBE_LIB)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.onebit_probe_stream.restype = I32
+    lib.onebit_probe_stream.argtypes = [P, P, P, P, I64, I32, I32, P]
+    dev = torch.device("cuda:0")
+    N, n = wl.N, wl.n
+    g = torch.Generator(device=dev)
+    g.manual_seed(N)
+    a = torch.empty((n, N), device=dev).normal_(0.0, 1e-3, generator=g)  # the momentum
+    b = torch.zeros((n, N), device=dev)                        # the state
+    bits = torch.zeros((n, N // 32), dtype=torch.int32, device=dev)
+    scales = torch.zeros((n, n), device=dev)
+    ws = torch.empty(ob.workspace_bytes(N, n, 0), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = P(stream.cuda_stream)
+
+    def probe(mode):
+        rc = lib.onebit_probe_stream(a.data_ptr(), b.data_ptr(), bits.data_ptr(), ws.data_ptr(),
+                                     N, n, mode, sp)
+        if rc != 0:
+            raise RuntimeError(f"probe mode {mode}: status {rc}")
+
+    def compress():
+        ob.onebit_compress(a, b, scales, bits, N, n, clip=wl.clip, reset=False, ws=ws)
+
+    ob.onebit_compress(a, b, scales, bits, N, n, clip=wl.clip, reset=True, ws=ws)
+    fns = [lambda mode=mode: probe(mode) for mode, _ in PROBE_MODES] + [compress]
+    ms = _time_calls(fns, warmup, steps, stream)
+    nbytes = [B_COMPRESS * n * N - n * N / 8, B_COMPRESS * n * N, B_COMPRESS * n * N - n * N / 8,
+              B_COMPRESS * n * N, B_COMPRESS * n * N]
+    names = [name for _, name in PROBE_MODES] + ["the worker compression (clamp on, with finalize)"]
+    rows = [{"kernel": nm, "ms": round(t, 4), "GBps": round(nb / (t * 1e-3) / 1e9, 1),
+             "frac_of_8TBps": round(nb / (t * 1e-3) / 8e12, 4)}
+            for nm, t, nb in zip(names, ms, nbytes)]
+    del a, b, bits, scales, ws
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "N": N, "workers": n, "elements_per_launch": n * N,
+            "steps": steps, "warmup": warmup, "rows": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -645,6 +706,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="time the step over buffer sizes from 2^20 to the workload's N "
+                         "(profiling aid; prints its own JSON line)")
+    ap.add_argument("--probe", action="store_true",
+                    help="time memory-pattern probes of the worker compression beside it "
                          "(profiling aid; prints its own JSON line)")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the rows measured after the headline step (LAMB, INT8, fused, "
@@ -675,6 +739,9 @@ def main() -> int:
     N, n = wl.N, wl.n
     if args.sweep:
         print(json.dumps({"sweep": measure_sweep(wl, args.steps, args.warmup)}))
+        return 0
+    if args.probe:
+        print(json.dumps({"probe": measure_probe(wl, args.steps, args.warmup)}))
         return 0
     print(f"[bench] workload={wl.name} N={N} n={n} steps={args.steps} warmup={args.warmup}",
           file=sys.stderr, flush=True)

@@ -66,6 +66,22 @@ def _compile(src: str) -> str:
     return obj
 
 
+# the memory-pattern probes of the benchmark, in a library of their own
+PROBE_SRC = "stream_probe.hip"
+PROBE_LIB = os.path.join(HERE, "libonebit_probe.so")
+
+
+def build_probe() -> str:
+    obj = _compile(PROBE_SRC)
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"probe link failed:\n{res.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 CAPI_SRC = os.path.join(ROOT, "tests", "capi", "capi_roundtrip.c")
 CAPI_BIN = os.path.join(BUILD, "capi_roundtrip")
 
@@ -92,11 +108,13 @@ def build_capi() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every kernel source for gfx950, link libonebit.so, and build
-    the plain C test program against it."""
+    """Compile every kernel source for gfx950, link libonebit.so, build the
+    plain C test program against it, and build the benchmark's probe
+    library."""
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
+        probe = ex.submit(build_probe)
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -104,8 +122,9 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"link failed:\n{res.stderr}")
     os.replace(tmp, LIB)
     build_capi()
+    probe.result()
     if verbose:
-        print(f"built {LIB} and {CAPI_BIN}")
+        print(f"built {LIB}, {CAPI_BIN} and {PROBE_LIB}")
     return LIB
 
 

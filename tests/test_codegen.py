@@ -17,7 +17,7 @@ from momentum_compression_amd import build as B
 pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists(
     "/opt/rocm/bin/hipcc"), reason="hipcc not available")
 
-KERNEL_SOURCES = [s for s in B.SOURCES if s != "api.hip"]
+KERNEL_SOURCES = [s for s in B.SOURCES if s != "api.hip"] + [B.PROBE_SRC]
 PACKED_FP32 = re.compile(r"^\s+v_pk_(add|mul|fma)_f32\b", re.M)
 SCALAR_WRITE = re.compile(r"^\s+s_(store|buffer_store|scratch_store|atomic|buffer_atomic|dcache_wb)", re.M)
 KERNEL = re.compile(r"^\s+\.amdhsa_kernel\s+(\S+)", re.M)
