@@ -695,6 +695,57 @@ def measure_probe(wl, steps: int, warmup: int) -> dict:
             "steps": steps, "warmup": warmup, "rows": rows}
 
 
+def measure_probe_server(wl, steps: int, warmup: int) -> dict:
+    """The ceiling of the server's memory pattern: a probe kernel
+    (libonebit_probe.so) with the server's grid and launch shape that does
+    its global memory operations (every worker's sign words staged through
+    LDS, the state in and out, the server's sign words, the block sum)
+    without decoding and adding the workers, timed like the server in the
+    step: each right after a worker compression of the same buffers."""
+    import ctypes
+
+    import torch
+
+    from momentum_compression_amd import onebit as ob
+    from momentum_compression_amd.build import PROBE_LIB
+    from momentum_compression_amd.state import OneBitGroup
+
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is not built (python __graft_entry__.py build)")
+    lib = ctypes.CDLL(PROBE_LIB)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.onebit_probe_server.restype = I32
+    lib.onebit_probe_server.argtypes = [P, P, P, P, I64, I32, P]
+    dev = torch.device("cuda:0")
+    N, n = wl.N, wl.n
+    g = torch.Generator(device=dev)
+    g.manual_seed(N + 1)
+    m = torch.empty((n, N), device=dev).normal_(0.0, 1e-3, generator=g)
+    grp = OneBitGroup(N, n, dev)
+    stream = torch.cuda.current_stream()
+    sp = P(stream.cuda_stream)
+
+    def probe():
+        rc = lib.onebit_probe_server(grp.bits.data_ptr(), grp.sv_ef.data_ptr(),
+                                     grp.sv_bits.data_ptr(), grp.ws.data_ptr(), N, n, sp)
+        if rc != 0:
+            raise RuntimeError(f"server probe: status {rc}")
+
+    grp.compress(m, 1, first=True)
+    grp.server(1, first=True, decompress=False)
+    ms = _time_calls([lambda: grp.compress(m, 2), probe, lambda: grp.compress(m, 2),
+                      lambda: grp.server(2, decompress=False)], warmup, steps, stream)
+    nb = b_server(n) * N
+    rows = [{"kernel": nm, "ms": round(t, 4), "GBps": round(nb / (t * 1e-3) / 1e9, 1),
+             "frac_of_8TBps": round(nb / (t * 1e-3) / 8e12, 4)}
+            for nm, t in (("probe: the server's memory operations, after a compression", ms[1]),
+                          ("the server (with finalize), after a compression", ms[3]))]
+    del m, grp
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "N": N, "workers": n, "bytes_per_element": b_server(n),
+            "steps": steps, "warmup": warmup, "rows": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -707,9 +758,10 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="time the step over buffer sizes from 2^20 to the workload's N "
                          "(profiling aid; prints its own JSON line)")
-    ap.add_argument("--probe", action="store_true",
-                    help="time memory-pattern probes of the worker compression beside it "
-                         "(profiling aid; prints its own JSON line)")
+    ap.add_argument("--probe", nargs="?", const="compress", default="",
+                    choices=["", "compress", "server"],
+                    help="time memory-pattern probes of the worker compression (or of the "
+                         "server) beside it (profiling aid; prints its own JSON line)")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the rows measured after the headline step (LAMB, INT8, fused, "
                          "warmup, the other Adam workload, copy reference)")
@@ -731,6 +783,9 @@ def main() -> int:
         return 2
     ob.load()
     wl = C.get(args.workload)
+    if args.probe == "server":  # any 1-bit workload: the server's shape is (N, n)
+        print(json.dumps({"probe": measure_probe_server(wl, args.steps, args.warmup)}))
+        return 0
     if wl.kind != "adam":
         print(f"workload {wl.name} is a parity case; the bench times the 1-bit Adam path",
               file=sys.stderr)

@@ -1,7 +1,7 @@
-// Stream probes shaped like the worker compression, built into a separate
-// library (libonebit_probe.so) that only the benchmark loads: they give the
-// ceiling of the compression's memory pattern on this GPU, not a step of the
-// method.
+// Stream probes shaped like the worker compression and the server, built
+// into a separate library (libonebit_probe.so) that only the benchmark
+// loads: they give the ceiling of each kernel's memory pattern on this GPU,
+// not a step of the method.
 //
 // Same geometry as the compression: n rows of N floats, chunks of L = N / n,
 // grid (workgroups per chunk, n * n), one 1024-element tile per 256-thread
@@ -64,6 +64,89 @@ __global__ __launch_bounds__(256) void stream_probe_kernel(const float* __restri
     }
 }
 
+// The server's memory operations without its arithmetic: two 1024-element
+// tiles of chunk c per 256-thread workgroup (grid (workgroups per chunk, n)),
+// every worker's 64 sign words of the group staged through LDS by coalesced
+// wave loads exactly as the server does, the carried state read and written
+// in place (nontemporal), one server sign word per 8 lanes and the binary64
+// block sum.  Each lane folds its n staged words with XOR (so every word is
+// read) instead of decoding and adding the workers.
+// NW: the worker count when known at compile time (16), else 0 (any n).
+template <int NW>
+__global__ __launch_bounds__(256) void server_probe_kernel(const uint32_t* __restrict__ bits,
+                                                           float* __restrict__ ef,
+                                                           uint32_t* __restrict__ sv_bits,
+                                                           double* __restrict__ part, int64_t N,
+                                                           int32_t n, int64_t L, int64_t bpc) {
+    __shared__ double red[4];
+    extern __shared__ uint32_t stage[];  // [n][64]
+    const int64_t c = blockIdx.y;
+    const int64_t wg = blockIdx.x;
+    const int64_t cbase = c * L;
+    const int64_t g0 = wg * 2048;
+    int64_t end = g0 + 2048;
+    if (end > L) end = L;
+    const int64_t gw = (cbase + g0) >> 5;
+    const int64_t gwords = (end - g0 + 31) >> 5;
+    const int64_t wrow = N >> 5;
+    const int nn = NW > 0 ? NW : n;
+    f4 pv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t j = g0 + u * 1024 + 4 * (int64_t)threadIdx.x;
+        pv[u] = f4{0.f, 0.f, 0.f, 0.f};
+        if (j < end) pv[u] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(ef + cbase + j));
+    }
+    {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int lane = threadIdx.x & 63;
+        const bool okw = lane < gwords;
+        for (int r0 = 0; r0 < nn; r0 += 16) {
+            uint32_t v[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int i = r0 + 4 * b + wave;
+                v[b] = 0u;
+                if (i < nn) v[b] = bits[(int64_t)i * wrow + gw + (okw ? lane : 0)];
+            }
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int i = r0 + 4 * b + wave;
+                if (i < nn) stage[i * 64 + lane] = okw ? ~v[b] : ~0u;
+            }
+        }
+    }
+    __syncthreads();
+    double acc = 0.0;
+    const int lane8 = threadIdx.x & 7;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t j = g0 + u * 1024 + 4 * (int64_t)threadIdx.x;
+        const bool active = j < end;
+        const int wl = u * 32 + (threadIdx.x >> 3);
+        uint32_t x = 0;
+#pragma unroll 16
+        for (int i = 0; i < nn; ++i) x ^= stage[i * 64 + wl];
+        const float d = (float)(x & 1u);
+        const f4 g = pv[u] + f4{d, d, d, d};
+        const uint32_t nib = (g.x >= 0.f ? 1u : 0u) | (g.y >= 0.f ? 2u : 0u) |
+                             (g.z >= 0.f ? 4u : 0u) | (g.w >= 0.f ? 8u : 0u);
+        const uint32_t word = or8(nib << (4 * lane8));
+        if (active) {
+            __builtin_nontemporal_store(g, reinterpret_cast<f4*>(ef + cbase + j));
+            acc += (double)fabsf(g.x);
+            acc += (double)fabsf(g.y);
+            acc += (double)fabsf(g.z);
+            acc += (double)fabsf(g.w);
+            if (lane8 == 0) sv_bits[(cbase + j) >> 5] = word;
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) part[c * bpc + wg] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
 }  // namespace
 
 extern "C" {
@@ -98,6 +181,28 @@ int onebit_probe_stream(const float* a, float* b, uint32_t* bits, double* part, 
                                bits, part, N, n, L, bpc);
             break;
     }
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Runs one server probe launch on `stream`: bits n rows of N / 32 words (the
+// workers' sign words), ef N floats (the server state, 16-byte aligned,
+// overwritten), sv_bits N / 32 words, part n * ceil(N / n / 2048) doubles.
+// N must be a multiple of 64 n.  Returns 0, -2 for invalid sizes, -6 for a
+// HIP launch error.
+int onebit_probe_server(const uint32_t* bits, float* ef, uint32_t* sv_bits, double* part,
+                        int64_t N, int32_t n, hipStream_t stream) {
+    if (n < 1 || n > 64 || N <= 0 || N % (64 * (int64_t)n)) return -2;
+    const int64_t L = N / n;
+    const int64_t bpc = (L + 2047) / 2048;
+    if (bpc * 256 >= ((int64_t)1 << 32)) return -2;
+    const dim3 grid((unsigned)bpc, (unsigned)n);
+    const size_t lds = (size_t)n * 64 * sizeof(uint32_t);
+    if (n == 16)
+        hipLaunchKernelGGL(server_probe_kernel<16>, grid, dim3(256), lds, stream, bits, ef, sv_bits,
+                           part, N, n, L, bpc);
+    else
+        hipLaunchKernelGGL(server_probe_kernel<0>, grid, dim3(256), lds, stream, bits, ef, sv_bits,
+                           part, N, n, L, bpc);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
