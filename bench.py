@@ -640,36 +640,56 @@ PROBE_MODES = [(0, "stream: read m and state, write state"),
                (3, "stream + sign words + block sum (the compression's memory operations)")]
 
 
-def measure_probe(wl, steps: int, warmup: int) -> dict:
+def _probe_lib():
+    """The probe library (built by build() next to libonebit.so), or None."""
+    import ctypes
+
+    from momentum_compression_amd.build import PROBE_LIB
+
+    if not os.path.exists(PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(PROBE_LIB)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.onebit_probe_stream.restype = I32
+    lib.onebit_probe_stream.argtypes = [P, P, P, P, I64, I32, I32, P]
+    lib.onebit_probe_server.restype = I32
+    lib.onebit_probe_server.argtypes = [P, P, P, P, I64, I32, P]
+    return lib
+
+
+def measure_probe(wl, steps: int, warmup: int, bufs=None, modes=None) -> dict:
     """The ceiling of the worker compression's memory pattern: probe kernels
     (libonebit_probe.so) with the compression's geometry and launch shape that
     only move its bytes, each extra output switched on in turn, timed with
     HIP events interleaved with the real compression (clamp on, non-reset) on
-    the same two [n][N] buffers, so that placement is shared."""
+    the same two [n][N] buffers, so that placement is shared.  bufs: the
+    momentum, state, sign words and workspace to use (overwritten), else
+    allocated here; modes: the probe modes to time (all by default)."""
     import ctypes
 
     import torch
 
     from momentum_compression_amd import onebit as ob
-    from momentum_compression_amd.build import PROBE_LIB
 
-    if not os.path.exists(PROBE_LIB):
-        raise RuntimeError(f"{PROBE_LIB} is not built (python __graft_entry__.py build)")
-    lib = ctypes.CDLL(PROBE_LIB)
-    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
-    lib.onebit_probe_stream.restype = I32
-    lib.onebit_probe_stream.argtypes = [P, P, P, P, I64, I32, I32, P]
+    lib = _probe_lib()
+    if lib is None:
+        raise RuntimeError("libonebit_probe.so is not built (python __graft_entry__.py build)")
+    P = ctypes.c_void_p
     dev = torch.device("cuda:0")
     N, n = wl.N, wl.n
-    g = torch.Generator(device=dev)
-    g.manual_seed(N)
-    a = torch.empty((n, N), device=dev).normal_(0.0, 1e-3, generator=g)  # the momentum
-    b = torch.zeros((n, N), device=dev)                        # the state
-    bits = torch.zeros((n, N // 32), dtype=torch.int32, device=dev)
+    if bufs is None:
+        g = torch.Generator(device=dev)
+        g.manual_seed(N)
+        a = torch.empty((n, N), device=dev).normal_(0.0, 1e-3, generator=g)  # the momentum
+        b = torch.zeros((n, N), device=dev)                        # the state
+        bits = torch.zeros((n, N // 32), dtype=torch.int32, device=dev)
+        ws = torch.empty(ob.workspace_bytes(N, n, 0), dtype=torch.uint8, device=dev)
+    else:
+        a, b, bits, ws = bufs
     scales = torch.zeros((n, n), device=dev)
-    ws = torch.empty(ob.workspace_bytes(N, n, 0), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sp = P(stream.cuda_stream)
+    modes = [m for m in PROBE_MODES if modes is None or m[0] in modes]
 
     def probe(mode):
         rc = lib.onebit_probe_stream(a.data_ptr(), b.data_ptr(), bits.data_ptr(), ws.data_ptr(),
@@ -681,47 +701,49 @@ def measure_probe(wl, steps: int, warmup: int) -> dict:
         ob.onebit_compress(a, b, scales, bits, N, n, clip=wl.clip, reset=False, ws=ws)
 
     ob.onebit_compress(a, b, scales, bits, N, n, clip=wl.clip, reset=True, ws=ws)
-    fns = [lambda mode=mode: probe(mode) for mode, _ in PROBE_MODES] + [compress]
+    fns = [lambda mode=mode: probe(mode) for mode, _ in modes] + [compress]
     ms = _time_calls(fns, warmup, steps, stream)
-    nbytes = [B_COMPRESS * n * N - n * N / 8, B_COMPRESS * n * N, B_COMPRESS * n * N - n * N / 8,
-              B_COMPRESS * n * N, B_COMPRESS * n * N]
-    names = [name for _, name in PROBE_MODES] + ["the worker compression (clamp on, with finalize)"]
+    # sign words in modes 1 and 3 (and the compression): 1/8 byte per element
+    nbytes = [B_COMPRESS * n * N - (0 if mode & 1 else n * N / 8) for mode, _ in modes]
+    nbytes.append(B_COMPRESS * n * N)
+    names = [name for _, name in modes] + ["the worker compression (clamp on, with finalize)"]
     rows = [{"kernel": nm, "ms": round(t, 4), "GBps": round(nb / (t * 1e-3) / 1e9, 1),
              "frac_of_8TBps": round(nb / (t * 1e-3) / 8e12, 4)}
             for nm, t, nb in zip(names, ms, nbytes)]
     del a, b, bits, scales, ws
-    torch.cuda.empty_cache()
+    if bufs is None:
+        torch.cuda.empty_cache()
     return {"workload": wl.name, "N": N, "workers": n, "elements_per_launch": n * N,
             "steps": steps, "warmup": warmup, "rows": rows}
 
 
-def measure_probe_server(wl, steps: int, warmup: int) -> dict:
+def measure_probe_server(wl, steps: int, warmup: int, grp=None, m=None) -> dict:
     """The ceiling of the server's memory pattern: a probe kernel
     (libonebit_probe.so) with the server's grid and launch shape that does
     its global memory operations (every worker's sign words staged through
     LDS, the state in and out, the server's sign words, the block sum)
     without decoding and adding the workers, timed like the server in the
-    step: each right after a worker compression of the same buffers."""
+    step: each right after a worker compression of the same buffers.  grp,
+    m: the group and momentum to use (their state is overwritten), else
+    allocated here."""
     import ctypes
 
     import torch
 
-    from momentum_compression_amd import onebit as ob
-    from momentum_compression_amd.build import PROBE_LIB
     from momentum_compression_amd.state import OneBitGroup
 
-    if not os.path.exists(PROBE_LIB):
-        raise RuntimeError(f"{PROBE_LIB} is not built (python __graft_entry__.py build)")
-    lib = ctypes.CDLL(PROBE_LIB)
-    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
-    lib.onebit_probe_server.restype = I32
-    lib.onebit_probe_server.argtypes = [P, P, P, P, I64, I32, P]
+    lib = _probe_lib()
+    if lib is None:
+        raise RuntimeError("libonebit_probe.so is not built (python __graft_entry__.py build)")
+    P = ctypes.c_void_p
     dev = torch.device("cuda:0")
     N, n = wl.N, wl.n
-    g = torch.Generator(device=dev)
-    g.manual_seed(N + 1)
-    m = torch.empty((n, N), device=dev).normal_(0.0, 1e-3, generator=g)
-    grp = OneBitGroup(N, n, dev)
+    own = grp is None
+    if own:
+        g = torch.Generator(device=dev)
+        g.manual_seed(N + 1)
+        m = torch.empty((n, N), device=dev).normal_(0.0, 1e-3, generator=g)
+        grp = OneBitGroup(N, n, dev)
     stream = torch.cuda.current_stream()
     sp = P(stream.cuda_stream)
 
@@ -741,7 +763,8 @@ def measure_probe_server(wl, steps: int, warmup: int) -> dict:
             for nm, t in (("probe: the server's memory operations, after a compression", ms[1]),
                           ("the server (with finalize), after a compression", ms[3]))]
     del m, grp
-    torch.cuda.empty_cache()
+    if own:
+        torch.cuda.empty_cache()
     return {"workload": wl.name, "N": N, "workers": n, "bytes_per_element": b_server(n),
             "steps": steps, "warmup": warmup, "rows": rows}
 
@@ -932,6 +955,16 @@ def main() -> int:
         out["cpu_baseline"] = cpu_baseline(wl, m, x, v)
     else:
         out["cpu_baseline"] = None
+    # the hot kernels beside probes of their memory patterns, on the
+    # headline's own buffers (after every use of their contents above)
+    if _probe_lib() is not None:
+        print("[bench] pattern probes", file=sys.stderr, flush=True)
+        k = max(3, args.steps // 2)
+        pc = measure_probe(wl, k, 1, bufs=(m, grp.ef, grp.bits, grp.ws), modes=[3])
+        ps = measure_probe_server(wl, k, 1, grp=grp, m=m)
+        out["rows"]["pattern_ceiling"] = {"compress": pc["rows"], "server": ps["rows"]}
+    else:
+        out["rows"]["pattern_ceiling"] = None
     if not args.no_rows:
         other = "bert_large_335M_x8" if wl.name == "gpt_1.3B_x16" else "gpt_1.3B_x16"
         del grp, m, x, v
