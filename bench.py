@@ -963,6 +963,8 @@ def main() -> int:
         pc = measure_probe(wl, k, 1, bufs=(m, grp.ef, grp.bits, grp.ws), modes=[3])
         ps = measure_probe_server(wl, k, 1, grp=grp, m=m)
         out["rows"]["pattern_ceiling"] = {"compress": pc["rows"], "server": ps["rows"]}
+        # the same bytes over the probe's time: the access pattern's ceiling
+        out["roofline"]["pattern_probe_GBps"] = pc["rows"][0]["GBps"]
     else:
         out["rows"]["pattern_ceiling"] = None
     if not args.no_rows:
