@@ -654,6 +654,8 @@ def _probe_lib():
     lib.onebit_probe_stream.argtypes = [P, P, P, P, I64, I32, I32, P]
     lib.onebit_probe_server.restype = I32
     lib.onebit_probe_server.argtypes = [P, P, P, P, I64, I32, P]
+    lib.onebit_probe_int8.restype = I32
+    lib.onebit_probe_int8.argtypes = [P, P, P, P, P, I64, P]
     return lib
 
 
@@ -769,6 +771,53 @@ def measure_probe_server(wl, steps: int, warmup: int, grp=None, m=None) -> dict:
             "steps": steps, "warmup": warmup, "rows": rows}
 
 
+def measure_probe_int8(steps: int, warmup: int) -> dict:
+    """The ceiling of the INT8 quantiser's memory pattern on 2^30 elements: a
+    probe kernel with its grid and launch shape that reads g and the error
+    and writes the codes, the error, the dequantised values and the block
+    scales without quantising, timed interleaved with the quantiser (block
+    256, stochastic rounding, error feedback, dequantised output) on the
+    same buffers."""
+    import ctypes
+
+    import torch
+
+    from momentum_compression_amd import onebit as ob
+    from workloads import synth as S
+
+    lib = _probe_lib()
+    if lib is None:
+        raise RuntimeError("libonebit_probe.so is not built (python __graft_entry__.py build)")
+    P = ctypes.c_void_p
+    dev = torch.device("cuda:0")
+    N, block = 1 << 30, 256
+    g = S.laplace_gradient(N, 1, 4, dev)
+    err = torch.zeros(N, device=dev)
+    codes = torch.empty(N, dtype=torch.int8, device=dev)
+    scales = torch.empty(N // block, device=dev)
+    deq = torch.empty(N, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = P(stream.cuda_stream)
+
+    def probe():
+        rc = lib.onebit_probe_int8(g.data_ptr(), err.data_ptr(), codes.data_ptr(),
+                                   scales.data_ptr(), deq.data_ptr(), N, sp)
+        if rc != 0:
+            raise RuntimeError(f"int8 probe: status {rc}")
+
+    def quantise():  # the error carries whatever the probe left: finite values
+        ob.int8_sr_quantize(g, err, codes, scales, deq, N, block, 4, 1)
+
+    ms = _time_calls([probe, quantise], warmup, steps, stream)
+    rows = [{"kernel": "probe: the quantiser's memory operations", **_row(ms[0], B_INT8 * N, N)},
+            {"kernel": "the quantiser (block 256, stochastic rounding, error feedback, "
+                       "dequantised output)", **_row(ms[1], B_INT8 * N, N)}]
+    del g, err, codes, scales, deq
+    torch.cuda.empty_cache()
+    return {"N": N, "block": block, "bytes_per_element": B_INT8, "steps": steps,
+            "warmup": warmup, "rows": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -782,7 +831,7 @@ def main() -> int:
                     help="time the step over buffer sizes from 2^20 to the workload's N "
                          "(profiling aid; prints its own JSON line)")
     ap.add_argument("--probe", nargs="?", const="compress", default="",
-                    choices=["", "compress", "server"],
+                    choices=["", "compress", "server", "int8"],
                     help="time memory-pattern probes of the worker compression (or of the "
                          "server) beside it (profiling aid; prints its own JSON line)")
     ap.add_argument("--no-rows", action="store_true",
@@ -808,6 +857,9 @@ def main() -> int:
     wl = C.get(args.workload)
     if args.probe == "server":  # any 1-bit workload: the server's shape is (N, n)
         print(json.dumps({"probe": measure_probe_server(wl, args.steps, args.warmup)}))
+        return 0
+    if args.probe == "int8":
+        print(json.dumps({"probe": measure_probe_int8(args.steps, args.warmup)}))
         return 0
     if wl.kind != "adam":
         print(f"workload {wl.name} is a parity case; the bench times the 1-bit Adam path",

@@ -1,4 +1,5 @@
-// Stream probes shaped like the worker compression and the server, built
+// Stream probes shaped like the worker compression, the server and the INT8
+// quantiser, built
 // into a separate library (libonebit_probe.so) that only the benchmark
 // loads: they give the ceiling of each kernel's memory pattern on this GPU,
 // not a step of the method.
@@ -147,6 +148,42 @@ __global__ __launch_bounds__(256) void server_probe_kernel(const uint32_t* __res
     if (threadIdx.x == 0) part[c * bpc + wg] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
+// The block INT8 quantiser's memory operations without its arithmetic: two
+// 1024-element tiles per 256-thread workgroup, g and the error read
+// (nontemporal float4), the packed codes (4 bytes per lane), the error and
+// the dequantised values written (nontemporal), and one block scale per 256
+// elements (one lane in 64), as the quantiser with block 256, error
+// feedback and dequantised output does.
+__global__ __launch_bounds__(256) void int8_probe_kernel(const float* __restrict__ g,
+                                                         float* __restrict__ err,
+                                                         int8_t* __restrict__ codes,
+                                                         float* __restrict__ scales,
+                                                         float* __restrict__ deq, int64_t N) {
+    const int64_t base = (int64_t)blockIdx.x * 2048;
+    f4 gv[2], ev[2];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int64_t J = base + it * 1024 + 4 * (int64_t)threadIdx.x;
+        gv[it] = f4{0.f, 0.f, 0.f, 0.f};
+        ev[it] = f4{0.f, 0.f, 0.f, 0.f};
+        if (J < N) {
+            gv[it] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(g + J));
+            ev[it] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(err + J));
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int64_t J = base + it * 1024 + 4 * (int64_t)threadIdx.x;
+        if (J >= N) continue;
+        const f4 x = gv[it] + ev[it];
+        const uint32_t packed = __float_as_uint(x.x) ^ __float_as_uint(x.w);
+        __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t*>(codes + J));
+        __builtin_nontemporal_store(x, reinterpret_cast<f4*>(err + J));
+        __builtin_nontemporal_store(x * 0.5f, reinterpret_cast<f4*>(deq + J));
+        if ((threadIdx.x & 63) == 0) scales[J / 256] = x.y;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -203,6 +240,20 @@ int onebit_probe_server(const uint32_t* bits, float* ef, uint32_t* sv_bits, doub
     else
         hipLaunchKernelGGL(server_probe_kernel<0>, grid, dim3(256), lds, stream, bits, ef, sv_bits,
                            part, N, n, L, bpc);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Runs one INT8 probe launch on `stream`: g, err, deq N floats, codes N
+// bytes, scales N / 256 floats (device; err and deq 16-byte aligned and
+// overwritten).  N must be a positive multiple of 256.  Returns 0, -2 for an
+// invalid size, -6 for a HIP launch error.
+int onebit_probe_int8(const float* g, float* err, int8_t* codes, float* scales, float* deq,
+                      int64_t N, hipStream_t stream) {
+    if (N <= 0 || N % 256) return -2;
+    const int64_t wgs = (N + 2047) / 2048;
+    if (wgs * 256 >= ((int64_t)1 << 32)) return -2;
+    hipLaunchKernelGGL(int8_probe_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, g, err, codes,
+                       scales, deq, N);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
