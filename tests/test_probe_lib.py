@@ -1,0 +1,50 @@
+"""Host-side checks of the benchmark's probe library (libonebit_probe.so):
+it is built next to libonebit.so, exports its three probes, and rejects
+invalid sizes before any HIP call (no GPU needed)."""
+
+import ctypes
+import os
+
+import pytest
+
+from momentum_compression_amd import build as B
+
+P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.PROBE_LIB):
+        pytest.skip("libonebit_probe.so is not built")
+    L = ctypes.CDLL(B.PROBE_LIB)
+    L.onebit_probe_stream.restype = I32
+    L.onebit_probe_stream.argtypes = [P, P, P, P, I64, I32, I32, P]
+    L.onebit_probe_server.restype = I32
+    L.onebit_probe_server.argtypes = [P, P, P, P, I64, I32, P]
+    L.onebit_probe_int8.restype = I32
+    L.onebit_probe_int8.argtypes = [P, P, P, P, P, I64, P]
+    return L
+
+
+def test_probe_sizes_rejected_before_launch(lib):
+    # compression probe: N a positive multiple of 64 n, 1 <= n <= 64, mode 0..3
+    assert lib.onebit_probe_stream(None, None, None, None, 0, 4, 0, None) == -2
+    assert lib.onebit_probe_stream(None, None, None, None, 1000, 4, 0, None) == -2
+    assert lib.onebit_probe_stream(None, None, None, None, 4096, 0, 0, None) == -2
+    assert lib.onebit_probe_stream(None, None, None, None, 4096, 65, 0, None) == -2
+    assert lib.onebit_probe_stream(None, None, None, None, 4096, 4, 4, None) == -2
+    assert lib.onebit_probe_stream(None, None, None, None, 4096, 4, -1, None) == -2
+    # server probe
+    assert lib.onebit_probe_server(None, None, None, None, 0, 16, None) == -2
+    assert lib.onebit_probe_server(None, None, None, None, 64 * 16 + 64, 16, None) == -2
+    assert lib.onebit_probe_server(None, None, None, None, 4096, 65, None) == -2
+    # INT8 probe: N a positive multiple of 256
+    assert lib.onebit_probe_int8(None, None, None, None, None, 0, None) == -2
+    assert lib.onebit_probe_int8(None, None, None, None, None, 1000, None) == -2
+
+
+def test_probe_library_is_not_the_product_library():
+    # the product library exports no probe (the probes are the benchmark's)
+    prod = ctypes.CDLL(os.path.join(os.path.dirname(B.PROBE_LIB), "libonebit.so"))
+    for name in ("onebit_probe_stream", "onebit_probe_server", "onebit_probe_int8"):
+        assert not hasattr(prod, name)
