@@ -653,7 +653,7 @@ def _probe_lib():
     lib.onebit_probe_stream.restype = I32
     lib.onebit_probe_stream.argtypes = [P, P, P, P, I64, I32, I32, P]
     lib.onebit_probe_server.restype = I32
-    lib.onebit_probe_server.argtypes = [P, P, P, P, I64, I32, P]
+    lib.onebit_probe_server.argtypes = [P, P, P, P, I64, I32, I64, P]
     lib.onebit_probe_int8.restype = I32
     lib.onebit_probe_int8.argtypes = [P, P, P, P, P, I64, P]
     return lib
@@ -751,7 +751,7 @@ def measure_probe_server(wl, steps: int, warmup: int, grp=None, m=None) -> dict:
 
     def probe():
         rc = lib.onebit_probe_server(grp.bits.data_ptr(), grp.sv_ef.data_ptr(),
-                                     grp.sv_bits.data_ptr(), grp.ws.data_ptr(), N, n, sp)
+                                     grp.sv_bits.data_ptr(), grp.ws.data_ptr(), N, n, 0, sp)
         if rc != 0:
             raise RuntimeError(f"server probe: status {rc}")
 

@@ -78,7 +78,8 @@ __global__ __launch_bounds__(256) void server_probe_kernel(const uint32_t* __res
                                                            float* __restrict__ ef,
                                                            uint32_t* __restrict__ sv_bits,
                                                            double* __restrict__ part, int64_t N,
-                                                           int32_t n, int64_t L, int64_t bpc) {
+                                                           int32_t n, int64_t L, int64_t bpc,
+                                                           int64_t wrow) {
     __shared__ double red[4];
     extern __shared__ uint32_t stage[];  // [n][64]
     const int64_t c = blockIdx.y;
@@ -89,7 +90,6 @@ __global__ __launch_bounds__(256) void server_probe_kernel(const uint32_t* __res
     if (end > L) end = L;
     const int64_t gw = (cbase + g0) >> 5;
     const int64_t gwords = (end - g0 + 31) >> 5;
-    const int64_t wrow = N >> 5;
     const int nn = NW > 0 ? NW : n;
     f4 pv[2];
 #pragma unroll
@@ -221,14 +221,17 @@ int onebit_probe_stream(const float* a, float* b, uint32_t* bits, double* part, 
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
-// Runs one server probe launch on `stream`: bits n rows of N / 32 words (the
-// workers' sign words), ef N floats (the server state, 16-byte aligned,
+// Runs one server probe launch on `stream`: bits n rows of `pitch` words
+// each holding a worker's N / 32 sign words (pitch 0 means N / 32, the
+// library's layout), ef N floats (the server state, 16-byte aligned,
 // overwritten), sv_bits N / 32 words, part n * ceil(N / n / 2048) doubles.
-// N must be a multiple of 64 n.  Returns 0, -2 for invalid sizes, -6 for a
-// HIP launch error.
+// N must be a multiple of 64 n and pitch 0 or at least N / 32.  Returns 0,
+// -2 for invalid sizes, -6 for a HIP launch error.
 int onebit_probe_server(const uint32_t* bits, float* ef, uint32_t* sv_bits, double* part,
-                        int64_t N, int32_t n, hipStream_t stream) {
+                        int64_t N, int32_t n, int64_t pitch, hipStream_t stream) {
     if (n < 1 || n > 64 || N <= 0 || N % (64 * (int64_t)n)) return -2;
+    if (pitch == 0) pitch = N >> 5;
+    if (pitch < (N >> 5)) return -2;
     const int64_t L = N / n;
     const int64_t bpc = (L + 2047) / 2048;
     if (bpc * 256 >= ((int64_t)1 << 32)) return -2;
@@ -236,10 +239,10 @@ int onebit_probe_server(const uint32_t* bits, float* ef, uint32_t* sv_bits, doub
     const size_t lds = (size_t)n * 64 * sizeof(uint32_t);
     if (n == 16)
         hipLaunchKernelGGL(server_probe_kernel<16>, grid, dim3(256), lds, stream, bits, ef, sv_bits,
-                           part, N, n, L, bpc);
+                           part, N, n, L, bpc, pitch);
     else
         hipLaunchKernelGGL(server_probe_kernel<0>, grid, dim3(256), lds, stream, bits, ef, sv_bits,
-                           part, N, n, L, bpc);
+                           part, N, n, L, bpc, pitch);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

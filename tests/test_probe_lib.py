@@ -20,7 +20,7 @@ def lib():
     L.onebit_probe_stream.restype = I32
     L.onebit_probe_stream.argtypes = [P, P, P, P, I64, I32, I32, P]
     L.onebit_probe_server.restype = I32
-    L.onebit_probe_server.argtypes = [P, P, P, P, I64, I32, P]
+    L.onebit_probe_server.argtypes = [P, P, P, P, I64, I32, I64, P]
     L.onebit_probe_int8.restype = I32
     L.onebit_probe_int8.argtypes = [P, P, P, P, P, I64, P]
     return L
@@ -35,9 +35,10 @@ def test_probe_sizes_rejected_before_launch(lib):
     assert lib.onebit_probe_stream(None, None, None, None, 4096, 4, 4, None) == -2
     assert lib.onebit_probe_stream(None, None, None, None, 4096, 4, -1, None) == -2
     # server probe
-    assert lib.onebit_probe_server(None, None, None, None, 0, 16, None) == -2
-    assert lib.onebit_probe_server(None, None, None, None, 64 * 16 + 64, 16, None) == -2
-    assert lib.onebit_probe_server(None, None, None, None, 4096, 65, None) == -2
+    assert lib.onebit_probe_server(None, None, None, None, 0, 16, 0, None) == -2
+    assert lib.onebit_probe_server(None, None, None, None, 64 * 16 + 64, 16, 0, None) == -2
+    assert lib.onebit_probe_server(None, None, None, None, 4096, 65, 0, None) == -2
+    assert lib.onebit_probe_server(None, None, None, None, 4096, 16, 127, None) == -2  # < N/32
     # INT8 probe: N a positive multiple of 256
     assert lib.onebit_probe_int8(None, None, None, None, None, 0, None) == -2
     assert lib.onebit_probe_int8(None, None, None, None, None, 1000, None) == -2
