@@ -1009,16 +1009,19 @@ def main() -> int:
         out["cpu_baseline"] = None
     # the hot kernels beside probes of their memory patterns, on the
     # headline's own buffers (after every use of their contents above)
+    # (a diagnostic: a probe that cannot run is reported, never fatal)
+    out["rows"]["pattern_ceiling"] = None
     if _probe_lib() is not None:
         print("[bench] pattern probes", file=sys.stderr, flush=True)
         k = max(3, args.steps // 2)
-        pc = measure_probe(wl, k, 1, bufs=(m, grp.ef, grp.bits, grp.ws), modes=[3])
-        ps = measure_probe_server(wl, k, 1, grp=grp, m=m)
-        out["rows"]["pattern_ceiling"] = {"compress": pc["rows"], "server": ps["rows"]}
-        # the same bytes over the probe's time: the access pattern's ceiling
-        out["roofline"]["pattern_probe_GBps"] = pc["rows"][0]["GBps"]
-    else:
-        out["rows"]["pattern_ceiling"] = None
+        try:
+            pc = measure_probe(wl, k, 1, bufs=(m, grp.ef, grp.bits, grp.ws), modes=[3])
+            ps = measure_probe_server(wl, k, 1, grp=grp, m=m)
+            out["rows"]["pattern_ceiling"] = {"compress": pc["rows"], "server": ps["rows"]}
+            # the same bytes over the probe's time: the access pattern's ceiling
+            out["roofline"]["pattern_probe_GBps"] = pc["rows"][0]["GBps"]
+        except RuntimeError as exc:
+            out["rows"]["pattern_ceiling"] = {"error": str(exc)}
     if not args.no_rows:
         other = "bert_large_335M_x8" if wl.name == "gpt_1.3B_x16" else "gpt_1.3B_x16"
         del grp, m, x, v
