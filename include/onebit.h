@@ -10,10 +10,12 @@
  *   The library never allocates, frees or synchronises; it validates
  *   arguments on the host (before any HIP call) and enqueues kernels on
  *   `stream` only.  Results are ready when the stream reaches them.
- * - The library keeps no global state: calls on different streams or host
- *   threads are safe when their buffers (workspace included) are disjoint;
- *   calls that share a buffer must be ordered by the caller.  Results do
- *   not depend on the stream or on the launch geometry.
+ * - The library keeps no global state apart from the scratch array of
+ *   onebit_server_reduce_noalloc (one per device, shared by every call of
+ *   that entry point on the device): other calls on different streams or
+ *   host threads are safe when their buffers (workspace included) are
+ *   disjoint; calls that share a buffer must be ordered by the caller.
+ *   Results do not depend on the stream or on the launch geometry.
  * - Return value: ONEBIT_OK (0) or a negative onebit_status.  Validation
  *   failures leave every buffer untouched.  ONEBIT_E_HIP reports a launch
  *   error from the HIP runtime.
