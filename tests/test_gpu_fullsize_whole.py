@@ -19,6 +19,9 @@ must be bit-identical:
   server, m / k, x, the fresh variance and every layer's ratio, r_t, c_t and
   error factor, over two steps; a second LAMB state that reads m_{t-1} as
   the previous step's words from the second step on matches it bit for bit;
+* the step-ratio error feedback chained at full size (302 tensors x 16,
+  three steps, the factors the LAMB pass writes fed to the next step's
+  compression and server);
 * the fused step from gradients on 335M x 8 (momentum formed inside
   compression from the packed global momentum), over two steps;
 * INT8 with Philox stochastic rounding on 2^30 elements, over the
@@ -67,7 +70,7 @@ def _need(dev, nbytes):
 _same = same_whole
 
 
-def _workers(grp, m, e_state, reset, tag, clip=0.0, k=None, rows=None):
+def _workers(grp, m, e_state, reset, tag, clip=0.0, k=None, rows=None, err_ratio=None):
     """The oracle's worker compression of the given rows (all by default; rows
     in parallel), each compared with the GPU's state, sign words and scales
     as it completes. ``m`` is the [n, N] device momentum, or a function that
@@ -86,7 +89,8 @@ def _workers(grp, m, e_state, reset, tag, clip=0.0, k=None, rows=None):
     with ThreadPoolExecutor(max_workers=batch) as ex:
         for b0 in range(0, len(rows), batch):
             part = rows[b0:b0 + batch]
-            futs = {i: ex.submit(R.worker_compress_row, row_m(i), e_state[i], n, clip, reset, k)
+            futs = {i: ex.submit(R.worker_compress_row, row_m(i), e_state[i], n, clip, reset, k,
+                                 err_ratio=err_ratio)
                     for i in part}
             for i in part:
                 w = futs.pop(i).result()
@@ -100,8 +104,8 @@ def _workers(grp, m, e_state, reset, tag, clip=0.0, k=None, rows=None):
     return bits, s
 
 
-def _server(grp, bits, s, E_state, reset, tag):
-    sv = R.server_reduce(bits, s, E_state, reset=reset, threads=THREADS)
+def _server(grp, bits, s, E_state, reset, tag, err_ratio=None):
+    sv = R.server_reduce(bits, s, E_state, reset=reset, err_ratio=err_ratio, threads=THREADS)
     _same(host(grp.sv_bits), sv["bits"], f"{tag} server sign words")
     _same(host(grp.sv_scales), sv["S"], f"{tag} server scales")
     _same(host(grp.sv_ef), sv["g2"], f"{tag} server compensated values")
@@ -343,6 +347,71 @@ def test_bert_large_lamb_302t_x16_whole_buffer():
         _same(host(st.c), out["c"], f"{tag} c_t")
         _same(host(st.err_ratio), out["err_ratio"], f"{tag} error factor c_(t-1)/c_t")
         x_ref, vf_ref, r_ref, c_ref, mp_ref = out["x"], out["v"], out["r"], out["c"], mbar
+        del sv, bits, s, out
+        print(f"[whole] {tag} ok", flush=True)
+    del grp, st, m, sig, e_ref, E_ref
+    _free()
+
+
+def test_bert_large_lamb_302t_x16_step_ratio_whole_buffer():
+    """The step-ratio-scaled error feedback of the 1-bit LAMB page (analysis
+    paragraph) chained at full size: each step's LAMB pass writes c_{t-1}/c_t
+    per layer, and the next step's compression and server multiply their
+    carried errors by it. 302 tensors x 16 workers over three steps, with a
+    wide clip of the ratio so that the coefficients move; every worker row,
+    the server, the decompressed momentum, the parameters and the layer
+    factors on the whole buffer."""
+    dev = device()
+    wl = C.get("bert_large_lamb_302t_x16")
+    N, n = wl.N, wl.n
+    _need(dev, int(n * N * 4 * 2.2 + N * 4 * 12))
+    from momentum_compression_amd.state import momentum_scale
+
+    print(f"[whole] {wl.name} step-ratio N={N} n={n}", flush=True)
+    off = np.array(C.segment_offsets(wl.segments), dtype=np.int64)
+    c_avg = S.lamb_c_avg(wl)
+    sig = S.per_element(S.segment_sigmas(wl), wl, dev)
+    off_d = torch.from_numpy(off).to(dev)
+    m_tw = S.lamb_prev_momentum(wl, dev, sig)
+    k_d = momentum_scale(m_tw, off_d)  # from the warmup momentum, as the LAMB test checks
+    k = host(k_d)
+    k_el = np.repeat(k, np.diff(off)).astype(F32)
+    st = LambState.create(S.params(wl, dev), S.frozen_variance(wl, dev), m_tw, off_d,
+                          torch.from_numpy(c_avg).to(dev))
+    grp = OneBitGroup(N, n, dev, seg_off=off_d, seg_k=k_d, seg_err_ratio=st.err_ratio)
+    m = torch.empty((n, N), dtype=torch.float32, device=dev)
+    x_ref, vf_ref, mp_ref = host(st.x).copy(), host(st.v_fresh).copy(), host(st.m_prev).copy()
+    r_ref, c_ref = host(st.r).copy(), host(st.c).copy()
+    v_tw = host(st.v_frozen)
+    rho = np.ones(len(k), dtype=F32)
+    e_ref = np.zeros((n, N), dtype=F32)
+    E_ref = np.zeros(N, dtype=F32)
+    hp = (wl.lr, wl.eps, wl.beta1, wl.beta2, 0.5, 0.1, 10.0)  # thr, r_min, r_max: c moves
+    for t in (1, 2, 3):
+        S.momentum(wl, t, dev, sigma_elem=sig, out=m)
+        first = t == 1
+        grp.compress(m, t, first=first)
+        grp.server(t, first=first, decompress=False)
+        st.step_packed(grp.sv_bits, grp.sv_scales, k_d, n, *hp)
+        torch.cuda.synchronize()
+        tag = f"lamb step-ratio t={t}"
+        rho_el = np.repeat(rho, np.diff(off)).astype(F32)
+        bits, s = _workers(grp, m, e_ref, first, tag, k=k_el, err_ratio=rho_el)
+        sv = _server(grp, bits, s, E_ref, first, tag, err_ratio=rho_el)
+        E_ref = sv["E"]
+        mbar = R.decompress(sv["bits"], sv["S"], k_el, threads=THREADS)
+        _same(host(st.m_prev), mbar, f"{tag} decompressed momentum / k")
+        out = R.lamb_frozen_step(x_ref, mbar, mp_ref, vf_ref, v_tw, off, c_avg, r_ref, c_ref,
+                                 *hp)
+        _same(host(st.x), out["x"], f"{tag} parameters")
+        _same(host(st.v_fresh), out["v"], f"{tag} fresh variance")
+        _same(host(st.r), out["r"], f"{tag} r_t")
+        _same(host(st.c), out["c"], f"{tag} c_t")
+        _same(host(st.err_ratio), out["err_ratio"], f"{tag} error factor c_(t-1)/c_t")
+        if t >= 2:
+            assert np.any(out["err_ratio"] != 1), "the coefficients did not move"
+        x_ref, vf_ref, r_ref, c_ref, mp_ref = out["x"], out["v"], out["r"], out["c"], mbar
+        rho = out["err_ratio"]
         del sv, bits, s, out
         print(f"[whole] {tag} ok", flush=True)
     del grp, st, m, sig, e_ref, E_ref
