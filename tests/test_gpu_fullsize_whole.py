@@ -43,9 +43,10 @@ from tests._gpu import device, host, same_whole, same_whole_par
 from workloads import configs as C
 from workloads import synth as S
 
-# ONEBIT_WHOLE_CONFIG_STEPS=1 runs the 335M x 8 and 302-tensor x 16 tests over
-# their workloads' own step counts (20 each, about 10 minutes together);
-# by default they run 3 and 2 steps, which keeps the suite to minutes.
+# ONEBIT_WHOLE_CONFIG_STEPS=1 runs the 335M x 8 (momentum and gradient
+# forms) and 302-tensor x 16 tests over their workloads' own step counts (20
+# each, about 13 minutes together); by default they run 3, 2 and 2 steps,
+# which keeps the suite to minutes.
 CONFIG_STEPS = os.environ.get("ONEBIT_WHOLE_CONFIG_STEPS") == "1"
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(1500 if CONFIG_STEPS else 600)]
 F32 = np.float32
@@ -437,7 +438,7 @@ def test_bert_large_335M_x8_from_gradients_whole_buffer():
     e_ref = np.zeros((n, N), dtype=F32)
     E_ref = np.zeros(N, dtype=F32)
     sbits_prev, S_prev = np.zeros(N // 32, dtype=np.uint32), np.zeros(n, dtype=F32)
-    for t in (1, 2):
+    for t in _steps(wl, 2):
         S.momentum(wl, 100 + t, dev, sigma_elem=sig, out=g)
         first = t == 1
         grp.compress_grad(g, t, wl.beta1, first=first)
@@ -445,7 +446,7 @@ def test_bert_large_335M_x8_from_gradients_whole_buffer():
         grp.adam_step_packed(x, v, wl.lr, wl.eps)
         torch.cuda.synchronize()
         tag = f"fused t={t}"
-        mbar_prev = R.decompress(sbits_prev, S_prev)
+        mbar_prev = R.decompress(sbits_prev, S_prev, threads=THREADS)
 
         def momentum_row(i):
             return R.local_momentum(host(g[i])[None, :], mbar_prev, wl.beta1)[0]
@@ -453,9 +454,9 @@ def test_bert_large_335M_x8_from_gradients_whole_buffer():
         bits, s = _workers(grp, momentum_row, e_ref, first, tag)
         sv = _server(grp, bits, s, E_ref, first, tag)
         E_ref = sv["E"]
-        mbar = R.decompress(sv["bits"], sv["S"])
+        mbar = R.decompress(sv["bits"], sv["S"], threads=THREADS)
         _same(host(grp.mbar), mbar, f"{tag} decompressed momentum")
-        x_ref = R.adam_frozen_step(x_ref, mbar, v_h, wl.lr, wl.eps)
+        x_ref = R.adam_frozen_step(x_ref, mbar, v_h, wl.lr, wl.eps, threads=THREADS)
         _same(host(x), x_ref, f"{tag} parameters")
         sbits_prev, S_prev = sv["bits"], sv["S"]
         del sv, mbar, bits, s
