@@ -344,6 +344,51 @@ def momentum_scale_counts_empty(m, seg_off):
     return k
 
 
+def trust_ratio_root_of_quotient(x_l, u_l):
+    import math
+    sx, su = W.exact_sumsq(x_l), W.exact_sumsq(u_l)
+    if sx == 0.0 or su == 0.0:
+        return F32(1.0)
+    return F32(math.sqrt(sx / su))
+
+
+def sumsq_binary64_running(a):
+    acc = 0.0
+    for t in np.asarray(a, dtype=F32).astype(np.float64):
+        acc += t * t
+    return acc
+
+
+def _momentum_scale_variant(root_over_root=False, running_mean=False):
+    import math
+
+    def f(m, seg_off):
+        m = np.asarray(m, dtype=F32)
+        S = len(seg_off) - 1
+        rms = [0.0] * S
+        for l in range(S):
+            a, b = int(seg_off[l]), int(seg_off[l + 1])
+            if b > a:
+                s = W.exact_sumsq(m[a:b])
+                rms[l] = math.sqrt(s) / math.sqrt(b - a) if root_over_root else math.sqrt(s / (b - a))
+        valid = [r for r in rms if r > 0.0]
+        k = np.ones(S, dtype=F32)
+        if not valid:
+            return k
+        if running_mean:
+            acc = 0.0
+            for r in valid:
+                acc += r
+        else:
+            acc = math.fsum(valid)
+        mean = acc / len(valid)
+        for l in range(S):
+            if rms[l] > 0.0:
+                k[l] = F32(mean / rms[l])
+        return k
+    return f
+
+
 CASES = [
     # (id, module, attribute, replacement, pin modules)
     ("sign(0) = -1", B, "sign_bit", sign_gt, ["tests.test_oracle_bits", "tests.test_oracle_onebit"]),
@@ -393,6 +438,14 @@ CASES = [
     ("zero norm gives c = 0", W, "trust_ratio", trust_ratio_zero_norm_zero, ["tests.test_oracle_warmup"]),
     ("average started at 1", W, "coefficient_average", average_started_at_one, ["tests.test_oracle_warmup"]),
     ("k averages empty layers", W, "momentum_scale", momentum_scale_counts_empty, ["tests.test_oracle_warmup"]),
+    ("trust ratio as the root of the quotient", W, "trust_ratio", trust_ratio_root_of_quotient,
+     ["tests.test_oracle_warmup"]),
+    ("sum of squares in running binary64", W, "exact_sumsq", sumsq_binary64_running,
+     ["tests.test_oracle_warmup"]),
+    ("RMS as a root over a root", W, "momentum_scale", _momentum_scale_variant(root_over_root=True),
+     ["tests.test_oracle_warmup"]),
+    ("mean of RMS values by a running sum", W, "momentum_scale", _momentum_scale_variant(running_mean=True),
+     ["tests.test_oracle_warmup"]),
 ]
 
 

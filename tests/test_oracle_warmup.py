@@ -148,3 +148,149 @@ def test_lamb_direction_uses_new_moments():
     assert np.array_equal(out["u"], a(1.0, 0.0))
     # ||x|| = 2, ||u|| = 1: c = 2, x = (0 - 0.5 * 2 * 1, 2)
     assert out["c"][0] == 2.0 and np.array_equal(out["x"], a(-1.0, 2.0))
+
+
+# ------------------------------------------ rounding of the exact layer norms
+# The readings fix how the exact sums become binary32 results: each squared
+# norm is the exact sum rounded once to binary64; the trust ratio is the
+# binary64 quotient of the two correctly rounded roots; the RMS is the
+# correctly rounded root of the correctly rounded mean square.  The cases
+# below are built (with exact integer arithmetic, independent of the oracle)
+# so that the other natural compositions give a different binary32 result.
+
+from fractions import Fraction  # noqa: E402
+
+from tests._exactref import rn, rn64, sqrt_rn64  # noqa: E402
+
+
+def _exact_sumsq(vals) -> Fraction:
+    return sum(Fraction(float(v)) ** 2 for v in np.asarray(vals, dtype=F32))
+
+
+def _complete_squares(target: Fraction, count: int = 4) -> list:
+    """Up to `count` binary32 values whose squares sum to at most `target`,
+    within about target 2^-90 of it (each the largest square that fits)."""
+    vals, rem = [], target
+    for _ in range(count):
+        if rem <= 0:
+            break
+        y = F32(math.sqrt(float(rem)))
+        while Fraction(float(y)) ** 2 > rem:
+            y = np.nextafter(y, F32(0), dtype=F32)
+        if y == 0:
+            break
+        vals.append(y)
+        rem -= Fraction(float(y)) ** 2
+    return vals
+
+
+def _midpoint(k: int) -> Fraction:
+    """The binary32 midpoint just above f = 1 + k 2^-15 + 2^-23, whose
+    significand is odd, so that the tie rounds up (to even) while anything
+    just below the midpoint rounds down."""
+    f = F32(1.0 + k * 2.0 ** -15 + 2.0 ** -23)
+    return (Fraction(float(f)) + Fraction(float(np.nextafter(f, F32(2), dtype=F32)))) / 2
+
+
+def test_exact_rounding_helpers_match_ieee_binary64():
+    """rn64 and sqrt_rn64, which the rounding pins below rest on, agree with
+    the platform's correctly rounded binary64 division and square root on
+    seeded operands over a wide exponent range, and on exact squares."""
+    rng = np.random.default_rng(20)
+    x = rng.uniform(1, 2, 3000) * 2.0 ** rng.integers(-300, 300, 3000)
+    y = rng.uniform(1, 2, 3000) * 2.0 ** rng.integers(-300, 300, 3000)
+    r = (rng.uniform(1, 2, 3000) * 2.0 ** rng.integers(-120, 120, 3000)).astype(F32)
+    for a_, b_, r_ in zip(x, y, r):
+        assert rn64(Fraction(a_) / Fraction(b_)) == Fraction(a_ / b_)
+        assert sqrt_rn64(Fraction(a_)) == Fraction(math.sqrt(a_))
+        assert sqrt_rn64(Fraction(float(r_)) ** 2) == Fraction(float(r_))
+
+
+def test_sum_of_squares_is_exact_then_rounded_once():
+    """Squares 1, eight of 2^-56 and 2^-200: the exact sum 1 + 2^-53 + 2^-200
+    lies just above the midpoint between 1 and 1 + 2^-52, so its binary64
+    rounding is 1 + 2^-52, while a running binary64 sum drops every small
+    square and returns 1."""
+    v = a(1.0, *([2.0 ** -28] * 8), 2.0 ** -100)
+    want = rn64(_exact_sumsq(v))
+    assert want == 1 + Fraction(2) ** -52
+    assert W.exact_sumsq(v) == float(want)
+
+
+def test_trust_ratio_is_the_quotient_of_the_roots():
+    """||u||^2 = 2 and ||x|| / ||u|| within about 2^-80 of a binary32
+    midpoint: the reading's fl32(fl64(fl64(sqrt Sx) / fl64(sqrt Su))) and
+    the root of the quotient fl32(fl64(sqrt(fl64(Sx / Su)))) round to
+    different binary32 values; the oracle must give the first."""
+    u = a(1.0, 1.0)
+    for k in range(1, 2000):
+        M = _midpoint(k)
+        x = a(*_complete_squares(2 * M * M))
+        sx = rn64(_exact_sumsq(x))
+        reading = rn(rn64(sqrt_rn64(sx) / sqrt_rn64(Fraction(2))))
+        other = rn(sqrt_rn64(rn64(sx / 2)))
+        if reading != other:
+            break
+    else:
+        raise AssertionError("no discriminating case found")
+    assert W.trust_ratio(x, u) == reading
+
+
+def test_rms_is_the_root_of_the_rounded_mean_square():
+    """Layer 0 holds the single value 1 and layer 1 three values whose RMS
+    is within about 2^-70 of 2T - 1 - 2^-51 for a binary32 midpoint T (odd
+    significand below it). The reading's a_1 = fl64(sqrt(fl64(S_1 / 3)))
+    is that value, 1 + a_1 = 2T - 2^-51 is exact and k_0 = fl32(T - 2^-52)
+    rounds down; where the quotient of roots fl64(fl64(sqrt S_1) /
+    fl64(sqrt 3)) comes out one binary64 step higher, 1 + a_1 ties to the
+    even 2T and k_0 = fl32(T) rounds up. The oracle must give the reading's
+    k (the mean: the exact sum of the RMS values rounded once, then divided
+    by the count)."""
+    off = np.array([0, 1, 4], dtype=np.int64)
+
+    def k_of(a1):
+        mean = rn64(rn64(1 + a1) / 2)
+        return np.array([rn(rn64(mean / 1)), rn(rn64(mean / a1))], dtype=F32)
+
+    for k in range(1, 2000):
+        T = _midpoint(k)
+        m = np.zeros(4, dtype=F32)
+        m[0] = 1.0
+        fill = _complete_squares(3 * (2 * T - 1 - Fraction(2) ** -51) ** 2, count=3)
+        m[1:1 + len(fill)] = fill
+        s1 = rn64(_exact_sumsq(m[1:4]))
+        want = k_of(sqrt_rn64(rn64(s1 / 3)))
+        other = k_of(rn64(sqrt_rn64(s1) / sqrt_rn64(Fraction(3))))
+        if not np.array_equal(want, other):
+            break
+    else:
+        raise AssertionError("no discriminating case found")
+    assert np.array_equal(W.momentum_scale(m, off), want)
+
+
+def test_mean_of_rms_values_is_summed_exactly():
+    """RMS values 1, y, delta, delta with 1 + y = 4T - 2^-50 (T a binary32
+    midpoint with odd significand below it) and delta the binary32 value
+    just below 2^-51: the exact sum rounds once to 4T, the mean over the
+    four layers is T and k_0 = fl32(T) rounds up, while a running binary64
+    sum drops both deltas (each under half a step of 1 + y), leaving the
+    mean T - 2^-52 and k_0 rounding down."""
+    off = np.array([0, 1, 4, 5, 6], dtype=np.int64)
+    delta = np.nextafter(F32(2.0 ** -51), F32(0), dtype=F32)
+    for k in range(1, 2000):
+        T = _midpoint(k)
+        y = 4 * T - 1 - Fraction(2) ** -50
+        m = np.zeros(6, dtype=F32)
+        m[0] = 1.0
+        fill = _complete_squares(3 * y ** 2, count=3)
+        m[1:1 + len(fill)] = fill
+        m[4] = m[5] = delta
+        if sqrt_rn64(rn64(_exact_sumsq(m[1:4]) / 3)) == y:
+            break
+    else:
+        raise AssertionError("no layer with RMS exactly y found")
+    d = Fraction(float(delta))
+    want = np.array([rn(T), rn(rn64(T / y)), rn(rn64(T / d)), rn(rn64(T / d))],
+                    dtype=F32)
+    assert rn(T) != rn(T - Fraction(2) ** -52)
+    assert np.array_equal(W.momentum_scale(m, off), want)
