@@ -77,9 +77,8 @@ template <int NW>
 __global__ __launch_bounds__(256) void server_probe_kernel(const uint32_t* __restrict__ bits,
                                                            float* __restrict__ ef,
                                                            uint32_t* __restrict__ sv_bits,
-                                                           double* __restrict__ part, int64_t N,
-                                                           int32_t n, int64_t L, int64_t bpc,
-                                                           int64_t wrow) {
+                                                           double* __restrict__ part, int32_t n,
+                                                           int64_t L, int64_t bpc, int64_t wrow) {
     __shared__ double red[4];
     extern __shared__ uint32_t stage[];  // [n][64]
     const int64_t c = blockIdx.y;
@@ -239,10 +238,10 @@ int onebit_probe_server(const uint32_t* bits, float* ef, uint32_t* sv_bits, doub
     const size_t lds = (size_t)n * 64 * sizeof(uint32_t);
     if (n == 16)
         hipLaunchKernelGGL(server_probe_kernel<16>, grid, dim3(256), lds, stream, bits, ef, sv_bits,
-                           part, N, n, L, bpc, pitch);
+                           part, n, L, bpc, pitch);
     else
         hipLaunchKernelGGL(server_probe_kernel<0>, grid, dim3(256), lds, stream, bits, ef, sv_bits,
-                           part, N, n, L, bpc, pitch);
+                           part, n, L, bpc, pitch);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
