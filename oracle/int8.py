@@ -26,9 +26,11 @@ nearest integer, halves away from zero.
 
 Parity pins (tests/test_oracle_int8.py): codes in range, |deq - g'| < scale
 away from the clamp, integral x gives a deterministic code, all-zero blocks,
-the block maximum's code, unbiasedness over seeds, and the comparison u < p
+the block maximum's code, unbiasedness over seeds, the comparison u < p
 (a fraction equal to its own uniform rounds down: of the 2^24 grid values of
-u exactly p 2^24 lie below such a p).
+u exactly p 2^24 lie below such a p), the clamp reached from -128 and +128
+(a scale that rounds down puts the maximum just past 127), and a NaN left
+out of the block maximum.
 """
 
 from __future__ import annotations

@@ -101,3 +101,33 @@ def test_int8_large_step_counter_and_index():
         sl = slice(J0, J0 + 1024)
         o = int8_sr(host(g[sl]), None, 2**40 + 3, 0xFFFF_FFF0, block, J0=J0)
         assert np.array_equal(host(codes[sl]), o["codes"]), J0
+
+
+def test_int8_clamp_reached_from_128():
+    """The block maxima of the oracle pin's clamp case (x = -(127 + 2^-17)
+    and +(127 + 2^-17) at elements whose uniforms send them to -128 and
+    +128 before the clamp) code to -127 and +127 on the GPU too, bit-exact
+    with the oracle over the whole buffer, residuals included."""
+    from tests.test_oracle_int8 import clamp_case
+
+    dev = device()
+    seed, step, block = 3, 1, 256
+    M, scale, j_neg, j_pos = clamp_case(seed, step)
+    N = 1 << 19
+    print(f"[int8 clamp] N={N} J-={j_neg} J+={j_pos}", flush=True)
+    g_h = np.zeros(N, dtype=F32)
+    g_h[j_neg], g_h[j_pos] = -M, M
+    g = torch.from_numpy(g_h).to(dev)
+    err = torch.zeros(N, device=dev)
+    codes = torch.empty(N, dtype=torch.int8, device=dev)
+    scales = torch.empty(N // block, device=dev)
+    deq = torch.empty(N, device=dev)
+    ob.int8_sr_quantize(g, err, codes, scales, deq, N, block, seed, step)
+    torch.cuda.synchronize()
+    o = int8_sr(g_h, np.zeros(N, dtype=F32), seed, step, block)
+    c = host(codes)
+    assert int(c[j_neg]) == -127 and int(c[j_pos]) == 127
+    assert np.array_equal(c, o["codes"])
+    same_f32(host(scales), o["scales"], "scales")
+    same_f32(host(deq), o["deq"], "deq")
+    same_f32(host(err), o["e"], "residual")

@@ -564,3 +564,53 @@ def test_exact_sums_at_the_extreme_exponents():
         assert d <= abs(Fraction(float(lo)) - exact)
         if np.isfinite(hi):
             assert d <= abs(Fraction(float(hi)) - exact)
+
+
+def _cpp_trust_ratio(x_l, u_l):
+    """The C++ oracle's coefficient of one layer, taken through its warm-up
+    step: with u's entries 0 or 1, m = g = u, v = 1, beta1 = beta2 = 1/2 and
+    eps = 0 leave the update direction equal to u; zero padding to a common
+    length changes neither norm."""
+    x = np.asarray(x_l, dtype=F32)
+    u = np.asarray(u_l, dtype=F32)
+    assert np.all((u == 0) | (u == 1))
+    n = max(x.size, u.size)
+    xp, up = np.zeros(n, F32), np.zeros(n, F32)
+    xp[:x.size], up[:u.size] = x, u
+    out = R.lamb_warmup_step(xp, up, np.ones(n, F32), up, np.array([0, n], dtype=np.int64),
+                             lr=0.0, eps=0.0, beta1=0.5, beta2=0.5)
+    return out["c"][0]
+
+
+_CPP_PINS = [
+    ("tests.test_oracle_warmup", "test_sum_of_squares_is_exact_then_rounded_once", W, "exact_sumsq",
+     R.exact_sumsq),
+    ("tests.test_oracle_warmup", "test_trust_ratio_is_the_quotient_of_the_roots", W, "trust_ratio",
+     _cpp_trust_ratio),
+    ("tests.test_oracle_warmup", "test_rms_is_the_root_of_the_rounded_mean_square", W,
+     "momentum_scale", R.momentum_scale),
+    ("tests.test_oracle_warmup", "test_mean_of_rms_values_is_summed_exactly", W, "momentum_scale",
+     R.momentum_scale),
+    ("tests.test_oracle_int8", "test_codes_clamp_to_127_on_both_sides", None, "int8_sr", R.int8_sr),
+    ("tests.test_oracle_int8", "test_nan_is_left_out_of_the_block_maximum", None, "int8_sr",
+     R.int8_sr),
+    ("tests.test_oracle_optim", "test_lamb_step_by_hand", P, "lamb_frozen_step", R.lamb_frozen_step),
+    ("tests.test_oracle_onebit", "test_layer_coefficient_scales_the_momentum_not_the_error", O,
+     "worker_compress", R.worker_compress),
+]
+
+
+@pytest.mark.parametrize("pin", _CPP_PINS, ids=[p[1] for p in _CPP_PINS])
+def test_cpp_oracle_passes_the_rounding_and_edge_pins(pin):
+    """The numpy oracle's pins for rounding compositions, the INT8 clamp and
+    NaN, the LAMB step by hand and the layer coefficient, run with the C++
+    oracle's function in place of the numpy one (the pin module's own name
+    where it imported the function)."""
+    import importlib
+    from unittest import mock
+
+    mod_name, test_name, module, attr, cpp_fn = pin
+    tm = importlib.import_module(mod_name)
+    target = tm if module is None else module
+    with mock.patch.object(target, attr, cpp_fn):
+        getattr(tm, test_name)()

@@ -152,3 +152,53 @@ def test_per_tensor_scale():
     assert out["codes"][1234] in (126, 127)
     q = out["codes"].astype(np.int32)
     assert q.min() >= -127 and q.max() <= 127
+
+
+def clamp_case(seed: int = 3, step: int = 1):
+    """A block maximum M (the first binary32 above 1 with this property)
+    whose scale fl(M / 127) rounds down, so that the maximum's x is
+    +-(127 + 2^-17), and the first element indices below 2^19 whose uniform
+    lies on the far side of the fraction: u >= p for -x (floor -128), u < p
+    for +x. Returns (M, scale, J for -M, J for +M)."""
+    M = F32(1.0)
+    while F32(M / F32(M / F32(127))) <= F32(127):
+        M = np.nextafter(M, F32(2), dtype=F32)
+    scale = F32(M / F32(127))
+    x = F32(M / scale)
+    assert x > F32(127) and np.floor(-x) == -128
+    u = uniforms(0, 1 << 19, seed, step)
+    j_neg = int(np.nonzero(u >= F32(F32(-x) + F32(128)))[0][0])
+    j_pos = int(np.nonzero(u < F32(x - F32(127)))[0][0])
+    return M, scale, j_neg, j_pos
+
+
+def test_codes_clamp_to_127_on_both_sides():
+    """The clamp to [-127, 127] (tutorial, step 3) is reached: with the
+    block maximum of clamp_case() at an element whose uniform lies on the
+    far side of its fraction, the rounded value is -128 or +128, and the
+    code must come out -127 or +127, with deq = +-127 scale and
+    e = g' - deq."""
+    seed, step = 3, 1
+    M, scale, j_neg, j_pos = clamp_case(seed, step)
+    for J, sign in ((j_neg, -1), (j_pos, 1)):
+        b, j = divmod(J, 256)
+        g = np.zeros(256, dtype=F32)
+        g[j] = F32(sign) * M
+        out = int8_sr(g, None, seed=seed, step=step, J0=256 * b)
+        assert out["scales"][0] == scale
+        assert int(out["codes"][j]) == 127 * sign
+        deq = F32(F32(127 * sign) * scale)
+        assert out["deq"][j] == deq and out["e"][j] == F32(g[j] - deq)
+
+
+def test_nan_is_left_out_of_the_block_maximum():
+    """M is the maximum of |g'| over the block's non-NaN elements, so a NaN
+    leaves the other codes as they were; the NaN's own x is NaN, which the
+    fmin/fmax clamp turns into -127."""
+    g = np.zeros(256, dtype=F32)
+    g[:4] = [127, np.nan, 5, -3]
+    out = int8_sr(g, None, seed=1, step=1)
+    assert out["scales"][0] == 1
+    assert out["codes"][[0, 2, 3]].tolist() == [127, 5, -3]
+    assert int(out["codes"][1]) == -127 and out["deq"][1] == -127
+    assert np.isnan(out["e"][1])

@@ -3,14 +3,16 @@
 Each case plants one plausible mistake in the oracle -- a flipped sign, a
 wrong bit order, a swapped factor, a missing term -- for the duration of the
 case only (on the CPU, through the module attribute the oracle itself looks
-up at call time), runs the pins of the affected oracle modules, and asserts
-that at least one of them fails.  A case that no pin caught would mean the
+up at call time, and for the cases so marked also where a pin module
+imported the function by name), runs the pins of the affected oracle
+modules, and asserts that at least one of them fails.  A case that no pin caught would mean the
 oracle could carry that mistake unnoticed.
 
 The Philox cases rerun the rocRAND cross-check pins with the cross-check
 built once for this module.
 """
 
+import contextlib
 import importlib
 import inspect
 from unittest import mock
@@ -389,6 +391,139 @@ def _momentum_scale_variant(root_over_root=False, running_mean=False):
     return f
 
 
+def _int8_variant(clamp_lo=-127.0, div=127.0, err_flip=False, nan_in_max=False):
+    """The block quantiser with one planted change (stochastic rounding)."""
+    def f(g, e, seed, step, block=256, J0=0, rounding="stochastic"):
+        g = np.asarray(g, dtype=F32).ravel()
+        N = g.size
+        block = block or N
+        gc = g if e is None else (g + np.asarray(e, dtype=F32).ravel()).astype(F32)
+        a = np.abs(gc).reshape(-1, block)
+        if not nan_in_max:
+            a = np.where(np.isnan(a), F32(0.0), a)
+        scale = (np.fmax(a.max(axis=1).astype(F32), F32(0.0)) / F32(div)).astype(F32)
+        sc = np.repeat(scale, block)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            x = (gc / sc).astype(F32)
+            if rounding == "nearest":
+                q = I.round_half_away(x)
+            else:
+                u = I.uniforms(J0, N, seed, step)
+                fl = np.floor(x).astype(F32)
+                q = (fl + np.where(u < (x - fl).astype(F32), F32(1.0), F32(0.0))).astype(F32)
+            q = np.fmin(np.fmax(q, F32(clamp_lo)), F32(127.0))
+        zero = sc == 0
+        q = np.where(zero, F32(0.0), q)
+        with np.errstate(invalid="ignore", over="ignore"):
+            deq = np.where(zero, F32(0.0), (q * sc).astype(F32)).astype(F32)
+            e_new = ((deq - gc) if err_flip else (gc - deq)).astype(F32)
+        return {"gc": gc, "codes": q.astype(np.int8), "scales": scale, "deq": deq, "e": e_new}
+    return f
+
+
+def _uniforms_variant(step_word=2, key_swapped=False, words_reversed=False, low_bits=False,
+                      half_step=False):
+    """Element uniforms with one planted change in the counter, key, word
+    choice or the mapping of the word to [0, 1)."""
+    mask = np.uint64(0xFFFFFFFF)
+
+    def f(J0, count, seed, step):
+        J = np.arange(J0, J0 + count, dtype=np.uint64)
+        blk = J >> np.uint64(2)
+        cols = [blk & mask, blk >> np.uint64(32), np.zeros_like(blk), np.zeros_like(blk)]
+        cols[step_word] = np.full_like(blk, np.uint64(step) & mask)
+        key = [seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF]
+        if key_swapped:
+            key = key[::-1]
+        words = PH.philox4x32_10(np.stack(cols, axis=-1).astype(np.uint32),
+                                 np.array(key, dtype=np.uint32))
+        idx = (J & np.uint64(3)).astype(np.int64)
+        w = words[np.arange(count), 3 - idx if words_reversed else idx]
+        v = ((w & np.uint32(0xFFFFFF)) if low_bits else (w >> np.uint32(8))).astype(np.float64)
+        v = v * 2.0 ** -24 + (2.0 ** -25 if half_step else 0.0)
+        return v.astype(F32)
+    return f
+
+
+def _ratio_update_variant(nan_to_one=False, band_around_one=False):
+    def f(R, r_prev, c_avg, thr, r_min, r_max):
+        R = np.asarray(R, dtype=F32)
+        r_prev = np.asarray(r_prev, dtype=F32)
+        R = np.where(np.isnan(R), F32(1.0) if nan_to_one else r_prev, R).astype(F32)
+        base = np.ones_like(r_prev) if band_around_one else r_prev
+        lo = (F32(F32(1.0) - F32(thr)) * base).astype(F32)
+        hi = (F32(F32(1.0) + F32(thr)) * base).astype(F32)
+        r = np.fmin(np.fmax(np.fmin(np.fmax(R, lo), hi), F32(r_min)), F32(r_max)).astype(F32)
+        return r, (np.asarray(c_avg, dtype=F32) * r).astype(F32)
+    return f
+
+
+def _lamb_step_variant(ratio_inverted=False, fresh_v_in_step=False, c_t_always=None):
+    def f(x, m, m_prev, v_f, v_tw, seg_off, c_avg, r_prev, c_prev, lr, eps, beta1, beta2,
+          thr, r_min, r_max, use_c_t=False):
+        g = P.reconstruct_gradient(m, m_prev, beta1)
+        v_new = P.fresh_variance(v_f, g, beta2)
+        vt = np.asarray(v_tw, dtype=F32)
+        ratio = ((v_new / vt) if ratio_inverted else (vt / v_new)).astype(F32)
+        R = P.layer_max(ratio, seg_off)
+        r, c = P.lamb_ratio_update(R, r_prev, c_avg, thr, r_min, r_max)
+        use = use_c_t if c_t_always is None else c_t_always
+        c_used = c if use else np.asarray(c_prev, dtype=F32)
+        x_new = P.lamb_apply(x, m, v_new if fresh_v_in_step else v_tw, seg_off, c_used, lr, eps)
+        rho = (np.asarray(c_prev, dtype=F32) / c).astype(F32)
+        return {"x": x_new, "v": v_new, "R": R, "r": r, "c": c, "g": g, "err_ratio": rho}
+    return f
+
+
+def adam_step_adds(x, m, v, lr, eps):
+    x = np.asarray(x, dtype=F32)
+    den = (np.sqrt(np.asarray(v, dtype=F32)) + F32(eps)).astype(F32)
+    upd = (np.asarray(m, dtype=F32) / den).astype(F32)
+    return (x + (F32(lr) * upd).astype(F32)).astype(F32)
+
+
+def clamp_nan_to_plus(x, clip):
+    c = F32(clip)
+    if not (c > 0) or np.isinf(c):
+        return x
+    return np.where(np.isnan(x), c, np.fmin(np.fmax(x, -c), c)).astype(F32)
+
+
+def clamp_keeps_nan(x, clip):
+    c = F32(clip)
+    if not (c > 0) or np.isinf(c):
+        return x
+    return np.minimum(np.maximum(x, -c), c).astype(F32)
+
+
+def worker_k_on_the_sum(m, e, clip=0.0, reset=False, k=None, unit_scale=False, err_ratio=None):
+    """k_l (m + e) in place of k_l m + e: the scaled momentum's error scaled again."""
+    orig = O.__dict__["_orig_worker_compress"]
+    if k is None or reset:
+        return orig(m, e, clip, reset, k, unit_scale, err_ratio)
+    e = np.asarray(e, dtype=F32)
+    if err_ratio is not None:
+        e = (np.asarray(err_ratio, dtype=F32)[None, :] * e).astype(F32)
+    kk = np.asarray(k, dtype=F32)
+    # fold the extra factor into the error: k m + (k e) == k (m + e) up to rounding
+    return orig(m, (kk[None, :] * e).astype(F32), clip, reset, k, unit_scale, None)
+
+
+def server_scales_divided_first(bits_c, s_c, E_c, reset=False, unit_scale=False, err_ratio_c=None):
+    """The average as the ordered sum of +-s_i / n in place of (sum of +-s_i) / n."""
+    s_c = np.asarray(s_c, dtype=F32)
+    n = s_c.shape[0]
+    acc = np.zeros(np.asarray(bits_c).shape[1] * 32, dtype=F32)
+    for i in range(n):
+        acc = (acc + B.signed(B.unpack(bits_c[i]), F32(s_c[i] / F32(n)))).astype(F32)
+    E_in = np.zeros_like(acc) if reset else np.asarray(E_c, dtype=F32)
+    if err_ratio_c is not None and not reset:
+        E_in = (np.asarray(err_ratio_c, dtype=F32) * E_in).astype(F32)
+    g2 = (acc + E_in).astype(F32)
+    S = F32(1.0) if unit_scale else X.mean_abs_f32(g2)
+    return {"avg": acc, "g2": g2, "bits": B.pack(B.sign_bit(g2)), "S": S, "E": O.error_from(g2, S)}
+
+
 CASES = [
     # (id, module, attribute, replacement, pin modules)
     ("sign(0) = -1", B, "sign_bit", sign_gt, ["tests.test_oracle_bits", "tests.test_oracle_onebit"]),
@@ -446,6 +581,42 @@ CASES = [
      ["tests.test_oracle_warmup"]),
     ("mean of RMS values by a running sum", W, "momentum_scale", _momentum_scale_variant(running_mean=True),
      ["tests.test_oracle_warmup"]),
+    # the cases below also replace the name where a pin module imported it
+    ("INT8 codes clamped at -128", I, "int8_sr", _int8_variant(clamp_lo=-128.0),
+     ["tests.test_oracle_int8"], True),
+    ("INT8 scale max/128", I, "int8_sr", _int8_variant(div=128.0), ["tests.test_oracle_int8"], True),
+    ("INT8 error with the wrong sign", I, "int8_sr", _int8_variant(err_flip=True),
+     ["tests.test_oracle_int8"], True),
+    ("INT8 NaN kept in the block maximum", I, "int8_sr", _int8_variant(nan_in_max=True),
+     ["tests.test_oracle_int8"], True),
+    ("Philox step in counter word 3", PH, "uniforms", _uniforms_variant(step_word=3),
+     ["tests.test_oracle_philox"], True),
+    ("Philox key halves swapped", PH, "uniforms", _uniforms_variant(key_swapped=True),
+     ["tests.test_oracle_philox"], True),
+    ("Philox words in reverse order", PH, "uniforms", _uniforms_variant(words_reversed=True),
+     ["tests.test_oracle_philox"], True),
+    ("uniform from the low 24 bits", PH, "uniforms", _uniforms_variant(low_bits=True),
+     ["tests.test_oracle_philox"], True),
+    ("uniform offset by half a step", PH, "uniforms", _uniforms_variant(half_step=True),
+     ["tests.test_oracle_philox"], True),
+    ("no valid ratio gives r = 1", P, "lamb_ratio_update", _ratio_update_variant(nan_to_one=True),
+     ["tests.test_oracle_optim"]),
+    ("ratio band around 1", P, "lamb_ratio_update", _ratio_update_variant(band_around_one=True),
+     ["tests.test_oracle_optim"]),
+    ("LAMB ratio fresh over frozen", P, "lamb_frozen_step", _lamb_step_variant(ratio_inverted=True),
+     ["tests.test_oracle_optim"]),
+    ("LAMB step with the fresh variance", P, "lamb_frozen_step",
+     _lamb_step_variant(fresh_v_in_step=True), ["tests.test_oracle_optim"]),
+    ("LAMB step always with c_t", P, "lamb_frozen_step", _lamb_step_variant(c_t_always=True),
+     ["tests.test_oracle_optim"]),
+    ("LAMB step never with c_t", P, "lamb_frozen_step", _lamb_step_variant(c_t_always=False),
+     ["tests.test_oracle_optim"]),
+    ("Adam step adds the update", P, "adam_frozen_step", adam_step_adds, ["tests.test_oracle_optim"]),
+    ("clamp sends NaN to +clip", O, "clamp", clamp_nan_to_plus, ["tests.test_oracle_onebit"]),
+    ("clamp keeps NaN", O, "clamp", clamp_keeps_nan, ["tests.test_oracle_onebit"]),
+    ("k on momentum plus error", O, "worker_compress", worker_k_on_the_sum, ["tests.test_oracle_onebit"]),
+    ("server divides the scales first", O, "server_chunk", server_scales_divided_first,
+     ["tests.test_oracle_onebit"]),
 ]
 
 
@@ -459,15 +630,25 @@ def fixtures():
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_pins_catch_planted_mistake(case, fixtures):
-    _, module, attr, mutant, pins = case
+    _, module, attr, mutant, pins = case[:5]
+    by_name = len(case) > 5 and case[5]
     if "tests.test_oracle_philox" in pins and "rocrand_dump" not in fixtures:
         pytest.skip("hipcc not available to build the rocRAND cross-check")
+    # imported before any patching, so that no pin module binds a mutant
+    pin_mods = [importlib.import_module(m) for m in pins]
     original = getattr(module, attr)
     extra = {f"_orig_{attr}": original}
     if attr == "uniforms":
         extra = {"_orig_uniforms": PH.uniforms}
-    with mock.patch.dict(module.__dict__, extra), mock.patch.object(module, attr, mutant):
+    with contextlib.ExitStack() as stack:
+        stack.enter_context(mock.patch.dict(module.__dict__, extra))
+        stack.enter_context(mock.patch.object(module, attr, mutant))
+        if by_name:  # pin modules that imported the function by name
+            for tm in pin_mods:
+                if getattr(tm, attr, None) is original:
+                    stack.enter_context(mock.patch.object(tm, attr, mutant))
         caught = _first_failing(pins, fixtures)
     assert caught is not None, f"no pin caught the planted mistake in {module.__name__}.{attr}"
-    # and the unmodified oracle passes the same pins
+    # and the unmodified oracle is back in place everywhere
     assert getattr(module, attr) is original
+    assert all(getattr(tm, attr, original) is not mutant for tm in pin_mods)

@@ -389,3 +389,19 @@ def test_two_level_identity_with_step_ratio():
                 assert frac(mbar[j]) == avg_m + Fraction(rho) * delta_prev[j] - delta
                 delta_prev[j] = delta
             e, E = w["e"], sv["E"]
+
+
+def test_layer_coefficient_scales_the_momentum_not_the_error():
+    """g' = k_l m + e: the 1-bit LAMB page (layer-scaling paragraph) scales
+    each layer's local momentum before the compressed exchange, and the
+    carried error, formed on scaled values, is added as it is. With m = 1,
+    e = 1/2 and k = 2 on the first layer, 4 on the second, g' is 2.5 and
+    4.5, the chunk mean 3.5 and the new error -1 and +1."""
+    m = np.ones((1, 64), dtype=F32)
+    e = np.full((1, 64), 0.5, dtype=F32)
+    k = np.repeat(np.array([2, 4], dtype=F32), 32)
+    out = O.worker_compress(m, e, k=k)
+    assert np.all(out["gc"][0, :32] == 2.5) and np.all(out["gc"][0, 32:] == 4.5)
+    assert out["s"][0, 0] == 3.5
+    assert np.all(out["e"][0, :32] == -1) and np.all(out["e"][0, 32:] == 1)
+    assert np.all(out["bits"] == 0xFFFFFFFF)

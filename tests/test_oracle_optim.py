@@ -146,3 +146,22 @@ def test_lamb_error_ratio_output():
                              lr=1.0, eps=0.0, beta1=0.5, beta2=0.5, thr=0.1, r_min=1.0, r_max=1.0)
     assert np.array_equal(out["c"], a(2.0, 3.0))
     assert np.array_equal(out["err_ratio"], a(0.5, 2.0))
+
+
+def test_lamb_step_by_hand():
+    """One layer by hand, every value dyadic: beta1 = beta2 = 1/2, m = 1,
+    m_prev = 0 give g = 2 and v = (0 + 4) / 2 = 2; v_Tw = 16 gives the ratio
+    v_Tw / v = 8 (frozen over fresh, 1-bit LAMB page, algorithm), clipped to
+    1.1 r_{t-1} = fl(1.1); the step uses the frozen variance and c_{t-1}:
+    x = 1 - (1 * 1/2) * (1 / sqrt(16)) = 0.875."""
+    one = np.ones(4, dtype=F32)
+    out = P.lamb_frozen_step(one, one, 0 * one, 0 * one, 16 * one, [0, 4],
+                             c_avg=np.array([2], F32), r_prev=np.array([1], F32),
+                             c_prev=np.array([0.5], F32), lr=1.0, eps=0.0, beta1=0.5,
+                             beta2=0.5, thr=0.1, r_min=0.5, r_max=4.0)
+    assert np.all(out.get("g", 2) == 2) and np.all(out["v"] == 2)
+    assert out["R"][0] == 8
+    r = F32(F32(1) + F32(0.1))
+    assert out["r"][0] == r and out["c"][0] == F32(2 * r)
+    assert np.all(out["x"] == F32(0.875))
+    assert out["err_ratio"][0] == F32(F32(0.5) / F32(2 * r))
