@@ -597,15 +597,19 @@ _CPP_PINS = [
     ("tests.test_oracle_optim", "test_lamb_step_by_hand", P, "lamb_frozen_step", R.lamb_frozen_step),
     ("tests.test_oracle_onebit", "test_layer_coefficient_scales_the_momentum_not_the_error", O,
      "worker_compress", R.worker_compress),
+    ("tests.test_oracle_optim", "test_adam_step_rounding_sequence", P, "adam_frozen_step",
+     R.adam_frozen_step),
+    ("tests.test_oracle_onebit", "test_division_by_the_layer_coefficient_is_a_true_division", O,
+     "decompress", R.decompress),
 ]
 
 
 @pytest.mark.parametrize("pin", _CPP_PINS, ids=[p[1] for p in _CPP_PINS])
 def test_cpp_oracle_passes_the_rounding_and_edge_pins(pin):
-    """The numpy oracle's pins for rounding compositions, the INT8 clamp and
-    NaN, the LAMB step by hand and the layer coefficient, run with the C++
-    oracle's function in place of the numpy one (the pin module's own name
-    where it imported the function)."""
+    """The numpy oracle's pins for rounding compositions and sequences, the
+    INT8 clamp and NaN, the LAMB step by hand and the layer coefficient, run
+    with the C++ oracle's function in place of the numpy one (the pin
+    module's own name where it imported the function)."""
     import importlib
     from unittest import mock
 

@@ -524,6 +524,67 @@ def server_scales_divided_first(bits_c, s_c, E_c, reset=False, unit_scale=False,
     return {"avg": acc, "g2": g2, "bits": B.pack(B.sign_bit(g2)), "S": S, "E": O.error_from(g2, S)}
 
 
+def layer_scale_by_reciprocal(buf, seg_off, k, divide):
+    buf = np.asarray(buf, dtype=F32)
+    out = np.empty_like(buf)
+    k = np.asarray(k, dtype=F32)
+    for l in range(len(seg_off) - 1):
+        a, b = int(seg_off[l]), int(seg_off[l + 1])
+        out[..., a:b] = buf[..., a:b] * (F32(F32(1) / k[l]) if divide else k[l])
+    return out
+
+
+def decompress_by_reciprocal(sbits, S, k=None):
+    out = O.__dict__["_orig_decompress"](sbits, S)
+    if k is not None:
+        out = (out * (F32(1) / np.asarray(k, dtype=F32)).astype(F32)).astype(F32)
+    return out
+
+
+def reconstruct_by_reciprocal(m, m_prev, beta1):
+    b1 = F32(beta1)
+    omb1 = F32(F32(1) - b1)
+    num = (np.asarray(m, dtype=F32) - (b1 * np.asarray(m_prev, dtype=F32)).astype(F32)).astype(F32)
+    return (num * F32(F32(1) / omb1)).astype(F32)
+
+
+def fresh_variance_square_last(v_f, g, beta2):
+    b2 = F32(beta2)
+    omb2 = F32(F32(1) - b2)
+    g = np.asarray(g, dtype=F32)
+    return ((b2 * np.asarray(v_f, dtype=F32)).astype(F32)
+            + ((omb2 * g).astype(F32) * g).astype(F32)).astype(F32)
+
+
+def adam_lr_times_m_first(x, m, v, lr, eps):
+    den = (np.sqrt(np.asarray(v, dtype=F32)) + F32(eps)).astype(F32)
+    upd = ((F32(lr) * np.asarray(m, dtype=F32)).astype(F32) / den).astype(F32)
+    return (np.asarray(x, dtype=F32) - upd).astype(F32)
+
+
+def adam_by_reciprocal(x, m, v, lr, eps):
+    den = (np.sqrt(np.asarray(v, dtype=F32)) + F32(eps)).astype(F32)
+    upd = (np.asarray(m, dtype=F32) * (F32(1) / den).astype(F32)).astype(F32)
+    return (np.asarray(x, dtype=F32) - (F32(lr) * upd).astype(F32)).astype(F32)
+
+
+def lamb_apply_c_times_update_first(x, m, v_tw, seg_off, c_used, lr, eps):
+    x = np.asarray(x, dtype=F32)
+    den = (np.sqrt(np.asarray(v_tw, dtype=F32)) + F32(eps)).astype(F32)
+    upd = (np.asarray(m, dtype=F32) / den).astype(F32)
+    out = np.empty_like(x)
+    for l in range(len(seg_off) - 1):
+        a, b = int(seg_off[l]), int(seg_off[l + 1])
+        cu = (F32(c_used[l]) * upd[a:b]).astype(F32)
+        out[a:b] = (x[a:b] - (F32(lr) * cu).astype(F32)).astype(F32)
+    return out
+
+
+def momentum_scale_inverted(m, seg_off):
+    k = W.__dict__["_orig_momentum_scale"](m, seg_off)
+    return (F32(1) / k).astype(F32)
+
+
 CASES = [
     # (id, module, attribute, replacement, pin modules)
     ("sign(0) = -1", B, "sign_bit", sign_gt, ["tests.test_oracle_bits", "tests.test_oracle_onebit"]),
@@ -617,6 +678,20 @@ CASES = [
     ("k on momentum plus error", O, "worker_compress", worker_k_on_the_sum, ["tests.test_oracle_onebit"]),
     ("server divides the scales first", O, "server_chunk", server_scales_divided_first,
      ["tests.test_oracle_onebit"]),
+    ("layer scale divides by a reciprocal", O, "layer_scale", layer_scale_by_reciprocal,
+     ["tests.test_oracle_onebit"]),
+    ("decompression divides by a reciprocal", O, "decompress", decompress_by_reciprocal,
+     ["tests.test_oracle_onebit"]),
+    ("gradient reconstruction by a reciprocal", P, "reconstruct_gradient", reconstruct_by_reciprocal,
+     ["tests.test_oracle_optim"]),
+    ("fresh variance squares last", P, "fresh_variance", fresh_variance_square_last,
+     ["tests.test_oracle_optim"]),
+    ("Adam step with lr m first", P, "adam_frozen_step", adam_lr_times_m_first,
+     ["tests.test_oracle_optim"]),
+    ("Adam step by a reciprocal", P, "adam_frozen_step", adam_by_reciprocal, ["tests.test_oracle_optim"]),
+    ("LAMB step with c times the update first", P, "lamb_apply", lamb_apply_c_times_update_first,
+     ["tests.test_oracle_optim"]),
+    ("k_l inverted", W, "momentum_scale", momentum_scale_inverted, ["tests.test_oracle_warmup"]),
 ]
 
 

@@ -405,3 +405,28 @@ def test_layer_coefficient_scales_the_momentum_not_the_error():
     assert out["s"][0, 0] == 3.5
     assert np.all(out["e"][0, :32] == -1) and np.all(out["e"][0, 32:] == 1)
     assert np.all(out["bits"] == 0xFFFFFFFF)
+
+
+def test_division_by_the_layer_coefficient_is_a_true_division():
+    """x / k_l is one correctly rounded division, in the layer scale and in
+    the decompression (1-bit LAMB page, layer-scaling paragraph: divide by
+    the same coefficient afterwards), never x * fl(1 / k_l); the sample's
+    coefficients are not powers of two, so the two differ on some elements."""
+    rng = np.random.default_rng(12)
+    N = 512
+    off = [0, 100, 300, 512]
+    k = np.array([3.0, 0.7, 10.3], dtype=F32)
+    x = (rng.uniform(-2, 2, N)).astype(F32)
+    kk = O.per_element_k(off, k)
+    want = np.array([rn(frac(a) / frac(b)) for a, b in zip(x, kk)], dtype=F32)
+    recip = np.array([rn(frac(a) * frac(rn(1 / frac(b)))) for a, b in zip(x, kk)], dtype=F32)
+    assert not np.array_equal(want, recip)
+    assert np.array_equal(O.layer_scale(x, off, k, divide=True), want)
+    # decompression: +-S[c] / k_l with two chunks
+    S = np.array([0.3, 1.7], dtype=F32)
+    words = rng.integers(0, 2 ** 32, N // 32, dtype=np.uint64).astype(np.uint32)
+    b = B.unpack(words)
+    sc = np.repeat(S, N // 2)
+    dec = np.array([rn(frac(s if bit else -s) / frac(kv)) for bit, s, kv in zip(b, sc, kk)],
+                   dtype=F32)
+    assert np.array_equal(O.decompress(words, S, kk), dec)

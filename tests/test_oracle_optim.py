@@ -7,9 +7,12 @@ r_t, the basic-1-bit-LAMB special case r_min = r_max = 1, and a fixed point
 where the fresh variance equals the frozen one.
 """
 
+from fractions import Fraction
+
 import numpy as np
 
 from oracle import optim as P
+from tests._exactref import rn
 
 F32 = np.float32
 
@@ -165,3 +168,90 @@ def test_lamb_step_by_hand():
     assert out["r"][0] == r and out["c"][0] == F32(2 * r)
     assert np.all(out["x"] == F32(0.875))
     assert out["err_ratio"][0] == F32(F32(0.5) / F32(2 * r))
+
+
+# ------------------------------------------------ rounding sequences, exactly
+# The pages fix no rounding order; the step formulas are read as the
+# sequences below (one binary32 rounding per operation, true division, the
+# square root correctly rounded). Each pin evaluates its sequence on seeded
+# values with exact rationals and one explicit rounding per step, and checks
+# that the sample separates it from the plausible other orders.
+
+def _fr(a):
+    return [Fraction(float(t)) for t in np.asarray(a, dtype=F32).ravel()]
+
+
+def _sample(seed, n=400, lo=-3.0, hi=3.0):
+    rng = np.random.default_rng(seed)
+    return (rng.uniform(lo, hi, n) * 2.0 ** rng.integers(-4, 5, n)).astype(F32)
+
+
+def test_adam_step_rounding_sequence():
+    """x - fl(lr fl(m / fl(sqrt(v) + eps))); half of x is 0, so that the
+    update's own rounding shows."""
+    x, m = _sample(1), _sample(2)
+    x[::2] = 0
+    v = np.abs(_sample(3)) + F32(1e-3)
+    lr, eps = F32(0.37), F32(1e-6)
+    den = [rn(Fraction(float(np.sqrt(vi))) + Fraction(float(eps))) for vi in v]
+    q = [rn(mi / Fraction(float(d))) for mi, d in zip(_fr(m), den)]
+    want = [rn(xi - Fraction(float(rn(Fraction(float(lr)) * Fraction(float(qi))))))
+            for xi, qi in zip(_fr(x), q)]
+    got = P.adam_frozen_step(x, m, v, lr, eps)
+    assert np.array_equal(got, np.array(want, dtype=F32))
+    lr_first = [rn(xi - Fraction(float(rn(Fraction(float(rn(Fraction(float(lr)) * mi)))
+                                             / Fraction(float(d))))))
+                for xi, mi, d in zip(_fr(x), _fr(m), den)]
+    recip = [rn(xi - Fraction(float(rn(Fraction(float(lr)) * Fraction(float(
+        rn(mi * Fraction(float(rn(1 / Fraction(float(d))))))))))))
+        for xi, mi, d in zip(_fr(x), _fr(m), den)]
+    assert want != lr_first and want != recip
+
+
+def test_gradient_reconstruction_rounding_sequence():
+    """fl(fl(m - fl(beta1 m_prev)) / fl(1 - beta1)), a true division."""
+    m, mp = _sample(4), _sample(5)
+    b1 = F32(0.9)
+    omb1 = Fraction(float(F32(F32(1) - b1)))
+    num = [rn(mi - Fraction(float(rn(Fraction(float(b1)) * pi)))) for mi, pi in zip(_fr(m), _fr(mp))]
+    want = [rn(Fraction(float(t)) / omb1) for t in num]
+    assert np.array_equal(P.reconstruct_gradient(m, mp, b1), np.array(want, dtype=F32))
+    recip = Fraction(float(rn(1 / omb1)))
+    assert want != [rn(Fraction(float(t)) * recip) for t in num]
+
+
+def test_fresh_variance_rounding_sequence():
+    """fl(fl(beta2 v) + fl(fl(1 - beta2) fl(g g))): the square first."""
+    v = np.abs(_sample(6))
+    g = _sample(7)
+    b2 = F32(0.999)
+    omb2 = Fraction(float(F32(F32(1) - b2)))
+    a = [rn(Fraction(float(b2)) * vi) for vi in _fr(v)]
+    want = [rn(Fraction(float(ai)) + Fraction(float(rn(omb2 * Fraction(float(rn(gi * gi)))))))
+            for ai, gi in zip(a, _fr(g))]
+    assert np.array_equal(P.fresh_variance(v, g, b2), np.array(want, dtype=F32))
+    other = [rn(Fraction(float(ai)) + Fraction(float(rn(Fraction(float(rn(omb2 * gi))) * gi))))
+             for ai, gi in zip(a, _fr(g))]
+    assert want != other
+
+
+def test_lamb_apply_rounding_sequence():
+    """x - fl(fl(lr c_l) fl(m / fl(sqrt(v_Tw) + eps))) per layer."""
+    x, m = _sample(8), _sample(9)
+    x[::2] = 0
+    v = np.abs(_sample(10)) + F32(1e-3)
+    off = [0, 150, 400]
+    c = np.array([0.7, 1.3], dtype=F32)
+    lr, eps = F32(1e-3), F32(1e-6)
+    den = [rn(Fraction(float(np.sqrt(vi))) + Fraction(float(eps))) for vi in v]
+    q = [rn(mi / Fraction(float(d))) for mi, d in zip(_fr(m), den)]
+    want, other = [], []
+    for l in range(2):
+        step = Fraction(float(rn(Fraction(float(lr)) * Fraction(float(c[l])))))
+        for j in range(off[l], off[l + 1]):
+            xj, qj = Fraction(float(x[j])), Fraction(float(q[j]))
+            want.append(rn(xj - Fraction(float(rn(step * qj)))))
+            cq = Fraction(float(rn(Fraction(float(c[l])) * qj)))
+            other.append(rn(xj - Fraction(float(rn(Fraction(float(lr)) * cq)))))
+    assert np.array_equal(P.lamb_apply(x, m, v, off, c, lr, eps), np.array(want, dtype=F32))
+    assert want != other
