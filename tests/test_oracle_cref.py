@@ -601,6 +601,8 @@ _CPP_PINS = [
      R.adam_frozen_step),
     ("tests.test_oracle_onebit", "test_division_by_the_layer_coefficient_is_a_true_division", O,
      "decompress", R.decompress),
+    ("tests.test_oracle_warmup", "test_lamb_step_takes_this_steps_coefficient_not_the_average", W,
+     "lamb_warmup_step", R.lamb_warmup_step),
 ]
 
 

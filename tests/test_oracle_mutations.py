@@ -585,6 +585,65 @@ def momentum_scale_inverted(m, seg_off):
     return (F32(1) / k).astype(F32)
 
 
+def adam_warmup_with_old_moments(x, m, v, g, lr, eps, beta1, beta2):
+    m_new, v_new = W.moments(m, v, g, beta1, beta2)
+    u = W.adam_direction(m, v, eps)
+    return {"x": (np.asarray(x, dtype=F32) - (F32(lr) * u).astype(F32)).astype(F32),
+            "m": m_new, "v": v_new}
+
+
+def moments_square_last(m, v, g, beta1, beta2):
+    b1, b2 = F32(beta1), F32(beta2)
+    g = np.asarray(g, dtype=F32)
+    m_new = ((b1 * np.asarray(m, dtype=F32)).astype(F32)
+             + (F32(F32(1) - b1) * g).astype(F32)).astype(F32)
+    v_new = ((b2 * np.asarray(v, dtype=F32)).astype(F32)
+             + ((F32(F32(1) - b2) * g).astype(F32) * g).astype(F32)).astype(F32)
+    return m_new, v_new
+
+
+def direction_eps_inside_the_root(m, v, eps):
+    den = np.sqrt((np.asarray(v, dtype=F32) + F32(eps)).astype(F32)).astype(F32)
+    return (np.asarray(m, dtype=F32) / den).astype(F32)
+
+
+def lamb_warmup_step_scaled_by_the_average(x, m, v, g, seg_off, lr, eps, beta1, beta2,
+                                           c_avg=None, beta_c=0.9):
+    r = dict(W.__dict__["_orig_lamb_warmup_step"](x, m, v, g, seg_off, lr, eps, beta1, beta2,
+                                                    c_avg, beta_c))
+    if c_avg is not None:
+        x = np.asarray(x, dtype=F32)
+        r["x"] = x.copy()
+        for l in range(len(seg_off) - 1):
+            a, b = int(seg_off[l]), int(seg_off[l + 1])
+            step = F32(F32(lr) * F32(np.asarray(c_avg, dtype=F32)[l]))
+            r["x"][a:b] = (x[a:b] - (step * r["u"][a:b]).astype(F32)).astype(F32)
+    return r
+
+
+def average_with_binary64_one_minus_beta(c_avg, c, beta_c):
+    c = np.asarray(c, dtype=F32)
+    if c_avg is None:
+        return c.copy()
+    return ((F32(beta_c) * np.asarray(c_avg, dtype=F32)).astype(F32)
+            + (np.float64(1.0 - beta_c) * c.astype(np.float64)).astype(F32)).astype(F32)
+
+
+def server_error_before_the_divide(bits_c, s_c, E_c, reset=False, unit_scale=False, err_ratio_c=None):
+    s_c = np.asarray(s_c, dtype=F32)
+    n = s_c.shape[0]
+    acc = np.zeros(np.asarray(bits_c).shape[1] * 32, dtype=F32)
+    for i in range(n):
+        acc = (acc + B.signed(B.unpack(bits_c[i]), s_c[i])).astype(F32)
+    E_in = np.zeros_like(acc) if reset else np.asarray(E_c, dtype=F32)
+    if err_ratio_c is not None and not reset:
+        E_in = (np.asarray(err_ratio_c, dtype=F32) * E_in).astype(F32)
+    g2 = ((acc + E_in).astype(F32) / F32(n)).astype(F32)
+    S = F32(1.0) if unit_scale else X.mean_abs_f32(g2)
+    return {"avg": (acc / F32(n)).astype(F32), "g2": g2, "bits": B.pack(B.sign_bit(g2)), "S": S,
+            "E": O.error_from(g2, S)}
+
+
 CASES = [
     # (id, module, attribute, replacement, pin modules)
     ("sign(0) = -1", B, "sign_bit", sign_gt, ["tests.test_oracle_bits", "tests.test_oracle_onebit"]),
@@ -692,6 +751,17 @@ CASES = [
     ("LAMB step with c times the update first", P, "lamb_apply", lamb_apply_c_times_update_first,
      ["tests.test_oracle_optim"]),
     ("k_l inverted", W, "momentum_scale", momentum_scale_inverted, ["tests.test_oracle_warmup"]),
+    ("Adam warm-up step with the old moments", W, "adam_warmup_step", adam_warmup_with_old_moments,
+     ["tests.test_oracle_warmup"]),
+    ("variance with the square last", W, "moments", moments_square_last, ["tests.test_oracle_warmup"]),
+    ("warm-up direction with eps inside the root", W, "adam_direction", direction_eps_inside_the_root,
+     ["tests.test_oracle_warmup"]),
+    ("LAMB warm-up step scaled by the average", W, "lamb_warmup_step",
+     lamb_warmup_step_scaled_by_the_average, ["tests.test_oracle_warmup"]),
+    ("coefficient average with a binary64 1 - beta", W, "coefficient_average",
+     average_with_binary64_one_minus_beta, ["tests.test_oracle_warmup"]),
+    ("server adds its error before dividing by n", O, "server_chunk", server_error_before_the_divide,
+     ["tests.test_oracle_onebit"]),
 ]
 
 

@@ -294,3 +294,49 @@ def test_mean_of_rms_values_is_summed_exactly():
                     dtype=F32)
     assert rn(T) != rn(T - Fraction(2) ** -52)
     assert np.array_equal(W.momentum_scale(m, off), want)
+
+
+def test_lamb_step_takes_this_steps_coefficient_not_the_average():
+    """With a running average already in place (c_avg = 2 from earlier
+    steps), the step still moves x by lr * c_l * u with this step's c_l = 5
+    (x = (3, 4), u = (1, 0)); the average moves to 1/2 * 2 + 1/2 * 5."""
+    out = W.lamb_warmup_step(a(3.0, 4.0), a(0.5, 0.0), a(0.25, 0.25), a(0.5, 0.0), [0, 2],
+                             lr=0.25, eps=0.0, beta1=0.5, beta2=0.5, c_avg=a(2.0), beta_c=0.5)
+    assert out["c"][0] == 5
+    assert np.array_equal(out["x"], a(3.0 - 1.25, 4.0))
+    assert out["c_avg"][0] == F32(3.5)
+
+
+def test_moments_and_average_rounding_sequences():
+    """m = fl(fl(b1 m) + fl(fl(1 - b1) g)), v = fl(fl(b2 v) + fl(fl(1 - b2)
+    fl(g g))) and c_avg = fl(fl(b_c c_avg) + fl(fl(1 - b_c) c)): each 1 - b
+    formed from the binary32 b (exact for these b), the square before the
+    product. Exact rationals on seeded values; the sample also separates the
+    sequence from the square taken last and from 1 - b of the binary64 b."""
+    rng = np.random.default_rng(30)
+    n = 400
+    m = (rng.standard_normal(n) * 1e-2).astype(F32)
+    v = (np.abs(rng.standard_normal(n)) * 1e-4).astype(F32)
+    v[::2] = 0  # fresh variance: the new term alone, so its rounding shows
+    g = (rng.standard_normal(n) * 1e-2).astype(F32)
+    b1, b2, bc = F32(0.9), F32(0.999), F32(0.9)
+    fr = lambda t: Fraction(float(t))  # noqa: E731
+    o1, o2, oc = fr(F32(1) - b1), fr(F32(1) - b2), fr(F32(1) - bc)
+    want_m = [rn(fr(rn(fr(b1) * fr(mi))) + fr(rn(o1 * fr(gi)))) for mi, gi in zip(m, g)]
+    want_v = [rn(fr(rn(fr(b2) * fr(vi))) + fr(rn(o2 * fr(rn(fr(gi) * fr(gi))))))
+              for vi, gi in zip(v, g)]
+    m_new, v_new = W.moments(m, v, g, 0.9, 0.999)  # the caller's binary64 betas
+    assert np.array_equal(m_new, np.array(want_m, dtype=F32))
+    assert np.array_equal(v_new, np.array(want_v, dtype=F32))
+    square_last = [rn(fr(rn(fr(b2) * fr(vi))) + fr(rn(fr(rn(o2 * fr(gi))) * fr(gi))))
+                   for vi, gi in zip(v, g)]
+    assert want_v != square_last
+    c_avg = (rng.uniform(0.5, 3, n)).astype(F32)
+    c = (rng.uniform(0.5, 3, n)).astype(F32)
+    want_c = [rn(fr(rn(fr(bc) * fr(ai))) + fr(rn(oc * fr(ci)))) for ai, ci in zip(c_avg, c)]
+    assert np.array_equal(W.coefficient_average(c_avg, c, 0.9), np.array(want_c, dtype=F32))
+    # 1 - b_c taken from the binary64 0.9 (0.09999999999999998), not from
+    # binary32 b_c (1 - fl32(0.9) = 0.10000002384..., exact)
+    unrounded = [rn(fr(rn(fr(bc) * fr(ai))) + fr(rn(Fraction(1.0 - 0.9) * fr(ci))))
+                 for ai, ci in zip(c_avg, c)]
+    assert want_c != unrounded
