@@ -603,6 +603,8 @@ _CPP_PINS = [
      "decompress", R.decompress),
     ("tests.test_oracle_warmup", "test_lamb_step_takes_this_steps_coefficient_not_the_average", W,
      "lamb_warmup_step", R.lamb_warmup_step),
+    ("tests.test_oracle_exact", "test_mean_abs_is_rounded_once_from_the_exact_value", None,
+     "mean_abs_f32", R.mean_abs_f32),
 ]
 
 

@@ -114,3 +114,22 @@ def test_mean_abs_specials():
     assert mean_abs_f32(z) == 0.0 and not np.signbit(mean_abs_f32(z))
     big = np.full(64, np.finfo(np.float32).max, dtype=np.float32)
     assert mean_abs_f32(big) == np.finfo(np.float32).max
+
+
+def test_mean_abs_is_rounded_once_from_the_exact_value():
+    """The mean must not pass through binary64. |x| = 3, 3 2^-24 and 2^-100:
+    the exact mean 1 + 2^-24 + 2^-100 / 3 lies just above the midpoint
+    between 1 and 1 + 2^-23 and rounds up; a binary64 sum drops the 2^-100,
+    its quotient is the midpoint itself, and the tie goes to the even 1.
+    Mirrored: |y| = 3, 9 2^-24 - 2^-44 and 2^-44 - 2^-68 (binary32 values)
+    sum to 3 (1 + 3 2^-24) - 2^-68, whose mean lies just below the midpoint
+    between 1 + 2^-23 (odd) and 1 + 2^-22 and rounds down; through binary64
+    it ties up."""
+    F = np.float32
+    x = np.array([3.0, -3.0 * 2.0 ** -24, 2.0 ** -100], dtype=F)
+    assert mean_abs_f32(x) == F(1 + 2.0 ** -23)
+    y = np.array([3.0, np.nextafter(F(9 * 2.0 ** -24), F(0)),
+                  -np.nextafter(F(2.0 ** -44), F(0))], dtype=F)
+    assert Fraction(float(y[1])) == Fraction(9, 2 ** 24) - Fraction(1, 2 ** 44)
+    assert -Fraction(float(y[2])) == Fraction(1, 2 ** 44) - Fraction(1, 2 ** 68)
+    assert mean_abs_f32(y) == F(1 + 2.0 ** -23)

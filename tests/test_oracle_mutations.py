@@ -15,6 +15,7 @@ built once for this module.
 import contextlib
 import importlib
 import inspect
+import math
 from unittest import mock
 
 import numpy as np
@@ -644,6 +645,15 @@ def server_error_before_the_divide(bits_c, s_c, E_c, reset=False, unit_scale=Fal
             "E": O.error_from(g2, S)}
 
 
+def mean_through_binary64_sum(x):
+    a = np.abs(np.asarray(x, dtype=F32)).astype(np.float64)
+    return F32(math.fsum(a.tolist()) / a.size)
+
+
+def mean_by_numpy_pairwise(x):
+    return F32(np.mean(np.abs(np.asarray(x, dtype=F32)).astype(np.float64)))
+
+
 CASES = [
     # (id, module, attribute, replacement, pin modules)
     ("sign(0) = -1", B, "sign_bit", sign_gt, ["tests.test_oracle_bits", "tests.test_oracle_onebit"]),
@@ -762,6 +772,10 @@ CASES = [
      average_with_binary64_one_minus_beta, ["tests.test_oracle_warmup"]),
     ("server adds its error before dividing by n", O, "server_chunk", server_error_before_the_divide,
      ["tests.test_oracle_onebit"]),
+    ("chunk mean through a binary64 sum", X, "mean_abs_f32", mean_through_binary64_sum,
+     ["tests.test_oracle_exact"], True),
+    ("chunk mean by numpy's pairwise sum", X, "mean_abs_f32", mean_by_numpy_pairwise,
+     ["tests.test_oracle_exact"], True),
 ]
 
 
