@@ -150,6 +150,34 @@ def test_exact_tie_takes_exact_path():
     same_bits(host(grp.sv_bits), sv["bits"], "tie server bits")
 
 
+
+def test_mean_within_binary64_error_of_a_midpoint():
+    """Chunk means a hair above and a hair below a binary32 midpoint, closer
+    than binary64 can tell: the fp64 partial sums land on the midpoint
+    itself, the certified rounding must find the decision ambiguous and the
+    exact path must round the true value (up, and down)."""
+    dev = device()
+    n, L = 2, 2048
+    N = n * L
+    F = np.float32
+    m_h = np.zeros((n, N), dtype=F)
+    m_h[:, L:] = F(0.5)
+    # worker 0, chunk 0: (2^11 + 2^-13 + 2^-100) / 2^11 = 1 + 2^-24 + 2^-111 -> up
+    m_h[0, :3] = [2.0 ** 11, 2.0 ** -13, -(2.0 ** -100)]
+    # worker 1, chunk 0: (2^11 + 3 2^-13 - 2^-59) / 2^11 = 1 + 3 2^-24 - 2^-70 -> down
+    m_h[1, :3] = [-(2.0 ** 11), np.nextafter(F(3 * 2.0 ** -13), F(0)),
+                  np.nextafter(F(2.0 ** -35), F(0))]
+    print("[mean near midpoint] n=2 L=2048", flush=True)
+    grp = OneBitGroup(N, n, dev)
+    m = torch.from_numpy(m_h).to(dev)
+    grp.compress(m, 1, first=True)
+    torch.cuda.synchronize()
+    s = host(grp.scales)
+    assert s[0, 0] == F(1 + 2.0 ** -23) and s[1, 0] == F(1 + 2.0 ** -23)
+    w = O.worker_compress(m_h, np.zeros_like(m_h), reset=True)
+    same_f32(s, w["s"], "scales")
+
+
 def test_zero_size_is_a_noop():
     dev = device()
     t = torch.zeros(16, device=dev)
