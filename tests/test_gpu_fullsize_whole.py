@@ -44,9 +44,9 @@ from workloads import configs as C
 from workloads import synth as S
 
 # ONEBIT_WHOLE_CONFIG_STEPS=1 runs the 335M x 8 (momentum and gradient
-# forms) and 302-tensor x 16 tests over their workloads' own step counts (20
-# each, about 13 minutes together); by default they run 3, 2 and 2 steps,
-# which keeps the suite to minutes.
+# forms) and the two 302-tensor x 16 tests (plain and step-ratio error) over
+# their workloads' own step counts (20 each, about 19 minutes together); by
+# default they run 3, 2, 2 and 3 steps, which keeps the suite to minutes.
 CONFIG_STEPS = os.environ.get("ONEBIT_WHOLE_CONFIG_STEPS") == "1"
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(1500 if CONFIG_STEPS else 600)]
 F32 = np.float32
@@ -358,7 +358,8 @@ def test_bert_large_lamb_302t_x16_step_ratio_whole_buffer():
     """The step-ratio-scaled error feedback of the 1-bit LAMB page (analysis
     paragraph) chained at full size: each step's LAMB pass writes c_{t-1}/c_t
     per layer, and the next step's compression and server multiply their
-    carried errors by it. 302 tensors x 16 workers over three steps, with a
+    carried errors by it. 302 tensors x 16 workers over three steps (the
+    workload's 20 with ONEBIT_WHOLE_CONFIG_STEPS=1), with a
     wide clip of the ratio so that the coefficients move; every worker row,
     the server, the decompressed momentum, the parameters and the layer
     factors on the whole buffer."""
@@ -388,7 +389,7 @@ def test_bert_large_lamb_302t_x16_step_ratio_whole_buffer():
     e_ref = np.zeros((n, N), dtype=F32)
     E_ref = np.zeros(N, dtype=F32)
     hp = (wl.lr, wl.eps, wl.beta1, wl.beta2, 0.5, 0.1, 10.0)  # thr, r_min, r_max: c moves
-    for t in (1, 2, 3):
+    for t in _steps(wl, 3):
         S.momentum(wl, t, dev, sigma_elem=sig, out=m)
         first = t == 1
         grp.compress(m, t, first=first)
