@@ -818,6 +818,29 @@ def measure_probe_int8(steps: int, warmup: int) -> dict:
             "warmup": warmup, "rows": rows}
 
 
+def step_log_lines(step_ms: dict, t_first: int, elems: int, bytes_: dict) -> list:
+    """One record per timed step from the per-call event times already taken
+    (``step_ms[k][i]``: call k of the i-th timed step, in ms): each call's time
+    and algorithmic rate, the step's sum of calls and its worker elements/s.
+    Pure host arithmetic; nothing here touches the GPU."""
+    keys = list(step_ms)
+    count = min(len(v) for v in step_ms.values()) if keys else 0
+    lines = []
+    for i in range(count):
+        rec = {"step": t_first + i}
+        total = 0.0
+        for k in keys:
+            ms = step_ms[k][i]
+            total += ms
+            gbs = bytes_[k] / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+            rec[k] = {"ms": round(ms, 4), "algorithmic_GBps": round(gbs, 1),
+                      "frac_of_8TBps": round(gbs / PEAK_HBM_GBS, 4)}
+        rec["calls_ms"] = round(total, 4)
+        rec["worker_elements_per_s"] = elems / (total * 1e-3) if total > 0 else 0.0
+        lines.append(rec)
+    return lines
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -827,6 +850,9 @@ def main() -> int:
     ap.add_argument("--only", default="", choices=["", "compress", "server", "decompress_adam",
                                                    "decompress", "adam", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--log", default="",
+                    help="also write one JSON line per timed step (each call's time and rate, "
+                         "from the same events) and a closing line with the diagnostics")
     ap.add_argument("--sweep", action="store_true",
                     help="time the step over buffer sizes from 2^20 to the workload's N "
                          "(profiling aid; prints its own JSON line)")
@@ -968,6 +994,13 @@ def main() -> int:
     # step (worker 0 and the server), outside every timed region
     diagnostics = {"worker0_error_rel": _rel(grp.worker_error()[0], grp.ef[0]),
                    "server_error_rel": _rel(grp.server_error(), grp.sv_ef)}
+    if args.log:
+        per_step = {k: [a.elapsed_time(b) for a, b in v_] for k, v_ in ev.items()}
+        with open(args.log, "w") as f:
+            for rec in step_log_lines(per_step, args.warmup + 1, n * N, bytes_):
+                f.write(json.dumps({"workload": wl.name, **rec}) + "\n")
+            f.write(json.dumps({"workload": wl.name, "after_step": args.warmup + args.steps,
+                                "diagnostics": diagnostics}) + "\n")
 
     comp_gbs = bytes_["compress"] / (ms["compress"] * 1e-3) / 1e9
     traffic = read_traffic(wl.name, n * N)

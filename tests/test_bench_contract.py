@@ -61,3 +61,17 @@ def test_cpu_baseline_record():
     mt = rec["multithreaded"]
     assert mt["value"] > 0 and mt["cores"] >= 1 and mt["unit"] == "elements/s"
     assert isinstance(rec["cpu_model"], str)
+
+
+def test_step_log_lines():
+    """The per-step log: one record per timed step with each call's time and
+    rate and the step's worker elements/s, numbered from the first timed step."""
+    ms = {"compress": [2.0, 4.0], "server": [1.0, 1.0]}
+    bytes_ = {"compress": 8e9, "server": 2e9}
+    lines = bench.step_log_lines(ms, 6, 10 ** 9, bytes_)
+    assert [r["step"] for r in lines] == [6, 7]
+    assert lines[0]["compress"]["algorithmic_GBps"] == 4000.0
+    assert lines[0]["compress"]["frac_of_8TBps"] == 0.5
+    assert lines[1]["calls_ms"] == 5.0
+    assert lines[1]["worker_elements_per_s"] == 10 ** 9 / 5e-3
+    assert bench.step_log_lines({}, 1, 1, {}) == []
