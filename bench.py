@@ -868,6 +868,10 @@ def main() -> int:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the n workers are simulated as a batch on one device)", file=sys.stderr)
         return 2
+    if args.steps < 1 or args.warmup < 0:
+        print(f"bench.py needs --steps >= 1 and --warmup >= 0 (got {args.steps}, {args.warmup})",
+              file=sys.stderr)
+        return 2
 
     import torch
 

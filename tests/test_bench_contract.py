@@ -75,3 +75,11 @@ def test_step_log_lines():
     assert lines[1]["calls_ms"] == 5.0
     assert lines[1]["worker_elements_per_s"] == 10 ** 9 / 5e-3
     assert bench.step_log_lines({}, 1, 1, {}) == []
+
+
+@pytest.mark.parametrize("flags", [["--steps", "0"], ["--warmup", "-1"]])
+def test_invalid_step_counts_are_refused(flags):
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *flags],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2 and "--steps >= 1" in res.stderr
+    assert res.stdout.strip() == ""
