@@ -622,3 +622,50 @@ def test_cpp_oracle_passes_the_rounding_and_edge_pins(pin):
     target = tm if module is None else module
     with mock.patch.object(target, attr, cpp_fn):
         getattr(tm, test_name)()
+
+
+def test_cpp_oracle_passes_every_applicable_pin():
+    """Every pin of the numpy oracle's modules, run with every function the
+    C++ oracle offers put in place of its numpy counterpart at once (also
+    where a pin module imported it by name). A pin that reads an output the
+    C++ binding leaves out (the LAMB warm-up's update direction u) does not
+    apply; every other pin must pass."""
+    import contextlib
+    import importlib
+    from unittest import mock
+
+    from oracle import exact as X
+    from tests.test_oracle_mutations import _pin_calls
+    from tests.test_oracle_philox import build_rocrand_dump
+
+    subs = [(O, "worker_compress", R.worker_compress), (O, "server_reduce", R.server_reduce),
+            (O, "decompress", R.decompress), (O, "local_momentum", R.local_momentum),
+            (P, "adam_frozen_step", R.adam_frozen_step),
+            (P, "lamb_frozen_step", R.lamb_frozen_step), (I, "int8_sr", R.int8_sr),
+            (PH, "philox4x32_10", R.philox4x32_10), (PH, "uniforms", R.uniforms),
+            (W, "momentum_scale", R.momentum_scale), (W, "exact_sumsq", R.exact_sumsq),
+            (W, "lamb_warmup_step", R.lamb_warmup_step),
+            (W, "adam_warmup_step", R.adam_warmup_step), (X, "mean_abs_f32", R.mean_abs_f32)]
+    names = ["tests.test_oracle_bits", "tests.test_oracle_exact", "tests.test_oracle_onebit",
+             "tests.test_oracle_optim", "tests.test_oracle_int8", "tests.test_oracle_philox",
+             "tests.test_oracle_warmup"]
+    mods = [importlib.import_module(m) for m in names]
+    run = build_rocrand_dump()
+    fixtures = {} if run is None else {"rocrand_dump": run}
+    passed, not_applicable = 0, []
+    with contextlib.ExitStack() as stack:
+        for mod, attr, fn in subs:
+            orig = getattr(mod, attr)
+            stack.enter_context(mock.patch.object(mod, attr, fn))
+            for tm in mods:
+                if getattr(tm, attr, None) is orig:
+                    stack.enter_context(mock.patch.object(tm, attr, fn))
+        for m in names:
+            for name, fn, kw in _pin_calls(m, fixtures):
+                try:
+                    fn(**kw)
+                    passed += 1
+                except KeyError as e:  # an output the C++ binding does not return
+                    not_applicable.append((name, str(e)))
+    assert passed >= 80
+    assert all(key == "'u'" for _, key in not_applicable), not_applicable
