@@ -14,6 +14,8 @@ roundings, with and without error feedback, random 64-bit seeds and steps;
 two steps, every code, scale, dequantised value and residual.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -25,6 +27,12 @@ from tests._gpu import device, gen, host, same_whole
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(300)]
 F32 = np.float32
+
+
+def _seeds(default: int) -> range:
+    """The seeds of this family: `default` of them, or more when
+    ONEBIT_RANDOM_SEEDS asks for a wider campaign."""
+    return range(max(default, int(os.environ.get("ONEBIT_RANDOM_SEEDS", "0"))))
 
 
 def _lamb_config(seed):
@@ -41,7 +49,7 @@ def _lamb_config(seed):
                 scale=float(10.0 ** rng.uniform(-5, -2)))
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", _seeds(16))
 def test_random_lamb(seed):
     cfg = _lamb_config(seed)
     n, N, off = cfg["n"], cfg["N"], cfg["off"]
@@ -108,7 +116,7 @@ def _int8_config(seed):
                 seed=int(rng.integers(0, 2**63)), step=int(rng.integers(0, 2**32)))
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", _seeds(24))
 def test_random_int8(seed):
     cfg = _int8_config(seed)
     N, block = cfg["N"], cfg["block"]

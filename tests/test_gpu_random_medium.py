@@ -6,6 +6,8 @@ the step-ratio error at both levels, clamp, periodic reset and the unscaled
 sign, with the decompression inside the Adam pass. Three free-running steps
 each; every worker and server output and every parameter bit-identical."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -16,6 +18,12 @@ from tests._gpu import device, gen, host, same_whole
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(300)]
 F32 = np.float32
+
+
+def _seeds(default: int) -> range:
+    """The seeds of this family: `default` of them, or more when
+    ONEBIT_RANDOM_SEEDS asks for a wider campaign."""
+    return range(max(default, int(os.environ.get("ONEBIT_RANDOM_SEEDS", "0"))))
 
 
 def _config(seed):
@@ -40,7 +48,7 @@ def _config(seed):
                 scale=float(10.0 ** rng.uniform(-5, -1)))
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", _seeds(24))
 def test_random_medium(seed):
     cfg = _config(seed)
     n, N, off = cfg["n"], cfg["N"], cfg["off"]

@@ -5,6 +5,8 @@
 unscaled sign, the layer coefficient, and the decompression inside the Adam
 pass.  Three free-running steps each, against the oracle."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -16,6 +18,12 @@ from tests._gpu import device, gen, host, same_bits, same_f32
 
 pytestmark = pytest.mark.gpu
 F32 = np.float32
+
+
+def _seeds(default: int) -> range:
+    """The seeds of this family: `default` of them, or more when
+    ONEBIT_RANDOM_SEEDS asks for a wider campaign."""
+    return range(max(default, int(os.environ.get("ONEBIT_RANDOM_SEEDS", "0"))))
 
 
 def _config(seed):
@@ -35,7 +43,7 @@ def _config(seed):
                 scale=float(10.0 ** rng.uniform(-5, -1)))
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", _seeds(16))
 def test_random_shape(seed):
     cfg = _config(seed)
     n, N, off = cfg["n"], cfg["N"], cfg["off"]
