@@ -244,6 +244,11 @@ class LambState:
 
     def step(self, mbar: torch.Tensor, lr: float, eps: float, beta1: float, beta2: float,
              thr: float, r_min: float, r_max: float, use_c_t: bool = False, stream=None) -> None:
+        """LAMB step on the decompressed global momentum ``mbar`` (m_t) with
+        ``m_prev`` as m_{t-1}.  ``m_prev`` is the caller's: before the next
+        step put m_t into it (``st.m_prev.copy_(mbar)``), since the server
+        rewrites its own ``mbar`` on the next step; ``step_packed`` keeps it
+        by itself."""
         S = self.seg_off.numel() - 1
         ob.frozen_v_step(mode=1, N=self.x.numel(), x=self.x, m=mbar, v=self.v_frozen, lr=lr,
                          eps=eps, beta1=beta1, beta2=beta2, m_prev=self.m_prev,
