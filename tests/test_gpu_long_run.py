@@ -1,0 +1,129 @@
+"""A long free-running 1-bit Adam run against the C++ oracle: 3000 steps
+with the clamp on and the periodic error reset every 1000 steps (1-bit Adam
+article, sections 2.1 and 4.1), so that the carried worker and server
+errors accumulate over a thousand compressions between resets. Every
+step's sign words, scales, compensated values and parameters are compared
+bit for bit, so a drift at any step is caught where it starts."""
+
+import numpy as np
+import pytest
+import torch
+
+from momentum_compression_amd.state import OneBitGroup
+from oracle import cref as R
+from tests._gpu import device, gen, host
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
+F32 = np.float32
+
+
+def _eq(got, want, what):
+    g, w = np.ascontiguousarray(got), np.ascontiguousarray(want)
+    assert g.shape == w.shape and np.array_equal(g.view(np.uint32), w.view(np.uint32)), what
+
+
+def test_three_thousand_steps_with_resets():
+    dev = device()
+    n, L = 8, 3 * 1024 + 64
+    N, steps, R_int, clip, lr, eps = n * L, 3000, 1000, 2e-3, 6e-5, 1e-6
+    print(f"[long run] n={n} N={N} steps={steps} reset every {R_int}", flush=True)
+    grp = OneBitGroup(N, n, dev, clip=clip, reset_interval=R_int)
+    g0 = gen(4242, dev)
+    x = torch.randn(N, generator=g0, device=dev) * 0.02
+    v = torch.rand(N, generator=g0, device=dev) * 1e-6 + 1e-8
+    x_h, v_h = host(x).copy(), host(v)
+    e = np.zeros((n, N), dtype=F32)
+    E = np.zeros(N, dtype=F32)
+    m = torch.empty((n, N), device=dev)
+    for t in range(1, steps + 1):
+        # momenta of a slowly moving scale, so the errors carry real content
+        m.normal_(0.0, 1e-3 * (1.0 + 0.5 * np.sin(t / 97.0)), generator=g0)
+        first = t == 1
+        reset = first or grp.is_reset(t)
+        grp.compress(m, t, first=first)
+        grp.server(t, first=first, decompress=False)
+        grp.adam_step_packed(x, v, lr, eps, decompress=True)
+        torch.cuda.synchronize()
+        w = R.worker_compress(host(m), e, clip=clip, reset=reset)
+        sv = R.server_reduce(w["bits"], w["s"], E, reset=reset)
+        mbar = R.decompress(sv["bits"], sv["S"])
+        x_h = R.adam_frozen_step(x_h, mbar, v_h, lr, eps)
+        tag = f"t={t}{' (reset)' if reset else ''}"
+        _eq(host(grp.bits), w["bits"], f"{tag} worker sign words")
+        _eq(host(grp.scales), w["s"], f"{tag} worker scales")
+        _eq(host(grp.ef), w["gc"], f"{tag} worker compensated values")
+        _eq(host(grp.sv_bits), sv["bits"], f"{tag} server sign words")
+        _eq(host(grp.sv_scales), sv["S"], f"{tag} server scales")
+        _eq(host(grp.sv_ef), sv["g2"], f"{tag} server compensated values")
+        _eq(host(grp.mbar), mbar, f"{tag} decompressed momentum")
+        _eq(host(x), x_h, f"{tag} parameters")
+        e, E = w["e"], sv["E"]
+        if t % 500 == 0:
+            print(f"[long run] t={t} ok", flush=True)
+    # the errors stayed bounded by the clamp's range between resets
+    assert np.all(np.abs(e) <= 2 * clip) and np.all(np.isfinite(E))
+
+
+def test_lamb_thousand_steps_step_ratio_chained():
+    """1-bit LAMB on the BERT-Large layer structure scaled down (every
+    tensor kept, 303 layers), 8 workers, 1000 steps: the step ratio
+    c_{t-1}/c_t written by each step's LAMB pass scales the next step's
+    carried errors at both levels (1-bit LAMB page, analysis paragraph), the
+    clipped ratio r_t moves every step, and m_{t-1} is the previous step's
+    decompressed momentum. Every step bit for bit against the C++ oracle."""
+    from momentum_compression_amd.state import LambState, momentum_scale
+    from workloads import configs as C
+    from workloads import synth as S
+
+    dev = device()
+    wl = C.scaled_lamb(n=8, target_elems=1 << 16, seed=11)
+    N, n = wl.N, wl.n
+    steps = 1000
+    off = np.array(C.segment_offsets(wl.segments), dtype=np.int64)
+    print(f"[long lamb] N={N} n={n} layers={len(off) - 1} steps={steps}", flush=True)
+    off_d = torch.from_numpy(off).to(dev)
+    sig = S.per_element(S.segment_sigmas(wl), wl, dev)
+    m_tw = S.lamb_prev_momentum(wl, dev, sig)
+    k_d = momentum_scale(m_tw, off_d)
+    k_el = np.repeat(host(k_d), np.diff(off)).astype(F32)
+    c_avg = S.lamb_c_avg(wl)
+    st = LambState.create(S.params(wl, dev), S.frozen_variance(wl, dev), m_tw, off_d,
+                          torch.from_numpy(c_avg).to(dev))
+    grp = OneBitGroup(N, n, dev, seg_off=off_d, seg_k=k_d, seg_err_ratio=st.err_ratio)
+    hp = (wl.lr, wl.eps, wl.beta1, wl.beta2, 0.5, 0.1, 10.0)  # a wide clip: c moves
+    x_h, vf_h, mp_h = host(st.x).copy(), host(st.v_fresh).copy(), host(st.m_prev).copy()
+    r_h, c_h, v_tw = host(st.r).copy(), host(st.c).copy(), host(st.v_frozen)
+    rho = np.ones(len(off) - 1, dtype=F32)
+    e = np.zeros((n, N), dtype=F32)
+    E = np.zeros(N, dtype=F32)
+    m = torch.empty((n, N), device=dev)
+    g0 = gen(77, dev)
+    for t in range(1, steps + 1):
+        m.normal_(0.0, 1.0, generator=g0)
+        m.mul_(sig)
+        first = t == 1
+        grp.compress(m, t, first=first)
+        grp.server(t, first=first, decompress=False)
+        st.step_packed(grp.sv_bits, grp.sv_scales, k_d, n, *hp)
+        torch.cuda.synchronize()
+        rho_el = np.repeat(rho, np.diff(off)).astype(F32)
+        w = R.worker_compress(host(m), e, reset=first, k=k_el, err_ratio=None if first else rho_el)
+        sv = R.server_reduce(w["bits"], w["s"], E, reset=first,
+                             err_ratio=None if first else rho_el)
+        mbar = R.decompress(sv["bits"], sv["S"], k_el)
+        out = R.lamb_frozen_step(x_h, mbar, mp_h, vf_h, v_tw, off, c_avg, r_h, c_h, *hp)
+        tag = f"t={t}"
+        _eq(host(grp.bits), w["bits"], f"{tag} worker sign words")
+        _eq(host(grp.scales), w["s"], f"{tag} worker scales")
+        _eq(host(grp.sv_bits), sv["bits"], f"{tag} server sign words")
+        _eq(host(grp.sv_scales), sv["S"], f"{tag} server scales")
+        _eq(host(st.m_prev), mbar, f"{tag} decompressed momentum / k")
+        _eq(host(st.x), out["x"], f"{tag} parameters")
+        _eq(host(st.v_fresh), out["v"], f"{tag} fresh variance")
+        _eq(host(st.r), out["r"], f"{tag} r_t")
+        _eq(host(st.c), out["c"], f"{tag} c_t")
+        _eq(host(st.err_ratio), out["err_ratio"], f"{tag} step ratio")
+        x_h, vf_h, r_h, c_h, mp_h = out["x"], out["v"], out["r"], out["c"], mbar
+        e, E, rho = w["e"], sv["E"], out["err_ratio"]
+        if t % 250 == 0:
+            print(f"[long lamb] t={t} ok", flush=True)
