@@ -127,3 +127,39 @@ def test_lamb_thousand_steps_step_ratio_chained():
         e, E, rho = w["e"], sv["E"], out["err_ratio"]
         if t % 250 == 0:
             print(f"[long lamb] t={t} ok", flush=True)
+
+
+def test_int8_two_thousand_steps_error_feedback():
+    """Block-wise INT8 stochastic rounding with error feedback over 2000
+    steps (gradient-quantisation tutorial, "FP32 -> INT8" and the error
+    feedback of its 1-bit section): the residual of every step is added to
+    the next gradient, and each step draws fresh Philox uniforms keyed by
+    the step. Codes, scales, dequantised values and residuals bit for bit
+    against the C++ oracle at every step."""
+    from momentum_compression_amd import onebit as ob
+
+    dev = device()
+    N, block, steps, seed = 256 * 997, 256, 2000, 0x5EED_0F_1B17
+    print(f"[long int8] N={N} block={block} steps={steps}", flush=True)
+    err = torch.zeros(N, device=dev)
+    codes = torch.empty(N, dtype=torch.int8, device=dev)
+    scales = torch.empty(N // block, device=dev)
+    deq = torch.empty(N, device=dev)
+    g = torch.empty(N, device=dev)
+    g0 = gen(91, dev)
+    e_h = np.zeros(N, dtype=F32)
+    for t in range(1, steps + 1):
+        g.normal_(0.0, 1e-3, generator=g0)
+        ob.int8_sr_quantize(g, err, codes, scales, deq, N, block, seed, t)
+        torch.cuda.synchronize()
+        o = R.int8_sr(host(g), e_h, seed, t, block=block)
+        tag = f"t={t}"
+        assert np.array_equal(host(codes), o["codes"]), f"{tag} codes"
+        _eq(host(scales), o["scales"], f"{tag} scales")
+        _eq(host(deq), o["deq"], f"{tag} dequantised")
+        _eq(host(err), o["e"], f"{tag} residual")
+        e_h = o["e"]
+        if t % 500 == 0:
+            print(f"[long int8] t={t} ok", flush=True)
+    # the residual stays below one quantisation step of its block
+    assert np.all(np.abs(e_h) <= np.repeat(host(scales), block) * (1 + 2.0 ** -20))
