@@ -163,3 +163,47 @@ def test_int8_two_thousand_steps_error_feedback():
             print(f"[long int8] t={t} ok", flush=True)
     # the residual stays below one quantisation step of its block
     assert np.all(np.abs(e_h) <= np.repeat(host(scales), block) * (1 + 2.0 ** -20))
+
+
+def test_lamb_warmup_five_hundred_steps():
+    """500 uncompressed LAMB warmup steps on the scaled 303-layer BERT
+    structure (1-bit LAMB page, algorithm paragraph: warmup before the
+    compressed phase), the coefficient average carried from step to step,
+    then the per-layer momentum scale k_l at the end (layer-scaling
+    paragraph). Every step's x, m, v, c and c_avg, and k_l, bit for bit
+    against the C++ oracle."""
+    from momentum_compression_amd import onebit as ob
+    from momentum_compression_amd.state import LambWarmup
+    from workloads import configs as C
+    from workloads import synth as S
+
+    dev = device()
+    wl = C.scaled_lamb(n=8, target_elems=1 << 16, seed=12)
+    N = wl.N
+    steps = 500
+    off = np.array(C.segment_offsets(wl.segments), dtype=np.int64)
+    print(f"[long warmup] N={N} layers={len(off) - 1} steps={steps}", flush=True)
+    off_d = torch.from_numpy(off).to(dev)
+    sig = S.per_element(S.segment_sigmas(wl), wl, dev)
+    hp = dict(lr=1e-3, eps=1e-6, beta1=0.9, beta2=0.999)
+    x0 = S.params(wl, dev)
+    st = LambWarmup.create(x0.clone(), off_d)
+    xh, mh, vh, cav = host(x0).copy(), np.zeros(N, F32), np.zeros(N, F32), None
+    g = torch.empty(N, device=dev)
+    g0 = gen(13, dev)
+    for t in range(1, steps + 1):
+        g.normal_(0.0, 1.0, generator=g0)
+        g.mul_(sig)
+        st.step(g, beta_c=0.9, **hp)
+        torch.cuda.synchronize()
+        o = R.lamb_warmup_step(xh, mh, vh, host(g), off, c_avg=cav, beta_c=0.9, **hp)
+        for name in ("x", "m", "v", "c", "c_avg"):
+            _eq(host(getattr(st, name)), o[name], f"t={t} {name}")
+        xh, mh, vh, cav = o["x"], o["m"], o["v"], o["c_avg"]
+        if t % 100 == 0:
+            print(f"[long warmup] t={t} ok", flush=True)
+    k = torch.empty(len(off) - 1, device=dev)
+    ws = torch.empty(ob.warmup_workspace_bytes(N, len(off) - 1), dtype=torch.uint8, device=dev)
+    ob.lamb_momentum_scale(st.m, N, off_d, len(off) - 1, k, ws)
+    torch.cuda.synchronize()
+    _eq(host(k), R.momentum_scale(mh, off), "k_l")
