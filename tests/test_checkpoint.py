@@ -3,7 +3,6 @@ manifest, and refusal of damaged or escaping entries; the group and LAMB
 state round trip through ``from_state`` (host tensors, no kernel runs)."""
 
 import json
-import os
 
 import numpy as np
 import pytest
