@@ -77,6 +77,13 @@ size_t partial_bytes(int64_t N, int32_t n) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ONEBIT_OK : ONEBIT_E_HIP; }
 
+// The launch helpers return hipGetLastError after their launches, which
+// reports the last error of any HIP call on this thread.  An entry point
+// therefore drops an error an earlier call left behind (a caller's stream
+// or event query that returned hipErrorNotReady, say) before its first
+// launch, so that its status reflects only its own launches.
+void drop_stale_error() { (void)hipGetLastError(); }
+
 // Scratch of onebit_server_reduce_noalloc: the fp64 partial sums of the
 // server's chunk means (one per workgroup), in a file-scope device array.
 // Every device the library runs on holds its own copy until the process
@@ -167,6 +174,7 @@ int onebit_compress_ex(const float* m, const uint32_t* mb_bits, const float* mb_
     double* partials = static_cast<double*>(ws);
     CompressArgs a{m, ef, scales, bits, partials, N, n, clip, clamp_on, reset != 0,
                    seg_off, seg_k, n_seg, mb_bits, mb_scales, beta1, seg_err_ratio};
+    drop_stale_error();
     hipError_t e = launch_compress(a, plan, stream);
     if (e != hipSuccess) return ONEBIT_E_HIP;
     MeanTarget tgt{ef, N, n, scales, (flags & ONEBIT_UNIT_SCALE) != 0};
@@ -223,6 +231,7 @@ int server_launch(const uint32_t* bits, const float* scales, float* ef, float* s
                   const float* seg_err_ratio, int32_t n_seg, int64_t N, int32_t n,
                   int32_t reset, uint32_t flags, double* partials, hipStream_t stream) {
     const ChunkPlan plan = server_plan(N / n, n);
+    drop_stale_error();
     hipError_t e = launch_server(bits, scales, ef, sv_scales, sv_bits, partials, N, n, plan,
                                  reset != 0, seg_off, seg_err_ratio, n_seg, stream);
     if (e != hipSuccess) return ONEBIT_E_HIP;
@@ -294,6 +303,7 @@ int onebit_decompress(const uint32_t* sv_bits, const float* sv_scales, float* m_
     if (!aligned(sv_bits, 4) || !aligned(sv_scales, 4) || !aligned(m_out, 16)) return ONEBIT_E_ALIGN;
     if (N == 0) return ONEBIT_OK;
     if (!groups_ok(ceil_div(N, (int64_t)kDecompressTiles * kTile))) return ONEBIT_E_SIZE;
+    drop_stale_error();
     return hip_status(
         launch_decompress(sv_bits, sv_scales, m_out, seg_off, seg_k, n_seg, N, n, stream));
 }
@@ -307,6 +317,7 @@ int onebit_error_materialize(const float* ef, const float* scales, float* e_out,
     if (!aligned(ef, 16) || !aligned(e_out, 16) || !aligned(scales, 4)) return ONEBIT_E_ALIGN;
     if (N == 0) return ONEBIT_OK;
     if (!groups_ok(ceil_div(N, kTile))) return ONEBIT_E_SIZE;
+    drop_stale_error();
     return hip_status(launch_materialize(ef, scales, e_out, N, rows, n, stream));
 }
 
@@ -318,6 +329,7 @@ int lamb_layer_scale(float* buf, int64_t N, int32_t batch, const int64_t* seg_of
     if (!aligned(buf, 16) || !aligned(seg_off, 8) || !aligned(seg_k, 4)) return ONEBIT_E_ALIGN;
     if (N == 0) return ONEBIT_OK;
     if (batch > 65535 || !groups_ok(ceil_div(ceil_div(N, kTile), 8))) return ONEBIT_E_SIZE;
+    drop_stale_error();
     return hip_status(launch_layer_scale(buf, N, batch, seg_off, seg_k, n_seg, divide != 0, stream));
 }
 
@@ -331,6 +343,7 @@ int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes, hipS
     if (!aligned(a->x, 16) || !aligned(a->m, 16) || !aligned(a->v, 16)) return ONEBIT_E_ALIGN;
     if (a->mode == 0) {
         if (a->N == 0) return ONEBIT_OK;
+        drop_stale_error();
         return hip_status(launch_adam(a->x, a->m, a->v, a->N, a->lr, a->eps, stream));
     }
     if (a->mode == 2) {
@@ -340,6 +353,7 @@ int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes, hipS
         if (!aligned(a->m_bits, 4) || !aligned(a->m_scales, 4) || !aligned(a->m_out, 16))
             return ONEBIT_E_ALIGN;
         if (a->N == 0) return ONEBIT_OK;
+        drop_stale_error();
         return hip_status(launch_adam_packed(a->x, a->m_bits, a->m_scales, a->v, a->m_out, a->N,
                                              a->m_chunks, a->lr, a->eps, stream));
     }
@@ -376,6 +390,7 @@ int frozen_v_step(const onebit_frozen_v_args* a, void* ws, size_t ws_bytes, hipS
     if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
     uint32_t* keys = static_cast<uint32_t*>(ws);
     uint32_t* wg_max = keys + round_up((size_t)a->n_seg * sizeof(uint32_t)) / sizeof(uint32_t);
+    drop_stale_error();
     return hip_status(launch_lamb(*a, keys, wg_max, stream));
 }
 
@@ -396,6 +411,7 @@ int int8_quantize(const float* g, float* err, int8_t* codes, float* block_scales
         if (!ws || ws_bytes < 256) return ONEBIT_E_WORKSPACE;
         if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
     }
+    drop_stale_error();
     return hip_status(launch_int8(g, err, codes, block_scales, deq, N, block, seed, step,
                                   rounding == 1, static_cast<uint32_t*>(ws), stream));
 }
@@ -427,6 +443,7 @@ int warmup_adam_step(float* x, float* m, float* v, const float* g, int64_t N, fl
     if (!x || !m || !v || !g) return ONEBIT_E_NULL;
     if (!aligned(x, 16) || !aligned(m, 16) || !aligned(v, 16) || !aligned(g, 16))
         return ONEBIT_E_ALIGN;
+    drop_stale_error();
     return hip_status(launch_warmup_adam(x, m, v, g, N, lr, eps, beta1, beta2, stream));
 }
 
@@ -460,6 +477,7 @@ int warmup_lamb_step(float* x, float* m, float* v, const float* g, int64_t N,
     a.c = c;
     a.c_avg = c_avg;
     // N == 0: every layer is empty, c = 1 (the coefficient of a zero norm)
+    drop_stale_error();
     return hip_status(launch_warmup_lamb(a, split_warmup_ws(ws, N, n_seg), stream));
 }
 
@@ -472,6 +490,7 @@ int lamb_momentum_scale(const float* m, int64_t N, const int64_t* seg_off, int32
     if (!aligned(m, 16) || !aligned(seg_off, 8) || !aligned(k, 4)) return ONEBIT_E_ALIGN;
     if (!ws || ws_bytes < warmup_workspace_bytes(N, n_seg)) return ONEBIT_E_WORKSPACE;
     if (!aligned(ws, 256)) return ONEBIT_E_ALIGN;
+    drop_stale_error();
     return hip_status(
         launch_momentum_scale(m, N, seg_off, n_seg, k, split_warmup_ws(ws, N, n_seg), stream));
 }
