@@ -92,9 +92,19 @@ class OnebitError(RuntimeError):
 
 
 def load() -> ctypes.CDLL:
-    """Load libonebit.so (raises if it has not been built)."""
+    """Load libonebit.so (raises if it has not been built).
+
+    torch is imported first.  Its wheel carries its own HIP runtime, whose
+    soname (libamdhip64.so.7) the library's dependency then resolves to, so
+    the process holds one runtime, the one torch's tensors and streams
+    belong to.  Loaded before torch, the library would bind to the system's
+    runtime and torch would then load its own beside it: two runtimes, and
+    the library's calls fail (a runtime that finds the device already taken
+    reports no device)."""
     global _lib
     if _lib is None:
+        import torch  # noqa: F401  (before the library: one HIP runtime)
+
         if not os.path.exists(LIB_PATH):
             raise ImportError(
                 f"{LIB_PATH} is missing: build it with `python -m momentum_compression_amd.build`")

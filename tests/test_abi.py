@@ -320,3 +320,27 @@ def test_binding_refuses_host_short_and_mistyped_tensors(monkeypatch):
     with pytest.raises(ValueError, match="int64"):
         ob.lamb_layer_scale(torch.zeros(N), N, 1, torch.zeros(3, dtype=torch.int32),
                             torch.zeros(2), 2, False)
+
+
+def test_binding_shares_torchs_hip_runtime():
+    """Loading the library through the binding before torch leaves one HIP
+    runtime in the process, torch's (the binding imports torch first): a
+    second runtime beside torch's would report no device to the library's
+    calls.  Checked in a fresh interpreter from the mapped files; nothing
+    is initialised, so no GPU is needed."""
+    import ast
+    import os
+    import subprocess
+    import sys
+
+    code = ("from momentum_compression_amd import onebit as ob\n"
+            "ob.load()\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(sorted({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    runtimes = ast.literal_eval(out.stdout.strip().splitlines()[-1])
+    assert len(runtimes) == 1, runtimes
