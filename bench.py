@@ -510,20 +510,52 @@ def measure_adam_row(name: str, steps: int, warmup: int) -> dict:
     return out
 
 
+# plain stream probes (libonebit_probe.so): mode, name, bytes per float
+BASIC_PROBES = ((0, "read", 4.0), (1, "write", 4.0), (2, "copy", 8.0),
+                (3, "read_two_write_one_in_place", 12.0))
+
+
 def measure_copy(steps: int, warmup: int) -> dict:
-    """A plain device copy of 2^31 floats (torch's copy kernel): the bandwidth
-    a simple read-one-write-one stream reaches, as context for the rows."""
+    """Plain streams over 2^31 floats as context for the rows: torch's device
+    copy, and the probe library's hand-written read, write, copy and
+    read-two-write-one-in-place streams (one float4 per lane, 256-thread
+    workgroups, nontemporal, the library kernels' access shape), the
+    practical HBM ceilings of those mixes on this GPU."""
+    import ctypes
+
     import torch
 
     dev = torch.device("cuda:0")
     src = torch.empty(1 << 31, device=dev)
     src.fill_(1.0)
     dst = torch.empty_like(src)
+    dst.fill_(0.5)
     stream = torch.cuda.current_stream()
+    N = src.numel()
+
+    def rate(ms, nbytes):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"ms": round(ms, 4), "GBps": round(gbs, 1),
+                "frac_of_8TBps": round(gbs / PEAK_HBM_GBS, 4)}
+
     ms = _time_calls([lambda: dst.copy_(src)], warmup, steps, stream)[0]
-    out = {"floats": src.numel(), "ms": round(ms, 4),
-           "GBps": round(8.0 * src.numel() / (ms * 1e-3) / 1e9, 1),
-           "frac_of_8TBps": round(8.0 * src.numel() / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    out = {"floats": N, **rate(ms, 8.0 * N)}
+    lib = _probe_lib()
+    if lib is not None:
+        lib.onebit_probe_basic.restype = ctypes.c_int32
+        lib.onebit_probe_basic.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                           ctypes.c_int32, ctypes.c_void_p]
+
+        def probe(mode):
+            rc = lib.onebit_probe_basic(src.data_ptr(), dst.data_ptr(), N, mode,
+                                        ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"stream probe mode {mode}: status {rc}")
+
+        fns = [lambda mode=mode: probe(mode) for mode, _, _ in BASIC_PROBES]
+        ms_p = _time_calls(fns, warmup, steps, stream)
+        out["stream_probes"] = {name: rate(t, per * N)
+                                for (_, name, per), t in zip(BASIC_PROBES, ms_p)}
     del src, dst
     torch.cuda.empty_cache()
     return out
@@ -641,8 +673,12 @@ PROBE_MODES = [(0, "stream: read m and state, write state"),
 
 
 def _probe_lib():
-    """The probe library (built by build() next to libonebit.so), or None."""
+    """The probe library (built by build() next to libonebit.so), or None.
+    torch is imported first, so that the library binds to torch's HIP
+    runtime (see ``onebit.load``)."""
     import ctypes
+
+    import torch  # noqa: F401
 
     from momentum_compression_amd.build import PROBE_LIB
 

@@ -1,8 +1,8 @@
 // Stream probes shaped like the worker compression, the server and the INT8
-// quantiser, built
-// into a separate library (libonebit_probe.so) that only the benchmark
-// loads: they give the ceiling of each kernel's memory pattern on this GPU,
-// not a step of the method.
+// quantiser, and plain read, write and copy streams, built into a separate
+// library (libonebit_probe.so) that only the benchmark loads: they give the
+// ceiling of each kernel's memory pattern on this GPU, not a step of the
+// method.
 //
 // Same geometry as the compression: n rows of N floats, chunks of L = N / n,
 // grid (workgroups per chunk, n * n), one 1024-element tile per 256-thread
@@ -183,9 +183,56 @@ __global__ __launch_bounds__(256) void int8_probe_kernel(const float* __restrict
     }
 }
 
+// Plain streams over N floats with the library's access shape (one float4
+// per lane, 256-thread workgroups, nontemporal loads and stores): the
+// practical HBM ceilings of reading, writing, copying, and reading two
+// streams while writing one back in place (the compression's mix).
+// MODE 0: read a; 1: write b; 2: b = a; 3: b = a + b.  The read-only form
+// stores one value only if it sees a sentinel no benchmark input holds, so
+// its loads are kept.
+template <int MODE>
+__global__ __launch_bounds__(256) void basic_probe_kernel(const float* __restrict__ a,
+                                                          float* __restrict__ b) {
+    const int64_t j = (int64_t)blockIdx.x * 1024 + 4 * (int64_t)threadIdx.x;
+    if (MODE == 1) {
+        __builtin_nontemporal_store(f4{1.f, 2.f, 3.f, 4.f}, reinterpret_cast<f4*>(b + j));
+        return;
+    }
+    const f4 x = __builtin_nontemporal_load(reinterpret_cast<const f4*>(a + j));
+    if (MODE == 0) {
+        if (x.x == -1234.5f && x.y == 1234.5f) b[j] = x.z;
+        return;
+    }
+    if (MODE == 2) {
+        __builtin_nontemporal_store(x, reinterpret_cast<f4*>(b + j));
+        return;
+    }
+    const f4 y = __builtin_nontemporal_load(reinterpret_cast<const f4*>(b + j));
+    __builtin_nontemporal_store(x + y, reinterpret_cast<f4*>(b + j));
+}
+
 }  // namespace
 
 extern "C" {
+
+// Runs one plain stream probe launch on `stream`: a and b N floats each
+// (device, 16-byte aligned; b is overwritten by modes 1 to 3), mode 0 read
+// a, 1 write b, 2 copy a to b, 3 b = a + b.  N must be a positive multiple
+// of 1024 with N / 4 below 2^32.  Returns 0, -2 for an invalid size or
+// mode, -6 for a HIP launch error.
+int onebit_probe_basic(const float* a, float* b, int64_t N, int32_t mode, hipStream_t stream) {
+    if (N <= 0 || N % 1024 || mode < 0 || mode > 3) return -2;
+    if (N / 4 >= ((int64_t)1 << 32)) return -2;
+    (void)hipGetLastError();  // drop an error an earlier call left behind
+    const dim3 grid((unsigned)(N / 1024));
+    switch (mode) {
+        case 0: hipLaunchKernelGGL(basic_probe_kernel<0>, grid, dim3(256), 0, stream, a, b); break;
+        case 1: hipLaunchKernelGGL(basic_probe_kernel<1>, grid, dim3(256), 0, stream, a, b); break;
+        case 2: hipLaunchKernelGGL(basic_probe_kernel<2>, grid, dim3(256), 0, stream, a, b); break;
+        default: hipLaunchKernelGGL(basic_probe_kernel<3>, grid, dim3(256), 0, stream, a, b); break;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
 
 // Runs one probe launch on `stream`.  a, b: n rows of N floats (device,
 // 16-byte aligned; b is overwritten); bits: n rows of N / 32 words; part:
@@ -198,6 +245,7 @@ int onebit_probe_stream(const float* a, float* b, uint32_t* bits, double* part, 
     const int64_t L = N / n;
     const int64_t bpc = (L + 1023) / 1024;
     if (bpc * 256 >= ((int64_t)1 << 32)) return -2;
+    (void)hipGetLastError();  // drop an error an earlier call left behind
     const dim3 grid((unsigned)bpc, (unsigned)((int64_t)n * n));
     switch (mode) {
         case 0:
@@ -235,6 +283,7 @@ int onebit_probe_server(const uint32_t* bits, float* ef, uint32_t* sv_bits, doub
     const int64_t bpc = (L + 2047) / 2048;
     if (bpc * 256 >= ((int64_t)1 << 32)) return -2;
     const dim3 grid((unsigned)bpc, (unsigned)n);
+    (void)hipGetLastError();  // drop an error an earlier call left behind
     const size_t lds = (size_t)n * 64 * sizeof(uint32_t);
     if (n == 16)
         hipLaunchKernelGGL(server_probe_kernel<16>, grid, dim3(256), lds, stream, bits, ef, sv_bits,
@@ -254,6 +303,7 @@ int onebit_probe_int8(const float* g, float* err, int8_t* codes, float* scales, 
     if (N <= 0 || N % 256) return -2;
     const int64_t wgs = (N + 2047) / 2048;
     if (wgs * 256 >= ((int64_t)1 << 32)) return -2;
+    (void)hipGetLastError();  // drop an error an earlier call left behind
     hipLaunchKernelGGL(int8_probe_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, g, err, codes,
                        scales, deq, N);
     return hipGetLastError() == hipSuccess ? 0 : -6;

@@ -1,5 +1,5 @@
 """Host-side checks of the benchmark's probe library (libonebit_probe.so):
-it is built next to libonebit.so, exports its three probes, and rejects
+it is built next to libonebit.so, exports its four probes, and rejects
 invalid sizes before any HIP call (no GPU needed)."""
 
 import ctypes
@@ -23,6 +23,8 @@ def lib():
     L.onebit_probe_server.argtypes = [P, P, P, P, I64, I32, I64, P]
     L.onebit_probe_int8.restype = I32
     L.onebit_probe_int8.argtypes = [P, P, P, P, P, I64, P]
+    L.onebit_probe_basic.restype = I32
+    L.onebit_probe_basic.argtypes = [P, P, I64, I32, P]
     return L
 
 
@@ -42,10 +44,17 @@ def test_probe_sizes_rejected_before_launch(lib):
     # INT8 probe: N a positive multiple of 256
     assert lib.onebit_probe_int8(None, None, None, None, None, 0, None) == -2
     assert lib.onebit_probe_int8(None, None, None, None, None, 1000, None) == -2
+    # plain streams: N a positive multiple of 1024, N / 4 below 2^32, mode 0..3
+    assert lib.onebit_probe_basic(None, None, 0, 0, None) == -2
+    assert lib.onebit_probe_basic(None, None, 1000, 0, None) == -2
+    assert lib.onebit_probe_basic(None, None, 1 << 34, 0, None) == -2
+    assert lib.onebit_probe_basic(None, None, 4096, 4, None) == -2
+    assert lib.onebit_probe_basic(None, None, 4096, -1, None) == -2
 
 
 def test_probe_library_is_not_the_product_library():
     # the product library exports no probe (the probes are the benchmark's)
     prod = ctypes.CDLL(os.path.join(os.path.dirname(B.PROBE_LIB), "libonebit.so"))
-    for name in ("onebit_probe_stream", "onebit_probe_server", "onebit_probe_int8"):
+    for name in ("onebit_probe_stream", "onebit_probe_server", "onebit_probe_int8",
+                 "onebit_probe_basic"):
         assert not hasattr(prod, name)
