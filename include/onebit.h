@@ -18,7 +18,9 @@
  *   Results do not depend on the stream or on the launch geometry.
  * - Return value: ONEBIT_OK (0) or a negative onebit_status.  Validation
  *   failures leave every buffer untouched.  ONEBIT_E_HIP reports a launch
- *   error from the HIP runtime.
+ *   error from the HIP runtime.  An error that an earlier HIP call left as
+ *   the calling thread's last error is cleared before the first launch, so
+ *   it is neither reported nor kept.
  * - Floating point is IEEE binary32 throughout: round to nearest even, no
  *   fused multiply-add contraction, correctly rounded division and square
  *   root, subnormals kept.  NaN and Inf in the data are not errors; they
