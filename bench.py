@@ -553,9 +553,12 @@ def measure_copy(steps: int, warmup: int) -> dict:
                 raise RuntimeError(f"stream probe mode {mode}: status {rc}")
 
         fns = [lambda mode=mode: probe(mode) for mode, _, _ in BASIC_PROBES]
-        ms_p = _time_calls(fns, warmup, steps, stream)
-        out["stream_probes"] = {name: rate(t, per * N)
-                                for (_, name, per), t in zip(BASIC_PROBES, ms_p)}
+        try:  # context only: a probe failure never fails the bench line
+            ms_p = _time_calls(fns, warmup, steps, stream)
+            out["stream_probes"] = {name: rate(t, per * N)
+                                    for (_, name, per), t in zip(BASIC_PROBES, ms_p)}
+        except RuntimeError as exc:
+            out["stream_probes"] = {"error": str(exc)}
     del src, dst
     torch.cuda.empty_cache()
     return out
