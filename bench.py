@@ -513,14 +513,21 @@ def measure_adam_row(name: str, steps: int, warmup: int) -> dict:
 # plain stream probes (libonebit_probe.so): mode, name, bytes per float
 BASIC_PROBES = ((0, "read", 4.0), (1, "write", 4.0), (2, "copy", 8.0),
                 (3, "read_two_write_one_in_place", 12.0))
+# the parameter passes' mixes: (reads, writes), name, bytes per float, and
+# the element count of the row whose pass has that mix (the LAMB pass on the
+# 302-tensor buffer, the Adam warm-up step on the 335M buffer)
+MIX_PROBES = (((3, 2), "read_three_write_two_in_place", 20.0, 336226304),
+              ((4, 3), "read_four_write_three_in_place", 28.0, 335141888))
 
 
 def measure_copy(steps: int, warmup: int) -> dict:
     """Plain streams over 2^31 floats as context for the rows: torch's device
     copy, and the probe library's hand-written read, write, copy and
     read-two-write-one-in-place streams (one float4 per lane, 256-thread
-    workgroups, nontemporal, the library kernels' access shape), the
-    practical HBM ceilings of those mixes on this GPU."""
+    workgroups, nontemporal, the library kernels' access shape), and the
+    read/write mixes of the LAMB pass (three reads, two writes) and the Adam
+    warm-up step (four reads, three writes): the practical HBM ceilings of
+    those mixes on this GPU."""
     import ctypes
 
     import torch
@@ -552,13 +559,36 @@ def measure_copy(steps: int, warmup: int) -> dict:
             if rc != 0:
                 raise RuntimeError(f"stream probe mode {mode}: status {rc}")
 
+        lib.onebit_probe_mix.restype = ctypes.c_int32
+        lib.onebit_probe_mix.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int32,
+                                                                 ctypes.c_int32, ctypes.c_void_p]
+        c3 = torch.empty_like(src)
+        c3.fill_(0.25)
+        c4 = torch.empty_like(src)
+        c4.fill_(0.125)
+
+        def mix(reads, writes, n_el):
+            rc = lib.onebit_probe_mix(src.data_ptr(), dst.data_ptr(), c3.data_ptr(), c4.data_ptr(),
+                                      n_el, reads, writes, ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"mix probe {reads}r{writes}w: status {rc}")
+
         fns = [lambda mode=mode: probe(mode) for mode, _, _ in BASIC_PROBES]
+        fns += [lambda rw=rw: mix(*rw, N) for rw, _, _, _ in MIX_PROBES]
+        fns += [lambda rw=rw, n_row=n_row: mix(*rw, n_row) for rw, _, _, n_row in MIX_PROBES]
         try:  # context only: a probe failure never fails the bench line
             ms_p = _time_calls(fns, warmup, steps, stream)
-            out["stream_probes"] = {name: rate(t, per * N)
-                                    for (_, name, per), t in zip(BASIC_PROBES, ms_p)}
+            nb = len(BASIC_PROBES)
+            sp = {name: rate(t, per * N) for (_, name, per), t in zip(BASIC_PROBES, ms_p)}
+            sp.update({name: rate(t, per * N)
+                       for (_, name, per, _), t in zip(MIX_PROBES, ms_p[nb:])})
+            out["stream_probes"] = sp
+            out["mix_probes_at_row_size"] = {
+                name: {"floats": n_row, **rate(t, per * n_row)}
+                for (_, name, per, n_row), t in zip(MIX_PROBES, ms_p[nb + len(MIX_PROBES):])}
         except RuntimeError as exc:
             out["stream_probes"] = {"error": str(exc)}
+        del c3, c4
     del src, dst
     torch.cuda.empty_cache()
     return out

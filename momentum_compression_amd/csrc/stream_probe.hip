@@ -211,9 +211,50 @@ __global__ __launch_bounds__(256) void basic_probe_kernel(const float* __restric
     __builtin_nontemporal_store(x + y, reinterpret_cast<f4*>(b + j));
 }
 
+// Streams with the read/write mixes of the parameter passes: R buffers read,
+// the first W of them written back in place (3 and 2: the LAMB pass with
+// both momenta packed, x, v_f and v_Tw read, x and v_f written; 4 and 3:
+// the Adam warm-up step).  Same access shape as above.
+template <int R, int W>
+__global__ __launch_bounds__(256) void mix_probe_kernel(float* __restrict__ a,
+                                                        float* __restrict__ b,
+                                                        float* __restrict__ c,
+                                                        float* __restrict__ d) {
+    static_assert(R >= 1 && R <= 4 && W >= 1 && W <= R, "mix");
+    const int64_t j = (int64_t)blockIdx.x * 1024 + 4 * (int64_t)threadIdx.x;
+    float* const p[4] = {a, b, c, d};
+    f4 v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[r] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p[r] + j));
+    f4 sum = v[0];
+#pragma unroll
+    for (int r = 1; r < R; ++r) sum = sum + v[r];
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+        __builtin_nontemporal_store(v[w] * 0.5f + sum, reinterpret_cast<f4*>(p[w] + j));
+}
+
 }  // namespace
 
 extern "C" {
+
+// Runs one read/write mix probe launch on `stream`: a, b, c, d N floats each
+// (device, 16-byte aligned; d may be NULL when reads is 3), the first
+// `reads` of them read and the first `writes` written back in place.
+// (reads, writes) must be (3, 2) or (4, 3); N a positive multiple of 1024
+// with N / 4 below 2^32.  Returns 0, -2 for an invalid size or mix, -6 for a
+// HIP launch error.
+int onebit_probe_mix(float* a, float* b, float* c, float* d, int64_t N, int32_t reads,
+                     int32_t writes, hipStream_t stream) {
+    if (N <= 0 || N % 1024 || N / 4 >= ((int64_t)1 << 32)) return -2;
+    const bool m32 = reads == 3 && writes == 2, m43 = reads == 4 && writes == 3;
+    if (!m32 && !m43) return -2;
+    (void)hipGetLastError();  // drop an error an earlier call left behind
+    const dim3 grid((unsigned)(N / 1024));
+    if (m32) hipLaunchKernelGGL((mix_probe_kernel<3, 2>), grid, dim3(256), 0, stream, a, b, c, d);
+    else hipLaunchKernelGGL((mix_probe_kernel<4, 3>), grid, dim3(256), 0, stream, a, b, c, d);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
 
 // Runs one plain stream probe launch on `stream`: a and b N floats each
 // (device, 16-byte aligned; b is overwritten by modes 1 to 3), mode 0 read

@@ -1,5 +1,5 @@
 """Host-side checks of the benchmark's probe library (libonebit_probe.so):
-it is built next to libonebit.so, exports its four probes, and rejects
+it is built next to libonebit.so, exports its five probes, and rejects
 invalid sizes before any HIP call (no GPU needed)."""
 
 import ctypes
@@ -25,6 +25,8 @@ def lib():
     L.onebit_probe_int8.argtypes = [P, P, P, P, P, I64, P]
     L.onebit_probe_basic.restype = I32
     L.onebit_probe_basic.argtypes = [P, P, I64, I32, P]
+    L.onebit_probe_mix.restype = I32
+    L.onebit_probe_mix.argtypes = [P, P, P, P, I64, I32, I32, P]
     return L
 
 
@@ -50,11 +52,16 @@ def test_probe_sizes_rejected_before_launch(lib):
     assert lib.onebit_probe_basic(None, None, 1 << 34, 0, None) == -2
     assert lib.onebit_probe_basic(None, None, 4096, 4, None) == -2
     assert lib.onebit_probe_basic(None, None, 4096, -1, None) == -2
+    # read/write mixes: (3, 2) or (4, 3) only, N as above
+    assert lib.onebit_probe_mix(None, None, None, None, 4096, 2, 1, None) == -2
+    assert lib.onebit_probe_mix(None, None, None, None, 4096, 3, 3, None) == -2
+    assert lib.onebit_probe_mix(None, None, None, None, 1000, 3, 2, None) == -2
+    assert lib.onebit_probe_mix(None, None, None, None, 1 << 34, 4, 3, None) == -2
 
 
 def test_probe_library_is_not_the_product_library():
     # the product library exports no probe (the probes are the benchmark's)
     prod = ctypes.CDLL(os.path.join(os.path.dirname(B.PROBE_LIB), "libonebit.so"))
     for name in ("onebit_probe_stream", "onebit_probe_server", "onebit_probe_int8",
-                 "onebit_probe_basic"):
+                 "onebit_probe_basic", "onebit_probe_mix"):
         assert not hasattr(prod, name)
