@@ -83,9 +83,21 @@ int main(void) {
     CHECK_HIP(hipMemcpy(x, h_x, sizeof h_x, hipMemcpyHostToDevice));
     CHECK_HIP(hipMemcpy(v, h_v, sizeof h_v, hipMemcpyHostToDevice));
 
+    /* an error that an earlier HIP call left as this thread's last error (a
+       device ordinal no machine has) is neither reported by the library nor
+       kept after its call */
+    if (hipSetDevice(ndev + 4096) == hipSuccess || hipPeekAtLastError() == hipSuccess) {
+        printf("could not leave a stale HIP error at line %d\n", __LINE__);
+        return 1;
+    }
+
     /* one reset step on the null stream */
     CHECK_ONEBIT(onebit_compress(m, ef, scales, bits, NE, NW, 0.0f, 1, NULL, NULL, 0, ws, ws_bytes,
                                  NULL));
+    if (hipPeekAtLastError() != hipSuccess) {
+        printf("stale HIP error kept at line %d\n", __LINE__);
+        return 1;
+    }
     CHECK_ONEBIT(onebit_server_reduce(bits, scales, sv_ef, sv_scales, sv_bits, mbar, NULL, NULL, 0,
                                       NE, NW, 1, ws, ws_bytes, NULL));
     onebit_frozen_v_args a;
